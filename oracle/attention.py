@@ -1,0 +1,131 @@
+"""Oracle attention and error metrics in fp64.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Definitions ([E21W, Benchmark]: attention output and the attention
+distribution are compared against fp16; K/V error is squared error over signal
+energy; attention error is the relative error of the attention output; KL is
+the divergence of the attention distribution from the fp16 one):
+
+* logits l_t = sigma * (q . k_t) over keys t < n, sigma = 1/sqrt(D) unless given;
+* p = softmax(l) (max-subtracted), o = sum_t p_t v_t;
+* KL_r = sum_t p_t (ln p_t - ln phat_t) with p from fp16 K/V and phat from the
+  dequantised K/V, in nats; terms with p_t = 0 contribute 0;
+* eps_r = ||ohat - o||_2 / ||o||_2;
+* E_u = sum (xhat - x)^2 / sum x^2 per (batch, layer, KV head) unit.
+
+GQA: query head j reads KV head floor(j / (Hq/H)) (the pages never say; this is
+the repeat-kv convention of the Hugging Face simulation in [E22L, Result]).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _lse(x: np.ndarray) -> np.ndarray:
+    m = x.max(-1, keepdims=True)
+    return (m + np.log(np.exp(x - m).sum(-1, keepdims=True)))[..., 0]
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, n: int, sm_scale: float):
+    """q [G, D], K/V [T, D] (any float, used in fp64), keys [0, n) ->
+    (out [G, D], lse [G], logits [G, n])."""
+    q = np.asarray(q, dtype=np.float64)
+    if n == 0:
+        G, D = q.shape
+        return np.zeros((G, V.shape[1])), np.full(G, -np.inf), np.zeros((G, 0))
+    k = np.asarray(K[:n], dtype=np.float64)
+    v = np.asarray(V[:n], dtype=np.float64)
+    logits = sm_scale * (q @ k.T)
+    m = logits.max(-1, keepdims=True)
+    e = np.exp(logits - m)
+    Z = e.sum(-1, keepdims=True)
+    p = e / Z
+    return p @ v, (m + np.log(Z))[..., 0], logits
+
+
+def attend_unit(q, K, V, kv_len, sm_scale):
+    """All queries of one (batch, layer, KV head) unit: q [nq, G, D] ->
+    (out [nq, G, D], lse [nq, G])."""
+    nq, G, D = q.shape
+    out = np.zeros((nq, G, V.shape[1]))
+    lse = np.zeros((nq, G))
+    for i in range(nq):
+        out[i], lse[i], _ = attend(q[i], K, V, int(kv_len[i]), sm_scale)
+    return out, lse
+
+
+def _scale(D, sm_scale):
+    return 1.0 / np.sqrt(D) if not sm_scale else float(sm_scale)
+
+
+def decode_attn(q16, Kd, Vd, kv_len=None, sm_scale=0.0):
+    """q16 [B][L][nq][Hq][D] fp16, Kd/Vd [B][L][H][T][D] dequantised (or fp16)
+    -> (out float64 [B][L][nq][Hq][D], lse [B][L][nq][Hq])."""
+    B, L, nq, Hq, D = q16.shape
+    H, T = Kd.shape[2], Kd.shape[3]
+    G = Hq // H
+    s = _scale(D, sm_scale)
+    out = np.zeros((B, L, nq, Hq, Vd.shape[-1]))
+    lse = np.zeros((B, L, nq, Hq))
+    q = q16.astype(np.float64)
+    for b in range(B):
+        for l in range(L):
+            n = np.full(nq, T) if kv_len is None else kv_len[b, l]
+            for h in range(H):
+                o, z = attend_unit(q[b, l, :, h * G:(h + 1) * G], Kd[b, l, h], Vd[b, l, h], n, s)
+                out[b, l, :, h * G:(h + 1) * G] = o
+                lse[b, l, :, h * G:(h + 1) * G] = z
+    return out, lse
+
+
+def kl_div(logits_ref: np.ndarray, logits_q: np.ndarray) -> np.ndarray:
+    """KL(p_ref || p_q) in nats over the last axis of two logit arrays."""
+    if logits_ref.shape[-1] == 0:
+        return np.zeros(logits_ref.shape[:-1])
+    lp = logits_ref - _lse(logits_ref)[..., None]
+    lq = logits_q - _lse(logits_q)[..., None]
+    p = np.exp(lp)
+    return np.where(p > 0, p * (lp - lq), 0.0).sum(-1)
+
+
+def rel_err(o_hat: np.ndarray, o: np.ndarray) -> np.ndarray:
+    num = np.linalg.norm(o_hat - o, axis=-1)
+    den = np.linalg.norm(o, axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), 0.0)
+
+
+def kv_err_unit(x16: np.ndarray, x_hat: np.ndarray):
+    """(sum (xhat - x)^2, sum x^2) in fp64 for one unit's rows."""
+    x = x16.astype(np.float64)
+    d = np.asarray(x_hat, dtype=np.float64) - x
+    return float((d * d).sum()), float((x * x).sum())
+
+
+def attn_error(q16, K16, V16, Kd, Vd, kv_len=None, sm_scale=0.0, units=None):
+    """Per-row KL and relative output error of attention through (Kd, Vd) vs
+    fp16 (K16, V16), plus per-unit K/V error sums.
+
+    Returns kl [B][L][nq][Hq], relerr [B][L][nq][Hq], kv_err [B][L][H][4] with
+    (sum dK^2, sum K^2, sum dV^2, sum V^2).  `units`, if given, is a list of
+    (b, l, h) to evaluate (others are left as NaN).
+    """
+    B, L, nq, Hq, D = q16.shape
+    H, T = K16.shape[2], K16.shape[3]
+    G = Hq // H
+    s = _scale(D, sm_scale)
+    kl = np.full((B, L, nq, Hq), np.nan)
+    re = np.full((B, L, nq, Hq), np.nan)
+    kv = np.full((B, L, H, 4), np.nan)
+    q = q16.astype(np.float64)
+    todo = units if units is not None else [(b, l, h) for b in range(B) for l in range(L) for h in range(H)]
+    for (b, l, h) in todo:
+        n = np.full(nq, T) if kv_len is None else kv_len[b, l]
+        for i in range(nq):
+            o, _, lr = attend(q[b, l, i, h * G:(h + 1) * G], K16[b, l, h], V16[b, l, h], int(n[i]), s)
+            oh, _, lq = attend(q[b, l, i, h * G:(h + 1) * G], Kd[b, l, h], Vd[b, l, h], int(n[i]), s)
+            kl[b, l, i, h * G:(h + 1) * G] = kl_div(lr, lq)
+            re[b, l, i, h * G:(h + 1) * G] = rel_err(oh, o)
+        kv[b, l, h, 0:2] = kv_err_unit(K16[b, l, h], Kd[b, l, h])
+        kv[b, l, h, 2:4] = kv_err_unit(V16[b, l, h], Vd[b, l, h])
+    return kl, re, kv
