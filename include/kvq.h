@@ -1,0 +1,206 @@
+/*
+ * kvq.h - C ABI of libkvq: group-wise low-bit KV-cache quantisation and decode
+ * attention read back through the packed cache, for AMD MI355X (gfx950).
+ *
+ * Sources of the operations (web pages; cited by title and section):
+ *  [E22L]  "Can 4-bit keys and 2-bit values hit a 1M-token memory budget?
+ *          Simulated KV cache, 4B model, 64K" - What I tested, Result.
+ *  [E21W]  "PROVISIONAL: known 3-bit KV cache methods on the 4B fall well short
+ *          of 4-bit quality (proxy queries)" - Benchmark, What I tested, Result.
+ *  [FMAG-6] HF forum "Fourier Magnitude KV Cache Quantization", post #6 -
+ *          Minimal recipe, Milestone, Best results, Mechanism findings.
+ *  [FMAG-R] same thread, the Colab-probe reply - the rFFT physical codec
+ *          (packed magnitude index + packed phase-angle index), real/imag control.
+ *  [LCPP]  llama.cpp issue #21385 - independent K and V cache types (-ctk/-ctv).
+ *
+ * Conventions for every entry point
+ *  - Tensors are dense, row-major [batch][layers][heads][tokens][head_dim]; a
+ *    "row" is one head_dim vector.  Device pointers must be 16-byte aligned.
+ *  - The caller owns every buffer (allocate with the sizes the layout and
+ *    workspace queries return).  The library never allocates, frees or
+ *    synchronises; all device work is enqueued on `stream` (a hipStream_t; NULL
+ *    = the null stream) and returns before it completes.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error nothing is written.  A failed launch returns KVQ_ERR_HIP.
+ *  - Inputs must be finite; results for NaN/Inf inputs are unspecified (but
+ *    every access stays in bounds).
+ *  - Calls on one stream are ordered; calls that write the same buffers on
+ *    different streams race.  No C++ exception crosses this interface.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,          /* null pointer, bad shape, inconsistent K/V shapes */
+  KVQ_ERR_UNSUPPORTED = -2,  /* codec/bits/group/rotation not supported */
+  KVQ_ERR_ALIGN = -3,        /* device pointer not 16-byte aligned */
+  KVQ_ERR_WORKSPACE = -4,    /* workspace smaller than the query returned */
+  KVQ_ERR_HIP = -5           /* HIP launch or runtime error */
+} kvq_status;
+
+/* Codebooks.  Dequantised values (before the inverse rotation) per group with
+ * fp16 scale s (and fp16 minimum z):
+ *  FP16        identity; the "codes" are the fp16 rows (anchor layers, [FMAG-6]
+ *              Minimal recipe: layer 0 kept fp16).
+ *  INT_ABSMAX  {-2^(b-1), ..., 2^(b-1)-1} * s, ggml-style signed absmax; the
+ *              scale takes the sign of the group's extreme value ([E22L] Result:
+ *              the 2-bit grid {-2,-1,0,1}*s).  bits 2..8.
+ *  INT_MINMAX  {0, ..., 2^b-1} * s + z ([E21W] What I tested, arm A).  bits 2..8.
+ *  TERNARY     {-s, 0, +s}, s = group absmax, 2 stored bits ([FMAG-6] Milestone).
+ *  SIGN        {-s, +s}, s = mean |y|, 1 bit ([FMAG-6] Minimal recipe).
+ *  NF4         NormalFloat-4 levels * s, s = group absmax, 4 bits ([FMAG-6]
+ *              Milestone "NF4-K").
+ *  INT8_SYM    {-127..127} * s, s = absmax/127, 8 bits ([FMAG-6] int8 KV row).
+ *  RFFT_POLAR  rFFT along head_dim (D/2+1 bins); per bin an unsigned `bits`
+ *              magnitude code (fp16 scale per `group` bins) and an `aux_bits`
+ *              phase-sector code ([FMAG-R] physical codec).  Keys only.
+ *  RFFT_CART   rFFT; real and imaginary parts each INT_ABSMAX with `bits` bits
+ *              per `group` bins ([FMAG-R] real/imag control).  Keys only.
+ * Scalar rules (rounding, ties, zero groups) are those of the CPU oracle:
+ * binary32 arithmetic, round-to-nearest-even, fp16 scales saturated to
+ * +-65504 and never -0. */
+typedef enum {
+  KVQ_FP16 = 0,
+  KVQ_INT_ABSMAX = 1,
+  KVQ_INT_MINMAX = 2,
+  KVQ_TERNARY = 3,
+  KVQ_SIGN = 4,
+  KVQ_NF4 = 5,
+  KVQ_INT8_SYM = 6,
+  KVQ_RFFT_POLAR = 7,
+  KVQ_RFFT_CART = 8
+} kvq_codebook;
+
+typedef struct {
+  int32_t codebook;   /* kvq_codebook */
+  int32_t bits;       /* INT_ABSMAX/INT_MINMAX: 2..8; RFFT_*: 2..8 magnitude/component
+                         bits; ignored (implied) for the other codebooks */
+  int32_t group;      /* values per scale: 8, 16, 32, 64, 128 or 256 (<= head_dim);
+                         RFFT_*: bins per scale (8..128) */
+  int32_t rot_width;  /* Walsh-Hadamard width: 0 (none) or a power of two in
+                         [2, head_dim]; applied per rot_width block of each row
+                         ([E22L] What I tested: 256-wide Hadamard rotation) */
+  int32_t aux_bits;   /* RFFT_POLAR phase bits: 3..8; else 0 */
+} kvq_codec;
+
+typedef struct {
+  int32_t batch, layers, heads, tokens, head_dim;  /* head_dim in {64, 128, 256} */
+} kvq_shape;
+
+/* A packed tensor.  codes: uint32 [rows][code_words_per_row] (FP16: the fp16
+ * rows themselves); scales: fp16 [rows][scales_per_row]; mins: fp16
+ * [rows][mins_per_row] (INT_MINMAX only, else NULL); chan_scale: optional fp32
+ * [layers][heads][head_dim] per-channel multipliers applied before the rotation
+ * and divided back out after dequantising ([E21W] What I tested, arms C/D),
+ * NULL for none.  Bit layout: per row, code j occupies bits [j*b, (j+1)*b) of a
+ * little-endian stream of uint32 words (RFFT_POLAR: all magnitude codes, then
+ * all phase codes; RFFT_CART: all real codes, then all imaginary codes). */
+typedef struct {
+  kvq_codec codec;
+  kvq_shape shape;
+  uint32_t* codes;
+  uint16_t* scales;
+  uint16_t* mins;
+  const float* chan_scale;
+} kvq_packed;
+
+/* Human-readable status. */
+const char* kvq_status_string(kvq_status s);
+
+/* Library version string. */
+const char* kvq_version(void);
+
+/* Host only (no device needed).  Per-row sizes of a packed tensor. */
+kvq_status kvq_packed_layout(const kvq_shape* shape, const kvq_codec* codec,
+                             size_t* code_words_per_row, size_t* scales_per_row,
+                             size_t* mins_per_row);
+
+/* Host only.  Stored bits per value including fp16 scales (and mins): b + 16 *
+ * n_params / group; FP16 = 16; rFFT codecs: exact bits per row / head_dim
+ * ([E21W] Result: 3.5 / 4.5 bits at group 32; [E22L] What I tested: 3.125 ...
+ * 3.625 for the K+V arms).  Returns a negative value for an invalid codec. */
+double kvq_bits_per_value(const kvq_codec* codec, int32_t head_dim);
+
+/* Host only.  Copies a constant table the kernels use into `out` (n floats):
+ * which = 0 NF4 levels (16), 1 NF4 midpoints (15), 2/3 FFT twiddle cos/-sin
+ * for head_dim n*2 (n = D/2 entries), 4/5 phase-sector direction cos/sin for
+ * 2^aux sectors (n = 2^aux), 6/7 first-octant sector boundary cos/sin (n =
+ * 2^aux / 8). */
+kvq_status kvq_constant_table(int32_t which, int32_t n, float* out);
+
+/* Per-channel key multipliers from a calibration sequence ([E21W] What I
+ * tested, arm C: per-channel K scaling calibrated offline): chan_scale[l][h][d]
+ * = RN32(1 / max_t |k[0][l][h][t][d]|), or 1 for an all-zero channel.  k_fp16
+ * is [1][layers][heads][tokens][head_dim] (batch must be 1); chan_scale is
+ * fp32 [layers][heads][head_dim]. */
+kvq_status kvq_calibrate_chan_scale(const uint16_t* k_fp16, const kvq_shape* shape,
+                                    float* chan_scale, void* stream);
+
+/* Quantise and pack fp16 rows x_fp16 [B][L][H][T][D] into `out` (codes,
+ * scales, mins; shape and codec taken from `out`).  One fused kernel per call:
+ * load, optional per-channel multiply, optional Walsh-Hadamard rotation, group
+ * statistic, fp16 scale, code, bit-pack ([E22L] What I tested; [E21W] What I
+ * tested).  Codes and scales are bit-identical to the CPU oracle. */
+kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void* stream);
+
+/* Dequantise `in` to fp32 x_hat [B][L][H][T][D] in the original coordinates
+ * (inverse codebook, inverse rotation, division by chan_scale). */
+kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream);
+
+/* Bytes of workspace kvq_decode_attn needs for these sizes. */
+size_t kvq_decode_attn_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q);
+
+/* Decode attention read back through packed K and V ([E22L] What I tested:
+ * attention over the quantised post-RoPE cache; [E21W] Benchmark: causal
+ * proxy queries).  q: fp16 [B][L][n_q][q_heads][D]; query head j reads KV head
+ * j / (q_heads / heads).  kv_len: int32 [B][L][n_q] keys attended per query
+ * (keys [0, kv_len)), NULL = all tokens; values are clamped to [0, tokens].
+ * sm_scale: logit scale, 0 = 1/sqrt(head_dim).  out: fp32 [B][L][n_q][q_heads][D];
+ * lse: fp32 [B][L][n_q][q_heads] natural-log partition (-inf for no keys),
+ * nullable.  K and V must have the same shape; V's codebook may not be an rFFT
+ * codec.  ws: device workspace of at least kvq_decode_attn_workspace() bytes.
+ * K dequantisation happens in registers/LDS: rotated keys are read by rotating
+ * the query instead, rotated values by rotating the output once per query. */
+kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
+                           int32_t n_q, const uint16_t* q, const int32_t* kv_len,
+                           float sm_scale, float* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* As kvq_decode_attn, choosing the kernel: path 0 = automatic, 1 = the general
+ * kernel (every codec), 2 = the MFMA kernel (INT_ABSMAX K and V with group a
+ * multiple of 32, head_dim 128/256; KVQ_ERR_UNSUPPORTED otherwise). */
+kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
+                              int32_t n_q, const uint16_t* q, const int32_t* kv_len,
+                              float sm_scale, float* out, float* lse, void* ws,
+                              size_t ws_bytes, int32_t path, void* stream);
+
+/* Bytes of workspace kvq_attn_error needs. */
+size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q);
+
+/* Attention-visible error of the packed cache against fp16 ([E21W] Benchmark:
+ * K/V error is squared error over signal energy, attention error is the
+ * relative error of the attention output, KL is the divergence of the
+ * attention distribution from f16).  One pass over fp16 K/V and packed K/V per
+ * query: kl_rows [B][L][n_q][q_heads] = KL(p_fp16 || p_quant) in nats,
+ * relerr_rows = ||o_quant - o_fp16|| / ||o_fp16||; kv_err [B][L][H][4] fp64 =
+ * (sum dK^2, sum K^2, sum dV^2, sum V^2) over the unit's rows, with dK the
+ * dequantised minus fp16 value in original coordinates.  Other arguments as
+ * for kvq_decode_attn. */
+kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16,
+                          const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
+                          int32_t n_q, const uint16_t* q, const int32_t* kv_len,
+                          float sm_scale, float* kl_rows, float* relerr_rows,
+                          double* kv_err, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

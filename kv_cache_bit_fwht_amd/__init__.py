@@ -1,0 +1,248 @@
+"""Python binding of libkvq (MI355X / gfx950 group-wise low-bit KV-cache codec and
+packed decode attention).
+
+Argument marshalling only: every function here forwards to the C entry point of
+the same name in ``libkvq.so`` (declared in ``include/kvq.h``); all computation
+runs in the HIP kernels.  PyTorch supplies device memory (``tensor.data_ptr()``)
+and the current stream.  Importing this package fails loudly if the library has
+not been built; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+# codebooks (kvq_codebook)
+FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART = range(9)
+
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_ALIGN",
+          -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
+
+EXPORTS = [
+    "kvq_status_string", "kvq_version", "kvq_packed_layout", "kvq_bits_per_value",
+    "kvq_constant_table", "kvq_calibrate_chan_scale", "kvq_quantize_pack", "kvq_dequant",
+    "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_ex",
+    "kvq_attn_error_workspace", "kvq_attn_error",
+]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+
+
+class kvq_codec(ctypes.Structure):
+    _fields_ = [("codebook", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("rot_width", ctypes.c_int32), ("aux_bits", ctypes.c_int32)]
+
+
+class kvq_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("layers", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("tokens", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class kvq_packed(ctypes.Structure):
+    _fields_ = [("codec", kvq_codec), ("shape", kvq_shape), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("mins", ctypes.c_void_p), ("chan_scale", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_bit_fwht_amd.build` "
+                          "(or __graft_entry__.build()); there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_double
+    sig = {
+        "kvq_status_string": ([I32], ctypes.c_char_p),
+        "kvq_version": ([], ctypes.c_char_p),
+        "kvq_packed_layout": ([P, P, P, P, P], I32),
+        "kvq_bits_per_value": ([P, I32], D),
+        "kvq_constant_table": ([I32, I32, P], I32),
+        "kvq_calibrate_chan_scale": ([P, P, P, P], I32),
+        "kvq_quantize_pack": ([P, P, P], I32),
+        "kvq_dequant": ([P, P, P], I32),
+        "kvq_decode_attn_workspace": ([P, I32, I32], SZ),
+        "kvq_decode_attn": ([P, P, I32, I32, P, P, F, P, P, P, SZ, P], I32),
+        "kvq_decode_attn_ex": ([P, P, I32, I32, P, P, F, P, P, P, SZ, I32, P], I32),
+        "kvq_attn_error_workspace": ([P, I32, I32], SZ),
+        "kvq_attn_error": ([P, P, P, P, I32, I32, P, P, F, P, P, P, P, SZ, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+# ------------------------------------------------------------------ python-side descriptions
+
+@dataclasses.dataclass(frozen=True)
+class Codec:
+    codebook: int
+    bits: int = 0
+    group: int = 0
+    rot_width: int = 0
+    aux_bits: int = 0
+
+    def c(self) -> kvq_codec:
+        return kvq_codec(self.codebook, self.bits, self.group, self.rot_width, self.aux_bits)
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    batch: int
+    layers: int
+    heads: int
+    tokens: int
+    head_dim: int
+
+    def c(self) -> kvq_shape:
+        return kvq_shape(self.batch, self.layers, self.heads, self.tokens, self.head_dim)
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.layers * self.heads * self.tokens
+
+
+@dataclasses.dataclass
+class Packed:
+    """A packed tensor: torch tensors on the device plus its codec and shape."""
+    codec: Codec
+    shape: Shape
+    codes: object           # torch.int32 [rows][words]  (uint32 bit pattern)
+    scales: object          # torch.int16 [rows][ns]     (fp16 bit pattern)
+    mins: object            # torch.int16 [rows][nm] or None
+    chan_scale: object = None  # torch.float32 [L][H][D] or None
+
+    def c(self) -> kvq_packed:
+        return kvq_packed(self.codec.c(), self.shape.c(), _ptr(self.codes), _ptr(self.scales),
+                          _ptr(self.mins), _ptr(self.chan_scale))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr() if t.numel() else None
+
+
+def _check(fn, st):
+    if st != 0:
+        raise KvqError(fn, st)
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ------------------------------------------------------------------ entry points
+
+def kvq_status_string(status: int) -> str:
+    return _lib.kvq_status_string(status).decode()
+
+
+def kvq_version() -> str:
+    return _lib.kvq_version().decode()
+
+
+def kvq_packed_layout(shape: Shape, codec: Codec):
+    w, s, m = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    sc, cc = shape.c(), codec.c()
+    _check("kvq_packed_layout", _lib.kvq_packed_layout(ctypes.byref(sc), ctypes.byref(cc), ctypes.byref(w),
+                                                       ctypes.byref(s), ctypes.byref(m)))
+    return w.value, s.value, m.value
+
+
+def kvq_bits_per_value(codec: Codec, head_dim: int) -> float:
+    cc = codec.c()
+    return _lib.kvq_bits_per_value(ctypes.byref(cc), head_dim)
+
+
+def kvq_constant_table(which: int, n: int):
+    import numpy as np
+    out = np.zeros(n, dtype=np.float32)
+    _check("kvq_constant_table", _lib.kvq_constant_table(which, n, out.ctypes.data))
+    return out
+
+
+def kvq_calibrate_chan_scale(k_fp16, shape: Shape, chan_scale, stream=None):
+    sc = shape.c()
+    _check("kvq_calibrate_chan_scale",
+           _lib.kvq_calibrate_chan_scale(_ptr(k_fp16), ctypes.byref(sc), _ptr(chan_scale), _stream(stream)))
+
+
+def kvq_quantize_pack(x_fp16, out: Packed, stream=None):
+    pc = out.c()
+    _check("kvq_quantize_pack", _lib.kvq_quantize_pack(_ptr(x_fp16), ctypes.byref(pc), _stream(stream)))
+
+
+def kvq_dequant(inp: Packed, x_hat, stream=None):
+    pc = inp.c()
+    _check("kvq_dequant", _lib.kvq_dequant(ctypes.byref(pc), _ptr(x_hat), _stream(stream)))
+
+
+def kvq_decode_attn_workspace(shape: Shape, q_heads: int, n_q: int) -> int:
+    sc = shape.c()
+    return _lib.kvq_decode_attn_workspace(ctypes.byref(sc), q_heads, n_q)
+
+
+def kvq_decode_attn(k: Packed, v: Packed, q_heads: int, n_q: int, q, kv_len, sm_scale: float, out, lse,
+                    ws, ws_bytes: int, stream=None, path: int | None = None):
+    kc, vc = k.c(), v.c()
+    if path is None:
+        st = _lib.kvq_decode_attn(ctypes.byref(kc), ctypes.byref(vc), q_heads, n_q, _ptr(q), _ptr(kv_len),
+                                  sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+        _check("kvq_decode_attn", st)
+    else:
+        st = _lib.kvq_decode_attn_ex(ctypes.byref(kc), ctypes.byref(vc), q_heads, n_q, _ptr(q), _ptr(kv_len),
+                                     sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, path, _stream(stream))
+        _check("kvq_decode_attn_ex", st)
+
+
+def kvq_decode_attn_ex(k: Packed, v: Packed, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes,
+                       path: int, stream=None):
+    kvq_decode_attn(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes, stream, path)
+
+
+def kvq_attn_error_workspace(shape: Shape, q_heads: int, n_q: int) -> int:
+    sc = shape.c()
+    return _lib.kvq_attn_error_workspace(ctypes.byref(sc), q_heads, n_q)
+
+
+def kvq_attn_error(k_fp16, v_fp16, k: Packed, v: Packed, q_heads: int, n_q: int, q, kv_len, sm_scale: float,
+                   kl_rows, relerr_rows, kv_err, ws, ws_bytes: int, stream=None):
+    kc, vc = k.c(), v.c()
+    st = _lib.kvq_attn_error(_ptr(k_fp16), _ptr(v_fp16), ctypes.byref(kc), ctypes.byref(vc), q_heads, n_q,
+                             _ptr(q), _ptr(kv_len), sm_scale, _ptr(kl_rows), _ptr(relerr_rows), _ptr(kv_err),
+                             _ptr(ws), ws_bytes, _stream(stream))
+    _check("kvq_attn_error", st)
+
+
+# ------------------------------------------------------------------ device-memory plumbing
+
+def alloc_packed(codec: Codec, shape: Shape, device="cuda", chan_scale=None) -> Packed:
+    """Allocate the device buffers of a packed tensor (sizes from kvq_packed_layout)."""
+    import torch
+    w, s, m = kvq_packed_layout(shape, codec)
+    rows = shape.rows
+    codes = torch.empty((rows, w), dtype=torch.int32, device=device)
+    scales = torch.empty((rows, s), dtype=torch.int16, device=device)
+    mins = torch.empty((rows, m), dtype=torch.int16, device=device) if m else None
+    return Packed(codec, shape, codes, scales, mins, chan_scale)
+
+
+def packed_from_fp16(x_fp16, shape: Shape) -> Packed:
+    """View fp16 rows as an FP16-codebook packed tensor (anchor layers): no copy."""
+    return Packed(Codec(FP16), shape, x_fp16, None, None, None)

@@ -1,0 +1,360 @@
+// libkvq C ABI: argument validation, layout and workspace queries, constant
+// tables, and dispatch to the kernels.  Every check runs on the host before any
+// launch, so an invalid call writes nothing.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "kvq_internal.hpp"
+
+namespace kvq {
+
+// ------------------------------------------------------------------ constant tables
+
+// Standard normal quantile by bisection on Phi(x) = erfc(-x/sqrt 2)/2 in fp64.
+static double norm_ppf(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 2000; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid == lo || mid == hi) break;
+    const double c = 0.5 * std::erfc(-mid / std::sqrt(2.0));
+    if (c < p) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+// NormalFloat-4 (QLoRA, Dettmers et al. 2023, section 3): 8 positive normal
+// quantiles at probabilities linspace(1-d, 1/2, 9) without its last point, 7
+// negative ones at linspace(1-d, 1/2, 8) without its last point, d = (1/30 +
+// 1/32)/2, an exact zero, all divided by the largest; fp64 then binary32.
+// The pages name NF4 ([FMAG-6] Milestone) without printing levels.
+static Tables build_tables() {
+  Tables t{};
+  const double off = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
+  double v[16];
+  int n = 0;
+  {
+    const double step = (0.5 - off) / 8.0;
+    for (int i = 0; i < 8; ++i) v[n++] = norm_ppf(i * step + off);
+  }
+  v[n++] = 0.0;
+  {
+    const double step = (0.5 - off) / 7.0;
+    for (int i = 0; i < 7; ++i) v[n++] = -norm_ppf(i * step + off);
+  }
+  // sort ascending (insertion sort: 16 values)
+  for (int i = 1; i < 16; ++i)
+    for (int k = i; k > 0 && v[k - 1] > v[k]; --k) { double tmp = v[k]; v[k] = v[k - 1]; v[k - 1] = tmp; }
+  const double mx = v[15];
+  for (int i = 0; i < 16; ++i) t.nf4_lv[i] = (float)(v[i] / mx);
+  for (int i = 0; i < 15; ++i) {
+    const float s = t.nf4_lv[i] + t.nf4_lv[i + 1];
+    t.nf4_mid[i] = s * 0.5f;
+  }
+  t.nf4_mid[15] = INFINITY;
+  return t;
+}
+
+const Tables& host_tables() {
+  static const Tables t = build_tables();
+  return t;
+}
+
+void host_fft_tables(int N, FftTables* t) {
+  std::memset(t, 0, sizeof(*t));
+  for (int k = 0; k < N / 2; ++k) {
+    const double ang = 2.0 * M_PI * k / N;
+    t->tw_c[k] = (float)std::cos(ang);
+    t->tw_s[k] = (float)(-std::sin(ang));
+  }
+}
+
+void host_phase_tables(int P, PhaseTables* t) {
+  std::memset(t, 0, sizeof(*t));
+  for (int k = 0; k < P; ++k) {
+    const double ang = 2.0 * M_PI * k / P;
+    t->dir_c[k] = (float)std::cos(ang);
+    t->dir_s[k] = (float)std::sin(ang);
+  }
+  for (int j = 0; j < P / 8; ++j) {
+    const double ang = (2.0 * j + 1.0) * M_PI / P;
+    t->bnd_c[j] = (float)std::cos(ang);
+    t->bnd_s[j] = (float)std::sin(ang);
+  }
+}
+
+// ------------------------------------------------------------------ validation
+
+static bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static kvq_status check_shape(const kvq_shape* s) {
+  if (!s) return KVQ_ERR_ARG;
+  if (s->batch < 1 || s->layers < 1 || s->heads < 1 || s->tokens < 0) return KVQ_ERR_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  const double rows = (double)s->batch * s->layers * s->heads * s->tokens;
+  if (rows * s->head_dim > 9.0e15) return KVQ_ERR_ARG;
+  return KVQ_OK;
+}
+
+static bool is_rfft(int cb) { return cb == KVQ_RFFT_POLAR || cb == KVQ_RFFT_CART; }
+
+static kvq_status check_codec(const kvq_codec* c, int D) {
+  if (!c) return KVQ_ERR_ARG;
+  const int cb = c->codebook;
+  if (cb < KVQ_FP16 || cb > KVQ_RFFT_CART) return KVQ_ERR_UNSUPPORTED;
+  if (cb == KVQ_FP16) return KVQ_OK;
+  if (is_rfft(cb)) {
+    if (c->bits < 2 || c->bits > 8) return KVQ_ERR_UNSUPPORTED;
+    if (c->group < 8 || c->group > 128 || !pow2(c->group)) return KVQ_ERR_UNSUPPORTED;
+    if (c->rot_width != 0) return KVQ_ERR_UNSUPPORTED;
+    if (cb == KVQ_RFFT_POLAR && (c->aux_bits < 3 || c->aux_bits > 8)) return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+  }
+  if (cb == KVQ_INT_ABSMAX || cb == KVQ_INT_MINMAX) {
+    if (c->bits < 2 || c->bits > 8) return KVQ_ERR_UNSUPPORTED;
+  }
+  if (!pow2(c->group) || c->group < 8 || c->group > 256 || c->group > D) return KVQ_ERR_UNSUPPORTED;
+  if (c->rot_width != 0 && (!pow2(c->rot_width) || c->rot_width < 2 || c->rot_width > D))
+    return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+static int code_bits(const kvq_codec& c) {
+  switch (c.codebook) {
+    case KVQ_FP16: return 16;
+    case KVQ_TERNARY: return 2;
+    case KVQ_SIGN: return 1;
+    case KVQ_NF4: return 4;
+    case KVQ_INT8_SYM: return 8;
+    default: return c.bits;
+  }
+}
+
+static void layout_of(const kvq_codec& c, int D, size_t* words, size_t* ns, size_t* nm) {
+  if (is_rfft(c.codebook)) {
+    const int F = D / 2 + 1, ng = (F + c.group - 1) / c.group;
+    const long bits = (c.codebook == KVQ_RFFT_POLAR) ? (long)F * (c.bits + c.aux_bits) : 2L * F * c.bits;
+    *words = (size_t)((bits + 31) / 32);
+    *ns = (size_t)((c.codebook == KVQ_RFFT_POLAR) ? ng : 2 * ng);
+    *nm = 0;
+    return;
+  }
+  *words = (size_t)D * code_bits(c) / 32;
+  *ns = (c.codebook == KVQ_FP16) ? 0 : (size_t)(D / c.group);
+  *nm = (c.codebook == KVQ_INT_MINMAX) ? *ns : 0;
+}
+
+static kvq_status check_packed(const kvq_packed* p, bool need_write) {
+  (void)need_write;
+  if (!p) return KVQ_ERR_ARG;
+  kvq_status st = check_shape(&p->shape);
+  if (st != KVQ_OK) return st;
+  st = check_codec(&p->codec, p->shape.head_dim);
+  if (st != KVQ_OK) return st;
+  size_t w, ns, nm;
+  layout_of(p->codec, p->shape.head_dim, &w, &ns, &nm);
+  if (!p->codes) return KVQ_ERR_ARG;
+  if (ns && !p->scales) return KVQ_ERR_ARG;
+  if (nm && !p->mins) return KVQ_ERR_ARG;
+  if (!aligned16(p->codes) || (p->scales && !aligned16(p->scales)) || (p->mins && !aligned16(p->mins)) ||
+      (p->chan_scale && !aligned16(p->chan_scale)))
+    return KVQ_ERR_ALIGN;
+  if (p->chan_scale && p->codec.codebook == KVQ_FP16) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+static bool same_shape(const kvq_shape& a, const kvq_shape& b) {
+  return a.batch == b.batch && a.layers == b.layers && a.heads == b.heads && a.tokens == b.tokens &&
+         a.head_dim == b.head_dim;
+}
+
+static kvq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVQ_OK;
+  return KVQ_ERR_HIP;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported codec or shape";
+    case KVQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kvq_version(void) { return "kvq 0.1 gfx950"; }
+
+kvq_status kvq_packed_layout(const kvq_shape* shape, const kvq_codec* codec, size_t* code_words_per_row,
+                             size_t* scales_per_row, size_t* mins_per_row) {
+  kvq_status st = check_shape(shape);
+  if (st != KVQ_OK) return st;
+  st = check_codec(codec, shape->head_dim);
+  if (st != KVQ_OK) return st;
+  if (!code_words_per_row || !scales_per_row || !mins_per_row) return KVQ_ERR_ARG;
+  layout_of(*codec, shape->head_dim, code_words_per_row, scales_per_row, mins_per_row);
+  return KVQ_OK;
+}
+
+double kvq_bits_per_value(const kvq_codec* codec, int32_t head_dim) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return -1.0;
+  if (check_codec(codec, head_dim) != KVQ_OK) return -1.0;
+  if (codec->codebook == KVQ_FP16) return 16.0;
+  size_t w, ns, nm;
+  layout_of(*codec, head_dim, &w, &ns, &nm);
+  if (is_rfft(codec->codebook)) {
+    const int F = head_dim / 2 + 1;
+    const double payload = (codec->codebook == KVQ_RFFT_POLAR) ? (double)F * (codec->bits + codec->aux_bits)
+                                                              : 2.0 * F * codec->bits;
+    return (payload + 16.0 * (double)ns) / head_dim;
+  }
+  const double nparams = (codec->codebook == KVQ_INT_MINMAX) ? 2.0 : 1.0;
+  return code_bits(*codec) + 16.0 * nparams / codec->group;
+}
+
+kvq_status kvq_constant_table(int32_t which, int32_t n, float* out) {
+  if (!out || n < 1) return KVQ_ERR_ARG;
+  if (which == 0 || which == 1) {
+    const Tables& t = host_tables();
+    const int len = which == 0 ? 16 : 15;
+    if (n != len) return KVQ_ERR_ARG;
+    std::memcpy(out, which == 0 ? t.nf4_lv : t.nf4_mid, sizeof(float) * len);
+    return KVQ_OK;
+  }
+  if (which == 2 || which == 3) {
+    if (n > 128 || !pow2(n)) return KVQ_ERR_ARG;
+    FftTables t;
+    host_fft_tables(2 * n, &t);
+    std::memcpy(out, which == 2 ? t.tw_c : t.tw_s, sizeof(float) * n);
+    return KVQ_OK;
+  }
+  if (which >= 4 && which <= 7) {
+    const int P = which <= 5 ? n : 8 * n;
+    if (P < 8 || P > 256 || !pow2(P)) return KVQ_ERR_ARG;
+    PhaseTables t;
+    host_phase_tables(P, &t);
+    const float* src = which == 4 ? t.dir_c : which == 5 ? t.dir_s : which == 6 ? t.bnd_c : t.bnd_s;
+    std::memcpy(out, src, sizeof(float) * n);
+    return KVQ_OK;
+  }
+  return KVQ_ERR_ARG;
+}
+
+kvq_status kvq_calibrate_chan_scale(const uint16_t* k_fp16, const kvq_shape* shape, float* chan_scale,
+                                    void* stream) {
+  kvq_status st = check_shape(shape);
+  if (st != KVQ_OK) return st;
+  if (shape->batch != 1) return KVQ_ERR_ARG;
+  if (!k_fp16 || !chan_scale) return KVQ_ERR_ARG;
+  if (!aligned16(k_fp16) || !aligned16(chan_scale)) return KVQ_ERR_ALIGN;
+  return hip_status(launch_calibrate(k_fp16, *shape, chan_scale, (hipStream_t)stream));
+}
+
+kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void* stream) {
+  kvq_status st = check_packed(out, true);
+  if (st != KVQ_OK) return st;
+  if (!x_fp16) return KVQ_ERR_ARG;
+  if (!aligned16(x_fp16)) return KVQ_ERR_ALIGN;
+  if (is_rfft(out->codec.codebook)) return hip_status(launch_rfft_quantize(x_fp16, *out, (hipStream_t)stream));
+  return hip_status(launch_quantize(x_fp16, *out, (hipStream_t)stream));
+}
+
+kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream) {
+  kvq_status st = check_packed(in, false);
+  if (st != KVQ_OK) return st;
+  if (!x_hat) return KVQ_ERR_ARG;
+  if (!aligned16(x_hat)) return KVQ_ERR_ALIGN;
+  if (is_rfft(in->codec.codebook)) return hip_status(launch_rfft_dequant(*in, x_hat, (hipStream_t)stream));
+  return hip_status(launch_dequant(*in, x_hat, (hipStream_t)stream));
+}
+
+static kvq_status check_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
+                             const uint16_t* q) {
+  kvq_status st = check_packed(k, false);
+  if (st != KVQ_OK) return st;
+  st = check_packed(v, false);
+  if (st != KVQ_OK) return st;
+  if (!same_shape(k->shape, v->shape)) return KVQ_ERR_ARG;
+  if (is_rfft(v->codec.codebook)) return KVQ_ERR_UNSUPPORTED;
+  if (q_heads < 1 || q_heads % k->shape.heads != 0 || q_heads / k->shape.heads > 8) return KVQ_ERR_UNSUPPORTED;
+  if (n_q < 1) return KVQ_ERR_ARG;
+  if (!q) return KVQ_ERR_ARG;
+  if (!aligned16(q)) return KVQ_ERR_ALIGN;
+  return KVQ_OK;
+}
+
+size_t kvq_decode_attn_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q) {
+  if (check_shape(kv) != KVQ_OK || q_heads < 1 || n_q < 1) return 0;
+  return decode_ws_bytes(*kv, q_heads, n_q);
+}
+
+kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
+                              const uint16_t* q, const int32_t* kv_len, float sm_scale, float* out, float* lse,
+                              void* ws, size_t ws_bytes, int32_t path, void* stream) {
+  kvq_status st = check_attn(k, v, q_heads, n_q, q);
+  if (st != KVQ_OK) return st;
+  if (!out) return KVQ_ERR_ARG;
+  if (!aligned16(out) || (lse && !aligned16(lse)) || (kv_len && !aligned16(kv_len))) return KVQ_ERR_ALIGN;
+  if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
+  if (path < 0 || path > 2) return KVQ_ERR_ARG;
+  const size_t need = decode_ws_bytes(k->shape, q_heads, n_q);
+  if (ws_bytes < need || (need && !ws)) return KVQ_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return KVQ_ERR_ALIGN;
+  const bool fast_ok = fast_decode_supported(*k, *v, q_heads);
+  if (path == 2 && !fast_ok) return KVQ_ERR_UNSUPPORTED;
+  AttnProblem pr{};
+  pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
+  pr.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)k->shape.head_dim));
+  pr.out = out; pr.lse = lse; pr.ws = ws; pr.ws_bytes = ws_bytes;
+  if (k->shape.tokens == 0) {
+    // no keys: zero output, lse = -inf (handled by the generic kernel's combine)
+  }
+  const bool use_fast = (path == 2) || (path == 0 && fast_ok);
+  return hip_status(use_fast ? launch_decode_fast(pr, (hipStream_t)stream)
+                             : launch_decode_generic(pr, (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
+                           const uint16_t* q, const int32_t* kv_len, float sm_scale, float* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  return kvq_decode_attn_ex(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes, 0, stream);
+}
+
+size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q) {
+  if (check_shape(kv) != KVQ_OK || q_heads < 1 || n_q < 1) return 0;
+  return error_ws_bytes(*kv, q_heads, n_q);
+}
+
+kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16, const kvq_packed* k,
+                          const kvq_packed* v, int32_t q_heads, int32_t n_q, const uint16_t* q,
+                          const int32_t* kv_len, float sm_scale, float* kl_rows, float* relerr_rows,
+                          double* kv_err, void* ws, size_t ws_bytes, void* stream) {
+  kvq_status st = check_attn(k, v, q_heads, n_q, q);
+  if (st != KVQ_OK) return st;
+  if (!k_fp16 || !v_fp16 || !kl_rows || !relerr_rows || !kv_err) return KVQ_ERR_ARG;
+  if (!aligned16(k_fp16) || !aligned16(v_fp16) || !aligned16(kl_rows) || !aligned16(relerr_rows) ||
+      !aligned16(kv_err) || (kv_len && !aligned16(kv_len)))
+    return KVQ_ERR_ALIGN;
+  if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
+  const size_t need = error_ws_bytes(k->shape, q_heads, n_q);
+  if (ws_bytes < need || (need && !ws)) return KVQ_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return KVQ_ERR_ALIGN;
+  AttnProblem pr{};
+  pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
+  pr.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)k->shape.head_dim));
+  pr.k16 = k_fp16; pr.v16 = v_fp16; pr.kl = kl_rows; pr.relerr = relerr_rows; pr.kv_err = kv_err;
+  pr.ws = ws; pr.ws_bytes = ws_bytes;
+  return hip_status(launch_attn_error(pr, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// Internal declarations shared by the libkvq translation units (not part of the ABI).
+//
+// Thread layout used by the row kernels ("layout 1"): a row of D values is
+// owned by LPT = D/16 consecutive lanes of one wavefront, lane j holding the 16
+// consecutive values [16j, 16j+16).  A 256-thread block therefore holds
+// 256/LPT rows at a time.  "Layout 2" (used only inside the Walsh-Hadamard
+// transform) has lane j holding values j + LPT*r, r = 0..15, so the transform
+// stages with strides >= 16 run in registers; the two layouts are exchanged
+// through a padded LDS tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kBlock = 256;      // threads per block for every kernel
+constexpr int kVals = 16;        // values per lane in layout 1
+
+// Constant tables passed by value in kernel arguments (no device globals).
+struct Tables {
+  float nf4_lv[16];
+  float nf4_mid[16];             // 15 midpoints, [15] = +inf
+};
+
+struct FftTables {               // for head_dim N <= 256 and up to 256 phase sectors
+  float tw_c[128], tw_s[128];    // cos(2 pi k/N), -sin(2 pi k/N), k < N/2
+};
+struct PhaseTables {
+  float dir_c[256], dir_s[256];  // cos/sin(2 pi k/P), k < P
+  float bnd_c[32], bnd_s[32];    // first-octant boundaries (2j+1) pi / P, j < P/8
+};
+
+const Tables& host_tables();
+void host_fft_tables(int N, FftTables* t);
+void host_phase_tables(int P, PhaseTables* t);
+
+// ------------------------------------------------------------------ device helpers
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// fp32 -> stored fp16 scale: saturate to +-65504, round to nearest even, -0 -> +0.
+__device__ __forceinline__ uint16_t rn16(float x) {
+  x = __builtin_fminf(__builtin_fmaxf(x, -65504.0f), 65504.0f);
+  uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)x);
+  return (b & 0x7fffu) ? b : (uint16_t)0;
+}
+
+// Correctly rounded reciprocal of a stored scale; zero scale -> zero.
+__device__ __forceinline__ float inv_scale(uint16_t sb) {
+  float s = h2f(sb);
+  return s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+}
+
+__device__ __forceinline__ float xor_max(float v, int m) { return __builtin_fmaxf(v, __shfl_xor(v, m)); }
+__device__ __forceinline__ float xor_min(float v, int m) { return __builtin_fminf(v, __shfl_xor(v, m)); }
+__device__ __forceinline__ float xor_add(float v, int m) { return v + __shfl_xor(v, m); }
+
+// Padded LDS index of value i of a row (one pad float per 16 values).
+__device__ __forceinline__ int pidx(int i) { return i + (i >> 4); }
+
+// Pack 16 codes of BITS bits into a little-endian bit string (2*BITS bytes).
+template <int BITS>
+__device__ __forceinline__ void pack16(const uint32_t c[16], uint32_t w[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int pos = i * BITS;
+    const int wi = pos >> 5, sh = pos & 31;
+    w[wi] |= c[i] << sh;
+    if (sh + BITS > 32) w[wi + 1] |= c[i] >> (32 - sh);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void unpack16(const uint32_t w[8], uint32_t c[16]) {
+  constexpr uint32_t mask = (BITS >= 32) ? 0xffffffffu : ((1u << BITS) - 1u);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int pos = i * BITS;
+    const int wi = pos >> 5, sh = pos & 31;
+    uint32_t v = w[wi] >> sh;
+    if (sh + BITS > 32) v |= w[wi + 1] << (32 - sh);
+    c[i] = v & mask;
+  }
+}
+
+// Store / load a lane's 2*BITS-byte chunk at byte offset `off` of `base`.
+// Offsets are multiples of 2*BITS bytes, so even BITS give 4-byte alignment.
+template <int BITS>
+__device__ __forceinline__ void store_chunk(uint8_t* base, size_t off, const uint32_t w[8]) {
+  if constexpr (BITS == 8) {
+    *reinterpret_cast<uint4*>(base + off) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (BITS == 16) {
+    *reinterpret_cast<uint4*>(base + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(base + off + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  } else if constexpr (BITS == 4) {
+    *reinterpret_cast<uint2*>(base + off) = make_uint2(w[0], w[1]);
+  } else if constexpr ((BITS & 1) == 0) {
+#pragma unroll
+    for (int k = 0; k < BITS / 2; ++k) reinterpret_cast<uint32_t*>(base + off)[k] = w[k];
+  } else {
+    uint16_t* p = reinterpret_cast<uint16_t*>(base + off);
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) p[k] = (uint16_t)(w[k >> 1] >> ((k & 1) * 16));
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_chunk(const uint8_t* base, size_t off, uint32_t w[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = 0u;
+  if constexpr (BITS == 8) {
+    uint4 t = *reinterpret_cast<const uint4*>(base + off);
+    w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+  } else if constexpr (BITS == 16) {
+    uint4 t = *reinterpret_cast<const uint4*>(base + off);
+    uint4 u = *reinterpret_cast<const uint4*>(base + off + 16);
+    w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+    w[4] = u.x; w[5] = u.y; w[6] = u.z; w[7] = u.w;
+  } else if constexpr (BITS == 4) {
+    uint2 t = *reinterpret_cast<const uint2*>(base + off);
+    w[0] = t.x; w[1] = t.y;
+  } else if constexpr ((BITS & 1) == 0) {
+#pragma unroll
+    for (int k = 0; k < BITS / 2; ++k) w[k] = reinterpret_cast<const uint32_t*>(base + off)[k];
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base + off);
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) w[k >> 1] |= (uint32_t)p[k] << ((k & 1) * 16);
+  }
+}
+
+#endif  // device helpers
+
+// ------------------------------------------------------------------ launchers
+struct RowGeom {        // a [B][L][H][T][D] tensor seen as rows
+  long long rows;
+  int D, T, H, L;
+};
+
+hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st);
+hipError_t launch_dequant(const kvq_packed& p, float* xhat, hipStream_t st);
+hipError_t launch_calibrate(const uint16_t* k, const kvq_shape& s, float* c, hipStream_t st);
+hipError_t launch_rfft_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st);
+hipError_t launch_rfft_dequant(const kvq_packed& p, float* xhat, hipStream_t st);
+
+struct AttnProblem {
+  const kvq_packed* k;
+  const kvq_packed* v;
+  int Hq, n_q;
+  const uint16_t* q;
+  const int32_t* kv_len;
+  float sm_scale;
+  // decode outputs
+  float* out;
+  float* lse;
+  // error outputs (attn_error only)
+  const uint16_t* k16;
+  const uint16_t* v16;
+  float* kl;
+  float* relerr;
+  double* kv_err;
+  void* ws;
+  size_t ws_bytes;
+};
+
+size_t decode_ws_bytes(const kvq_shape& s, int Hq, int n_q);
+size_t error_ws_bytes(const kvq_shape& s, int Hq, int n_q);
+int decode_splits(const kvq_shape& s, int Hq, int n_q);
+hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st);
+hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st);
+bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
+hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st);
+
+}  // namespace kvq

@@ -1,0 +1,136 @@
+"""GPU parity of kvq_quantize_pack / kvq_dequant / kvq_calibrate_chan_scale
+against the CPU oracle: codes, scales and mins bit-exact; dequantised values
+equal to the oracle's (same binary32 operation order)."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_util import announce, oracle_codec, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, L, H, T, D, seed, specials=True):
+    rng = np.random.default_rng([7, seed, D, T])
+    x = rng.standard_normal((B, L, H, T, D), dtype=np.float32)
+    ch = rng.choice(D, size=max(1, D // 32), replace=False)
+    x[..., ch] *= 10.0
+    if specials and T >= 6:
+        x[0, 0, 0, 0] = 0.0                                 # zero row
+        x[0, 0, 0, 1, : D // 2] = -0.0                      # -0 half row
+        x[0, 0, 0, 2] *= 1e-6                               # fp16 subnormals
+        x[0, 0, 0, 3] = np.sign(x[0, 0, 0, 3]) * 60000.0    # saturation after rotation
+        x[0, 0, 0, 4, ::2] = 3.0
+        x[0, 0, 0, 4, 1::2] = -3.0                          # +-A ties
+        x[0, 0, 0, 5] = 1.0                                 # constant row
+    return x.astype(np.float16)
+
+
+def _run(K, x, codec, chan=None):
+    B, L, H, T, D = x.shape
+    shape = K.Shape(B, L, H, T, D)
+    chan_d = to_dev(chan) if chan is not None else None
+    p = K.alloc_packed(codec, shape, chan_scale=chan_d)
+    K.kvq_quantize_pack(to_dev(x), p)
+    import torch
+    xh = torch.empty((B, L, H, T, D), dtype=torch.float32, device="cuda:0")
+    K.kvq_dequant(p, xh)
+    torch.cuda.synchronize()
+    return p, to_np(xh)
+
+
+def _compare(K, x, codec, chan=None):
+    oc = oracle_codec(K, O, codec)
+    p, xh = _run(K, x, codec, chan)
+    w, s, z = O.quantize_pack(x, oc, chan)
+    codes = to_np(p.codes, np.uint32)
+    assert codes.shape == w.shape
+    bad = np.nonzero((codes != w).any(1))[0]
+    assert bad.size == 0, f"{bad.size} rows with code mismatches, first row {bad[:3]}"
+    if s.shape[1]:
+        assert np.array_equal(to_np(p.scales, np.uint16), s.view(np.uint16)), "scales differ"
+    if z.shape[1]:
+        assert np.array_equal(to_np(p.mins, np.uint16), z.view(np.uint16)), "mins differ"
+    ref = O.dequant(w, s, z, oc, x.shape, chan)
+    assert np.array_equal(xh, ref), f"dequant max abs diff {np.abs(xh - ref).max()}"
+
+
+CASES = []
+for D in (64, 128, 256):
+    for b in (2, 3, 4, 5, 6, 7, 8):
+        for g in (8, 32, 128):
+            if g <= D:
+                CASES.append((D, (1, b, g, 0)))
+        CASES.append((D, (1, b, 32, D)))
+    CASES += [(D, (2, 4, 32, 0)), (D, (2, 3, 8, 0)), (D, (2, 2, 64, D)), (D, (3, 2, 8, 0)), (D, (4, 1, 8, 0)),
+              (D, (4, 1, 32, 0)), (D, (5, 4, 64, 0)), (D, (6, 8, D, 0)), (D, (0, 16, 0, 0)), (D, (1, 4, 16, 0)),
+              (D, (1, 4, 64, D // 2)), (D, (1, 6, 32, 16)), (D, (1, 4, 8, 8)), (D, (3, 2, 8, D))]
+CASES.append((256, (1, 4, 256, 256)))
+
+
+@pytest.mark.parametrize("D,cspec", CASES)
+def test_quantize_pack_bit_exact(D, cspec):
+    import kv_cache_bit_fwht_amd as K
+    cb, b, g, rot = cspec
+    codec = K.Codec(cb, b, g, rot)
+    x = _inputs(1, 2, 3, 37, D, seed=cb * 100 + b * 10 + g + rot)
+    announce(f"quantize D={D} codec={codec}")
+    _compare(K, x, codec)
+
+
+@pytest.mark.parametrize("arm", ["C", "D"])
+def test_prescaled_keys_bit_exact(arm):
+    """E21W arms C/D: per-channel K scaling calibrated on sequence 0."""
+    import kv_cache_bit_fwht_amd as K
+    import torch
+    w = synth.get("c2", B=2, L=2, H=2, Hq=2, T=300, pos_range=(100, 300), n_q=4)
+    Kx, _ = synth.gen_kv(w)
+    announce(f"calibrate + quantize arm {arm}")
+    cal = torch.empty((w.L, w.H, w.D), dtype=torch.float32, device="cuda:0")
+    K.kvq_calibrate_chan_scale(to_dev(np.ascontiguousarray(Kx[:1])), K.Shape(1, w.L, w.H, w.T, w.D), cal)
+    torch.cuda.synchronize()
+    c_ref = O.calibrate_chan_scale(Kx[0])
+    assert np.array_equal(to_np(cal), c_ref)
+    codec = K.Codec(K.INT_MINMAX, 3, 32, 0) if arm == "C" else K.Codec(K.INT_ABSMAX, 3, 32, 256)
+    _compare(K, Kx, codec, c_ref)
+
+
+def test_full_size_64k_sampled_rows():
+    """The 64K decode workload at full size (8 x 4 x 65536 x 256) in the launch
+    configuration the benchmark times; the oracle checks sampled units."""
+    import kv_cache_bit_fwht_amd as K
+    import torch
+    w = synth.get("c3")
+    announce("full-size 64K quantize")
+    Kx, Vx = synth.gen_kv(w)
+    shape = K.Shape(w.B, w.L, w.H, w.T, w.D)
+    kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    kp, vp = K.alloc_packed(kc, shape), K.alloc_packed(vc, shape)
+    K.kvq_quantize_pack(to_dev(Kx), kp)
+    K.kvq_quantize_pack(to_dev(Vx), vp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    for (l, h) in [(0, 0), (7, 3), (int(rng.integers(8)), int(rng.integers(4)))]:
+        rows = slice(((0 * w.L + l) * w.H + h) * w.T, ((0 * w.L + l) * w.H + h + 1) * w.T)
+        for x, p, c in ((Kx, kp, kc), (Vx, vp, vc)):
+            unit = x[0, l, h][None, None, None]
+            wo, so, _ = O.quantize_pack(unit, oracle_codec(K, O, c))
+            assert np.array_equal(to_np(p.codes[rows], np.uint32), wo), f"unit {(l, h)} codes"
+            assert np.array_equal(to_np(p.scales[rows], np.uint16), so.view(np.uint16)), f"unit {(l, h)} scales"
+
+
+def test_invalid_arguments_write_nothing():
+    import kv_cache_bit_fwht_amd as K
+    import torch
+    shape = K.Shape(1, 1, 1, 16, 128)
+    p = K.alloc_packed(K.Codec(K.INT_ABSMAX, 4, 32, 0), shape)
+    p.codes.fill_(-1)
+    x = to_dev(np.zeros((1, 1, 1, 16, 128), np.float16))
+    bad = K.Packed(K.Codec(K.INT_ABSMAX, 4, 48, 0), shape, p.codes, p.scales, None)
+    with pytest.raises(K.KvqError):
+        K.kvq_quantize_pack(x, bad)
+    with pytest.raises(K.KvqError):
+        K.kvq_quantize_pack(x[..., 1:].contiguous().view(-1)[1:], p)   # misaligned input
+    torch.cuda.synchronize()
+    assert bool((p.codes == -1).all())
