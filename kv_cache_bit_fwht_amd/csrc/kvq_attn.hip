@@ -1,12 +1,739 @@
-// placeholder: attention kernels (replaced below)
-#include "kvq_internal.hpp"
+// Decode attention read back through the packed cache, and the attention-error
+// reduction ([E22L] "Can 4-bit keys and 2-bit values hit a 1M-token memory
+// budget?", What I tested: attention through the quantised post-RoPE cache;
+// [E21W] "PROVISIONAL: known 3-bit KV cache methods ...", Benchmark: attention
+// output relative error, KL of the attention distribution from f16, K/V squared
+// error over signal energy).
+//
+// General kernel (every codec): split-K over tokens ("flash decoding").  Block
+// (split s, KV head h, query row r) streams TB-token tiles: the K and V rows
+// are dequantised by the same per-lane decode as kvq_dequant into padded LDS
+// tiles, in the codec's own coordinates (rotated keys are met by a rotated
+// query, rotated values are rotated back once per query in the combine; rFFT
+// keys by the query's spectrum), then logits, online softmax and P.V for the
+// G = Hq/H query heads that share the KV head.  Each block writes (m, l, o)
+// partials; the combine kernel merges them with log-sum-exp weights.
+#include <cmath>
+#include <type_traits>
+
+#include "kvq_codec.hpp"
+#include "kvq_rfft.hpp"
+
 namespace kvq {
-size_t decode_ws_bytes(const kvq_shape&, int, int) { return 0; }
-size_t error_ws_bytes(const kvq_shape&, int, int) { return 0; }
-hipError_t launch_decode_generic(const AttnProblem&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_attn_error(const AttnProblem&, hipStream_t) { return hipErrorNotSupported; }
-bool fast_decode_supported(const kvq_packed&, const kvq_packed&, int) { return false; }
-hipError_t launch_decode_fast(const AttnProblem&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_rfft_quantize(const uint16_t*, const kvq_packed&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_rfft_dequant(const kvq_packed&, float*, hipStream_t) { return hipErrorNotSupported; }
+
+constexpr int TB = 16;          // tokens per tile
+constexpr int kMaxG = 8;
+
+struct DevCodec {
+  int cb, bits, g, W, ng;
+  float kappa;
+  size_t row_bytes;
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* mins;
+  const float* chan;
+  RfftCodec rc;
+};
+
+struct DirTables {
+  float dir_c[256], dir_s[256];
+};
+
+struct AArgs {
+  DevCodec k, v;
+  const uint16_t* q;
+  const int32_t* kv_len;
+  const uint16_t* k16;
+  const uint16_t* v16;
+  float sm_scale;
+  int B, L, H, T, D, Hq, G, n_q, S, chunk;
+  int lpt_log2;
+  int Dc;              // coded key length (D, or 2*(D/2+1) for rFFT keys)
+  float* ws;           // split partials
+  Tables tab;
+  FftTables tw;        // twiddles of head_dim (rFFT keys: the query's DFT)
+  DirTables dirs;      // phase-sector directions (rFFT polar keys)
+};
+
+// ------------------------------------------------------------------ tile dequantisation
+
+template <int CB, int BITS>
+__device__ __forceinline__ void dq_row(const DevCodec& c, long long row, int j, const Tables& tab, float v[16]) {
+  uint32_t w[8], cc[16];
+  uint16_t s16[2] = {0, 0}, z16[2] = {0, 0};
+  load_chunk<BITS>(c.codes, (size_t)row * c.row_bytes + (size_t)j * 2 * BITS, w);
+  if constexpr (CB != KVQ_FP16) {
+    const size_t sbase = (size_t)row * c.ng;
+    if (c.g == 8) {
+      s16[0] = c.scales[sbase + 2 * j];
+      s16[1] = c.scales[sbase + 2 * j + 1];
+      if constexpr (CB == KVQ_INT_MINMAX) { z16[0] = c.mins[sbase + 2 * j]; z16[1] = c.mins[sbase + 2 * j + 1]; }
+    } else {
+      const int gi = (16 * j) / c.g;
+      s16[0] = s16[1] = c.scales[sbase + gi];
+      if constexpr (CB == KVQ_INT_MINMAX) z16[0] = z16[1] = c.mins[sbase + gi];
+    }
+  }
+  unpack16<BITS>(w, cc);
+  decode16<CB, BITS>(cc, s16, z16, tab, v);
 }
+
+__device__ __noinline__ void dq_row_any(const DevCodec& c, long long row, int j, const Tables& tab, float v[16]) {
+  switch (c.cb) {
+    case KVQ_FP16: dq_row<KVQ_FP16, 16>(c, row, j, tab, v); return;
+    case KVQ_TERNARY: dq_row<KVQ_TERNARY, 2>(c, row, j, tab, v); return;
+    case KVQ_SIGN: dq_row<KVQ_SIGN, 1>(c, row, j, tab, v); return;
+    case KVQ_NF4: dq_row<KVQ_NF4, 4>(c, row, j, tab, v); return;
+    case KVQ_INT8_SYM: dq_row<KVQ_INT8_SYM, 8>(c, row, j, tab, v); return;
+    case KVQ_INT_ABSMAX:
+      switch (c.bits) {
+        case 2: dq_row<KVQ_INT_ABSMAX, 2>(c, row, j, tab, v); return;
+        case 3: dq_row<KVQ_INT_ABSMAX, 3>(c, row, j, tab, v); return;
+        case 4: dq_row<KVQ_INT_ABSMAX, 4>(c, row, j, tab, v); return;
+        case 5: dq_row<KVQ_INT_ABSMAX, 5>(c, row, j, tab, v); return;
+        case 6: dq_row<KVQ_INT_ABSMAX, 6>(c, row, j, tab, v); return;
+        case 7: dq_row<KVQ_INT_ABSMAX, 7>(c, row, j, tab, v); return;
+        default: dq_row<KVQ_INT_ABSMAX, 8>(c, row, j, tab, v); return;
+      }
+    default:
+      switch (c.bits) {
+        case 2: dq_row<KVQ_INT_MINMAX, 2>(c, row, j, tab, v); return;
+        case 3: dq_row<KVQ_INT_MINMAX, 3>(c, row, j, tab, v); return;
+        case 4: dq_row<KVQ_INT_MINMAX, 4>(c, row, j, tab, v); return;
+        case 5: dq_row<KVQ_INT_MINMAX, 5>(c, row, j, tab, v); return;
+        case 6: dq_row<KVQ_INT_MINMAX, 6>(c, row, j, tab, v); return;
+        case 7: dq_row<KVQ_INT_MINMAX, 7>(c, row, j, tab, v); return;
+        default: dq_row<KVQ_INT_MINMAX, 8>(c, row, j, tab, v); return;
+      }
+  }
+}
+
+// Rows [t0, t0+TB) of one unit (first row urow0) into tile[TB][RS] at pidx
+// positions, in coded coordinates; rows at or beyond tend are zero.
+__device__ void tile_dequant(const AArgs& a, const DevCodec& c, long long urow0, int t0, int tend, float* tile,
+                             int RS) {
+  const int tid = threadIdx.x;
+  if (c.cb == KVQ_RFFT_POLAR || c.cb == KVQ_RFFT_CART) {
+    const int F = c.rc.F;
+    for (int it = tid; it < TB * F; it += kBlock) {
+      const int r = it / F, f = it - r * F, t = t0 + r;
+      float zr = 0.0f, zi = 0.0f;
+      if (t < tend) {
+        const long long row = urow0 + t;
+        rfft_bin_value(c.rc, reinterpret_cast<const uint32_t*>(c.codes) + (size_t)row * c.rc.words,
+                       c.scales + (size_t)row * c.rc.nscales, f, a.dirs.dir_c, a.dirs.dir_s, zr, zi);
+      }
+      tile[r * RS + pidx(f)] = zr;
+      tile[r * RS + pidx(F + f)] = zi;
+    }
+    return;
+  }
+  const int LPT = 1 << a.lpt_log2, j = tid & (LPT - 1), rloc = tid >> a.lpt_log2, RPB = kBlock >> a.lpt_log2;
+  for (int r0 = 0; r0 < TB; r0 += RPB) {
+    const int r = r0 + rloc;
+    if (r < TB) {
+      const int t = t0 + r;
+      float v[16];
+      if (t < tend) {
+        dq_row_any(c, urow0 + t, j, a.tab, v);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) tile[r * RS + pidx(16 * j + k)] = v[k];
+    }
+  }
+}
+
+// fp16 rows [t0, t0+TB) of one unit into tile (original coordinates).
+__device__ void tile_fp16(const AArgs& a, const uint16_t* x, long long urow0, int t0, int tend, float* tile,
+                          int RS) {
+  for (int it = threadIdx.x; it < TB * a.D; it += kBlock) {
+    const int r = it / a.D, d = it - r * a.D, t = t0 + r;
+    tile[r * RS + pidx(d)] = (t < tend) ? h2f(x[(size_t)(urow0 + t) * a.D + d]) : 0.0f;
+  }
+}
+
+// Normalised Walsh-Hadamard transform (width W) of `rows` LDS rows of D values
+// (pidx layout, row stride RS); all threads call it.
+__device__ void fwht_lds_rows(float* base, int rows, int RS, int D, int W, float kappa) {
+  for (int s = 1; s < W; s <<= 1) {
+    for (int p = threadIdx.x; p < rows * (D / 2); p += kBlock) {
+      const int r = p / (D / 2), pp = p - r * (D / 2);
+      const int i = (pp / s) * 2 * s + (pp % s);
+      float* row = base + r * RS;
+      const float x = row[pidx(i)], y = row[pidx(i + s)];
+      row[pidx(i)] = x + y;
+      row[pidx(i + s)] = x - y;
+    }
+    __syncthreads();
+  }
+  for (int p = threadIdx.x; p < rows * D; p += kBlock) {
+    const int r = p / D, d = p - r * D;
+    base[r * RS + pidx(d)] *= kappa;
+  }
+  __syncthreads();
+}
+
+// Query prologue: qc[g] = the query in the key codec's coordinates times the
+// logit scale; optionally qr[g] = sigma * q in original coordinates.
+__device__ void query_prologue(const AArgs& a, int b, int l, int i, int h, float* qc, float* qr, int RS) {
+  const int D = a.D, G = a.G;
+  const uint16_t* qsrc = a.q + ((((size_t)b * a.L + l) * a.n_q + i) * a.Hq + (size_t)h * G) * D;
+  const float* kch = a.k.chan ? a.k.chan + ((size_t)l * a.H + h) * D : nullptr;
+  for (int p = threadIdx.x; p < G * D; p += kBlock) {
+    const int g = p / D, d = p - g * D;
+    const float x = h2f(qsrc[(size_t)g * D + d]);
+    if (qr) qr[g * RS + pidx(d)] = x * a.sm_scale;
+    qc[g * RS + pidx(d)] = kch ? x / kch[d] : x;
+  }
+  __syncthreads();
+  if (a.k.cb == KVQ_RFFT_POLAR || a.k.cb == KVQ_RFFT_CART) {
+    // logit = sigma * sum_f w_f (Re Z_f Re Q_f + Im Z_f Im Q_f), Q = DFT(q), w = 1/N at f = 0, N/2 else 2/N
+    const int N = D, F = N / 2 + 1;
+    float* tmp = qc + G * RS;   // scratch row block (caller provides 2*G rows)
+    for (int p = threadIdx.x; p < G * F; p += kBlock) {
+      const int g = p / F, f = p - g * F;
+      float sr = 0.0f, si = 0.0f;
+      for (int n = 0; n < N; ++n) {
+        const int m = (f * n) & (N - 1);
+        const float cs = (m < N / 2) ? a.tw.tw_c[m] : -a.tw.tw_c[m - N / 2];
+        const float sn = (m < N / 2) ? -a.tw.tw_s[m] : a.tw.tw_s[m - N / 2];   // sin(2 pi m / N)
+        const float x = qc[g * RS + pidx(n)];
+        sr += x * cs;
+        si -= x * sn;
+      }
+      const float wf = ((f == 0 || f == N / 2) ? 1.0f : 2.0f) / (float)N * a.sm_scale;
+      tmp[g * RS + pidx(f)] = sr * wf;
+      tmp[g * RS + pidx(F + f)] = si * wf;
+    }
+    __syncthreads();
+    for (int p = threadIdx.x; p < G * 2 * F; p += kBlock) {
+      const int g = p / (2 * F), e = p - g * 2 * F;
+      qc[g * RS + pidx(e)] = tmp[g * RS + pidx(e)];
+    }
+    __syncthreads();
+    return;
+  }
+  if (a.k.W > 1) fwht_lds_rows(qc, G, RS, D, a.k.W, a.k.kappa);
+  for (int p = threadIdx.x; p < G * D; p += kBlock) {
+    const int g = p / D, d = p - g * D;
+    qc[g * RS + pidx(d)] *= a.sm_scale;
+  }
+  __syncthreads();
+}
+
+template <typename T>
+__device__ __forceinline__ T grp_max16(T v) {
+#pragma unroll
+  for (int m = 1; m < TB; m <<= 1) { const T o = __shfl_xor(v, m); v = v > o ? v : o; }
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T grp_sum16(T v) {
+#pragma unroll
+  for (int m = 1; m < TB; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ float exp_t(float x) { return expf(x); }
+__device__ __forceinline__ double exp_t(double x) { return exp(x); }
+
+// ------------------------------------------------------------------ split kernel
+//
+// ERR = false: decode.  ERR = true: attention-error pass over fp16 and packed
+// K/V together; its logits and softmax statistics are accumulated in fp64 (the
+// error of a KL that is a small difference of large log-partition terms).
+
+template <bool ERR>
+__global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
+  using acc_t = typename std::conditional<ERR, double, float>::type;
+  extern __shared__ float smem[];
+  const int RS = 17 * (a.D / 16) + 17;           // row stride of LDS rows (odd)
+  float* qc = smem;                              // [2*G][RS] (second half: rFFT scratch)
+  float* qr = qc + 2 * kMaxG * RS;               // [G][RS] (ERR)
+  float* kt = qr + (ERR ? kMaxG * RS : 0);       // [TB][RS]
+  float* vt = kt + TB * RS;                      // [TB][RS]
+  float* kt2 = vt + TB * RS;                     // [TB][RS] fp16 K (ERR)
+  float* vt2 = kt2 + (ERR ? TB * RS : 0);        // [TB][RS] fp16 V (ERR)
+  float* pb = vt2 + (ERR ? TB * RS : 0);         // [G][TB] weights (quant)
+  float* pb2 = pb + kMaxG * TB;                  // [G][TB] weights (fp16)
+  acc_t* sc = reinterpret_cast<acc_t*>(pb2 + kMaxG * TB);   // [G][TB] logits (quant)
+  acc_t* sc2 = sc + kMaxG * TB;                  // [G][TB] logits (fp16)
+  acc_t* st = sc2 + kMaxG * TB;                  // stats [8][kMaxG]
+
+  const int s = blockIdx.x, h = blockIdx.y;
+  const long long rq = blockIdx.z;                // (b*L + l)*n_q + i
+  const int i = (int)(rq % a.n_q);
+  const int l = (int)((rq / a.n_q) % a.L);
+  const int b = (int)(rq / ((long long)a.n_q * a.L));
+  const int G = a.G, D = a.D, tid = threadIdx.x;
+  const long long urow0 = (((long long)b * a.L + l) * a.H + h) * a.T;
+  int n = a.T;
+  if (a.kv_len) n = min(max(a.kv_len[rq], 0), a.T);
+  const int tb0 = s * a.chunk, tb1 = min(tb0 + a.chunk, n);
+  const acc_t NEG_INF = -(acc_t)INFINITY;
+
+  query_prologue(a, b, l, i, h, qc, ERR ? qr : nullptr, RS);
+  // stats: 0 m, 1 l, 2 alpha, 3 A, 4 m2, 5 l2, 6 alpha2
+  if (tid < kMaxG) {
+    st[0 * kMaxG + tid] = NEG_INF; st[1 * kMaxG + tid] = 0; st[2 * kMaxG + tid] = 1;
+    st[3 * kMaxG + tid] = 0; st[4 * kMaxG + tid] = NEG_INF; st[5 * kMaxG + tid] = 0;
+    st[6 * kMaxG + tid] = 1;
+  }
+  float acc[kMaxG], acc2[kMaxG];
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) { acc[g] = 0.0f; acc2[g] = 0.0f; }
+  __syncthreads();
+
+  for (int t0 = tb0; t0 < tb1; t0 += TB) {
+    tile_dequant(a, a.k, urow0, t0, tb1, kt, RS);
+    tile_dequant(a, a.v, urow0, t0, tb1, vt, RS);
+    if (ERR) {
+      tile_fp16(a, a.k16, urow0, t0, tb1, kt2, RS);
+      tile_fp16(a, a.v16, urow0, t0, tb1, vt2, RS);
+    }
+    __syncthreads();
+    if (tid < TB * G) {
+      const int t = tid % TB, g = tid / TB;
+      const bool valid = t0 + t < tb1;
+      acc_t sq = 0;
+      for (int e = 0; e < a.Dc; ++e) sq += (acc_t)qc[g * RS + pidx(e)] * (acc_t)kt[t * RS + pidx(e)];
+      sc[g * TB + t] = valid ? sq : NEG_INF;
+      if (ERR) {
+        acc_t sr = 0;
+        for (int d = 0; d < D; ++d) sr += (acc_t)qr[g * RS + pidx(d)] * (acc_t)kt2[t * RS + pidx(d)];
+        sc2[g * TB + t] = valid ? sr : NEG_INF;
+      }
+    }
+    __syncthreads();
+    if (tid < TB * G) {
+      const int t = tid % TB, g = tid / TB;
+      {  // packed cache: online softmax
+        const acc_t x = sc[g * TB + t];
+        const acc_t mo = st[0 * kMaxG + g];
+        const acc_t mt = grp_max16(x);
+        const acc_t M = mo > mt ? mo : mt;
+        const acc_t p = (x == NEG_INF) ? (acc_t)0 : exp_t(x - M);
+        const acc_t ps = grp_sum16(p);
+        pb[g * TB + t] = (float)p;
+        if (t == 0) {
+          const acc_t al = (M == NEG_INF) ? (acc_t)1 : exp_t(mo - M);
+          st[2 * kMaxG + g] = al;
+          st[1 * kMaxG + g] = st[1 * kMaxG + g] * al + ps;
+          st[0 * kMaxG + g] = M;
+        }
+      }
+      if (ERR) {  // fp16 cache, and A = sum_t e^{l_t - m} (l_t - lhat_t)
+        const acc_t x = sc2[g * TB + t], xq = sc[g * TB + t];
+        const acc_t mo = st[4 * kMaxG + g];
+        const acc_t mt = grp_max16(x);
+        const acc_t M = mo > mt ? mo : mt;
+        const acc_t p = (x == NEG_INF) ? (acc_t)0 : exp_t(x - M);
+        const acc_t ps = grp_sum16(p);
+        const acc_t pa = grp_sum16((x == NEG_INF) ? (acc_t)0 : p * (x - xq));
+        pb2[g * TB + t] = (float)p;
+        if (t == 0) {
+          const acc_t al = (M == NEG_INF) ? (acc_t)1 : exp_t(mo - M);
+          st[6 * kMaxG + g] = al;
+          st[5 * kMaxG + g] = st[5 * kMaxG + g] * al + ps;
+          st[3 * kMaxG + g] = st[3 * kMaxG + g] * al + pa;
+          st[4 * kMaxG + g] = M;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < D) {
+#pragma unroll
+      for (int g = 0; g < kMaxG; ++g) {
+        if (g >= G) break;
+        float o = acc[g] * (float)st[2 * kMaxG + g];
+#pragma unroll
+        for (int t = 0; t < TB; ++t) o += pb[g * TB + t] * vt[t * RS + pidx(tid)];
+        acc[g] = o;
+        if (ERR) {
+          float o2 = acc2[g] * (float)st[6 * kMaxG + g];
+#pragma unroll
+          for (int t = 0; t < TB; ++t) o2 += pb2[g * TB + t] * vt2[t * RS + pidx(tid)];
+          acc2[g] = o2;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // partials: decode [rq][Hq][S][D+2 floats] = (o[D], m, l); error
+  // [rq][Hq][S][2D floats + 5 doubles] = (o_quant[D], o_fp16[D]; m, l, m2, l2, A)
+  const int P = ERR ? 2 * D + 10 : D + 2;
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) {
+    if (g >= G) break;
+    float* dst = a.ws + ((rq * a.Hq + (size_t)h * G + g) * a.S + s) * P;
+    if (tid < D) {
+      dst[tid] = acc[g];
+      if (ERR) dst[D + tid] = acc2[g];
+    }
+    if (tid == 0) {
+      if (ERR) {
+        double* dd = reinterpret_cast<double*>(dst + 2 * D);
+        dd[0] = (double)st[0 * kMaxG + g];
+        dd[1] = (double)st[1 * kMaxG + g];
+        dd[2] = (double)st[4 * kMaxG + g];
+        dd[3] = (double)st[5 * kMaxG + g];
+        dd[4] = (double)st[3 * kMaxG + g];
+      } else {
+        dst[D] = (float)st[0 * kMaxG + g];
+        dst[D + 1] = (float)st[1 * kMaxG + g];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ combine
+
+// One block per (query row, query head).  Merges the S split partials:
+// M = max m_s, L = sum l_s e^{m_s - M}, o = sum o_s e^{m_s - M} / L; then
+// rotates o back if V was rotated and divides V's per-channel scale.
+template <bool ERR>
+__global__ __launch_bounds__(kBlock) void k_attn_combine(AArgs a, float* out, float* lse, float* kl,
+                                                         float* relerr) {
+  __shared__ float orow[2][17 * 16 + 17];
+  __shared__ float red[kBlock];
+  const long long rh = blockIdx.x;               // rq * Hq + j
+  const int j = (int)(rh % a.Hq);
+  const long long rq = rh / a.Hq;
+  const int l = (int)((rq / a.n_q) % a.L);
+  const int h = j / a.G;
+  const int D = a.D, tid = threadIdx.x;
+  const int P = ERR ? 2 * D + 10 : D + 2;
+  const float* src = a.ws + (size_t)rh * a.S * P;
+  // per split: m, l (packed cache) and m2, l2, A (fp16 cache)
+  auto stat = [&](int s, int k) -> double {
+    const float* p = src + (size_t)s * P;
+    if (ERR) return reinterpret_cast<const double*>(p + 2 * D)[k];
+    return (double)p[D + k];
+  };
+  double M = -INFINITY, M2 = -INFINITY;
+  for (int s = 0; s < a.S; ++s) {
+    M = fmax(M, stat(s, 0));
+    if (ERR) M2 = fmax(M2, stat(s, 2));
+  }
+  double Lq = 0.0, L2 = 0.0, A = 0.0;
+  for (int s = 0; s < a.S; ++s) {
+    if (M != -INFINITY && stat(s, 0) != -INFINITY) Lq += stat(s, 1) * exp(stat(s, 0) - M);
+    if (ERR && M2 != -INFINITY && stat(s, 2) != -INFINITY) {
+      const double w = exp(stat(s, 2) - M2);
+      L2 += stat(s, 3) * w;
+      A += stat(s, 4) * w;
+    }
+  }
+  float o = 0.0f, o2 = 0.0f;
+  if (tid < D) {
+    double acc = 0.0, acc2 = 0.0;
+    for (int s = 0; s < a.S; ++s) {
+      const float* p = src + (size_t)s * P;
+      if (M != -INFINITY && stat(s, 0) != -INFINITY) acc += (double)p[tid] * exp(stat(s, 0) - M);
+      if (ERR && M2 != -INFINITY && stat(s, 2) != -INFINITY) acc2 += (double)p[D + tid] * exp(stat(s, 2) - M2);
+    }
+    o = Lq > 0.0 ? (float)(acc / Lq) : 0.0f;
+    if (ERR) o2 = L2 > 0.0 ? (float)(acc2 / L2) : 0.0f;
+    orow[0][pidx(tid)] = o;
+  }
+  __syncthreads();
+  if (a.v.W > 1) {
+    fwht_lds_rows(orow[0], 1, 0, D, a.v.W, a.v.kappa);
+  }
+  if (tid < D) {
+    o = orow[0][pidx(tid)];
+    if (a.v.chan) o = o / a.v.chan[((size_t)l * a.H + h) * D + tid];
+  }
+  if (!ERR) {
+    if (tid < D) out[(size_t)rh * D + tid] = o;
+    if (tid == 0 && lse) lse[rh] = (Lq > 0.0) ? (float)(M + log(Lq)) : -INFINITY;
+    return;
+  }
+  // relative error of the quantised output against the fp16 one, and KL
+  const float dlt = (tid < D) ? (o - o2) : 0.0f;
+  red[tid] = dlt * dlt;
+  __syncthreads();
+  for (int st = kBlock / 2; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  const float num = red[0];
+  __syncthreads();
+  red[tid] = (tid < D) ? o2 * o2 : 0.0f;
+  __syncthreads();
+  for (int st = kBlock / 2; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float den = red[0];
+    relerr[rh] = den > 0.0f ? sqrtf(num) / sqrtf(den) : 0.0f;
+    double k = 0.0;
+    if (L2 > 0.0 && Lq > 0.0) k = A / L2 - (M2 + log(L2)) + (M + log(Lq));
+    kl[rh] = (float)k;
+  }
+}
+
+// ------------------------------------------------------------------ K/V squared error
+
+struct EArgs {
+  DevCodec c;
+  const uint16_t* x;
+  int T, H, L, D, lpt_log2, chunks;
+  double* part;     // [units][chunks][2]
+  Tables tab;
+};
+
+__global__ __launch_bounds__(kBlock) void k_kverr(EArgs a) {
+  __shared__ float lds[kBlock * 17];
+  __shared__ double red[2][kBlock];
+  const int tid = threadIdx.x;
+  const int LPT = 1 << a.lpt_log2, j = tid & (LPT - 1), rloc = tid >> a.lpt_log2, RPB = kBlock >> a.lpt_log2;
+  float* rowlds = lds + rloc * 17 * LPT;
+  const long long unit = blockIdx.y;
+  const int per = (a.T + a.chunks - 1) / a.chunks;
+  const int t0 = blockIdx.x * per, t1 = min(a.T, t0 + per);
+  const float* cp = nullptr;
+  if (a.c.chan) {
+    const int h = (int)(unit % a.H), l = (int)((unit / a.H) % a.L);
+    cp = a.c.chan + ((size_t)l * a.H + h) * a.D + 16 * j;
+  }
+  double se = 0.0, sx = 0.0;
+  for (int tb = t0; tb < t1; tb += RPB) {
+    const int t = tb + rloc;
+    const bool active = t < t1;
+    const long long row = unit * a.T + t;
+    float v[16];
+    if (active) {
+      dq_row_any(a.c, row, j, a.tab, v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = 0.0f;
+    }
+    if (a.c.W > 1) fwht_rows(v, rowlds, j, LPT, a.c.W, a.c.kappa);
+    if (active) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float y = cp ? __fdiv_rn(v[k], cp[k]) : v[k];
+        const double x = (double)h2f(a.x[(size_t)row * a.D + 16 * j + k]);
+        const double d = (double)y - x;
+        se += d * d;
+        sx += x * x;
+      }
+    }
+  }
+  red[0][tid] = se;
+  red[1][tid] = sx;
+  __syncthreads();
+  for (int st = kBlock / 2; st > 0; st >>= 1) {
+    if (tid < st) { red[0][tid] += red[0][tid + st]; red[1][tid] += red[1][tid + st]; }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.part[(unit * a.chunks + blockIdx.x) * 2 + 0] = red[0][0];
+    a.part[(unit * a.chunks + blockIdx.x) * 2 + 1] = red[1][0];
+  }
+}
+
+// Fixed-order sum of the chunk partials: kv_err[unit] = (dK^2, K^2, dV^2, V^2).
+__global__ void k_kverr_final(const double* pk, const double* pv, int chunks, long long units, double* out) {
+  const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  double a0 = 0, a1 = 0, b0 = 0, b1 = 0;
+  for (int c = 0; c < chunks; ++c) {
+    a0 += pk[(u * chunks + c) * 2]; a1 += pk[(u * chunks + c) * 2 + 1];
+    b0 += pv[(u * chunks + c) * 2]; b1 += pv[(u * chunks + c) * 2 + 1];
+  }
+  out[u * 4 + 0] = a0; out[u * 4 + 1] = a1; out[u * 4 + 2] = b0; out[u * 4 + 3] = b1;
+}
+
+// ------------------------------------------------------------------ host side
+
+static int lpt_log2_of(int D) { return D == 64 ? 2 : D == 128 ? 3 : 4; }
+
+static float kappa_of(int W) {
+  if (W <= 1) return 1.0f;
+  int e = 0;
+  while ((1 << e) < W) ++e;
+  return (e % 2 == 0) ? ldexpf(1.0f, -e / 2) : (float)(1.0 / std::sqrt((double)W));
+}
+
+static DevCodec dev_codec(const kvq_packed& p) {
+  DevCodec c{};
+  c.cb = p.codec.codebook;
+  c.bits = p.codec.bits;
+  c.g = p.codec.group;
+  c.W = p.codec.rot_width > 1 ? p.codec.rot_width : 0;
+  c.kappa = kappa_of(c.W);
+  const int D = p.shape.head_dim;
+  int b = p.codec.bits;
+  switch (c.cb) {
+    case KVQ_FP16: b = 16; break;
+    case KVQ_TERNARY: b = 2; break;
+    case KVQ_SIGN: b = 1; break;
+    case KVQ_NF4: b = 4; break;
+    case KVQ_INT8_SYM: b = 8; break;
+    default: break;
+  }
+  c.row_bytes = (size_t)D * b / 8;
+  c.ng = (c.cb == KVQ_FP16 || c.g == 0) ? 0 : D / c.g;
+  c.codes = reinterpret_cast<const uint8_t*>(p.codes);
+  c.scales = p.scales;
+  c.mins = p.mins;
+  c.chan = p.chan_scale;
+  if (c.cb == KVQ_RFFT_POLAR || c.cb == KVQ_RFFT_CART) {
+    RfftCodec& r = c.rc;
+    r.cb = c.cb;
+    r.N = D;
+    r.F = D / 2 + 1;
+    r.bits = p.codec.bits;
+    r.pbits = (c.cb == KVQ_RFFT_POLAR) ? p.codec.aux_bits : 0;
+    r.g = p.codec.group;
+    r.ngroups = (r.F + r.g - 1) / r.g;
+    r.nscales = (c.cb == KVQ_RFFT_POLAR) ? r.ngroups : 2 * r.ngroups;
+    const long bits = (c.cb == KVQ_RFFT_POLAR) ? (long)r.F * (r.bits + r.pbits) : 2L * r.F * r.bits;
+    r.words = (int)((bits + 31) / 32);
+  }
+  return c;
+}
+
+int decode_splits(const kvq_shape& s, int Hq, int n_q) {
+  (void)Hq;
+  const long long pairs = (long long)s.batch * s.layers * n_q * s.heads;
+  const int max_s = std::max(1, (s.tokens + TB - 1) / TB);
+  long long S = (2048 + pairs - 1) / pairs;
+  if (S < 1) S = 1;
+  if (S > max_s) S = max_s;
+  // equalise: chunk is a multiple of TB; recompute S so no split is empty
+  const int chunk = (int)(((s.tokens + S - 1) / S + TB - 1) / TB * TB);
+  return chunk > 0 ? std::max(1, (s.tokens + chunk - 1) / chunk) : 1;
+}
+
+static int split_chunk(const kvq_shape& s, int S) {
+  const int c = ((s.tokens + S - 1) / S + TB - 1) / TB * TB;
+  return c > 0 ? c : TB;
+}
+
+size_t decode_ws_bytes(const kvq_shape& s, int Hq, int n_q) {
+  const int S = decode_splits(s, Hq, n_q);
+  return (size_t)s.batch * s.layers * n_q * Hq * S * (s.head_dim + 2) * sizeof(float);
+}
+
+static int kverr_chunks(const kvq_shape& s) {
+  const long long units = (long long)s.batch * s.layers * s.heads;
+  long long c = (4096 + units - 1) / units;
+  if (c > 64) c = 64;
+  if (c > s.tokens) c = s.tokens;
+  return (int)(c < 1 ? 1 : c);
+}
+
+size_t error_ws_bytes(const kvq_shape& s, int Hq, int n_q) {
+  const int S = decode_splits(s, Hq, n_q);
+  const size_t part = (size_t)s.batch * s.layers * n_q * Hq * S * (2 * s.head_dim + 10) * sizeof(float);
+  const size_t units = (size_t)s.batch * s.layers * s.heads;
+  const size_t kv = 2 * units * kverr_chunks(s) * 2 * sizeof(double);
+  return ((part + 255) / 256) * 256 + kv;
+}
+
+static AArgs make_aargs(const AttnProblem& pr) {
+  AArgs a{};
+  a.k = dev_codec(*pr.k);
+  a.v = dev_codec(*pr.v);
+  a.q = pr.q;
+  a.kv_len = pr.kv_len;
+  a.k16 = pr.k16;
+  a.v16 = pr.v16;
+  a.sm_scale = pr.sm_scale;
+  const kvq_shape& s = pr.k->shape;
+  a.B = s.batch; a.L = s.layers; a.H = s.heads; a.T = s.tokens; a.D = s.head_dim;
+  a.Hq = pr.Hq; a.G = pr.Hq / s.heads; a.n_q = pr.n_q;
+  a.S = decode_splits(s, pr.Hq, pr.n_q);
+  a.chunk = split_chunk(s, a.S);
+  a.lpt_log2 = lpt_log2_of(a.D);
+  a.Dc = (a.k.cb == KVQ_RFFT_POLAR || a.k.cb == KVQ_RFFT_CART) ? 2 * (a.D / 2 + 1) : a.D;
+  a.ws = static_cast<float*>(pr.ws);
+  a.tab = host_tables();
+  host_fft_tables(a.D, &a.tw);
+  if (a.k.cb == KVQ_RFFT_POLAR) {
+    PhaseTables pt;
+    host_phase_tables(1 << a.k.rc.pbits, &pt);
+    for (int k = 0; k < 256; ++k) { a.dirs.dir_c[k] = pt.dir_c[k]; a.dirs.dir_s[k] = pt.dir_s[k]; }
+  }
+  return a;
+}
+
+static size_t split_smem(const AArgs& a, bool err) {
+  const int RS = 17 * (a.D / 16) + 17;
+  size_t f = (size_t)2 * kMaxG * RS + 2 * TB * RS + 2 * kMaxG * TB;
+  if (err) f += (size_t)kMaxG * RS + 2 * TB * RS;
+  f = (f + 3) / 4 * 4;                                   // 16-byte align the logit/stat arrays
+  const size_t acc_bytes = err ? sizeof(double) : sizeof(float);
+  return f * sizeof(float) + (2 * kMaxG * TB + 8 * kMaxG) * acc_bytes;
+}
+
+hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
+  AArgs a = make_aargs(pr);
+  const long long R = (long long)a.B * a.L * a.n_q;
+  const size_t smem = split_smem(a, false);
+  hipError_t e0 = hipFuncSetAttribute((const void*)k_attn_split<false>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e0 != hipSuccess) return e0;
+  k_attn_split<false><<<dim3(a.S, a.H, (unsigned)R), kBlock, smem, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_attn_combine<false><<<(unsigned)(R * a.Hq), kBlock, 0, st>>>(a, pr.out, pr.lse, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st) {
+  AArgs a = make_aargs(pr);
+  const kvq_shape& s = pr.k->shape;
+  const long long R = (long long)a.B * a.L * a.n_q;
+  const size_t smem = split_smem(a, true);
+  hipError_t e0 = hipFuncSetAttribute((const void*)k_attn_split<true>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e0 != hipSuccess) return e0;
+  k_attn_split<true><<<dim3(a.S, a.H, (unsigned)R), kBlock, smem, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_attn_combine<true><<<(unsigned)(R * a.Hq), kBlock, 0, st>>>(a, nullptr, nullptr, pr.kl, pr.relerr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // per-unit K/V squared error
+  const long long units = (long long)s.batch * s.layers * s.heads;
+  const int chunks = kverr_chunks(s);
+  const size_t part_bytes = (size_t)R * a.Hq * a.S * (2 * a.D + 10) * sizeof(float);
+  double* pk = reinterpret_cast<double*>(static_cast<char*>(pr.ws) + ((part_bytes + 255) / 256) * 256);
+  double* pv = pk + units * chunks * 2;
+  if (units == 0 || s.tokens == 0) {
+    return hipMemsetAsync(pr.kv_err, 0, sizeof(double) * 4 * units, st);
+  }
+  const kvq_packed* tens[2] = {pr.k, pr.v};
+  const uint16_t* xs[2] = {pr.k16, pr.v16};
+  double* parts[2] = {pk, pv};
+  for (int w = 0; w < 2; ++w) {
+    const kvq_packed& p = *tens[w];
+    if (p.codec.codebook == KVQ_RFFT_POLAR || p.codec.codebook == KVQ_RFFT_CART) {
+      e = launch_rfft_kverr(xs[w], p, parts[w], chunks, st);
+    } else {
+      EArgs ea{};
+      ea.c = dev_codec(p);
+      ea.x = xs[w];
+      ea.T = s.tokens; ea.H = s.heads; ea.L = s.layers; ea.D = s.head_dim;
+      ea.lpt_log2 = lpt_log2_of(s.head_dim);
+      ea.chunks = chunks;
+      ea.part = parts[w];
+      ea.tab = host_tables();
+      k_kverr<<<dim3(chunks, (unsigned)units), kBlock, 0, st>>>(ea);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+  }
+  k_kverr_final<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(pk, pv, chunks, units, pr.kv_err);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

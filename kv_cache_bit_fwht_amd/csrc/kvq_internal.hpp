@@ -148,6 +148,7 @@ hipError_t launch_dequant(const kvq_packed& p, float* xhat, hipStream_t st);
 hipError_t launch_calibrate(const uint16_t* k, const kvq_shape& s, float* c, hipStream_t st);
 hipError_t launch_rfft_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st);
 hipError_t launch_rfft_dequant(const kvq_packed& p, float* xhat, hipStream_t st);
+hipError_t launch_rfft_kverr(const uint16_t* x, const kvq_packed& p, double* part, int chunks, hipStream_t st);
 
 struct AttnProblem {
   const kvq_packed* k;
