@@ -1,0 +1,250 @@
+"""Benchmark of the hot path on the 64K-token decode workload (one GPU).
+
+Workload: 8 layers x 4 KV heads x 65,536 tokens x head_dim 256, batch 1, 16
+query heads (GQA 4:1); keys Walsh-Hadamard-rotated (256) 4-bit signed absmax at
+group 128, values 2-bit signed absmax at group 128 (3.125 bits per value with
+the fp16 scales); 256 decode queries ~ N(0,1).  Seeded synthetic fp16 K/V stand
+in for the real 64K-span caches the pages measure on.
+
+One step = quantise+pack K and V of the whole cache (kvq_quantize_pack, two
+launches) + 256 decode-attention calls (kvq_decode_attn, one per decode query,
+each reading the whole packed cache).  Inputs are resident in HBM before the
+timed region; three copies of the packed cache are rotated so the 256 MB
+Infinity Cache cannot serve repeats.
+
+Prints one JSON line: value = decode tokens per second of the whole step
+(quantise included); the split rates, the roofline of the dominant kernel
+(decode) measured with HIP events on the launch stream, and the CPU oracle
+timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
+KERNEL_SRC = {"decode": ["kv_cache_bit_fwht_amd/csrc/kvq_attn_fast.hip", "kv_cache_bit_fwht_amd/csrc/kvq_attn.hip"],
+              "quantize": ["kv_cache_bit_fwht_amd/csrc/kvq_quant.hip", "kv_cache_bit_fwht_amd/csrc/kvq_codec.hpp"]}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kind, per_launch_units):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f).get(kind)
+    if not d or d.get("src_hash") != src_hash(KERNEL_SRC[kind]):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(Kx, Vx, q, units_sample=2, queries_sample=4):
+    """The oracle as it stands on a bounded sample of the same workload, scaled
+    to the whole step: quantise+pack+dequantise `units_sample` (layer, head)
+    units and run fp64 attention for `queries_sample` queries on them."""
+    from threadpoolctl import threadpool_limits
+    import oracle as O
+    B, L, H, T, D = Kx.shape
+    nq = q.shape[2]
+    G = q.shape[3] // H
+    kc = O.Codec(O.INT_ABSMAX, 4, 128, rot=256)
+    vc = O.Codec(O.INT_ABSMAX, 2, 128)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        deq = []
+        for u in range(units_sample):
+            l, h = u // H, u % H
+            ku = Kx[0, l, h][None, None, None]
+            vu = Vx[0, l, h][None, None, None]
+            wk, sk, zk = O.quantize_pack(ku, kc)
+            wv, sv, zv = O.quantize_pack(vu, vc)
+            deq.append((O.dequant(wk, sk, zk, kc, ku.shape)[0, 0, 0], O.dequant(wv, sv, zv, vc, vu.shape)[0, 0, 0]))
+        t_qd = (time.perf_counter() - t0) / units_sample
+        t0 = time.perf_counter()
+        for u in range(units_sample):
+            l, h = u // H, u % H
+            Kd, Vd = deq[u]
+            for i in range(queries_sample):
+                O.attention.attend(q[0, l, i, h * G:(h + 1) * G].astype(np.float64), Kd, Vd, T, 1.0 / np.sqrt(D))
+        t_att = (time.perf_counter() - t0) / (units_sample * queries_sample)
+    units = B * L * H
+    step_s = units * t_qd + nq * units * t_att
+    return {
+        "value": round(nq * B / step_s, 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{units_sample} of {units} (layer, head) units quantised+packed+dequantised and "
+                   f"{queries_sample} of {nq} decode queries attended in fp64, scaled to the full step "
+                   f"({units} units, {nq} queries); NumPy, BLAS limited to 1 thread"),
+        "seconds_per_unit_codec": round(t_qd, 3), "seconds_per_query_unit_attention": round(t_att, 4),
+        "cpu": _cpu_name(),
+    }
+
+
+def _cpu_name():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--decode-queries", type=int, default=256)
+    ap.add_argument("--path", type=int, default=0, help="decode kernel: 0 auto, 1 general, 2 MFMA")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the path would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.get("c3")
+    nq = min(args.decode_queries, w.n_q)
+    log(f"generating {w.description}")
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    shape = K.Shape(w.B, w.L, w.H, w.T, w.D)
+    kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    kd = torch.from_numpy(Kx.view(np.int16)).to(dev)
+    vd = torch.from_numpy(Vx.view(np.int16)).to(dev)
+    # one contiguous [B][L][1][Hq][D] query per decode step
+    qs = np.ascontiguousarray(q.transpose(2, 0, 1, 3, 4)[:nq, :, :, None])
+    qd = torch.from_numpy(qs.view(np.int16)).to(dev)
+    copies = [(K.alloc_packed(kc, shape, dev), K.alloc_packed(vc, shape, dev)) for _ in range(args.copies)]
+    out = torch.empty((w.B, w.L, 1, w.Hq, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.L, 1, w.Hq), dtype=torch.float32, device=dev)
+    wsb = K.kvq_decode_attn_workspace(shape, w.Hq, 1)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for kp, vp in copies:
+        K.kvq_quantize_pack(kd, kp)
+        K.kvq_quantize_pack(vd, vp)
+    torch.cuda.synchronize()
+
+    rows = w.B * w.L * w.H * w.T
+    q_bytes = rows * (w.D * 2) * 2 + rows * (w.D * 4 // 8 + 2 * 2) + rows * (w.D * 2 // 8 + 2 * 2)
+    d_bytes = rows * (w.D * 4 // 8 + 2 * 2 + w.D * 2 // 8 + 2 * 2)
+    step_idx = [0]
+
+    def step(record):
+        c = step_idx[0] % len(copies)
+        step_idx[0] += 1
+        kp, vp = copies[c]
+        ev = []
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        K.kvq_quantize_pack(kd, kp)
+        K.kvq_quantize_pack(vd, vp)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(stream)
+        ev.append(("quantize", e0, e1))
+        for i in range(nq):
+            kp2, vp2 = copies[(c + i) % len(copies)]
+            a = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            K.kvq_decode_attn(kp2, vp2, w.Hq, 1, qd[i], None, 0.0, out, lse, ws, wsb, path=args.path or None)
+            b = torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            ev.append(("decode", a, b))
+        if record is not None:
+            record.extend(ev)
+
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    rec = []
+    log(f"timing {args.steps} step(s) of quantize+pack + {nq} decode calls")
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(rec)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    qz = [a.elapsed_time(b) for k, a, b in rec if k == "quantize"]
+    dc = [a.elapsed_time(b) for k, a, b in rec if k == "decode"]
+    qz_ms, dc_ms = float(np.mean(qz)), float(np.mean(dc))
+    log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.1f} ms); quantize {qz_ms * 1e3:.1f} us; "
+        f"decode {dc_ms * 1e3:.1f} us")
+
+    value = nq * w.B / (ms_step * 1e-3)
+    dec_gbs = d_bytes / (dc_ms * 1e-3) / 1e9
+    qz_gbs = q_bytes / (qz_ms * 1e-3) / 1e9
+    fast = K.kvq_decode_attn_workspace is not None and args.path != 1
+    rec_line = {
+        "metric": "quantize+pack GB/s and packed decode-attn tok/s @64K; % of HBM peak",
+        "value": round(value, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded fp16 K/V with outlier channels, N(0,1) queries)",
+        "config": {"workload": "64K decode: B=1 L=8 H=4 T=65536 D=256, Hq=16 (GQA 4:1), "
+                               "K FWHT-256 int4 absmax g128, V int2 absmax g128 (3.125 bpv), "
+                               f"{nq} decode queries per step",
+                   "decode_calls_per_step": nq, "packed_cache_copies": len(copies),
+                   "decode_path": {0: "auto", 1: "general", 2: "mfma"}[args.path]},
+        "quantize_pack": {"GB/s": round(qz_gbs, 1), "frac_hbm": round(qz_gbs / HBM_PEAK_GBS, 4),
+                          "us_per_call_pair": round(qz_ms * 1e3, 2), "bytes": q_bytes},
+        "decode": {"tok/s": round(1e3 / dc_ms, 1), "us_per_token": round(dc_ms * 1e3, 2),
+                   "GB/s": round(dec_gbs, 1), "frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "bytes_per_launch": d_bytes},
+        "roofline": {"bound": "hbm", "kernel": "kvq_decode_attn", "achieved": round(dec_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("decode", 1)},
+    }
+    del fast
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        rec_line["cpu_baseline"] = cpu_baseline(Kx, Vx, q)
+    print(json.dumps(rec_line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

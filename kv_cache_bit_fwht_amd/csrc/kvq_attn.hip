@@ -23,6 +23,7 @@ namespace kvq {
 
 constexpr int TB = 16;          // tokens per tile
 constexpr int kMaxG = 8;
+constexpr int kMaxSplits = 1024;   // split partials merged per query head
 
 struct DevCodec {
   int cb, bits, g, W, ng;
@@ -394,11 +395,20 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
 // One block per (query row, query head).  Merges the S split partials:
 // M = max m_s, L = sum l_s e^{m_s - M}, o = sum o_s e^{m_s - M} / L; then
 // rotates o back if V was rotated and divides V's per-channel scale.
+struct CArgs {
+  const float* ws;
+  int S, D, Hq, G, H, L, n_q;
+  int vW;
+  float vkappa;
+  const float* vchan;
+};
+
 template <bool ERR>
-__global__ __launch_bounds__(kBlock) void k_attn_combine(AArgs a, float* out, float* lse, float* kl,
+__global__ __launch_bounds__(kBlock) void k_attn_combine(CArgs a, float* out, float* lse, float* kl,
                                                          float* relerr) {
-  __shared__ float orow[2][17 * 16 + 17];
-  __shared__ float red[kBlock];
+  __shared__ float orow[17 * 16 + 17];
+  __shared__ double wq[kMaxSplits], w2[kMaxSplits];   // per-split weights e^{m_s - M}
+  __shared__ double red[3][kBlock];
   const long long rh = blockIdx.x;               // rq * Hq + j
   const int j = (int)(rh % a.Hq);
   const long long rq = rh / a.Hq;
@@ -413,39 +423,70 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AArgs a, float* out, fl
     if (ERR) return reinterpret_cast<const double*>(p + 2 * D)[k];
     return (double)p[D + k];
   };
-  double M = -INFINITY, M2 = -INFINITY;
-  for (int s = 0; s < a.S; ++s) {
-    M = fmax(M, stat(s, 0));
-    if (ERR) M2 = fmax(M2, stat(s, 2));
+  // 1. maxima over splits
+  double mx = -INFINITY, mx2 = -INFINITY;
+  for (int s = tid; s < a.S; s += kBlock) {
+    mx = fmax(mx, stat(s, 0));
+    if (ERR) mx2 = fmax(mx2, stat(s, 2));
   }
-  double Lq = 0.0, L2 = 0.0, A = 0.0;
-  for (int s = 0; s < a.S; ++s) {
-    if (M != -INFINITY && stat(s, 0) != -INFINITY) Lq += stat(s, 1) * exp(stat(s, 0) - M);
-    if (ERR && M2 != -INFINITY && stat(s, 2) != -INFINITY) {
-      const double w = exp(stat(s, 2) - M2);
-      L2 += stat(s, 3) * w;
-      A += stat(s, 4) * w;
+  red[0][tid] = mx;
+  red[1][tid] = mx2;
+  __syncthreads();
+  for (int st = kBlock / 2; st > 0; st >>= 1) {
+    if (tid < st) {
+      red[0][tid] = fmax(red[0][tid], red[0][tid + st]);
+      red[1][tid] = fmax(red[1][tid], red[1][tid + st]);
+    }
+    __syncthreads();
+  }
+  const double M = red[0][0], M2 = red[1][0];
+  __syncthreads();
+  // 2. split weights and the normalisers
+  double lq = 0.0, l2 = 0.0, aa = 0.0;
+  for (int s = tid; s < a.S; s += kBlock) {
+    const double ms = stat(s, 0);
+    const double w = (M == -INFINITY || ms == -INFINITY) ? 0.0 : exp(ms - M);
+    wq[s] = w;
+    lq += stat(s, 1) * w;
+    if (ERR) {
+      const double m2s = stat(s, 2);
+      const double v = (M2 == -INFINITY || m2s == -INFINITY) ? 0.0 : exp(m2s - M2);
+      w2[s] = v;
+      l2 += stat(s, 3) * v;
+      aa += stat(s, 4) * v;
     }
   }
+  red[0][tid] = lq;
+  red[1][tid] = l2;
+  red[2][tid] = aa;
+  __syncthreads();
+  for (int st = kBlock / 2; st > 0; st >>= 1) {
+    if (tid < st) {
+      red[0][tid] += red[0][tid + st];
+      red[1][tid] += red[1][tid + st];
+      red[2][tid] += red[2][tid + st];
+    }
+    __syncthreads();
+  }
+  const double Lq = red[0][0], L2 = red[1][0], A = red[2][0];
+  // 3. outputs, one dimension per thread (coalesced over the partial rows)
   float o = 0.0f, o2 = 0.0f;
   if (tid < D) {
     double acc = 0.0, acc2 = 0.0;
     for (int s = 0; s < a.S; ++s) {
       const float* p = src + (size_t)s * P;
-      if (M != -INFINITY && stat(s, 0) != -INFINITY) acc += (double)p[tid] * exp(stat(s, 0) - M);
-      if (ERR && M2 != -INFINITY && stat(s, 2) != -INFINITY) acc2 += (double)p[D + tid] * exp(stat(s, 2) - M2);
+      acc += (double)p[tid] * wq[s];
+      if (ERR) acc2 += (double)p[D + tid] * w2[s];
     }
     o = Lq > 0.0 ? (float)(acc / Lq) : 0.0f;
     if (ERR) o2 = L2 > 0.0 ? (float)(acc2 / L2) : 0.0f;
-    orow[0][pidx(tid)] = o;
+    orow[pidx(tid)] = o;
   }
   __syncthreads();
-  if (a.v.W > 1) {
-    fwht_lds_rows(orow[0], 1, 0, D, a.v.W, a.v.kappa);
-  }
+  if (a.vW > 1) fwht_lds_rows(orow, 1, 0, D, a.vW, a.vkappa);
   if (tid < D) {
-    o = orow[0][pidx(tid)];
-    if (a.v.chan) o = o / a.v.chan[((size_t)l * a.H + h) * D + tid];
+    o = orow[pidx(tid)];
+    if (a.vchan) o = o / a.vchan[((size_t)l * a.H + h) * D + tid];
   }
   if (!ERR) {
     if (tid < D) out[(size_t)rh * D + tid] = o;
@@ -453,24 +494,21 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AArgs a, float* out, fl
     return;
   }
   // relative error of the quantised output against the fp16 one, and KL
+  __syncthreads();
   const float dlt = (tid < D) ? (o - o2) : 0.0f;
-  red[tid] = dlt * dlt;
+  red[0][tid] = (double)dlt * dlt;
+  red[1][tid] = (tid < D) ? (double)o2 * o2 : 0.0;
   __syncthreads();
   for (int st = kBlock / 2; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
-    __syncthreads();
-  }
-  const float num = red[0];
-  __syncthreads();
-  red[tid] = (tid < D) ? o2 * o2 : 0.0f;
-  __syncthreads();
-  for (int st = kBlock / 2; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
+    if (tid < st) {
+      red[0][tid] += red[0][tid + st];
+      red[1][tid] += red[1][tid + st];
+    }
     __syncthreads();
   }
   if (tid == 0) {
-    const float den = red[0];
-    relerr[rh] = den > 0.0f ? sqrtf(num) / sqrtf(den) : 0.0f;
+    const double num = red[0][0], den = red[1][0];
+    relerr[rh] = den > 0.0 ? (float)(sqrt(num) / sqrt(den)) : 0.0f;
     double k = 0.0;
     if (L2 > 0.0 && Lq > 0.0) k = A / L2 - (M2 + log(L2)) + (M + log(Lq));
     kl[rh] = (float)k;
@@ -607,6 +645,7 @@ int decode_splits(const kvq_shape& s, int Hq, int n_q) {
   long long S = (2048 + pairs - 1) / pairs;
   if (S < 1) S = 1;
   if (S > max_s) S = max_s;
+  if (S > kMaxSplits) S = kMaxSplits;
   // equalise: chunk is a multiple of TB; recompute S so no split is empty
   const int chunk = (int)(((s.tokens + S - 1) / S + TB - 1) / TB * TB);
   return chunk > 0 ? std::max(1, (s.tokens + chunk - 1) / chunk) : 1;
@@ -619,7 +658,9 @@ static int split_chunk(const kvq_shape& s, int S) {
 
 size_t decode_ws_bytes(const kvq_shape& s, int Hq, int n_q) {
   const int S = decode_splits(s, Hq, n_q);
-  return (size_t)s.batch * s.layers * n_q * Hq * S * (s.head_dim + 2) * sizeof(float);
+  const size_t gen = (size_t)s.batch * s.layers * n_q * Hq * S * (s.head_dim + 2) * sizeof(float);
+  const size_t fast = fast_ws_bytes(s, Hq, n_q);
+  return gen > fast ? gen : fast;
 }
 
 static int kverr_chunks(const kvq_shape& s) {
@@ -684,7 +725,31 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
   k_attn_split<false><<<dim3(a.S, a.H, (unsigned)R), kBlock, smem, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_attn_combine<false><<<(unsigned)(R * a.Hq), kBlock, 0, st>>>(a, pr.out, pr.lse, nullptr, nullptr);
+  return launch_combine_partials(pr, a.S, st);
+}
+
+static CArgs make_cargs(const AttnProblem& pr, int S, float* ws) {
+  CArgs c{};
+  const kvq_shape& s = pr.k->shape;
+  c.ws = ws;
+  c.S = S;
+  c.D = s.head_dim;
+  c.Hq = pr.Hq;
+  c.G = pr.Hq / s.heads;
+  c.H = s.heads;
+  c.L = s.layers;
+  c.n_q = pr.n_q;
+  c.vW = pr.v->codec.rot_width > 1 ? pr.v->codec.rot_width : 0;
+  c.vkappa = kappa_of(c.vW);
+  c.vchan = pr.v->chan_scale;
+  return c;
+}
+
+hipError_t launch_combine_partials(const AttnProblem& pr, int S, hipStream_t st) {
+  const kvq_shape& s = pr.k->shape;
+  const long long R = (long long)s.batch * s.layers * pr.n_q;
+  const CArgs c = make_cargs(pr, S, static_cast<float*>(pr.ws));
+  k_attn_combine<false><<<(unsigned)(R * pr.Hq), kBlock, 0, st>>>(c, pr.out, pr.lse, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -699,7 +764,8 @@ hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st) {
   k_attn_split<true><<<dim3(a.S, a.H, (unsigned)R), kBlock, smem, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_attn_combine<true><<<(unsigned)(R * a.Hq), kBlock, 0, st>>>(a, nullptr, nullptr, pr.kl, pr.relerr);
+  k_attn_combine<true><<<(unsigned)(R * a.Hq), kBlock, 0, st>>>(make_cargs(pr, a.S, a.ws), nullptr, nullptr,
+                                                                pr.kl, pr.relerr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // per-unit K/V squared error

@@ -1,0 +1,117 @@
+"""GPU parity of the MFMA decode-attention kernel (4-bit keys, 2-bit values,
+head_dim 256) against the CPU oracle, and against the general kernel.
+
+Bar: outputs within 2e-3 relative L2 per row (the query enters the matrix
+cores rounded to fp16: about 2^-12 relative per element, far inside the bar),
+lse within 1e-3 absolute.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_util import announce, oracle_codec, to_dev, to_np
+from tests.test_gpu_attn import _check_decode, _gpu_decode, _gpu_pack, _oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(K, w, kc, vc, kv_len=None, compare_general=True):
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    kp, vp = _gpu_pack(K, Kx, kc), _gpu_pack(K, Vx, vc)
+    _, Kd, Vd = _oracle(Kx, Vx, oracle_codec(K, O, kc), oracle_codec(K, O, vc), q, kv_len)
+    out, lse = _gpu_decode(K, kp, vp, q, kv_len, path=2)
+    ref_out, ref_lse = O.decode_attn(q, Kd, Vd, kv_len)
+    rel = _check_decode(out, lse, ref_out, ref_lse, kv_len, lse_tol=1e-3)
+    if compare_general:
+        out1, lse1 = _gpu_decode(K, kp, vp, q, kv_len, path=1)
+        rel1 = np.linalg.norm(out1 - out, axis=-1) / np.maximum(np.linalg.norm(out1, axis=-1), 1e-30)
+        assert rel1.max() < 2e-3
+    return rel
+
+
+def test_fast_c3_shape_shrunk():
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=2, T=2048, n_q=3)
+    announce("mfma c3 shrunk")
+    rel = _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0))
+    print(f"max rel err {rel:.2e}")
+
+
+@pytest.mark.parametrize("variant", ["kgroup256", "vgroup64", "vgroup256", "rot128", "norot", "G2", "G1",
+                                     "vrot"])
+def test_fast_variants(variant):
+    import kv_cache_bit_fwht_amd as K
+    kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    w = synth.get("c3", L=1, T=640, n_q=2)
+    if variant == "kgroup256":
+        kc = K.Codec(K.INT_ABSMAX, 4, 256, 256)
+    elif variant == "vgroup64":
+        vc = K.Codec(K.INT_ABSMAX, 2, 64, 0)
+    elif variant == "vgroup256":
+        vc = K.Codec(K.INT_ABSMAX, 2, 256, 0)
+    elif variant == "rot128":
+        kc = K.Codec(K.INT_ABSMAX, 4, 128, 128)
+    elif variant == "norot":
+        kc = K.Codec(K.INT_ABSMAX, 4, 128, 0)
+    elif variant == "G2":
+        w = w.with_sizes(Hq=8)
+    elif variant == "G1":
+        w = w.with_sizes(Hq=4)
+    elif variant == "vrot":
+        vc = K.Codec(K.INT_ABSMAX, 2, 128, 256)
+    announce(f"mfma variant {variant}")
+    _case(K, w, kc, vc)
+
+
+def test_fast_causal_lengths():
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=1, T=1024, n_q=8)
+    kv_len = np.array([[[0, 1, 31, 32, 33, 500, 1023, 1024]]], dtype=np.int32)
+    announce("mfma causal lengths")
+    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), kv_len)
+
+
+def test_fast_rejects_unsupported_and_auto_falls_back():
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=1, T=100, n_q=1)                 # tokens not a multiple of 32
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    kp = _gpu_pack(K, Kx, K.Codec(K.INT_ABSMAX, 4, 128, 256))
+    vp = _gpu_pack(K, Vx, K.Codec(K.INT_ABSMAX, 2, 128, 0))
+    announce("mfma unsupported shape")
+    with pytest.raises(K.KvqError):
+        _gpu_decode(K, kp, vp, q, None, path=2)
+    out, _ = _gpu_decode(K, kp, vp, q, None, path=None)   # automatic: general kernel
+    assert np.isfinite(out).all()
+
+
+def test_fast_full_size_64k_sampled():
+    """The 64K-token decode workload at full size, one decode query per call as
+    the benchmark times it, checked on sampled (layer, KV head) units."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3")
+    announce("mfma full-size 64K")
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    kp, vp = _gpu_pack(K, Kx, kc), _gpu_pack(K, Vx, vc)
+    okc, ovc = oracle_codec(K, O, kc), oracle_codec(K, O, vc)
+    for i in (0, 137):
+        qi = np.ascontiguousarray(q[:, :, i:i + 1])
+        out, lse = _gpu_decode(K, kp, vp, qi, None)
+        for (l, h) in ((0, 0), (5, 2), (7, 3)):
+            ku = Kx[0, l, h][None, None, None]
+            vu = Vx[0, l, h][None, None, None]
+            wk, sk, zk = O.quantize_pack(ku, okc)
+            wv, sv, zv = O.quantize_pack(vu, ovc)
+            Kd = O.dequant(wk, sk, zk, okc, ku.shape)[0, 0, 0]
+            Vd = O.dequant(wv, sv, zv, ovc, vu.shape)[0, 0, 0]
+            G = w.Hq // w.H
+            ro, rl, _ = O.attention.attend(qi[0, l, 0, h * G:(h + 1) * G].astype(np.float64), Kd, Vd, w.T,
+                                           1.0 / 16.0)
+            go = out[0, l, 0, h * G:(h + 1) * G].astype(np.float64)
+            rel = np.linalg.norm(go - ro, axis=-1) / np.linalg.norm(ro, axis=-1)
+            assert rel.max() < 2e-3, f"query {i} unit {(l, h)} rel {rel.max():.3g}"
+            assert np.abs(lse[0, l, 0, h * G:(h + 1) * G] - rl).max() < 1e-3
