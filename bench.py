@@ -122,6 +122,9 @@ def main():
     ap.add_argument("--path", type=int, default=0, help="decode kernel: 0 auto, 1 general, 2 MFMA")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for hardware-counter passes: a known-size copy (the counters' "
+                         "calibration), one quantize+pack pair and --decode-queries decode calls")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -156,62 +159,76 @@ def main():
         K.kvq_quantize_pack(vd, vp)
     torch.cuda.synchronize()
 
+    if args.profile:
+        # 1 GiB device-to-device copy of known size: FETCH_SIZE / WRITE_SIZE of this kernel
+        # calibrate the counters (expected 1 GiB read and 1 GiB written)
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        kp, vp = copies[0]
+        K.kvq_quantize_pack(kd, kp)
+        K.kvq_quantize_pack(vd, vp)
+        for i in range(nq):
+            kp2, vp2 = copies[i % len(copies)]
+            K.kvq_decode_attn(kp2, vp2, w.Hq, 1, qd[i], None, 0.0, out, lse, ws, wsb, None,
+                              args.path or None)
+        torch.cuda.synchronize()
+        log("profile run done")
+        return
+
     rows = w.B * w.L * w.H * w.T
     q_bytes = rows * (w.D * 2) * 2 + rows * (w.D * 4 // 8 + 2 * 2) + rows * (w.D * 2 // 8 + 2 * 2)
     d_bytes = rows * (w.D * 4 // 8 + 2 * 2 + w.D * 2 // 8 + 2 * 2)
     step_idx = [0]
 
-    def step(record):
+    sh = stream.cuda_stream
+    path = args.path or None
+    # raw device addresses, so the per-call host work is only argument marshalling
+    q_ptrs = [qd[i].data_ptr() for i in range(nq)]
+    out_p, lse_p, ws_p = out.data_ptr(), lse.data_ptr(), ws.data_ptr()
+
+    def step(ev):
+        """One step; ev = (start, after quantise, after the decode calls) events or None."""
         c = step_idx[0] % len(copies)
         step_idx[0] += 1
         kp, vp = copies[c]
-        ev = []
-        e0 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        K.kvq_quantize_pack(kd, kp)
-        K.kvq_quantize_pack(vd, vp)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e1.record(stream)
-        ev.append(("quantize", e0, e1))
+        if ev:
+            ev[0].record(stream)
+        K.kvq_quantize_pack(kd, kp, sh)
+        K.kvq_quantize_pack(vd, vp, sh)
+        if ev:
+            ev[1].record(stream)
         for i in range(nq):
             kp2, vp2 = copies[(c + i) % len(copies)]
-            a = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            K.kvq_decode_attn(kp2, vp2, w.Hq, 1, qd[i], None, 0.0, out, lse, ws, wsb, path=args.path or None)
-            b = torch.cuda.Event(enable_timing=True)
-            b.record(stream)
-            ev.append(("decode", a, b))
-        if record is not None:
-            record.extend(ev)
+            K.kvq_decode_attn(kp2, vp2, w.Hq, 1, q_ptrs[i], None, 0.0, out_p, lse_p, ws_p, wsb, sh, path)
+        if ev:
+            ev[2].record(stream)
 
     log(f"warmup {args.warmup} step(s)")
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
-    rec = []
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} step(s) of quantize+pack + {nq} decode calls")
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    for s in range(args.steps):
-        step(rec)
-    t_end.record(stream)
+    for s_ in range(args.steps):
+        step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms = evs[0][0].elapsed_time(evs[-1][2])
     ms_step = total_ms / args.steps
-    qz = [a.elapsed_time(b) for k, a, b in rec if k == "quantize"]
-    dc = [a.elapsed_time(b) for k, a, b in rec if k == "decode"]
-    qz_ms, dc_ms = float(np.mean(qz)), float(np.mean(dc))
+    qz_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) / nq
     log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.1f} ms); quantize {qz_ms * 1e3:.1f} us; "
-        f"decode {dc_ms * 1e3:.1f} us")
+        f"decode {dc_ms * 1e3:.1f} us per call")
 
     value = nq * w.B / (ms_step * 1e-3)
     dec_gbs = d_bytes / (dc_ms * 1e-3) / 1e9
     qz_gbs = q_bytes / (qz_ms * 1e-3) / 1e9
-    fast = K.kvq_decode_attn_workspace is not None and args.path != 1
     rec_line = {
         "metric": "quantize+pack GB/s and packed decode-attn tok/s @64K; % of HBM peak",
         "value": round(value, 2),
@@ -239,7 +256,6 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for("decode", 1)},
     }
-    del fast
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         rec_line["cpu_baseline"] = cpu_baseline(Kx, Vx, q)

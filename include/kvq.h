@@ -155,7 +155,9 @@ kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void
  * (inverse codebook, inverse rotation, division by chan_scale). */
 kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream);
 
-/* Bytes of workspace kvq_decode_attn needs for these sizes. */
+/* Bytes of workspace kvq_decode_attn needs for these sizes (split-K partials;
+ * no initial contents are required).  Calls that share a workspace must not
+ * overlap in time. */
 size_t kvq_decode_attn_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q);
 
 /* Decode attention read back through packed K and V ([E22L] What I tested:
@@ -168,7 +170,10 @@ size_t kvq_decode_attn_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n
  * nullable.  K and V must have the same shape; V's codebook may not be an rFFT
  * codec.  ws: device workspace of at least kvq_decode_attn_workspace() bytes.
  * K dequantisation happens in registers/LDS: rotated keys are read by rotating
- * the query instead, rotated values by rotating the output once per query. */
+ * the query instead, rotated values by rotating the output once per query.
+ * Supported: every codebook for K, every non-rFFT codebook for V, head_dim
+ * 64/128/256, up to 8 query heads per KV head, kv_len batch*layers*n_q rows of
+ * at most 65535 per launch grid dimension. */
 kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
                            int32_t n_q, const uint16_t* q, const int32_t* kv_len,
                            float sm_scale, float* out, float* lse, void* ws,

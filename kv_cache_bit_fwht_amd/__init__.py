@@ -123,8 +123,13 @@ class Packed:
     chan_scale: object = None  # torch.float32 [L][H][D] or None
 
     def c(self) -> kvq_packed:
-        return kvq_packed(self.codec.c(), self.shape.c(), _ptr(self.codes), _ptr(self.scales),
-                          _ptr(self.mins), _ptr(self.chan_scale))
+        # cached: the tensors of a Packed are fixed once it is built
+        cs = self.__dict__.get("_cstruct")
+        if cs is None:
+            cs = kvq_packed(self.codec.c(), self.shape.c(), _ptr(self.codes), _ptr(self.scales),
+                            _ptr(self.mins), _ptr(self.chan_scale))
+            self.__dict__["_cstruct"] = cs
+        return cs
 
 
 def _ptr(t):

@@ -656,10 +656,11 @@ static int split_chunk(const kvq_shape& s, int S) {
   return c > 0 ? c : TB;
 }
 
+// Workspace of kvq_decode_attn: split partials of whichever kernel runs.
 size_t decode_ws_bytes(const kvq_shape& s, int Hq, int n_q) {
   const int S = decode_splits(s, Hq, n_q);
   const size_t gen = (size_t)s.batch * s.layers * n_q * Hq * S * (s.head_dim + 2) * sizeof(float);
-  const size_t fast = fast_ws_bytes(s, Hq, n_q);
+  const size_t fast = fast_part_bytes(s, Hq, n_q);
   return gen > fast ? gen : fast;
 }
 

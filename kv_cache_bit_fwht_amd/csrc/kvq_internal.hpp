@@ -177,7 +177,7 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st);
 hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st);
 bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st);
-size_t fast_ws_bytes(const kvq_shape& s, int Hq, int n_q);
+size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q);
 hipError_t launch_combine_partials(const AttnProblem& pr, int S, hipStream_t st);
 
 }  // namespace kvq

@@ -33,7 +33,7 @@ def _gpu_decode(K, kp, vp, q, kv_len, path=None):
     out = torch.empty((B, L, nq, Hq, D), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, L, nq, Hq), dtype=torch.float32, device="cuda:0")
     wsb = K.kvq_decode_attn_workspace(kp.shape, Hq, nq)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda:0")
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda:0")
     kl = to_dev(kv_len) if kv_len is not None else None
     K.kvq_decode_attn(kp, vp, Hq, nq, to_dev(q), kl, 0.0, out, lse, ws, wsb, path=path)
     torch.cuda.synchronize()
