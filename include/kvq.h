@@ -179,9 +179,13 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
                            float sm_scale, float* out, float* lse, void* ws,
                            size_t ws_bytes, void* stream);
 
-/* As kvq_decode_attn, choosing the kernel: path 0 = automatic, 1 = the general
- * kernel (every codec), 2 = the MFMA kernel (INT_ABSMAX K and V with group a
- * multiple of 32, head_dim 128/256; KVQ_ERR_UNSUPPORTED otherwise). */
+/* As kvq_decode_attn, choosing the kernel: path 0 = automatic (the MFMA kernel
+ * where it applies, else the general one), 1 = the general kernel (every codec
+ * above), 2 = the MFMA kernel, KVQ_ERR_UNSUPPORTED unless: head_dim 256, tokens
+ * a positive multiple of 32, at most 4 query heads per KV head, K INT_ABSMAX
+ * 4-bit at group 128 or 256 (any rotation, optional chan_scale), V INT_ABSMAX
+ * 2-bit at group 64..256 without chan_scale (any rotation) -- the 4-bit-key /
+ * 2-bit-value arms of [E22L] What I tested. */
 kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
                               int32_t n_q, const uint16_t* q, const int32_t* kv_len,
                               float sm_scale, float* out, float* lse, void* ws,

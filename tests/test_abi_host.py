@@ -1,0 +1,248 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/kvq.h declares, and its host-only calls (layouts, bit accounting,
+constant tables, argument validation) agree with the oracle and the header.
+
+Every call here either is host-only or is rejected by argument validation
+before anything is launched; no kernel runs.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE = 0, -1, -2, -3, -4
+FAKE = 0x10000            # a 16-byte-aligned non-null address; never dereferenced (validation fails first)
+FAKE_ODD = FAKE + 8       # 8-byte aligned only
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    import kv_cache_bit_fwht_amd as K
+    return K
+
+
+def test_library_exports_every_declared_entry_point(K):
+    declared = _declared()
+    assert len(declared) >= 13
+    lib = ctypes.CDLL(K.LIB_PATH)
+    missing = [n for n in declared if not hasattr(lib, n)]
+    assert not missing, f"declared in kvq.h but not exported: {missing}"
+    assert sorted(K.EXPORTS) == declared, "the Python binding must mirror the header one to one"
+
+
+def test_status_strings_and_version(K):
+    assert K.kvq_version().startswith("kvq")
+    for st in (OK, ERR_ARG, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, -5):
+        s = K.kvq_status_string(st)
+        assert s and s != K.kvq_status_string(12345)
+
+
+CODECS = [
+    O.Codec(O.FP16),
+    O.Codec(O.INT_ABSMAX, 2, 128),
+    O.Codec(O.INT_ABSMAX, 3, 32),
+    O.Codec(O.INT_ABSMAX, 4, 128, rot=256),
+    O.Codec(O.INT_ABSMAX, 4, 256, rot=128),
+    O.Codec(O.INT_MINMAX, 4, 64),
+    O.Codec(O.INT_MINMAX, 8, 16),
+    O.Codec(O.TERNARY, 0, 32),
+    O.Codec(O.SIGN, 0, 8),
+    O.Codec(O.NF4, 0, 64),
+    O.Codec(O.INT8_SYM, 0, 128),
+    O.Codec(O.RFFT_POLAR, 4, 32, aux_bits=8),
+    O.Codec(O.RFFT_CART, 3, 16),
+]
+
+
+def _valid_dims(c):
+    if c.codebook in (O.FP16, O.RFFT_POLAR, O.RFFT_CART):
+        return (64, 128, 256)
+    return tuple(D for D in (64, 128, 256) if c.group <= D and c.rot <= D)
+
+
+def _kcodec(K, c):
+    return K.Codec(c.codebook, c.bits, c.group, c.rot, c.aux_bits)
+
+
+@pytest.mark.parametrize("ci", range(len(CODECS)))
+def test_layout_and_bits_match_the_oracle(K, ci):
+    oc = CODECS[ci]
+    dims = _valid_dims(oc)
+    assert dims
+    for D in dims:
+        shape = K.Shape(1, 2, 3, 5, D)
+        assert K.kvq_packed_layout(shape, _kcodec(K, oc)) == O.layout(oc, D)
+        assert K.kvq_bits_per_value(_kcodec(K, oc), D) == pytest.approx(O.accounting.bits_per_value(oc, D), abs=0)
+
+
+def test_bits_per_value_of_the_pages_figures(K):
+    """The library's accounting against the figures the pages print (cited per
+    case in tests/golden/accounting.json)."""
+    import json
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "accounting.json")))["cases"]
+    names = {"int_absmax": K.INT_ABSMAX, "nf4": K.NF4}
+    for c in cases:
+        kc = K.Codec(names[c["k"][0]], c["k"][1], c["k"][2], 0)
+        vc = K.Codec(names[c["v"][0]], c["v"][1], c["v"][2], 0)
+        got = (K.kvq_bits_per_value(kc, c["D"]) + K.kvq_bits_per_value(vc, c["D"])) / 2
+        assert got == pytest.approx(c["bpv"]), c["cite"]
+
+
+def test_constant_tables_match_the_oracle(K):
+    np.testing.assert_array_equal(K.kvq_constant_table(0, 16), O.codec.nf4_levels().astype(np.float32))
+    np.testing.assert_array_equal(K.kvq_constant_table(1, 15), O.codec.nf4_midpoints().astype(np.float32))
+    for D in (64, 128, 256):
+        c, s = O.rfft.twiddles(D)
+        np.testing.assert_array_equal(K.kvq_constant_table(2, D // 2), c)
+        np.testing.assert_array_equal(K.kvq_constant_table(3, D // 2), s)
+    for P in (8, 16, 64, 256):
+        c, s = O.rfft.directions(P)
+        np.testing.assert_array_equal(K.kvq_constant_table(4, P), c)
+        np.testing.assert_array_equal(K.kvq_constant_table(5, P), s)
+        bc, bs = O.rfft.boundaries(P)
+        np.testing.assert_array_equal(K.kvq_constant_table(6, P // 8), bc)
+        np.testing.assert_array_equal(K.kvq_constant_table(7, P // 8), bs)
+
+
+@pytest.mark.parametrize("which,n", [(0, 15), (1, 16), (2, 3), (2, 256), (4, 4), (4, 512), (6, 0), (8, 4), (-1, 4)])
+def test_constant_table_rejects_bad_sizes(K, which, n):
+    out = np.zeros(max(n, 1), dtype=np.float32)
+    assert K._lib.kvq_constant_table(which, n, out.ctypes.data) == ERR_ARG
+
+
+@pytest.mark.parametrize("codec,D,status", [
+    ((1, 4, 96, 0, 0), 128, ERR_UNSUPPORTED),       # group not a power of two
+    ((1, 4, 4, 0, 0), 128, ERR_UNSUPPORTED),        # group below 8
+    ((1, 4, 256, 0, 0), 128, ERR_UNSUPPORTED),      # group above head_dim
+    ((1, 1, 32, 0, 0), 128, ERR_UNSUPPORTED),       # 1-bit INT_ABSMAX
+    ((2, 9, 32, 0, 0), 128, ERR_UNSUPPORTED),       # 9-bit INT_MINMAX
+    ((1, 4, 32, 48, 0), 128, ERR_UNSUPPORTED),      # rotation width not a power of two
+    ((1, 4, 32, 512, 0), 256, ERR_UNSUPPORTED),     # rotation wider than head_dim
+    ((7, 4, 32, 0, 2), 128, ERR_UNSUPPORTED),       # polar rFFT with 4 phase sectors
+    ((8, 4, 32, 64, 0), 128, ERR_UNSUPPORTED),      # rFFT codecs take no rotation
+    ((9, 4, 32, 0, 0), 128, ERR_UNSUPPORTED),       # no such codebook
+])
+def test_layout_rejects_invalid_codecs(K, codec, D, status):
+    c = K.kvq_codec(*codec)
+    s = K.kvq_shape(1, 1, 1, 4, D)
+    w, ns, nm = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert K._lib.kvq_packed_layout(ctypes.byref(s), ctypes.byref(c), ctypes.byref(w), ctypes.byref(ns),
+                                    ctypes.byref(nm)) == status
+    assert K._lib.kvq_bits_per_value(ctypes.byref(c), D) < 0
+
+
+@pytest.mark.parametrize("shape,status", [
+    ((1, 1, 1, 4, 96), ERR_UNSUPPORTED),   # head_dim must be 64, 128 or 256
+    ((0, 1, 1, 4, 128), ERR_ARG),
+    ((1, 1, 1, -1, 128), ERR_ARG),
+])
+def test_layout_rejects_invalid_shapes(K, shape, status):
+    c = K.kvq_codec(1, 4, 32, 0, 0)
+    s = K.kvq_shape(*shape)
+    w, ns, nm = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert K._lib.kvq_packed_layout(ctypes.byref(s), ctypes.byref(c), ctypes.byref(w), ctypes.byref(ns),
+                                    ctypes.byref(nm)) == status
+
+
+def _packed(K, codec=(1, 4, 128, 256, 0), shape=(1, 2, 4, 64, 256), codes=FAKE, scales=FAKE, mins=None):
+    return K.kvq_packed(K.kvq_codec(*codec), K.kvq_shape(*shape), codes, scales, mins, None)
+
+
+def test_quantize_and_dequant_validate_before_launching(K):
+    L = K._lib
+    p = _packed(K)
+    assert L.kvq_quantize_pack(None, ctypes.byref(p), None) == ERR_ARG
+    assert L.kvq_quantize_pack(FAKE_ODD, ctypes.byref(p), None) == ERR_ALIGN
+    assert L.kvq_dequant(ctypes.byref(p), None, None) == ERR_ARG
+    assert L.kvq_dequant(ctypes.byref(p), FAKE_ODD, None) == ERR_ALIGN
+    assert L.kvq_quantize_pack(FAKE, ctypes.byref(_packed(K, codes=FAKE_ODD)), None) == ERR_ALIGN
+    assert L.kvq_quantize_pack(FAKE, ctypes.byref(_packed(K, codes=None)), None) == ERR_ARG
+    assert L.kvq_quantize_pack(FAKE, ctypes.byref(_packed(K, scales=None)), None) == ERR_ARG
+    # INT_MINMAX needs its mins array
+    assert L.kvq_quantize_pack(FAKE, ctypes.byref(_packed(K, codec=(2, 4, 64, 0, 0))), None) == ERR_ARG
+    assert L.kvq_quantize_pack(FAKE, None, None) == ERR_ARG
+    # per-channel key calibration takes batch 1 only
+    s2 = K.kvq_shape(2, 1, 1, 8, 128)
+    assert L.kvq_calibrate_chan_scale(FAKE, ctypes.byref(s2), FAKE, None) == ERR_ARG
+
+
+def _decode(K, k, v, q_heads=16, n_q=1, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=None, path=0, sm=0.0, lse=None):
+    if ws_bytes is None:
+        ws_bytes = K._lib.kvq_decode_attn_workspace(ctypes.byref(k.shape), q_heads, n_q)
+    return K._lib.kvq_decode_attn_ex(ctypes.byref(k), ctypes.byref(v), q_heads, n_q, q, None, sm, out, lse,
+                                     ws, ws_bytes, path, None)
+
+
+def test_decode_validates_before_launching(K):
+    k = _packed(K)
+    v = _packed(K, codec=(1, 2, 128, 0, 0))
+    need = K._lib.kvq_decode_attn_workspace(ctypes.byref(k.shape), 16, 1)
+    assert need > 0
+    assert _decode(K, k, v, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert _decode(K, k, v, ws=None) == ERR_WORKSPACE
+    assert _decode(K, k, v, q=None) == ERR_ARG
+    assert _decode(K, k, v, q=FAKE_ODD) == ERR_ALIGN
+    assert _decode(K, k, v, out=None) == ERR_ARG
+    assert _decode(K, k, v, lse=FAKE_ODD) == ERR_ALIGN
+    assert _decode(K, k, v, ws=FAKE_ODD) == ERR_ALIGN
+    assert _decode(K, k, v, path=3) == ERR_ARG
+    assert _decode(K, k, v, sm=-1.0) == ERR_ARG
+    assert _decode(K, k, v, sm=float("nan")) == ERR_ARG
+    assert _decode(K, k, v, q_heads=6) == ERR_UNSUPPORTED          # not a multiple of the 4 KV heads
+    assert _decode(K, k, v, q_heads=36) == ERR_UNSUPPORTED         # 9 query heads per KV head
+    assert _decode(K, k, v, n_q=0) == ERR_ARG
+    # K and V must have the same shape; V may not use an rFFT codec
+    v_other = _packed(K, codec=(1, 2, 128, 0, 0), shape=(1, 2, 4, 32, 256))
+    assert _decode(K, k, v_other) == ERR_ARG
+    v_rfft = _packed(K, codec=(7, 4, 32, 0, 8))
+    assert _decode(K, k, v_rfft) == ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("case", ["tokens_not_mult_32", "head_dim_128", "k_3bit", "v_group_32",
+                                  "k_minmax", "v_chan_scale", "g8"])
+def test_mfma_path_rejects_what_it_does_not_cover(K, case):
+    kc, vc, shape, q_heads = (1, 4, 128, 256, 0), (1, 2, 128, 0, 0), (1, 2, 4, 64, 256), 16
+    v_chan = None
+    if case == "tokens_not_mult_32":
+        shape = (1, 2, 4, 100, 256)
+    elif case == "head_dim_128":
+        shape = (1, 2, 4, 64, 128)
+        kc = (1, 4, 128, 128, 0)
+    elif case == "k_3bit":
+        kc = (1, 3, 128, 256, 0)
+    elif case == "v_group_32":
+        vc = (1, 2, 32, 0, 0)
+    elif case == "k_minmax":
+        kc = (2, 4, 128, 0, 0)
+    elif case == "v_chan_scale":
+        v_chan = FAKE
+    elif case == "g8":
+        q_heads = 32
+    k = _packed(K, codec=kc, shape=shape, mins=FAKE if kc[0] == 2 else None)
+    v = _packed(K, codec=vc, shape=shape)
+    if v_chan is not None:
+        v.chan_scale = v_chan
+    assert _decode(K, k, v, q_heads=q_heads, path=2) == ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_cover_the_decode_partials(K):
+    # one fp32 partial of head_dim + 2 values per (row, query head, split) at least
+    s = K.kvq_shape(1, 8, 4, 65536, 256)
+    ws = K._lib.kvq_decode_attn_workspace(ctypes.byref(s), 16, 1)
+    assert ws >= 8 * 16 * 2 * 258 * 4
+    assert ws % 256 == 0 or ws > 0
+    assert K._lib.kvq_decode_attn_workspace(ctypes.byref(s), 0, 1) == 0
+    assert K._lib.kvq_attn_error_workspace(ctypes.byref(s), 16, 1) > 0
