@@ -236,10 +236,204 @@ static int grid_for(long long rows, int lpt_log2) {
       }                                                                                          \
   }
 
+
+// ------------------------------------------------------------------ signed absmax, head_dim 256
+// A leaner path for the signed-absmax codebook at head_dim 256 with rotation 0 or
+// 256, group >= 16 and 2, 4 or 8 bits (the keys and values of the 64K decode
+// workload).  Same arithmetic, same results as k_quantize, fewer instructions:
+//  * a row is held by 16 lanes of one wavefront, so the FWHT's transposes through
+//    LDS are wavefront-local and need no barrier; the contiguous side moves 16 bytes
+//    per access (quads XOR-swizzled by lane, so the strided side is conflict-free);
+//  * the 2^-4 normalisation of the 256-point transform is a power of two: scaling by
+//    it is exact, so it is folded into the scale and its inverse instead of being
+//    applied to every value (u * 2^-4 never underflows for fp16-derived values);
+//  * the code is RN32(RN32(u * inv) + (1.5 * 2^23 + 2^(b-1))): in [2^23, 2^24) the ulp
+//    is 1, so that addition performs the round-to-nearest-even, and the integer sits
+//    in the low bits of the result (bits b..21 zero after clamping), ready to pack.
+constexpr int kRowLds = 256 + 16;                    // LDS floats per row (padding spreads banks)
+
+// Quads of rows q_first, q_first + q_stride, ... of one tensor; each wavefront of the
+// caller owns one quad per step (16 lanes per row).
+template <int BITS, bool ROT>
+__device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first, long long q_stride,
+                                               float* rl, int lane) {
+  constexpr int D = 256;
+  constexpr float kFold = ROT ? 0.0625f : 1.0f;      // the 256-point transform's 1/sqrt(256)
+  constexpr float neg_step = -kFold / (float)(1 << (BITS - 1));
+  constexpr uint32_t kMagic = 0x4B400000u;           // bit pattern of 1.5 * 2^23
+  constexpr float kBias = 12582912.0f + (float)(1 << (BITS - 1));
+  const int j = lane & 15;                           // lane within the row
+  const int lpg = a.g >> 4;                          // lanes per group
+  const long long nquads = (a.rows + 3) >> 2;
+  for (long long qd = q_first; qd < nquads; qd += q_stride) {
+    const long long row = qd * 4 + (lane >> 4);
+    const bool active = row < a.rows;
+    uint4 p0 = make_uint4(0, 0, 0, 0), p1 = p0;
+    if (active) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)row * D + 16 * j);
+      p0 = src[0];
+      p1 = src[1];
+    }
+    const uint32_t raw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[2 * k] = h2f((uint16_t)(raw[k] & 0xffffu));
+      v[2 * k + 1] = h2f((uint16_t)(raw[k] >> 16));
+    }
+    if (a.chan != nullptr && active) {
+      int l, h;
+      row_unit(row, a.T, a.H, a.L, l, h);
+      const float4* cp = reinterpret_cast<const float4*>(a.chan + ((size_t)l * a.H + h) * D + 16 * j);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 cc = cp[k];
+        v[4 * k] = v[4 * k] * cc.x;
+        v[4 * k + 1] = v[4 * k + 1] * cc.y;
+        v[4 * k + 2] = v[4 * k + 2] * cc.z;
+        v[4 * k + 3] = v[4 * k + 3] * cc.w;
+      }
+    }
+    if constexpr (ROT) {
+      // strides 1, 2, 4, 8: inside the lane's 16 consecutive values
+#pragma unroll
+      for (int s = 1; s < 16; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (!(i & s)) {
+            const float x = v[i], y = v[i + s];
+            v[i] = x + y;
+            v[i + s] = x - y;
+          }
+      }
+      // transpose: lane j takes values j + 16 r (r = 0..15); quads of a lane's values sit
+      // at quad index (q ^ (owner & 3)) of the owner's 16-float slot
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(rl + 16 * j + 4 * (q ^ (j & 3))) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = rl[16 * r + 4 * ((j >> 2) ^ (r & 3)) + (j & 3)];
+      // strides 16, 32, 64, 128: pairs (r, r + rs) of the transposed values
+#pragma unroll
+      for (int rs = 1; rs < 16; rs <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (!(i & rs)) {
+            const float x = v[i], y = v[i + rs];
+            v[i] = x + y;
+            v[i + rs] = x - y;
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rl[16 * r + 4 * ((j >> 2) ^ (r & 3)) + (j & 3)] = v[r];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = *reinterpret_cast<const float4*>(rl + 16 * j + 4 * (q ^ (j & 3)));
+        v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+      }
+    }
+    // group statistic: the signed extreme of the group (lpg lanes)
+    float mx = v[0], mn = v[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      mx = __builtin_fmaxf(mx, v[i]);
+      mn = __builtin_fminf(mn, v[i]);
+    }
+    for (int m = 1; m < lpg; m <<= 1) {
+      mx = xor_max(mx, m);
+      mn = xor_min(mn, m);
+    }
+    const float ext = (-mn >= mx) ? mn : mx;
+    const uint16_t s16 = rn16(ext * neg_step);       // exact product: neg_step is a power of two
+    const float inv = inv_scale(s16) * kFold;        // exact: kFold is a power of two
+    uint32_t c[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float f = __fadd_rn(__fmul_rn(v[i], inv), kBias);
+      const int b = (int)__builtin_bit_cast(uint32_t, f);
+      c[i] = (uint32_t)min(max(b, (int)kMagic), (int)(kMagic + (1u << BITS) - 1u));
+    }
+    if (!active) continue;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + (size_t)row * (D * BITS / 8) + (size_t)j * 2 * BITS;
+    if constexpr (BITS == 4) {
+      uint32_t w[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t t0 = (c[8 * k + 1] << 4) | c[8 * k + 0], t1 = (c[8 * k + 3] << 4) | c[8 * k + 2];
+        const uint32_t t2 = (c[8 * k + 5] << 4) | c[8 * k + 4], t3 = (c[8 * k + 7] << 4) | c[8 * k + 6];
+        const uint32_t h0 = __builtin_amdgcn_perm(t1, t0, 0x0C0C0400u);
+        const uint32_t h1 = __builtin_amdgcn_perm(t3, t2, 0x0C0C0400u);
+        w[k] = (h1 << 16) | h0;
+      }
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    } else if constexpr (BITS == 2) {
+      uint32_t by[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = (c[4 * k + 1] << 2) | c[4 * k + 0], hi = (c[4 * k + 3] << 2) | c[4 * k + 2];
+        by[k] = (hi << 4) | lo;
+      }
+      const uint32_t h0 = __builtin_amdgcn_perm(by[1], by[0], 0x0C0C0400u);
+      const uint32_t h1 = __builtin_amdgcn_perm(by[3], by[2], 0x0C0C0400u);
+      *reinterpret_cast<uint32_t*>(dst) = (h1 << 16) | h0;
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t h0 = __builtin_amdgcn_perm(c[4 * k + 1], c[4 * k + 0], 0x0C0C0400u);
+        const uint32_t h1 = __builtin_amdgcn_perm(c[4 * k + 3], c[4 * k + 2], 0x0C0C0400u);
+        w[k] = (h1 << 16) | h0;
+      }
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    if ((j & (lpg - 1)) == 0) a.scales[(size_t)row * (D / a.g) + j / lpg] = s16;
+  }
+}
+
+template <int BITS, bool ROT>
+__global__ __launch_bounds__(kBlock) void k_quantize_absmax256(QArgs a) {
+  __shared__ float lds[kBlock / 16][kRowLds];
+  const int tid = threadIdx.x;
+  constexpr int waves = kBlock / 64;
+  absmax256_rows<BITS, ROT>(a, (long long)blockIdx.x * waves + (tid >> 6), (long long)gridDim.x * waves,
+                            lds[tid >> 4], tid & 63);
+}
+
+static bool absmax256_supported(const kvq_packed& p) {
+  const kvq_codec& c = p.codec;
+  if (c.codebook != KVQ_INT_ABSMAX || p.shape.head_dim != 256) return false;
+  if (c.bits != 2 && c.bits != 4 && c.bits != 8) return false;
+  if (c.group < 16 || c.group > 256) return false;
+  return c.rot_width <= 1 || c.rot_width == 256;
+}
+
+static long long absmax256_blocks(long long rows) {
+  const long long quads = (rows + 3) / 4;
+  long long blocks = (quads + (kBlock / 64) - 1) / (kBlock / 64);
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  return blocks < 1 ? 1 : blocks;
+}
+
+static void launch_absmax256(const QArgs& a, const kvq_codec& c, hipStream_t st) {
+  const dim3 grid((unsigned)absmax256_blocks(a.rows));
+  const bool rot = c.rot_width == 256;
+  if (c.bits == 2) rot ? k_quantize_absmax256<2, true><<<grid, kBlock, 0, st>>>(a)
+                       : k_quantize_absmax256<2, false><<<grid, kBlock, 0, st>>>(a);
+  else if (c.bits == 4) rot ? k_quantize_absmax256<4, true><<<grid, kBlock, 0, st>>>(a)
+                            : k_quantize_absmax256<4, false><<<grid, kBlock, 0, st>>>(a);
+  else rot ? k_quantize_absmax256<8, true><<<grid, kBlock, 0, st>>>(a)
+           : k_quantize_absmax256<8, false><<<grid, kBlock, 0, st>>>(a);
+}
+
 hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st) {
   QArgs a = make_args(p);
   a.x = x;
   if (a.rows == 0) return hipSuccess;
+  if (absmax256_supported(p)) {
+    launch_absmax256(a, p.codec, st);
+    return hipGetLastError();
+  }
   const dim3 grid(grid_for(a.rows, a.lpt_log2)), block(kBlock);
   KVQ_DISPATCH_CODEC(p.codec.codebook, p.codec.bits, k_quantize, <<<grid, block, 0, st>>>(a))
   return hipGetLastError();

@@ -79,7 +79,7 @@ def test_quantize_pack_bit_exact(D, cspec):
     _compare(K, x, codec)
 
 
-@pytest.mark.parametrize("arm", ["C", "D"])
+@pytest.mark.parametrize("arm", ["C", "D", "D4"])
 def test_prescaled_keys_bit_exact(arm):
     """E21W arms C/D: per-channel K scaling calibrated on sequence 0."""
     import kv_cache_bit_fwht_amd as K
@@ -92,7 +92,8 @@ def test_prescaled_keys_bit_exact(arm):
     torch.cuda.synchronize()
     c_ref = O.calibrate_chan_scale(Kx[0])
     assert np.array_equal(to_np(cal), c_ref)
-    codec = K.Codec(K.INT_MINMAX, 3, 32, 0) if arm == "C" else K.Codec(K.INT_ABSMAX, 3, 32, 256)
+    codec = {"C": K.Codec(K.INT_MINMAX, 3, 32, 0), "D": K.Codec(K.INT_ABSMAX, 3, 32, 256),
+             "D4": K.Codec(K.INT_ABSMAX, 4, 32, 256)}[arm]
     _compare(K, Kx, codec, c_ref)
 
 
