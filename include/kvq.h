@@ -155,9 +155,12 @@ kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void
  * (inverse codebook, inverse rotation, division by chan_scale). */
 kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream);
 
-/* Bytes of workspace kvq_decode_attn needs for these sizes (split-K partials;
- * no initial contents are required).  Calls that share a workspace must not
- * overlap in time. */
+/* Bytes of workspace kvq_decode_attn needs for these sizes.  Its first 65536
+ * bytes hold the MFMA kernel's work counters: they must be zero before the
+ * first call that uses the workspace (fill it with zeros once after
+ * allocating it), and every call leaves them zero again.  The rest holds
+ * split-K partials and needs no initial contents.  Calls that share a
+ * workspace must not overlap in time. */
 size_t kvq_decode_attn_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q);
 
 /* Decode attention read back through packed K and V ([E22L] What I tested:

@@ -295,7 +295,7 @@ static kvq_status check_attn(const kvq_packed* k, const kvq_packed* v, int32_t q
 
 size_t kvq_decode_attn_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q) {
   if (check_shape(kv) != KVQ_OK || q_heads < 1 || n_q < 1) return 0;
-  return decode_ws_bytes(*kv, q_heads, n_q);
+  return kWsCounterBytes + decode_ws_bytes(*kv, q_heads, n_q);
 }
 
 kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
@@ -307,7 +307,7 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
   if (!aligned16(out) || (lse && !aligned16(lse)) || (kv_len && !aligned16(kv_len))) return KVQ_ERR_ALIGN;
   if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
   if (path < 0 || path > 2) return KVQ_ERR_ARG;
-  const size_t need = decode_ws_bytes(k->shape, q_heads, n_q);
+  const size_t need = kWsCounterBytes + decode_ws_bytes(k->shape, q_heads, n_q);
   if (ws_bytes < need || (need && !ws)) return KVQ_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return KVQ_ERR_ALIGN;
   const bool fast_ok = fast_decode_supported(*k, *v, q_heads);
@@ -315,7 +315,10 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
   AttnProblem pr{};
   pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
   pr.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)k->shape.head_dim));
-  pr.out = out; pr.lse = lse; pr.ws = ws; pr.ws_bytes = ws_bytes;
+  pr.out = out; pr.lse = lse;
+  pr.ctr = static_cast<int*>(ws);
+  pr.ws = static_cast<char*>(ws) + kWsCounterBytes;
+  pr.ws_bytes = ws_bytes - kWsCounterBytes;
   if (k->shape.tokens == 0) {
     // no keys: zero output, lse = -inf (handled by the generic kernel's combine)
   }
@@ -332,7 +335,7 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
 
 size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q) {
   if (check_shape(kv) != KVQ_OK || q_heads < 1 || n_q < 1) return 0;
-  return error_ws_bytes(*kv, q_heads, n_q);
+  return kWsCounterBytes + error_ws_bytes(*kv, q_heads, n_q);
 }
 
 kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16, const kvq_packed* k,
@@ -346,14 +349,16 @@ kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16, const 
       !aligned16(kv_err) || (kv_len && !aligned16(kv_len)))
     return KVQ_ERR_ALIGN;
   if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
-  const size_t need = error_ws_bytes(k->shape, q_heads, n_q);
+  const size_t need = kWsCounterBytes + error_ws_bytes(k->shape, q_heads, n_q);
   if (ws_bytes < need || (need && !ws)) return KVQ_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return KVQ_ERR_ALIGN;
   AttnProblem pr{};
   pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
   pr.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)k->shape.head_dim));
   pr.k16 = k_fp16; pr.v16 = v_fp16; pr.kl = kl_rows; pr.relerr = relerr_rows; pr.kv_err = kv_err;
-  pr.ws = ws; pr.ws_bytes = ws_bytes;
+  pr.ctr = nullptr;                                  // same layout as decode; no counters used
+  pr.ws = static_cast<char*>(ws) + kWsCounterBytes;
+  pr.ws_bytes = ws_bytes - kWsCounterBytes;
   return hip_status(launch_attn_error(pr, (hipStream_t)stream));
 }
 

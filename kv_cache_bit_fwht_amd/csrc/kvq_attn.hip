@@ -401,6 +401,7 @@ struct CArgs {
   int vW;
   float vkappa;
   const float* vchan;
+  int* ctr;             // decode chunk counters to set back to zero, or null
 };
 
 template <bool ERR>
@@ -491,6 +492,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(CArgs a, float* out, fl
   if (!ERR) {
     if (tid < D) out[(size_t)rh * D + tid] = o;
     if (tid == 0 && lse) lse[rh] = (Lq > 0.0) ? (float)(M + log(Lq)) : -INFINITY;
+    if (tid == 0 && a.ctr && j % a.G == 0) a.ctr[rq * a.H + h] = 0;   // ready for the next call
     return;
   }
   // relative error of the quantised output against the fp16 one, and KL
@@ -726,7 +728,7 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
   k_attn_split<false><<<dim3(a.S, a.H, (unsigned)R), kBlock, smem, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_combine_partials(pr, a.S, st);
+  return launch_combine_partials(pr, a.S, nullptr, st);
 }
 
 static CArgs make_cargs(const AttnProblem& pr, int S, float* ws) {
@@ -746,10 +748,11 @@ static CArgs make_cargs(const AttnProblem& pr, int S, float* ws) {
   return c;
 }
 
-hipError_t launch_combine_partials(const AttnProblem& pr, int S, hipStream_t st) {
+hipError_t launch_combine_partials(const AttnProblem& pr, int S, int* ctr, hipStream_t st) {
   const kvq_shape& s = pr.k->shape;
   const long long R = (long long)s.batch * s.layers * pr.n_q;
-  const CArgs c = make_cargs(pr, S, static_cast<float*>(pr.ws));
+  CArgs c = make_cargs(pr, S, static_cast<float*>(pr.ws));
+  c.ctr = ctr;
   k_attn_combine<false><<<(unsigned)(R * pr.Hq), kBlock, 0, st>>>(c, pr.out, pr.lse, nullptr, nullptr);
   return hipGetLastError();
 }

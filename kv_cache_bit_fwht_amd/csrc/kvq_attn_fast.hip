@@ -26,10 +26,12 @@
 //    four accumulators per byte hold prefix sums of its fields weighted 1, 4,
 //    16, 64 and the fields come out as differences after the loop.
 //    Output: 2^24 * field - 2 * sum of the weights per group.
-// A block of 8 wavefronts (two per SIMD) covers one token range of one (query,
-// KV head) and hands its steps out from an LDS counter; it merges its
-// wavefronts and writes one (o, m, l) partial, and the general combine kernel
-// merges the blocks and rotates rotated values back.
+// Several blocks of 8 wavefronts (two per SIMD) share the tokens of one (query,
+// KV head): each block claims chunks of steps from a device-wide counter of the
+// unit and hands their steps to its wavefronts from an LDS counter, then merges
+// its wavefronts into one (o, m, l) partial.  The unit's last block to finish
+// merges the partials into the output; with rotated values, or with more units
+// than the workspace has counters for, a separate kernel does that merge.
 #include <cmath>
 
 #include "kvq_internal.hpp"
@@ -47,6 +49,8 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 constexpr int kFastD = 256;
 constexpr int kStep = 32;          // tokens per wavefront step
 constexpr int kFastBlock = 512;    // threads per block: two wavefronts per SIMD
+constexpr int kMaxChunks = 256;    // chunks per (query row, KV head) at most
+constexpr int kMaxSlots = kMaxChunks + 4;
 
 struct FArgs {
   const uint8_t* kc;               // key codes, 128 B per row
@@ -63,6 +67,11 @@ struct FArgs {
   float kkappa;
   float sm_scale;
   int blocks_per_unit;             // blocks (and partials) per (query row, KV head)
+  int chunk_log2;                  // log2 of the 32-token steps per chunk (>= 4)
+  int* ctr;                        // per (query row, KV head) chunk counters, or null (static chunks)
+  int* done;                       // per (query row, KV head) finished-block counters, or null (separate merge)
+  float* out;                      // merged output and log-sum-exp, written when done is set
+  float* lse;
 };
 
 __device__ __forceinline__ uint32_t h2bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
@@ -148,6 +157,12 @@ __device__ __forceinline__ uint32_t row_bcast(uint32_t x, int j) {
   }
 }
 
+// x + (x of the lane 4 places along in the same row of 16, cyclically): joins the
+// high- and low-part logits of a query head, which sit in columns n and n ^ 4.
+__device__ __forceinline__ float add_row_ror4(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
+}
+
 // fp16 value scales of tokens 8kg + k and 8kg + k + 1 (k constant) in this lane's
 // value group, packed low/high.  vsel picks the group's half of a scale word and the
 // all-ones mask vhi the second word of a pair (four groups per row).
@@ -168,6 +183,27 @@ __device__ __forceinline__ uint32_t vscale_pair(const uint32_t* vs, int k, uint3
   return __builtin_amdgcn_perm(w1, w0, vsel);
 }
 
+// Adds 1 to a device-wide counter from lane 0 alone and returns the old value to
+// the whole wavefront.  Same-address atomics from several lanes are serialised at
+// the memory side, so the other lanes are masked off for the one instruction;
+// the result is waited for inside the block, as its register is written late.
+// Needs every lane of the wavefront active.
+__device__ __forceinline__ int claim_global(int* ctr) {
+  int old = 0;
+  unsigned long long saved;
+  asm volatile(
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %0, %2, %3, off sc0\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "s_mov_b64 exec, %1\n\t"
+      "s_nop 4"
+      : "+v"(old), "=&s"(saved)
+      : "v"(ctr), "v"(1)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(old);
+}
+
 // One block per (unit, token range, query): 8 wavefronts, two per SIMD.  The two
 // wavefronts that share a SIMD do not run at the same speed (the older one is
 // issued first), so the block's 32-token steps are handed out dynamically from an
@@ -176,11 +212,12 @@ template <int NKS, int NVS>
 __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   constexpr int NW = kFastBlock / 64;                // wavefronts per block
   __shared__ float qs[4][kFastD + 16];
-  __shared__ float qsum_s[4][2];
+  __shared__ float qsum_s[2][4][2];                 // [part][head][key group] sums of the MFMA query operand
   __shared__ float so[NW][4][kFastD];               // per-wave outputs [wave][head][dim]
   __shared__ float sm[NW][4], sl[NW][4];            // per-wave reference max (log2 units) and sum
-  __shared__ half8_t qbs[8][16];                     // MFMA B operands [chunk][4 kg + head]
-  __shared__ int next_step;                          // next step of the block not yet handed out
+  __shared__ half8_t qbs[8][32];                     // MFMA B operands [chunk][16 part + 4 kg + head]
+  __shared__ int next_local;                         // next step index of the block not yet handed out
+  __shared__ int slot_chunk[kMaxSlots];              // chunk of each slot of C local indices (-1 = not yet known)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront-uniform
   const int kg = lane >> 4, n16 = lane & 15;
@@ -194,23 +231,33 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   int n = a.T;
   if (a.kv_len) n = min(max(a.kv_len[rq], 0), a.T);
 
-  // ---- token range of this block and its steps
+  // ---- steps.  The unit's 32-token steps are grouped in chunks of C = 2^chunk_log2.
+  // Block x starts on chunk x; every further chunk comes from a counter shared by the
+  // unit's blocks (which sit on different XCDs, whose speeds differ from run to run),
+  // or, without counters, is chunk x + s * bpu for the block's slot s.  Inside the
+  // block, wavefronts take local step indices from an LDS counter: index k is step
+  // (k mod C) of the chunk of slot k / C.  Chunks are claimed one slot ahead by the
+  // wavefront that takes a slot's first index, and only after that slot's own chunk is
+  // known, so a block's chunks increase with the slot: once a slot holds the end
+  // marker every later one does too.
   const int bpu = a.blocks_per_unit;
-  const int per_block = ((a.T + bpu - 1) / bpu + kStep - 1) / kStep * kStep;   // tokens per block
-  const int t_begin = blockIdx.x * per_block;
-  const int t_end = min(t_begin + per_block, n);
-  const int nsteps = (t_end > t_begin) ? (t_end - t_begin + kStep - 1) / kStep : 0;
+  const int x = blockIdx.x;
+  const int cl2 = a.chunk_log2;
+  const int t_end = n;                               // tokens >= t_end are masked
+  const int total_steps = (n + kStep - 1) / kStep;
+  const int total_chunks = (total_steps + (1 << cl2) - 1) >> cl2;
+  int* const ctr = a.ctr ? a.ctr + (rq * a.H + h) : nullptr;
   const size_t row0 = (size_t)unit * a.T;
   const int vgrp = (16 * n16) / a.gv;                // scale group of this lane's value word
   const uint32_t vsel = (NVS > 1 && (vgrp & 1)) ? 0x07060302u : 0x05040100u;
   const uint32_t vhi = (NVS == 4 && (vgrp & 2)) ? 0xFFFFFFFFu : 0u;
-  auto step_tok = [&](int j) { return t_begin + j * kStep; };   // first token of local step j
-  // first row of local step j, clamped into the block's steps: a step past the end stands
-  // for the last one (loads of it are discarded), and a block without steps reads the
-  // unit's first rows, which always exist
-  auto step_row = [&](int j) -> size_t {
-    return row0 + (nsteps > 0 ? step_tok(max(min(j, nsteps - 1), 0)) : 0);
+  // first row of step s; a refill past the end re-reads the wavefront's last valid step
+  // (an L2 hit), and a wavefront that never had a step reads the unit's first rows
+  auto step_row = [&](int s, int last) -> size_t {
+    return row0 + (size_t)(s >= 0 ? s : (last >= 0 ? last : 0)) * kStep;
   };
+  int claim1 = 0;                                    // slot 1's chunk (counter value), fetched early
+  if (ctr && tid == 0) claim1 = atomicAdd(ctr, 1);
 
   // The query is read first so that the prologue waits for it alone; each wavefront's
   // first two steps (w and w + NW, handed out statically) are loaded right after it and
@@ -222,10 +269,13 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   float2_t kch = float2_t{1.0f, 1.0f};               // key channel scales of those dims
   if (a.kchan) kch = *reinterpret_cast<const float2_t*>(a.kchan + ((size_t)l * a.H + h) * kFastD + 2 * (tid & 127));
   const LaneOffsets lofs = lane_offsets<NKS, NVS>(kg, n16);
-  int i0 = wave, i1 = wave + NW;                     // steps held by the two buffers
+  // local indices wave and wave + NW of slot 0 (chunk x, C >= 16) are handed out statically
+  auto first_step = [&](int k) { return (x < total_chunks && (x << cl2) + k < total_steps) ? (x << cl2) + k : -1; };
+  int i0 = first_step(wave), i1 = first_step(wave + NW);   // steps held by the two buffers (-1: none)
+  int last = i1 >= 0 ? i1 : i0;                       // the wavefront's latest valid step
   StepData<NVS> b0, b1;
-  load_step<NKS, NVS>(a, step_row(i0), lofs, b0);
-  load_step<NKS, NVS>(a, step_row(i1), lofs, b1);
+  load_step<NKS, NVS>(a, step_row(i0, last), lofs, b0);
+  load_step<NKS, NVS>(a, step_row(i1, last), lofs, b1);
 
   // ---- query prologue: q in the key coordinates (divide channel scale, rotate), fp32 in LDS
   {
@@ -238,8 +288,14 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     qs[g][d0] = x0;
     qs[g][d0 + 1] = x1;
   }
-  if (tid == 0) next_step = 2 * NW;
+  for (int k = tid; k < kMaxSlots; k += kFastBlock) slot_chunk[k] = -1;
+  if (tid == 0) next_local = 2 * NW;
   __syncthreads();
+  if (tid == 0) {
+    slot_chunk[0] = min(x, total_chunks);
+    const int c1 = ctr ? bpu + claim1 : x + bpu;
+    slot_chunk[1] = x < total_chunks ? min(c1, total_chunks) : total_chunks;
+  }
   if (a.kW > 1) {
     for (int ls = 0; (1 << ls) < a.kW; ++ls) {
       const int s = 1 << ls;
@@ -253,49 +309,52 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     for (int p = tid; p < 4 * kFastD; p += kFastBlock) qs[p >> 8][p & 255] *= a.kkappa;
     __syncthreads();
   }
-  if (wave < 4) {  // per-group sums of the fp16 query (wave w: head w): sum_g q for the (c - 8) offset folding
-    float s0 = (float)(_Float16)qs[wave][2 * lane] + (float)(_Float16)qs[wave][2 * lane + 1];
-    float s1 = (float)(_Float16)qs[wave][128 + 2 * lane] + (float)(_Float16)qs[wave][128 + 2 * lane + 1];
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      s0 += __shfl_xor(s0, m);
-      s1 += __shfl_xor(s1, m);
-    }
-    if (lane == 0) { qsum_s[wave][0] = s0; qsum_s[wave][1] = s1; }
-  }
   // B operands: chunk c < 4 -> key word 4kg + c (dims 8w..8w+7, group 0), c >= 4 -> word 16 + 4kg + (c-4).
   // Register order of the 8 k-slots: dims (0,4), (1,5)/16, (2,6), (3,7)/16 of the word.
+  // Column n holds query head n % 4: its fp16 rounding (high part) where n / 4 is
+  // even, the fp16 rounding of what that leaves (low part) where it is odd, so the
+  // two columns' logits add up to those of the query with 22 bits or so instead of
+  // 11.  Each part folds the (c - 8) code offset with its own per-group sum.
   // Columns of heads >= G see an all-zero query row; their logits and output rows
   // are computed but never written.  They stay in LDS (read once per step) to keep
   // registers for the second buffer of loads in flight.
   const int hq = n16 & 3;                            // query head of this column
-  if (wave == 0 && n16 < 4) {
+  const int part = (n16 >> 2) & 1;                   // 0: high part, 1: low part
+  if (wave == 0 && n16 < 8) {
+    float gsum[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int w = (c < 4) ? (4 * kg + c) : (16 + 4 * kg + (c - 4));
       const int d0 = 8 * w;
       half8_t v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const _Float16 lo = (_Float16)qs[hq][d0 + r];
-        const _Float16 hi = (_Float16)qs[hq][d0 + r + 4];
-        if (r & 1) {
-          v[2 * r] = lo * (_Float16)0.0625f;
-          v[2 * r + 1] = hi * (_Float16)0.0625f;
-        } else {
-          v[2 * r] = lo;
-          v[2 * r + 1] = hi;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int r = e >> 1;                        // slot e: dim d0 + r (+4 when e is odd)
+        const float sc = (r & 1) ? 0.0625f : 1.0f;   // the shifted nibble reads as 16 c
+        const float t = qs[hq][d0 + r + 4 * (e & 1)] * sc;
+        const _Float16 th = (_Float16)t;
+        const _Float16 tv = part ? (_Float16)(t - (float)th) : th;
+        v[e] = tv;
+        gsum[c >> 2] += (float)tv / sc;
       }
-      qbs[c][4 * kg + hq] = v;
+      qbs[c][16 * part + 4 * kg + hq] = v;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      gsum[g] += __shfl_xor(gsum[g], 16);
+      gsum[g] += __shfl_xor(gsum[g], 32);
+    }
+    if (kg == 0) {
+      qsum_s[part][hq][0] = gsum[0];
+      qsum_s[part][hq][1] = gsum[1];
     }
   }
   __syncthreads();
   constexpr float kLog2e = 1.4426950408889634f;
   const float lsc = a.sm_scale * kLog2e;             // logits kept in log2 units
   const float cK = lsc * 16777216.0f;                // 2^24
-  const float off0 = lsc * 8.0f * qsum_s[hq][0];
-  const float off1 = lsc * 8.0f * qsum_s[hq][1];
+  const float off0 = lsc * 8.0f * qsum_s[part][hq][0];
+  const float off1 = lsc * 8.0f * qsum_s[part][hq][1];
   constexpr bool kone = (NKS == 1);                  // key group 256: one scale per row
 
   float4_t acc[16];
@@ -317,7 +376,7 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     }
     // The LDS index is made opaque per step so the operands are re-read here rather
     // than hoisted out of the loop into 32 loop-carried registers.
-    int qi = 4 * kg + hq;
+    int qi = 16 * part + 4 * kg + hq;
     asm volatile("" : "+v"(qi));
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -349,6 +408,8 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
         lg[j] = s0 * (cq[u][0][r] * cK - off0) + s1 * (cq[u][1][r] * cK - off1);
       }
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lg[j] = add_row_ror4(lg[j]);   // high + low part
     if (t0 + kStep > t_end) {                        // partial step: mask tokens >= t_end
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -415,25 +476,42 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     }
   };
 
-  // next unclaimed step of the block (wavefront-uniform).  Every lane takes part in
-  // the atomic, lane 0 adding 1 and the others 0, so lane 0 receives the old count
-  // whatever order the lanes are served in, and no single-lane branch (which would cost
-  // registers in this loop) is needed.
+  // Next step for this wavefront (wavefront-uniform), or -1 when the block is done.
+  // Every lane takes part in the LDS atomic (lane 0 adds 1, the others 0), so lane 0
+  // receives the old count whatever order the lanes are served in, with no single-lane
+  // branch (which would cost registers in this loop); the counter atomic likewise.
   auto claim = [&]() -> int {
-    const int v = atomicAdd(&next_step, lane == 0 ? 1 : 0);
-    return __builtin_amdgcn_readfirstlane(v);
+    const int k = __builtin_amdgcn_readfirstlane(atomicAdd(&next_local, lane == 0 ? 1 : 0));
+    const int sl = min(k >> cl2, kMaxSlots - 2), pos = k & ((1 << cl2) - 1);
+    int c;
+    do {                                             // the slot's chunk, once its claimer has written it
+      c = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&slot_chunk[sl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    } while (c < 0);
+    if (pos == 0) {                                  // first index of the slot: claim the next slot's chunk
+      int nc = total_chunks;
+      if (c < total_chunks) {
+        nc = ctr ? bpu + claim_global(ctr) : c + bpu;
+        nc = min(nc, total_chunks);
+      }
+      __hip_atomic_store(&slot_chunk[sl + 1], nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    const int step = (c << cl2) + pos;
+    return (c < total_chunks && step < total_steps) ? step : -1;
   };
-  // Each buffer is refilled right after it is consumed, with the next step claimed
-  // then.  Steps a wavefront holds only grow (i0 < i1 < next i0 ...), so the first one
-  // past the range ends the loop.
-  while (i0 < nsteps) {
-    process(b0, step_tok(i0));
+  // Each buffer is refilled right after it is consumed.  A wavefront's claims follow
+  // its local indices, so once one returns -1 so do all later ones: the first -1 ends
+  // the loop with no claimed step left unprocessed.
+  while (i0 >= 0) {
+    process(b0, i0 * kStep);
     i0 = claim();
-    load_step<NKS, NVS>(a, step_row(i0), lofs, b0);
-    if (i1 >= nsteps) break;
-    process(b1, step_tok(i1));
+    if (i0 >= 0) last = i0;
+    load_step<NKS, NVS>(a, step_row(i0, last), lofs, b0);
+    if (i1 < 0) break;
+    process(b1, i1 * kStep);
     i1 = claim();
-    load_step<NKS, NVS>(a, step_row(i1), lofs, b1);
+    if (i1 >= 0) last = i1;
+    load_step<NKS, NVS>(a, step_row(i1, last), lofs, b1);
   }
 
   // ---- reduce the token subsets of the four lane groups (same word, kg = 0..3)
@@ -493,12 +571,113 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
         O += wt * so[w][c][d];
       }
       float* dst = a.ws + ((rq * a.Hq + (size_t)h * G + c) * a.blocks_per_unit + blockIdx.x) * P;
-      dst[d] = O;
+      // merged in this kernel: device-coherent stores (written through to memory), so
+      // that another XCD's block can read them without any cache being flushed
+      auto put = [&](float* ptr, float val) {
+        if (a.done) __hip_atomic_store(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *ptr = val;
+      };
+      put(dst + d, O);
       if (d == 0) {
-        dst[kFastD] = (M == -INFINITY) ? -INFINITY : M * kLn2;
-        dst[kFastD + 1] = L;
+        put(dst + kFastD, (M == -INFINITY) ? -INFINITY : M * kLn2);
+        put(dst + kFastD + 1, L);
       }
     }
+  }
+  if (!a.done) return;
+  // ---- the unit's last block to finish merges the bpu partials:
+  // out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, lse = M + ln(that sum).
+  // Every thread waits until its coherent partial stores have completed before the
+  // block is counted, and the last block reads the partials with coherent loads.
+  __shared__ int is_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(a.done + (rq * a.H + h), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == bpu - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  auto get = [](const float* ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  // (m, l) of every partial into LDS (the per-wave output buffer is free by now), all
+  // loads in flight at once; then each thread's output loads go out 8 at a time.
+  static_assert(8 * kMaxChunks <= NW * 4 * kFastD, "merge tables exceed the per-wave output buffer");
+  float* const pm = &so[0][0][0];                    // [head][block], stride kMaxChunks (blocks <= chunks)
+  float* const pl = pm + 4 * kMaxChunks;
+  const float* const ubase = a.ws + (rq * a.Hq + (size_t)h * G) * bpu * P;
+  for (int t = tid; t < G * bpu; t += kFastBlock) {
+    const int c = t / bpu, sb = t - c * bpu;
+    const float* p = ubase + (size_t)t * P;
+    const float mv = get(p + kFastD), lv = get(p + kFastD + 1);
+    pm[c * kMaxChunks + sb] = mv;
+    pl[c * kMaxChunks + sb] = lv;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c0 = 0; c0 < 4; c0 += kFastBlock / kFastD) {
+    const int c = c0 + tid / kFastD;
+    if (c < G) {
+      const size_t rh = rq * a.Hq + (size_t)h * G + c;
+      const float* src = a.ws + rh * bpu * P;
+      const float* cm = pm + c * kMaxChunks;
+      const float* cl = pl + c * kMaxChunks;
+      float M = -INFINITY;
+      for (int sb = 0; sb < bpu; ++sb) M = fmaxf(M, cm[sb]);
+      float L = 0.0f, O = 0.0f;
+      for (int s0 = 0; s0 < bpu; s0 += 8) {
+        float ov[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ov[j] = get(src + (size_t)min(s0 + j, bpu - 1) * P + d);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (s0 + j < bpu) {
+            const float ms = cm[s0 + j];
+            const float wt = (ms == -INFINITY) ? 0.0f : expf(ms - M);
+            L += wt * cl[s0 + j];
+            O += wt * ov[j];
+          }
+        }
+      }
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      a.out[rh * kFastD + d] = O * inv;
+      if (d == 0 && a.lse) a.lse[rh] = L > 0.0f ? M + logf(L) : -INFINITY;
+    }
+  }
+  if (tid == 0) {   // ready for the next call: every block of the unit has made its last claim
+    ctr[0] = 0;
+    a.done[rq * a.H + h] = 0;
+  }
+}
+
+// Merge of the blocks' partials for one (query row, query head) per wavefront, when
+// the values are not rotated and the blocks took fixed chunks (no counters):
+// out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, lse = M + ln(that sum).
+// Each lane owns 4 of the 256 dimensions.
+__global__ __launch_bounds__(256) void k_fast_combine(const float* __restrict__ ws, int S, int Hq, int G, int H,
+                                                      long long rows_hq, float* out, float* lse, int* ctr) {
+  const long long rh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rh >= rows_hq) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int P = kFastD + 2;
+  const float* src = ws + (size_t)rh * S * P;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, src[(size_t)s * P + kFastD]);
+  float L = 0.0f;
+  float4_t o = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < S; ++s) {
+    const float* p = src + (size_t)s * P;
+    const float ms = p[kFastD];
+    const float w = (ms == -INFINITY) ? 0.0f : expf(ms - M);
+    L += w * p[kFastD + 1];
+    const float4_t v = *reinterpret_cast<const float4_t*>(p + 4 * lane);
+    o += w * v;
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  *reinterpret_cast<float4_t*>(out + (size_t)rh * kFastD + 4 * lane) = o * inv;
+  const int j = (int)(rh % Hq);
+  if (lane == 0) {
+    if (lse) lse[rh] = L > 0.0f ? M + logf(L) : -INFINITY;
+    if (ctr && j % G == 0) ctr[(rh / Hq) * H + j / G] = 0;   // ready for the next call
   }
 }
 
@@ -517,12 +696,21 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   return true;
 }
 
+// Chunk size: at least 16 steps (one step per wavefront of a block to start with), and
+// at most kMaxChunks chunks per (query row, KV head).
+static int fast_chunk_log2(const kvq_shape& s) {
+  const long long steps = s.tokens / kStep;
+  int cl2 = 4;
+  while (((steps + (1LL << cl2) - 1) >> cl2) > kMaxChunks) ++cl2;
+  return cl2;
+}
+
 static int fast_blocks_per_unit(const kvq_shape& s, int n_q) {
   const long long pairs = (long long)s.batch * s.layers * n_q * s.heads;
-  // about one block (eight wavefronts, two per SIMD) per CU, and at least one step per wavefront
+  // about one block (eight wavefronts, two per SIMD) per CU, and no more blocks than chunks
   long long bpu = (256 + pairs - 1) / pairs;
-  const long long max_bpu = std::max(1, s.tokens / (8 * kStep));
-  if (bpu > max_bpu) bpu = max_bpu;
+  const long long chunks = ((long long)(s.tokens / kStep) + (1LL << fast_chunk_log2(s)) - 1) >> fast_chunk_log2(s);
+  if (bpu > chunks) bpu = chunks;
   if (bpu < 1) bpu = 1;
   return (int)bpu;
 }
@@ -560,6 +748,15 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
   }
   a.sm_scale = pr.sm_scale;
   a.blocks_per_unit = fast_blocks_per_unit(s, pr.n_q);
+  a.chunk_log2 = fast_chunk_log2(s);
+  // shared chunk counters when the rows fit the workspace's counter region
+  const long long rows_kv = (long long)s.batch * s.layers * pr.n_q * s.heads;
+  a.ctr = (pr.ctr && rows_kv <= kWsCounterRows) ? pr.ctr : nullptr;
+  // unrotated values without channel scales: the last block of a unit merges its partials
+  const bool fused = a.ctr && v.codec.rot_width <= 1 && !v.chan_scale;
+  a.done = fused ? pr.ctr + kWsCounterRows : nullptr;
+  a.out = pr.out;
+  a.lse = pr.lse;
   const long long units = (long long)s.batch * s.layers * s.heads;
   const dim3 grid(a.blocks_per_unit, (unsigned)units, (unsigned)pr.n_q);
   if (a.nks == 2) {
@@ -572,8 +769,12 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
     else k_decode_mfma<1, 4><<<grid, kFastBlock, 0, st>>>(a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_combine_partials(pr, a.blocks_per_unit, st);
+  if (e != hipSuccess || fused) return e;
+  if (v.codec.rot_width > 1 || v.chan_scale) return launch_combine_partials(pr, a.blocks_per_unit, a.ctr, st);
+  const long long rows_hq = (long long)s.batch * s.layers * pr.n_q * pr.Hq;
+  k_fast_combine<<<(unsigned)((rows_hq + 3) / 4), 256, 0, st>>>(a.ws, a.blocks_per_unit, pr.Hq, a.G, s.heads, rows_hq,
+                                                             pr.out, pr.lse, a.ctr);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

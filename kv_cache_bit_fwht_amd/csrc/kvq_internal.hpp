@@ -166,9 +166,17 @@ struct AttnProblem {
   float* kl;
   float* relerr;
   double* kv_err;
-  void* ws;
+  void* ws;          // partials (the workspace past its counter region)
   size_t ws_bytes;
+  int* ctr;          // the workspace's counter region (kWsCounterBytes, zero between calls)
 };
+
+// The first bytes of every decode workspace hold two arrays of per-(query row,
+// KV head) counters of the MFMA decode kernel, kWsCounterRows ints each: chunk
+// claims, then finished blocks.  They are zero before the first call, and each
+// call sets the ones it used back to zero.  Partials follow.
+constexpr size_t kWsCounterBytes = 65536;
+constexpr long long kWsCounterRows = (long long)(kWsCounterBytes / (2 * sizeof(int)));
 
 size_t decode_ws_bytes(const kvq_shape& s, int Hq, int n_q);
 size_t error_ws_bytes(const kvq_shape& s, int Hq, int n_q);
@@ -178,6 +186,6 @@ hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st);
 bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st);
 size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q);
-hipError_t launch_combine_partials(const AttnProblem& pr, int S, hipStream_t st);
+hipError_t launch_combine_partials(const AttnProblem& pr, int S, int* ctr, hipStream_t st);
 
 }  // namespace kvq

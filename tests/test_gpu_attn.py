@@ -27,13 +27,16 @@ def _gpu_pack(K, x, codec, chan=None):
     return p
 
 
-def _gpu_decode(K, kp, vp, q, kv_len, path=None):
+def _gpu_decode(K, kp, vp, q, kv_len, path=None, ws=None):
+    """One decode call; `ws` (a zero-filled device byte tensor) is reused when given."""
     import torch
     B, L, nq, Hq, D = q.shape
     out = torch.empty((B, L, nq, Hq, D), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, L, nq, Hq), dtype=torch.float32, device="cuda:0")
     wsb = K.kvq_decode_attn_workspace(kp.shape, Hq, nq)
-    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda:0")
+    if ws is None:
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda:0")
+    assert ws.numel() >= wsb
     kl = to_dev(kv_len) if kv_len is not None else None
     K.kvq_decode_attn(kp, vp, Hq, nq, to_dev(q), kl, 0.0, out, lse, ws, wsb, path=path)
     torch.cuda.synchronize()

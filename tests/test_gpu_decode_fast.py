@@ -73,6 +73,25 @@ def test_fast_causal_lengths():
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), kv_len)
 
 
+def test_fast_many_blocks_per_unit():
+    """Few (row, KV head) units over 16K tokens: 32 blocks share each unit's chunk
+    counter and the last of them merges the unit; causal lengths end chunks early."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=1, T=16384, n_q=2)
+    kv_len = np.array([[[16384, 9000]]], dtype=np.int32)
+    announce("mfma many blocks per unit")
+    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), kv_len)
+
+
+def test_fast_static_chunks_many_rows():
+    """More (query row, KV head) units than the workspace has counters for: blocks take
+    fixed chunks and a separate kernel merges the partials."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=2, T=64, n_q=1030)             # 2 * 1030 * 4 = 8240 units
+    announce("mfma static chunks, 8240 units")
+    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0))
+
+
 def test_fast_rejects_unsupported_and_auto_falls_back():
     import kv_cache_bit_fwht_amd as K
     w = synth.get("c3", L=1, T=100, n_q=1)                 # tokens not a multiple of 32
@@ -90,7 +109,9 @@ def test_fast_rejects_unsupported_and_auto_falls_back():
 def test_fast_repeat_calls_agree_to_rounding():
     """The MFMA kernel hands steps out dynamically, so the order in which a block's
     wavefronts sum their tokens varies from call to call: repeated calls agree to fp32
-    rounding, not bit for bit."""
+    rounding, not bit for bit.  The calls share one workspace, whose counters each
+    call must leave at zero (checked after the last call, and through the results)."""
+    import torch
     import kv_cache_bit_fwht_amd as K
     w = synth.get("c3", L=2, T=4096, n_q=2)
     Kx, Vx = synth.gen_kv(w)
@@ -98,11 +119,18 @@ def test_fast_repeat_calls_agree_to_rounding():
     announce("mfma repeat calls")
     kp = _gpu_pack(K, Kx, K.Codec(K.INT_ABSMAX, 4, 128, 256))
     vp = _gpu_pack(K, Vx, K.Codec(K.INT_ABSMAX, 2, 128, 0))
-    runs = [_gpu_decode(K, kp, vp, q, None, path=2) for _ in range(3)]
+    wsb = K.kvq_decode_attn_workspace(kp.shape, w.Hq, w.n_q)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda:0")
+    runs = [_gpu_decode(K, kp, vp, q, None, path=2, ws=ws) for _ in range(4)]
     for out, lse in runs[1:]:
         rel = np.linalg.norm(out - runs[0][0], axis=-1) / np.linalg.norm(runs[0][0], axis=-1)
         assert rel.max() < 1e-5
         assert np.abs(lse - runs[0][1]).max() < 1e-5
+    assert int(ws[:65536].count_nonzero()) == 0
+    _, Kd, Vd = _oracle(Kx, Vx, oracle_codec(K, O, K.Codec(K.INT_ABSMAX, 4, 128, 256)),
+                        oracle_codec(K, O, K.Codec(K.INT_ABSMAX, 2, 128, 0)), q, None)
+    ref_out, ref_lse = O.decode_attn(q, Kd, Vd, None)
+    _check_decode(runs[-1][0], runs[-1][1], ref_out, ref_lse, None, lse_tol=1e-3)
 
 
 def test_fast_full_size_64k_sampled():
