@@ -61,6 +61,35 @@ def traffic_for(kind, per_launch_units):
     return d.get("bytes_per_launch")
 
 
+def measure_ceilings(torch, dev):
+    """Achievable-bandwidth reference measured with a library kernel (not this
+    package's): a 1 GiB device-to-device copy (1 GiB read + 1 GiB written).
+    Median of 5 after 2 warm-ups."""
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+
+    def med(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    t_copy = med(lambda: dst.copy_(src))
+    del src, dst
+    torch.cuda.empty_cache()
+    nbytes = n * 4
+    return {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
+            "how": "1 GiB device-to-device copy (1 GiB read + 1 GiB written), median of 5"}
+
+
 def cpu_baseline(Kx, Vx, q, units_sample=2, queries_sample=4):
     """The oracle as it stands on a bounded sample of the same workload, scaled
     to the whole step: quantise+pack+dequantise `units_sample` (layer, head)
@@ -226,6 +255,7 @@ def main():
     log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.1f} ms); quantize {qz_ms * 1e3:.1f} us; "
         f"decode {dc_ms * 1e3:.1f} us per call")
 
+    ceil = measure_ceilings(torch, dev)
     value = nq * w.B / (ms_step * 1e-3)
     dec_gbs = d_bytes / (dc_ms * 1e-3) / 1e9
     qz_gbs = q_bytes / (qz_ms * 1e-3) / 1e9
@@ -248,10 +278,13 @@ def main():
                    "decode_calls_per_step": nq, "packed_cache_copies": len(copies),
                    "decode_path": {0: "auto", 1: "general", 2: "mfma"}[args.path]},
         "quantize_pack": {"GB/s": round(qz_gbs, 1), "frac_hbm": round(qz_gbs / HBM_PEAK_GBS, 4),
+                          "frac_copy_ceiling": round(qz_gbs / ceil["copy_GBps"], 4),
                           "us_per_call_pair": round(qz_ms * 1e3, 2), "bytes": q_bytes},
         "decode": {"tok/s": round(1e3 / dc_ms, 1), "us_per_token": round(dc_ms * 1e3, 2),
                    "GB/s": round(dec_gbs, 1), "frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "frac_copy_ceiling": round(dec_gbs / ceil["copy_GBps"], 4),
                    "bytes_per_launch": d_bytes},
+        "ceilings": ceil,
         "roofline": {"bound": "hbm", "kernel": "kvq_decode_attn", "achieved": round(dec_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for("decode", 1)},

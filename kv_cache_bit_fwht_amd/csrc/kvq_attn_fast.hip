@@ -211,7 +211,7 @@ __device__ __forceinline__ int claim_global(int* ctr) {
 template <int NKS, int NVS>
 __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   constexpr int NW = kFastBlock / 64;                // wavefronts per block
-  __shared__ float qs[4][kFastD + 16];
+  __shared__ __align__(16) float qs[4][kFastD + 16];
   __shared__ float qsum_s[2][4][2];                 // [part][head][key group] sums of the MFMA query operand
   __shared__ float so[NW][4][kFastD];               // per-wave outputs [wave][head][dim]
   __shared__ float sm[NW][4], sl[NW][4];            // per-wave reference max (log2 units) and sum
@@ -232,14 +232,16 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   if (a.kv_len) n = min(max(a.kv_len[rq], 0), a.T);
 
   // ---- steps.  The unit's 32-token steps are grouped in chunks of C = 2^chunk_log2.
-  // Block x starts on chunk x; every further chunk comes from a counter shared by the
-  // unit's blocks (which sit on different XCDs, whose speeds differ from run to run),
-  // or, without counters, is chunk x + s * bpu for the block's slot s.  Inside the
-  // block, wavefronts take local step indices from an LDS counter: index k is step
-  // (k mod C) of the chunk of slot k / C.  Chunks are claimed one slot ahead by the
-  // wavefront that takes a slot's first index, and only after that slot's own chunk is
-  // known, so a block's chunks increase with the slot: once a slot holds the end
-  // marker every later one does too.
+  // Slot s < S0 of block x holds chunk x + s * bpu (about three quarters of the unit's
+  // chunks, taken without any atomic); every later chunk comes from a counter shared by
+  // the unit's blocks, which sit on different XCDs whose speeds differ from run to run,
+  // so the fast ones take more of the tail.  Without counters every slot is static.
+  // Inside the block, wavefronts take local step indices from an LDS counter: index k
+  // is step (k mod C) of the chunk of slot k / C.  Chunks are claimed one slot ahead by
+  // the wavefront that takes a slot's first index, and only after that slot's own chunk
+  // is known, so a block's chunks increase with the slot (static ones lie below
+  // S0 * bpu, counted ones above): once a slot holds the end marker every later one
+  // does too.
   const int bpu = a.blocks_per_unit;
   const int x = blockIdx.x;
   const int cl2 = a.chunk_log2;
@@ -247,6 +249,8 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   const int total_steps = (n + kStep - 1) / kStep;
   const int total_chunks = (total_steps + (1 << cl2) - 1) >> cl2;
   int* const ctr = a.ctr ? a.ctr + (rq * a.H + h) : nullptr;
+  // static slots per block: at least 2 (slots 0 and 1 are known at the start)
+  const int S0 = ctr ? max(2, (3 * total_chunks) / (4 * bpu)) : 0x7fffffff;
   const size_t row0 = (size_t)unit * a.T;
   const int vgrp = (16 * n16) / a.gv;                // scale group of this lane's value word
   const uint32_t vsel = (NVS > 1 && (vgrp & 1)) ? 0x07060302u : 0x05040100u;
@@ -256,18 +260,19 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   auto step_row = [&](int s, int last) -> size_t {
     return row0 + (size_t)(s >= 0 ? s : (last >= 0 ? last : 0)) * kStep;
   };
-  int claim1 = 0;                                    // slot 1's chunk (counter value), fetched early
-  if (ctr && tid == 0) claim1 = atomicAdd(ctr, 1);
 
   // The query is read first so that the prologue waits for it alone; each wavefront's
   // first two steps (w and w + NW, handed out statically) are loaded right after it and
   // land while the prologue runs.  Loads are never issued under a branch, so that every
   // wait names exactly the data it needs.
   const uint16_t* qsrc = a.q + (size_t)rq * a.Hq * kFastD + (size_t)h * G * kFastD;
-  uint32_t qraw = 0u;                                // elements 2 tid, 2 tid + 1 of [4 heads][256]
-  if (2 * tid < G * kFastD) qraw = *reinterpret_cast<const uint32_t*>(qsrc + 2 * tid);
-  float2_t kch = float2_t{1.0f, 1.0f};               // key channel scales of those dims
-  if (a.kchan) kch = *reinterpret_cast<const float2_t*>(a.kchan + ((size_t)l * a.H + h) * kFastD + 2 * (tid & 127));
+  // wavefront w < 4 holds query head w, dims 4 lane .. 4 lane + 3 (zero for heads >= G)
+  u32x2_t qraw = u32x2_t{0u, 0u};
+  float4_t kch = float4_t{1.0f, 1.0f, 1.0f, 1.0f};   // key channel scales of those dims
+  if (wave < G) {
+    qraw = *reinterpret_cast<const u32x2_t*>(qsrc + (size_t)wave * kFastD + 4 * lane);
+    if (a.kchan) kch = *reinterpret_cast<const float4_t*>(a.kchan + ((size_t)l * a.H + h) * kFastD + 4 * lane);
+  }
   const LaneOffsets lofs = lane_offsets<NKS, NVS>(kg, n16);
   // local indices wave and wave + NW of slot 0 (chunk x, C >= 16) are handed out statically
   auto first_step = [&](int k) { return (x < total_chunks && (x << cl2) + k < total_steps) ? (x << cl2) + k : -1; };
@@ -277,38 +282,13 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   load_step<NKS, NVS>(a, step_row(i0, last), lofs, b0);
   load_step<NKS, NVS>(a, step_row(i1, last), lofs, b1);
 
-  // ---- query prologue: q in the key coordinates (divide channel scale, rotate), fp32 in LDS
-  {
-    const int g = tid >> 7, d0 = 2 * (tid & 127);
-    float x0 = h2f((uint16_t)(qraw & 0xffffu)), x1 = h2f((uint16_t)(qraw >> 16));
-    if (a.kchan) {
-      x0 = x0 / kch[0];
-      x1 = x1 / kch[1];
-    }
-    qs[g][d0] = x0;
-    qs[g][d0 + 1] = x1;
-  }
-  for (int k = tid; k < kMaxSlots; k += kFastBlock) slot_chunk[k] = -1;
+  // ---- query prologue, one wavefront per query head (no block barrier until the end):
+  // q in the key coordinates (divide by the channel scale, rotate: strides 1 and 2 in the
+  // lane, 4 to 128 across lanes), then the MFMA B operands and per-group offset sums.
+  for (int k = tid; k < kMaxSlots; k += kFastBlock)
+    slot_chunk[k] = (k == 0) ? min(x, total_chunks)
+                  : (k == 1) ? (x < total_chunks ? min(x + bpu, total_chunks) : total_chunks) : -1;
   if (tid == 0) next_local = 2 * NW;
-  __syncthreads();
-  if (tid == 0) {
-    slot_chunk[0] = min(x, total_chunks);
-    const int c1 = ctr ? bpu + claim1 : x + bpu;
-    slot_chunk[1] = x < total_chunks ? min(c1, total_chunks) : total_chunks;
-  }
-  if (a.kW > 1) {
-    for (int ls = 0; (1 << ls) < a.kW; ++ls) {
-      const int s = 1 << ls;
-      const int g = tid >> 7, pp = tid & 127;        // one butterfly per thread and stage
-      const int ii = ((pp >> ls) << (ls + 1)) | (pp & (s - 1));
-      const float x = qs[g][ii], y = qs[g][ii + s];
-      qs[g][ii] = x + y;
-      qs[g][ii + s] = x - y;
-      __syncthreads();
-    }
-    for (int p = tid; p < 4 * kFastD; p += kFastBlock) qs[p >> 8][p & 255] *= a.kkappa;
-    __syncthreads();
-  }
   // B operands: chunk c < 4 -> key word 4kg + c (dims 8w..8w+7, group 0), c >= 4 -> word 16 + 4kg + (c-4).
   // Register order of the 8 k-slots: dims (0,4), (1,5)/16, (2,6), (3,7)/16 of the word.
   // Column n holds query head n % 4: its fp16 rounding (high part) where n / 4 is
@@ -318,37 +298,62 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   // Columns of heads >= G see an all-zero query row; their logits and output rows
   // are computed but never written.  They stay in LDS (read once per step) to keep
   // registers for the second buffer of loads in flight.
-  const int hq = n16 & 3;                            // query head of this column
-  const int part = (n16 >> 2) & 1;                   // 0: high part, 1: low part
-  if (wave == 0 && n16 < 8) {
-    float gsum[2] = {0.0f, 0.0f};
+  if (wave < 4) {
+    float v[4] = {h2f((uint16_t)(qraw[0] & 0xffffu)), h2f((uint16_t)(qraw[0] >> 16)),
+                  h2f((uint16_t)(qraw[1] & 0xffffu)), h2f((uint16_t)(qraw[1] >> 16))};
+    if (a.kchan) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int w = (c < 4) ? (4 * kg + c) : (16 + 4 * kg + (c - 4));
-      const int d0 = 8 * w;
-      half8_t v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = e >> 1;                        // slot e: dim d0 + r (+4 when e is odd)
-        const float sc = (r & 1) ? 0.0625f : 1.0f;   // the shifted nibble reads as 16 c
-        const float t = qs[hq][d0 + r + 4 * (e & 1)] * sc;
-        const _Float16 th = (_Float16)t;
-        const _Float16 tv = part ? (_Float16)(t - (float)th) : th;
-        v[e] = tv;
-        gsum[c >> 2] += (float)tv / sc;
+      for (int e = 0; e < 4; ++e) v[e] = v[e] / kch[e];
+    }
+    if (a.kW > 1) {
+      if (a.kW >= 2) {                               // stride 1
+        const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+        v[0] = x0 + x1; v[1] = x0 - x1; v[2] = x2 + x3; v[3] = x2 - x3;
       }
-      qbs[c][16 * part + 4 * kg + hq] = v;
-    }
+      if (a.kW >= 4) {                               // stride 2
+        const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+        v[0] = x0 + x2; v[2] = x0 - x2; v[1] = x1 + x3; v[3] = x1 - x3;
+      }
+      for (int m = 1; 4 * m < a.kW; m <<= 1) {       // stride 4m: lane ^ m
+        const bool hi = (lane & m) != 0;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      gsum[g] += __shfl_xor(gsum[g], 16);
-      gsum[g] += __shfl_xor(gsum[g], 32);
+        for (int e = 0; e < 4; ++e) {
+          const float y = __shfl_xor(v[e], m);
+          v[e] = hi ? (y - v[e]) : (v[e] + y);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= a.kkappa;
     }
-    if (kg == 0) {
-      qsum_s[part][hq][0] = gsum[0];
-      qsum_s[part][hq][1] = gsum[1];
+    *reinterpret_cast<float4_t*>(&qs[wave][4 * lane]) = float4_t{v[0], v[1], v[2], v[3]};
+    // lane -> B entry (chunk c, lane group kg, part); its 8 dims are d0 .. d0 + 7
+    const int c = lane & 7, ekg = (lane >> 3) & 3, epart = lane >> 5;
+    const int d0 = 8 * ((c < 4) ? (4 * ekg + c) : (16 + 4 * ekg + (c - 4)));
+    const float4_t f0 = *reinterpret_cast<const float4_t*>(&qs[wave][d0]);
+    const float4_t f1 = *reinterpret_cast<const float4_t*>(&qs[wave][d0 + 4]);
+    const float f[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+    half8_t hv;
+    float gsum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = e >> 1;                          // slot e: dim d0 + r (+4 when e is odd)
+      const float sc = (r & 1) ? 0.0625f : 1.0f;     // the shifted nibble reads as 16 c
+      const float t = f[r + 4 * (e & 1)] * sc;
+      const _Float16 th = (_Float16)t;
+      const _Float16 tv = epart ? (_Float16)(t - (float)th) : th;
+      hv[e] = tv;
+      gsum += (float)tv / sc;
     }
+    qbs[c][16 * epart + 4 * ekg + wave] = hv;
+    // sum over the lanes of the same (part, key group): lane bits 0, 1 (c % 4) and 3, 4 (kg)
+    gsum += __shfl_xor(gsum, 1);
+    gsum += __shfl_xor(gsum, 2);
+    gsum += __shfl_xor(gsum, 8);
+    gsum += __shfl_xor(gsum, 16);
+    if ((lane & 0x1B) == 0) qsum_s[epart][wave][c >> 2] = gsum;
   }
+  const int hq = n16 & 3;                            // query head of this lane's column
+  const int part = (n16 >> 2) & 1;                   // 0: high part, 1: low part
   __syncthreads();
   constexpr float kLog2e = 1.4426950408889634f;
   const float lsc = a.sm_scale * kLog2e;             // logits kept in log2 units
@@ -491,7 +496,7 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     if (pos == 0) {                                  // first index of the slot: claim the next slot's chunk
       int nc = total_chunks;
       if (c < total_chunks) {
-        nc = ctr ? bpu + claim_global(ctr) : c + bpu;
+        nc = (sl + 1 < S0) ? c + bpu : S0 * bpu + claim_global(ctr);
         nc = min(nc, total_chunks);
       }
       __hip_atomic_store(&slot_chunk[sl + 1], nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);

@@ -79,6 +79,17 @@ def test_quantize_pack_bit_exact(D, cspec):
     _compare(K, x, codec)
 
 
+@pytest.mark.parametrize("cspec", [(1, 4, 128, 256), (1, 2, 128, 0)])
+def test_quantize_many_passes_ragged(cspec):
+    """90,003 rows at head_dim 256: every wavefront encodes several row quads (the
+    two-buffer loop), and the last quad is ragged (3 of 4 rows); all rows checked."""
+    import kv_cache_bit_fwht_amd as K
+    codec = K.Codec(*cspec)
+    x = _inputs(1, 1, 3, 30001, 256, seed=911 + cspec[1])
+    announce(f"quantize 90003 rows codec={codec}")
+    _compare(K, x, codec)
+
+
 @pytest.mark.parametrize("arm", ["C", "D", "D4"])
 def test_prescaled_keys_bit_exact(arm):
     """E21W arms C/D: per-channel K scaling calibrated on sequence 0."""
