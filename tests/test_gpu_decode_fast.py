@@ -1,9 +1,10 @@
 """GPU parity of the MFMA decode-attention kernel (4-bit keys, 2-bit values,
 head_dim 256) against the CPU oracle, and against the general kernel.
 
-Bar: outputs within 2e-3 relative L2 per row (the query enters the matrix
-cores rounded to fp16: about 2^-12 relative per element, far inside the bar),
-lse within 1e-3 absolute.
+Bar: outputs within 2e-3 relative L2 per row, lse within 1e-4 absolute.  The
+rotated query enters the matrix cores as an fp16 high part plus an fp16
+remainder (about 22 bits), and the P.V weights as fp16 (2^-11 relative per
+weight), which sets the output error (a few 1e-4 at most).
 """
 import numpy as np
 import pytest
@@ -23,7 +24,7 @@ def _case(K, w, kc, vc, kv_len=None, compare_general=True):
     _, Kd, Vd = _oracle(Kx, Vx, oracle_codec(K, O, kc), oracle_codec(K, O, vc), q, kv_len)
     out, lse = _gpu_decode(K, kp, vp, q, kv_len, path=2)
     ref_out, ref_lse = O.decode_attn(q, Kd, Vd, kv_len)
-    rel = _check_decode(out, lse, ref_out, ref_lse, kv_len, lse_tol=1e-3)
+    rel = _check_decode(out, lse, ref_out, ref_lse, kv_len, lse_tol=1e-4)
     if compare_general:
         out1, lse1 = _gpu_decode(K, kp, vp, q, kv_len, path=1)
         rel1 = np.linalg.norm(out1 - out, axis=-1) / np.maximum(np.linalg.norm(out1, axis=-1), 1e-30)
@@ -130,7 +131,7 @@ def test_fast_repeat_calls_agree_to_rounding():
     _, Kd, Vd = _oracle(Kx, Vx, oracle_codec(K, O, K.Codec(K.INT_ABSMAX, 4, 128, 256)),
                         oracle_codec(K, O, K.Codec(K.INT_ABSMAX, 2, 128, 0)), q, None)
     ref_out, ref_lse = O.decode_attn(q, Kd, Vd, None)
-    _check_decode(runs[-1][0], runs[-1][1], ref_out, ref_lse, None, lse_tol=1e-3)
+    _check_decode(runs[-1][0], runs[-1][1], ref_out, ref_lse, None, lse_tol=1e-4)
 
 
 def test_fast_full_size_64k_sampled():
@@ -160,4 +161,4 @@ def test_fast_full_size_64k_sampled():
             go = out[0, l, 0, h * G:(h + 1) * G].astype(np.float64)
             rel = np.linalg.norm(go - ro, axis=-1) / np.linalg.norm(ro, axis=-1)
             assert rel.max() < 2e-3, f"query {i} unit {(l, h)} rel {rel.max():.3g}"
-            assert np.abs(lse[0, l, 0, h * G:(h + 1) * G] - rl).max() < 1e-3
+            assert np.abs(lse[0, l, 0, h * G:(h + 1) * G] - rl).max() < 1e-4
