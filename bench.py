@@ -142,6 +142,103 @@ def _cpu_name():
     return "unknown"
 
 
+def _median_time(torch, fn, reps):
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return float(np.median(ts))
+
+
+def secondary(workload, reps):
+    """The other decode configurations (not the headline line): c4, extreme low-bit
+    codecs at head_dim 128 with layer 0 kept in fp16, and c5, transformed keys at
+    head_dim 128 with fp16 values.  One JSON line per arm: quantize+pack of the
+    arm's K and V, and one decode step (every layer, every query head, B queries)."""
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.get(workload)
+    log(f"generating {w.description}")
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    kd = torch.from_numpy(Kx.view(np.int16)).to(dev)
+    vd = torch.from_numpy(Vx.view(np.int16)).to(dev)
+    qd = torch.from_numpy(np.ascontiguousarray(q[:, :, :1]).view(np.int16)).to(dev)
+    del Kx, Vx
+    f16 = K.Codec(K.FP16)
+    if workload == "c4":
+        arms = {"ternary g8": (K.Codec(K.TERNARY, 2, 8, 0),) * 2, "sign g8": (K.Codec(K.SIGN, 1, 8, 0),) * 2,
+                "NF4 K g64 + int4 V g64": (K.Codec(K.NF4, 4, 64, 0), K.Codec(K.INT_ABSMAX, 4, 64, 0)),
+                "int8 g128": (K.Codec(K.INT8_SYM, 8, 128, 0),) * 2}
+        lo = 1                                       # layer 0 is the fp16 anchor
+    else:
+        arms = {"rFFT polar 5+7 g32": (K.Codec(K.RFFT_POLAR, 5, 32, 0, 7), f16),
+                "rFFT Cartesian 6+6 g32": (K.Codec(K.RFFT_CART, 6, 32, 0), f16),
+                "FWHT-128 int6 absmax g32": (K.Codec(K.INT_ABSMAX, 6, 32, 128), f16)}
+        lo = 0
+    B, L, H, T, D, Hq = w.B, w.L, w.H, w.T, w.D, w.Hq
+    shape = K.Shape(B, L - lo, H, T, D)
+    kq, vq = kd[:, lo:].contiguous() if lo else kd, vd[:, lo:].contiguous() if lo else vd
+    qq = qd[:, lo:].contiguous() if lo else qd
+    out = torch.empty((B, L - lo, 1, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, L - lo, 1, Hq), dtype=torch.float32, device=dev)
+    wsb = K.kvq_decode_attn_workspace(shape, Hq, 1)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+    anchor_s = 0.0
+    if lo:
+        ashape = K.Shape(B, 1, H, T, D)
+        ka, va = K.packed_from_fp16(kd[:, :1].contiguous(), ashape), K.packed_from_fp16(vd[:, :1].contiguous(), ashape)
+        qa = qd[:, :1].contiguous()
+        oa = torch.empty((B, 1, 1, Hq, D), dtype=torch.float32, device=dev)
+        la = torch.empty((B, 1, 1, Hq), dtype=torch.float32, device=dev)
+        wsa_b = K.kvq_decode_attn_workspace(ashape, Hq, 1)
+        wsa = torch.zeros(max(wsa_b, 16), dtype=torch.uint8, device=dev)
+        anchor_s = _median_time(torch, lambda: K.kvq_decode_attn(ka, va, Hq, 1, qa, None, 0.0, oa, la, wsa, wsa_b),
+                                reps)
+    rows = B * (L - lo) * H * T
+    for name, (kc, vc) in arms.items():
+        kp = K.alloc_packed(kc, shape, dev)
+        vp = K.packed_from_fp16(vq, shape) if vc.codebook == K.FP16 else K.alloc_packed(vc, shape, dev)
+
+        def quant():
+            K.kvq_quantize_pack(kq, kp)
+            if vc.codebook != K.FP16:
+                K.kvq_quantize_pack(vq, vp)
+
+        quant()
+        torch.cuda.synchronize()
+        t_q = _median_time(torch, quant, reps)
+        K.kvq_decode_attn(kp, vp, Hq, 1, qq, None, 0.0, out, lse, ws, wsb)
+        torch.cuda.synchronize()
+        t_d = _median_time(torch, lambda: K.kvq_decode_attn(kp, vp, Hq, 1, qq, None, 0.0, out, lse, ws, wsb), reps)
+        kw, ks, km = K.kvq_packed_layout(shape, kc)
+        vw, vs, vm = K.kvq_packed_layout(shape, vc)
+        kb = rows * (4 * kw + 2 * (ks + km))
+        vb = rows * (D * 2 if vc.codebook == K.FP16 else 4 * vw + 2 * (vs + vm))
+        q_bytes = rows * D * 2 * (1 if vc.codebook == K.FP16 else 2) + kb + (0 if vc.codebook == K.FP16 else vb)
+        d_bytes = kb + vb
+        anchor_bytes = (B * H * T * D * 2 * 2) if lo else 0
+        step = t_d + anchor_s
+        print(json.dumps({
+            "workload": f"{workload}: B={B} L={L} H={H} T={T} D={D} Hq={Hq}" + (", layer 0 fp16" if lo else ""),
+            "arm": name,
+            "quantize_pack": {"us": round(t_q * 1e6, 1), "GB/s": round(q_bytes / t_q / 1e9, 1),
+                              "frac_hbm": round(q_bytes / t_q / 1e9 / HBM_PEAK_GBS, 4), "bytes": q_bytes},
+            "decode_step": {"us": round(step * 1e6, 1), "tok/s": round(B / step, 1),
+                            "GB/s": round((d_bytes + anchor_bytes) / step / 1e9, 1),
+                            "frac_hbm": round((d_bytes + anchor_bytes) / step / 1e9 / HBM_PEAK_GBS, 4),
+                            "bytes": d_bytes + anchor_bytes, "anchor_us": round(anchor_s * 1e6, 1)},
+        }), flush=True)
+        del kp, vp
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,11 +251,18 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for hardware-counter passes: a known-size copy (the counters' "
                          "calibration), one quantize+pack pair and --decode-queries decode calls")
+    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5"],
+                    help="c3: the headline line (default); c4/c5: one line per codec arm of those configs")
+    ap.add_argument("--reps", type=int, default=5, help="timed repetitions per arm (c4/c5)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the path would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != "c3":
+        secondary(args.workload, args.reps)
+        return
 
     import torch
     import kv_cache_bit_fwht_amd as K

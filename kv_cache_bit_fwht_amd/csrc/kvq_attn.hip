@@ -390,6 +390,211 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ wavefront decode kernel
+//
+// The decode path of every codec except the rFFT keys.  Each wavefront owns one
+// split (a token range) of one (query row, KV head) and runs on its own: lane
+// (r, j) dequantises the 16 values j of row slot r straight into registers (the
+// codec's per-lane decode, as kvq_dequant), the logits of up to 4 query heads are
+// dot products against the query held in registers, reduced across the D/16
+// lanes of the row, and the online softmax (log2 units, a reference maximum that
+// moves only when a logit exceeds it by more than 8) and P.V accumulate per lane.
+// No barrier in the loop; three iterations of code and scale loads are in flight.
+// The wavefront's (o, m, l) partial is merged by the combine kernel.
+
+constexpr int kWaveHeads = 4;     // query heads per wavefront (G > 4: several head groups)
+
+template <int CB, int BITS>
+struct RawChunk {                 // a lane's undecoded 16 values of one row
+  uint32_t w[8];
+  uint16_t s[2], z[2];            // fp16 scale (and min-max min) of values 0-7 and 8-15
+  long long row;                  // for the runtime-codec fallback, which loads as it decodes
+};
+
+template <int CB, int BITS>
+__device__ __forceinline__ void raw_load(const DevCodec& c, long long row, int j, int glog2, RawChunk<CB, BITS>& r) {
+  r.row = row;
+  if constexpr (CB >= 0) {
+    load_chunk<BITS>(c.codes, (size_t)row * c.row_bytes + (size_t)j * 2 * BITS, r.w);
+    if constexpr (CB != KVQ_FP16) {
+      // groups of values 0-7 and 8-15 of the lane (the same group unless g = 8)
+      const size_t i0 = (size_t)row * c.ng + ((16 * j) >> glog2), i1 = (size_t)row * c.ng + ((16 * j + 8) >> glog2);
+      r.s[0] = c.scales[i0];
+      r.s[1] = c.scales[i1];
+      if constexpr (CB == KVQ_INT_MINMAX) {
+        r.z[0] = c.mins[i0];
+        r.z[1] = c.mins[i1];
+      }
+    }
+  }
+}
+
+template <int CB, int BITS>
+__device__ __forceinline__ void raw_decode(const DevCodec& c, const RawChunk<CB, BITS>& r, int j, const Tables& tab,
+                                           float v[16]) {
+  if constexpr (CB < 0) {
+    dq_row_any(c, r.row, j, tab, v);
+  } else {
+    uint32_t cc[16];
+    unpack16<BITS>(r.w, cc);
+    const uint16_t z0[2] = {0, 0};
+    decode16<CB, BITS>(cc, r.s, CB == KVQ_INT_MINMAX ? r.z : z0, tab, v);
+  }
+}
+
+// Sum over the lanes of a row (lpt = 4, 8 or 16 consecutive lanes) with DPP: quad
+// swaps, then the half-row and row mirrors.  Every lane must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_lanes_sum(float x, int lpt) {
+  x += dpp_mov<0xB1>(x);                             // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);                             // quad_perm [2,3,0,1]
+  if (lpt >= 8) x += dpp_mov<0x141>(x);              // row_half_mirror
+  if (lpt >= 16) x += dpp_mov<0x140>(x);             // row_mirror
+  return x;
+}
+
+template <int KCB, int KB, int VCB, int VB>
+__global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
+  extern __shared__ float smem[];
+  const int D = a.D, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int RS = 17 * (D / 16) + 17;
+  float* qc = smem;                                  // [kWaveHeads][RS] query rows
+  const int lg = a.lpt_log2, LPT = 1 << lg, RPW = 64 >> lg;   // lanes per row, rows per wavefront step
+  const int j = lane & (LPT - 1), r = lane >> lg;
+  const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
+  const int h = blockIdx.y / HG, hg = blockIdx.y - h * HG;
+  const int GH = min(kWaveHeads, a.G - kWaveHeads * hg);      // query heads of this head group
+  const long long rq = blockIdx.z;                   // (b*L + l)*n_q + i
+  const int l = (int)((rq / a.n_q) % a.L);
+  const int b = (int)(rq / ((long long)a.n_q * a.L));
+  const long long urow0 = (((long long)b * a.L + l) * a.H + h) * a.T;
+  int n = a.T;
+  if (a.kv_len) n = min(max(a.kv_len[rq], 0), a.T);
+  const int split = blockIdx.x * (kBlock / 64) + wave;
+  const int t_begin = split * a.chunk, t_end = min(t_begin + a.chunk, n);
+  const int glog2k = 31 - __builtin_clz(a.k.g > 0 ? a.k.g : 1), glog2v = 31 - __builtin_clz(a.v.g > 0 ? a.v.g : 1);
+
+  // ---- query prologue: heads 4 hg .. 4 hg + GH - 1 in the key codec's coordinates,
+  // times the logit scale in log2 units; rows of absent heads are zero
+  const uint16_t* qsrc = a.q + ((size_t)rq * a.Hq + (size_t)h * a.G + (size_t)kWaveHeads * hg) * D;
+  const float* kch = a.k.chan ? a.k.chan + ((size_t)l * a.H + h) * D : nullptr;
+  for (int p = tid; p < kWaveHeads * D; p += kBlock) {
+    const int g = p / D, d = p - g * D;
+    float x = (g < GH) ? h2f(qsrc[(size_t)g * D + d]) : 0.0f;
+    if (kch) x = x / kch[d];
+    qc[g * RS + pidx(d)] = x;
+  }
+  __syncthreads();
+  if (a.k.W > 1) fwht_lds_rows(qc, kWaveHeads, RS, D, a.k.W, a.k.kappa);
+  const float lsc = a.sm_scale * 1.4426950408889634f;
+  float q[kWaveHeads][16];
+#pragma unroll
+  for (int g = 0; g < kWaveHeads; ++g)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) q[g][k] = qc[g * RS + pidx(16 * j + k)] * lsc;
+
+  float acc[kWaveHeads][16];
+  float mref[kWaveHeads], lsum[kWaveHeads];
+#pragma unroll
+  for (int g = 0; g < kWaveHeads; ++g) {
+    mref[g] = -INFINITY;
+    lsum[g] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[g][k] = 0.0f;
+  }
+  // rows past the range re-read a valid row of the unit (weight 0, nothing stored)
+  auto load = [&](int it, RawChunk<KCB, KB>& kr, RawChunk<VCB, VB>& vr) {
+    const long long row = urow0 + min(t_begin + it * RPW + r, a.T - 1);
+    raw_load<KCB, KB>(a.k, row, j, glog2k, kr);
+    raw_load<VCB, VB>(a.v, row, j, glog2v, vr);
+  };
+  auto step = [&](int it, const RawChunk<KCB, KB>& kr, const RawChunk<VCB, VB>& vr) {
+    const bool valid = t_begin + it * RPW + r < t_end;
+    float kv[16];
+    raw_decode<KCB, KB>(a.k, kr, j, a.tab, kv);
+    float sc[kWaveHeads];
+    bool grow = false;
+#pragma unroll
+    for (int g = 0; g < kWaveHeads; ++g) {
+      float x = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) x = __builtin_fmaf(q[g][k], kv[k], x);
+      x = row_lanes_sum(x, LPT);
+      sc[g] = valid ? x : -INFINITY;
+      grow |= sc[g] > mref[g] + 8.0f;
+    }
+    // the wavefront's maximum is only needed when some logit passes the reference by 8
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int g = 0; g < kWaveHeads; ++g) {
+        float mt = sc[g];
+        for (int m = LPT; m < 64; m <<= 1) mt = fmaxf(mt, __shfl_xor(mt, m));   // the same in every lane
+        if (mt > mref[g] + 8.0f) {
+          const float al = (mref[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mref[g] - mt);
+          mref[g] = mt;
+          lsum[g] *= al;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) acc[g][k] *= al;
+        }
+      }
+    }
+    float vv[16];
+    raw_decode<VCB, VB>(a.v, vr, j, a.tab, vv);
+#pragma unroll
+    for (int g = 0; g < kWaveHeads; ++g) {
+      const float pw = (sc[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[g] - mref[g]);
+      lsum[g] += pw;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc[g][k] = __builtin_fmaf(pw, vv[k], acc[g][k]);
+    }
+  };
+  const int n_it = (t_end > t_begin) ? (t_end - t_begin + RPW - 1) / RPW : 0;
+  RawChunk<KCB, KB> k0, k1, k2;
+  RawChunk<VCB, VB> v0, v1, v2;
+  load(0, k0, v0);
+  load(1, k1, v1);
+  load(2, k2, v2);
+  for (int it = 0; it < n_it; it += 3) {
+    step(it, k0, v0);
+    load(it + 3, k0, v0);
+    if (it + 1 >= n_it) break;
+    step(it + 1, k1, v1);
+    load(it + 4, k1, v1);
+    if (it + 2 >= n_it) break;
+    step(it + 2, k2, v2);
+    load(it + 5, k2, v2);
+  }
+  // ---- sum the row slots; lanes of slot 0 write the partial (o in original value
+  // coordinates of the codec, m in natural-log units, l)
+#pragma unroll
+  for (int g = 0; g < kWaveHeads; ++g) {
+    for (int m = LPT; m < 64; m <<= 1) lsum[g] += __shfl_xor(lsum[g], m);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      for (int m = LPT; m < 64; m <<= 1) acc[g][k] += __shfl_xor(acc[g][k], m);
+  }
+  if (split < a.S && r == 0) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    const int P = D + 2;
+#pragma unroll
+    for (int g = 0; g < kWaveHeads; ++g) {
+      if (g < GH) {
+        float* dst = a.ws + (((size_t)rq * a.Hq + (size_t)h * a.G + (size_t)kWaveHeads * hg + g) * a.S + split) * P;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dst[16 * j + k] = acc[g][k];
+        if (j == 0) {
+          dst[D] = (mref[g] == -INFINITY) ? -INFINITY : mref[g] * kLn2;
+          dst[D + 1] = lsum[g];
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ combine
 
 // One block per (query row, query head).  Merges the S split partials:
@@ -658,9 +863,22 @@ static int split_chunk(const kvq_shape& s, int S) {
   return c > 0 ? c : TB;
 }
 
+// Splits (one wavefront each) of the wavefront decode kernel: about 8192 wavefronts
+// in all, a multiple of the 4 wavefronts of a block, at least 4 steps each.
+static int wave_rows_per_step(int D) { return 64 / (D / 16); }
+static int decode_wave_splits(const kvq_shape& s, int Hq, int n_q) {
+  const int G = Hq / s.heads, HG = (G + kWaveHeads - 1) / kWaveHeads;
+  const long long units = (long long)s.batch * s.layers * n_q * s.heads * HG;
+  long long S = (8192 + units - 1) / units;
+  const long long max_s = std::max(1, s.tokens / (4 * wave_rows_per_step(s.head_dim)));
+  S = std::min(S, max_s);
+  S = (S + 3) / 4 * 4;
+  return (int)std::max(4LL, std::min(S, (long long)kMaxSplits));
+}
+
 // Workspace of kvq_decode_attn: split partials of whichever kernel runs.
 size_t decode_ws_bytes(const kvq_shape& s, int Hq, int n_q) {
-  const int S = decode_splits(s, Hq, n_q);
+  const int S = std::max(decode_splits(s, Hq, n_q), decode_wave_splits(s, Hq, n_q));
   const size_t gen = (size_t)s.batch * s.layers * n_q * Hq * S * (s.head_dim + 2) * sizeof(float);
   const size_t fast = fast_part_bytes(s, Hq, n_q);
   return gen > fast ? gen : fast;
@@ -718,8 +936,56 @@ static size_t split_smem(const AArgs& a, bool err) {
   return f * sizeof(float) + (2 * kMaxG * TB + 8 * kMaxG) * acc_bytes;
 }
 
+template <int KCB, int KB, int VCB, int VB>
+static hipError_t launch_wave(const AArgs& a, long long R, hipStream_t st) {
+  const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
+  const size_t smem = (size_t)kWaveHeads * (17 * (a.D / 16) + 17) * sizeof(float);
+  k_decode_wave<KCB, KB, VCB, VB><<<dim3(a.S / 4, a.H * HG, (unsigned)R), kBlock, smem, st>>>(a);
+  return hipGetLastError();
+}
+
+// The codec pairs of the five workloads get their own instantiation (codes decoded
+// with compile-time widths); any other pair takes the runtime-codec one.
+static hipError_t dispatch_wave(const AArgs& a, long long R, hipStream_t st) {
+  const int kc = a.k.cb, kb = a.k.bits, vc = a.v.cb, vb = a.v.bits;
+  auto is = [](int cb, int bits, int c2, int b2) { return cb == c2 && (bits == b2 || b2 < 0); };
+  if (is(kc, kb, KVQ_INT_ABSMAX, 4) && is(vc, vb, KVQ_INT_ABSMAX, 2))
+    return launch_wave<KVQ_INT_ABSMAX, 4, KVQ_INT_ABSMAX, 2>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 4) && is(vc, vb, KVQ_INT_ABSMAX, 4))
+    return launch_wave<KVQ_INT_ABSMAX, 4, KVQ_INT_ABSMAX, 4>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 3) && is(vc, vb, KVQ_INT_ABSMAX, 3))
+    return launch_wave<KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 3>(a, R, st);
+  if (is(kc, kb, KVQ_INT_MINMAX, 4) && is(vc, vb, KVQ_INT_MINMAX, 4))
+    return launch_wave<KVQ_INT_MINMAX, 4, KVQ_INT_MINMAX, 4>(a, R, st);
+  if (is(kc, kb, KVQ_INT_MINMAX, 3) && is(vc, vb, KVQ_INT_MINMAX, 3))
+    return launch_wave<KVQ_INT_MINMAX, 3, KVQ_INT_MINMAX, 3>(a, R, st);
+  if (is(kc, kb, KVQ_TERNARY, -1) && is(vc, vb, KVQ_TERNARY, -1))
+    return launch_wave<KVQ_TERNARY, 2, KVQ_TERNARY, 2>(a, R, st);
+  if (is(kc, kb, KVQ_SIGN, -1) && is(vc, vb, KVQ_SIGN, -1))
+    return launch_wave<KVQ_SIGN, 1, KVQ_SIGN, 1>(a, R, st);
+  if (is(kc, kb, KVQ_NF4, -1) && is(vc, vb, KVQ_INT_ABSMAX, 4))
+    return launch_wave<KVQ_NF4, 4, KVQ_INT_ABSMAX, 4>(a, R, st);
+  if (is(kc, kb, KVQ_INT8_SYM, -1) && is(vc, vb, KVQ_INT8_SYM, -1))
+    return launch_wave<KVQ_INT8_SYM, 8, KVQ_INT8_SYM, 8>(a, R, st);
+  if (is(kc, kb, KVQ_FP16, -1) && is(vc, vb, KVQ_FP16, -1))
+    return launch_wave<KVQ_FP16, 16, KVQ_FP16, 16>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 6) && is(vc, vb, KVQ_FP16, -1))
+    return launch_wave<KVQ_INT_ABSMAX, 6, KVQ_FP16, 16>(a, R, st);
+  return launch_wave<-1, 0, -1, 0>(a, R, st);
+}
+
 hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
   AArgs a = make_aargs(pr);
+  if (a.k.cb != KVQ_RFFT_POLAR && a.k.cb != KVQ_RFFT_CART) {
+    const kvq_shape& s = pr.k->shape;
+    a.S = decode_wave_splits(s, pr.Hq, pr.n_q);
+    const int rpw = wave_rows_per_step(a.D);
+    a.chunk = ((s.tokens + a.S - 1) / a.S + rpw - 1) / rpw * rpw;
+    const long long R = (long long)a.B * a.L * a.n_q;
+    hipError_t e = dispatch_wave(a, R, st);
+    if (e != hipSuccess) return e;
+    return launch_combine_partials(pr, a.S, nullptr, st);
+  }
   const long long R = (long long)a.B * a.L * a.n_q;
   const size_t smem = split_smem(a, false);
   hipError_t e0 = hipFuncSetAttribute((const void*)k_attn_split<false>,
