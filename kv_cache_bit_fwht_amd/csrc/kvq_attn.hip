@@ -408,13 +408,17 @@ template <int CB, int BITS>
 struct RawChunk {                 // a lane's undecoded 16 values of one row
   uint32_t w[8];
   uint16_t s[2], z[2];            // fp16 scale (and min-max min) of values 0-7 and 8-15
-  long long row;                  // for the runtime-codec fallback, which loads as it decodes
+};
+template <int BITS>
+struct RawChunk<-1, BITS> {       // the runtime-codec fallback loads as it decodes
+  long long row;
 };
 
 template <int CB, int BITS>
 __device__ __forceinline__ void raw_load(const DevCodec& c, long long row, int j, int glog2, RawChunk<CB, BITS>& r) {
-  r.row = row;
-  if constexpr (CB >= 0) {
+  if constexpr (CB < 0) {
+    r.row = row;
+  } else {
     load_chunk<BITS>(c.codes, (size_t)row * c.row_bytes + (size_t)j * 2 * BITS, r.w);
     if constexpr (CB != KVQ_FP16) {
       // groups of values 0-7 and 8-15 of the lane (the same group unless g = 8)
@@ -456,8 +460,93 @@ __device__ __forceinline__ float row_lanes_sum(float x, int lpt) {
   return x;
 }
 
+// rFFT keys: lane j of a row owns bins 8j .. 8j+7, whose first fields (magnitude or real
+// codes) form one run of at most 64 bits and whose second fields (phase or imaginary
+// codes) another, so three words hold each run; the last lane also takes the Nyquist
+// bin.  A lane's 8 bins share one scale group (group >= 8).
+struct RawRfft {
+  uint32_t a[3], b[3];            // words holding the lane's first / second field runs
+  uint32_t na[2], nb[2];          // words holding the Nyquist bin's fields
+  uint16_t sa, sb, nsa, nsb;      // scales (Cartesian: real, imaginary) of the lane's group and the Nyquist bin
+};
+
+__device__ __forceinline__ uint32_t rfft_word(const uint32_t* w, int i, int words) { return w[min(i, words - 1)]; }
+
+// nb bits at bit o (< 96, and o + nb <= 96) of the 3-word window w
+// (selects between shifted values, not array elements, so the window stays in registers)
+__device__ __forceinline__ uint32_t field3(const uint32_t w[3], int o, int nb) {
+  const int wi = o >> 5, sh = o & 31;
+  const uint32_t r0 = __builtin_amdgcn_alignbit(w[1], w[0], sh);
+  const uint32_t r1 = __builtin_amdgcn_alignbit(w[2], w[1], sh);
+  const uint32_t r2 = w[2] >> sh;
+  return (wi == 0 ? r0 : (wi == 1 ? r1 : r2)) & ((1u << nb) - 1u);
+}
+
+__device__ __forceinline__ void rfft_raw_load(const DevCodec& c, long long row, int j, int lpt, RawRfft& r) {
+  const RfftCodec& rc = c.rc;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(c.codes) + (size_t)row * rc.words;
+  const uint16_t* sc = c.scales + (size_t)row * rc.nscales;
+  const int ab = rc.bits, bb = (rc.cb == KVQ_RFFT_POLAR) ? rc.pbits : rc.bits;
+  const int f0 = 8 * j, fN = rc.F - 1;
+  const int wa = (f0 * ab) >> 5, wb = (rc.F * ab + f0 * bb) >> 5;
+  const int wna = (fN * ab) >> 5, wnb = (rc.F * ab + fN * bb) >> 5;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    r.a[k] = rfft_word(w, wa + k, rc.words);
+    r.b[k] = rfft_word(w, wb + k, rc.words);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    r.na[k] = rfft_word(w, wna + k, rc.words);
+    r.nb[k] = rfft_word(w, wnb + k, rc.words);
+  }
+  const int gi = f0 / rc.g, gN = fN / rc.g;
+  const int second = (rc.cb == KVQ_RFFT_POLAR) ? 0 : rc.ngroups;   // imaginary scales follow the real ones
+  r.sa = sc[gi];
+  r.sb = sc[second + gi];
+  r.nsa = sc[gN];
+  r.nsb = sc[second + gN];
+  (void)lpt;
+}
+
+// The lane's spectrum values (bins 8j .. 8j+7, then the Nyquist bin) of one row.
+__device__ __forceinline__ void rfft_raw_decode(const DevCodec& c, const RawRfft& r, int j, const float* dirc,
+                                                const float* dirs, float zr[9], float zi[9]) {
+  const RfftCodec& rc = c.rc;
+  const bool polar = rc.cb == KVQ_RFFT_POLAR;
+  const int ab = rc.bits, bb = polar ? rc.pbits : rc.bits;
+  const int f0 = 8 * j, fN = rc.F - 1;
+  const int oa = (f0 * ab) & 31, ob = (rc.F * ab + f0 * bb) & 31;
+  const float off = (float)(1 << (ab - 1));
+  const float sa = h2f(r.sa), sb = h2f(r.sb);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t A = field3(r.a, oa + k * ab, ab), B = field3(r.b, ob + k * bb, bb);
+    if (polar) {
+      const float mu = (float)A * sa;
+      zr[k] = mu * dirc[B];
+      zi[k] = mu * dirs[B];
+    } else {
+      zr[k] = ((float)A - off) * sa;
+      zi[k] = ((float)B - off) * sb;
+    }
+  }
+  const uint32_t wa3[3] = {r.na[0], r.na[1], 0u}, wb3[3] = {r.nb[0], r.nb[1], 0u};
+  const uint32_t A = field3(wa3, (fN * ab) & 31, ab), B = field3(wb3, (rc.F * ab + fN * bb) & 31, bb);
+  if (polar) {
+    const float mu = (float)A * h2f(r.nsa);
+    zr[8] = mu * dirc[B];
+    zi[8] = mu * dirs[B];
+  } else {
+    zr[8] = ((float)A - off) * h2f(r.nsa);
+    zi[8] = ((float)B - off) * h2f(r.nsb);
+  }
+}
+
 template <int KCB, int KB, int VCB, int VB>
 __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
+  constexpr bool KR = (KCB == KVQ_RFFT_POLAR || KCB == KVQ_RFFT_CART);
+  using KRaw = typename std::conditional<KR, RawRfft, RawChunk<KCB, KB>>::type;
   extern __shared__ float smem[];
   const int D = a.D, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -489,13 +578,54 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
     qc[g * RS + pidx(d)] = x;
   }
   __syncthreads();
-  if (a.k.W > 1) fwht_lds_rows(qc, kWaveHeads, RS, D, a.k.W, a.k.kappa);
   const float lsc = a.sm_scale * 1.4426950408889634f;
-  float q[kWaveHeads][16];
+  float q[kWaveHeads][16];                           // the query chunk (codec coordinates)
+  float* dirc = qc + 2 * kWaveHeads * RS;            // rFFT polar keys: sector directions
+  float* dirs = dirc + 256;
+  // rFFT keys: per (head, lane j) the query spectrum of bins 8j .. 8j+7 and the Nyquist
+  // bin: Re[0..7], Im[0..7], Re, Im, 2 pad (16-byte rows)
+  float* qsp = dirs + 256;
+  if constexpr (KR) {
+    // logit = sigma * sum_f w_f (Re Z_f Re Q_f + Im Z_f Im Q_f), Q = DFT(q), w = 1/N at f = 0, N/2, else 2/N
+    const int N = D, F = N / 2 + 1;
+    float* tmp = qc + kWaveHeads * RS;
+    for (int p = tid; p < kWaveHeads * F; p += kBlock) {
+      const int g = p / F, f = p - g * F;
+      float sr = 0.0f, si = 0.0f;
+      for (int nn = 0; nn < N; ++nn) {
+        const int m = (f * nn) & (N - 1);
+        const float cs = (m < N / 2) ? a.tw.tw_c[m] : -a.tw.tw_c[m - N / 2];
+        const float sn = (m < N / 2) ? -a.tw.tw_s[m] : a.tw.tw_s[m - N / 2];   // sin(2 pi m / N)
+        const float x = qc[g * RS + pidx(nn)];
+        sr = __builtin_fmaf(x, cs, sr);
+        si = __builtin_fmaf(-x, sn, si);
+      }
+      const float wf = ((f == 0 || f == N / 2) ? 1.0f : 2.0f) / (float)N * lsc;
+      tmp[g * RS + pidx(f)] = sr * wf;
+      tmp[g * RS + pidx(F + f)] = si * wf;
+    }
+    if (KCB == KVQ_RFFT_POLAR)
+      for (int p = tid; p < (1 << a.k.rc.pbits); p += kBlock) {
+        dirc[p] = a.dirs.dir_c[p];
+        dirs[p] = a.dirs.dir_s[p];
+      }
+    __syncthreads();
+    for (int p = tid; p < kWaveHeads * LPT * 20; p += kBlock) {
+      const int g = p / (LPT * 20), jj = (p / 20) % LPT, e = p % 20;
+      float v = 0.0f;
+      if (e < 16) v = tmp[g * RS + pidx((e < 8 ? 0 : F) + 8 * jj + (e & 7))];
+      else if (jj == LPT - 1 && e == 16) v = tmp[g * RS + pidx(F - 1)];        // Nyquist bin (last lane)
+      else if (jj == LPT - 1 && e == 17) v = tmp[g * RS + pidx(2 * F - 1)];
+      qsp[p] = v;
+    }
+    __syncthreads();
+  } else {
+    if (a.k.W > 1) fwht_lds_rows(qc, kWaveHeads, RS, D, a.k.W, a.k.kappa);
 #pragma unroll
-  for (int g = 0; g < kWaveHeads; ++g)
+    for (int g = 0; g < kWaveHeads; ++g)
 #pragma unroll
-    for (int k = 0; k < 16; ++k) q[g][k] = qc[g * RS + pidx(16 * j + k)] * lsc;
+      for (int k = 0; k < 16; ++k) q[g][k] = qc[g * RS + pidx(16 * j + k)] * lsc;
+  }
 
   float acc[kWaveHeads][16];
   float mref[kWaveHeads], lsum[kWaveHeads];
@@ -507,22 +637,34 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
     for (int k = 0; k < 16; ++k) acc[g][k] = 0.0f;
   }
   // rows past the range re-read a valid row of the unit (weight 0, nothing stored)
-  auto load = [&](int it, RawChunk<KCB, KB>& kr, RawChunk<VCB, VB>& vr) {
+  auto load = [&](int it, KRaw& kr, RawChunk<VCB, VB>& vr) {
     const long long row = urow0 + min(t_begin + it * RPW + r, a.T - 1);
-    raw_load<KCB, KB>(a.k, row, j, glog2k, kr);
+    if constexpr (KR) rfft_raw_load(a.k, row, j, LPT, kr);
+    else raw_load<KCB, KB>(a.k, row, j, glog2k, kr);
     raw_load<VCB, VB>(a.v, row, j, glog2v, vr);
   };
-  auto step = [&](int it, const RawChunk<KCB, KB>& kr, const RawChunk<VCB, VB>& vr) {
+  auto step = [&](int it, const KRaw& kr, const RawChunk<VCB, VB>& vr) {
     const bool valid = t_begin + it * RPW + r < t_end;
-    float kv[16];
-    raw_decode<KCB, KB>(a.k, kr, j, a.tab, kv);
+    float kv[16], zr[9], zi[9];
+    if constexpr (KR) rfft_raw_decode(a.k, kr, j, dirc, dirs, zr, zi);
+    else raw_decode<KCB, KB>(a.k, kr, j, a.tab, kv);
     float sc[kWaveHeads];
     bool grow = false;
 #pragma unroll
     for (int g = 0; g < kWaveHeads; ++g) {
       float x = 0.0f;
+      if constexpr (KR) {
+        const float4* qv = reinterpret_cast<const float4*>(qsp + (g * LPT + j) * 20);
+        const float4 r0 = qv[0], r1 = qv[1], i0 = qv[2], i1 = qv[3], ny = qv[4];
+        const float qr8[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        const float qi8[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-      for (int k = 0; k < 16; ++k) x = __builtin_fmaf(q[g][k], kv[k], x);
+        for (int k = 0; k < 8; ++k) x = __builtin_fmaf(qi8[k], zi[k], __builtin_fmaf(qr8[k], zr[k], x));
+        x = __builtin_fmaf(ny.y, zi[8], __builtin_fmaf(ny.x, zr[8], x));
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) x = __builtin_fmaf(q[g][k], kv[k], x);
+      }
       x = row_lanes_sum(x, LPT);
       sc[g] = valid ? x : -INFINITY;
       grow |= sc[g] > mref[g] + 8.0f;
@@ -553,20 +695,34 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
     }
   };
   const int n_it = (t_end > t_begin) ? (t_end - t_begin + RPW - 1) / RPW : 0;
-  RawChunk<KCB, KB> k0, k1, k2;
-  RawChunk<VCB, VB> v0, v1, v2;
-  load(0, k0, v0);
-  load(1, k1, v1);
-  load(2, k2, v2);
-  for (int it = 0; it < n_it; it += 3) {
-    step(it, k0, v0);
-    load(it + 3, k0, v0);
-    if (it + 1 >= n_it) break;
-    step(it + 1, k1, v1);
-    load(it + 4, k1, v1);
-    if (it + 2 >= n_it) break;
-    step(it + 2, k2, v2);
-    load(it + 5, k2, v2);
+  if constexpr (KR) {                                // two iterations in flight (registers)
+    KRaw k0, k1;
+    RawChunk<VCB, VB> v0, v1;
+    load(0, k0, v0);
+    load(1, k1, v1);
+    for (int it = 0; it < n_it; it += 2) {
+      step(it, k0, v0);
+      load(it + 2, k0, v0);
+      if (it + 1 >= n_it) break;
+      step(it + 1, k1, v1);
+      load(it + 3, k1, v1);
+    }
+  } else {
+    KRaw k0, k1, k2;
+    RawChunk<VCB, VB> v0, v1, v2;
+    load(0, k0, v0);
+    load(1, k1, v1);
+    load(2, k2, v2);
+    for (int it = 0; it < n_it; it += 3) {
+      step(it, k0, v0);
+      load(it + 3, k0, v0);
+      if (it + 1 >= n_it) break;
+      step(it + 1, k1, v1);
+      load(it + 4, k1, v1);
+      if (it + 2 >= n_it) break;
+      step(it + 2, k2, v2);
+      load(it + 5, k2, v2);
+    }
   }
   // ---- sum the row slots; lanes of slot 0 write the partial (o in original value
   // coordinates of the codec, m in natural-log units, l)
@@ -939,7 +1095,7 @@ static size_t split_smem(const AArgs& a, bool err) {
 template <int KCB, int KB, int VCB, int VB>
 static hipError_t launch_wave(const AArgs& a, long long R, hipStream_t st) {
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
-  const size_t smem = (size_t)kWaveHeads * (17 * (a.D / 16) + 17) * sizeof(float);
+  const size_t smem = ((size_t)2 * kWaveHeads * (17 * (a.D / 16) + 17) + 512 + kWaveHeads * 16 * 20) * sizeof(float);
   k_decode_wave<KCB, KB, VCB, VB><<<dim3(a.S / 4, a.H * HG, (unsigned)R), kBlock, smem, st>>>(a);
   return hipGetLastError();
 }
@@ -971,12 +1127,17 @@ static hipError_t dispatch_wave(const AArgs& a, long long R, hipStream_t st) {
     return launch_wave<KVQ_FP16, 16, KVQ_FP16, 16>(a, R, st);
   if (is(kc, kb, KVQ_INT_ABSMAX, 6) && is(vc, vb, KVQ_FP16, -1))
     return launch_wave<KVQ_INT_ABSMAX, 6, KVQ_FP16, 16>(a, R, st);
+  if (kc == KVQ_RFFT_POLAR && vc == KVQ_FP16) return launch_wave<KVQ_RFFT_POLAR, 0, KVQ_FP16, 16>(a, R, st);
+  if (kc == KVQ_RFFT_CART && vc == KVQ_FP16) return launch_wave<KVQ_RFFT_CART, 0, KVQ_FP16, 16>(a, R, st);
   return launch_wave<-1, 0, -1, 0>(a, R, st);
 }
 
 hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
   AArgs a = make_aargs(pr);
-  if (a.k.cb != KVQ_RFFT_POLAR && a.k.cb != KVQ_RFFT_CART) {
+  // rFFT keys on the wavefront kernel: fp16 values, and a lane's 8 bins in one scale group
+  const bool rk = a.k.cb == KVQ_RFFT_POLAR || a.k.cb == KVQ_RFFT_CART;
+  const bool rk_wave = rk && a.v.cb == KVQ_FP16 && a.k.rc.g >= 8 && (a.k.rc.g & 7) == 0;
+  if (!rk || rk_wave) {
     const kvq_shape& s = pr.k->shape;
     a.S = decode_wave_splits(s, pr.Hq, pr.n_q);
     const int rpw = wave_rows_per_step(a.D);
