@@ -1,7 +1,8 @@
 // rFFT physical codecs ([FMAG-R] HF forum thread "Fourier Magnitude KV Cache
 // Quantization", Colab-probe reply: rFFT + packed magnitude index + packed
 // phase-angle index, and the real/imaginary control): quantise+pack and
-// dequantise kernels.  One wavefront per row; the transform runs in LDS.
+// dequantise kernels.  One wavefront per row, in an LDS region of its own, so the
+// per-row steps need no block barrier; the transform runs in LDS.
 #include "kvq_rfft.hpp"
 
 namespace kvq {
@@ -23,6 +24,29 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kMaxN = 256;
 constexpr int kMaxWords = 72;
 
+// The constant tables in LDS, copied once per block: per-lane indexed reads of the
+// kernel-argument copies would each be a memory round trip.
+struct LdsTables {
+  float twc[kMaxN / 2], tws[kMaxN / 2];    // twiddles of head_dim
+  float dirc[256], dirs[256];              // phase-sector directions
+  float bndc[32], bnds[32];                // first-octant sector boundaries
+};
+__device__ __forceinline__ void load_tables(const RArgs& a, LdsTables& t) {
+  for (int i = threadIdx.x; i < kMaxN / 2; i += kBlock) {
+    t.twc[i] = a.tw.tw_c[i];
+    t.tws[i] = a.tw.tw_s[i];
+  }
+  for (int i = threadIdx.x; i < 256; i += kBlock) {
+    t.dirc[i] = a.pt.dir_c[i];
+    t.dirs[i] = a.pt.dir_s[i];
+  }
+  for (int i = threadIdx.x; i < 32; i += kBlock) {
+    t.bndc[i] = a.pt.bnd_c[i];
+    t.bnds[i] = a.pt.bnd_s[i];
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ void unit_of(long long row, int T, int H, int L, int& l, int& h) {
   const long long u = row / T;
   h = (int)(u % H);
@@ -35,6 +59,8 @@ __global__ __launch_bounds__(kBlock) void k_rfft_quantize(RArgs a) {
   __shared__ float s_inv[kWaves][64];
   __shared__ uint16_t s_sc[kWaves][64];
   __shared__ uint32_t s_w[kWaves][kMaxWords];
+  __shared__ LdsTables ltab;
+  load_tables(a, ltab);
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const RfftCodec& c = a.c;
   const int N = c.N, F = c.F, nb = __builtin_ctz((unsigned)N);
@@ -55,8 +81,8 @@ __global__ __launch_bounds__(kBlock) void k_rfft_quantize(RArgs a) {
       re[bitrev(n, nb)] = v;
       im[bitrev(n, nb)] = 0.0f;
     }
-    __syncthreads();
-    fft_lds(re, im, N, a.tw, false, lane, 64);
+    wave_lds_sync();
+    fft_lds(re, im, N, ltab.twc, ltab.tws, false, lane, 64);
     // per-bin value(s) to code
     for (int f = lane; f < F; f += 64) {
       if (c.cb == KVQ_RFFT_POLAR) {
@@ -67,7 +93,7 @@ __global__ __launch_bounds__(kBlock) void k_rfft_quantize(RArgs a) {
       }
     }
     for (int k = lane; k < c.words; k += 64) s_w[wv][k] = 0u;
-    __syncthreads();
+    wave_lds_sync();
     // group scales: one lane per (component, group), serial extreme over the bins
     if (lane < c.nscales) {
       const int comp = lane / c.ngroups, gi = lane - comp * c.ngroups;
@@ -87,14 +113,14 @@ __global__ __launch_bounds__(kBlock) void k_rfft_quantize(RArgs a) {
       s_sc[wv][lane] = s16;
       s_inv[wv][lane] = inv_scale(s16);
     }
-    __syncthreads();
+    wave_lds_sync();
     for (int f = lane; f < F; f += 64) {
       const int gi = f / c.g;
       if (c.cb == KVQ_RFFT_POLAR) {
         const float hi = (float)((1 << c.bits) - 1);
         const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(s_val[wv][0][f] * s_inv[wv][gi]), 0.0f), hi);
         const uint32_t qm = (uint32_t)(int)q;
-        const uint32_t k = (uint32_t)phase_sector(re[f], im[f], 1 << c.pbits, a.pt.bnd_c, a.pt.bnd_s);
+        const uint32_t k = (uint32_t)phase_sector(re[f], im[f], 1 << c.pbits, ltab.bndc, ltab.bnds);
         const int p0 = f * c.bits, p1 = F * c.bits + f * c.pbits;
         atomicOr(&s_w[wv][p0 >> 5], qm << (p0 & 31));
         if ((p0 & 31) + c.bits > 32) atomicOr(&s_w[wv][(p0 >> 5) + 1], qm >> (32 - (p0 & 31)));
@@ -113,24 +139,25 @@ __global__ __launch_bounds__(kBlock) void k_rfft_quantize(RArgs a) {
         }
       }
     }
-    __syncthreads();
+    wave_lds_sync();
     if (active) {
       for (int k = lane; k < c.words; k += 64) a.codes[(size_t)row * c.words + k] = s_w[wv][k];
       if (lane < c.nscales) a.scales[(size_t)row * c.nscales + lane] = s_sc[wv][lane];
     }
-    __syncthreads();
+    wave_lds_sync();
   }
 }
 
 // Inverse: spectrum of one row (from its codes) -> real values in re[] (times 1/N).
-__device__ void rfft_decode_row(const RArgs& a, long long row, bool active, float* re, float* im, int lane) {
+__device__ void rfft_decode_row(const RArgs& a, const LdsTables& ltab, long long row, bool active, float* re, float* im,
+                                int lane) {
   const RfftCodec& c = a.c;
   const int N = c.N, F = c.F, nb = __builtin_ctz((unsigned)N);
   const uint32_t* w = a.codes + (size_t)row * c.words;
   const uint16_t* s = a.scales + (size_t)row * c.nscales;
   for (int f = lane; f < F; f += 64) {
     float zr = 0.0f, zi = 0.0f;
-    if (active) rfft_bin_value(c, w, s, f, a.pt.dir_c, a.pt.dir_s, zr, zi);
+    if (active) rfft_bin_value(c, w, s, f, ltab.dirc, ltab.dirs, zr, zi);
     re[bitrev(f, nb)] = zr;
     im[bitrev(f, nb)] = zi;
     if (f >= 1 && f < N / 2) {
@@ -138,19 +165,21 @@ __device__ void rfft_decode_row(const RArgs& a, long long row, bool active, floa
       im[bitrev(N - f, nb)] = -zi;
     }
   }
-  __syncthreads();
-  fft_lds(re, im, N, a.tw, true, lane, 64);
+  wave_lds_sync();
+  fft_lds(re, im, N, ltab.twc, ltab.tws, true, lane, 64);
 }
 
 __global__ __launch_bounds__(kBlock) void k_rfft_dequant(RArgs a) {
   __shared__ float s_re[kWaves][kMaxN], s_im[kWaves][kMaxN];
+  __shared__ LdsTables ltab;
+  load_tables(a, ltab);
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = a.c.N;
   const float invN = 1.0f / (float)N;
   for (long long base = (long long)blockIdx.x * kWaves; base < a.rows; base += (long long)gridDim.x * kWaves) {
     const long long row = base + wv;
     const bool active = row < a.rows;
-    rfft_decode_row(a, row, active, s_re[wv], s_im[wv], lane);
+    rfft_decode_row(a, ltab, row, active, s_re[wv], s_im[wv], lane);
     if (active) {
       const float* cp = nullptr;
       if (a.chan) {
@@ -164,13 +193,15 @@ __global__ __launch_bounds__(kBlock) void k_rfft_dequant(RArgs a) {
         a.xhat[(size_t)row * N + n] = v;
       }
     }
-    __syncthreads();
+    wave_lds_sync();
   }
 }
 
 // Per-unit squared error of rFFT-coded keys against fp16: partial sums per block.
 __global__ __launch_bounds__(kBlock) void k_rfft_kverr(RArgs a, double* part, int chunks) {
   __shared__ float s_re[kWaves][kMaxN], s_im[kWaves][kMaxN];
+  __shared__ LdsTables ltab;
+  load_tables(a, ltab);
   __shared__ double s_red[2][kBlock];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = a.c.N;
@@ -189,7 +220,7 @@ __global__ __launch_bounds__(kBlock) void k_rfft_kverr(RArgs a, double* part, in
     const int t = tb + wv;
     const bool active = t < t1;
     const long long row = unit * T + t;
-    rfft_decode_row(a, row, active, s_re[wv], s_im[wv], lane);
+    rfft_decode_row(a, ltab, row, active, s_re[wv], s_im[wv], lane);
     if (active) {
       for (int n = lane; n < N; n += 64) {
         float v = s_re[wv][n] * invN;
@@ -200,7 +231,7 @@ __global__ __launch_bounds__(kBlock) void k_rfft_kverr(RArgs a, double* part, in
         sx += x * x;
       }
     }
-    __syncthreads();
+    wave_lds_sync();
   }
   s_red[0][threadIdx.x] = se;
   s_red[1][threadIdx.x] = sx;

@@ -77,21 +77,26 @@ __device__ __forceinline__ void rfft_bin_value(const RfftCodec& c, const uint32_
   }
 }
 
+// Orders one wavefront's LDS accesses: every earlier LDS access of the wavefront has
+// completed before any later one is issued, and the compiler moves no memory access
+// across it.  Enough between lanes of one wavefront working on its own LDS region.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // In-place radix-2 DIT FFT of N complex values in LDS (already in bit-reversed
-// order).  Butterflies are spread over the `nl` lanes [0, nl) of a wavefront
-// (`lane` < 0: this thread only synchronises).  Every thread of the block must
-// call it: it ends each stage with a block barrier.  conj selects conjugate
-// twiddles (the inverse transform, without the 1/N).
-__device__ __forceinline__ void fft_lds(float* re, float* im, int N, const FftTables& tw, bool conj, int lane,
+// order).  Butterflies are spread over the `nl` lanes [0, nl) of one wavefront,
+// which owns the arrays; each stage ends with a wavefront-local LDS sync.  conj
+// selects conjugate twiddles (the inverse transform, without the 1/N).
+__device__ __forceinline__ void fft_lds(float* re, float* im, int N, const float* twc, const float* tws, bool conj,
+                                        int lane,
                                         int nl) {
   for (int span = 2; span <= N; span <<= 1) {
     const int half = span >> 1, step = N / span;
-    if (lane >= 0) {
+    {
       for (int b = lane; b < N / 2; b += nl) {
         const int blk = b / half, jj = b - blk * half;
         const int top = blk * span + jj, bot = top + half;
-        const float wr = tw.tw_c[jj * step];
-        const float wi = conj ? -tw.tw_s[jj * step] : tw.tw_s[jj * step];
+        const float wr = twc[jj * step];
+        const float wi = conj ? -tws[jj * step] : tws[jj * step];
         const float br = re[bot], bi = im[bot];
         const float tr = br * wr - bi * wi;
         const float ti = br * wi + bi * wr;
@@ -102,7 +107,7 @@ __device__ __forceinline__ void fft_lds(float* re, float* im, int N, const FftTa
         im[top] = xi + ti;
       }
     }
-    __syncthreads();
+    wave_lds_sync();
   }
 }
 
