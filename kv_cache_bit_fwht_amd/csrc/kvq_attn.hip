@@ -435,9 +435,15 @@ __device__ __forceinline__ void raw_load(const DevCodec& c, long long row, int j
 
 template <int CB, int BITS>
 __device__ __forceinline__ void raw_decode(const DevCodec& c, const RawChunk<CB, BITS>& r, int j, const Tables& tab,
-                                           float v[16]) {
+                                           const float* nf4_lds, float v[16]) {
   if constexpr (CB < 0) {
     dq_row_any(c, r.row, j, tab, v);
+  } else if constexpr (CB == KVQ_NF4) {              // levels from LDS (a per-lane index)
+    uint32_t cc[16];
+    unpack16<BITS>(r.w, cc);
+    const float s0 = h2f(r.s[0]), s1 = h2f(r.s[1]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = nf4_lds[cc[i] & 15u] * (i < 8 ? s0 : s1);
   } else {
     uint32_t cc[16];
     unpack16<BITS>(r.w, cc);
@@ -577,6 +583,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
     if (kch) x = x / kch[d];
     qc[g * RS + pidx(d)] = x;
   }
+  if (tid < 16) qc[2 * kWaveHeads * RS + 512 + kWaveHeads * 16 * 20 + tid] = a.tab.nf4_lv[tid];   // NF4 levels
   __syncthreads();
   const float lsc = a.sm_scale * 1.4426950408889634f;
   float q[kWaveHeads][16];                           // the query chunk (codec coordinates)
@@ -585,6 +592,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
   // rFFT keys: per (head, lane j) the query spectrum of bins 8j .. 8j+7 and the Nyquist
   // bin: Re[0..7], Im[0..7], Re, Im, 2 pad (16-byte rows)
   float* qsp = dirs + 256;
+  float* const nf4l = qsp + kWaveHeads * 16 * 20;    // NF4 levels (written before the first barrier)
   if constexpr (KR) {
     // logit = sigma * sum_f w_f (Re Z_f Re Q_f + Im Z_f Im Q_f), Q = DFT(q), w = 1/N at f = 0, N/2, else 2/N
     const int N = D, F = N / 2 + 1;
@@ -647,7 +655,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
     const bool valid = t_begin + it * RPW + r < t_end;
     float kv[16], zr[9], zi[9];
     if constexpr (KR) rfft_raw_decode(a.k, kr, j, dirc, dirs, zr, zi);
-    else raw_decode<KCB, KB>(a.k, kr, j, a.tab, kv);
+    else raw_decode<KCB, KB>(a.k, kr, j, a.tab, nf4l, kv);
     float sc[kWaveHeads];
     bool grow = false;
 #pragma unroll
@@ -685,7 +693,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
       }
     }
     float vv[16];
-    raw_decode<VCB, VB>(a.v, vr, j, a.tab, vv);
+    raw_decode<VCB, VB>(a.v, vr, j, a.tab, nf4l, vv);
 #pragma unroll
     for (int g = 0; g < kWaveHeads; ++g) {
       const float pw = (sc[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[g] - mref[g]);
@@ -1095,7 +1103,7 @@ static size_t split_smem(const AArgs& a, bool err) {
 template <int KCB, int KB, int VCB, int VB>
 static hipError_t launch_wave(const AArgs& a, long long R, hipStream_t st) {
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
-  const size_t smem = ((size_t)2 * kWaveHeads * (17 * (a.D / 16) + 17) + 512 + kWaveHeads * 16 * 20) * sizeof(float);
+  const size_t smem = ((size_t)2 * kWaveHeads * (17 * (a.D / 16) + 17) + 512 + kWaveHeads * 16 * 20 + 16) * sizeof(float);
   k_decode_wave<KCB, KB, VCB, VB><<<dim3(a.S / 4, a.H * HG, (unsigned)R), kBlock, smem, st>>>(a);
   return hipGetLastError();
 }

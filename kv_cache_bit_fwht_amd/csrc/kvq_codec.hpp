@@ -164,12 +164,12 @@ __device__ __forceinline__ void encode16(const float v[16], int g, const Tables&
       } else if constexpr (CB == KVQ_INT8_SYM) {
         c[i] = (uint32_t)((int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(t), -127.0f), 127.0f) + 127);
       } else {
-        // number of midpoints strictly below t (binary search; mid[15] = +inf)
-        int k = 0;
+        // number of midpoints strictly below t (the 15 compares use uniform table
+        // indices: a per-lane index into the argument table would be a memory read)
+        uint32_t k = 0;
 #pragma unroll
-        for (int st = 8; st >= 1; st >>= 1)
-          if (tab.nf4_mid[k + st - 1] < t) k += st;
-        c[i] = (uint32_t)k;
+        for (int m = 0; m < 15; ++m) k += (tab.nf4_mid[m] < t) ? 1u : 0u;
+        c[i] = k;
       }
     }
   } else if constexpr (CB == KVQ_SIGN) {
