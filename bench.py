@@ -156,14 +156,17 @@ def _median_time(torch, fn, reps):
 
 def secondary(workload, reps):
     """The other decode configurations (not the headline line): c4, extreme low-bit
-    codecs at head_dim 128 with layer 0 kept in fp16, and c5, transformed keys at
-    head_dim 128 with fp16 values.  One JSON line per arm: quantize+pack of the
-    arm's K and V, and one decode step (every layer, every query head, B queries)."""
+    codecs at head_dim 128 with layer 0 kept in fp16; c5, transformed keys at
+    head_dim 128 with fp16 values; c3v, the 64K cache with rotated 4-bit keys and
+    each value codebook (the one-sided 2-bit grid, and the symmetric and Gaussian
+    Lloyd-Max grids named as the next test), with the attention KL and output
+    error of 16 queries.  One JSON line per arm: quantize+pack of the arm's K and
+    V, and one decode step (every layer, every query head, B queries)."""
     import torch
     import kv_cache_bit_fwht_amd as K
     import synth
     dev = torch.device("cuda:0")
-    w = synth.get(workload)
+    w = synth.get("c3" if workload == "c3v" else workload)
     log(f"generating {w.description}")
     Kx, Vx = synth.gen_kv(w)
     q, _ = synth.gen_queries(w)
@@ -172,7 +175,15 @@ def secondary(workload, reps):
     qd = torch.from_numpy(np.ascontiguousarray(q[:, :, :1]).view(np.int16)).to(dev)
     del Kx, Vx
     f16 = K.Codec(K.FP16)
-    if workload == "c4":
+    if workload == "c3v":
+        kc3 = K.Codec(K.INT_ABSMAX, 4, 128, 256)
+        arms = {"V int2 absmax g128 (one-sided grid)": (kc3, K.Codec(K.INT_ABSMAX, 2, 128, 0)),
+                "V int2 symmetric g128, rotated": (kc3, K.Codec(K.INT_SYM, 2, 128, 256)),
+                "V Lloyd-Max 2-bit g128, rotated": (kc3, K.Codec(K.LLOYD, 2, 128, 256)),
+                "V int3 symmetric g128, rotated": (kc3, K.Codec(K.INT_SYM, 3, 128, 256)),
+                "V Lloyd-Max 3-bit g128, rotated": (kc3, K.Codec(K.LLOYD, 3, 128, 256))}
+        lo = 0
+    elif workload == "c4":
         arms = {"ternary g8": (K.Codec(K.TERNARY, 2, 8, 0),) * 2, "sign g8": (K.Codec(K.SIGN, 1, 8, 0),) * 2,
                 "NF4 K g64 + int4 V g64": (K.Codec(K.NF4, 4, 64, 0), K.Codec(K.INT_ABSMAX, 4, 64, 0)),
                 "int8 g128": (K.Codec(K.INT8_SYM, 8, 128, 0),) * 2}
@@ -217,6 +228,22 @@ def secondary(workload, reps):
         K.kvq_decode_attn(kp, vp, Hq, 1, qq, None, 0.0, out, lse, ws, wsb)
         torch.cuda.synchronize()
         t_d = _median_time(torch, lambda: K.kvq_decode_attn(kp, vp, Hq, 1, qq, None, 0.0, out, lse, ws, wsb), reps)
+        quality = None
+        if workload == "c3v":                        # attention-visible error of 16 queries
+            nqe = 16
+            qe = torch.from_numpy(np.ascontiguousarray(q[:, :, :nqe]).view(np.int16)).to(dev)
+            kl = torch.empty((B, L, nqe, Hq), dtype=torch.float32, device=dev)
+            re = torch.empty_like(kl)
+            kv = torch.empty((B, L, H, 4), dtype=torch.float64, device=dev)
+            web = K.kvq_attn_error_workspace(shape, Hq, nqe)
+            we = torch.empty(max(web, 16), dtype=torch.uint8, device=dev)
+            K.kvq_attn_error(kd, vd, kp, vp, Hq, nqe, qe, None, 0.0, kl, re, kv, we, web)
+            torch.cuda.synchronize()
+            kvn = kv.double().sum(dim=(0, 1, 2)).cpu().numpy()
+            quality = {"mean_KL": float(kl.double().mean()), "p99_KL": float(torch.quantile(kl.double().flatten(), 0.99)),
+                       "mean_out_relerr": float(re.double().mean()), "K_rel_sq_err": float(kvn[0] / kvn[1]),
+                       "V_rel_sq_err": float(kvn[2] / kvn[3]), "queries": nqe}
+            del we, kl, re, kv
         kw, ks, km = K.kvq_packed_layout(shape, kc)
         vw, vs, vm = K.kvq_packed_layout(shape, vc)
         kb = rows * (4 * kw + 2 * (ks + km))
@@ -225,16 +252,20 @@ def secondary(workload, reps):
         d_bytes = kb + vb
         anchor_bytes = (B * H * T * D * 2 * 2) if lo else 0
         step = t_d + anchor_s
-        print(json.dumps({
+        rec = {
             "workload": f"{workload}: B={B} L={L} H={H} T={T} D={D} Hq={Hq}" + (", layer 0 fp16" if lo else ""),
             "arm": name,
+            "bits_per_value": round((K.kvq_bits_per_value(kc, D) + K.kvq_bits_per_value(vc, D)) / 2, 4),
             "quantize_pack": {"us": round(t_q * 1e6, 1), "GB/s": round(q_bytes / t_q / 1e9, 1),
                               "frac_hbm": round(q_bytes / t_q / 1e9 / HBM_PEAK_GBS, 4), "bytes": q_bytes},
             "decode_step": {"us": round(step * 1e6, 1), "tok/s": round(B / step, 1),
                             "GB/s": round((d_bytes + anchor_bytes) / step / 1e9, 1),
                             "frac_hbm": round((d_bytes + anchor_bytes) / step / 1e9 / HBM_PEAK_GBS, 4),
                             "bytes": d_bytes + anchor_bytes, "anchor_us": round(anchor_s * 1e6, 1)},
-        }), flush=True)
+        }
+        if quality:
+            rec["quality"] = quality
+        print(json.dumps(rec), flush=True)
         del kp, vp
         torch.cuda.empty_cache()
 
@@ -251,8 +282,9 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for hardware-counter passes: a known-size copy (the counters' "
                          "calibration), one quantize+pack pair and --decode-queries decode calls")
-    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5"],
-                    help="c3: the headline line (default); c4/c5: one line per codec arm of those configs")
+    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v"],
+                    help="c3: the headline line (default); c4/c5: one line per codec arm of those configs; "
+                         "c3v: the 64K cache with each value codebook, with attention KL")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions per arm (c4/c5)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -64,6 +64,14 @@ typedef enum {
  *              phase-sector code ([FMAG-R] physical codec).  Keys only.
  *  RFFT_CART   rFFT; real and imaginary parts each INT_ABSMAX with `bits` bits
  *              per `group` bins ([FMAG-R] real/imag control).  Keys only.
+ *  INT_SYM     symmetric grid {-(2^b-1)/2, ..., (2^b-1)/2} * s (half-integer
+ *              levels, as many on each side), s = absmax / ((2^b-1)/2); bits
+ *              2..8.  The symmetric value grid [E22L] Result names as the next
+ *              test after the one-sided {-2,-1,0,1} grid.
+ *  LLOYD       Lloyd-Max levels of a unit Gaussian (2^b of them) * s, s = the
+ *              group's root mean square; bits 2..4 ([E22L] Result: Gaussian
+ *              Lloyd-Max levels on rotated values; use rot_width for the
+ *              rotation).
  * Scalar rules (rounding, ties, zero groups) are those of the CPU oracle:
  * binary32 arithmetic, round-to-nearest-even, fp16 scales saturated to
  * +-65504 and never -0. */
@@ -76,13 +84,16 @@ typedef enum {
   KVQ_NF4 = 5,
   KVQ_INT8_SYM = 6,
   KVQ_RFFT_POLAR = 7,
-  KVQ_RFFT_CART = 8
+  KVQ_RFFT_CART = 8,
+  KVQ_INT_SYM = 9,
+  KVQ_LLOYD = 10
 } kvq_codebook;
 
 typedef struct {
   int32_t codebook;   /* kvq_codebook */
-  int32_t bits;       /* INT_ABSMAX/INT_MINMAX: 2..8; RFFT_*: 2..8 magnitude/component
-                         bits; ignored (implied) for the other codebooks */
+  int32_t bits;       /* INT_ABSMAX/INT_MINMAX/INT_SYM: 2..8; LLOYD: 2..4; RFFT_*:
+                         2..8 magnitude/component bits; ignored (implied) for the
+                         other codebooks */
   int32_t group;      /* values per scale: 8, 16, 32, 64, 128 or 256 (<= head_dim);
                          RFFT_*: bins per scale (8..128) */
   int32_t rot_width;  /* Walsh-Hadamard width: 0 (none) or a power of two in
@@ -133,7 +144,7 @@ double kvq_bits_per_value(const kvq_codec* codec, int32_t head_dim);
  * which = 0 NF4 levels (16), 1 NF4 midpoints (15), 2/3 FFT twiddle cos/-sin
  * for head_dim n*2 (n = D/2 entries), 4/5 phase-sector direction cos/sin for
  * 2^aux sectors (n = 2^aux), 6/7 first-octant sector boundary cos/sin (n =
- * 2^aux / 8). */
+ * 2^aux / 8), 8/9/10 LLOYD levels for 2/3/4 bits (n = 2^bits). */
 kvq_status kvq_constant_table(int32_t which, int32_t n, float* out);
 
 /* Per-channel key multipliers from a calibration sequence ([E21W] What I

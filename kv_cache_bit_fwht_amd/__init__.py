@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 # codebooks (kvq_codebook)
-FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART = range(9)
+FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART, INT_SYM, LLOYD = range(11)
 
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_ALIGN",
           -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}

@@ -24,6 +24,31 @@ static double norm_ppf(double p) {
   return 0.5 * (lo + hi);
 }
 
+// Lloyd-Max quantiser of the standard normal with n levels (fp64 fixed point,
+// rounded to binary32): boundaries halfway between neighbouring levels, each
+// level the mean of the normal over its cell, (phi(a) - phi(b)) / (Phi(b) - Phi(a)).
+// Started from the cell-centre quantiles and iterated to convergence.
+static void lloyd_max_levels(int n, float* out) {
+  double L[16], t[17];
+  for (int k = 0; k < n; ++k) L[k] = norm_ppf((k + 0.5) / n);
+  auto pdf = [](double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI); };
+  auto cdf = [](double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); };
+  for (int it = 0; it < 100000; ++it) {
+    t[0] = -INFINITY;
+    t[n] = INFINITY;
+    for (int k = 1; k < n; ++k) t[k] = 0.5 * (L[k - 1] + L[k]);
+    double change = 0.0;
+    for (int k = 0; k < n; ++k) {
+      const double m = (pdf(t[k]) - pdf(t[k + 1])) / (cdf(t[k + 1]) - cdf(t[k]));
+      change = std::max(change, std::fabs(m - L[k]));
+      L[k] = m;
+    }
+    if (change < 1e-14) break;
+  }
+  for (int k = 0; k < n; ++k) out[k] = (float)L[k];
+  for (int k = n; k < 16; ++k) out[k] = INFINITY;
+}
+
 // NormalFloat-4 (QLoRA, Dettmers et al. 2023, section 3): 8 positive normal
 // quantiles at probabilities linspace(1-d, 1/2, 9) without its last point, 7
 // negative ones at linspace(1-d, 1/2, 8) without its last point, d = (1/30 +
@@ -53,6 +78,7 @@ static Tables build_tables() {
     t.nf4_mid[i] = s * 0.5f;
   }
   t.nf4_mid[15] = INFINITY;
+  for (int b = 2; b <= 4; ++b) lloyd_max_levels(1 << b, t.lloyd_lv[b - 2]);
   return t;
 }
 
@@ -103,7 +129,7 @@ static bool is_rfft(int cb) { return cb == KVQ_RFFT_POLAR || cb == KVQ_RFFT_CART
 static kvq_status check_codec(const kvq_codec* c, int D) {
   if (!c) return KVQ_ERR_ARG;
   const int cb = c->codebook;
-  if (cb < KVQ_FP16 || cb > KVQ_RFFT_CART) return KVQ_ERR_UNSUPPORTED;
+  if (cb < KVQ_FP16 || cb > KVQ_LLOYD) return KVQ_ERR_UNSUPPORTED;
   if (cb == KVQ_FP16) return KVQ_OK;
   if (is_rfft(cb)) {
     if (c->bits < 2 || c->bits > 8) return KVQ_ERR_UNSUPPORTED;
@@ -112,9 +138,10 @@ static kvq_status check_codec(const kvq_codec* c, int D) {
     if (cb == KVQ_RFFT_POLAR && (c->aux_bits < 3 || c->aux_bits > 8)) return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
   }
-  if (cb == KVQ_INT_ABSMAX || cb == KVQ_INT_MINMAX) {
+  if (cb == KVQ_INT_ABSMAX || cb == KVQ_INT_MINMAX || cb == KVQ_INT_SYM) {
     if (c->bits < 2 || c->bits > 8) return KVQ_ERR_UNSUPPORTED;
   }
+  if (cb == KVQ_LLOYD && (c->bits < 2 || c->bits > 4)) return KVQ_ERR_UNSUPPORTED;
   if (!pow2(c->group) || c->group < 8 || c->group > 256 || c->group > D) return KVQ_ERR_UNSUPPORTED;
   if (c->rot_width != 0 && (!pow2(c->rot_width) || c->rot_width < 2 || c->rot_width > D))
     return KVQ_ERR_UNSUPPORTED;
@@ -236,6 +263,12 @@ kvq_status kvq_constant_table(int32_t which, int32_t n, float* out) {
     FftTables t;
     host_fft_tables(2 * n, &t);
     std::memcpy(out, which == 2 ? t.tw_c : t.tw_s, sizeof(float) * n);
+    return KVQ_OK;
+  }
+  if (which >= 8 && which <= 10) {
+    const int b = which - 6;
+    if (n != (1 << b)) return KVQ_ERR_ARG;
+    std::memcpy(out, host_tables().lloyd_lv[b - 2], sizeof(float) * n);
     return KVQ_OK;
   }
   if (which >= 4 && which <= 7) {

@@ -96,6 +96,22 @@ __device__ __noinline__ void dq_row_any(const DevCodec& c, long long row, int j,
         case 7: dq_row<KVQ_INT_ABSMAX, 7>(c, row, j, tab, v); return;
         default: dq_row<KVQ_INT_ABSMAX, 8>(c, row, j, tab, v); return;
       }
+    case KVQ_INT_SYM:
+      switch (c.bits) {
+        case 2: dq_row<KVQ_INT_SYM, 2>(c, row, j, tab, v); return;
+        case 3: dq_row<KVQ_INT_SYM, 3>(c, row, j, tab, v); return;
+        case 4: dq_row<KVQ_INT_SYM, 4>(c, row, j, tab, v); return;
+        case 5: dq_row<KVQ_INT_SYM, 5>(c, row, j, tab, v); return;
+        case 6: dq_row<KVQ_INT_SYM, 6>(c, row, j, tab, v); return;
+        case 7: dq_row<KVQ_INT_SYM, 7>(c, row, j, tab, v); return;
+        default: dq_row<KVQ_INT_SYM, 8>(c, row, j, tab, v); return;
+      }
+    case KVQ_LLOYD:
+      switch (c.bits) {
+        case 2: dq_row<KVQ_LLOYD, 2>(c, row, j, tab, v); return;
+        case 3: dq_row<KVQ_LLOYD, 3>(c, row, j, tab, v); return;
+        default: dq_row<KVQ_LLOYD, 4>(c, row, j, tab, v); return;
+      }
     default:
       switch (c.bits) {
         case 2: dq_row<KVQ_INT_MINMAX, 2>(c, row, j, tab, v); return;
@@ -438,12 +454,13 @@ __device__ __forceinline__ void raw_decode(const DevCodec& c, const RawChunk<CB,
                                            const float* nf4_lds, float v[16]) {
   if constexpr (CB < 0) {
     dq_row_any(c, r.row, j, tab, v);
-  } else if constexpr (CB == KVQ_NF4) {              // levels from LDS (a per-lane index)
+  } else if constexpr (CB == KVQ_NF4 || CB == KVQ_LLOYD) {   // levels from LDS (a per-lane index)
     uint32_t cc[16];
     unpack16<BITS>(r.w, cc);
     const float s0 = h2f(r.s[0]), s1 = h2f(r.s[1]);
+    const float* lv = (CB == KVQ_NF4) ? nf4_lds : nf4_lds + 16 * (BITS - 1);   // LLOYD b: after NF4's 16
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = nf4_lds[cc[i] & 15u] * (i < 8 ? s0 : s1);
+    for (int i = 0; i < 16; ++i) v[i] = lv[cc[i] & 15u] * (i < 8 ? s0 : s1);
   } else {
     uint32_t cc[16];
     unpack16<BITS>(r.w, cc);
@@ -583,7 +600,9 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
     if (kch) x = x / kch[d];
     qc[g * RS + pidx(d)] = x;
   }
-  if (tid < 16) qc[2 * kWaveHeads * RS + 512 + kWaveHeads * 16 * 20 + tid] = a.tab.nf4_lv[tid];   // NF4 levels
+  if (tid < 64)                                      // NF4 levels, then the Lloyd-Max levels of 2, 3, 4 bits
+    qc[2 * kWaveHeads * RS + 512 + kWaveHeads * 16 * 20 + tid] = tid < 16 ? a.tab.nf4_lv[tid]
+                                                                          : a.tab.lloyd_lv[(tid >> 4) - 1][tid & 15];
   __syncthreads();
   const float lsc = a.sm_scale * 1.4426950408889634f;
   float q[kWaveHeads][16];                           // the query chunk (codec coordinates)
@@ -592,7 +611,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
   // rFFT keys: per (head, lane j) the query spectrum of bins 8j .. 8j+7 and the Nyquist
   // bin: Re[0..7], Im[0..7], Re, Im, 2 pad (16-byte rows)
   float* qsp = dirs + 256;
-  float* const nf4l = qsp + kWaveHeads * 16 * 20;    // NF4 levels (written before the first barrier)
+  float* const nf4l = qsp + kWaveHeads * 16 * 20;    // NF4 and Lloyd-Max levels (written before the first barrier)
   if constexpr (KR) {
     // logit = sigma * sum_f w_f (Re Z_f Re Q_f + Im Z_f Im Q_f), Q = DFT(q), w = 1/N at f = 0, N/2, else 2/N
     const int N = D, F = N / 2 + 1;
@@ -1103,7 +1122,7 @@ static size_t split_smem(const AArgs& a, bool err) {
 template <int KCB, int KB, int VCB, int VB>
 static hipError_t launch_wave(const AArgs& a, long long R, hipStream_t st) {
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
-  const size_t smem = ((size_t)2 * kWaveHeads * (17 * (a.D / 16) + 17) + 512 + kWaveHeads * 16 * 20 + 16) * sizeof(float);
+  const size_t smem = ((size_t)2 * kWaveHeads * (17 * (a.D / 16) + 17) + 512 + kWaveHeads * 16 * 20 + 64) * sizeof(float);
   k_decode_wave<KCB, KB, VCB, VB><<<dim3(a.S / 4, a.H * HG, (unsigned)R), kBlock, smem, st>>>(a);
   return hipGetLastError();
 }
@@ -1135,6 +1154,15 @@ static hipError_t dispatch_wave(const AArgs& a, long long R, hipStream_t st) {
     return launch_wave<KVQ_FP16, 16, KVQ_FP16, 16>(a, R, st);
   if (is(kc, kb, KVQ_INT_ABSMAX, 6) && is(vc, vb, KVQ_FP16, -1))
     return launch_wave<KVQ_INT_ABSMAX, 6, KVQ_FP16, 16>(a, R, st);
+  // rotated 4-bit keys with the 2- and 3-bit value grids [E22L] Result names for the next test
+  if (is(kc, kb, KVQ_INT_ABSMAX, 4) && is(vc, vb, KVQ_INT_SYM, 2))
+    return launch_wave<KVQ_INT_ABSMAX, 4, KVQ_INT_SYM, 2>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 4) && is(vc, vb, KVQ_INT_SYM, 3))
+    return launch_wave<KVQ_INT_ABSMAX, 4, KVQ_INT_SYM, 3>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 4) && is(vc, vb, KVQ_LLOYD, 2))
+    return launch_wave<KVQ_INT_ABSMAX, 4, KVQ_LLOYD, 2>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 4) && is(vc, vb, KVQ_LLOYD, 3))
+    return launch_wave<KVQ_INT_ABSMAX, 4, KVQ_LLOYD, 3>(a, R, st);
   if (kc == KVQ_RFFT_POLAR && vc == KVQ_FP16) return launch_wave<KVQ_RFFT_POLAR, 0, KVQ_FP16, 16>(a, R, st);
   if (kc == KVQ_RFFT_CART && vc == KVQ_FP16) return launch_wave<KVQ_RFFT_CART, 0, KVQ_FP16, 16>(a, R, st);
   return launch_wave<-1, 0, -1, 0>(a, R, st);

@@ -107,6 +107,22 @@ __device__ __forceinline__ void stat_abssum(const float v[16], int g, float sm[2
   sm[0] = sm[1] = s;
 }
 
+// Group sums of squares RN32(y^2) with the same fixed pairwise tree as stat_abssum.
+__device__ __forceinline__ void stat_sqsum(const float v[16], int g, float sm[2]) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = v[i] * v[i];
+#pragma unroll
+  for (int w = 1; w < 8; w <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * w) t[i] = t[i] + t[i + w];
+  }
+  if (g == 8) { sm[0] = t[0]; sm[1] = t[8]; return; }
+  float s = t[0] + t[8];
+  for (int m = 1; m < g / 16; m <<= 1) s = xor_add(s, m);
+  sm[0] = sm[1] = s;
+}
+
 // ------------------------------------------------------------------ codebooks
 
 template <int CB, int BITS>
@@ -172,6 +188,44 @@ __device__ __forceinline__ void encode16(const float v[16], int g, const Tables&
         c[i] = k;
       }
     }
+  } else if constexpr (CB == KVQ_INT_SYM) {
+    // symmetric grid: levels k - h, h = (2^b - 1)/2; s = absmax / h; k = rne(RN32(t + h))
+    float am[2];
+    stat_absmax(v, g, am);
+    constexpr float h = (float)((1 << BITS) - 1) * 0.5f;
+    constexpr float top = (float)((1 << BITS) - 1);
+    float inv[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      s16[hh] = rn16(__fdiv_rn(am[hh], h));
+      inv[hh] = inv_scale(s16[hh]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float t = v[i] * inv[i >> 3];
+      c[i] = (uint32_t)(int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(t + h), 0.0f), top);
+    }
+  } else if constexpr (CB == KVQ_LLOYD) {
+    // Gaussian Lloyd-Max levels L; s = RMS = sqrt(RN32(sum y^2 * 1/g)); code = number of
+    // midpoints RN32(L_m + L_m+1) * 1/2 strictly below t (uniform table indices)
+    float sq[2];
+    stat_sqsum(v, g, sq);
+    const float invg = 1.0f / (float)g;   // exact: g is a power of two
+    float inv[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      s16[hh] = rn16(__fsqrt_rn(sq[hh] * invg));
+      inv[hh] = inv_scale(s16[hh]);
+    }
+    const float* L = tab.lloyd_lv[BITS - 2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float t = v[i] * inv[i >> 3];
+      uint32_t k = 0;
+#pragma unroll
+      for (int m = 0; m < (1 << BITS) - 1; ++m) k += (((L[m] + L[m + 1]) * 0.5f) < t) ? 1u : 0u;
+      c[i] = k;
+    }
   } else if constexpr (CB == KVQ_SIGN) {
     float sm[2];
     stat_abssum(v, g, sm);
@@ -202,6 +256,10 @@ __device__ __forceinline__ void decode16(const uint32_t c[16], const uint16_t s1
       v[i] = tab.nf4_lv[c[i] & 15u] * s;
     } else if constexpr (CB == KVQ_INT8_SYM) {
       v[i] = (float)((int)c[i] - 127) * s;
+    } else if constexpr (CB == KVQ_INT_SYM) {
+      v[i] = ((float)c[i] - (float)((1 << BITS) - 1) * 0.5f) * s;
+    } else if constexpr (CB == KVQ_LLOYD) {
+      v[i] = tab.lloyd_lv[BITS - 2][c[i] & 15u] * s;
     } else {
       v[i] = h2f((uint16_t)c[i]);
     }

@@ -23,6 +23,7 @@ constexpr int kVals = 16;        // values per lane in layout 1
 struct Tables {
   float nf4_lv[16];
   float nf4_mid[16];             // 15 midpoints, [15] = +inf
+  float lloyd_lv[3][16];         // Gaussian Lloyd-Max levels for 2, 3, 4 bits (ascending)
 };
 
 struct FftTables {               // for head_dim N <= 256 and up to 256 phase sectors

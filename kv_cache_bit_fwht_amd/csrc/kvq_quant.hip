@@ -224,6 +224,24 @@ static int grid_for(long long rows, int lpt_log2) {
         default: KERNEL<KVQ_INT_ABSMAX, 8> __VA_ARGS__; break;                                    \
       }                                                                                          \
       break;                                                                                     \
+    case KVQ_INT_SYM:                                                                            \
+      switch (BITS_) {                                                                           \
+        case 2: KERNEL<KVQ_INT_SYM, 2> __VA_ARGS__; break;                                        \
+        case 3: KERNEL<KVQ_INT_SYM, 3> __VA_ARGS__; break;                                        \
+        case 4: KERNEL<KVQ_INT_SYM, 4> __VA_ARGS__; break;                                        \
+        case 5: KERNEL<KVQ_INT_SYM, 5> __VA_ARGS__; break;                                        \
+        case 6: KERNEL<KVQ_INT_SYM, 6> __VA_ARGS__; break;                                        \
+        case 7: KERNEL<KVQ_INT_SYM, 7> __VA_ARGS__; break;                                        \
+        default: KERNEL<KVQ_INT_SYM, 8> __VA_ARGS__; break;                                       \
+      }                                                                                          \
+      break;                                                                                     \
+    case KVQ_LLOYD:                                                                              \
+      switch (BITS_) {                                                                           \
+        case 2: KERNEL<KVQ_LLOYD, 2> __VA_ARGS__; break;                                          \
+        case 3: KERNEL<KVQ_LLOYD, 3> __VA_ARGS__; break;                                          \
+        default: KERNEL<KVQ_LLOYD, 4> __VA_ARGS__; break;                                         \
+      }                                                                                          \
+      break;                                                                                     \
     default:                                                                                     \
       switch (BITS_) {                                                                           \
         case 2: KERNEL<KVQ_INT_MINMAX, 2> __VA_ARGS__; break;                                     \

@@ -32,12 +32,14 @@ in; stored scales are IEEE binary16 as the pages fix (fp16 group scales,
 oracle's own dequantised values.
 
 Functions whose results the pages do not pin are marked "parity unpinned" in
-their docstrings: the NF4 level values (the pages name NF4 but print no table).
+their docstrings: the NF4 level values (the pages name NF4 but print no table)
+and the Gaussian Lloyd-Max levels (named, not printed; pinned by the Lloyd-Max
+optimality conditions instead).
 """
 from .codec import (  # noqa: F401
     Codec,
-    FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART,
-    rn16, inv32, fwht, fwht_kappa, calibrate_chan_scale, nf4_levels, nf4_midpoints,
+    FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART, INT_SYM, LLOYD,
+    rn16, inv32, fwht, fwht_kappa, calibrate_chan_scale, nf4_levels, nf4_midpoints, lloyd_levels, lloyd_midpoints,
     quantize_rows, dequant_rows, layout, pack_bits, unpack_bits,
     quantize_pack, dequant,
 )

@@ -19,10 +19,10 @@ from .rounding import inv32, rn16  # noqa: F401
 
 F32 = np.float32
 
-FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART = range(9)
+FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART, INT_SYM, LLOYD = range(11)
 _NAMES = {FP16: "fp16", INT_ABSMAX: "int_absmax", INT_MINMAX: "int_minmax", TERNARY: "ternary",
           SIGN: "sign", NF4: "nf4", INT8_SYM: "int8_sym", RFFT_POLAR: "rfft_polar",
-          RFFT_CART: "rfft_cart"}
+          RFFT_CART: "rfft_cart", INT_SYM: "int_sym", LLOYD: "lloyd"}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -228,6 +228,74 @@ def _dec_nf4(codes, s16):
     return nf4_levels()[codes] * s16.astype(F32)[..., None]
 
 
+def _enc_int_sym(y, b):
+    """Symmetric b-bit grid: levels k - h for k = 0 .. 2^b - 1, h = (2^b - 1)/2,
+    i.e. half-integers with as many levels on each side ([E22L, Result]: the
+    symmetric value grid is the next test after the one-sided {-2,-1,0,1}).  The
+    pages fix no scale; reading: s = RN16(RN32(A / h)) with A = max |y| of the
+    group (the extreme lands on the outermost level), t = RN32(y * RN32(1/s)),
+    k = rne(RN32(t + h)) clipped to [0, 2^b - 1]."""
+    h = F32((2 ** b - 1) / 2)
+    A = np.abs(y).max(-1)
+    s16 = rn16(A / h)
+    inv = inv32(s16)
+    t = y * inv[..., None]
+    k = np.clip(np.rint(t + h), 0, 2 ** b - 1)
+    return k.astype(np.int64), s16, None
+
+
+def _dec_int_sym(codes, s16, b):
+    h = F32((2 ** b - 1) / 2)
+    return (codes.astype(F32) - h) * s16.astype(F32)[..., None]
+
+
+def lloyd_levels(b: int) -> np.ndarray:
+    """Lloyd-Max levels of the standard normal for 2^b levels ([E22L, Result]:
+    Gaussian Lloyd-Max levels on rotated values as the next test).  The fixed
+    point of Lloyd's two conditions in fp64: each cell boundary halfway between
+    its neighbouring levels, each level the mean of N(0, 1) over its cell,
+    (pdf(a) - pdf(b)) / (cdf(b) - cdf(a)); started from the cell-centre
+    quantiles, stopped when no level moves by 1e-14; rounded to binary32.
+
+    The pages print no levels: parity unpinned by the pages; pinned by the two
+    optimality conditions (checked by numerical integration) and symmetry."""
+    from scipy.stats import norm
+    n = 2 ** b
+    L = norm.ppf((np.arange(n) + 0.5) / n)
+    for _ in range(100000):
+        t = np.concatenate([[-np.inf], 0.5 * (L[:-1] + L[1:]), [np.inf]])
+        m = (norm.pdf(t[:-1]) - norm.pdf(t[1:])) / (norm.cdf(t[1:]) - norm.cdf(t[:-1]))
+        moved = np.abs(m - L).max()
+        L = m
+        if moved < 1e-14:
+            break
+    return L.astype(F32)
+
+
+def lloyd_midpoints(b: int) -> np.ndarray:
+    L = lloyd_levels(b)
+    return (L[:-1] + L[1:]) * F32(0.5)
+
+
+def _enc_lloyd(y, b):
+    """Gaussian Lloyd-Max codebook.  Reading: the levels are those of a unit
+    normal scaled by the group's root mean square s = RN16(sqrt(RN32(S * 1/g)))
+    with S the fixed pairwise-tree sum of RN32(y^2) (the tree of the sign
+    codec); t = RN32(y * RN32(1/s)); code = number of midpoints strictly below t
+    (a tie goes to the lower level)."""
+    g = y.shape[-1]
+    S = _pairwise_sum(y * y)
+    s16 = rn16(np.sqrt(S * F32(1.0 / g)))
+    inv = inv32(s16)
+    t = y * inv[..., None]
+    M = lloyd_midpoints(b)
+    return (t[..., None] > M).sum(-1).astype(np.int64), s16, None
+
+
+def _dec_lloyd(codes, s16, b):
+    return lloyd_levels(b)[codes] * s16.astype(F32)[..., None]
+
+
 def _enc_int8_sym(y):
     """int8 per-token reference ([FMAG-6, Milestone] int8 KV row): symmetric
     +-127 grid, s = RN16(RN32(absmax / 127)); stored q + 127."""
@@ -328,6 +396,10 @@ def quantize_rows(x16: np.ndarray, codec: Codec, cscale: np.ndarray | None = Non
         codes, s, z = _enc_nf4(y)
     elif cb == INT8_SYM:
         codes, s, z = _enc_int8_sym(y)
+    elif cb == INT_SYM:
+        codes, s, z = _enc_int_sym(y, codec.bits)
+    elif cb == LLOYD:
+        codes, s, z = _enc_lloyd(y, codec.bits)
     else:
         raise ValueError(f"unknown codebook {cb}")
     return [(codes.reshape(N, D), codec.code_bits())], s, z
@@ -359,6 +431,10 @@ def dequant_rows(codes_list, scales, mins, codec: Codec, D: int,
             y = _dec_nf4(c3, scales)
         elif cb == INT8_SYM:
             y = _dec_int8_sym(c3, scales)
+        elif cb == INT_SYM:
+            y = _dec_int_sym(c3, scales, codec.bits)
+        elif cb == LLOYD:
+            y = _dec_lloyd(c3, scales, codec.bits)
         else:
             raise ValueError(f"unknown codebook {cb}")
         x = y.reshape(N, D)

@@ -64,6 +64,10 @@ CODECS = [
     O.Codec(O.INT8_SYM, 0, 128),
     O.Codec(O.RFFT_POLAR, 4, 32, aux_bits=8),
     O.Codec(O.RFFT_CART, 3, 16),
+    O.Codec(O.INT_SYM, 2, 128, rot=256),
+    O.Codec(O.INT_SYM, 3, 32),
+    O.Codec(O.LLOYD, 2, 128, rot=256),
+    O.Codec(O.LLOYD, 4, 16),
 ]
 
 
@@ -115,9 +119,12 @@ def test_constant_tables_match_the_oracle(K):
         bc, bs = O.rfft.boundaries(P)
         np.testing.assert_array_equal(K.kvq_constant_table(6, P // 8), bc)
         np.testing.assert_array_equal(K.kvq_constant_table(7, P // 8), bs)
+    for b in (2, 3, 4):
+        np.testing.assert_array_equal(K.kvq_constant_table(6 + b, 2 ** b), O.lloyd_levels(b))
 
 
-@pytest.mark.parametrize("which,n", [(0, 15), (1, 16), (2, 3), (2, 256), (4, 4), (4, 512), (6, 0), (8, 4), (-1, 4)])
+@pytest.mark.parametrize("which,n", [(0, 15), (1, 16), (2, 3), (2, 256), (4, 4), (4, 512), (6, 0), (8, 5), (10, 8),
+                                     (11, 4), (-1, 4)])
 def test_constant_table_rejects_bad_sizes(K, which, n):
     out = np.zeros(max(n, 1), dtype=np.float32)
     assert K._lib.kvq_constant_table(which, n, out.ctypes.data) == ERR_ARG
@@ -133,7 +140,11 @@ def test_constant_table_rejects_bad_sizes(K, which, n):
     ((1, 4, 32, 512, 0), 256, ERR_UNSUPPORTED),     # rotation wider than head_dim
     ((7, 4, 32, 0, 2), 128, ERR_UNSUPPORTED),       # polar rFFT with 4 phase sectors
     ((8, 4, 32, 64, 0), 128, ERR_UNSUPPORTED),      # rFFT codecs take no rotation
-    ((9, 4, 32, 0, 0), 128, ERR_UNSUPPORTED),       # no such codebook
+    ((11, 4, 32, 0, 0), 128, ERR_UNSUPPORTED),      # no such codebook
+    ((9, 1, 32, 0, 0), 128, ERR_UNSUPPORTED),       # 1-bit INT_SYM
+    ((9, 9, 32, 0, 0), 128, ERR_UNSUPPORTED),       # 9-bit INT_SYM
+    ((10, 5, 32, 0, 0), 128, ERR_UNSUPPORTED),      # 5-bit LLOYD (tables for 2..4 bits)
+    ((10, 1, 32, 0, 0), 128, ERR_UNSUPPORTED),      # 1-bit LLOYD
 ])
 def test_layout_rejects_invalid_codecs(K, codec, D, status):
     c = K.kvq_codec(*codec)

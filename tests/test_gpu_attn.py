@@ -164,6 +164,22 @@ def test_c4_low_bit_arms_with_fp16_anchor(arm):
     _run_case(K, R(Kx), R(Vx), R(q), None, kc, vc)
 
 
+@pytest.mark.parametrize("arm", ["sym2", "sym2_rot", "lloyd2_rot", "lloyd3_rot", "sym3_rot"])
+def test_c3_value_codebooks_decode_and_error(arm):
+    """Rotated 4-bit keys with the value grids the 64K experiment names as its next
+    test: the symmetric grid and Gaussian Lloyd-Max levels, rotated or not."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=2, T=700, n_q=3)
+    Kx, Vx = synth.gen_kv(w)
+    q, kv_len = synth.gen_queries(w)
+    kc = K.Codec(K.INT_ABSMAX, 4, 128, 256)
+    vc = {"sym2": K.Codec(K.INT_SYM, 2, 128, 0), "sym2_rot": K.Codec(K.INT_SYM, 2, 128, 256),
+          "lloyd2_rot": K.Codec(K.LLOYD, 2, 128, 256), "lloyd3_rot": K.Codec(K.LLOYD, 3, 128, 256),
+          "sym3_rot": K.Codec(K.INT_SYM, 3, 128, 256)}[arm]
+    announce(f"c3 values {arm}")
+    _run_case(K, Kx, Vx, q, None, kc, vc)
+
+
 @pytest.mark.parametrize("arm", ["polar", "cart", "fwht6"])
 def test_c5_transform_arms(arm):
     import kv_cache_bit_fwht_amd as K

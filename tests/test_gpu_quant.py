@@ -67,6 +67,10 @@ for D in (64, 128, 256):
               (D, (4, 1, 32, 0)), (D, (5, 4, 64, 0)), (D, (6, 8, D, 0)), (D, (0, 16, 0, 0)), (D, (1, 4, 16, 0)),
               (D, (1, 4, 64, D // 2)), (D, (1, 6, 32, 16)), (D, (1, 4, 8, 8)), (D, (3, 2, 8, D))]
 CASES.append((256, (1, 4, 256, 256)))
+# the symmetric grid and the Gaussian Lloyd-Max codebook (value codecs the 64K experiment names next)
+for D in (64, 128, 256):
+    CASES += [(D, (9, 2, 8, 0)), (D, (9, 3, 32, D)), (D, (9, 4, 64, 0)), (D, (9, 8, 32, 0)),
+              (D, (10, 2, 8, 0)), (D, (10, 2, 64, D)), (D, (10, 3, 32, 0)), (D, (10, 4, 16, D))]
 
 
 @pytest.mark.parametrize("D,cspec", CASES)
