@@ -198,8 +198,9 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
  * above), 2 = the MFMA kernel, KVQ_ERR_UNSUPPORTED unless: head_dim 256, tokens
  * a positive multiple of 32, at most 4 query heads per KV head, K INT_ABSMAX
  * 4-bit at group 128 or 256 (any rotation, optional chan_scale), V INT_ABSMAX
- * 2-bit at group 64..256 without chan_scale (any rotation) -- the 4-bit-key /
- * 2-bit-value arms of [E22L] What I tested. */
+ * 2-bit or INT_SYM 2-bit at group 64..256 without chan_scale (any rotation) --
+ * the 4-bit-key / 2-bit-value arms of [E22L] What I tested, and the symmetric
+ * value grid of [E22L] Result. */
 kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
                               int32_t n_q, const uint16_t* q, const int32_t* kv_len,
                               float sm_scale, float* out, float* lse, void* ws,

@@ -25,7 +25,8 @@
 //    4 tokens' words masked to its low 2, 4, 6 or 8 bits as fp16 subnormals, so
 //    four accumulators per byte hold prefix sums of its fields weighted 1, 4,
 //    16, 64 and the fields come out as differences after the loop.
-//    Output: 2^24 * field - 2 * sum of the weights per group.
+//    Output: 2^24 * field - o * sum of the weights per group, o = 2 for signed
+//    absmax codes (levels c - 2) and 1.5 for the symmetric grid (levels c - 1.5).
 // Several blocks of 8 wavefronts (two per SIMD) share the tokens of one (query,
 // KV head): each block claims chunks of steps from a device-wide counter of the
 // unit and hands their steps to its wavefronts from an LDS counter, then merges
@@ -65,7 +66,10 @@ struct FArgs {
   int nks, nvs, gv;                // scales per row, value group
   int kW;                          // key rotation width (0 = none)
   float kkappa;
+  int vW;                          // value rotation width (0 = none): the merge rotates the output back
+  float vkappa;
   float sm_scale;
+  float voff;                      // value code offset: 2 (signed absmax, c - 2) or 1.5 (symmetric grid, c - 1.5)
   int blocks_per_unit;             // blocks (and partials) per (query row, KV head)
   int chunk_log2;                  // log2 of the 32-token steps per chunk (>= 4)
   int* ctr;                        // per (query row, KV head) chunk counters, or null (static chunks)
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
         const float m1 = acc[4 * k][c], m2 = acc[4 * k + 1][c], m3 = acc[4 * k + 2][c], m4 = acc[4 * k + 3][c];
         const float f[4] = {m1, (m2 - m1) * 0.25f, (m3 - m2) * 0.0625f, (m4 - m3) * 0.015625f};
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) so[wave][c][16 * n16 + 4 * k + ii] = f[ii] * 16777216.0f - 2.0f * wsum[c];
+        for (int ii = 0; ii < 4; ++ii) so[wave][c][16 * n16 + 4 * k + ii] = f[ii] * 16777216.0f - a.voff * wsum[c];
       }
     }
   }
@@ -606,9 +610,10 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   auto get = [](const float* ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   // (m, l) of every partial into LDS (the per-wave output buffer is free by now), all
   // loads in flight at once; then each thread's output loads go out 8 at a time.
-  static_assert(8 * kMaxChunks <= NW * 4 * kFastD, "merge tables exceed the per-wave output buffer");
+  static_assert(8 * kMaxChunks + 4 * kFastD <= NW * 4 * kFastD, "merge tables exceed the per-wave output buffer");
   float* const pm = &so[0][0][0];                    // [head][block], stride kMaxChunks (blocks <= chunks)
   float* const pl = pm + 4 * kMaxChunks;
+  float* const rot = pl + 4 * kMaxChunks;             // [head][dim] merged output before rotating back
   const float* const ubase = a.ws + (rq * a.Hq + (size_t)h * G) * bpu * P;
   for (int t = tid; t < G * bpu; t += kFastBlock) {
     const int c = t / bpu, sb = t - c * bpu;
@@ -644,9 +649,26 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
         }
       }
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      a.out[rh * kFastD + d] = O * inv;
+      if (a.vW > 1) rot[c * kFastD + d] = O * inv;
+      else a.out[rh * kFastD + d] = O * inv;
       if (d == 0 && a.lse) a.lse[rh] = L > 0.0f ? M + logf(L) : -INFINITY;
     }
+  }
+  if (a.vW > 1) {   // rotated values: the normalised transform is its own inverse
+    __syncthreads();
+    const int c = tid >> 7, pp = tid & 127;          // one butterfly per thread and stage (4 heads x 128)
+    for (int ls = 0; (1 << ls) < a.vW; ++ls) {
+      const int st = 1 << ls;
+      const int ii = ((pp >> ls) << (ls + 1)) | (pp & (st - 1));
+      if (c < G) {
+        const float x = rot[c * kFastD + ii], y = rot[c * kFastD + ii + st];
+        rot[c * kFastD + ii] = x + y;
+        rot[c * kFastD + ii + st] = x - y;
+      }
+      __syncthreads();
+    }
+    for (int p = tid; p < G * kFastD; p += kFastBlock)
+      a.out[(rq * a.Hq + (size_t)h * G) * kFastD + p] = rot[p] * a.vkappa;
   }
   if (tid == 0) {   // ready for the next call: every block of the unit has made its last claim
     ctr[0] = 0;
@@ -695,7 +717,8 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   if (Hq / s.heads > 4) return false;
   if (k.codec.codebook != KVQ_INT_ABSMAX || k.codec.bits != 4) return false;
   if (k.codec.group != 128 && k.codec.group != 256) return false;
-  if (v.codec.codebook != KVQ_INT_ABSMAX || v.codec.bits != 2) return false;
+  // 2-bit values: signed absmax (levels c - 2) or the symmetric grid (levels c - 1.5)
+  if ((v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) || v.codec.bits != 2) return false;
   if (v.codec.group < 64) return false;   // a P.V block's 4 value words share one scale group
   if (v.chan_scale) return false;
   return true;
@@ -751,14 +774,21 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
     while ((1 << e) < a.kW) ++e;
     a.kkappa = (a.kW > 1) ? ((e % 2 == 0) ? ldexpf(1.0f, -e / 2) : (float)(1.0 / std::sqrt((double)a.kW))) : 1.0f;
   }
+  a.vW = v.codec.rot_width > 1 ? v.codec.rot_width : 0;
+  {
+    int e = 0;
+    while ((1 << e) < a.vW) ++e;
+    a.vkappa = (a.vW > 1) ? ((e % 2 == 0) ? ldexpf(1.0f, -e / 2) : (float)(1.0 / std::sqrt((double)a.vW))) : 1.0f;
+  }
   a.sm_scale = pr.sm_scale;
+  a.voff = (v.codec.codebook == KVQ_INT_SYM) ? 1.5f : 2.0f;
   a.blocks_per_unit = fast_blocks_per_unit(s, pr.n_q);
   a.chunk_log2 = fast_chunk_log2(s);
   // shared chunk counters when the rows fit the workspace's counter region
   const long long rows_kv = (long long)s.batch * s.layers * pr.n_q * s.heads;
   a.ctr = (pr.ctr && rows_kv <= kWsCounterRows) ? pr.ctr : nullptr;
   // unrotated values without channel scales: the last block of a unit merges its partials
-  const bool fused = a.ctr && v.codec.rot_width <= 1 && !v.chan_scale;
+  const bool fused = a.ctr && !v.chan_scale;
   a.done = fused ? pr.ctr + kWsCounterRows : nullptr;
   a.out = pr.out;
   a.lse = pr.lse;

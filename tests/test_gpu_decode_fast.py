@@ -41,7 +41,7 @@ def test_fast_c3_shape_shrunk():
 
 
 @pytest.mark.parametrize("variant", ["kgroup256", "vgroup64", "vgroup256", "rot128", "norot", "G2", "G1",
-                                     "vrot"])
+                                     "vrot", "vsym", "vsym_rot"])
 def test_fast_variants(variant):
     import kv_cache_bit_fwht_amd as K
     kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
@@ -62,6 +62,10 @@ def test_fast_variants(variant):
         w = w.with_sizes(Hq=4)
     elif variant == "vrot":
         vc = K.Codec(K.INT_ABSMAX, 2, 128, 256)
+    elif variant == "vsym":
+        vc = K.Codec(K.INT_SYM, 2, 128, 0)
+    elif variant == "vsym_rot":
+        vc = K.Codec(K.INT_SYM, 2, 128, 256)
     announce(f"mfma variant {variant}")
     _case(K, w, kc, vc)
 
