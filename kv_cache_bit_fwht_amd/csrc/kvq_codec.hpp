@@ -214,7 +214,7 @@ __device__ __forceinline__ void encode16(const float v[16], int g, const Tables&
     float inv[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      s16[hh] = rn16(__fsqrt_rn(sq[hh] * invg));
+      s16[hh] = rn16(sqrt_rn(sq[hh] * invg));
       inv[hh] = inv_scale(s16[hh]);
     }
     const float* L = tab.lloyd_lv[BITS - 2];

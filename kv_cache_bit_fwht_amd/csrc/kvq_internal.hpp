@@ -50,6 +50,10 @@ __device__ __forceinline__ uint16_t rn16(float x) {
   return (b & 0x7fffu) ? b : (uint16_t)0;
 }
 
+// Correctly rounded binary32 square root.  (The hardware instruction alone is
+// accurate to about one ulp; the builtin adds the exact residual checks.)
+__device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }
+
 // Correctly rounded reciprocal of a stored scale; zero scale -> zero.
 __device__ __forceinline__ float inv_scale(uint16_t sb) {
   float s = h2f(sb);

@@ -83,10 +83,62 @@ def test_quantize_pack_bit_exact(D, cspec):
     _compare(K, x, codec)
 
 
-@pytest.mark.parametrize("cspec", [(1, 4, 128, 256), (1, 2, 128, 0)])
+# rFFT codecs: magnitude/phase (bits, phase bits, group) and real/imaginary (bits, group)
+RFFT_CASES = []
+for D in (64, 128, 256):
+    RFFT_CASES += [(D, "polar", b, pb, g) for (b, pb, g) in
+                   [(5, 7, 32), (4, 8, 16), (6, 6, 8), (2, 3, 128), (8, 8, 64), (3, 5, 8), (7, 4, 128)]]
+    RFFT_CASES += [(D, "cart", b, 0, g) for (b, g) in [(6, 32), (8, 8), (2, 128), (3, 16), (5, 64), (4, 8)]]
+
+
+def _rfft_codec(K, kind, b, pb, g):
+    return K.Codec(K.RFFT_POLAR, b, g, 0, pb) if kind == "polar" else K.Codec(K.RFFT_CART, b, g, 0)
+
+
+@pytest.mark.parametrize("D,kind,b,pb,g", RFFT_CASES)
+def test_rfft_quantize_bit_exact(D, kind, b, pb, g):
+    """222 rows (a ragged last wavefront at every head_dim) with the special rows of
+    _inputs; codes, scales and the dequantised rows against the oracle."""
+    import kv_cache_bit_fwht_amd as K
+    codec = _rfft_codec(K, kind, b, pb, g)
+    x = _inputs(1, 2, 3, 37, D, seed=1000 + 10 * b + pb + g)
+    announce(f"rfft quantize D={D} codec={codec}")
+    _compare(K, x, codec)
+
+
+@pytest.mark.parametrize("D,kind", [(64, "polar"), (128, "polar"), (256, "polar"), (128, "cart"), (256, "cart")])
+def test_rfft_quantize_channel_scales_extreme_magnitudes(D, kind):
+    """Per-unit channel multipliers of 1e-33, 1e-26, 1e30 and about 1 put spectrum
+    values below 2^-96 (products in the side tests underflow), above 2^96 (squares
+    overflow to infinity) and in the ordinary range; 3 x 401 rows per unit."""
+    import kv_cache_bit_fwht_amd as K
+    codec = _rfft_codec(K, kind, 5, 7, 32) if kind == "polar" else _rfft_codec(K, kind, 6, 0, 32)
+    x = _inputs(1, 2, 2, 401, D, seed=77 + D)
+    rng = np.random.default_rng([13, D])
+    chan = rng.uniform(0.5, 2.0, (2, 2, D)).astype(np.float32)
+    chan[0, 0] *= np.float32(1e-33)
+    chan[0, 1] *= np.float32(1e-26)
+    chan[1, 0] *= np.float32(1e30)
+    announce(f"rfft quantize channel scales D={D} codec={codec}")
+    _compare(K, x, codec, chan)
+
+
+def test_rfft_quantize_many_passes():
+    """70,001 rows at head_dim 256 (4 rows per wavefront): every wavefront of the
+    capped grid encodes several row groups and the last group is ragged."""
+    import kv_cache_bit_fwht_amd as K
+    codec = _rfft_codec(K, "polar", 5, 7, 32)
+    x = _inputs(1, 1, 1, 70001, 256, seed=4242)
+    announce(f"rfft quantize 70001 rows codec={codec}")
+    _compare(K, x, codec)
+
+
+@pytest.mark.parametrize("cspec", [(1, 4, 128, 256), (1, 2, 128, 0), (10, 2, 32, 256), (10, 3, 128, 0)])
 def test_quantize_many_passes_ragged(cspec):
-    """90,003 rows at head_dim 256: every wavefront encodes several row quads (the
-    two-buffer loop), and the last quad is ragged (3 of 4 rows); all rows checked."""
+    """90,003 rows at head_dim 256: every wavefront encodes several row quads, and
+    the last quad is ragged (3 of 4 rows); all rows checked.  The Lloyd-Max arms
+    check the RMS scale (a square root) over ~0.4-0.7M groups, where a last-ulp error
+    of the root would move some fp16 scale."""
     import kv_cache_bit_fwht_amd as K
     codec = K.Codec(*cspec)
     x = _inputs(1, 1, 3, 30001, 256, seed=911 + cspec[1])
