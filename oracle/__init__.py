@@ -39,7 +39,7 @@ optimality conditions instead).
 from .codec import (  # noqa: F401
     Codec,
     FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART, INT_SYM, LLOYD,
-    rn16, inv32, fwht, fwht_kappa, calibrate_chan_scale, nf4_levels, nf4_midpoints, lloyd_levels, lloyd_midpoints,
+    rn16, inv32, fwht, fwht_kappa, calibrate_chan_scale, key_mean, nf4_levels, nf4_midpoints, lloyd_levels, lloyd_midpoints,
     quantize_rows, dequant_rows, layout, pack_bits, unpack_bits,
     quantize_pack, dequant,
 )

@@ -103,6 +103,28 @@ def calibrate_chan_scale(k_cal: np.ndarray) -> np.ndarray:
     return c
 
 
+# ---------------------------------------------------------------- shared key mean
+
+def key_mean(k16: np.ndarray) -> np.ndarray:
+    """Per-(layer, head) key mean mu[l][h][d] over every sequence and token.
+
+    [LCPP] (llama.cpp issue "Per-head adaptive KV cache quantization", the later
+    comment measuring the failure mode): a shared per-head key mean carries about
+    half of the key energy; subtracting the running mean before quantising and
+    restoring it afterwards removes the failure.  The pages give no estimator;
+    the reading taken: the plain mean over the B*T rows present, from the exact
+    sum of the fp16 values (an integer in units of 2^-24), divided by B*T in fp64
+    and rounded to binary32 (the fp64 conversion of the sum, the fp64 quotient
+    and the binary32 rounding are the only roundings).  k16: fp16 [B][L][H][T][D].
+    """
+    B, L, H, T, D = k16.shape
+    ints = (k16.astype(np.float64) * 2.0 ** 24).astype(np.int64)   # exact: fp16 are multiples of 2^-24
+    S = ints.sum(axis=(0, 3))                                       # exact int64 [L][H][D]
+    n = B * T
+    mu = (S.astype(np.float64) / float(n)) * 2.0 ** -24 if n else np.zeros(S.shape)
+    return mu.astype(F32)
+
+
 # ---------------------------------------------------------------- codebooks
 # All encoders take y: float32 [..., G, g] (G groups of g values) and return
 # (codes int64 [..., G, g], scale fp16 [..., G], min fp16 [..., G] or None).
@@ -363,11 +385,13 @@ def layout(codec: Codec, D: int):
 
 # ---------------------------------------------------------------- rows
 
-def quantize_rows(x16: np.ndarray, codec: Codec, cscale: np.ndarray | None = None):
+def quantize_rows(x16: np.ndarray, codec: Codec, cscale: np.ndarray | None = None,
+                  mean: np.ndarray | None = None):
     """Quantise fp16 rows [N, D] -> (codes list of (int64 [N, n], bits), scales
     fp16 [N, ns] or None, mins fp16 [N, nm] or None).
 
     Steps ([E22L, What I tested]; [E21W, What I tested]): fp16 -> fp32 (exact);
+    optional shared-mean subtraction RN32(x - mu) ([LCPP], the shared key-mean comment);
     optional per-channel multiply RN32(x * c) (arms C/D); optional FWHT over
     each `rot`-wide block; groups of `group` consecutive values; codebook.
     """
@@ -376,6 +400,8 @@ def quantize_rows(x16: np.ndarray, codec: Codec, cscale: np.ndarray | None = Non
     if cb == FP16:
         return [(x16.view(np.uint16).astype(np.int64), 16)], None, None
     x = x16.astype(F32)
+    if mean is not None:
+        x = x - mean.astype(F32)
     if cscale is not None:
         x = x * cscale.astype(F32)
     if cb in (RFFT_POLAR, RFFT_CART):
@@ -406,9 +432,10 @@ def quantize_rows(x16: np.ndarray, codec: Codec, cscale: np.ndarray | None = Non
 
 
 def dequant_rows(codes_list, scales, mins, codec: Codec, D: int,
-                 cscale: np.ndarray | None = None) -> np.ndarray:
+                 cscale: np.ndarray | None = None, mean: np.ndarray | None = None) -> np.ndarray:
     """Invert quantize_rows: fp32 [N, D] in the original coordinates (inverse
-    codebook, inverse FWHT, then RN32(x / c) for pre-scaled keys)."""
+    codebook, inverse FWHT, then RN32(x / c) for pre-scaled keys, then RN32(x + mu)
+    where a shared mean was subtracted)."""
     cb = codec.codebook
     if cb == FP16:
         return codes_list[0][0].astype(np.uint16).view(np.float16).astype(F32)
@@ -442,13 +469,16 @@ def dequant_rows(codes_list, scales, mins, codec: Codec, D: int,
             x = fwht(x, codec.rot)
     if cscale is not None:
         x = x / cscale.astype(F32)
+    if mean is not None:
+        x = x + mean.astype(F32)
     return x
 
 
 # ---------------------------------------------------------------- whole tensors
 
 def _row_cscale(chan_scale, shape):
-    """Broadcast c[L][H][D] to rows of a [B][L][H][T][D] tensor."""
+    """Broadcast a [L][H][D] vector (channel scale or shared mean) to rows of a
+    [B][L][H][T][D] tensor."""
     if chan_scale is None:
         return None
     B, L, H, T, D = shape
@@ -466,13 +496,15 @@ def _field_widths(codec: Codec, D: int):
     return [(D, codec.code_bits())]
 
 
-def quantize_pack(x16: np.ndarray, codec: Codec, chan_scale: np.ndarray | None = None):
+def quantize_pack(x16: np.ndarray, codec: Codec, chan_scale: np.ndarray | None = None,
+                  mean: np.ndarray | None = None):
     """fp16 [B][L][H][T][D] -> (words uint32 [rows][nw], scales fp16 [rows][ns],
-    mins fp16 [rows][nm]); rows in [B][L][H][T] order."""
+    mins fp16 [rows][nm]); rows in [B][L][H][T] order.  chan_scale and mean are
+    [L][H][D] fp32 or None."""
     shape = x16.shape
     D = shape[-1]
     rows = x16.reshape(-1, D)
-    fields, s, z = quantize_rows(rows, codec, _row_cscale(chan_scale, shape))
+    fields, s, z = quantize_rows(rows, codec, _row_cscale(chan_scale, shape), _row_cscale(mean, shape))
     if codec.codebook == RFFT_CART:
         fields = [(np.concatenate([fields[0][0], fields[1][0]], axis=1), codec.bits)]
     words = pack_bits(fields)
@@ -482,7 +514,7 @@ def quantize_pack(x16: np.ndarray, codec: Codec, chan_scale: np.ndarray | None =
     return words, scales, mins
 
 
-def dequant(words, scales, mins, codec: Codec, shape, chan_scale=None) -> np.ndarray:
+def dequant(words, scales, mins, codec: Codec, shape, chan_scale=None, mean=None) -> np.ndarray:
     """Packed rows -> fp32 [B][L][H][T][D] in the original coordinates."""
     D = shape[-1]
     widths = _field_widths(codec, D)
@@ -498,5 +530,5 @@ def dequant(words, scales, mins, codec: Codec, shape, chan_scale=None) -> np.nda
             mins = np.asarray(mins).reshape(N, ng) if codec.codebook == INT_MINMAX else None
     fl = [(f, b) for f, (_, b) in zip(fields, widths)] if codec.codebook != RFFT_CART else \
         [(fields[0], codec.bits), (fields[1], codec.bits)]
-    x = dequant_rows(fl, scales, mins, codec, D, _row_cscale(chan_scale, shape))
+    x = dequant_rows(fl, scales, mins, codec, D, _row_cscale(chan_scale, shape), _row_cscale(mean, shape))
     return x.reshape(shape)

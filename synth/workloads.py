@@ -49,6 +49,7 @@ class Workload:
     pos_range: tuple | None       # query positions [lo, hi) for causal probes
     causal_inclusive: bool        # keys [0, p] (True) or [0, p) (False)
     description: str
+    k_mean_share: float = 0.0     # share of expected key energy in a shared per-(layer, head) mean
 
     def with_sizes(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -112,6 +113,16 @@ def _outlier_channels(w: Workload, l: int, h: int) -> np.ndarray:
     return np.sort(rng.choice(w.D, size=w.n_outlier, replace=False))
 
 
+def _shared_key_mean(w: Workload, l: int, h: int, n_out: int) -> np.ndarray:
+    """A per-(layer, head) vector added to every key row (a property of the
+    synthetic model, the same for every sequence), scaled so that it carries
+    k_mean_share of the expected key energy."""
+    m = unit_rng(w, 200, l, h).standard_normal(w.D)
+    e_row = w.k_sigma ** 2 * ((w.D - n_out) + n_out * w.outlier_mult ** 2)
+    target = w.k_mean_share / (1.0 - w.k_mean_share) * e_row
+    return (m * np.sqrt(target / float(m @ m))).astype(np.float32)
+
+
 def _rope_fp64(x: np.ndarray, pos: np.ndarray, D: int) -> np.ndarray:
     """Rotate-half RoPE (pairs (i, i + D/2), theta_i = 1e4^(-2i/D)) in fp64."""
     half = D // 2
@@ -134,6 +145,8 @@ def gen_unit(w: Workload, b: int, l: int, h: int, tensor: str) -> np.ndarray:
         ch = _outlier_channels(w, l, h)
         if ch.size:
             x[:, ch] *= np.float32(w.outlier_mult)
+        if w.k_mean_share > 0.0:
+            x += _shared_key_mean(w, l, h, ch.size)[None, :]
         if w.rope:
             return _rope_fp64(x, np.arange(w.T), w.D).astype(np.float16)
     else:
