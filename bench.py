@@ -160,13 +160,16 @@ def secondary(workload, reps):
     head_dim 128 with fp16 values; c3v, the 64K cache with rotated 4-bit keys and
     each value codebook (the one-sided 2-bit grid, and the symmetric and Gaussian
     Lloyd-Max grids named as the next test), with the attention KL and output
-    error of 16 queries.  One JSON line per arm: quantize+pack of the arm's K and
-    V, and one decode step (every layer, every query head, B queries)."""
+    error of 16 queries; c3m, the 64K cache whose keys carry a shared per-(layer,
+    head) mean (53% of key energy), 4- and 3-bit rotated keys coded with and
+    without the mean subtracted, with the same error figures and the time of
+    kvq_key_mean.  One JSON line per arm: quantize+pack of the arm's K and V, and
+    one decode step (every layer, every query head, B queries)."""
     import torch
     import kv_cache_bit_fwht_amd as K
     import synth
     dev = torch.device("cuda:0")
-    w = synth.get("c3" if workload == "c3v" else workload)
+    w = synth.get("c3" if workload == "c3v" else workload) if workload != "c3m" else synth.get("c3", k_mean_share=0.53)
     log(f"generating {w.description}")
     Kx, Vx = synth.gen_kv(w)
     q, _ = synth.gen_queries(w)
@@ -175,7 +178,25 @@ def secondary(workload, reps):
     qd = torch.from_numpy(np.ascontiguousarray(q[:, :, :1]).view(np.int16)).to(dev)
     del Kx, Vx
     f16 = K.Codec(K.FP16)
-    if workload == "c3v":
+    mean_d, mean_us = None, 0.0
+    if workload == "c3m":
+        # keys with a shared per-(layer, head) mean carrying 53% of their energy; each key
+        # codec with and without the mean subtracted (value codec fixed)
+        shape_all = K.Shape(w.B, w.L, w.H, w.T, w.D)
+        mean_d = torch.empty((w.L, w.H, w.D), dtype=torch.float32, device=dev)
+        wmb = K.kvq_key_mean_workspace(shape_all)
+        wm = torch.empty(wmb, dtype=torch.uint8, device=dev)
+        K.kvq_key_mean(kd, shape_all, mean_d, wm, wmb)
+        torch.cuda.synchronize()
+        mean_us = _median_time(torch, lambda: K.kvq_key_mean(kd, shape_all, mean_d, wm, wmb), reps) * 1e6
+        v2 = K.Codec(K.INT_ABSMAX, 2, 128, 0)
+        arms = {}
+        for kb_ in (4, 3):
+            kcm = K.Codec(K.INT_ABSMAX, kb_, 128, 256)
+            arms[f"K int{kb_} FWHT-256 g128, no mean"] = (kcm, v2)
+            arms[f"K int{kb_} FWHT-256 g128, key mean subtracted"] = (kcm, v2, True)
+        lo = 0
+    elif workload == "c3v":
         kc3 = K.Codec(K.INT_ABSMAX, 4, 128, 256)
         arms = {"V int2 absmax g128 (one-sided grid)": (kc3, K.Codec(K.INT_ABSMAX, 2, 128, 0)),
                 "V int2 symmetric g128, rotated": (kc3, K.Codec(K.INT_SYM, 2, 128, 256)),
@@ -213,8 +234,10 @@ def secondary(workload, reps):
         anchor_s = _median_time(torch, lambda: K.kvq_decode_attn(ka, va, Hq, 1, qa, None, 0.0, oa, la, wsa, wsa_b),
                                 reps)
     rows = B * (L - lo) * H * T
-    for name, (kc, vc) in arms.items():
-        kp = K.alloc_packed(kc, shape, dev)
+    for name, arm in arms.items():
+        kc, vc = arm[0], arm[1]
+        use_mean = len(arm) > 2 and arm[2]
+        kp = K.alloc_packed(kc, shape, dev, mean=mean_d if use_mean else None)
         vp = K.packed_from_fp16(vq, shape) if vc.codebook == K.FP16 else K.alloc_packed(vc, shape, dev)
 
         def quant():
@@ -229,7 +252,7 @@ def secondary(workload, reps):
         torch.cuda.synchronize()
         t_d = _median_time(torch, lambda: K.kvq_decode_attn(kp, vp, Hq, 1, qq, None, 0.0, out, lse, ws, wsb), reps)
         quality = None
-        if workload == "c3v":                        # attention-visible error of 16 queries
+        if workload in ("c3v", "c3m"):               # attention-visible error of 16 queries
             nqe = 16
             qe = torch.from_numpy(np.ascontiguousarray(q[:, :, :nqe]).view(np.int16)).to(dev)
             kl = torch.empty((B, L, nqe, Hq), dtype=torch.float32, device=dev)
@@ -265,6 +288,9 @@ def secondary(workload, reps):
         }
         if quality:
             rec["quality"] = quality
+        if workload == "c3m":
+            rec["key_mean"] = {"subtracted": bool(use_mean), "kvq_key_mean_us": round(mean_us, 1),
+                               "share_of_key_energy": w.k_mean_share}
         print(json.dumps(rec), flush=True)
         del kp, vp
         torch.cuda.empty_cache()
@@ -282,9 +308,10 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for hardware-counter passes: a known-size copy (the counters' "
                          "calibration), one quantize+pack pair and --decode-queries decode calls")
-    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v"],
+    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v", "c3m"],
                     help="c3: the headline line (default); c4/c5: one line per codec arm of those configs; "
-                         "c3v: the 64K cache with each value codebook, with attention KL")
+                         "c3v: the 64K cache with each value codebook, with attention KL; "
+                         "c3m: the 64K cache with a shared key mean, keys coded with and without it")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions per arm (c4/c5)")
     args = ap.parse_args()
     if args.gpus != 1:

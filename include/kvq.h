@@ -111,9 +111,15 @@ typedef struct {
  * [rows][mins_per_row] (INT_MINMAX only, else NULL); chan_scale: optional fp32
  * [layers][heads][head_dim] per-channel multipliers applied before the rotation
  * and divided back out after dequantising ([E21W] What I tested, arms C/D),
- * NULL for none.  Bit layout: per row, code j occupies bits [j*b, (j+1)*b) of a
- * little-endian stream of uint32 words (RFFT_POLAR: all magnitude codes, then
- * all phase codes; RFFT_CART: all real codes, then all imaginary codes). */
+ * NULL for none; mean: optional fp32 [layers][heads][head_dim] shared mean
+ * subtracted from every row before the channel multiply and added back after
+ * dequantising (the shared key-mean subtraction of [LCPP], the later comment
+ * measuring the failure mode; see kvq_key_mean), NULL for none.  Bit layout: per
+ * row, code j occupies bits [j*b, (j+1)*b) of a little-endian stream of uint32
+ * words (RFFT_POLAR: all magnitude codes, then all phase codes; RFFT_CART: all
+ * real codes, then all imaginary codes).  The per-row operations are, in order:
+ * x -> x - mean -> (x - mean) * chan_scale -> rotation -> codebook, each rounded
+ * to binary32. */
 typedef struct {
   kvq_codec codec;
   kvq_shape shape;
@@ -121,6 +127,7 @@ typedef struct {
   uint16_t* scales;
   uint16_t* mins;
   const float* chan_scale;
+  const float* mean;
 } kvq_packed;
 
 /* Human-readable status. */
@@ -155,15 +162,34 @@ kvq_status kvq_constant_table(int32_t which, int32_t n, float* out);
 kvq_status kvq_calibrate_chan_scale(const uint16_t* k_fp16, const kvq_shape* shape,
                                     float* chan_scale, void* stream);
 
+/* Bytes of workspace kvq_key_mean needs: 8 * layers * heads * head_dim. */
+size_t kvq_key_mean_workspace(const kvq_shape* shape);
+
+/* Shared per-(layer, head) key mean ([LCPP] llama.cpp issue "Per-head adaptive
+ * KV cache quantization", the later comment measuring the failure mode: a shared
+ * key mean carries about half of the key energy, and subtracting the running
+ * mean before quantising and restoring it after removes the failure).
+ * mean[l][h][d] = binary32 rounding of (fp64(S) / (batch * tokens)) * 2^-24,
+ * where S is the exact integer sum over every sequence and token of the fp16
+ * values times 2^24 (so the result does not depend on summation order).
+ * k_fp16: [B][L][H][T][D]; mean: fp32 [L][H][D]; ws: device scratch of
+ * kvq_key_mean_workspace() bytes (no initial contents needed).  batch * tokens
+ * must be at most 2^23 (the exact sum then fits 64 bits); tokens = 0 gives
+ * zeros.  Pass the result as kvq_packed.mean of the key cache. */
+kvq_status kvq_key_mean(const uint16_t* k_fp16, const kvq_shape* shape, float* mean, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* Quantise and pack fp16 rows x_fp16 [B][L][H][T][D] into `out` (codes,
  * scales, mins; shape and codec taken from `out`).  One fused kernel per call:
- * load, optional per-channel multiply, optional Walsh-Hadamard rotation, group
+ * load, optional mean subtraction, optional per-channel multiply, optional
+ * Walsh-Hadamard rotation, group
  * statistic, fp16 scale, code, bit-pack ([E22L] What I tested; [E21W] What I
  * tested).  Codes and scales are bit-identical to the CPU oracle. */
 kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void* stream);
 
 /* Dequantise `in` to fp32 x_hat [B][L][H][T][D] in the original coordinates
- * (inverse codebook, inverse rotation, division by chan_scale). */
+ * (inverse codebook, inverse rotation, division by chan_scale, addition of the
+ * mean). */
 kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream);
 
 /* Bytes of workspace kvq_decode_attn needs for these sizes.  Its first 65536
@@ -187,7 +213,9 @@ size_t kvq_decode_attn_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n
  * the query instead, rotated values by rotating the output once per query.
  * Supported: every codebook for K, every non-rFFT codebook for V, head_dim
  * 64/128/256, up to 8 query heads per KV head, kv_len batch*layers*n_q rows of
- * at most 65535 per launch grid dimension. */
+ * at most 65535 per launch grid dimension.  A key mean (k->mean) shifts every
+ * logit of a query by the same q.mean, which leaves the attention weights and
+ * out unchanged; lse gets sm_scale * q.mean added.  V may not carry a mean. */
 kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
                            int32_t n_q, const uint16_t* q, const int32_t* kv_len,
                            float sm_scale, float* out, float* lse, void* ws,
@@ -216,8 +244,8 @@ size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_
  * query: kl_rows [B][L][n_q][q_heads] = KL(p_fp16 || p_quant) in nats,
  * relerr_rows = ||o_quant - o_fp16|| / ||o_fp16||; kv_err [B][L][H][4] fp64 =
  * (sum dK^2, sum K^2, sum dV^2, sum V^2) over the unit's rows, with dK the
- * dequantised minus fp16 value in original coordinates.  Other arguments as
- * for kvq_decode_attn. */
+ * dequantised minus fp16 value in original coordinates (mean restored).  Other
+ * arguments as for kvq_decode_attn. */
 kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16,
                           const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
                           int32_t n_q, const uint16_t* q, const int32_t* kv_len,

@@ -24,7 +24,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ER
 
 EXPORTS = [
     "kvq_status_string", "kvq_version", "kvq_packed_layout", "kvq_bits_per_value",
-    "kvq_constant_table", "kvq_calibrate_chan_scale", "kvq_quantize_pack", "kvq_dequant",
+    "kvq_constant_table", "kvq_calibrate_chan_scale", "kvq_key_mean_workspace", "kvq_key_mean",
+    "kvq_quantize_pack", "kvq_dequant",
     "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_ex",
     "kvq_attn_error_workspace", "kvq_attn_error",
 ]
@@ -48,7 +49,8 @@ class kvq_shape(ctypes.Structure):
 
 class kvq_packed(ctypes.Structure):
     _fields_ = [("codec", kvq_codec), ("shape", kvq_shape), ("codes", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p), ("mins", ctypes.c_void_p), ("chan_scale", ctypes.c_void_p)]
+                ("scales", ctypes.c_void_p), ("mins", ctypes.c_void_p), ("chan_scale", ctypes.c_void_p),
+                ("mean", ctypes.c_void_p)]
 
 
 def _load():
@@ -64,6 +66,8 @@ def _load():
         "kvq_bits_per_value": ([P, I32], D),
         "kvq_constant_table": ([I32, I32, P], I32),
         "kvq_calibrate_chan_scale": ([P, P, P, P], I32),
+        "kvq_key_mean_workspace": ([P], SZ),
+        "kvq_key_mean": ([P, P, P, P, SZ, P], I32),
         "kvq_quantize_pack": ([P, P, P], I32),
         "kvq_dequant": ([P, P, P], I32),
         "kvq_decode_attn_workspace": ([P, I32, I32], SZ),
@@ -121,13 +125,14 @@ class Packed:
     scales: object          # torch.int16 [rows][ns]     (fp16 bit pattern)
     mins: object            # torch.int16 [rows][nm] or None
     chan_scale: object = None  # torch.float32 [L][H][D] or None
+    mean: object = None        # torch.float32 [L][H][D] or None (shared key mean)
 
     def c(self) -> kvq_packed:
         # cached: the tensors of a Packed are fixed once it is built
         cs = self.__dict__.get("_cstruct")
         if cs is None:
             cs = kvq_packed(self.codec.c(), self.shape.c(), _ptr(self.codes), _ptr(self.scales),
-                            _ptr(self.mins), _ptr(self.chan_scale))
+                            _ptr(self.mins), _ptr(self.chan_scale), _ptr(self.mean))
             self.__dict__["_cstruct"] = cs
         return cs
 
@@ -188,6 +193,17 @@ def kvq_calibrate_chan_scale(k_fp16, shape: Shape, chan_scale, stream=None):
            _lib.kvq_calibrate_chan_scale(_ptr(k_fp16), ctypes.byref(sc), _ptr(chan_scale), _stream(stream)))
 
 
+def kvq_key_mean_workspace(shape: Shape) -> int:
+    sc = shape.c()
+    return _lib.kvq_key_mean_workspace(ctypes.byref(sc))
+
+
+def kvq_key_mean(k_fp16, shape: Shape, mean, ws, ws_bytes: int, stream=None):
+    sc = shape.c()
+    _check("kvq_key_mean", _lib.kvq_key_mean(_ptr(k_fp16), ctypes.byref(sc), _ptr(mean), _ptr(ws), ws_bytes,
+                                             _stream(stream)))
+
+
 def kvq_quantize_pack(x_fp16, out: Packed, stream=None):
     pc = out.c()
     _check("kvq_quantize_pack", _lib.kvq_quantize_pack(_ptr(x_fp16), ctypes.byref(pc), _stream(stream)))
@@ -237,7 +253,7 @@ def kvq_attn_error(k_fp16, v_fp16, k: Packed, v: Packed, q_heads: int, n_q: int,
 
 # ------------------------------------------------------------------ device-memory plumbing
 
-def alloc_packed(codec: Codec, shape: Shape, device="cuda", chan_scale=None) -> Packed:
+def alloc_packed(codec: Codec, shape: Shape, device="cuda", chan_scale=None, mean=None) -> Packed:
     """Allocate the device buffers of a packed tensor (sizes from kvq_packed_layout)."""
     import torch
     w, s, m = kvq_packed_layout(shape, codec)
@@ -245,7 +261,7 @@ def alloc_packed(codec: Codec, shape: Shape, device="cuda", chan_scale=None) -> 
     codes = torch.empty((rows, w), dtype=torch.int32, device=device)
     scales = torch.empty((rows, s), dtype=torch.int16, device=device)
     mins = torch.empty((rows, m), dtype=torch.int16, device=device) if m else None
-    return Packed(codec, shape, codes, scales, mins, chan_scale)
+    return Packed(codec, shape, codes, scales, mins, chan_scale, mean)
 
 
 def packed_from_fp16(x_fp16, shape: Shape) -> Packed:

@@ -186,9 +186,9 @@ static kvq_status check_packed(const kvq_packed* p, bool need_write) {
   if (ns && !p->scales) return KVQ_ERR_ARG;
   if (nm && !p->mins) return KVQ_ERR_ARG;
   if (!aligned16(p->codes) || (p->scales && !aligned16(p->scales)) || (p->mins && !aligned16(p->mins)) ||
-      (p->chan_scale && !aligned16(p->chan_scale)))
+      (p->chan_scale && !aligned16(p->chan_scale)) || (p->mean && !aligned16(p->mean)))
     return KVQ_ERR_ALIGN;
-  if (p->chan_scale && p->codec.codebook == KVQ_FP16) return KVQ_ERR_UNSUPPORTED;
+  if ((p->chan_scale || p->mean) && p->codec.codebook == KVQ_FP16) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -293,6 +293,24 @@ kvq_status kvq_calibrate_chan_scale(const uint16_t* k_fp16, const kvq_shape* sha
   return hip_status(launch_calibrate(k_fp16, *shape, chan_scale, (hipStream_t)stream));
 }
 
+size_t kvq_key_mean_workspace(const kvq_shape* shape) {
+  if (check_shape(shape) != KVQ_OK) return 0;
+  return (size_t)8 * shape->layers * shape->heads * shape->head_dim;
+}
+
+kvq_status kvq_key_mean(const uint16_t* k_fp16, const kvq_shape* shape, float* mean, void* ws, size_t ws_bytes,
+                        void* stream) {
+  kvq_status st = check_shape(shape);
+  if (st != KVQ_OK) return st;
+  if (!k_fp16 || !mean) return KVQ_ERR_ARG;
+  if ((double)shape->batch * shape->tokens > (double)(1 << 23)) return KVQ_ERR_ARG;
+  if (!aligned16(k_fp16) || !aligned16(mean)) return KVQ_ERR_ALIGN;
+  const size_t need = (size_t)8 * shape->layers * shape->heads * shape->head_dim;
+  if (ws_bytes < need || !ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVQ_ERR_ALIGN;
+  return hip_status(launch_key_mean(k_fp16, *shape, mean, static_cast<long long*>(ws), (hipStream_t)stream));
+}
+
 kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void* stream) {
   kvq_status st = check_packed(out, true);
   if (st != KVQ_OK) return st;
@@ -318,7 +336,7 @@ static kvq_status check_attn(const kvq_packed* k, const kvq_packed* v, int32_t q
   st = check_packed(v, false);
   if (st != KVQ_OK) return st;
   if (!same_shape(k->shape, v->shape)) return KVQ_ERR_ARG;
-  if (is_rfft(v->codec.codebook)) return KVQ_ERR_UNSUPPORTED;
+  if (is_rfft(v->codec.codebook) || v->mean) return KVQ_ERR_UNSUPPORTED;
   if (q_heads < 1 || q_heads % k->shape.heads != 0 || q_heads / k->shape.heads > 8) return KVQ_ERR_UNSUPPORTED;
   if (n_q < 1) return KVQ_ERR_ARG;
   if (!q) return KVQ_ERR_ARG;
@@ -356,8 +374,10 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
     // no keys: zero output, lse = -inf (handled by the generic kernel's combine)
   }
   const bool use_fast = (path == 2) || (path == 0 && fast_ok);
-  return hip_status(use_fast ? launch_decode_fast(pr, (hipStream_t)stream)
-                             : launch_decode_generic(pr, (hipStream_t)stream));
+  hipError_t e = use_fast ? launch_decode_fast(pr, (hipStream_t)stream) : launch_decode_generic(pr, (hipStream_t)stream);
+  // a key mean adds q.mean to every logit of a query: weights unchanged, lse shifted
+  if (e == hipSuccess && k->mean && lse) e = launch_lse_mean(pr, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,

@@ -33,6 +33,7 @@ struct DevCodec {
   const uint16_t* scales;
   const uint16_t* mins;
   const float* chan;
+  const float* mean;
   RfftCodec rc;
 };
 
@@ -925,9 +926,11 @@ __global__ __launch_bounds__(kBlock) void k_kverr(EArgs a) {
   const int per = (a.T + a.chunks - 1) / a.chunks;
   const int t0 = blockIdx.x * per, t1 = min(a.T, t0 + per);
   const float* cp = nullptr;
-  if (a.c.chan) {
+  const float* mp = nullptr;
+  {
     const int h = (int)(unit % a.H), l = (int)((unit / a.H) % a.L);
-    cp = a.c.chan + ((size_t)l * a.H + h) * a.D + 16 * j;
+    if (a.c.chan) cp = a.c.chan + ((size_t)l * a.H + h) * a.D + 16 * j;
+    if (a.c.mean) mp = a.c.mean + ((size_t)l * a.H + h) * a.D + 16 * j;
   }
   double se = 0.0, sx = 0.0;
   for (int tb = t0; tb < t1; tb += RPB) {
@@ -945,7 +948,8 @@ __global__ __launch_bounds__(kBlock) void k_kverr(EArgs a) {
     if (active) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const float y = cp ? __fdiv_rn(v[k], cp[k]) : v[k];
+        float y = cp ? __fdiv_rn(v[k], cp[k]) : v[k];
+        if (mp) y = y + mp[k];
         const double x = (double)h2f(a.x[(size_t)row * a.D + 16 * j + k]);
         const double d = (double)y - x;
         se += d * d;
@@ -976,6 +980,27 @@ __global__ void k_kverr_final(const double* pk, const double* pv, int chunks, lo
     b0 += pv[(u * chunks + c) * 2]; b1 += pv[(u * chunks + c) * 2 + 1];
   }
   out[u * 4 + 0] = a0; out[u * 4 + 1] = a1; out[u * 4 + 2] = b0; out[u * 4 + 3] = b1;
+}
+
+// A shared key mean adds q.mean to every logit of a query (a constant per row, so
+// the attention weights do not move): lse[row] += sm * q.mean[l][kv head].  One
+// wavefront per (b, l, query, query head) row.
+__global__ __launch_bounds__(kBlock) void k_lse_mean(const uint16_t* __restrict__ q, const float* __restrict__ mean,
+                                                     float* __restrict__ lse, long long rows, int L, int n_q, int Hq,
+                                                     int H, int D, float sm) {
+  const long long row = (long long)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;                       // the whole wavefront shares the row
+  const int jq = (int)(row % Hq);
+  const int l = (int)((row / ((long long)Hq * n_q)) % L);
+  const int kvh = jq / (Hq / H);
+  const uint16_t* qp = q + row * D;
+  const float* mp = mean + ((size_t)l * H + kvh) * D;
+  float s = 0.0f;
+  for (int d = lane; d < D; d += 64) s += h2f(qp[d]) * mp[d];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (lane == 0) lse[row] = lse[row] + sm * s;   // -inf (no keys) stays -inf
 }
 
 // ------------------------------------------------------------------ host side
@@ -1012,6 +1037,7 @@ static DevCodec dev_codec(const kvq_packed& p) {
   c.scales = p.scales;
   c.mins = p.mins;
   c.chan = p.chan_scale;
+  c.mean = p.mean;
   if (c.cb == KVQ_RFFT_POLAR || c.cb == KVQ_RFFT_CART) {
     RfftCodec& r = c.rc;
     r.cb = c.cb;
@@ -1138,6 +1164,8 @@ static hipError_t dispatch_wave(const AArgs& a, long long R, hipStream_t st) {
     return launch_wave<KVQ_INT_ABSMAX, 4, KVQ_INT_ABSMAX, 4>(a, R, st);
   if (is(kc, kb, KVQ_INT_ABSMAX, 3) && is(vc, vb, KVQ_INT_ABSMAX, 3))
     return launch_wave<KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 3>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 3) && is(vc, vb, KVQ_INT_ABSMAX, 2))
+    return launch_wave<KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 2>(a, R, st);
   if (is(kc, kb, KVQ_INT_MINMAX, 4) && is(vc, vb, KVQ_INT_MINMAX, 4))
     return launch_wave<KVQ_INT_MINMAX, 4, KVQ_INT_MINMAX, 4>(a, R, st);
   if (is(kc, kb, KVQ_INT_MINMAX, 3) && is(vc, vb, KVQ_INT_MINMAX, 3))
@@ -1266,6 +1294,20 @@ hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   k_kverr_final<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(pk, pv, chunks, units, pr.kv_err);
+  return hipGetLastError();
+}
+
+}  // namespace kvq
+
+namespace kvq {
+
+hipError_t launch_lse_mean(const AttnProblem& pr, hipStream_t st) {
+  const kvq_shape& sh = pr.k->shape;
+  const long long rows = (long long)sh.batch * sh.layers * pr.n_q * pr.Hq;
+  if (rows == 0) return hipSuccess;
+  const long long blocks = (rows + kBlock / 64 - 1) / (kBlock / 64);
+  k_lse_mean<<<(unsigned)blocks, kBlock, 0, st>>>(pr.q, pr.k->mean, pr.lse, rows, sh.layers, pr.n_q, pr.Hq, sh.heads,
+                                                  sh.head_dim, pr.sm_scale);
   return hipGetLastError();
 }
 

@@ -151,6 +151,7 @@ struct RowGeom {        // a [B][L][H][T][D] tensor seen as rows
 hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st);
 hipError_t launch_dequant(const kvq_packed& p, float* xhat, hipStream_t st);
 hipError_t launch_calibrate(const uint16_t* k, const kvq_shape& s, float* c, hipStream_t st);
+hipError_t launch_key_mean(const uint16_t* k, const kvq_shape& s, float* mean, long long* ws, hipStream_t st);
 hipError_t launch_rfft_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st);
 hipError_t launch_rfft_dequant(const kvq_packed& p, float* xhat, hipStream_t st);
 hipError_t launch_rfft_kverr(const uint16_t* x, const kvq_packed& p, double* part, int chunks, hipStream_t st);
@@ -188,6 +189,7 @@ size_t error_ws_bytes(const kvq_shape& s, int Hq, int n_q);
 int decode_splits(const kvq_shape& s, int Hq, int n_q);
 hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st);
 hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st);
+hipError_t launch_lse_mean(const AttnProblem& pr, hipStream_t st);
 bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st);
 size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q);

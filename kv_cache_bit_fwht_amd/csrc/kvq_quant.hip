@@ -23,6 +23,7 @@ struct QArgs {
   uint16_t* scales;
   uint16_t* mins;
   const float* chan;      // [L][H][D] or null
+  const float* mean;      // [L][H][D] or null
   long long rows;
   int D, T, H, L;
   int lpt_log2;           // log2(D/16)
@@ -37,6 +38,33 @@ __device__ __forceinline__ void row_unit(long long row, int T, int H, int L, int
   const long long unit = row / T;
   h = (int)(unit % H);
   l = (int)((unit / H) % L);
+}
+
+// The lane's 16 values (dims 16j .. 16j+15 at `off` in the [L][H][D] vectors): subtract
+// the shared mean, then multiply by the channel scale, each rounded to binary32.
+__device__ __forceinline__ void pre_row(float (&v)[16], const float* mean, const float* chan, size_t off) {
+  if (mean != nullptr) {
+    const float4* mp = reinterpret_cast<const float4*>(mean + off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 m = mp[k];
+      v[4 * k] = v[4 * k] - m.x;
+      v[4 * k + 1] = v[4 * k + 1] - m.y;
+      v[4 * k + 2] = v[4 * k + 2] - m.z;
+      v[4 * k + 3] = v[4 * k + 3] - m.w;
+    }
+  }
+  if (chan != nullptr) {
+    const float4* cp = reinterpret_cast<const float4*>(chan + off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 cc = cp[k];
+      v[4 * k] = v[4 * k] * cc.x;
+      v[4 * k + 1] = v[4 * k + 1] * cc.y;
+      v[4 * k + 2] = v[4 * k + 2] * cc.z;
+      v[4 * k + 3] = v[4 * k + 3] * cc.w;
+    }
+  }
 }
 
 template <int CB, int BITS>
@@ -73,18 +101,10 @@ __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
       v[2 * k] = h2f((uint16_t)(raw[k] & 0xffffu));
       v[2 * k + 1] = h2f((uint16_t)(raw[k] >> 16));
     }
-    if (a.chan != nullptr && active) {
+    if ((a.chan != nullptr || a.mean != nullptr) && active) {
       int l, h;
       row_unit(row, a.T, a.H, a.L, l, h);
-      const float4* cp = reinterpret_cast<const float4*>(a.chan + ((size_t)l * a.H + h) * a.D + 16 * j);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 cc = cp[k];
-        v[4 * k] = v[4 * k] * cc.x;
-        v[4 * k + 1] = v[4 * k + 1] * cc.y;
-        v[4 * k + 2] = v[4 * k + 2] * cc.z;
-        v[4 * k + 3] = v[4 * k + 3] * cc.w;
-      }
+      pre_row(v, a.mean, a.chan, ((size_t)l * a.H + h) * a.D + 16 * j);
     }
     if (a.W > 1) fwht_rows(v, rowlds, j, LPT, a.W, a.kappa);
     uint32_t c[16];
@@ -148,12 +168,18 @@ __global__ __launch_bounds__(kBlock) void k_dequant(QArgs a) {
     decode16<CB, BITS>(c, s16, z16, a.tab, v);
     if (a.W > 1) fwht_rows(v, rowlds, j, LPT, a.W, a.kappa);
     if (!active) continue;
-    if (a.chan != nullptr) {
+    if (a.chan != nullptr || a.mean != nullptr) {
       int l, h;
       row_unit(row, a.T, a.H, a.L, l, h);
-      const float* cp = a.chan + ((size_t)l * a.H + h) * a.D + 16 * j;
+      const size_t off = ((size_t)l * a.H + h) * a.D + 16 * j;
+      if (a.chan != nullptr) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = __fdiv_rn(v[k], cp[k]);
+        for (int k = 0; k < 16; ++k) v[k] = __fdiv_rn(v[k], a.chan[off + k]);
+      }
+      if (a.mean != nullptr) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = v[k] + a.mean[off + k];
+      }
     }
     float4* dst = reinterpret_cast<float4*>(a.xhat + (size_t)row * a.D + 16 * j);
 #pragma unroll
@@ -174,6 +200,59 @@ __global__ __launch_bounds__(kBlock) void k_calibrate(const uint16_t* __restrict
   c[idx] = (m == 0.0f) ? 1.0f : __fdiv_rn(1.0f, m);
 }
 
+// Shared key mean ([LCPP] llama.cpp issue "Per-head adaptive KV cache quantization",
+// the later comment on a shared per-head key mean): exact integer sums of the fp16
+// values in units of 2^-24 (every fp16 value is such a multiple, so v * 2^24 is an
+// integer below 2^40 and the sums are exact in any order), then one fp64 quotient.
+__global__ void k_zero_u64(unsigned long long* p, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+// Block (chunk, unit): tokens [t0, t1) of every sequence.  A thread takes 8
+// consecutive channels of a row (one 16-byte load), so kBlock * 8 / D rows per pass.
+__global__ __launch_bounds__(kBlock) void k_key_sum(const uint16_t* __restrict__ k, int B, int L, int H, int T,
+                                                    int D, int chunk, unsigned long long* __restrict__ acc) {
+  __shared__ long long red[kBlock];
+  const int u = blockIdx.y, l = u / H, h = u - l * H;
+  const int tpr = D / 8, rpi = kBlock / tpr;            // threads per row, rows per pass
+  const int c8 = threadIdx.x % tpr, r0 = threadIdx.x / tpr;
+  const int t0 = blockIdx.x * chunk, t1 = min(T, t0 + chunk);
+  long long s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int b = 0; b < B; ++b) {
+    const uint16_t* base = k + (((size_t)b * L + l) * H + h) * (size_t)T * D + 8 * c8;
+    for (int t = t0 + r0; t < t1; t += rpi) {
+      const uint4 p = *reinterpret_cast<const uint4*>(base + (size_t)t * D);
+      const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[2 * i] += (long long)(h2f((uint16_t)(w[i] & 0xffffu)) * 16777216.0f);
+        s[2 * i + 1] += (long long)(h2f((uint16_t)(w[i] >> 16)) * 16777216.0f);
+      }
+    }
+  }
+  // channel 8*c8 + i: sum over the rpi row slots, then one atomic per channel
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    red[threadIdx.x] = s[i];
+    __syncthreads();
+    if (r0 == 0) {
+      long long v = s[i];
+      for (int r = 1; r < rpi; ++r) v += red[r * tpr + c8];
+      atomicAdd(&acc[(size_t)u * D + 8 * c8 + i], (unsigned long long)v);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void k_key_mean_final(const unsigned long long* __restrict__ acc, long long total, long long n,
+                                 float* __restrict__ mean) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const long long S = (long long)acc[i];
+  mean[i] = n ? (float)(((double)S / (double)n) * 0x1p-24) : 0.0f;
+}
+
 // ------------------------------------------------------------------ host launchers
 
 static QArgs make_args(const kvq_packed& p) {
@@ -182,6 +261,7 @@ static QArgs make_args(const kvq_packed& p) {
   a.scales = p.scales;
   a.mins = p.mins;
   a.chan = p.chan_scale;
+  a.mean = p.mean;
   a.D = p.shape.head_dim;
   a.T = p.shape.tokens;
   a.H = p.shape.heads;
@@ -272,7 +352,7 @@ constexpr int kRowLds = 256 + 16;                    // LDS floats per row (padd
 
 // Quads of rows q_first, q_first + q_stride, ... of one tensor; each wavefront of the
 // caller owns one quad per step (16 lanes per row).
-template <int BITS, bool ROT>
+template <int BITS, bool ROT, bool PRE>
 __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first, long long q_stride,
                                                float* rl, int lane) {
   constexpr int D = 256;
@@ -283,6 +363,10 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
   const int j = lane & 15;                           // lane within the row
   const int lpg = a.g >> 4;                          // lanes per group
   const long long nquads = (a.rows + 3) >> 2;
+  // PRE (a mean or channel scales): the row range and vector offset of the current
+  // (layer, head), recomputed only when a row leaves it (64-bit division is slow)
+  long long cu_lo = 0, cu_hi = 0;
+  size_t cu_off = 0;
   for (long long qd = q_first; qd < nquads; qd += q_stride) {
     const long long row = qd * 4 + (lane >> 4);
     const bool active = row < a.rows;
@@ -299,17 +383,16 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
       v[2 * k] = h2f((uint16_t)(raw[k] & 0xffffu));
       v[2 * k + 1] = h2f((uint16_t)(raw[k] >> 16));
     }
-    if (a.chan != nullptr && active) {
-      int l, h;
-      row_unit(row, a.T, a.H, a.L, l, h);
-      const float4* cp = reinterpret_cast<const float4*>(a.chan + ((size_t)l * a.H + h) * D + 16 * j);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 cc = cp[k];
-        v[4 * k] = v[4 * k] * cc.x;
-        v[4 * k + 1] = v[4 * k + 1] * cc.y;
-        v[4 * k + 2] = v[4 * k + 2] * cc.z;
-        v[4 * k + 3] = v[4 * k + 3] * cc.w;
+    if constexpr (PRE) {
+      if (active) {
+        if (row < cu_lo || row >= cu_hi) {
+          const long long unit = row / a.T;
+          cu_lo = unit * a.T;
+          cu_hi = cu_lo + a.T;
+          const int h = (int)(unit % a.H), l = (int)((unit / a.H) % a.L);
+          cu_off = ((size_t)l * a.H + h) * D + 16 * j;
+        }
+        pre_row(v, a.mean, a.chan, cu_off);
       }
     }
     if constexpr (ROT) {
@@ -409,13 +492,13 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
   }
 }
 
-template <int BITS, bool ROT>
+template <int BITS, bool ROT, bool PRE>
 __global__ __launch_bounds__(kBlock) void k_quantize_absmax256(QArgs a) {
   __shared__ float lds[kBlock / 16][kRowLds];
   const int tid = threadIdx.x;
   constexpr int waves = kBlock / 64;
-  absmax256_rows<BITS, ROT>(a, (long long)blockIdx.x * waves + (tid >> 6), (long long)gridDim.x * waves,
-                            lds[tid >> 4], tid & 63);
+  absmax256_rows<BITS, ROT, PRE>(a, (long long)blockIdx.x * waves + (tid >> 6), (long long)gridDim.x * waves,
+                                 lds[tid >> 4], tid & 63);
 }
 
 static bool absmax256_supported(const kvq_packed& p) {
@@ -426,22 +509,33 @@ static bool absmax256_supported(const kvq_packed& p) {
   return c.rot_width <= 1 || c.rot_width == 256;
 }
 
+// At most the blocks that are resident at once (8 wavefronts per SIMD).
 static long long absmax256_blocks(long long rows) {
   const long long quads = (rows + 3) / 4;
   long long blocks = (quads + (kBlock / 64) - 1) / (kBlock / 64);
-  if (blocks > 256 * 8) blocks = 256 * 8;
+  const long long cap = 256 * 8;
+  if (blocks > cap) blocks = cap;
   return blocks < 1 ? 1 : blocks;
 }
 
 static void launch_absmax256(const QArgs& a, const kvq_codec& c, hipStream_t st) {
   const dim3 grid((unsigned)absmax256_blocks(a.rows));
   const bool rot = c.rot_width == 256;
-  if (c.bits == 2) rot ? k_quantize_absmax256<2, true><<<grid, kBlock, 0, st>>>(a)
-                       : k_quantize_absmax256<2, false><<<grid, kBlock, 0, st>>>(a);
-  else if (c.bits == 4) rot ? k_quantize_absmax256<4, true><<<grid, kBlock, 0, st>>>(a)
-                            : k_quantize_absmax256<4, false><<<grid, kBlock, 0, st>>>(a);
-  else rot ? k_quantize_absmax256<8, true><<<grid, kBlock, 0, st>>>(a)
-           : k_quantize_absmax256<8, false><<<grid, kBlock, 0, st>>>(a);
+  if (a.chan != nullptr || a.mean != nullptr) {
+    if (c.bits == 2) rot ? k_quantize_absmax256<2, true, true><<<grid, kBlock, 0, st>>>(a)
+                         : k_quantize_absmax256<2, false, true><<<grid, kBlock, 0, st>>>(a);
+    else if (c.bits == 4) rot ? k_quantize_absmax256<4, true, true><<<grid, kBlock, 0, st>>>(a)
+                              : k_quantize_absmax256<4, false, true><<<grid, kBlock, 0, st>>>(a);
+    else rot ? k_quantize_absmax256<8, true, true><<<grid, kBlock, 0, st>>>(a)
+             : k_quantize_absmax256<8, false, true><<<grid, kBlock, 0, st>>>(a);
+    return;
+  }
+  if (c.bits == 2) rot ? k_quantize_absmax256<2, true, false><<<grid, kBlock, 0, st>>>(a)
+                       : k_quantize_absmax256<2, false, false><<<grid, kBlock, 0, st>>>(a);
+  else if (c.bits == 4) rot ? k_quantize_absmax256<4, true, false><<<grid, kBlock, 0, st>>>(a)
+                            : k_quantize_absmax256<4, false, false><<<grid, kBlock, 0, st>>>(a);
+  else rot ? k_quantize_absmax256<8, true, false><<<grid, kBlock, 0, st>>>(a)
+           : k_quantize_absmax256<8, false, false><<<grid, kBlock, 0, st>>>(a);
 }
 
 hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st) {
@@ -463,6 +557,27 @@ hipError_t launch_dequant(const kvq_packed& p, float* xhat, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
   const dim3 grid(grid_for(a.rows, a.lpt_log2)), block(kBlock);
   KVQ_DISPATCH_CODEC(p.codec.codebook, p.codec.bits, k_dequant, <<<grid, block, 0, st>>>(a))
+  return hipGetLastError();
+}
+
+hipError_t launch_key_mean(const uint16_t* k, const kvq_shape& s, float* mean, long long* ws, hipStream_t st) {
+  const long long units = (long long)s.layers * s.heads, total = units * s.head_dim;
+  if (total == 0) return hipSuccess;
+  unsigned long long* acc = reinterpret_cast<unsigned long long*>(ws);
+  k_zero_u64<<<(unsigned)((total + kBlock - 1) / kBlock), kBlock, 0, st>>>(acc, total);
+  if (s.tokens > 0 && s.batch > 0) {
+    const int rpi = kBlock * 8 / s.head_dim;
+    long long chunks = (2048 + units - 1) / units;
+    const long long max_chunks = (s.tokens + rpi * 32 - 1) / (rpi * 32);
+    if (chunks > max_chunks) chunks = max_chunks;
+    if (chunks < 1) chunks = 1;
+    const int chunk = (int)((s.tokens + chunks - 1) / chunks);
+    chunks = (s.tokens + chunk - 1) / chunk;
+    k_key_sum<<<dim3((unsigned)chunks, (unsigned)units), kBlock, 0, st>>>(k, s.batch, s.layers, s.heads, s.tokens,
+                                                                         s.head_dim, chunk, acc);
+  }
+  k_key_mean_final<<<(unsigned)((total + kBlock - 1) / kBlock), kBlock, 0, st>>>(
+      acc, total, (long long)s.batch * s.tokens, mean);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ struct RArgs {
   uint32_t* codes;
   uint16_t* scales;
   const float* chan;
+  const float* mean;
   long long rows;
   int T, H, L;
   RfftCodec c;
@@ -309,12 +310,18 @@ __global__ __launch_bounds__(kBlock) void k_rfft_quantize(RArgs a) {
       const uint16_t* xp = a.x + (size_t)row * N + rl;
 #pragma unroll
       for (int e = 0; e < 16; ++e) re[e] = h2f(xp[(N / 16) * rev4(e)]);
-      if (a.chan) {
+      if (a.chan || a.mean) {
         int ul, uh;
         unit_of(row, a.T, a.H, a.L, ul, uh);
-        const float* cp = a.chan + ((size_t)ul * a.H + uh) * N + rl;
+        const size_t off = ((size_t)ul * a.H + uh) * N + rl;
+        if (a.mean) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) re[e] = re[e] * cp[(N / 16) * rev4(e)];
+          for (int e = 0; e < 16; ++e) re[e] = re[e] - a.mean[off + (N / 16) * rev4(e)];
+        }
+        if (a.chan) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) re[e] = re[e] * a.chan[off + (N / 16) * rev4(e)];
+        }
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) im[e] = 0.0f;
@@ -566,14 +573,17 @@ __global__ __launch_bounds__(kBlock) void k_rfft_dequant(RArgs a) {
     rfft_decode_row(a, ltab, row, active, s_re[wv], s_im[wv], lane);
     if (active) {
       const float* cp = nullptr;
-      if (a.chan) {
+      const float* mp = nullptr;
+      if (a.chan || a.mean) {
         int l, h;
         unit_of(row, a.T, a.H, a.L, l, h);
-        cp = a.chan + ((size_t)l * a.H + h) * N;
+        if (a.chan) cp = a.chan + ((size_t)l * a.H + h) * N;
+        if (a.mean) mp = a.mean + ((size_t)l * a.H + h) * N;
       }
       for (int n = lane; n < N; n += 64) {
         float v = s_re[wv][n] * invN;
         if (cp) v = __fdiv_rn(v, cp[n]);
+        if (mp) v = v + mp[n];
         a.xhat[(size_t)row * N + n] = v;
       }
     }
@@ -596,9 +606,11 @@ __global__ __launch_bounds__(kBlock) void k_rfft_kverr(RArgs a, double* part, in
   const int t0 = blockIdx.x * per, t1 = min(T, t0 + per);
   double se = 0.0, sx = 0.0;
   const float* cp = nullptr;
-  if (a.chan) {
+  const float* mp = nullptr;
+  {
     const int h = (int)(unit % a.H), l = (int)((unit / a.H) % a.L);
-    cp = a.chan + ((size_t)l * a.H + h) * N;
+    if (a.chan) cp = a.chan + ((size_t)l * a.H + h) * N;
+    if (a.mean) mp = a.mean + ((size_t)l * a.H + h) * N;
   }
   for (int tb = t0; tb < t1; tb += kWaves) {
     const int t = tb + wv;
@@ -609,6 +621,7 @@ __global__ __launch_bounds__(kBlock) void k_rfft_kverr(RArgs a, double* part, in
       for (int n = lane; n < N; n += 64) {
         float v = s_re[wv][n] * invN;
         if (cp) v = __fdiv_rn(v, cp[n]);
+        if (mp) v = v + mp[n];
         const double x = (double)h2f(a.x[(size_t)row * N + n]);
         const double d = (double)v - x;
         se += d * d;
@@ -638,6 +651,7 @@ static RArgs make_rargs(const kvq_packed& p) {
   a.codes = p.codes;
   a.scales = p.scales;
   a.chan = p.chan_scale;
+  a.mean = p.mean;
   a.rows = (long long)p.shape.batch * p.shape.layers * p.shape.heads * p.shape.tokens;
   a.T = p.shape.tokens;
   a.H = p.shape.heads;

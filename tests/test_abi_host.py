@@ -257,3 +257,33 @@ def test_workspace_sizes_cover_the_decode_partials(K):
     assert ws % 256 == 0 or ws > 0
     assert K._lib.kvq_decode_attn_workspace(ctypes.byref(s), 0, 1) == 0
     assert K._lib.kvq_attn_error_workspace(ctypes.byref(s), 16, 1) > 0
+
+
+def test_key_mean_validates_before_launching(K):
+    L = K._lib
+    s = K.kvq_shape(2, 2, 4, 64, 128)
+    need = L.kvq_key_mean_workspace(ctypes.byref(s))
+    assert need == 8 * 2 * 4 * 128
+    assert L.kvq_key_mean(None, ctypes.byref(s), FAKE, FAKE, need, None) == ERR_ARG
+    assert L.kvq_key_mean(FAKE, ctypes.byref(s), None, FAKE, need, None) == ERR_ARG
+    assert L.kvq_key_mean(FAKE, ctypes.byref(s), FAKE, FAKE, need - 1, None) == ERR_WORKSPACE
+    assert L.kvq_key_mean(FAKE, ctypes.byref(s), FAKE, None, need, None) == ERR_WORKSPACE
+    assert L.kvq_key_mean(FAKE_ODD, ctypes.byref(s), FAKE, FAKE, need, None) == ERR_ALIGN
+    assert L.kvq_key_mean(FAKE, ctypes.byref(s), FAKE, FAKE_ODD, need, None) == ERR_ALIGN
+    big = K.kvq_shape(2, 1, 1, 2 ** 22 + 1, 64)          # batch * tokens above 2^23
+    assert L.kvq_key_mean(FAKE, ctypes.byref(big), FAKE, FAKE, 8 * 64, None) == ERR_ARG
+
+
+def test_mean_field_is_validated(K):
+    L = K._lib
+    p = _packed(K)
+    p.mean = FAKE_ODD
+    assert L.kvq_quantize_pack(FAKE, ctypes.byref(p), None) == ERR_ALIGN
+    p16 = _packed(K, codec=(0, 0, 0, 0, 0), scales=None)
+    p16.mean = FAKE
+    assert L.kvq_quantize_pack(FAKE, ctypes.byref(p16), None) == ERR_UNSUPPORTED
+    k = _packed(K)
+    k.mean = FAKE                                          # a key mean is fine for decode ...
+    v = _packed(K, codec=(1, 2, 128, 0, 0))
+    v.mean = FAKE                                          # ... a value mean is not
+    assert _decode(K, k, v) == ERR_UNSUPPORTED
