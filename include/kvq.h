@@ -187,6 +187,16 @@ kvq_status kvq_key_mean(const uint16_t* k_fp16, const kvq_shape* shape, float* m
  * tested).  Codes and scales are bit-identical to the CPU oracle. */
 kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void* stream);
 
+/* Append path: quantise and pack fp16 rows x_fp16 [B][L][H][n_tokens][D] into
+ * token positions [token0, token0 + n_tokens) of every (sequence, layer, head)
+ * unit of `out` (shape and codec from `out`; rows outside the window are not
+ * touched).  The codes of a row do not depend on any other row, so appending
+ * tokens one step at a time gives exactly the codes of quantising them all at
+ * once ([FMAG-6] The winning recipe: decode steps write the cache as they go).
+ * 0 <= token0, n_tokens >= 1, token0 + n_tokens <= out->shape.tokens. */
+kvq_status kvq_quantize_pack_tokens(const uint16_t* x_fp16, int32_t token0, int32_t n_tokens,
+                                    const kvq_packed* out, void* stream);
+
 /* Dequantise `in` to fp32 x_hat [B][L][H][T][D] in the original coordinates
  * (inverse codebook, inverse rotation, division by chan_scale, addition of the
  * mean). */
@@ -233,6 +243,47 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
                               int32_t n_q, const uint16_t* q, const int32_t* kv_len,
                               float sm_scale, float* out, float* lse, void* ws,
                               size_t ws_bytes, int32_t path, void* stream);
+
+/* One piece of a logical cache of `layers` x `tokens`: packed K and V (same
+ * shape, batch/heads/head_dim equal to the other segments') holding layers
+ * [layer0, layer0 + k->shape.layers) and tokens [token0, token0 + k->shape.tokens)
+ * of every sequence.  Segments describe decode anchors ([FMAG-6] The winning
+ * recipe, Selective-Layer Decode Anchoring: the KV of the first decoded tokens
+ * kept at fp16/int8/int4 on chosen layers), fp16 anchor layers ([FMAG-6] Minimal
+ * recipe), sliding windows and per-layer codec choices. */
+typedef struct {
+  const kvq_packed* k;
+  const kvq_packed* v;
+  int32_t layer0;
+  int32_t token0;
+} kvq_segment;
+
+/* Bytes of workspace kvq_decode_attn_segments needs (0 for invalid arguments).
+ * Its first 65536 bytes are the decode counters (zero before first use, left
+ * zero by every call), as for kvq_decode_attn. */
+size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg, int32_t layers,
+                                          int32_t q_heads, int32_t n_q);
+
+/* Decode attention over a logical cache [B][layers][H][tokens][D] given as 1..16
+ * segments that tile it: for every layer, the segments covering it cover tokens
+ * [0, tokens) exactly, without overlap.  q: fp16 [B][layers][n_q][q_heads][D];
+ * kv_len: int32 [B][layers][n_q] over the logical token axis (NULL = all);
+ * out/lse as for kvq_decode_attn over the whole logical cache.  Each segment is
+ * decoded by the kvq_decode_attn kernels (the MFMA kernel where it applies) and
+ * its (out, lse) merged into the running result by log-sum-exp weights; a
+ * segment's key mean shifts only its own lse, as the whole cache's would. */
+kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers,
+                                    int32_t tokens, int32_t q_heads, int32_t n_q, const uint16_t* q,
+                                    const int32_t* kv_len, float sm_scale, float* out, float* lse,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* Host only.  Effective bits per cached value of a tiled logical cache: the
+ * segments' K/V bits per value (kvq_bits_per_value, averaged over K and V)
+ * weighted by the layers x tokens each holds ([FMAG-6] Milestone and Minimal
+ * recipe: anchored rows count at their own precision, so anchors kept for the
+ * prompt and the first D decoded tokens cost (L + D) rows per anchored layer).
+ * Returns a negative value for segments that do not tile layers x tokens. */
+double kvq_effective_bits(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t tokens);
 
 /* Bytes of workspace kvq_attn_error needs. */
 size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q);

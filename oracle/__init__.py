@@ -44,6 +44,6 @@ from .codec import (  # noqa: F401
     quantize_pack, dequant,
 )
 from .attention import (  # noqa: F401
-    attend_unit, decode_attn, attn_error, kl_div, rel_err, kv_err_unit,
+    attend_unit, decode_attn, attn_error, kl_div, rel_err, kv_err_unit, assemble_segments,
 )
-from .accounting import bits_per_value, kv_bits_per_value, rfft_payload_bits_per_value  # noqa: F401
+from .accounting import bits_per_value, kv_bits_per_value, rfft_payload_bits_per_value, tiles, effective_bits  # noqa: F401

@@ -41,3 +41,34 @@ def kv_bits_per_value(k: Codec, v: Codec, D: int, anchor_layers: int = 0, layers
 def rfft_payload_bits_per_value(mag_bits: int, phase_bits: int, D: int) -> float:
     """Payload only (no scales): (mag + phase) bits on D/2 + 1 bins per D reals."""
     return (mag_bits + phase_bits) * (D // 2 + 1) / D
+
+
+def tiles(segments, layers: int, tokens: int) -> bool:
+    """True when the segments (layer0, n_layers, token0, n_tokens) cover every
+    (layer, token) of a layers x tokens cache exactly once."""
+    cover = [[0] * tokens for _ in range(layers)]
+    for (l0, nl, t0, nt) in segments:
+        if nl < 1 or nt < 1 or l0 < 0 or t0 < 0 or l0 + nl > layers or t0 + nt > tokens:
+            return False
+        for l in range(l0, l0 + nl):
+            for t in range(t0, t0 + nt):
+                cover[l][t] += 1
+    return all(c == 1 for row in cover for c in row)
+
+
+def effective_bits(segments, layers: int, tokens: int, D: int) -> float:
+    """Bits per cached value of a cache tiled by segments (k_codec, v_codec,
+    layer0, n_layers, token0, n_tokens): each segment's K/V mean bits per value
+    weighted by the layers x tokens it holds.
+
+    [FMAG-6, Milestone / Minimal recipe / Best results]: anchored rows count at
+    their own precision in the "effective bits"; decode anchors kept for the
+    prompt (L tokens) and the first D decoded tokens cost L + D rows on each
+    anchored layer, so the figure tends to the anchor precision as the prompt
+    grows, while a single fp16 anchor layer adds (16 - b) / n_layers.
+    """
+    assert tiles([(l0, nl, t0, nt) for (_, _, l0, nl, t0, nt) in segments], layers, tokens)
+    tot = 0.0
+    for (kc, vc, l0, nl, t0, nt) in segments:
+        tot += (bits_per_value(kc, D) + bits_per_value(vc, D)) / 2.0 * nl * nt
+    return tot / (layers * tokens)

@@ -129,3 +129,18 @@ def attn_error(q16, K16, V16, Kd, Vd, kv_len=None, sm_scale=0.0, units=None):
         kv[b, l, h, 0:2] = kv_err_unit(K16[b, l, h], Kd[b, l, h])
         kv[b, l, h, 2:4] = kv_err_unit(V16[b, l, h], Vd[b, l, h])
     return kl, re, kv
+
+
+def assemble_segments(segments, B: int, L: int, H: int, T: int, D: int):
+    """The logical [B][L][H][T][D] cache from dequantised segments (Kd_s, Vd_s,
+    layer0, token0), each [B][L_s][H][T_s][D]: every segment placed at its
+    layers and tokens.  Decoding over segments is, by definition, decoding over
+    this assembled cache."""
+    Kd = np.full((B, L, H, T, D), np.nan, dtype=np.float32)
+    Vd = np.full((B, L, H, T, D), np.nan, dtype=np.float32)
+    for (ks, vs, l0, t0) in segments:
+        nl, nt = ks.shape[1], ks.shape[3]
+        Kd[:, l0:l0 + nl, :, t0:t0 + nt] = ks
+        Vd[:, l0:l0 + nl, :, t0:t0 + nt] = vs
+    assert not np.isnan(Kd).any() and not np.isnan(Vd).any(), "segments do not cover the cache"
+    return Kd, Vd
