@@ -296,6 +296,84 @@ def secondary(workload, reps):
         torch.cuda.empty_cache()
 
 
+def anchors_workload(reps):
+    """c3a: the 64K cache in a decoding loop ([FMAG-6] The winning recipe, Selective-Layer
+    Decode Anchoring).  Tokens [0, 65472) of every layer in the 4-bit-key / 2-bit-value
+    codec; the next 48 (the first decoded tokens) at fp16 on layers 0-3 and in the
+    same 4/2 codec on layers 4-7; the last 16 in 4/2 everywhere.  Times the append of
+    one decoded token (K and V of every layer and head into the packed cache) and one
+    decode step over the four segments, against the decode of the same cache held as
+    one packed tensor; reports the effective bits."""
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.get("c3")
+    log(f"generating {w.description}")
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    B, L, H, T, D, Hq = w.B, w.L, w.H, w.T, w.D, w.Hq
+    P, A = 65472, 48
+    kc, vc, f16 = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), K.Codec(K.FP16)
+    qd = torch.from_numpy(np.ascontiguousarray(q[:, :, :1]).view(np.int16)).to(dev)
+
+    def part(x, l0, nl, t0, nt, codec):
+        sub = torch.from_numpy(np.ascontiguousarray(x[:, l0:l0 + nl, :, t0:t0 + nt]).view(np.int16)).to(dev)
+        shape = K.Shape(B, nl, H, nt, D)
+        if codec.codebook == K.FP16:
+            return K.packed_from_fp16(sub, shape)
+        p = K.alloc_packed(codec, shape, dev)
+        K.kvq_quantize_pack(sub, p)
+        return p
+
+    layout = [(0, L, 0, P, kc, vc), (0, 4, P, A, f16, f16), (0, 4, P + A, T - P - A, kc, vc),
+              (4, L - 4, P, T - P, kc, vc)]
+    segs = [K.Segment(part(Kx, l0, nl, t0, nt, ck), part(Vx, l0, nl, t0, nt, cv), l0, t0)
+            for (l0, nl, t0, nt, ck, cv) in layout]
+    shape = K.Shape(B, L, H, T, D)
+    kfull, vfull = K.alloc_packed(kc, shape, dev), K.alloc_packed(vc, shape, dev)
+    K.kvq_quantize_pack(torch.from_numpy(Kx.view(np.int16)).to(dev), kfull)
+    K.kvq_quantize_pack(torch.from_numpy(Vx.view(np.int16)).to(dev), vfull)
+    newk = torch.from_numpy(np.ascontiguousarray(Kx[:, :, :, T - 1:T]).view(np.int16)).to(dev)
+    newv = torch.from_numpy(np.ascontiguousarray(Vx[:, :, :, T - 1:T]).view(np.int16)).to(dev)
+    del Kx, Vx
+    out = torch.empty((B, L, 1, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, L, 1, Hq), dtype=torch.float32, device=dev)
+    wsb = K.kvq_decode_attn_segments_workspace(segs, L, Hq, 1)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    wsb1 = K.kvq_decode_attn_workspace(shape, Hq, 1)
+    ws1 = torch.zeros(wsb1, dtype=torch.uint8, device=dev)
+
+    def seg_step():
+        K.kvq_decode_attn_segments(segs, L, T, Hq, 1, qd, None, 0.0, out, lse, ws, wsb)
+
+    def one_step():
+        K.kvq_decode_attn(kfull, vfull, Hq, 1, qd, None, 0.0, out, lse, ws1, wsb1)
+
+    def append():
+        K.kvq_quantize_pack_tokens(newk, T - 1, 1, kfull)
+        K.kvq_quantize_pack_tokens(newv, T - 1, 1, vfull)
+
+    for f in (seg_step, one_step, append):
+        f()
+    torch.cuda.synchronize()
+    t_seg = _median_time(torch, seg_step, reps)
+    t_one = _median_time(torch, one_step, reps)
+    t_app = _median_time(torch, append, reps)
+    eff = K.kvq_effective_bits(segs, L, T)
+    d_bytes = sum(s.k.codes.numel() * 4 + (s.k.scales.numel() * 2 if s.k.scales is not None else 0) +
+                  s.v.codes.numel() * 4 + (s.v.scales.numel() * 2 if s.v.scales is not None else 0) for s in segs)
+    rec = {"workload": f"c3a: B={B} L={L} H={H} T={T} D={D} Hq={Hq}, prompt {P} + {A} decode anchors fp16 on "
+                       f"layers 0-3 + {T - P - A} tokens, K int4 FWHT-256 g128 / V int2 g128 elsewhere",
+           "segments": len(segs), "effective_bits": round(eff, 4),
+           "decode_step_segments": {"us": round(t_seg * 1e6, 1), "tok/s": round(B / t_seg, 1),
+                                    "GB/s": round(d_bytes / t_seg / 1e9, 1),
+                                    "frac_hbm": round(d_bytes / t_seg / 1e9 / HBM_PEAK_GBS, 4), "bytes": d_bytes},
+           "decode_step_one_tensor": {"us": round(t_one * 1e6, 1)},
+           "append_one_token_kv": {"us": round(t_app * 1e6, 1), "rows": 2 * B * L * H}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,10 +386,11 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for hardware-counter passes: a known-size copy (the counters' "
                          "calibration), one quantize+pack pair and --decode-queries decode calls")
-    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v", "c3m"],
+    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v", "c3m", "c3a"],
                     help="c3: the headline line (default); c4/c5: one line per codec arm of those configs; "
                          "c3v: the 64K cache with each value codebook, with attention KL; "
-                         "c3m: the 64K cache with a shared key mean, keys coded with and without it")
+                         "c3m: the 64K cache with a shared key mean, keys coded with and without it; "
+                         "c3a: the 64K cache as decode segments with fp16 anchors, and the append path")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions per arm (c4/c5)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -319,6 +398,9 @@ def main():
               "(see DESIGN.md for how the path would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "c3a":
+        anchors_workload(args.reps)
+        return
     if args.workload != "c3":
         secondary(args.workload, args.reps)
         return

@@ -27,7 +27,8 @@ EXPORTS = [
     "kvq_constant_table", "kvq_calibrate_chan_scale", "kvq_key_mean_workspace", "kvq_key_mean",
     "kvq_quantize_pack", "kvq_dequant",
     "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_ex",
-    "kvq_attn_error_workspace", "kvq_attn_error",
+    "kvq_attn_error_workspace", "kvq_attn_error", "kvq_quantize_pack_tokens",
+    "kvq_decode_attn_segments_workspace", "kvq_decode_attn_segments", "kvq_effective_bits",
 ]
 
 
@@ -53,6 +54,11 @@ class kvq_packed(ctypes.Structure):
                 ("mean", ctypes.c_void_p)]
 
 
+class kvq_segment(ctypes.Structure):
+    _fields_ = [("k", ctypes.POINTER(kvq_packed)), ("v", ctypes.POINTER(kvq_packed)),
+                ("layer0", ctypes.c_int32), ("token0", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_bit_fwht_amd.build` "
@@ -75,6 +81,10 @@ def _load():
         "kvq_decode_attn_ex": ([P, P, I32, I32, P, P, F, P, P, P, SZ, I32, P], I32),
         "kvq_attn_error_workspace": ([P, I32, I32], SZ),
         "kvq_attn_error": ([P, P, P, P, I32, I32, P, P, F, P, P, P, P, SZ, P], I32),
+        "kvq_quantize_pack_tokens": ([P, I32, I32, P, P], I32),
+        "kvq_decode_attn_segments_workspace": ([P, I32, I32, I32, I32], SZ),
+        "kvq_decode_attn_segments": ([P, I32, I32, I32, I32, I32, P, P, F, P, P, P, SZ, P], I32),
+        "kvq_effective_bits": ([P, I32, I32, I32], D),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -207,6 +217,51 @@ def kvq_key_mean(k_fp16, shape: Shape, mean, ws, ws_bytes: int, stream=None):
 def kvq_quantize_pack(x_fp16, out: Packed, stream=None):
     pc = out.c()
     _check("kvq_quantize_pack", _lib.kvq_quantize_pack(_ptr(x_fp16), ctypes.byref(pc), _stream(stream)))
+
+
+def kvq_quantize_pack_tokens(x_fp16, token0: int, n_tokens: int, out: Packed, stream=None):
+    """Append path: code x_fp16 [B][L][H][n_tokens][D] into tokens [token0, token0 + n_tokens) of `out`."""
+    pc = out.c()
+    _check("kvq_quantize_pack_tokens",
+           _lib.kvq_quantize_pack_tokens(_ptr(x_fp16), token0, n_tokens, ctypes.byref(pc), _stream(stream)))
+
+
+@dataclasses.dataclass
+class Segment:
+    """Packed K and V holding layers [layer0, layer0 + k.shape.layers) and tokens
+    [token0, token0 + k.shape.tokens) of a logical cache."""
+    k: Packed
+    v: Packed
+    layer0: int = 0
+    token0: int = 0
+
+
+def _segments_c(segs):
+    arr = (kvq_segment * len(segs))()
+    keep = []
+    for i, sg in enumerate(segs):
+        kc, vc = sg.k.c(), sg.v.c()
+        keep += [kc, vc]
+        arr[i] = kvq_segment(ctypes.pointer(kc), ctypes.pointer(vc), sg.layer0, sg.token0)
+    return arr, keep
+
+
+def kvq_decode_attn_segments_workspace(segs, layers: int, q_heads: int, n_q: int) -> int:
+    arr, _keep = _segments_c(segs)
+    return _lib.kvq_decode_attn_segments_workspace(arr, len(segs), layers, q_heads, n_q)
+
+
+def kvq_decode_attn_segments(segs, layers: int, tokens: int, q_heads: int, n_q: int, q, kv_len, sm_scale: float,
+                             out, lse, ws, ws_bytes: int, stream=None):
+    arr, _keep = _segments_c(segs)
+    _check("kvq_decode_attn_segments",
+           _lib.kvq_decode_attn_segments(arr, len(segs), layers, tokens, q_heads, n_q, _ptr(q), _ptr(kv_len),
+                                         sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def kvq_effective_bits(segs, layers: int, tokens: int) -> float:
+    arr, _keep = _segments_c(segs)
+    return _lib.kvq_effective_bits(arr, len(segs), layers, tokens)
 
 
 def kvq_dequant(inp: Packed, x_hat, stream=None):

@@ -4,7 +4,10 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "kvq_internal.hpp"
 
@@ -320,6 +323,18 @@ kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void
   return hip_status(launch_quantize(x_fp16, *out, (hipStream_t)stream));
 }
 
+kvq_status kvq_quantize_pack_tokens(const uint16_t* x_fp16, int32_t token0, int32_t n_tokens, const kvq_packed* out,
+                                    void* stream) {
+  kvq_status st = check_packed(out, true);
+  if (st != KVQ_OK) return st;
+  if (!x_fp16) return KVQ_ERR_ARG;
+  if (!aligned16(x_fp16)) return KVQ_ERR_ALIGN;
+  if (token0 < 0 || n_tokens < 1 || (long long)token0 + n_tokens > out->shape.tokens) return KVQ_ERR_ARG;
+  if (is_rfft(out->codec.codebook))
+    return hip_status(launch_rfft_quantize_tokens(x_fp16, *out, token0, n_tokens, (hipStream_t)stream));
+  return hip_status(launch_quantize_tokens(x_fp16, *out, token0, n_tokens, (hipStream_t)stream));
+}
+
 kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream) {
   kvq_status st = check_packed(in, false);
   if (st != KVQ_OK) return st;
@@ -329,8 +344,7 @@ kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream) {
   return hip_status(launch_dequant(*in, x_hat, (hipStream_t)stream));
 }
 
-static kvq_status check_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
-                             const uint16_t* q) {
+static kvq_status check_kv(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q) {
   kvq_status st = check_packed(k, false);
   if (st != KVQ_OK) return st;
   st = check_packed(v, false);
@@ -339,9 +353,126 @@ static kvq_status check_attn(const kvq_packed* k, const kvq_packed* v, int32_t q
   if (is_rfft(v->codec.codebook) || v->mean) return KVQ_ERR_UNSUPPORTED;
   if (q_heads < 1 || q_heads % k->shape.heads != 0 || q_heads / k->shape.heads > 8) return KVQ_ERR_UNSUPPORTED;
   if (n_q < 1) return KVQ_ERR_ARG;
+  return KVQ_OK;
+}
+
+static kvq_status check_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
+                             const uint16_t* q) {
+  kvq_status st = check_kv(k, v, q_heads, n_q);
+  if (st != KVQ_OK) return st;
   if (!q) return KVQ_ERR_ARG;
   if (!aligned16(q)) return KVQ_ERR_ALIGN;
   return KVQ_OK;
+}
+
+// Segments of a logical layers x tokens cache: each valid on its own, all with the same
+// batch, heads and head_dim, inside the cache, and tiling every layer's tokens exactly.
+static kvq_status check_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t tokens,
+                                 int32_t q_heads, int32_t n_q) {
+  if (!segs || n_seg < 1 || n_seg > 16 || layers < 1 || tokens < 1) return KVQ_ERR_ARG;
+  const kvq_packed* k0 = segs[0].k;
+  if (!k0) return KVQ_ERR_ARG;
+  for (int i = 0; i < n_seg; ++i) {
+    const kvq_segment& sg = segs[i];
+    if (!sg.k || !sg.v) return KVQ_ERR_ARG;
+    kvq_status st = check_kv(sg.k, sg.v, q_heads, n_q);
+    if (st != KVQ_OK) return st;
+    const kvq_shape& sh = sg.k->shape;
+    if (sh.batch != k0->shape.batch || sh.heads != k0->shape.heads || sh.head_dim != k0->shape.head_dim)
+      return KVQ_ERR_ARG;
+    if (sh.tokens < 1 || sg.layer0 < 0 || sg.token0 < 0 || (long long)sg.layer0 + sh.layers > layers ||
+        (long long)sg.token0 + sh.tokens > tokens)
+      return KVQ_ERR_ARG;
+  }
+  for (int l = 0; l < layers; ++l) {
+    std::vector<std::pair<int, int>> r;
+    for (int i = 0; i < n_seg; ++i)
+      if (l >= segs[i].layer0 && l < segs[i].layer0 + segs[i].k->shape.layers)
+        r.emplace_back(segs[i].token0, segs[i].k->shape.tokens);
+    std::sort(r.begin(), r.end());
+    long long next = 0;
+    for (const auto& [t0, n] : r) {
+      if (t0 != next) return KVQ_ERR_ARG;
+      next = (long long)t0 + n;
+    }
+    if (next != tokens) return KVQ_ERR_ARG;
+  }
+  return KVQ_OK;
+}
+
+// How kvq_decode_attn_segments runs (byte offsets into its workspace).  With batch 1,
+// a segment none of whose layers an earlier segment covered decodes straight into the
+// output (its query and length rows are contiguous there); every other segment decodes
+// into partials of its own, merged into the output by one kernel at the end.  Rows that
+// no direct segment writes start at (0, -inf).
+struct SegPlan {
+  size_t dec, dec_bytes, q, kvl, lacc, total;
+  size_t out_off[kMaxSegments], lse_off[kMaxSegments];
+  bool direct[kMaxSegments];
+  bool need_init;
+};
+
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static SegPlan seg_plan(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t q_heads, int32_t n_q) {
+  SegPlan p{};
+  const kvq_shape& s0 = segs[0].k->shape;
+  std::vector<char> touched(layers, 0), direct_layer(layers, 0);
+  size_t dec = 0, q = 0, kvl = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    const kvq_shape& sh = segs[i].k->shape;
+    const int l0 = segs[i].layer0, l1 = l0 + sh.layers;
+    const bool inside = l0 >= 0 && l1 <= layers;
+    bool fresh = inside && s0.batch == 1;
+    for (int l = l0; fresh && l < l1; ++l) fresh = !touched[l];
+    p.direct[i] = fresh;
+    for (int l = std::max(l0, 0); l < std::min(l1, (int)layers); ++l) {
+      touched[l] = 1;
+      if (fresh) direct_layer[l] = 1;
+    }
+    const size_t rows = (size_t)sh.batch * sh.layers * n_q;
+    dec = std::max(dec, decode_ws_bytes(sh, q_heads, n_q));
+    q = std::max(q, rows * q_heads * sh.head_dim * 2);
+    kvl = std::max(kvl, rows * 4);
+  }
+  for (int l = 0; l < layers; ++l) p.need_init |= !direct_layer[l];
+  p.dec_bytes = dec;
+  p.dec = kWsCounterBytes;
+  p.q = p.dec + round256(dec);
+  p.kvl = p.q + round256(q);
+  size_t off = p.kvl + round256(kvl);
+  for (int i = 0; i < n_seg; ++i) {
+    if (p.direct[i]) continue;
+    const kvq_shape& sh = segs[i].k->shape;
+    const size_t rows = (size_t)sh.batch * sh.layers * n_q * q_heads;
+    p.out_off[i] = off;
+    off += round256(rows * sh.head_dim * 4);
+    p.lse_off[i] = off;
+    off += round256(rows * 4);
+  }
+  p.lacc = off;
+  p.total = p.lacc + round256((size_t)s0.batch * layers * n_q * q_heads * 4);
+  return p;
+}
+
+// One decode of a packed K/V pair: counters at ctr (kWsCounterBytes, zero and left zero),
+// split-K partials at part.
+static hipError_t decode_packed(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
+                                const uint16_t* q, const int32_t* kv_len, float sm_scale, float* out, float* lse,
+                                void* ctr, void* part, size_t part_bytes, int32_t path, hipStream_t st) {
+  const bool fast_ok = fast_decode_supported(*k, *v, q_heads);
+  AttnProblem pr{};
+  pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
+  pr.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)k->shape.head_dim));
+  pr.out = out; pr.lse = lse;
+  pr.ctr = static_cast<int*>(ctr);
+  pr.ws = part;
+  pr.ws_bytes = part_bytes;
+  const bool use_fast = (path == 2) || (path == 0 && fast_ok);
+  hipError_t e = use_fast ? launch_decode_fast(pr, st) : launch_decode_generic(pr, st);
+  // a key mean adds q.mean to every logit of a query: weights unchanged, lse shifted
+  if (e == hipSuccess && k->mean && lse) e = launch_lse_mean(pr, st);
+  return e;
 }
 
 size_t kvq_decode_attn_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q) {
@@ -361,29 +492,108 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
   const size_t need = kWsCounterBytes + decode_ws_bytes(k->shape, q_heads, n_q);
   if (ws_bytes < need || (need && !ws)) return KVQ_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return KVQ_ERR_ALIGN;
-  const bool fast_ok = fast_decode_supported(*k, *v, q_heads);
-  if (path == 2 && !fast_ok) return KVQ_ERR_UNSUPPORTED;
-  AttnProblem pr{};
-  pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
-  pr.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)k->shape.head_dim));
-  pr.out = out; pr.lse = lse;
-  pr.ctr = static_cast<int*>(ws);
-  pr.ws = static_cast<char*>(ws) + kWsCounterBytes;
-  pr.ws_bytes = ws_bytes - kWsCounterBytes;
-  if (k->shape.tokens == 0) {
-    // no keys: zero output, lse = -inf (handled by the generic kernel's combine)
-  }
-  const bool use_fast = (path == 2) || (path == 0 && fast_ok);
-  hipError_t e = use_fast ? launch_decode_fast(pr, (hipStream_t)stream) : launch_decode_generic(pr, (hipStream_t)stream);
-  // a key mean adds q.mean to every logit of a query: weights unchanged, lse shifted
-  if (e == hipSuccess && k->mean && lse) e = launch_lse_mean(pr, (hipStream_t)stream);
-  return hip_status(e);
+  if (path == 2 && !fast_decode_supported(*k, *v, q_heads)) return KVQ_ERR_UNSUPPORTED;
+  // no keys (tokens = 0): zero output, lse = -inf (the generic kernel's combine)
+  return hip_status(decode_packed(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws,
+                                  static_cast<char*>(ws) + kWsCounterBytes, ws_bytes - kWsCounterBytes, path,
+                                  (hipStream_t)stream));
 }
 
 kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
                            const uint16_t* q, const int32_t* kv_len, float sm_scale, float* out, float* lse,
                            void* ws, size_t ws_bytes, void* stream) {
   return kvq_decode_attn_ex(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes, 0, stream);
+}
+
+size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg, int32_t layers,
+                                          int32_t q_heads, int32_t n_q) {
+  if (!segs || n_seg < 1 || n_seg > 16 || layers < 1) return 0;
+  for (int i = 0; i < n_seg; ++i) {
+    if (!segs[i].k || !segs[i].v) return 0;
+    if (check_kv(segs[i].k, segs[i].v, q_heads, n_q) != KVQ_OK) return 0;
+  }
+  return seg_plan(segs, n_seg, layers, q_heads, n_q).total;
+}
+
+kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t tokens,
+                                    int32_t q_heads, int32_t n_q, const uint16_t* q, const int32_t* kv_len,
+                                    float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  kvq_status st = check_segments(segs, n_seg, layers, tokens, q_heads, n_q);
+  if (st != KVQ_OK) return st;
+  if (!q || !out) return KVQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(out) || (lse && !aligned16(lse)) || (kv_len && !aligned16(kv_len)))
+    return KVQ_ERR_ALIGN;
+  if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
+  const SegPlan pl = seg_plan(segs, n_seg, layers, q_heads, n_q);
+  if (ws_bytes < pl.total || !ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVQ_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  const int B = segs[0].k->shape.batch, D = segs[0].k->shape.head_dim;
+  const size_t rpl = (size_t)n_q * q_heads;                     // output rows per (sequence, layer)
+  float* lacc = lse ? lse : reinterpret_cast<float*>(w + pl.lacc);
+  hipError_t e = hipSuccess;
+  if (pl.need_init) e = launch_seg_init(out, lacc, (long long)B * layers * rpl, D, s);
+  int nm = 0, ml0[kMaxSegments], mls[kMaxSegments];
+  float* mos[kMaxSegments];
+  float* mlse[kMaxSegments];
+  for (int i = 0; i < n_seg && e == hipSuccess; ++i) {
+    const kvq_segment& sg = segs[i];
+    const kvq_shape& sh = sg.k->shape;
+    const uint16_t* qs = q;
+    const int32_t* kvls = kv_len;
+    uint16_t* qbuf = nullptr;
+    int32_t* kbuf = nullptr;
+    if (B == 1) {
+      qs = q + (size_t)sg.layer0 * rpl * D;                     // contiguous layer slice
+      if (kv_len) kvls = kv_len + (size_t)sg.layer0 * n_q;
+      if (kv_len && sg.token0 != 0) kbuf = reinterpret_cast<int32_t*>(w + pl.kvl);
+    } else {
+      qbuf = reinterpret_cast<uint16_t*>(w + pl.q);
+      if (kv_len) kbuf = reinterpret_cast<int32_t*>(w + pl.kvl);
+    }
+    if (qbuf || kbuf)
+      e = launch_seg_prepare(q, kv_len, qbuf, kbuf, B, layers, sh.layers, sg.layer0, n_q, q_heads, D, sg.token0,
+                             sh.tokens, s);
+    if (qbuf) qs = qbuf;
+    if (kbuf) kvls = kbuf;
+    // (keys [0, kv_len) clamp to [0, tokens] inside the decode, so a segment at token 0
+    // needs no adjusted lengths)
+    float* os;
+    float* ls;
+    if (pl.direct[i]) {
+      os = out + (size_t)sg.layer0 * rpl * D;
+      ls = lacc + (size_t)sg.layer0 * rpl;
+    } else {
+      os = reinterpret_cast<float*>(w + pl.out_off[i]);
+      ls = reinterpret_cast<float*>(w + pl.lse_off[i]);
+      ml0[nm] = sg.layer0;
+      mls[nm] = sh.layers;
+      mos[nm] = os;
+      mlse[nm] = ls;
+      ++nm;
+    }
+    if (e == hipSuccess)
+      e = decode_packed(sg.k, sg.v, q_heads, n_q, qs, kvls, sm_scale, os, ls, w, w + pl.dec, pl.dec_bytes, 0, s);
+  }
+  if (e == hipSuccess) e = launch_seg_merge(nm, ml0, mls, mos, mlse, out, lacc, B, layers, (int)rpl, D, s);
+  return hip_status(e);
+}
+
+double kvq_effective_bits(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t tokens) {
+  int32_t q_heads = 0;
+  if (segs && n_seg >= 1 && segs[0].k) q_heads = segs[0].k->shape.heads;
+  if (check_segments(segs, n_seg, layers, tokens, q_heads, 1) != KVQ_OK) return -1.0;
+  double tot = 0.0;
+  for (int i = 0; i < n_seg; ++i) {
+    const kvq_packed& k = *segs[i].k;
+    const kvq_packed& v = *segs[i].v;
+    const double b = 0.5 * (kvq_bits_per_value(&k.codec, k.shape.head_dim) +
+                            kvq_bits_per_value(&v.codec, v.shape.head_dim));
+    tot += b * k.shape.layers * k.shape.tokens;
+  }
+  return tot / ((double)layers * tokens);
 }
 
 size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q) {

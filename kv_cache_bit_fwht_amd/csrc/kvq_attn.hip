@@ -1312,3 +1312,113 @@ hipError_t launch_lse_mean(const AttnProblem& pr, hipStream_t st) {
 }
 
 }  // namespace kvq
+
+namespace kvq {
+
+// ------------------------------------------------------------------ segments of a logical cache
+// A segment holds layers [l0, l0 + Ls) and tokens [t0, t0 + Ts) of a logical cache; it is
+// decoded on its own and its (out, lse) merged into the logical result.
+
+// Query rows of the segment's layers, copied out of q [B][L][n_q][Hq][D] (16-byte units).
+__global__ void k_seg_gather_q(const uint4* __restrict__ src, uint4* __restrict__ dst, long long per_layer, int L,
+                               int Ls, int l0, long long total) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const long long bl = i / per_layer, e = i - bl * per_layer;
+  const long long b = bl / Ls, l = bl - b * Ls;
+  dst[i] = src[(b * L + l0 + l) * per_layer + e];
+}
+
+// Keys attended inside the segment: clamp(kv_len - t0, 0, Ts) for its layers.
+__global__ void k_seg_kvlen(const int32_t* __restrict__ kvl, int32_t* __restrict__ out, int L, int Ls, int l0,
+                            int n_q, int t0, int Ts, long long total) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const long long bl = i / n_q, j = i - bl * n_q;
+  const long long b = bl / Ls, l = bl - b * Ls;
+  const int v = kvl[(b * L + l0 + l) * n_q + j] - t0;
+  out[i] = v < 0 ? 0 : (v > Ts ? Ts : v);
+}
+
+// Logical result before any segment: out = 0, lse = -inf.
+__global__ void k_seg_init(float* __restrict__ out, float* __restrict__ lse, long long rows, int D) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < rows * D) out[i] = 0.0f;
+  if (i < rows) lse[i] = -INFINITY;
+}
+
+// (out, lse) of every logical row <- the log-sum-exp merge with each listed segment
+// covering the row's layer, in list order: weights e^(lse - m), m the larger lse.  One
+// wavefront per logical row.
+struct SegMergeArgs {
+  int n;
+  int l0[kMaxSegments], ls[kMaxSegments];
+  const float* os[kMaxSegments];
+  const float* lsp[kMaxSegments];
+};
+
+__global__ __launch_bounds__(kBlock) void k_seg_merge(SegMergeArgs sa, float* __restrict__ out, float* __restrict__ lse,
+                                                      int L, int rpl, int D, long long rows) {
+  const long long g = (long long)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= rows) return;                                   // uniform per wavefront
+  const long long bl = g / rpl, k = g - bl * rpl;
+  const long long b = bl / L;
+  const int l = (int)(bl - b * L);
+  float la = lse[g];
+  for (int i = 0; i < sa.n; ++i) {
+    if (l < sa.l0[i] || l >= sa.l0[i] + sa.ls[i]) continue;
+    const long long r = (b * sa.ls[i] + (l - sa.l0[i])) * rpl + k;    // the segment's row
+    const float lb = sa.lsp[i][r];
+    const float m = __builtin_fmaxf(la, lb);
+    if (m == -INFINITY) continue;                          // no keys on either side
+    const float wa = la == -INFINITY ? 0.0f : expf(la - m);
+    const float wb = lb == -INFINITY ? 0.0f : expf(lb - m);
+    const float inv = 1.0f / (wa + wb);
+    const float* os = sa.os[i] + r * D;
+    for (int d = lane; d < D; d += 64) out[g * D + d] = (wa * out[g * D + d] + wb * os[d]) * inv;
+    la = m + logf(wa + wb);
+  }
+  if (lane == 0) lse[g] = la;
+}
+
+hipError_t launch_seg_init(float* out, float* lse, long long rows, int D, hipStream_t st) {
+  const long long n = rows * D;
+  if (n == 0) return hipSuccess;
+  k_seg_init<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, st>>>(out, lse, rows, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_prepare(const uint16_t* q, const int32_t* kvl, uint16_t* qs, int32_t* kvls, int B, int L,
+                              int Ls, int l0, int n_q, int Hq, int D, int t0, int Ts, hipStream_t st) {
+  if (qs) {
+    const long long per_layer = (long long)n_q * Hq * D / 8;
+    const long long tq = (long long)B * Ls * per_layer;
+    k_seg_gather_q<<<(unsigned)((tq + kBlock - 1) / kBlock), kBlock, 0, st>>>(
+        reinterpret_cast<const uint4*>(q), reinterpret_cast<uint4*>(qs), per_layer, L, Ls, l0, tq);
+  }
+  if (kvls) {
+    const long long tk = (long long)B * Ls * n_q;
+    k_seg_kvlen<<<(unsigned)((tk + kBlock - 1) / kBlock), kBlock, 0, st>>>(kvl, kvls, L, Ls, l0, n_q, t0, Ts, tk);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_merge(int n, const int* l0, const int* ls, float* const* os, float* const* lsp, float* out,
+                            float* lse, int B, int L, int rpl, int D, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  SegMergeArgs sa{};
+  sa.n = n;
+  for (int i = 0; i < n; ++i) {
+    sa.l0[i] = l0[i];
+    sa.ls[i] = ls[i];
+    sa.os[i] = os[i];
+    sa.lsp[i] = lsp[i];
+  }
+  const long long rows = (long long)B * L * rpl;
+  if (rows == 0) return hipSuccess;
+  k_seg_merge<<<(unsigned)((rows + kBlock / 64 - 1) / (kBlock / 64)), kBlock, 0, st>>>(sa, out, lse, L, rpl, D, rows);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -17,6 +17,7 @@
 namespace kvq {
 
 constexpr int kBlock = 256;      // threads per block for every kernel
+constexpr int kMaxSegments = 16; // segments of one logical cache (kvq_decode_attn_segments)
 constexpr int kVals = 16;        // values per lane in layout 1
 
 // Constant tables passed by value in kernel arguments (no device globals).
@@ -149,6 +150,8 @@ struct RowGeom {        // a [B][L][H][T][D] tensor seen as rows
 };
 
 hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st);
+hipError_t launch_quantize_tokens(const uint16_t* x, const kvq_packed& p, int t0, int n, hipStream_t st);
+hipError_t launch_rfft_quantize_tokens(const uint16_t* x, const kvq_packed& p, int t0, int n, hipStream_t st);
 hipError_t launch_dequant(const kvq_packed& p, float* xhat, hipStream_t st);
 hipError_t launch_calibrate(const uint16_t* k, const kvq_shape& s, float* c, hipStream_t st);
 hipError_t launch_key_mean(const uint16_t* k, const kvq_shape& s, float* mean, long long* ws, hipStream_t st);
@@ -190,6 +193,11 @@ int decode_splits(const kvq_shape& s, int Hq, int n_q);
 hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st);
 hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st);
 hipError_t launch_lse_mean(const AttnProblem& pr, hipStream_t st);
+hipError_t launch_seg_init(float* out, float* lse, long long rows, int D, hipStream_t st);
+hipError_t launch_seg_prepare(const uint16_t* q, const int32_t* kvl, uint16_t* qs, int32_t* kvls, int B, int L,
+                              int Ls, int l0, int n_q, int Hq, int D, int t0, int Ts, hipStream_t st);
+hipError_t launch_seg_merge(int n, const int* l0, const int* ls, float* const* os, float* const* lsp, float* out,
+                            float* lse, int B, int L, int rpl, int D, hipStream_t st);
 bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st);
 size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q);

@@ -24,8 +24,9 @@ struct QArgs {
   uint16_t* mins;
   const float* chan;      // [L][H][D] or null
   const float* mean;      // [L][H][D] or null
-  long long rows;
-  int D, T, H, L;
+  long long rows;          // input rows: B * L * H * T
+  int D, T, H, L;          // T: tokens per unit in the input
+  int Tout, t0;            // output tensor's tokens per unit; the input's first token there
   int lpt_log2;           // log2(D/16)
   int g;                  // group
   int W;                  // rotation width, 0 = none
@@ -33,6 +34,13 @@ struct QArgs {
   int ng;                 // scales per row
   Tables tab;
 };
+
+// Output row of input row `row`: the same (sequence, layer, head) unit, token t0 + t.
+__device__ __forceinline__ long long out_row(const QArgs& a, long long row) {
+  if (a.T == a.Tout) return row;
+  const long long u = row / a.T;
+  return u * a.Tout + a.t0 + (row - u * a.T);
+}
 
 __device__ __forceinline__ void row_unit(long long row, int T, int H, int L, int& l, int& h) {
   const long long unit = row / T;
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
       for (int k = 0; k < 8; ++k) raw[k] = 0u;
     }
     if constexpr (CB == KVQ_FP16) {
-      if (active) store_chunk<16>(cbytes, (size_t)row * row_bytes + (size_t)j * 32, raw);
+      if (active) store_chunk<16>(cbytes, (size_t)out_row(a, row) * row_bytes + (size_t)j * 32, raw);
       continue;
     }
 #pragma unroll
@@ -113,8 +121,9 @@ __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
     if (!active) continue;
     uint32_t w[8];
     pack16<BITS>(c, w);
-    store_chunk<BITS>(cbytes, (size_t)row * row_bytes + (size_t)j * 2 * BITS, w);
-    const size_t sbase = (size_t)row * a.ng;
+    const long long orow = out_row(a, row);
+    store_chunk<BITS>(cbytes, (size_t)orow * row_bytes + (size_t)j * 2 * BITS, w);
+    const size_t sbase = (size_t)orow * a.ng;
     if (a.g == 8) {
       const uint32_t pk = (uint32_t)s16[0] | ((uint32_t)s16[1] << 16);
       *reinterpret_cast<uint32_t*>(a.scales + sbase + 2 * j) = pk;
@@ -264,6 +273,8 @@ static QArgs make_args(const kvq_packed& p) {
   a.mean = p.mean;
   a.D = p.shape.head_dim;
   a.T = p.shape.tokens;
+  a.Tout = p.shape.tokens;
+  a.t0 = 0;
   a.H = p.shape.heads;
   a.L = p.shape.layers;
   a.rows = (long long)p.shape.batch * p.shape.layers * p.shape.heads * p.shape.tokens;
@@ -456,7 +467,8 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
       c[i] = (uint32_t)min(max(b, (int)kMagic), (int)(kMagic + (1u << BITS) - 1u));
     }
     if (!active) continue;
-    uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + (size_t)row * (D * BITS / 8) + (size_t)j * 2 * BITS;
+    const long long orow = out_row(a, row);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + (size_t)orow * (D * BITS / 8) + (size_t)j * 2 * BITS;
     if constexpr (BITS == 4) {
       uint32_t w[2];
 #pragma unroll
@@ -488,7 +500,7 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
       }
       *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    if ((j & (lpg - 1)) == 0) a.scales[(size_t)row * (D / a.g) + j / lpg] = s16;
+    if ((j & (lpg - 1)) == 0) a.scales[(size_t)orow * (D / a.g) + j / lpg] = s16;
   }
 }
 
@@ -541,6 +553,22 @@ static void launch_absmax256(const QArgs& a, const kvq_codec& c, hipStream_t st)
 hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st) {
   QArgs a = make_args(p);
   a.x = x;
+  if (a.rows == 0) return hipSuccess;
+  if (absmax256_supported(p)) {
+    launch_absmax256(a, p.codec, st);
+    return hipGetLastError();
+  }
+  const dim3 grid(grid_for(a.rows, a.lpt_log2)), block(kBlock);
+  KVQ_DISPATCH_CODEC(p.codec.codebook, p.codec.bits, k_quantize, <<<grid, block, 0, st>>>(a))
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_tokens(const uint16_t* x, const kvq_packed& p, int t0, int n, hipStream_t st) {
+  QArgs a = make_args(p);
+  a.x = x;
+  a.T = n;
+  a.t0 = t0;
+  a.rows = (long long)p.shape.batch * p.shape.layers * p.shape.heads * n;
   if (a.rows == 0) return hipSuccess;
   if (absmax256_supported(p)) {
     launch_absmax256(a, p.codec, st);

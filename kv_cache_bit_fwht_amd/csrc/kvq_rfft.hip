@@ -14,8 +14,9 @@ struct RArgs {
   uint16_t* scales;
   const float* chan;
   const float* mean;
-  long long rows;
-  int T, H, L;
+  long long rows;          // input rows: B * L * H * T
+  int T, H, L;             // T: tokens per unit in the input
+  int Tout, t0;            // output tensor's tokens per unit; the input's first token there
   RfftCodec c;
   FftTables tw;
   PhaseTables pt;
@@ -527,13 +528,22 @@ __global__ __launch_bounds__(kBlock) void k_rfft_quantize(RArgs a) {
       }
     }
     wave_lds_sync();
-    // 9. the wavefront's rows are contiguous in the outputs
+    // 9. the wavefront's rows are contiguous in the outputs (a token window: row by row)
     {
       const int nv = (int)min((long long)G::RPW, a.rows - base);
-      uint32_t* cw = a.codes + (size_t)base * words;
-      for (int i = lane; i < nv * words; i += 64) cw[i] = wbuf[i];
-      uint16_t* sw = a.scales + (size_t)base * ns;
-      for (int i = lane; i < nv * ns; i += 64) sw[i] = scb[i];
+      if (a.T == a.Tout) {
+        uint32_t* cw = a.codes + (size_t)base * words;
+        for (int i = lane; i < nv * words; i += 64) cw[i] = wbuf[i];
+        uint16_t* sw = a.scales + (size_t)base * ns;
+        for (int i = lane; i < nv * ns; i += 64) sw[i] = scb[i];
+      } else {
+        for (int r = 0; r < nv; ++r) {
+          const long long u = (base + r) / a.T;
+          const long long orow = u * a.Tout + a.t0 + (base + r - u * a.T);
+          for (int i = lane; i < words; i += 64) a.codes[(size_t)orow * words + i] = wbuf[r * words + i];
+          for (int i = lane; i < ns; i += 64) a.scales[(size_t)orow * ns + i] = scb[r * ns + i];
+        }
+      }
     }
     wave_lds_sync();
   }
@@ -654,6 +664,8 @@ static RArgs make_rargs(const kvq_packed& p) {
   a.mean = p.mean;
   a.rows = (long long)p.shape.batch * p.shape.layers * p.shape.heads * p.shape.tokens;
   a.T = p.shape.tokens;
+  a.Tout = p.shape.tokens;
+  a.t0 = 0;
   a.H = p.shape.heads;
   a.L = p.shape.layers;
   RfftCodec& c = a.c;
@@ -678,10 +690,7 @@ static unsigned rgrid(long long rows) {
   return (unsigned)(b < 1 ? 1 : b);
 }
 
-hipError_t launch_rfft_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st) {
-  RArgs a = make_rargs(p);
-  a.x = x;
-  if (a.rows == 0) return hipSuccess;
+static hipError_t launch_rfft_quantize_args(const RArgs& a, hipStream_t st) {
   const int N = a.c.N, rpw = 64 / (N / 16);
   long long blocks = (a.rows + (long long)kWaves * rpw - 1) / ((long long)kWaves * rpw);
   const unsigned grid = (unsigned)(blocks > 4096 ? 4096 : blocks);
@@ -699,6 +708,23 @@ hipError_t launch_rfft_quantize(const uint16_t* x, const kvq_packed& p, hipStrea
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_rfft_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st) {
+  RArgs a = make_rargs(p);
+  a.x = x;
+  if (a.rows == 0) return hipSuccess;
+  return launch_rfft_quantize_args(a, st);
+}
+
+hipError_t launch_rfft_quantize_tokens(const uint16_t* x, const kvq_packed& p, int t0, int n, hipStream_t st) {
+  RArgs a = make_rargs(p);
+  a.x = x;
+  a.T = n;
+  a.t0 = t0;
+  a.rows = (long long)p.shape.batch * p.shape.layers * p.shape.heads * n;
+  if (a.rows == 0) return hipSuccess;
+  return launch_rfft_quantize_args(a, st);
 }
 
 hipError_t launch_rfft_dequant(const kvq_packed& p, float* xhat, hipStream_t st) {

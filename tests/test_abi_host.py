@@ -287,3 +287,97 @@ def test_mean_field_is_validated(K):
     v = _packed(K, codec=(1, 2, 128, 0, 0))
     v.mean = FAKE                                          # ... a value mean is not
     assert _decode(K, k, v) == ERR_UNSUPPORTED
+
+
+def _seg_pair(K, codec_k, codec_v, shape):
+    k = K.kvq_packed(K.kvq_codec(*codec_k), K.kvq_shape(*shape), FAKE, FAKE if codec_k[0] else None, None, None)
+    v = K.kvq_packed(K.kvq_codec(*codec_v), K.kvq_shape(*shape), FAKE, FAKE if codec_v[0] else None, None, None)
+    return k, v
+
+
+def _segs(K, parts):
+    keep, arr = [], (K.kvq_segment * len(parts))()
+    for i, (ck, cv, shape, l0, t0) in enumerate(parts):
+        k, v = _seg_pair(K, ck, cv, shape)
+        keep += [k, v]
+        arr[i] = K.kvq_segment(ctypes.pointer(k), ctypes.pointer(v), l0, t0)
+    return arr, keep
+
+
+F16 = (0, 0, 0, 0, 0)
+NF4 = (5, 4, 64, 0, 0)
+I4 = (1, 4, 64, 0, 0)
+
+
+def test_effective_bits_match_the_oracle(K):
+    """Layer-0 fp16 anchors with NF4/int4 elsewhere, and prompt + decode anchors on two
+    of four layers, against the oracle's accounting."""
+    L = K._lib
+    arr, keep = _segs(K, [(F16, F16, (1, 1, 4, 100, 128), 0, 0), (NF4, I4, (1, 25, 4, 100, 128), 1, 0)])
+    e = L.kvq_effective_bits(arr, 2, 26, 100)
+    ref = O.effective_bits([(O.Codec(O.FP16), O.Codec(O.FP16), 0, 1, 0, 100),
+                            (O.Codec(O.NF4, 4, 64), O.Codec(O.INT_ABSMAX, 4, 64), 1, 25, 0, 100)], 26, 100, 128)
+    assert e == pytest.approx(ref, abs=1e-12) and round(e, 2) == 4.70
+    parts = [(F16, F16, (1, 2, 4, 80, 128), 0, 0), (NF4, I4, (1, 2, 4, 176, 128), 0, 80),
+             (NF4, I4, (1, 2, 4, 256, 128), 2, 0)]
+    arr, keep = _segs(K, parts)
+    ref = O.effective_bits([(O.Codec(O.FP16), O.Codec(O.FP16), 0, 2, 0, 80),
+                            (O.Codec(O.NF4, 4, 64), O.Codec(O.INT_ABSMAX, 4, 64), 0, 2, 80, 176),
+                            (O.Codec(O.NF4, 4, 64), O.Codec(O.INT_ABSMAX, 4, 64), 2, 2, 0, 256)], 4, 256, 128)
+    assert L.kvq_effective_bits(arr, 3, 4, 256) == pytest.approx(ref, abs=1e-12)
+
+
+@pytest.mark.parametrize("case", ["gap", "overlap", "uncovered_layer", "past_end", "batch_mismatch", "zero_segments",
+                                  "seventeen"])
+def test_segments_reject_bad_tilings(K, case):
+    L = K._lib
+    sh = (1, 2, 4, 64, 128)
+    parts = [(I4, I4, sh, 0, 0), (I4, I4, (1, 2, 4, 36, 128), 0, 64)]        # 2 layers x 100 tokens
+    n, layers, tokens = 2, 2, 100
+    if case == "gap":
+        parts[1] = (I4, I4, (1, 2, 4, 30, 128), 0, 65)
+        tokens = 95
+    elif case == "overlap":
+        parts[1] = (I4, I4, (1, 2, 4, 37, 128), 0, 63)
+    elif case == "uncovered_layer":
+        layers = 3
+    elif case == "past_end":
+        tokens = 90
+    elif case == "batch_mismatch":
+        parts[1] = (I4, I4, (2, 2, 4, 36, 128), 0, 64)
+    elif case == "zero_segments":
+        n = 0
+    elif case == "seventeen":
+        parts = [(I4, I4, (1, 2, 4, 4, 128), 0, 4 * i) for i in range(17)]
+        n, tokens = 17, 68
+    arr, keep = _segs(K, parts)
+    assert L.kvq_effective_bits(arr, n, layers, tokens) < 0
+    st = L.kvq_decode_attn_segments(arr, n, layers, tokens, 16, 1, FAKE, None, 0.0, FAKE, None, FAKE, 1 << 30, None)
+    assert st == ERR_ARG
+
+
+def test_segments_validate_before_launching(K):
+    L = K._lib
+    arr, keep = _segs(K, [(I4, I4, (1, 2, 4, 64, 128), 0, 0)])
+    need = L.kvq_decode_attn_segments_workspace(arr, 1, 2, 16, 1)
+    assert need > 65536
+    args = dict(q=FAKE, out=FAKE, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.kvq_decode_attn_segments(arr, 1, 2, 64, 16, 1, a["q"], None, 0.0, a["out"], None, a["ws"], a["wsb"],
+                                          None)
+    assert call(wsb=need - 1) == ERR_WORKSPACE
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(q=None) == ERR_ARG
+    assert call(out=FAKE_ODD) == ERR_ALIGN
+
+
+def test_append_validates_before_launching(K):
+    L = K._lib
+    p = _packed(K)                                         # 64 tokens
+    assert L.kvq_quantize_pack_tokens(FAKE, 60, 5, ctypes.byref(p), None) == ERR_ARG
+    assert L.kvq_quantize_pack_tokens(FAKE, -1, 2, ctypes.byref(p), None) == ERR_ARG
+    assert L.kvq_quantize_pack_tokens(FAKE, 0, 0, ctypes.byref(p), None) == ERR_ARG
+    assert L.kvq_quantize_pack_tokens(None, 0, 1, ctypes.byref(p), None) == ERR_ARG
+    assert L.kvq_quantize_pack_tokens(FAKE_ODD, 0, 1, ctypes.byref(p), None) == ERR_ALIGN

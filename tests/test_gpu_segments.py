@@ -1,0 +1,171 @@
+"""GPU parity of the pieces around the path in real decoding ([FMAG-6] The winning
+recipe, Selective-Layer Decode Anchoring):
+
+* the append path (kvq_quantize_pack_tokens) writes exactly the codes of quantising
+  the whole tensor, window by window, and touches no other row;
+* decode over segments (anchors at other precisions on chosen layers and tokens,
+  per-layer codecs, a key mean on one segment) against the oracle's decode of the
+  assembled cache, within the attention bars;
+* an append-then-decode loop gives, step by step, the decode of the fully quantised
+  cache at the same lengths."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_util import announce, oracle_codec, to_dev, to_np
+from tests.test_gpu_attn import _check_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed_arrays(p):
+    out = [to_np(p.codes, np.uint32)]
+    if p.scales is not None and p.scales.numel():
+        out.append(to_np(p.scales, np.uint16))
+    if p.mins is not None:
+        out.append(to_np(p.mins, np.uint16))
+    return out
+
+
+APPEND = [((1, 4, 128, 256), 256, False), ((1, 2, 128, 0), 256, False), ((2, 3, 32, 0), 128, False),
+          ((5, 4, 64, 0), 64, False), ((7, 5, 32, 0, 7), 128, False), ((8, 6, 16, 0), 256, False),
+          ((0,), 128, False), ((1, 4, 128, 256), 256, True), ((10, 3, 32, 128), 128, True)]
+
+
+@pytest.mark.parametrize("cspec,D,with_mean", APPEND)
+def test_append_windows_equal_the_whole_tensor(cspec, D, with_mean):
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", B=2, L=2, H=2, T=90, D=D, k_mean_share=0.5 if with_mean else 0.0)
+    Kx, _ = synth.gen_kv(w)
+    shape = K.Shape(*Kx.shape)
+    codec = K.Codec(*cspec)
+    mean = to_dev(O.key_mean(Kx)) if with_mean else None
+    announce(f"append windows codec={codec} D={D} mean={with_mean}")
+    full = K.alloc_packed(codec, shape, mean=mean)
+    K.kvq_quantize_pack(to_dev(Kx), full)
+    win = K.alloc_packed(codec, shape, mean=mean)
+    for t in (win.codes, win.scales, win.mins):
+        if t is not None and t.numel():
+            t.fill_(0x5a5a)
+    for (t0, n) in ((0, 50), (50, 1), (51, 39)):
+        K.kvq_quantize_pack_tokens(to_dev(np.ascontiguousarray(Kx[:, :, :, t0:t0 + n])), t0, n, win)
+    torch.cuda.synchronize()
+    for a, b in zip(_packed_arrays(full), _packed_arrays(win)):
+        assert np.array_equal(a, b)
+    # a middle window alone: only its rows change
+    mid = K.alloc_packed(codec, shape, mean=mean)
+    for t in (mid.codes, mid.scales, mid.mins):
+        if t is not None and t.numel():
+            t.fill_(0x5a5a)
+    before = _packed_arrays(mid)
+    K.kvq_quantize_pack_tokens(to_dev(np.ascontiguousarray(Kx[:, :, :, 30:37])), 30, 7, mid)
+    torch.cuda.synchronize()
+    rows = np.zeros((2, 2, 2, 90), bool)
+    rows[:, :, :, 30:37] = True
+    rows = rows.ravel()
+    for a, b, f in zip(_packed_arrays(full), _packed_arrays(mid), before):
+        assert np.array_equal(b[rows], a[rows]) and np.array_equal(b[~rows], f[~rows])
+
+
+def _oracle_seg(K, x, codec, mean=None):
+    oc = oracle_codec(K, O, codec)
+    w, s, z = O.quantize_pack(x, oc, None, mean)
+    return O.dequant(w, s, z, oc, x.shape, None, mean)
+
+
+def _gpu_seg(K, x, codec, mean=None):
+    p = K.alloc_packed(codec, K.Shape(*x.shape), mean=to_dev(mean) if mean is not None else None)
+    if codec.codebook == K.FP16:
+        return K.packed_from_fp16(to_dev(x), K.Shape(*x.shape))
+    K.kvq_quantize_pack(to_dev(x), p)
+    return p
+
+
+def _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg=None):
+    """layout: list of (kcodec, vcodec, layer0, n_layers, token0, n_tokens)."""
+    import torch
+    B, L, H, T, D = Kx.shape
+    nq, Hq = q.shape[2], q.shape[3]
+    segs, ref = [], []
+    for i, (kc, vc, l0, nl, t0, nt) in enumerate(layout):
+        ks = np.ascontiguousarray(Kx[:, l0:l0 + nl, :, t0:t0 + nt])
+        vs = np.ascontiguousarray(Vx[:, l0:l0 + nl, :, t0:t0 + nt])
+        mean = O.key_mean(ks) if i == mean_seg else None
+        segs.append(K.Segment(_gpu_seg(K, ks, kc, mean), _gpu_seg(K, vs, vc), l0, t0))
+        ref.append((_oracle_seg(K, ks, kc, mean), _oracle_seg(K, vs, vc), l0, t0))
+    Kd, Vd = O.assemble_segments(ref, B, L, H, T, D)
+    out = torch.empty((B, L, nq, Hq, D), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, L, nq, Hq), dtype=torch.float32, device="cuda:0")
+    wsb = K.kvq_decode_attn_segments_workspace(segs, L, Hq, nq)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda:0")
+    K.kvq_decode_attn_segments(segs, L, T, Hq, nq, to_dev(q), to_dev(kv_len) if kv_len is not None else None, 0.0,
+                               out, lse, ws, wsb)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = O.decode_attn(q, Kd, Vd, kv_len)
+    _check_decode(to_np(out), to_np(lse), ref_out, ref_lse, kv_len)
+    assert np.all(to_np(ws[:65536]) == 0)                 # counters left zero
+    return segs
+
+
+@pytest.mark.parametrize("variant", ["anchors", "per_layer", "causal_mean", "window"])
+def test_decode_over_segments(variant):
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=4, T=704, n_q=3)
+    Kx, Vx = synth.gen_kv(w)
+    q, kv_len = synth.gen_queries(w)
+    k4, v2 = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    f16, i8 = K.Codec(K.FP16), K.Codec(K.INT8_SYM, 8, 256, 0)
+    mean_seg = None
+    if variant == "anchors":
+        # prompt [0, 640) in 4/2 bits; the first 48 decoded tokens at fp16 on layers 0-1
+        # and in 4/2 bits on layers 2-3; the last 16 tokens int8 on every layer
+        layout = [(k4, v2, 0, 4, 0, 640), (f16, f16, 0, 2, 640, 48), (k4, v2, 2, 2, 640, 48), (i8, i8, 0, 4, 688, 16)]
+    elif variant == "per_layer":
+        layout = [(f16, f16, 0, 1, 0, 704), (k4, v2, 1, 3, 0, 704)]
+    elif variant == "causal_mean":
+        kv_len = np.array([[[704, 650, 17], [0, 640, 700], [1, 688, 689], [300, 301, 704]]], dtype=np.int32)
+        layout = [(k4, v2, 0, 4, 0, 640), (K.Codec(K.INT_ABSMAX, 4, 64, 0), K.Codec(K.INT_ABSMAX, 4, 64, 0), 0, 4, 640, 64)]
+        mean_seg = 0
+    else:
+        layout = [(K.Codec(K.SIGN, 1, 8, 0), K.Codec(K.SIGN, 1, 8, 0), 0, 4, 0, 640), (f16, f16, 0, 4, 640, 64)]
+    announce(f"segments {variant}")
+    _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg)
+
+
+def test_append_then_decode_loop_matches_the_whole_cache():
+    """Tokens appended one by one (the last 8 of 520) with a decode after each, against
+    the same decode on the cache quantised in one call."""
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=2, T=520, n_q=1)
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    B, L, H, T, D = Kx.shape
+    Hq = q.shape[3]
+    shape = K.Shape(B, L, H, T, D)
+    kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    announce("append + decode loop")
+    kf, vf = K.alloc_packed(kc, shape), K.alloc_packed(vc, shape)
+    K.kvq_quantize_pack(to_dev(Kx), kf)
+    K.kvq_quantize_pack(to_dev(Vx), vf)
+    ka, va = K.alloc_packed(kc, shape), K.alloc_packed(vc, shape)
+    K.kvq_quantize_pack_tokens(to_dev(np.ascontiguousarray(Kx[:, :, :, :512])), 0, 512, ka)
+    K.kvq_quantize_pack_tokens(to_dev(np.ascontiguousarray(Vx[:, :, :, :512])), 0, 512, va)
+    wsb = K.kvq_decode_attn_workspace(shape, Hq, 1)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda:0")
+    qd = to_dev(q)
+    for t in range(512, 520):
+        K.kvq_quantize_pack_tokens(to_dev(np.ascontiguousarray(Kx[:, :, :, t:t + 1])), t, 1, ka)
+        K.kvq_quantize_pack_tokens(to_dev(np.ascontiguousarray(Vx[:, :, :, t:t + 1])), t, 1, va)
+        kvl = to_dev(np.full((B, L, 1), t + 1, dtype=np.int32))
+        o1 = torch.empty((B, L, 1, Hq, D), dtype=torch.float32, device="cuda:0")
+        o2, l1, l2 = torch.empty_like(o1), torch.empty((B, L, 1, Hq), dtype=torch.float32, device="cuda:0"), \
+            torch.empty((B, L, 1, Hq), dtype=torch.float32, device="cuda:0")
+        K.kvq_decode_attn(ka, va, Hq, 1, qd, kvl, 0.0, o1, l1, ws, wsb)
+        K.kvq_decode_attn(kf, vf, Hq, 1, qd, kvl, 0.0, o2, l2, ws, wsb)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"step {t}"
+    for a, b in zip(_packed_arrays(kf) + _packed_arrays(vf), _packed_arrays(ka) + _packed_arrays(va)):
+        assert np.array_equal(a, b)
