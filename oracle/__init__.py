@@ -45,5 +45,6 @@ from .codec import (  # noqa: F401
 )
 from .attention import (  # noqa: F401
     attend_unit, decode_attn, attn_error, kl_div, rel_err, kv_err_unit, assemble_segments,
+    renyi2, js_div, logit_relerr, top1_flip, entropy_adaptive_bits, attn_error_ex,
 )
 from .accounting import bits_per_value, kv_bits_per_value, rfft_payload_bits_per_value, tiles, effective_bits  # noqa: F401

@@ -102,6 +102,83 @@ def kv_err_unit(x16: np.ndarray, x_hat: np.ndarray):
     return float((d * d).sum()), float((x * x).sum())
 
 
+def renyi2(logits: np.ndarray) -> np.ndarray:
+    """Renyi entropy of order 2 of softmax(logits), -ln sum_t p_t^2, in nats
+    ([LCPP] Finding 2: H_2(h) of a head's attention distribution); 0 for no keys."""
+    if logits.shape[-1] == 0:
+        return np.zeros(logits.shape[:-1])
+    lp = logits - _lse(logits)[..., None]
+    return -np.log(np.exp(2.0 * lp).sum(-1))
+
+
+def js_div(logits_ref: np.ndarray, logits_q: np.ndarray) -> np.ndarray:
+    """Jensen-Shannon divergence of the two attention distributions in nats:
+    (KL(p || m) + KL(phat || m)) / 2 with m = (p + phat) / 2, 0 ln 0 = 0
+    ([FMAG-R] reply's diagnostic ladder: attention KL / JS); 0 for no keys."""
+    if logits_ref.shape[-1] == 0:
+        return np.zeros(logits_ref.shape[:-1])
+    p = np.exp(logits_ref - _lse(logits_ref)[..., None])
+    r = np.exp(logits_q - _lse(logits_q)[..., None])
+    m = 0.5 * (p + r)
+    a = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0) / np.where(m > 0, m, 1.0)), 0.0).sum(-1)
+    b = np.where(r > 0, r * np.log(np.where(r > 0, r, 1.0) / np.where(m > 0, m, 1.0)), 0.0).sum(-1)
+    return 0.5 * (a + b)
+
+
+def logit_relerr(logits_ref: np.ndarray, logits_q: np.ndarray) -> np.ndarray:
+    """||lhat - l||_2 / ||l||_2 over the attended keys (the ladder's QK-logit error);
+    0 for no keys or an all-zero reference."""
+    num = np.sqrt(((logits_q - logits_ref) ** 2).sum(-1))
+    den = np.sqrt((logits_ref ** 2).sum(-1))
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), 0.0)
+
+
+def top1_flip(logits_ref: np.ndarray, logits_q: np.ndarray) -> np.ndarray:
+    """1 where the most-attended key differs (first index on ties), else 0 (the
+    ladder's top-attended-token flips); 0 for no keys."""
+    if logits_ref.shape[-1] == 0:
+        return np.zeros(logits_ref.shape[:-1])
+    return (np.argmax(logits_ref, -1) != np.argmax(logits_q, -1)).astype(np.float64)
+
+
+def entropy_adaptive_bits(h2: np.ndarray, b_avg: float) -> np.ndarray:
+    """Per-head bits b_h = b_avg + 0.25 (H_avg - H_2(h)) ([LCPP] Finding 2), with
+    H_avg the mean of H_2 over the heads given (the plain reading); the mean of
+    b_h is b_avg."""
+    h2 = np.asarray(h2, dtype=np.float64)
+    return b_avg + 0.25 * (h2.mean() - h2)
+
+
+def attn_error_ex(q16, K16, V16, Kd, Vd, kv_len=None, sm_scale=0.0, units=None):
+    """attn_error plus the other rungs of the diagnostic ladder, per row: Renyi-2
+    entropy of the fp16 distribution, JS divergence, QK-logit relative error and
+    top-1 flips (dict of arrays [B][L][nq][Hq]; 'kv_err' [B][L][H][4])."""
+    B, L, nq, Hq, D = q16.shape
+    H, T = K16.shape[2], K16.shape[3]
+    G = Hq // H
+    s = _scale(D, sm_scale)
+    names = ("kl", "relerr", "renyi2", "js", "logit_relerr", "top1_flip")
+    res = {k: np.full((B, L, nq, Hq), np.nan) for k in names}
+    res["kv_err"] = np.full((B, L, H, 4), np.nan)
+    q = q16.astype(np.float64)
+    todo = units if units is not None else [(b, l, h) for b in range(B) for l in range(L) for h in range(H)]
+    for (b, l, h) in todo:
+        n = np.full(nq, T) if kv_len is None else kv_len[b, l]
+        for i in range(nq):
+            o, _, lr = attend(q[b, l, i, h * G:(h + 1) * G], K16[b, l, h], V16[b, l, h], int(n[i]), s)
+            oh, _, lq = attend(q[b, l, i, h * G:(h + 1) * G], Kd[b, l, h], Vd[b, l, h], int(n[i]), s)
+            sl = (b, l, i, slice(h * G, (h + 1) * G))
+            res["kl"][sl] = kl_div(lr, lq)
+            res["relerr"][sl] = rel_err(oh, o)
+            res["renyi2"][sl] = renyi2(lr)
+            res["js"][sl] = js_div(lr, lq)
+            res["logit_relerr"][sl] = logit_relerr(lr, lq)
+            res["top1_flip"][sl] = top1_flip(lr, lq)
+        res["kv_err"][b, l, h, 0:2] = kv_err_unit(K16[b, l, h], Kd[b, l, h])
+        res["kv_err"][b, l, h, 2:4] = kv_err_unit(V16[b, l, h], Vd[b, l, h])
+    return res
+
+
 def attn_error(q16, K16, V16, Kd, Vd, kv_len=None, sm_scale=0.0, units=None):
     """Per-row KL and relative output error of attention through (Kd, Vd) vs
     fp16 (K16, V16), plus per-unit K/V error sums.
