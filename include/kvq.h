@@ -303,6 +303,32 @@ kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16,
                           float sm_scale, float* kl_rows, float* relerr_rows,
                           double* kv_err, void* ws, size_t ws_bytes, void* stream);
 
+/* Outputs of kvq_attn_error_ex, each nullable; row arrays are fp32
+ * [B][L][n_q][q_heads] over the attended keys of the row.  The rungs of the
+ * diagnostic ladder ([FMAG-R] the Colab-probe reply: QK-logit error, attention
+ * KL / JS, top-attended-token flips, attention-output error) and the Renyi
+ * entropy that sizes per-head bits ([LCPP] Finding 2). */
+typedef struct {
+  float* kl;            /* KL(p_fp16 || p_quant), nats */
+  float* relerr;        /* ||o_quant - o_fp16|| / ||o_fp16|| */
+  double* kv_err;       /* [B][L][H][4] as for kvq_attn_error */
+  float* renyi2;        /* H_2(p_fp16) = -ln sum_t p_t^2, nats (0 without keys) */
+  float* js;            /* Jensen-Shannon divergence of p_fp16 and p_quant, nats
+                           (one more pass over the keys) */
+  float* logit_relerr;  /* ||l_quant - l_fp16|| / ||l_fp16|| of the logits sm * q.k */
+  float* top1;          /* 1 where the most-attended key differs (first index on
+                           ties), else 0 */
+} kvq_error_outputs;
+
+/* kvq_attn_error with the outputs chosen by `outs` (any subset; the same
+ * workspace size).  A key mean is restored in every output (the quantised
+ * logits include q.mean). */
+kvq_status kvq_attn_error_ex(const uint16_t* k_fp16, const uint16_t* v_fp16,
+                             const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
+                             int32_t n_q, const uint16_t* q, const int32_t* kv_len,
+                             float sm_scale, const kvq_error_outputs* outs, void* ws,
+                             size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

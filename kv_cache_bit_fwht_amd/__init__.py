@@ -29,6 +29,7 @@ EXPORTS = [
     "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_ex",
     "kvq_attn_error_workspace", "kvq_attn_error", "kvq_quantize_pack_tokens",
     "kvq_decode_attn_segments_workspace", "kvq_decode_attn_segments", "kvq_effective_bits",
+    "kvq_attn_error_ex",
 ]
 
 
@@ -52,6 +53,12 @@ class kvq_packed(ctypes.Structure):
     _fields_ = [("codec", kvq_codec), ("shape", kvq_shape), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("mins", ctypes.c_void_p), ("chan_scale", ctypes.c_void_p),
                 ("mean", ctypes.c_void_p)]
+
+
+class kvq_error_outputs(ctypes.Structure):
+    _fields_ = [("kl", ctypes.c_void_p), ("relerr", ctypes.c_void_p), ("kv_err", ctypes.c_void_p),
+                ("renyi2", ctypes.c_void_p), ("js", ctypes.c_void_p), ("logit_relerr", ctypes.c_void_p),
+                ("top1", ctypes.c_void_p)]
 
 
 class kvq_segment(ctypes.Structure):
@@ -85,6 +92,7 @@ def _load():
         "kvq_decode_attn_segments_workspace": ([P, I32, I32, I32, I32], SZ),
         "kvq_decode_attn_segments": ([P, I32, I32, I32, I32, I32, P, P, F, P, P, P, SZ, P], I32),
         "kvq_effective_bits": ([P, I32, I32, I32], D),
+        "kvq_attn_error_ex": ([P, P, P, P, I32, I32, P, P, F, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -304,6 +312,18 @@ def kvq_attn_error(k_fp16, v_fp16, k: Packed, v: Packed, q_heads: int, n_q: int,
                              _ptr(q), _ptr(kv_len), sm_scale, _ptr(kl_rows), _ptr(relerr_rows), _ptr(kv_err),
                              _ptr(ws), ws_bytes, _stream(stream))
     _check("kvq_attn_error", st)
+
+
+def kvq_attn_error_ex(k_fp16, v_fp16, k: Packed, v: Packed, q_heads: int, n_q: int, q, kv_len, sm_scale: float,
+                      ws, ws_bytes: int, stream=None, kl=None, relerr=None, kv_err=None, renyi2=None, js=None,
+                      logit_relerr=None, top1=None):
+    """The error reduction with any subset of its outputs (torch tensors or None)."""
+    kc, vc = k.c(), v.c()
+    o = kvq_error_outputs(_ptr(kl), _ptr(relerr), _ptr(kv_err), _ptr(renyi2), _ptr(js), _ptr(logit_relerr),
+                          _ptr(top1))
+    st = _lib.kvq_attn_error_ex(_ptr(k_fp16), _ptr(v_fp16), ctypes.byref(kc), ctypes.byref(vc), q_heads, n_q,
+                                _ptr(q), _ptr(kv_len), sm_scale, ctypes.byref(o), _ptr(ws), ws_bytes, _stream(stream))
+    _check("kvq_attn_error_ex", st)
 
 
 # ------------------------------------------------------------------ device-memory plumbing

@@ -601,16 +601,17 @@ size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_
   return kWsCounterBytes + error_ws_bytes(*kv, q_heads, n_q);
 }
 
-kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16, const kvq_packed* k,
-                          const kvq_packed* v, int32_t q_heads, int32_t n_q, const uint16_t* q,
-                          const int32_t* kv_len, float sm_scale, float* kl_rows, float* relerr_rows,
-                          double* kv_err, void* ws, size_t ws_bytes, void* stream) {
+kvq_status kvq_attn_error_ex(const uint16_t* k_fp16, const uint16_t* v_fp16, const kvq_packed* k,
+                             const kvq_packed* v, int32_t q_heads, int32_t n_q, const uint16_t* q,
+                             const int32_t* kv_len, float sm_scale, const kvq_error_outputs* outs, void* ws,
+                             size_t ws_bytes, void* stream) {
   kvq_status st = check_attn(k, v, q_heads, n_q, q);
   if (st != KVQ_OK) return st;
-  if (!k_fp16 || !v_fp16 || !kl_rows || !relerr_rows || !kv_err) return KVQ_ERR_ARG;
-  if (!aligned16(k_fp16) || !aligned16(v_fp16) || !aligned16(kl_rows) || !aligned16(relerr_rows) ||
-      !aligned16(kv_err) || (kv_len && !aligned16(kv_len)))
-    return KVQ_ERR_ALIGN;
+  if (!k_fp16 || !v_fp16 || !outs) return KVQ_ERR_ARG;
+  const void* ptrs[] = {outs->kl, outs->relerr, outs->kv_err, outs->renyi2, outs->js, outs->logit_relerr, outs->top1};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
+  if (!aligned16(k_fp16) || !aligned16(v_fp16) || (kv_len && !aligned16(kv_len))) return KVQ_ERR_ALIGN;
   if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
   const size_t need = kWsCounterBytes + error_ws_bytes(k->shape, q_heads, n_q);
   if (ws_bytes < need || (need && !ws)) return KVQ_ERR_WORKSPACE;
@@ -618,11 +619,25 @@ kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16, const 
   AttnProblem pr{};
   pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
   pr.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)k->shape.head_dim));
-  pr.k16 = k_fp16; pr.v16 = v_fp16; pr.kl = kl_rows; pr.relerr = relerr_rows; pr.kv_err = kv_err;
+  pr.k16 = k_fp16; pr.v16 = v_fp16;
+  pr.kl = outs->kl; pr.relerr = outs->relerr; pr.kv_err = outs->kv_err;
+  pr.renyi2 = outs->renyi2; pr.js = outs->js; pr.logit_relerr = outs->logit_relerr; pr.top1 = outs->top1;
   pr.ctr = nullptr;                                  // same layout as decode; no counters used
   pr.ws = static_cast<char*>(ws) + kWsCounterBytes;
   pr.ws_bytes = ws_bytes - kWsCounterBytes;
   return hip_status(launch_attn_error(pr, (hipStream_t)stream));
+}
+
+kvq_status kvq_attn_error(const uint16_t* k_fp16, const uint16_t* v_fp16, const kvq_packed* k,
+                          const kvq_packed* v, int32_t q_heads, int32_t n_q, const uint16_t* q,
+                          const int32_t* kv_len, float sm_scale, float* kl_rows, float* relerr_rows,
+                          double* kv_err, void* ws, size_t ws_bytes, void* stream) {
+  if (!kl_rows || !relerr_rows || !kv_err) return KVQ_ERR_ARG;
+  kvq_error_outputs o{};
+  o.kl = kl_rows;
+  o.relerr = relerr_rows;
+  o.kv_err = kv_err;
+  return kvq_attn_error_ex(k_fp16, v_fp16, k, v, q_heads, n_q, q, kv_len, sm_scale, &o, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

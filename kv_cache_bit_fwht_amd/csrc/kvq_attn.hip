@@ -52,10 +52,16 @@ struct AArgs {
   int lpt_log2;
   int Dc;              // coded key length (D, or 2*(D/2+1) for rFFT keys)
   float* ws;           // split partials
+  const double* js_rowz;  // error kernel, JS pass: per row (ln Z of fp16, ln Z of quant), else null
   Tables tab;
   FftTables tw;        // twiddles of head_dim (rFFT keys: the query's DFT)
   DirTables dirs;      // phase-sector directions (rFFT polar keys)
 };
+
+// Error-kernel split partials: [2*D floats (o_quant, o_fp16)][kErrDoubles doubles]:
+// m, l, m2, l2, A, S2 (sum e^{2(l - m2)}), LE (sum (lhat - l)^2), LL (sum l^2),
+// argmax fp16, argmax quant, JS (second pass).
+constexpr int kErrDoubles = 11;
 
 // ------------------------------------------------------------------ tile dequantisation
 
@@ -249,6 +255,12 @@ __device__ __forceinline__ T grp_max16(T v) {
   return v;
 }
 template <typename T>
+__device__ __forceinline__ T grp_min16(T v) {
+#pragma unroll
+  for (int m = 1; m < TB; m <<= 1) { const T o = __shfl_xor(v, m); v = v < o ? v : o; }
+  return v;
+}
+template <typename T>
 __device__ __forceinline__ T grp_sum16(T v) {
 #pragma unroll
   for (int m = 1; m < TB; m <<= 1) v += __shfl_xor(v, m);
@@ -278,7 +290,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
   float* pb2 = pb + kMaxG * TB;                  // [G][TB] weights (fp16)
   acc_t* sc = reinterpret_cast<acc_t*>(pb2 + kMaxG * TB);   // [G][TB] logits (quant)
   acc_t* sc2 = sc + kMaxG * TB;                  // [G][TB] logits (fp16)
-  acc_t* st = sc2 + kMaxG * TB;                  // stats [8][kMaxG]
+  acc_t* st = sc2 + kMaxG * TB;                  // stats [16][kMaxG]
 
   const int s = blockIdx.x, h = blockIdx.y;
   const long long rq = blockIdx.z;                // (b*L + l)*n_q + i
@@ -293,11 +305,23 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
   const acc_t NEG_INF = -(acc_t)INFINITY;
 
   query_prologue(a, b, l, i, h, qc, ERR ? qr : nullptr, RS);
-  // stats: 0 m, 1 l, 2 alpha, 3 A, 4 m2, 5 l2, 6 alpha2
+  // stats: 0 m, 1 l, 2 alpha, 3 A, 4 m2, 5 l2, 6 alpha2, 7 S2, 8 LE, 9 LL, 10 argmax fp16,
+  // 11 argmax quant, 12 JS, 13 q.mean (the quantised logits' shift when keys carry a mean)
+  const bool jsp = ERR && a.js_rowz != nullptr;  // second pass: JS only
   if (tid < kMaxG) {
     st[0 * kMaxG + tid] = NEG_INF; st[1 * kMaxG + tid] = 0; st[2 * kMaxG + tid] = 1;
     st[3 * kMaxG + tid] = 0; st[4 * kMaxG + tid] = NEG_INF; st[5 * kMaxG + tid] = 0;
     st[6 * kMaxG + tid] = 1;
+    if (ERR) {
+      st[7 * kMaxG + tid] = 0; st[8 * kMaxG + tid] = 0; st[9 * kMaxG + tid] = 0;
+      st[10 * kMaxG + tid] = -1; st[11 * kMaxG + tid] = -1; st[12 * kMaxG + tid] = 0;
+      acc_t qm = 0;
+      if (a.k.mean && tid < G) {
+        const float* mp = a.k.mean + ((size_t)l * a.H + h) * D;
+        for (int d = 0; d < D; ++d) qm += (acc_t)qr[tid * RS + pidx(d)] * (acc_t)mp[d];
+      }
+      st[13 * kMaxG + tid] = qm;
+    }
   }
   float acc[kMaxG], acc2[kMaxG];
 #pragma unroll
@@ -306,10 +330,10 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
 
   for (int t0 = tb0; t0 < tb1; t0 += TB) {
     tile_dequant(a, a.k, urow0, t0, tb1, kt, RS);
-    tile_dequant(a, a.v, urow0, t0, tb1, vt, RS);
+    if (!jsp) tile_dequant(a, a.v, urow0, t0, tb1, vt, RS);
     if (ERR) {
       tile_fp16(a, a.k16, urow0, t0, tb1, kt2, RS);
-      tile_fp16(a, a.v16, urow0, t0, tb1, vt2, RS);
+      if (!jsp) tile_fp16(a, a.v16, urow0, t0, tb1, vt2, RS);
     }
     __syncthreads();
     if (tid < TB * G) {
@@ -317,6 +341,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
       const bool valid = t0 + t < tb1;
       acc_t sq = 0;
       for (int e = 0; e < a.Dc; ++e) sq += (acc_t)qc[g * RS + pidx(e)] * (acc_t)kt[t * RS + pidx(e)];
+      if (ERR) sq += st[13 * kMaxG + g];
       sc[g * TB + t] = valid ? sq : NEG_INF;
       if (ERR) {
         acc_t sr = 0;
@@ -325,12 +350,34 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
       }
     }
     __syncthreads();
+    if (jsp) {   // JS terms with the final normalisers of both distributions
+      if (tid < TB * G) {
+        const int t = tid % TB, g = tid / TB;
+        const acc_t x = sc2[g * TB + t], xq = sc[g * TB + t];
+        const double* rz = a.js_rowz + ((size_t)rq * a.Hq + (size_t)h * G + g) * 2;
+        const acc_t pp = (x == NEG_INF || rz[0] == NEG_INF) ? (acc_t)0 : exp_t(x - rz[0]);
+        const acc_t rr = (xq == NEG_INF || rz[1] == NEG_INF) ? (acc_t)0 : exp_t(xq - rz[1]);
+        const acc_t mm = (acc_t)0.5 * (pp + rr);
+        acc_t term = 0;
+        if (pp > 0) term += pp * log(pp / mm);
+        if (rr > 0) term += rr * log(rr / mm);
+        const acc_t js = grp_sum16(term);
+        if (t == 0) st[12 * kMaxG + g] += (acc_t)0.5 * js;
+      }
+      __syncthreads();
+      continue;
+    }
     if (tid < TB * G) {
       const int t = tid % TB, g = tid / TB;
       {  // packed cache: online softmax
         const acc_t x = sc[g * TB + t];
         const acc_t mo = st[0 * kMaxG + g];
         const acc_t mt = grp_max16(x);
+        if (ERR) {  // first index of the running maximum
+          const acc_t cand = (x == mt && x != NEG_INF) ? (acc_t)(t0 + t) : (acc_t)INFINITY;
+          const acc_t at = grp_min16(cand);
+          if (t == 0 && mt > mo) st[11 * kMaxG + g] = at;
+        }
         const acc_t M = mo > mt ? mo : mt;
         const acc_t p = (x == NEG_INF) ? (acc_t)0 : exp_t(x - M);
         const acc_t ps = grp_sum16(p);
@@ -350,12 +397,21 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
         const acc_t p = (x == NEG_INF) ? (acc_t)0 : exp_t(x - M);
         const acc_t ps = grp_sum16(p);
         const acc_t pa = grp_sum16((x == NEG_INF) ? (acc_t)0 : p * (x - xq));
+        const acc_t p2 = grp_sum16(p * p);
+        const acc_t le = grp_sum16((x == NEG_INF) ? (acc_t)0 : (xq - x) * (xq - x));
+        const acc_t ll = grp_sum16((x == NEG_INF) ? (acc_t)0 : x * x);
+        const acc_t cand = (x == mt && x != NEG_INF) ? (acc_t)(t0 + t) : (acc_t)INFINITY;
+        const acc_t at = grp_min16(cand);
         pb2[g * TB + t] = (float)p;
         if (t == 0) {
           const acc_t al = (M == NEG_INF) ? (acc_t)1 : exp_t(mo - M);
           st[6 * kMaxG + g] = al;
           st[5 * kMaxG + g] = st[5 * kMaxG + g] * al + ps;
           st[3 * kMaxG + g] = st[3 * kMaxG + g] * al + pa;
+          st[7 * kMaxG + g] = st[7 * kMaxG + g] * al * al + p2;
+          st[8 * kMaxG + g] += le;
+          st[9 * kMaxG + g] += ll;
+          if (mt > mo) st[10 * kMaxG + g] = at;
           st[4 * kMaxG + g] = M;
         }
       }
@@ -381,8 +437,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
   }
 
   // partials: decode [rq][Hq][S][D+2 floats] = (o[D], m, l); error
-  // [rq][Hq][S][2D floats + 5 doubles] = (o_quant[D], o_fp16[D]; m, l, m2, l2, A)
-  const int P = ERR ? 2 * D + 10 : D + 2;
+  // [rq][Hq][S][2D floats + kErrDoubles doubles] (see kErrDoubles)
+  const int P = ERR ? 2 * D + 2 * kErrDoubles : D + 2;
 #pragma unroll
   for (int g = 0; g < kMaxG; ++g) {
     if (g >= G) break;
@@ -399,6 +455,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AArgs a) {
         dd[2] = (double)st[4 * kMaxG + g];
         dd[3] = (double)st[5 * kMaxG + g];
         dd[4] = (double)st[3 * kMaxG + g];
+#pragma unroll
+        for (int k = 5; k < kErrDoubles; ++k) dd[k] = (double)st[(k + 2) * kMaxG + g];
       } else {
         dst[D] = (float)st[0 * kMaxG + g];
         dst[D + 1] = (float)st[1 * kMaxG + g];
@@ -793,19 +851,26 @@ struct CArgs {
   int* ctr;             // decode chunk counters to set back to zero, or null
 };
 
+struct ErrOut {          // error outputs beyond KL / relative error (each nullable)
+  float* renyi2;
+  float* logit_relerr;
+  float* top1;
+  double* rowz;          // per row (ln Z fp16, ln Z quant) for the JS pass
+};
+
 template <bool ERR>
 __global__ __launch_bounds__(kBlock) void k_attn_combine(CArgs a, float* out, float* lse, float* kl,
-                                                         float* relerr) {
+                                                         float* relerr, ErrOut eo) {
   __shared__ float orow[17 * 16 + 17];
   __shared__ double wq[kMaxSplits], w2[kMaxSplits];   // per-split weights e^{m_s - M}
-  __shared__ double red[3][kBlock];
+  __shared__ double red[6][kBlock];
   const long long rh = blockIdx.x;               // rq * Hq + j
   const int j = (int)(rh % a.Hq);
   const long long rq = rh / a.Hq;
   const int l = (int)((rq / a.n_q) % a.L);
   const int h = j / a.G;
   const int D = a.D, tid = threadIdx.x;
-  const int P = ERR ? 2 * D + 10 : D + 2;
+  const int P = ERR ? 2 * D + 2 * kErrDoubles : D + 2;
   const float* src = a.ws + (size_t)rh * a.S * P;
   // per split: m, l (packed cache) and m2, l2, A (fp16 cache)
   auto stat = [&](int s, int k) -> double {
@@ -832,7 +897,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(CArgs a, float* out, fl
   const double M = red[0][0], M2 = red[1][0];
   __syncthreads();
   // 2. split weights and the normalisers
-  double lq = 0.0, l2 = 0.0, aa = 0.0;
+  double lq = 0.0, l2 = 0.0, aa = 0.0, s2 = 0.0, le = 0.0, ll = 0.0;
   for (int s = tid; s < a.S; s += kBlock) {
     const double ms = stat(s, 0);
     const double w = (M == -INFINITY || ms == -INFINITY) ? 0.0 : exp(ms - M);
@@ -844,21 +909,26 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(CArgs a, float* out, fl
       w2[s] = v;
       l2 += stat(s, 3) * v;
       aa += stat(s, 4) * v;
+      s2 += stat(s, 5) * v * v;
+      le += stat(s, 6);
+      ll += stat(s, 7);
     }
   }
   red[0][tid] = lq;
   red[1][tid] = l2;
   red[2][tid] = aa;
+  red[3][tid] = s2;
+  red[4][tid] = le;
+  red[5][tid] = ll;
   __syncthreads();
   for (int st = kBlock / 2; st > 0; st >>= 1) {
     if (tid < st) {
-      red[0][tid] += red[0][tid + st];
-      red[1][tid] += red[1][tid + st];
-      red[2][tid] += red[2][tid + st];
+#pragma unroll
+      for (int k = 0; k < 6; ++k) red[k][tid] += red[k][tid + st];
     }
     __syncthreads();
   }
-  const double Lq = red[0][0], L2 = red[1][0], A = red[2][0];
+  const double Lq = red[0][0], L2 = red[1][0], A = red[2][0], S2 = red[3][0], LE = red[4][0], LL = red[5][0];
   // 3. outputs, one dimension per thread (coalesced over the partial rows)
   float o = 0.0f, o2 = 0.0f;
   if (tid < D) {
@@ -899,11 +969,35 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(CArgs a, float* out, fl
   }
   if (tid == 0) {
     const double num = red[0][0], den = red[1][0];
-    relerr[rh] = den > 0.0 ? (float)(sqrt(num) / sqrt(den)) : 0.0f;
+    if (relerr) relerr[rh] = den > 0.0 ? (float)(sqrt(num) / sqrt(den)) : 0.0f;
     double k = 0.0;
     if (L2 > 0.0 && Lq > 0.0) k = A / L2 - (M2 + log(L2)) + (M + log(Lq));
-    kl[rh] = (float)k;
+    if (kl) kl[rh] = (float)k;
+    if (eo.renyi2) eo.renyi2[rh] = L2 > 0.0 ? (float)(2.0 * log(L2) - log(S2)) : 0.0f;
+    if (eo.logit_relerr) eo.logit_relerr[rh] = LL > 0.0 ? (float)(sqrt(LE) / sqrt(LL)) : 0.0f;
+    if (eo.top1) {
+      // the first key holding the maximum: the earliest split reaching it, then its first index
+      double a2 = -1.0, aq = -1.0;
+      for (int s = 0; s < a.S && a2 < 0.0; ++s)
+        if (stat(s, 2) == M2 && M2 != -INFINITY) a2 = stat(s, 8);
+      for (int s = 0; s < a.S && aq < 0.0; ++s)
+        if (stat(s, 0) == M && M != -INFINITY) aq = stat(s, 9);
+      eo.top1[rh] = (L2 > 0.0 && a2 != aq) ? 1.0f : 0.0f;
+    }
+    if (eo.rowz) {
+      eo.rowz[rh * 2 + 0] = L2 > 0.0 ? M2 + log(L2) : -INFINITY;
+      eo.rowz[rh * 2 + 1] = Lq > 0.0 ? M + log(Lq) : -INFINITY;
+    }
   }
+}
+
+// JS of a row: the second pass's split partials summed in split order.
+__global__ void k_js_final(const float* __restrict__ ws, int S, int P, int D, long long rows, float* __restrict__ js) {
+  const long long rh = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (rh >= rows) return;
+  double t = 0.0;
+  for (int s = 0; s < S; ++s) t += reinterpret_cast<const double*>(ws + ((size_t)rh * S + s) * P + 2 * D)[10];
+  js[rh] = (float)t;
 }
 
 // ------------------------------------------------------------------ K/V squared error
@@ -1103,10 +1197,11 @@ static int kverr_chunks(const kvq_shape& s) {
 
 size_t error_ws_bytes(const kvq_shape& s, int Hq, int n_q) {
   const int S = decode_splits(s, Hq, n_q);
-  const size_t part = (size_t)s.batch * s.layers * n_q * Hq * S * (2 * s.head_dim + 10) * sizeof(float);
+  const size_t part = (size_t)s.batch * s.layers * n_q * Hq * S * (2 * s.head_dim + 2 * kErrDoubles) * sizeof(float);
   const size_t units = (size_t)s.batch * s.layers * s.heads;
   const size_t kv = 2 * units * kverr_chunks(s) * 2 * sizeof(double);
-  return ((part + 255) / 256) * 256 + kv;
+  const size_t rowz = (size_t)s.batch * s.layers * n_q * Hq * 2 * sizeof(double);   // JS pass normalisers
+  return ((part + 255) / 256) * 256 + kv + rowz;
 }
 
 static AArgs make_aargs(const AttnProblem& pr) {
@@ -1142,7 +1237,7 @@ static size_t split_smem(const AArgs& a, bool err) {
   if (err) f += (size_t)kMaxG * RS + 2 * TB * RS;
   f = (f + 3) / 4 * 4;                                   // 16-byte align the logit/stat arrays
   const size_t acc_bytes = err ? sizeof(double) : sizeof(float);
-  return f * sizeof(float) + (2 * kMaxG * TB + 8 * kMaxG) * acc_bytes;
+  return f * sizeof(float) + (2 * kMaxG * TB + 16 * kMaxG) * acc_bytes;
 }
 
 template <int KCB, int KB, int VCB, int VB>
@@ -1244,7 +1339,7 @@ hipError_t launch_combine_partials(const AttnProblem& pr, int S, int* ctr, hipSt
   const long long R = (long long)s.batch * s.layers * pr.n_q;
   CArgs c = make_cargs(pr, S, static_cast<float*>(pr.ws));
   c.ctr = ctr;
-  k_attn_combine<false><<<(unsigned)(R * pr.Hq), kBlock, 0, st>>>(c, pr.out, pr.lse, nullptr, nullptr);
+  k_attn_combine<false><<<(unsigned)(R * pr.Hq), kBlock, 0, st>>>(c, pr.out, pr.lse, nullptr, nullptr, ErrOut{});
   return hipGetLastError();
 }
 
@@ -1259,16 +1354,32 @@ hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st) {
   k_attn_split<true><<<dim3(a.S, a.H, (unsigned)R), kBlock, smem, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_attn_combine<true><<<(unsigned)(R * a.Hq), kBlock, 0, st>>>(make_cargs(pr, a.S, a.ws), nullptr, nullptr,
-                                                                pr.kl, pr.relerr);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // per-unit K/V squared error
+  // workspace: split partials | per-unit K/V error partials | per-row normalisers (JS pass)
   const long long units = (long long)s.batch * s.layers * s.heads;
   const int chunks = kverr_chunks(s);
-  const size_t part_bytes = (size_t)R * a.Hq * a.S * (2 * a.D + 10) * sizeof(float);
+  const int P = 2 * a.D + 2 * kErrDoubles;
+  const size_t part_bytes = (size_t)R * a.Hq * a.S * P * sizeof(float);
   double* pk = reinterpret_cast<double*>(static_cast<char*>(pr.ws) + ((part_bytes + 255) / 256) * 256);
   double* pv = pk + units * chunks * 2;
+  double* rowz = pv + units * chunks * 2;
+  ErrOut eo{pr.renyi2, pr.logit_relerr, pr.top1, pr.js ? rowz : nullptr};
+  k_attn_combine<true><<<(unsigned)(R * a.Hq), kBlock, 0, st>>>(make_cargs(pr, a.S, a.ws), nullptr, nullptr,
+                                                                pr.kl, pr.relerr, eo);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (pr.js) {   // second pass: JS needs both distributions' final normalisers
+    AArgs aj = a;
+    aj.js_rowz = rowz;
+    k_attn_split<true><<<dim3(a.S, a.H, (unsigned)R), kBlock, smem, st>>>(aj);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long rows = R * a.Hq;
+    k_js_final<<<(unsigned)((rows + 255) / 256), 256, 0, st>>>(a.ws, a.S, P, a.D, rows, pr.js);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!pr.kv_err) return hipSuccess;
+  // per-unit K/V squared error
   if (units == 0 || s.tokens == 0) {
     return hipMemsetAsync(pr.kv_err, 0, sizeof(double) * 4 * units, st);
   }

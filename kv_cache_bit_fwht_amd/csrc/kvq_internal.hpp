@@ -175,6 +175,10 @@ struct AttnProblem {
   float* kl;
   float* relerr;
   double* kv_err;
+  float* renyi2;     // the further error outputs (attn_error_ex), each nullable
+  float* js;
+  float* logit_relerr;
+  float* top1;
   void* ws;          // partials (the workspace past its counter region)
   size_t ws_bytes;
   int* ctr;          // the workspace's counter region (kWsCounterBytes, zero between calls)
