@@ -339,13 +339,13 @@ def anchors_workload(reps):
     del Kx, Vx
     out = torch.empty((B, L, 1, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, L, 1, Hq), dtype=torch.float32, device=dev)
-    wsb = K.kvq_decode_attn_segments_workspace(segs, L, Hq, 1)
+    wsb = K.kvq_decode_attn_segments_workspace(segs, L, H, Hq, 1)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     wsb1 = K.kvq_decode_attn_workspace(shape, Hq, 1)
     ws1 = torch.zeros(wsb1, dtype=torch.uint8, device=dev)
 
     def seg_step():
-        K.kvq_decode_attn_segments(segs, L, T, Hq, 1, qd, None, 0.0, out, lse, ws, wsb)
+        K.kvq_decode_attn_segments(segs, L, H, T, Hq, 1, qd, None, 0.0, out, lse, ws, wsb)
 
     def one_step():
         K.kvq_decode_attn(kfull, vfull, Hq, 1, qd, None, 0.0, out, lse, ws1, wsb1)
@@ -360,7 +360,7 @@ def anchors_workload(reps):
     t_seg = _median_time(torch, seg_step, reps)
     t_one = _median_time(torch, one_step, reps)
     t_app = _median_time(torch, append, reps)
-    eff = K.kvq_effective_bits(segs, L, T)
+    eff = K.kvq_effective_bits(segs, L, H, T)
     d_bytes = sum(s.k.codes.numel() * 4 + (s.k.scales.numel() * 2 if s.k.scales is not None else 0) +
                   s.v.codes.numel() * 4 + (s.v.scales.numel() * 2 if s.v.scales is not None else 0) for s in segs)
     rec = {"workload": f"c3a: B={B} L={L} H={H} T={T} D={D} Hq={Hq}, prompt {P} + {A} decode anchors fp16 on "
@@ -372,6 +372,117 @@ def anchors_workload(reps):
            "decode_step_one_tensor": {"us": round(t_one * 1e6, 1)},
            "append_one_token_kv": {"us": round(t_app * 1e6, 1), "rows": 2 * B * L * H}}
     print(json.dumps(rec), flush=True)
+
+
+def _round_keep_sum(b, lo=2, hi=8):
+    """Integer bits from fractional ones, keeping their sum (largest remainders first)."""
+    fl = np.clip(np.floor(b), lo, hi).astype(int)
+    need = int(round(float(np.sum(b)))) - int(fl.sum())
+    order = np.argsort(-(b - np.floor(b)), kind="stable")
+    for h in order[:max(need, 0)]:
+        fl[h] = min(fl[h] + 1, hi)
+    return fl
+
+
+def entropy_workload(reps):
+    """c3h: per-head key bits from attention entropy ([LCPP] Finding 2: b_h = b_avg +
+    0.25 (H_avg - H_2(h)), and the per-head KV-type request).  The 64K cache with
+    per-head key scales (3, 1, 1, 0.5), so one head attends sharply and one diffusely;
+    H_2 per KV head from 8 calibration queries (kvq_attn_error_ex on the fp16 cache);
+    bits by the rule at an average of 4, rounded keeping the sum; keys of each head
+    coded at its bits (FWHT-256, g128) as head segments, values int4 g128.  Compared
+    with uniform 4-bit keys: attention KL of 16 queries, and one decode step."""
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.get("c3", k_head_scales=(3.0, 1.0, 1.0, 0.5))
+    log(f"generating {w.description} with per-head key scales {w.k_head_scales}")
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    B, L, H, T, D, Hq = w.B, w.L, w.H, w.T, w.D, w.Hq
+    G = Hq // H
+    shape = K.Shape(B, L, H, T, D)
+    kd = torch.from_numpy(Kx.view(np.int16)).to(dev)
+    vd = torch.from_numpy(Vx.view(np.int16)).to(dev)
+    nqc, nqe = 8, 16
+    qc = torch.from_numpy(np.ascontiguousarray(q[:, :, nqe:nqe + nqc]).view(np.int16)).to(dev)
+    qe = torch.from_numpy(np.ascontiguousarray(q[:, :, :nqe]).view(np.int16)).to(dev)
+    # calibration: Renyi-2 entropy of the fp16 attention of each head
+    f16k, f16v = K.packed_from_fp16(kd, shape), K.packed_from_fp16(vd, shape)
+    h2 = torch.empty((B, L, nqc, Hq), dtype=torch.float32, device=dev)
+    web = K.kvq_attn_error_workspace(shape, Hq, nqc)
+    we = torch.empty(web, dtype=torch.uint8, device=dev)
+    K.kvq_attn_error_ex(kd, vd, f16k, f16v, Hq, nqc, qc, None, 0.0, we, web, renyi2=h2)
+    torch.cuda.synchronize()
+    del we
+    h2_head = h2.double().cpu().numpy().reshape(B, L, nqc, H, G).mean(axis=(0, 1, 2, 4))
+    b_avg = 4.0
+    frac = b_avg + 0.25 * (h2_head.mean() - h2_head)
+    bits = _round_keep_sum(frac)
+    vc = K.Codec(K.INT_ABSMAX, 4, 128, 0)
+
+    def quality(kp, vp, k16, v16, qq, hq):
+        kl = torch.empty((B, L, nqe, hq), dtype=torch.float32, device=dev)
+        js = torch.empty_like(kl)
+        sh = kp.shape
+        wb = K.kvq_attn_error_workspace(sh, hq, nqe)
+        wsp = torch.empty(wb, dtype=torch.uint8, device=dev)
+        K.kvq_attn_error_ex(k16, v16, kp, vp, hq, nqe, qq, None, 0.0, wsp, wb, kl=kl, js=js)
+        torch.cuda.synchronize()
+        return kl.double().cpu().numpy(), js.double().cpu().numpy()
+
+    out = torch.empty((B, L, 1, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, L, 1, Hq), dtype=torch.float32, device=dev)
+    q1 = qe[:, :, :1].contiguous()
+    recs = []
+    # uniform 4-bit keys
+    ku = K.alloc_packed(K.Codec(K.INT_ABSMAX, 4, 128, 256), shape, dev)
+    vu = K.alloc_packed(vc, shape, dev)
+    K.kvq_quantize_pack(kd, ku)
+    K.kvq_quantize_pack(vd, vu)
+    klu, jsu = quality(ku, vu, kd, vd, qe, Hq)
+    wsb = K.kvq_decode_attn_workspace(shape, Hq, 1)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    fn = lambda: K.kvq_decode_attn(ku, vu, Hq, 1, q1, None, 0.0, out, lse, ws, wsb)
+    fn()
+    tu = _median_time(torch, fn, reps)
+    recs.append(("K int4 FWHT-256 g128, every head", [4] * H, klu, jsu, tu,
+                 K.kvq_bits_per_value(K.Codec(K.INT_ABSMAX, 4, 128, 256), D)))
+    del ku
+    # entropy-adaptive keys: one segment per head
+    segs, kls, jss = [], np.zeros_like(klu), np.zeros_like(jsu)
+    for h in range(H):
+        sub = K.Shape(B, L, 1, T, D)
+        k16 = kd[:, :, h:h + 1].contiguous()
+        v16 = vd[:, :, h:h + 1].contiguous()
+        kp = K.alloc_packed(K.Codec(K.INT_ABSMAX, int(bits[h]), 128, 256), sub, dev)
+        vp = K.alloc_packed(vc, sub, dev)
+        K.kvq_quantize_pack(k16, kp)
+        K.kvq_quantize_pack(v16, vp)
+        klh, jsh = quality(kp, vp, k16, v16, qe[:, :, :, h * G:(h + 1) * G].contiguous(), G)
+        kls[..., h * G:(h + 1) * G] = klh
+        jss[..., h * G:(h + 1) * G] = jsh
+        segs.append(K.Segment(kp, vp, 0, 0, h))
+    wsb = K.kvq_decode_attn_segments_workspace(segs, L, H, Hq, 1)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    fn = lambda: K.kvq_decode_attn_segments(segs, L, H, T, Hq, 1, q1, None, 0.0, out, lse, ws, wsb)
+    fn()
+    ta = _median_time(torch, fn, reps)
+    kb = sum(K.kvq_bits_per_value(sg.k.codec, D) for sg in segs) / H
+    recs.append(("K bits per head by b_h = 4 + 0.25 (H_avg - H_2(h)), head segments", [int(b) for b in bits], kls,
+                 jss, ta, kb))
+    for name, bh, kl, js, t, kbits in recs:
+        print(json.dumps({
+            "workload": f"c3h: B={B} L={L} H={H} T={T} D={D} Hq={Hq}, per-head key scales {list(w.k_head_scales)}, "
+                        f"V int4 g128",
+            "arm": name, "H2_per_kv_head": [round(float(x), 3) for x in h2_head],
+            "rule_bits": [round(float(x), 3) for x in frac], "key_bits_per_head": bh,
+            "key_bits_per_value": round(kbits, 4),
+            "quality": {"mean_KL": float(kl.mean()), "p99_KL": float(np.quantile(kl, 0.99)),
+                        "mean_KL_per_kv_head": [float(kl[..., h * G:(h + 1) * G].mean()) for h in range(H)],
+                        "mean_JS": float(js.mean()), "queries": nqe},
+            "decode_step_us": round(t * 1e6, 1)}), flush=True)
 
 
 def main():
@@ -386,11 +497,12 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for hardware-counter passes: a known-size copy (the counters' "
                          "calibration), one quantize+pack pair and --decode-queries decode calls")
-    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v", "c3m", "c3a"],
+    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v", "c3m", "c3a", "c3h"],
                     help="c3: the headline line (default); c4/c5: one line per codec arm of those configs; "
                          "c3v: the 64K cache with each value codebook, with attention KL; "
                          "c3m: the 64K cache with a shared key mean, keys coded with and without it; "
-                         "c3a: the 64K cache as decode segments with fp16 anchors, and the append path")
+                         "c3a: the 64K cache as decode segments with fp16 anchors, and the append path; "
+                         "c3h: per-head key bits from attention entropy, as head segments")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions per arm (c4/c5)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -400,6 +512,9 @@ def main():
 
     if args.workload == "c3a":
         anchors_workload(args.reps)
+        return
+    if args.workload == "c3h":
+        entropy_workload(args.reps)
         return
     if args.workload != "c3":
         secondary(args.workload, args.reps)

@@ -244,46 +244,53 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
                               float sm_scale, float* out, float* lse, void* ws,
                               size_t ws_bytes, int32_t path, void* stream);
 
-/* One piece of a logical cache of `layers` x `tokens`: packed K and V (same
- * shape, batch/heads/head_dim equal to the other segments') holding layers
- * [layer0, layer0 + k->shape.layers) and tokens [token0, token0 + k->shape.tokens)
- * of every sequence.  Segments describe decode anchors ([FMAG-6] The winning
- * recipe, Selective-Layer Decode Anchoring: the KV of the first decoded tokens
- * kept at fp16/int8/int4 on chosen layers), fp16 anchor layers ([FMAG-6] Minimal
- * recipe), sliding windows and per-layer codec choices. */
+/* One piece of a logical cache of `layers` x `heads` x `tokens`: packed K and V
+ * (same shape; batch and head_dim equal to the other segments') holding layers
+ * [layer0, layer0 + k->shape.layers), KV heads [head0, head0 + k->shape.heads)
+ * and tokens [token0, token0 + k->shape.tokens) of every sequence.  Segments
+ * describe decode anchors ([FMAG-6] The winning recipe, Selective-Layer Decode
+ * Anchoring: the KV of the first decoded tokens kept at fp16/int8/int4 on chosen
+ * layers), fp16 anchor layers ([FMAG-6] Minimal recipe), sliding windows, and
+ * per-layer and per-head codec choices ([LCPP] the per-head KV-type request: sink
+ * heads at f16 or q8_0, standard heads at q4_0, diffuse heads lower). */
 typedef struct {
   const kvq_packed* k;
   const kvq_packed* v;
   int32_t layer0;
   int32_t token0;
+  int32_t head0;
 } kvq_segment;
 
 /* Bytes of workspace kvq_decode_attn_segments needs (0 for invalid arguments).
  * Its first 65536 bytes are the decode counters (zero before first use, left
  * zero by every call), as for kvq_decode_attn. */
 size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg, int32_t layers,
-                                          int32_t q_heads, int32_t n_q);
+                                          int32_t heads, int32_t q_heads, int32_t n_q);
 
-/* Decode attention over a logical cache [B][layers][H][tokens][D] given as 1..16
- * segments that tile it: for every layer, the segments covering it cover tokens
- * [0, tokens) exactly, without overlap.  q: fp16 [B][layers][n_q][q_heads][D];
+/* Decode attention over a logical cache [B][layers][heads][tokens][D] given as
+ * 1..16 segments that tile it: for every (layer, KV head), the segments covering
+ * it cover tokens [0, tokens) exactly, without overlap.  q_heads is a multiple of
+ * heads (query head j reads KV head j / (q_heads / heads), as for
+ * kvq_decode_attn).  q: fp16 [B][layers][n_q][q_heads][D];
  * kv_len: int32 [B][layers][n_q] over the logical token axis (NULL = all);
  * out/lse as for kvq_decode_attn over the whole logical cache.  Each segment is
  * decoded by the kvq_decode_attn kernels (the MFMA kernel where it applies) and
  * its (out, lse) merged into the running result by log-sum-exp weights; a
  * segment's key mean shifts only its own lse, as the whole cache's would. */
 kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers,
-                                    int32_t tokens, int32_t q_heads, int32_t n_q, const uint16_t* q,
+                                    int32_t heads, int32_t tokens, int32_t q_heads, int32_t n_q,
+                                    const uint16_t* q,
                                     const int32_t* kv_len, float sm_scale, float* out, float* lse,
                                     void* ws, size_t ws_bytes, void* stream);
 
 /* Host only.  Effective bits per cached value of a tiled logical cache: the
  * segments' K/V bits per value (kvq_bits_per_value, averaged over K and V)
- * weighted by the layers x tokens each holds ([FMAG-6] Milestone and Minimal
- * recipe: anchored rows count at their own precision, so anchors kept for the
- * prompt and the first D decoded tokens cost (L + D) rows per anchored layer).
- * Returns a negative value for segments that do not tile layers x tokens. */
-double kvq_effective_bits(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t tokens);
+ * weighted by the layers x heads x tokens each holds ([FMAG-6] Milestone and
+ * Minimal recipe: anchored rows count at their own precision, so anchors kept for
+ * the prompt and the first D decoded tokens cost (L + D) rows per anchored layer).
+ * Returns a negative value for segments that do not tile the cache. */
+double kvq_effective_bits(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,
+                          int32_t tokens);
 
 /* Bytes of workspace kvq_attn_error needs. */
 size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q);

@@ -63,7 +63,7 @@ class kvq_error_outputs(ctypes.Structure):
 
 class kvq_segment(ctypes.Structure):
     _fields_ = [("k", ctypes.POINTER(kvq_packed)), ("v", ctypes.POINTER(kvq_packed)),
-                ("layer0", ctypes.c_int32), ("token0", ctypes.c_int32)]
+                ("layer0", ctypes.c_int32), ("token0", ctypes.c_int32), ("head0", ctypes.c_int32)]
 
 
 def _load():
@@ -89,9 +89,9 @@ def _load():
         "kvq_attn_error_workspace": ([P, I32, I32], SZ),
         "kvq_attn_error": ([P, P, P, P, I32, I32, P, P, F, P, P, P, P, SZ, P], I32),
         "kvq_quantize_pack_tokens": ([P, I32, I32, P, P], I32),
-        "kvq_decode_attn_segments_workspace": ([P, I32, I32, I32, I32], SZ),
-        "kvq_decode_attn_segments": ([P, I32, I32, I32, I32, I32, P, P, F, P, P, P, SZ, P], I32),
-        "kvq_effective_bits": ([P, I32, I32, I32], D),
+        "kvq_decode_attn_segments_workspace": ([P, I32, I32, I32, I32, I32], SZ),
+        "kvq_decode_attn_segments": ([P, I32, I32, I32, I32, I32, I32, P, P, F, P, P, P, SZ, P], I32),
+        "kvq_effective_bits": ([P, I32, I32, I32, I32], D),
         "kvq_attn_error_ex": ([P, P, P, P, I32, I32, P, P, F, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
@@ -236,12 +236,14 @@ def kvq_quantize_pack_tokens(x_fp16, token0: int, n_tokens: int, out: Packed, st
 
 @dataclasses.dataclass
 class Segment:
-    """Packed K and V holding layers [layer0, layer0 + k.shape.layers) and tokens
-    [token0, token0 + k.shape.tokens) of a logical cache."""
+    """Packed K and V holding layers [layer0, layer0 + k.shape.layers), KV heads
+    [head0, head0 + k.shape.heads) and tokens [token0, token0 + k.shape.tokens) of
+    a logical cache."""
     k: Packed
     v: Packed
     layer0: int = 0
     token0: int = 0
+    head0: int = 0
 
 
 def _segments_c(segs):
@@ -250,26 +252,27 @@ def _segments_c(segs):
     for i, sg in enumerate(segs):
         kc, vc = sg.k.c(), sg.v.c()
         keep += [kc, vc]
-        arr[i] = kvq_segment(ctypes.pointer(kc), ctypes.pointer(vc), sg.layer0, sg.token0)
+        arr[i] = kvq_segment(ctypes.pointer(kc), ctypes.pointer(vc), sg.layer0, sg.token0, sg.head0)
     return arr, keep
 
 
-def kvq_decode_attn_segments_workspace(segs, layers: int, q_heads: int, n_q: int) -> int:
+def kvq_decode_attn_segments_workspace(segs, layers: int, heads: int, q_heads: int, n_q: int) -> int:
     arr, _keep = _segments_c(segs)
-    return _lib.kvq_decode_attn_segments_workspace(arr, len(segs), layers, q_heads, n_q)
+    return _lib.kvq_decode_attn_segments_workspace(arr, len(segs), layers, heads, q_heads, n_q)
 
 
-def kvq_decode_attn_segments(segs, layers: int, tokens: int, q_heads: int, n_q: int, q, kv_len, sm_scale: float,
-                             out, lse, ws, ws_bytes: int, stream=None):
+def kvq_decode_attn_segments(segs, layers: int, heads: int, tokens: int, q_heads: int, n_q: int, q, kv_len,
+                             sm_scale: float, out, lse, ws, ws_bytes: int, stream=None):
     arr, _keep = _segments_c(segs)
     _check("kvq_decode_attn_segments",
-           _lib.kvq_decode_attn_segments(arr, len(segs), layers, tokens, q_heads, n_q, _ptr(q), _ptr(kv_len),
-                                         sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+           _lib.kvq_decode_attn_segments(arr, len(segs), layers, heads, tokens, q_heads, n_q, _ptr(q),
+                                         _ptr(kv_len), sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                         _stream(stream)))
 
 
-def kvq_effective_bits(segs, layers: int, tokens: int) -> float:
+def kvq_effective_bits(segs, layers: int, heads: int, tokens: int) -> float:
     arr, _keep = _segments_c(segs)
-    return _lib.kvq_effective_bits(arr, len(segs), layers, tokens)
+    return _lib.kvq_effective_bits(arr, len(segs), layers, heads, tokens)
 
 
 def kvq_dequant(inp: Packed, x_hat, stream=None):

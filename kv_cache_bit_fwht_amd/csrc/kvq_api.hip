@@ -365,37 +365,46 @@ static kvq_status check_attn(const kvq_packed* k, const kvq_packed* v, int32_t q
   return KVQ_OK;
 }
 
-// Segments of a logical layers x tokens cache: each valid on its own, all with the same
-// batch, heads and head_dim, inside the cache, and tiling every layer's tokens exactly.
-static kvq_status check_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t tokens,
-                                 int32_t q_heads, int32_t n_q) {
-  if (!segs || n_seg < 1 || n_seg > 16 || layers < 1 || tokens < 1) return KVQ_ERR_ARG;
+// Segments of a logical layers x heads x tokens cache: each valid on its own (with its
+// own KV-head count, q_heads / heads query heads per KV head), all with the same batch
+// and head_dim, inside the cache, and tiling every (layer, head)'s tokens exactly.
+static kvq_status check_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,
+                                 int32_t tokens, int32_t q_heads, int32_t n_q) {
+  if (!segs || n_seg < 1 || n_seg > kMaxSegments || layers < 1 || heads < 1 || tokens < 1) return KVQ_ERR_ARG;
+  if (q_heads < 1 || q_heads % heads != 0) return KVQ_ERR_UNSUPPORTED;
+  const int G = q_heads / heads;
   const kvq_packed* k0 = segs[0].k;
   if (!k0) return KVQ_ERR_ARG;
   for (int i = 0; i < n_seg; ++i) {
     const kvq_segment& sg = segs[i];
     if (!sg.k || !sg.v) return KVQ_ERR_ARG;
-    kvq_status st = check_kv(sg.k, sg.v, q_heads, n_q);
-    if (st != KVQ_OK) return st;
     const kvq_shape& sh = sg.k->shape;
-    if (sh.batch != k0->shape.batch || sh.heads != k0->shape.heads || sh.head_dim != k0->shape.head_dim)
-      return KVQ_ERR_ARG;
-    if (sh.tokens < 1 || sg.layer0 < 0 || sg.token0 < 0 || (long long)sg.layer0 + sh.layers > layers ||
+    if (sh.heads < 1) return KVQ_ERR_ARG;
+    kvq_status st = check_kv(sg.k, sg.v, sh.heads * G, n_q);
+    if (st != KVQ_OK) return st;
+    if (sh.batch != k0->shape.batch || sh.head_dim != k0->shape.head_dim) return KVQ_ERR_ARG;
+    if (sh.tokens < 1 || sg.layer0 < 0 || sg.token0 < 0 || sg.head0 < 0 ||
+        (long long)sg.layer0 + sh.layers > layers || (long long)sg.head0 + sh.heads > heads ||
         (long long)sg.token0 + sh.tokens > tokens)
       return KVQ_ERR_ARG;
   }
   for (int l = 0; l < layers; ++l) {
-    std::vector<std::pair<int, int>> r;
-    for (int i = 0; i < n_seg; ++i)
-      if (l >= segs[i].layer0 && l < segs[i].layer0 + segs[i].k->shape.layers)
-        r.emplace_back(segs[i].token0, segs[i].k->shape.tokens);
-    std::sort(r.begin(), r.end());
-    long long next = 0;
-    for (const auto& [t0, n] : r) {
-      if (t0 != next) return KVQ_ERR_ARG;
-      next = (long long)t0 + n;
+    for (int h = 0; h < heads; ++h) {
+      std::vector<std::pair<int, int>> r;
+      for (int i = 0; i < n_seg; ++i) {
+        const kvq_shape& sh = segs[i].k->shape;
+        if (l >= segs[i].layer0 && l < segs[i].layer0 + sh.layers && h >= segs[i].head0 &&
+            h < segs[i].head0 + sh.heads)
+          r.emplace_back(segs[i].token0, sh.tokens);
+      }
+      std::sort(r.begin(), r.end());
+      long long next = 0;
+      for (const auto& [t0, n] : r) {
+        if (t0 != next) return KVQ_ERR_ARG;
+        next = (long long)t0 + n;
+      }
+      if (next != tokens) return KVQ_ERR_ARG;
     }
-    if (next != tokens) return KVQ_ERR_ARG;
   }
   return KVQ_OK;
 }
@@ -414,25 +423,29 @@ struct SegPlan {
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static SegPlan seg_plan(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t q_heads, int32_t n_q) {
+static SegPlan seg_plan(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads, int32_t q_heads,
+                        int32_t n_q) {
   SegPlan p{};
   const kvq_shape& s0 = segs[0].k->shape;
+  const int G = q_heads / heads;
   std::vector<char> touched(layers, 0), direct_layer(layers, 0);
   size_t dec = 0, q = 0, kvl = 0;
   for (int i = 0; i < n_seg; ++i) {
     const kvq_shape& sh = segs[i].k->shape;
     const int l0 = segs[i].layer0, l1 = l0 + sh.layers;
     const bool inside = l0 >= 0 && l1 <= layers;
-    bool fresh = inside && s0.batch == 1;
+    // direct: batch 1, every head, and no earlier segment on these layers
+    bool fresh = inside && s0.batch == 1 && sh.heads == heads && segs[i].head0 == 0;
     for (int l = l0; fresh && l < l1; ++l) fresh = !touched[l];
     p.direct[i] = fresh;
     for (int l = std::max(l0, 0); l < std::min(l1, (int)layers); ++l) {
       touched[l] = 1;
       if (fresh) direct_layer[l] = 1;
     }
+    const int hq = sh.heads * G;
     const size_t rows = (size_t)sh.batch * sh.layers * n_q;
-    dec = std::max(dec, decode_ws_bytes(sh, q_heads, n_q));
-    q = std::max(q, rows * q_heads * sh.head_dim * 2);
+    dec = std::max(dec, decode_ws_bytes(sh, hq, n_q));
+    q = std::max(q, rows * hq * sh.head_dim * 2);
     kvl = std::max(kvl, rows * 4);
   }
   for (int l = 0; l < layers; ++l) p.need_init |= !direct_layer[l];
@@ -444,7 +457,7 @@ static SegPlan seg_plan(const kvq_segment* segs, int32_t n_seg, int32_t layers, 
   for (int i = 0; i < n_seg; ++i) {
     if (p.direct[i]) continue;
     const kvq_shape& sh = segs[i].k->shape;
-    const size_t rows = (size_t)sh.batch * sh.layers * n_q * q_heads;
+    const size_t rows = (size_t)sh.batch * sh.layers * n_q * sh.heads * G;
     p.out_off[i] = off;
     off += round256(rows * sh.head_dim * 4);
     p.lse_off[i] = off;
@@ -505,57 +518,64 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
   return kvq_decode_attn_ex(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes, 0, stream);
 }
 
-size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg, int32_t layers,
+size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,
                                           int32_t q_heads, int32_t n_q) {
-  if (!segs || n_seg < 1 || n_seg > 16 || layers < 1) return 0;
+  if (!segs || n_seg < 1 || n_seg > kMaxSegments || layers < 1 || heads < 1 || q_heads < 1 || q_heads % heads)
+    return 0;
+  const int G = q_heads / heads;
   for (int i = 0; i < n_seg; ++i) {
-    if (!segs[i].k || !segs[i].v) return 0;
-    if (check_kv(segs[i].k, segs[i].v, q_heads, n_q) != KVQ_OK) return 0;
+    if (!segs[i].k || !segs[i].v || segs[i].k->shape.heads < 1) return 0;
+    if (check_kv(segs[i].k, segs[i].v, segs[i].k->shape.heads * G, n_q) != KVQ_OK) return 0;
   }
-  return seg_plan(segs, n_seg, layers, q_heads, n_q).total;
+  return seg_plan(segs, n_seg, layers, heads, q_heads, n_q).total;
 }
 
-kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t tokens,
-                                    int32_t q_heads, int32_t n_q, const uint16_t* q, const int32_t* kv_len,
-                                    float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
-                                    void* stream) {
-  kvq_status st = check_segments(segs, n_seg, layers, tokens, q_heads, n_q);
+kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,
+                                    int32_t tokens, int32_t q_heads, int32_t n_q, const uint16_t* q,
+                                    const int32_t* kv_len, float sm_scale, float* out, float* lse, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  kvq_status st = check_segments(segs, n_seg, layers, heads, tokens, q_heads, n_q);
   if (st != KVQ_OK) return st;
   if (!q || !out) return KVQ_ERR_ARG;
   if (!aligned16(q) || !aligned16(out) || (lse && !aligned16(lse)) || (kv_len && !aligned16(kv_len)))
     return KVQ_ERR_ALIGN;
   if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
-  const SegPlan pl = seg_plan(segs, n_seg, layers, q_heads, n_q);
+  const SegPlan pl = seg_plan(segs, n_seg, layers, heads, q_heads, n_q);
   if (ws_bytes < pl.total || !ws) return KVQ_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVQ_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   char* w = static_cast<char*>(ws);
-  const int B = segs[0].k->shape.batch, D = segs[0].k->shape.head_dim;
+  const int B = segs[0].k->shape.batch, D = segs[0].k->shape.head_dim, G = q_heads / heads;
   const size_t rpl = (size_t)n_q * q_heads;                     // output rows per (sequence, layer)
   float* lacc = lse ? lse : reinterpret_cast<float*>(w + pl.lacc);
   hipError_t e = hipSuccess;
   if (pl.need_init) e = launch_seg_init(out, lacc, (long long)B * layers * rpl, D, s);
-  int nm = 0, ml0[kMaxSegments], mls[kMaxSegments];
+  int nm = 0, ml0[kMaxSegments], mls[kMaxSegments], mj0[kMaxSegments], mhq[kMaxSegments];
   float* mos[kMaxSegments];
   float* mlse[kMaxSegments];
   for (int i = 0; i < n_seg && e == hipSuccess; ++i) {
     const kvq_segment& sg = segs[i];
     const kvq_shape& sh = sg.k->shape;
+    const int hq = sh.heads * G, j0 = sg.head0 * G;              // the segment's query heads
+    const bool all_heads = hq == q_heads;
     const uint16_t* qs = q;
     const int32_t* kvls = kv_len;
     uint16_t* qbuf = nullptr;
     int32_t* kbuf = nullptr;
-    if (B == 1) {
+    if (B == 1 && all_heads) {
       qs = q + (size_t)sg.layer0 * rpl * D;                     // contiguous layer slice
       if (kv_len) kvls = kv_len + (size_t)sg.layer0 * n_q;
       if (kv_len && sg.token0 != 0) kbuf = reinterpret_cast<int32_t*>(w + pl.kvl);
     } else {
       qbuf = reinterpret_cast<uint16_t*>(w + pl.q);
-      if (kv_len) kbuf = reinterpret_cast<int32_t*>(w + pl.kvl);
+      if (kv_len) {
+        if (B == 1 && sg.token0 == 0) kvls = kv_len + (size_t)sg.layer0 * n_q;
+        else kbuf = reinterpret_cast<int32_t*>(w + pl.kvl);
+      }
     }
     if (qbuf || kbuf)
-      e = launch_seg_prepare(q, kv_len, qbuf, kbuf, B, layers, sh.layers, sg.layer0, n_q, q_heads, D, sg.token0,
-                             sh.tokens, s);
+      e = launch_seg_prepare(q, kv_len, qbuf, kbuf, B, layers, sh.layers, sg.layer0, n_q, q_heads, j0, hq, D,
+                             sg.token0, sh.tokens, s);
     if (qbuf) qs = qbuf;
     if (kbuf) kvls = kbuf;
     // (keys [0, kv_len) clamp to [0, tokens] inside the decode, so a segment at token 0
@@ -570,30 +590,31 @@ kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int3
       ls = reinterpret_cast<float*>(w + pl.lse_off[i]);
       ml0[nm] = sg.layer0;
       mls[nm] = sh.layers;
+      mj0[nm] = j0;
+      mhq[nm] = hq;
       mos[nm] = os;
       mlse[nm] = ls;
       ++nm;
     }
     if (e == hipSuccess)
-      e = decode_packed(sg.k, sg.v, q_heads, n_q, qs, kvls, sm_scale, os, ls, w, w + pl.dec, pl.dec_bytes, 0, s);
+      e = decode_packed(sg.k, sg.v, hq, n_q, qs, kvls, sm_scale, os, ls, w, w + pl.dec, pl.dec_bytes, 0, s);
   }
-  if (e == hipSuccess) e = launch_seg_merge(nm, ml0, mls, mos, mlse, out, lacc, B, layers, (int)rpl, D, s);
+  if (e == hipSuccess)
+    e = launch_seg_merge(nm, ml0, mls, mj0, mhq, mos, mlse, out, lacc, B, layers, n_q, q_heads, D, s);
   return hip_status(e);
 }
 
-double kvq_effective_bits(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t tokens) {
-  int32_t q_heads = 0;
-  if (segs && n_seg >= 1 && segs[0].k) q_heads = segs[0].k->shape.heads;
-  if (check_segments(segs, n_seg, layers, tokens, q_heads, 1) != KVQ_OK) return -1.0;
+double kvq_effective_bits(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads, int32_t tokens) {
+  if (check_segments(segs, n_seg, layers, heads, tokens, heads, 1) != KVQ_OK) return -1.0;
   double tot = 0.0;
   for (int i = 0; i < n_seg; ++i) {
     const kvq_packed& k = *segs[i].k;
     const kvq_packed& v = *segs[i].v;
     const double b = 0.5 * (kvq_bits_per_value(&k.codec, k.shape.head_dim) +
                             kvq_bits_per_value(&v.codec, v.shape.head_dim));
-    tot += b * k.shape.layers * k.shape.tokens;
+    tot += b * k.shape.layers * k.shape.heads * k.shape.tokens;
   }
-  return tot / ((double)layers * tokens);
+  return tot / ((double)layers * heads * tokens);
 }
 
 size_t kvq_attn_error_workspace(const kvq_shape* kv, int32_t q_heads, int32_t n_q) {

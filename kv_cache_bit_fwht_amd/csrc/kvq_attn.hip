@@ -933,7 +933,23 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(CArgs a, float* out, fl
   float o = 0.0f, o2 = 0.0f;
   if (tid < D) {
     double acc = 0.0, acc2 = 0.0;
-    for (int s = 0; s < a.S; ++s) {
+    int s = 0;
+    // eight splits' loads in flight at a time; the sums keep split order
+    for (; s + 8 <= a.S; s += 8) {
+      float v[8], v2[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* p = src + (size_t)(s + u) * P;
+        v[u] = p[tid];
+        if (ERR) v2[u] = p[D + tid];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc += (double)v[u] * wq[s + u];
+        if (ERR) acc2 += (double)v2[u] * w2[s + u];
+      }
+    }
+    for (; s < a.S; ++s) {
       const float* p = src + (size_t)s * P;
       acc += (double)p[tid] * wq[s];
       if (ERR) acc2 += (double)p[D + tid] * w2[s];
@@ -1176,7 +1192,9 @@ static int decode_wave_splits(const kvq_shape& s, int Hq, int n_q) {
   const long long max_s = std::max(1, s.tokens / (4 * wave_rows_per_step(s.head_dim)));
   S = std::min(S, max_s);
   S = (S + 3) / 4 * 4;
-  return (int)std::max(4LL, std::min(S, (long long)kMaxSplits));
+  // at most 512 splits: past that the combine's per-row merge costs more than the extra
+  // wavefronts gain (a one-head cache still gets 4096 wavefronts)
+  return (int)std::max(4LL, std::min(S, 512LL));
 }
 
 // Workspace of kvq_decode_attn: split partials of whichever kernel runs.
@@ -1261,6 +1279,10 @@ static hipError_t dispatch_wave(const AArgs& a, long long R, hipStream_t st) {
     return launch_wave<KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 3>(a, R, st);
   if (is(kc, kb, KVQ_INT_ABSMAX, 3) && is(vc, vb, KVQ_INT_ABSMAX, 2))
     return launch_wave<KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 2>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 3) && is(vc, vb, KVQ_INT_ABSMAX, 4))
+    return launch_wave<KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 4>(a, R, st);
+  if (is(kc, kb, KVQ_INT_ABSMAX, 5) && is(vc, vb, KVQ_INT_ABSMAX, 4))
+    return launch_wave<KVQ_INT_ABSMAX, 5, KVQ_INT_ABSMAX, 4>(a, R, st);
   if (is(kc, kb, KVQ_INT_MINMAX, 4) && is(vc, vb, KVQ_INT_MINMAX, 4))
     return launch_wave<KVQ_INT_MINMAX, 4, KVQ_INT_MINMAX, 4>(a, R, st);
   if (is(kc, kb, KVQ_INT_MINMAX, 3) && is(vc, vb, KVQ_INT_MINMAX, 3))
@@ -1430,14 +1452,17 @@ namespace kvq {
 // A segment holds layers [l0, l0 + Ls) and tokens [t0, t0 + Ts) of a logical cache; it is
 // decoded on its own and its (out, lse) merged into the logical result.
 
-// Query rows of the segment's layers, copied out of q [B][L][n_q][Hq][D] (16-byte units).
-__global__ void k_seg_gather_q(const uint4* __restrict__ src, uint4* __restrict__ dst, long long per_layer, int L,
-                               int Ls, int l0, long long total) {
+// Query rows of the segment's layers and query heads [j0, j0 + hq), copied out of
+// q [B][L][n_q][Hq][D] into [B][Ls][n_q][hq][D] (16-byte units; D8 = D / 8).
+__global__ void k_seg_gather_q(const uint4* __restrict__ src, uint4* __restrict__ dst, int L, int Ls, int l0,
+                               int n_q, int Hq, int j0, int hq, int D8, long long total) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
-  const long long bl = i / per_layer, e = i - bl * per_layer;
+  const long long per = (long long)hq * D8;
+  const long long row = i / per, e = i - row * per;         // row = (b * Ls + l) * n_q + qi
+  const long long qi = row % n_q, bl = row / n_q;
   const long long b = bl / Ls, l = bl - b * Ls;
-  dst[i] = src[(b * L + l0 + l) * per_layer + e];
+  dst[i] = src[(((b * L + l0 + l) * n_q + qi) * Hq + j0) * D8 + e];
 }
 
 // Keys attended inside the segment: clamp(kv_len - t0, 0, Ts) for its layers.
@@ -1463,23 +1488,25 @@ __global__ void k_seg_init(float* __restrict__ out, float* __restrict__ lse, lon
 // wavefront per logical row.
 struct SegMergeArgs {
   int n;
-  int l0[kMaxSegments], ls[kMaxSegments];
+  int l0[kMaxSegments], ls[kMaxSegments], j0[kMaxSegments], hq[kMaxSegments];
   const float* os[kMaxSegments];
   const float* lsp[kMaxSegments];
 };
 
 __global__ __launch_bounds__(kBlock) void k_seg_merge(SegMergeArgs sa, float* __restrict__ out, float* __restrict__ lse,
-                                                      int L, int rpl, int D, long long rows) {
+                                                      int L, int n_q, int Hq, int D, long long rows) {
   const long long g = (long long)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (g >= rows) return;                                   // uniform per wavefront
-  const long long bl = g / rpl, k = g - bl * rpl;
+  const int j = (int)(g % Hq);                             // g = ((b * L + l) * n_q + qi) * Hq + j
+  const long long t = g / Hq;
+  const long long qi = t % n_q, bl = t / n_q;
   const long long b = bl / L;
   const int l = (int)(bl - b * L);
   float la = lse[g];
   for (int i = 0; i < sa.n; ++i) {
-    if (l < sa.l0[i] || l >= sa.l0[i] + sa.ls[i]) continue;
-    const long long r = (b * sa.ls[i] + (l - sa.l0[i])) * rpl + k;    // the segment's row
+    if (l < sa.l0[i] || l >= sa.l0[i] + sa.ls[i] || j < sa.j0[i] || j >= sa.j0[i] + sa.hq[i]) continue;
+    const long long r = ((b * sa.ls[i] + (l - sa.l0[i])) * n_q + qi) * sa.hq[i] + (j - sa.j0[i]);   // its row
     const float lb = sa.lsp[i][r];
     const float m = __builtin_fmaxf(la, lb);
     if (m == -INFINITY) continue;                          // no keys on either side
@@ -1501,12 +1528,11 @@ hipError_t launch_seg_init(float* out, float* lse, long long rows, int D, hipStr
 }
 
 hipError_t launch_seg_prepare(const uint16_t* q, const int32_t* kvl, uint16_t* qs, int32_t* kvls, int B, int L,
-                              int Ls, int l0, int n_q, int Hq, int D, int t0, int Ts, hipStream_t st) {
+                              int Ls, int l0, int n_q, int Hq, int j0, int hq, int D, int t0, int Ts, hipStream_t st) {
   if (qs) {
-    const long long per_layer = (long long)n_q * Hq * D / 8;
-    const long long tq = (long long)B * Ls * per_layer;
+    const long long tq = (long long)B * Ls * n_q * hq * (D / 8);
     k_seg_gather_q<<<(unsigned)((tq + kBlock - 1) / kBlock), kBlock, 0, st>>>(
-        reinterpret_cast<const uint4*>(q), reinterpret_cast<uint4*>(qs), per_layer, L, Ls, l0, tq);
+        reinterpret_cast<const uint4*>(q), reinterpret_cast<uint4*>(qs), L, Ls, l0, n_q, Hq, j0, hq, D / 8, tq);
   }
   if (kvls) {
     const long long tk = (long long)B * Ls * n_q;
@@ -1515,20 +1541,24 @@ hipError_t launch_seg_prepare(const uint16_t* q, const int32_t* kvl, uint16_t* q
   return hipGetLastError();
 }
 
-hipError_t launch_seg_merge(int n, const int* l0, const int* ls, float* const* os, float* const* lsp, float* out,
-                            float* lse, int B, int L, int rpl, int D, hipStream_t st) {
+hipError_t launch_seg_merge(int n, const int* l0, const int* ls, const int* j0, const int* hq, float* const* os,
+                            float* const* lsp, float* out, float* lse, int B, int L, int n_q, int Hq, int D,
+                            hipStream_t st) {
   if (n == 0) return hipSuccess;
   SegMergeArgs sa{};
   sa.n = n;
   for (int i = 0; i < n; ++i) {
     sa.l0[i] = l0[i];
     sa.ls[i] = ls[i];
+    sa.j0[i] = j0[i];
+    sa.hq[i] = hq[i];
     sa.os[i] = os[i];
     sa.lsp[i] = lsp[i];
   }
-  const long long rows = (long long)B * L * rpl;
+  const long long rows = (long long)B * L * n_q * Hq;
   if (rows == 0) return hipSuccess;
-  k_seg_merge<<<(unsigned)((rows + kBlock / 64 - 1) / (kBlock / 64)), kBlock, 0, st>>>(sa, out, lse, L, rpl, D, rows);
+  k_seg_merge<<<(unsigned)((rows + kBlock / 64 - 1) / (kBlock / 64)), kBlock, 0, st>>>(sa, out, lse, L, n_q, Hq, D,
+                                                                                       rows);
   return hipGetLastError();
 }
 

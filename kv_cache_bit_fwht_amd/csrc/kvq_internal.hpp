@@ -199,9 +199,10 @@ hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st);
 hipError_t launch_lse_mean(const AttnProblem& pr, hipStream_t st);
 hipError_t launch_seg_init(float* out, float* lse, long long rows, int D, hipStream_t st);
 hipError_t launch_seg_prepare(const uint16_t* q, const int32_t* kvl, uint16_t* qs, int32_t* kvls, int B, int L,
-                              int Ls, int l0, int n_q, int Hq, int D, int t0, int Ts, hipStream_t st);
-hipError_t launch_seg_merge(int n, const int* l0, const int* ls, float* const* os, float* const* lsp, float* out,
-                            float* lse, int B, int L, int rpl, int D, hipStream_t st);
+                              int Ls, int l0, int n_q, int Hq, int j0, int hq, int D, int t0, int Ts, hipStream_t st);
+hipError_t launch_seg_merge(int n, const int* l0, const int* ls, const int* j0, const int* hq, float* const* os,
+                            float* const* lsp, float* out, float* lse, int B, int L, int n_q, int Hq, int D,
+                            hipStream_t st);
 bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st);
 size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q);

@@ -12,6 +12,8 @@ head_dim 64, tending to 6 as head_dim grows.
 """
 from __future__ import annotations
 
+import numpy as np
+
 from .codec import FP16, INT_MINMAX, RFFT_CART, RFFT_POLAR, Codec
 
 
@@ -43,23 +45,24 @@ def rfft_payload_bits_per_value(mag_bits: int, phase_bits: int, D: int) -> float
     return (mag_bits + phase_bits) * (D // 2 + 1) / D
 
 
-def tiles(segments, layers: int, tokens: int) -> bool:
-    """True when the segments (layer0, n_layers, token0, n_tokens) cover every
-    (layer, token) of a layers x tokens cache exactly once."""
-    cover = [[0] * tokens for _ in range(layers)]
-    for (l0, nl, t0, nt) in segments:
-        if nl < 1 or nt < 1 or l0 < 0 or t0 < 0 or l0 + nl > layers or t0 + nt > tokens:
+def tiles(segments, layers: int, tokens: int, heads: int = 1) -> bool:
+    """True when the segments (layer0, n_layers, token0, n_tokens[, head0, n_heads])
+    cover every (layer, head, token) of a layers x heads x tokens cache exactly
+    once (a segment without a head range holds every head)."""
+    cover = np.zeros((layers, heads, tokens), dtype=np.int64)
+    for sg in segments:
+        l0, nl, t0, nt = sg[:4]
+        h0, nh = (sg[4], sg[5]) if len(sg) > 4 else (0, heads)
+        if min(nl, nt, nh) < 1 or min(l0, t0, h0) < 0 or l0 + nl > layers or t0 + nt > tokens or h0 + nh > heads:
             return False
-        for l in range(l0, l0 + nl):
-            for t in range(t0, t0 + nt):
-                cover[l][t] += 1
-    return all(c == 1 for row in cover for c in row)
+        cover[l0:l0 + nl, h0:h0 + nh, t0:t0 + nt] += 1
+    return bool(np.all(cover == 1))
 
 
-def effective_bits(segments, layers: int, tokens: int, D: int) -> float:
+def effective_bits(segments, layers: int, tokens: int, D: int, heads: int = 1) -> float:
     """Bits per cached value of a cache tiled by segments (k_codec, v_codec,
-    layer0, n_layers, token0, n_tokens): each segment's K/V mean bits per value
-    weighted by the layers x tokens it holds.
+    layer0, n_layers, token0, n_tokens[, head0, n_heads]): each segment's K/V mean
+    bits per value weighted by the layers x heads x tokens it holds.
 
     [FMAG-6, Milestone / Minimal recipe / Best results]: anchored rows count at
     their own precision in the "effective bits"; decode anchors kept for the
@@ -67,8 +70,10 @@ def effective_bits(segments, layers: int, tokens: int, D: int) -> float:
     anchored layer, so the figure tends to the anchor precision as the prompt
     grows, while a single fp16 anchor layer adds (16 - b) / n_layers.
     """
-    assert tiles([(l0, nl, t0, nt) for (_, _, l0, nl, t0, nt) in segments], layers, tokens)
+    assert tiles([sg[2:] for sg in segments], layers, tokens, heads)
     tot = 0.0
-    for (kc, vc, l0, nl, t0, nt) in segments:
-        tot += (bits_per_value(kc, D) + bits_per_value(vc, D)) / 2.0 * nl * nt
-    return tot / (layers * tokens)
+    for sg in segments:
+        kc, vc, l0, nl, t0, nt = sg[:6]
+        nh = sg[7] if len(sg) > 6 else heads
+        tot += (bits_per_value(kc, D) + bits_per_value(vc, D)) / 2.0 * nl * nt * nh
+    return tot / (layers * tokens * heads)

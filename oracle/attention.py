@@ -210,14 +210,16 @@ def attn_error(q16, K16, V16, Kd, Vd, kv_len=None, sm_scale=0.0, units=None):
 
 def assemble_segments(segments, B: int, L: int, H: int, T: int, D: int):
     """The logical [B][L][H][T][D] cache from dequantised segments (Kd_s, Vd_s,
-    layer0, token0), each [B][L_s][H][T_s][D]: every segment placed at its
-    layers and tokens.  Decoding over segments is, by definition, decoding over
-    this assembled cache."""
+    layer0, token0[, head0]), each [B][L_s][H_s][T_s][D]: every segment placed at
+    its layers, heads and tokens.  Decoding over segments is, by definition,
+    decoding over this assembled cache."""
     Kd = np.full((B, L, H, T, D), np.nan, dtype=np.float32)
     Vd = np.full((B, L, H, T, D), np.nan, dtype=np.float32)
-    for (ks, vs, l0, t0) in segments:
-        nl, nt = ks.shape[1], ks.shape[3]
-        Kd[:, l0:l0 + nl, :, t0:t0 + nt] = ks
-        Vd[:, l0:l0 + nl, :, t0:t0 + nt] = vs
+    for sg in segments:
+        ks, vs, l0, t0 = sg[:4]
+        h0 = sg[4] if len(sg) > 4 else 0
+        nl, nh, nt = ks.shape[1], ks.shape[2], ks.shape[3]
+        Kd[:, l0:l0 + nl, h0:h0 + nh, t0:t0 + nt] = ks
+        Vd[:, l0:l0 + nl, h0:h0 + nh, t0:t0 + nt] = vs
     assert not np.isnan(Kd).any() and not np.isnan(Vd).any(), "segments do not cover the cache"
     return Kd, Vd

@@ -50,6 +50,7 @@ class Workload:
     causal_inclusive: bool        # keys [0, p] (True) or [0, p) (False)
     description: str
     k_mean_share: float = 0.0     # share of expected key energy in a shared per-(layer, head) mean
+    k_head_scales: tuple | None = None   # per KV head key multipliers (head h uses [h % len]); None: 1
 
     def with_sizes(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -145,6 +146,8 @@ def gen_unit(w: Workload, b: int, l: int, h: int, tensor: str) -> np.ndarray:
         ch = _outlier_channels(w, l, h)
         if ch.size:
             x[:, ch] *= np.float32(w.outlier_mult)
+        if w.k_head_scales is not None:
+            x *= np.float32(w.k_head_scales[h % len(w.k_head_scales)])
         if w.k_mean_share > 0.0:
             x += _shared_key_mean(w, l, h, ch.size)[None, :]
         if w.rope:

@@ -314,7 +314,7 @@ def test_effective_bits_match_the_oracle(K):
     of four layers, against the oracle's accounting."""
     L = K._lib
     arr, keep = _segs(K, [(F16, F16, (1, 1, 4, 100, 128), 0, 0), (NF4, I4, (1, 25, 4, 100, 128), 1, 0)])
-    e = L.kvq_effective_bits(arr, 2, 26, 100)
+    e = L.kvq_effective_bits(arr, 2, 26, 4, 100)
     ref = O.effective_bits([(O.Codec(O.FP16), O.Codec(O.FP16), 0, 1, 0, 100),
                             (O.Codec(O.NF4, 4, 64), O.Codec(O.INT_ABSMAX, 4, 64), 1, 25, 0, 100)], 26, 100, 128)
     assert e == pytest.approx(ref, abs=1e-12) and round(e, 2) == 4.70
@@ -324,7 +324,7 @@ def test_effective_bits_match_the_oracle(K):
     ref = O.effective_bits([(O.Codec(O.FP16), O.Codec(O.FP16), 0, 2, 0, 80),
                             (O.Codec(O.NF4, 4, 64), O.Codec(O.INT_ABSMAX, 4, 64), 0, 2, 80, 176),
                             (O.Codec(O.NF4, 4, 64), O.Codec(O.INT_ABSMAX, 4, 64), 2, 2, 0, 256)], 4, 256, 128)
-    assert L.kvq_effective_bits(arr, 3, 4, 256) == pytest.approx(ref, abs=1e-12)
+    assert L.kvq_effective_bits(arr, 3, 4, 4, 256) == pytest.approx(ref, abs=1e-12)
 
 
 @pytest.mark.parametrize("case", ["gap", "overlap", "uncovered_layer", "past_end", "batch_mismatch", "zero_segments",
@@ -351,22 +351,23 @@ def test_segments_reject_bad_tilings(K, case):
         parts = [(I4, I4, (1, 2, 4, 4, 128), 0, 4 * i) for i in range(17)]
         n, tokens = 17, 68
     arr, keep = _segs(K, parts)
-    assert L.kvq_effective_bits(arr, n, layers, tokens) < 0
-    st = L.kvq_decode_attn_segments(arr, n, layers, tokens, 16, 1, FAKE, None, 0.0, FAKE, None, FAKE, 1 << 30, None)
+    assert L.kvq_effective_bits(arr, n, layers, 4, tokens) < 0
+    st = L.kvq_decode_attn_segments(arr, n, layers, 4, tokens, 16, 1, FAKE, None, 0.0, FAKE, None, FAKE, 1 << 30,
+                                    None)
     assert st == ERR_ARG
 
 
 def test_segments_validate_before_launching(K):
     L = K._lib
     arr, keep = _segs(K, [(I4, I4, (1, 2, 4, 64, 128), 0, 0)])
-    need = L.kvq_decode_attn_segments_workspace(arr, 1, 2, 16, 1)
+    need = L.kvq_decode_attn_segments_workspace(arr, 1, 2, 4, 16, 1)
     assert need > 65536
     args = dict(q=FAKE, out=FAKE, ws=FAKE, wsb=need)
 
     def call(**kw):
         a = dict(args, **kw)
-        return L.kvq_decode_attn_segments(arr, 1, 2, 64, 16, 1, a["q"], None, 0.0, a["out"], None, a["ws"], a["wsb"],
-                                          None)
+        return L.kvq_decode_attn_segments(arr, 1, 2, 4, 64, 16, 1, a["q"], None, 0.0, a["out"], None, a["ws"],
+                                          a["wsb"], None)
     assert call(wsb=need - 1) == ERR_WORKSPACE
     assert call(ws=None) == ERR_WORKSPACE
     assert call(q=None) == ERR_ARG
@@ -381,3 +382,16 @@ def test_append_validates_before_launching(K):
     assert L.kvq_quantize_pack_tokens(FAKE, 0, 0, ctypes.byref(p), None) == ERR_ARG
     assert L.kvq_quantize_pack_tokens(None, 0, 1, ctypes.byref(p), None) == ERR_ARG
     assert L.kvq_quantize_pack_tokens(FAKE_ODD, 0, 1, ctypes.byref(p), None) == ERR_ALIGN
+
+
+def test_segments_reject_a_missing_head(K):
+    L = K._lib
+    parts = [(I4, I4, (1, 2, 1, 64, 128), 0, 0), (I4, I4, (1, 2, 2, 64, 128), 0, 0)]
+    arr, keep = _segs(K, parts)
+    arr[1].head0 = 2                                       # head 1 of 4 uncovered, head 3 too
+    assert L.kvq_effective_bits(arr, 2, 2, 4, 64) < 0
+    arr[1].head0 = 1
+    parts.append((I4, I4, (1, 2, 1, 64, 128), 0, 0))
+    arr2, keep2 = _segs(K, parts)
+    arr2[1].head0, arr2[2].head0 = 1, 3
+    assert L.kvq_effective_bits(arr2, 3, 2, 4, 64) == pytest.approx(4.25)

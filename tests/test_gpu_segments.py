@@ -84,23 +84,25 @@ def _gpu_seg(K, x, codec, mean=None):
 
 
 def _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg=None):
-    """layout: list of (kcodec, vcodec, layer0, n_layers, token0, n_tokens)."""
+    """layout: list of (kcodec, vcodec, layer0, n_layers, token0, n_tokens[, head0, n_heads])."""
     import torch
     B, L, H, T, D = Kx.shape
     nq, Hq = q.shape[2], q.shape[3]
     segs, ref = [], []
-    for i, (kc, vc, l0, nl, t0, nt) in enumerate(layout):
-        ks = np.ascontiguousarray(Kx[:, l0:l0 + nl, :, t0:t0 + nt])
-        vs = np.ascontiguousarray(Vx[:, l0:l0 + nl, :, t0:t0 + nt])
+    for i, sg in enumerate(layout):
+        kc, vc, l0, nl, t0, nt = sg[:6]
+        h0, nh = (sg[6], sg[7]) if len(sg) > 6 else (0, H)
+        ks = np.ascontiguousarray(Kx[:, l0:l0 + nl, h0:h0 + nh, t0:t0 + nt])
+        vs = np.ascontiguousarray(Vx[:, l0:l0 + nl, h0:h0 + nh, t0:t0 + nt])
         mean = O.key_mean(ks) if i == mean_seg else None
-        segs.append(K.Segment(_gpu_seg(K, ks, kc, mean), _gpu_seg(K, vs, vc), l0, t0))
-        ref.append((_oracle_seg(K, ks, kc, mean), _oracle_seg(K, vs, vc), l0, t0))
+        segs.append(K.Segment(_gpu_seg(K, ks, kc, mean), _gpu_seg(K, vs, vc), l0, t0, h0))
+        ref.append((_oracle_seg(K, ks, kc, mean), _oracle_seg(K, vs, vc), l0, t0, h0))
     Kd, Vd = O.assemble_segments(ref, B, L, H, T, D)
     out = torch.empty((B, L, nq, Hq, D), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, L, nq, Hq), dtype=torch.float32, device="cuda:0")
-    wsb = K.kvq_decode_attn_segments_workspace(segs, L, Hq, nq)
+    wsb = K.kvq_decode_attn_segments_workspace(segs, L, H, Hq, nq)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda:0")
-    K.kvq_decode_attn_segments(segs, L, T, Hq, nq, to_dev(q), to_dev(kv_len) if kv_len is not None else None, 0.0,
+    K.kvq_decode_attn_segments(segs, L, H, T, Hq, nq, to_dev(q), to_dev(kv_len) if kv_len is not None else None, 0.0,
                                out, lse, ws, wsb)
     torch.cuda.synchronize()
     ref_out, ref_lse = O.decode_attn(q, Kd, Vd, kv_len)
@@ -109,7 +111,7 @@ def _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg=None):
     return segs
 
 
-@pytest.mark.parametrize("variant", ["anchors", "per_layer", "causal_mean", "window"])
+@pytest.mark.parametrize("variant", ["anchors", "per_layer", "causal_mean", "window", "per_head", "per_head_b2"])
 def test_decode_over_segments(variant):
     import kv_cache_bit_fwht_amd as K
     w = synth.get("c3", L=4, T=704, n_q=3)
@@ -128,8 +130,19 @@ def test_decode_over_segments(variant):
         kv_len = np.array([[[704, 650, 17], [0, 640, 700], [1, 688, 689], [300, 301, 704]]], dtype=np.int32)
         layout = [(k4, v2, 0, 4, 0, 640), (K.Codec(K.INT_ABSMAX, 4, 64, 0), K.Codec(K.INT_ABSMAX, 4, 64, 0), 0, 4, 640, 64)]
         mean_seg = 0
-    else:
+    elif variant == "window":
         layout = [(K.Codec(K.SIGN, 1, 8, 0), K.Codec(K.SIGN, 1, 8, 0), 0, 4, 0, 640), (f16, f16, 0, 4, 640, 64)]
+    else:
+        # per-head KV types: a sink head at fp16, two heads in 4/2 bits, a diffuse head in
+        # 3-bit keys; layers 2-3 of head 0 back in 4/2 bits for the first 352 tokens
+        if variant == "per_head_b2":
+            w = synth.get("c3", B=2, L=4, T=704, n_q=2)
+            Kx, Vx = synth.gen_kv(w)
+            q, kv_len = synth.gen_queries(w)
+            kv_len = np.random.default_rng(2).integers(0, 705, (2, 4, 2)).astype(np.int32)
+        k3 = K.Codec(K.INT_ABSMAX, 3, 128, 256)
+        layout = [(f16, f16, 0, 2, 0, 704, 0, 1), (k4, v2, 2, 2, 0, 352, 0, 1), (f16, f16, 2, 2, 352, 352, 0, 1),
+                  (k4, v2, 0, 4, 0, 704, 1, 2), (k3, v2, 0, 4, 0, 704, 3, 1)]
     announce(f"segments {variant}")
     _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg)
 

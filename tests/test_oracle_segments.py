@@ -96,3 +96,22 @@ def test_rows_code_independently(cspec):
     ww, sw, zw = O.quantize_pack(np.ascontiguousarray(x[:, :, :, 7:12]), c)
     rows = np.arange(w.shape[0]).reshape(2, 2, 3, 20)[:, :, :, 7:12].ravel()
     assert np.array_equal(w[rows], ww) and np.array_equal(s[rows], sw) and np.array_equal(z[rows], zw)
+
+
+def test_head_ranges_tile_and_weigh():
+    """Per-head codec maps ([LCPP] the per-head KV-type request): segments over head
+    ranges tile (layer, head, token) cells; a sink head at fp16 among 4-bit heads
+    weighs 1 / heads of the cache."""
+    assert O.tiles([(0, 2, 0, 8, 0, 1), (0, 2, 0, 8, 1, 3)], 2, 8, heads=4)
+    assert not O.tiles([(0, 2, 0, 8, 0, 1), (0, 2, 0, 8, 2, 2)], 2, 8, heads=4)          # head 1 missing
+    assert not O.tiles([(0, 2, 0, 8, 0, 2), (0, 2, 0, 8, 1, 3)], 2, 8, heads=4)          # head 1 twice
+    i4 = O.Codec(O.INT_ABSMAX, 4, 64)
+    f16 = O.Codec(O.FP16)
+    e = O.effective_bits([(f16, f16, 0, 3, 0, 50, 0, 1), (i4, i4, 0, 3, 0, 50, 1, 7)], 3, 50, 128, heads=8)
+    assert e == pytest.approx((16 + 7 * 4.25) / 8, abs=1e-12)
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((1, 2, 4, 6, 8)).astype(np.float32)
+    segs = [(K[:, :, :1], K[:, :, :1], 0, 0, 0), (K[:, :, 1:, :4], K[:, :, 1:, :4], 0, 0, 1),
+            (K[:, :, 1:, 4:], K[:, :, 1:, 4:], 0, 4, 1)]
+    Kd, _ = O.assemble_segments(segs, 1, 2, 4, 6, 8)
+    assert np.array_equal(Kd, K)
