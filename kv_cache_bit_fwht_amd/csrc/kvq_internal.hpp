@@ -51,6 +51,11 @@ __device__ __forceinline__ uint16_t rn16(float x) {
   return (b & 0x7fffu) ? b : (uint16_t)0;
 }
 
+// Orders one wavefront's LDS accesses: every earlier LDS access of the wavefront has
+// completed before any later one is issued, and the compiler moves no memory access
+// across it.  Enough between lanes of one wavefront working on its own LDS region.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Correctly rounded binary32 square root.  (The hardware instruction alone is
 // accurate to about one ulp; the builtin adds the exact residual checks.)
 __device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }

@@ -42,7 +42,15 @@ __device__ __forceinline__ long long out_row(const QArgs& a, long long row) {
   return u * a.Tout + a.t0 + (row - u * a.T);
 }
 
+// (layer, head) of a row of a [B][L][H][T] row tensor; 32-bit division where the row
+// index fits (64-bit division is a long software sequence).
 __device__ __forceinline__ void row_unit(long long row, int T, int H, int L, int& l, int& h) {
+  if (row < (1ll << 32)) {
+    const uint32_t unit = (uint32_t)row / (uint32_t)T;
+    h = (int)(unit % (uint32_t)H);
+    l = (int)((unit / (uint32_t)H) % (uint32_t)L);
+    return;
+  }
   const long long unit = row / T;
   h = (int)(unit % H);
   l = (int)((unit / H) % L);
@@ -363,7 +371,9 @@ constexpr int kRowLds = 256 + 16;                    // LDS floats per row (padd
 
 // Quads of rows q_first, q_first + q_stride, ... of one tensor; each wavefront of the
 // caller owns one quad per step (16 lanes per row).
-template <int BITS, bool ROT, bool PRE>
+// PRE: bit 0 a mean, bit 1 channel scales (loaded with the row, applied before the
+// rotation); 0 for neither.
+template <int BITS, bool ROT, int PRE>
 __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first, long long q_stride,
                                                float* rl, int lane) {
   constexpr int D = 256;
@@ -374,18 +384,52 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
   const int j = lane & 15;                           // lane within the row
   const int lpg = a.g >> 4;                          // lanes per group
   const long long nquads = (a.rows + 3) >> 2;
-  // PRE (a mean or channel scales): the row range and vector offset of the current
-  // (layer, head), recomputed only when a row leaves it (64-bit division is slow)
-  long long cu_lo = 0, cu_hi = 0;
-  size_t cu_off = 0;
+  // PRE (a mean or channel scales; tokens per unit a multiple of 4, so a quad never
+  // spans two units): the (layer, head) of the wavefront's quad, kept as uniform state
+  // and stepped to the next unit without a division (64-bit division is a long
+  // software sequence)
+  long long w_lo = 0, w_hi = 0;
+  int w_l = 0, w_h = 0;
   for (long long qd = q_first; qd < nquads; qd += q_stride) {
     const long long row = qd * 4 + (lane >> 4);
     const bool active = row < a.rows;
+    if constexpr (PRE != 0) {
+      const long long row0 = qd * 4;                 // the quad's first row (uniform)
+      if (row0 < w_lo || row0 >= w_hi) {
+        if (w_hi > 0 && row0 >= w_hi && row0 < w_hi + a.T) {   // the next unit
+          w_lo = w_hi;
+          w_hi += a.T;
+          if (++w_h == a.H) {
+            w_h = 0;
+            if (++w_l == a.L) w_l = 0;
+          }
+        } else {
+          const long long unit = row0 / a.T;
+          w_lo = unit * a.T;
+          w_hi = w_lo + a.T;
+          w_h = (int)(unit % a.H);
+          w_l = (int)((unit / a.H) % a.L);
+        }
+      }
+    }
     uint4 p0 = make_uint4(0, 0, 0, 0), p1 = p0;
+    // PRE: the lane's mean and scale values, loaded together with the row (one round trip)
+    float4 pm[4], pc[4];
     if (active) {
       const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)row * D + 16 * j);
       p0 = src[0];
       p1 = src[1];
+      if constexpr (PRE != 0) {
+        const size_t off = ((size_t)w_l * a.H + w_h) * D + 16 * j;
+        if constexpr ((PRE & 1) != 0) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pm[k] = reinterpret_cast<const float4*>(a.mean + off)[k];
+        }
+        if constexpr ((PRE & 2) != 0) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pc[k] = reinterpret_cast<const float4*>(a.chan + off)[k];
+        }
+      }
     }
     const uint32_t raw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     float v[16];
@@ -394,16 +438,26 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
       v[2 * k] = h2f((uint16_t)(raw[k] & 0xffffu));
       v[2 * k + 1] = h2f((uint16_t)(raw[k] >> 16));
     }
-    if constexpr (PRE) {
+    if constexpr (PRE != 0) {
       if (active) {
-        if (row < cu_lo || row >= cu_hi) {
-          const long long unit = row / a.T;
-          cu_lo = unit * a.T;
-          cu_hi = cu_lo + a.T;
-          const int h = (int)(unit % a.H), l = (int)((unit / a.H) % a.L);
-          cu_off = ((size_t)l * a.H + h) * D + 16 * j;
+        if constexpr ((PRE & 1) != 0) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            v[4 * k] = v[4 * k] - pm[k].x;
+            v[4 * k + 1] = v[4 * k + 1] - pm[k].y;
+            v[4 * k + 2] = v[4 * k + 2] - pm[k].z;
+            v[4 * k + 3] = v[4 * k + 3] - pm[k].w;
+          }
         }
-        pre_row(v, a.mean, a.chan, cu_off);
+        if constexpr ((PRE & 2) != 0) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            v[4 * k] = v[4 * k] * pc[k].x;
+            v[4 * k + 1] = v[4 * k + 1] * pc[k].y;
+            v[4 * k + 2] = v[4 * k + 2] * pc[k].z;
+            v[4 * k + 3] = v[4 * k + 3] * pc[k].w;
+          }
+        }
       }
     }
     if constexpr (ROT) {
@@ -504,57 +558,59 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
   }
 }
 
-template <int BITS, bool ROT, bool PRE>
+template <int BITS, bool ROT, int PRE>
 __global__ __launch_bounds__(kBlock) void k_quantize_absmax256(QArgs a) {
   __shared__ float lds[kBlock / 16][kRowLds];
-  const int tid = threadIdx.x;
   constexpr int waves = kBlock / 64;
+  const int tid = threadIdx.x;
   absmax256_rows<BITS, ROT, PRE>(a, (long long)blockIdx.x * waves + (tid >> 6), (long long)gridDim.x * waves,
                                  lds[tid >> 4], tid & 63);
 }
 
-static bool absmax256_supported(const kvq_packed& p) {
+static bool absmax256_supported(const kvq_packed& p, int tokens_in) {
   const kvq_codec& c = p.codec;
   if (c.codebook != KVQ_INT_ABSMAX || p.shape.head_dim != 256) return false;
+  if ((p.chan_scale || p.mean) && tokens_in % 4 != 0) return false;   // a quad would span two units
   if (c.bits != 2 && c.bits != 4 && c.bits != 8) return false;
   if (c.group < 16 || c.group > 256) return false;
   return c.rot_width <= 1 || c.rot_width == 256;
 }
 
-// At most the blocks that are resident at once (8 wavefronts per SIMD).
-static long long absmax256_blocks(long long rows) {
+// At most the blocks that are resident at once: 8 wavefronts per SIMD, 6 for the
+// variants that hold a mean or scale vector (more registers).
+static long long absmax256_blocks(long long rows, int pre) {
   const long long quads = (rows + 3) / 4;
   long long blocks = (quads + (kBlock / 64) - 1) / (kBlock / 64);
-  const long long cap = 256 * 8;
+  const long long cap = 256 * (pre ? 6 : 8);
   if (blocks > cap) blocks = cap;
   return blocks < 1 ? 1 : blocks;
 }
 
-static void launch_absmax256(const QArgs& a, const kvq_codec& c, hipStream_t st) {
-  const dim3 grid((unsigned)absmax256_blocks(a.rows));
+template <int PRE>
+static void launch_absmax256_pre(const QArgs& a, const kvq_codec& c, hipStream_t st) {
+  const dim3 grid((unsigned)absmax256_blocks(a.rows, PRE));
   const bool rot = c.rot_width == 256;
-  if (a.chan != nullptr || a.mean != nullptr) {
-    if (c.bits == 2) rot ? k_quantize_absmax256<2, true, true><<<grid, kBlock, 0, st>>>(a)
-                         : k_quantize_absmax256<2, false, true><<<grid, kBlock, 0, st>>>(a);
-    else if (c.bits == 4) rot ? k_quantize_absmax256<4, true, true><<<grid, kBlock, 0, st>>>(a)
-                              : k_quantize_absmax256<4, false, true><<<grid, kBlock, 0, st>>>(a);
-    else rot ? k_quantize_absmax256<8, true, true><<<grid, kBlock, 0, st>>>(a)
-             : k_quantize_absmax256<8, false, true><<<grid, kBlock, 0, st>>>(a);
-    return;
-  }
-  if (c.bits == 2) rot ? k_quantize_absmax256<2, true, false><<<grid, kBlock, 0, st>>>(a)
-                       : k_quantize_absmax256<2, false, false><<<grid, kBlock, 0, st>>>(a);
-  else if (c.bits == 4) rot ? k_quantize_absmax256<4, true, false><<<grid, kBlock, 0, st>>>(a)
-                            : k_quantize_absmax256<4, false, false><<<grid, kBlock, 0, st>>>(a);
-  else rot ? k_quantize_absmax256<8, true, false><<<grid, kBlock, 0, st>>>(a)
-           : k_quantize_absmax256<8, false, false><<<grid, kBlock, 0, st>>>(a);
+  if (c.bits == 2) rot ? k_quantize_absmax256<2, true, PRE><<<grid, kBlock, 0, st>>>(a)
+                       : k_quantize_absmax256<2, false, PRE><<<grid, kBlock, 0, st>>>(a);
+  else if (c.bits == 4) rot ? k_quantize_absmax256<4, true, PRE><<<grid, kBlock, 0, st>>>(a)
+                            : k_quantize_absmax256<4, false, PRE><<<grid, kBlock, 0, st>>>(a);
+  else rot ? k_quantize_absmax256<8, true, PRE><<<grid, kBlock, 0, st>>>(a)
+           : k_quantize_absmax256<8, false, PRE><<<grid, kBlock, 0, st>>>(a);
+}
+
+static void launch_absmax256(const QArgs& a, const kvq_codec& c, hipStream_t st) {
+  const int pre = (a.mean != nullptr ? 1 : 0) | (a.chan != nullptr ? 2 : 0);
+  if (pre == 0) launch_absmax256_pre<0>(a, c, st);
+  else if (pre == 1) launch_absmax256_pre<1>(a, c, st);
+  else if (pre == 2) launch_absmax256_pre<2>(a, c, st);
+  else launch_absmax256_pre<3>(a, c, st);
 }
 
 hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st) {
   QArgs a = make_args(p);
   a.x = x;
   if (a.rows == 0) return hipSuccess;
-  if (absmax256_supported(p)) {
+  if (absmax256_supported(p, a.T)) {
     launch_absmax256(a, p.codec, st);
     return hipGetLastError();
   }
@@ -570,7 +626,7 @@ hipError_t launch_quantize_tokens(const uint16_t* x, const kvq_packed& p, int t0
   a.t0 = t0;
   a.rows = (long long)p.shape.batch * p.shape.layers * p.shape.heads * n;
   if (a.rows == 0) return hipSuccess;
-  if (absmax256_supported(p)) {
+  if (absmax256_supported(p, n)) {
     launch_absmax256(a, p.codec, st);
     return hipGetLastError();
   }

@@ -48,7 +48,14 @@ __device__ __forceinline__ void load_tables(const RArgs& a, LdsTables& t) {
   __syncthreads();
 }
 
+// (layer, head) of a row; 32-bit division where the row index fits.
 __device__ __forceinline__ void unit_of(long long row, int T, int H, int L, int& l, int& h) {
+  if (row < (1ll << 32)) {
+    const uint32_t u = (uint32_t)row / (uint32_t)T;
+    h = (int)(u % (uint32_t)H);
+    l = (int)((u / (uint32_t)H) % (uint32_t)L);
+    return;
+  }
   const long long u = row / T;
   h = (int)(u % H);
   l = (int)((u / H) % L);

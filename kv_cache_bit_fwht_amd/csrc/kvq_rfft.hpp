@@ -77,11 +77,6 @@ __device__ __forceinline__ void rfft_bin_value(const RfftCodec& c, const uint32_
   }
 }
 
-// Orders one wavefront's LDS accesses: every earlier LDS access of the wavefront has
-// completed before any later one is issued, and the compiler moves no memory access
-// across it.  Enough between lanes of one wavefront working on its own LDS region.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 // In-place radix-2 DIT FFT of N complex values in LDS (already in bit-reversed
 // order).  Butterflies are spread over the `nl` lanes [0, nl) of one wavefront,
 // which owns the arrays; each stage ends with a wavefront-local LDS sync.  conj

@@ -48,12 +48,15 @@ CODECS = [((1, 4, 128, 256), 256), ((1, 3, 128, 256), 256), ((1, 2, 128, 0), 256
           ((10, 3, 32, 128), 128)]
 
 
+@pytest.mark.parametrize("T", [203, 204])
 @pytest.mark.parametrize("with_chan", [False, True])
 @pytest.mark.parametrize("cspec,D", CODECS)
-def test_quantize_dequant_with_mean_bit_exact(cspec, D, with_chan):
+def test_quantize_dequant_with_mean_bit_exact(cspec, D, with_chan, T):
+    """T = 204 (a multiple of 4) takes the 256-wide absmax kernel's mean/scale variant
+    for the head_dim-256 absmax codecs; T = 203 the general kernel."""
     import torch
     import kv_cache_bit_fwht_amd as K
-    w = synth.get("c3", B=2, L=2, H=2, T=203, D=D, k_mean_share=0.53)
+    w = synth.get("c3", B=2, L=2, H=2, T=T, D=D, k_mean_share=0.53)
     Kx, _ = synth.gen_kv(w)
     mu = O.key_mean(Kx)
     chan = np.random.default_rng(D).uniform(0.5, 2.0, (2, 2, D)).astype(np.float32) if with_chan else None
