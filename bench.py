@@ -391,7 +391,8 @@ def entropy_workload(reps):
     H_2 per KV head from 8 calibration queries (kvq_attn_error_ex on the fp16 cache);
     bits by the rule at an average of 4, rounded keeping the sum; keys of each head
     coded at its bits (FWHT-256, g128) as head segments, values int4 g128.  Compared
-    with uniform 4-bit keys: attention KL of 16 queries, and one decode step."""
+    with uniform 4-bit keys: attention KL of 16 queries, and one decode step (the
+    head segments decoded as one codec-map launch and as a launch per segment)."""
     import torch
     import kv_cache_bit_fwht_amd as K
     import synth
@@ -466,12 +467,13 @@ def entropy_workload(reps):
         segs.append(K.Segment(kp, vp, 0, 0, h))
     wsb = K.kvq_decode_attn_segments_workspace(segs, L, H, Hq, 1)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-    fn = lambda: K.kvq_decode_attn_segments(segs, L, H, T, Hq, 1, q1, None, 0.0, out, lse, ws, wsb)
-    fn()
-    ta = _median_time(torch, fn, reps)
     kb = sum(K.kvq_bits_per_value(sg.k.codec, D) for sg in segs) / H
-    recs.append(("K bits per head by b_h = 4 + 0.25 (H_avg - H_2(h)), head segments", [int(b) for b in bits], kls,
-                 jss, ta, kb))
+    for path, how in ((2, "one launch for the codec map"), (1, "a launch per head segment")):
+        fn = lambda: K.kvq_decode_attn_segments(segs, L, H, T, Hq, 1, q1, None, 0.0, out, lse, ws, wsb, path=path)
+        fn()
+        ta = _median_time(torch, fn, reps)
+        recs.append((f"K bits per head by b_h = 4 + 0.25 (H_avg - H_2(h)), head segments, {how}",
+                     [int(b) for b in bits], kls, jss, ta, kb))
     for name, bh, kl, js, t, kbits in recs:
         print(json.dumps({
             "workload": f"c3h: B={B} L={L} H={H} T={T} D={D} Hq={Hq}, per-head key scales {list(w.k_head_scales)}, "

@@ -276,12 +276,34 @@ size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg
  * out/lse as for kvq_decode_attn over the whole logical cache.  Each segment is
  * decoded by the kvq_decode_attn kernels (the MFMA kernel where it applies) and
  * its (out, lse) merged into the running result by log-sum-exp weights; a
- * segment's key mean shifts only its own lse, as the whole cache's would. */
+ * segment's key mean shifts only its own lse, as the whole cache's would.
+ * A codec map (every segment holding all tokens of its layer range x head range,
+ * as for a per-layer bit allocation, [E21W] Result, or per-head bit widths,
+ * [LCPP] Finding 2) whose codec pairs the mixed kernel compiles is decoded by
+ * one launch when there are two or more segments and none would take the MFMA
+ * kernel: see kvq_decode_attn_segments_ex. */
 kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers,
                                     int32_t heads, int32_t tokens, int32_t q_heads, int32_t n_q,
                                     const uint16_t* q,
                                     const int32_t* kv_len, float sm_scale, float* out, float* lse,
                                     void* ws, size_t ws_bytes, void* stream);
+
+/* kvq_decode_attn_segments with the route chosen: path 0 = as
+ * kvq_decode_attn_segments; 1 = each segment by its own launches and a
+ * log-sum-exp merge; 2 = one decode launch for the whole codec map (every block
+ * looks up the segment of its (layer, KV head) and decodes with that segment's
+ * codecs) and one split combine.  Path 2 needs every segment to hold tokens
+ * [0, tokens) of its tile and a key/value codec pair among: signed absmax keys of
+ * 2-6 bits with signed absmax values of 2, 3 or 4 bits (any group, rotation and
+ * channel scale), fp16/fp16, int8/int8, ternary/ternary, sign/sign, NF4 keys with
+ * 4-bit signed absmax values; else KVQ_ERR_UNSUPPORTED (nothing launched).
+ * Segment key means are applied by both paths.  Same workspace query; any other
+ * path value is KVQ_ERR_ARG. */
+kvq_status kvq_decode_attn_segments_ex(const kvq_segment* segs, int32_t n_seg, int32_t layers,
+                                       int32_t heads, int32_t tokens, int32_t q_heads, int32_t n_q,
+                                       const uint16_t* q,
+                                       const int32_t* kv_len, float sm_scale, float* out, float* lse,
+                                       void* ws, size_t ws_bytes, int32_t path, void* stream);
 
 /* Host only.  Effective bits per cached value of a tiled logical cache: the
  * segments' K/V bits per value (kvq_bits_per_value, averaged over K and V)

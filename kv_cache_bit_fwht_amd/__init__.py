@@ -28,7 +28,8 @@ EXPORTS = [
     "kvq_quantize_pack", "kvq_dequant",
     "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_ex",
     "kvq_attn_error_workspace", "kvq_attn_error", "kvq_quantize_pack_tokens",
-    "kvq_decode_attn_segments_workspace", "kvq_decode_attn_segments", "kvq_effective_bits",
+    "kvq_decode_attn_segments_workspace", "kvq_decode_attn_segments", "kvq_decode_attn_segments_ex",
+    "kvq_effective_bits",
     "kvq_attn_error_ex",
 ]
 
@@ -91,6 +92,7 @@ def _load():
         "kvq_quantize_pack_tokens": ([P, I32, I32, P, P], I32),
         "kvq_decode_attn_segments_workspace": ([P, I32, I32, I32, I32, I32], SZ),
         "kvq_decode_attn_segments": ([P, I32, I32, I32, I32, I32, I32, P, P, F, P, P, P, SZ, P], I32),
+        "kvq_decode_attn_segments_ex": ([P, I32, I32, I32, I32, I32, I32, P, P, F, P, P, P, SZ, I32, P], I32),
         "kvq_effective_bits": ([P, I32, I32, I32, I32], D),
         "kvq_attn_error_ex": ([P, P, P, P, I32, I32, P, P, F, P, P, SZ, P], I32),
     }
@@ -262,12 +264,24 @@ def kvq_decode_attn_segments_workspace(segs, layers: int, heads: int, q_heads: i
 
 
 def kvq_decode_attn_segments(segs, layers: int, heads: int, tokens: int, q_heads: int, n_q: int, q, kv_len,
-                             sm_scale: float, out, lse, ws, ws_bytes: int, stream=None):
+                             sm_scale: float, out, lse, ws, ws_bytes: int, stream=None, path: int | None = None):
     arr, _keep = _segments_c(segs)
-    _check("kvq_decode_attn_segments",
-           _lib.kvq_decode_attn_segments(arr, len(segs), layers, heads, tokens, q_heads, n_q, _ptr(q),
-                                         _ptr(kv_len), sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
-                                         _stream(stream)))
+    if path is None:
+        _check("kvq_decode_attn_segments",
+               _lib.kvq_decode_attn_segments(arr, len(segs), layers, heads, tokens, q_heads, n_q, _ptr(q),
+                                             _ptr(kv_len), sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                             _stream(stream)))
+    else:
+        _check("kvq_decode_attn_segments_ex",
+               _lib.kvq_decode_attn_segments_ex(arr, len(segs), layers, heads, tokens, q_heads, n_q, _ptr(q),
+                                                _ptr(kv_len), sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                                path, _stream(stream)))
+
+
+def kvq_decode_attn_segments_ex(segs, layers, heads, tokens, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws,
+                                ws_bytes, path: int, stream=None):
+    kvq_decode_attn_segments(segs, layers, heads, tokens, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes,
+                             stream, path)
 
 
 def kvq_effective_bits(segs, layers: int, heads: int, tokens: int) -> float:

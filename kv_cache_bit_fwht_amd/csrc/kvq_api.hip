@@ -419,6 +419,7 @@ struct SegPlan {
   size_t out_off[kMaxSegments], lse_off[kMaxSegments];
   bool direct[kMaxSegments];
   bool need_init;
+  size_t mixed_bytes;
 };
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -465,6 +466,11 @@ static SegPlan seg_plan(const kvq_segment* segs, int32_t n_seg, int32_t layers, 
   }
   p.lacc = off;
   p.total = p.lacc + round256((size_t)s0.batch * layers * n_q * q_heads * 4);
+  // the one-launch path of a codec map: counters, then its split partials
+  int tokens = 0;
+  for (int i = 0; i < n_seg; ++i) tokens = std::max(tokens, segs[i].token0 + segs[i].k->shape.tokens);
+  p.mixed_bytes = mixed_ws_bytes(segs, layers, heads, tokens, q_heads, n_q);
+  p.total = std::max(p.total, kWsCounterBytes + p.mixed_bytes);
   return p;
 }
 
@@ -530,22 +536,37 @@ size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg
   return seg_plan(segs, n_seg, layers, heads, q_heads, n_q).total;
 }
 
-kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,
-                                    int32_t tokens, int32_t q_heads, int32_t n_q, const uint16_t* q,
-                                    const int32_t* kv_len, float sm_scale, float* out, float* lse, void* ws,
-                                    size_t ws_bytes, void* stream) {
+kvq_status kvq_decode_attn_segments_ex(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,
+                                       int32_t tokens, int32_t q_heads, int32_t n_q, const uint16_t* q,
+                                       const int32_t* kv_len, float sm_scale, float* out, float* lse, void* ws,
+                                       size_t ws_bytes, int32_t path, void* stream) {
   kvq_status st = check_segments(segs, n_seg, layers, heads, tokens, q_heads, n_q);
   if (st != KVQ_OK) return st;
   if (!q || !out) return KVQ_ERR_ARG;
   if (!aligned16(q) || !aligned16(out) || (lse && !aligned16(lse)) || (kv_len && !aligned16(kv_len)))
     return KVQ_ERR_ALIGN;
   if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
+  if (path < 0 || path > 2) return KVQ_ERR_ARG;
   const SegPlan pl = seg_plan(segs, n_seg, layers, heads, q_heads, n_q);
   if (ws_bytes < pl.total || !ws) return KVQ_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVQ_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   char* w = static_cast<char*>(ws);
   const int B = segs[0].k->shape.batch, D = segs[0].k->shape.head_dim, G = q_heads / heads;
+  // a codec map (every segment a whole-token tile) in one launch: asked for, or, by
+  // default, when there are several tiles and none would take the MFMA kernel
+  const bool mix_ok = mixed_decode_supported(segs, n_seg, tokens);
+  if (path == 2 && !mix_ok) return KVQ_ERR_UNSUPPORTED;
+  bool use_mix = path == 2;
+  if (path == 0 && mix_ok && n_seg > 1) {
+    use_mix = true;
+    for (int i = 0; i < n_seg; ++i)
+      if (fast_decode_supported(*segs[i].k, *segs[i].v, segs[i].k->shape.heads * G)) use_mix = false;
+  }
+  const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)D));
+  if (use_mix)
+    return hip_status(launch_decode_mixed(segs, n_seg, layers, heads, tokens, q_heads, n_q, q, kv_len, sm, out, lse,
+                                          w + kWsCounterBytes, s));
   const size_t rpl = (size_t)n_q * q_heads;                     // output rows per (sequence, layer)
   float* lacc = lse ? lse : reinterpret_cast<float*>(w + pl.lacc);
   hipError_t e = hipSuccess;
@@ -602,6 +623,14 @@ kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int3
   if (e == hipSuccess)
     e = launch_seg_merge(nm, ml0, mls, mj0, mhq, mos, mlse, out, lacc, B, layers, n_q, q_heads, D, s);
   return hip_status(e);
+}
+
+kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,
+                                    int32_t tokens, int32_t q_heads, int32_t n_q, const uint16_t* q,
+                                    const int32_t* kv_len, float sm_scale, float* out, float* lse, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  return kvq_decode_attn_segments_ex(segs, n_seg, layers, heads, tokens, q_heads, n_q, q, kv_len, sm_scale, out, lse,
+                                     ws, ws_bytes, 0, stream);
 }
 
 double kvq_effective_bits(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads, int32_t tokens) {

@@ -625,11 +625,14 @@ __device__ __forceinline__ void rfft_raw_decode(const DevCodec& c, const RawRfft
   }
 }
 
-template <int KCB, int KB, int VCB, int VB>
-__global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
+// One block's work: the (query row, KV head h, head group, 4 splits) of blockIdx, with
+// key codec kc and value codec vc whose rows of this unit start at urow0, and the key
+// channel scales of the unit at kch (or null).  `a` holds the problem-wide fields.
+template <int KCB, int KB, int VCB, int VB, typename A>
+__device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const DevCodec& vc, float* smem,
+                                          long long urow0, const float* kch) {
   constexpr bool KR = (KCB == KVQ_RFFT_POLAR || KCB == KVQ_RFFT_CART);
   using KRaw = typename std::conditional<KR, RawRfft, RawChunk<KCB, KB>>::type;
-  extern __shared__ float smem[];
   const int D = a.D, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int RS = 17 * (D / 16) + 17;
@@ -640,19 +643,15 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
   const int h = blockIdx.y / HG, hg = blockIdx.y - h * HG;
   const int GH = min(kWaveHeads, a.G - kWaveHeads * hg);      // query heads of this head group
   const long long rq = blockIdx.z;                   // (b*L + l)*n_q + i
-  const int l = (int)((rq / a.n_q) % a.L);
-  const int b = (int)(rq / ((long long)a.n_q * a.L));
-  const long long urow0 = (((long long)b * a.L + l) * a.H + h) * a.T;
   int n = a.T;
   if (a.kv_len) n = min(max(a.kv_len[rq], 0), a.T);
   const int split = blockIdx.x * (kBlock / 64) + wave;
   const int t_begin = split * a.chunk, t_end = min(t_begin + a.chunk, n);
-  const int glog2k = 31 - __builtin_clz(a.k.g > 0 ? a.k.g : 1), glog2v = 31 - __builtin_clz(a.v.g > 0 ? a.v.g : 1);
+  const int glog2k = 31 - __builtin_clz(kc.g > 0 ? kc.g : 1), glog2v = 31 - __builtin_clz(vc.g > 0 ? vc.g : 1);
 
   // ---- query prologue: heads 4 hg .. 4 hg + GH - 1 in the key codec's coordinates,
   // times the logit scale in log2 units; rows of absent heads are zero
   const uint16_t* qsrc = a.q + ((size_t)rq * a.Hq + (size_t)h * a.G + (size_t)kWaveHeads * hg) * D;
-  const float* kch = a.k.chan ? a.k.chan + ((size_t)l * a.H + h) * D : nullptr;
   for (int p = tid; p < kWaveHeads * D; p += kBlock) {
     const int g = p / D, d = p - g * D;
     float x = (g < GH) ? h2f(qsrc[(size_t)g * D + d]) : 0.0f;
@@ -691,7 +690,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
       tmp[g * RS + pidx(F + f)] = si * wf;
     }
     if (KCB == KVQ_RFFT_POLAR)
-      for (int p = tid; p < (1 << a.k.rc.pbits); p += kBlock) {
+      for (int p = tid; p < (1 << kc.rc.pbits); p += kBlock) {
         dirc[p] = a.dirs.dir_c[p];
         dirs[p] = a.dirs.dir_s[p];
       }
@@ -706,7 +705,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
     }
     __syncthreads();
   } else {
-    if (a.k.W > 1) fwht_lds_rows(qc, kWaveHeads, RS, D, a.k.W, a.k.kappa);
+    if (kc.W > 1) fwht_lds_rows(qc, kWaveHeads, RS, D, kc.W, kc.kappa);
 #pragma unroll
     for (int g = 0; g < kWaveHeads; ++g)
 #pragma unroll
@@ -725,15 +724,15 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
   // rows past the range re-read a valid row of the unit (weight 0, nothing stored)
   auto load = [&](int it, KRaw& kr, RawChunk<VCB, VB>& vr) {
     const long long row = urow0 + min(t_begin + it * RPW + r, a.T - 1);
-    if constexpr (KR) rfft_raw_load(a.k, row, j, LPT, kr);
-    else raw_load<KCB, KB>(a.k, row, j, glog2k, kr);
-    raw_load<VCB, VB>(a.v, row, j, glog2v, vr);
+    if constexpr (KR) rfft_raw_load(kc, row, j, LPT, kr);
+    else raw_load<KCB, KB>(kc, row, j, glog2k, kr);
+    raw_load<VCB, VB>(vc, row, j, glog2v, vr);
   };
   auto step = [&](int it, const KRaw& kr, const RawChunk<VCB, VB>& vr) {
     const bool valid = t_begin + it * RPW + r < t_end;
     float kv[16], zr[9], zi[9];
-    if constexpr (KR) rfft_raw_decode(a.k, kr, j, dirc, dirs, zr, zi);
-    else raw_decode<KCB, KB>(a.k, kr, j, a.tab, nf4l, kv);
+    if constexpr (KR) rfft_raw_decode(kc, kr, j, dirc, dirs, zr, zi);
+    else raw_decode<KCB, KB>(kc, kr, j, a.tab, nf4l, kv);
     float sc[kWaveHeads];
     bool grow = false;
 #pragma unroll
@@ -771,7 +770,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
       }
     }
     float vv[16];
-    raw_decode<VCB, VB>(a.v, vr, j, a.tab, nf4l, vv);
+    raw_decode<VCB, VB>(vc, vr, j, a.tab, nf4l, vv);
 #pragma unroll
     for (int g = 0; g < kWaveHeads; ++g) {
       const float pw = (sc[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[g] - mref[g]);
@@ -837,11 +836,121 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
   }
 }
 
+template <int KCB, int KB, int VCB, int VB>
+__global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
+  extern __shared__ float smem[];
+  const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
+  const int h = blockIdx.y / HG;
+  const long long rq = blockIdx.z;                   // (b*L + l)*n_q + i
+  const int l = (int)((rq / a.n_q) % a.L);
+  const int b = (int)(rq / ((long long)a.n_q * a.L));
+  const long long urow0 = (((long long)b * a.L + l) * a.H + h) * a.T;
+  const float* kch = a.k.chan ? a.k.chan + ((size_t)l * a.H + h) * a.D : nullptr;
+  wave_unit<KCB, KB, VCB, VB>(a, a.k, a.v, smem, urow0, kch);
+}
+
+// ------------------------------------------------------------------ codec maps in one launch
+//
+// A cache tiled into (layer range x KV-head range) tiles, each stored with its own key
+// and value codecs over every token: per-layer bit allocations ([E21W] Result, the
+// 3.19-bit allocation) and per-head bit widths ([LCPP] Finding 2).  One launch decodes
+// all of it: each block finds the tile of its (layer, KV head) and runs the compiled
+// decode of that tile's codec pair, so blocks of different pairs share the launch.
+// The pairs compiled in (id, key codebook, key bits, value codebook, value bits):
+#define KVQ_MIX_PAIRS(X)                                                                        \
+  X(0, KVQ_INT_ABSMAX, 2, KVQ_INT_ABSMAX, 2) X(1, KVQ_INT_ABSMAX, 2, KVQ_INT_ABSMAX, 3)         \
+  X(2, KVQ_INT_ABSMAX, 2, KVQ_INT_ABSMAX, 4) X(3, KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 2)         \
+  X(4, KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 3) X(5, KVQ_INT_ABSMAX, 3, KVQ_INT_ABSMAX, 4)         \
+  X(6, KVQ_INT_ABSMAX, 4, KVQ_INT_ABSMAX, 2) X(7, KVQ_INT_ABSMAX, 4, KVQ_INT_ABSMAX, 3)         \
+  X(8, KVQ_INT_ABSMAX, 4, KVQ_INT_ABSMAX, 4) X(9, KVQ_INT_ABSMAX, 5, KVQ_INT_ABSMAX, 2)         \
+  X(10, KVQ_INT_ABSMAX, 5, KVQ_INT_ABSMAX, 3) X(11, KVQ_INT_ABSMAX, 5, KVQ_INT_ABSMAX, 4)       \
+  X(12, KVQ_INT_ABSMAX, 6, KVQ_INT_ABSMAX, 2) X(13, KVQ_INT_ABSMAX, 6, KVQ_INT_ABSMAX, 3)       \
+  X(14, KVQ_INT_ABSMAX, 6, KVQ_INT_ABSMAX, 4) X(15, KVQ_FP16, 16, KVQ_FP16, 16)                 \
+  X(16, KVQ_INT8_SYM, 8, KVQ_INT8_SYM, 8) X(17, KVQ_TERNARY, 2, KVQ_TERNARY, 2)                 \
+  X(18, KVQ_SIGN, 1, KVQ_SIGN, 1) X(19, KVQ_NF4, 4, KVQ_INT_ABSMAX, 4)
+
+struct MixCodec {        // the fields of DevCodec the wavefront decode reads
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* mins;
+  const float* chan;
+  int row_bytes, ng, g, W;
+  float kappa;
+  int cb, bits;
+};
+
+struct MixTile {         // layers [l0, l0 + ls) x KV heads [h0, h0 + hs), all tokens
+  MixCodec k, v;
+  int l0, ls, h0, hs;
+  int pair;              // index into KVQ_MIX_PAIRS
+};
+
+struct MArgs {
+  const uint16_t* q;
+  const int32_t* kv_len;
+  float* ws;             // split partials, as the single-codec kernel writes them
+  float sm_scale;
+  int B, L, H, T, D, Hq, G, n_q, S, chunk, lpt_log2;
+  int ntiles;
+  Tables tab;
+  MixTile tile[kMaxSegments];
+};
+
+__device__ __forceinline__ DevCodec mix_codec(const MixCodec& m) {
+  DevCodec c{};
+  c.cb = m.cb;
+  c.bits = m.bits;
+  c.g = m.g;
+  c.W = m.W;
+  c.ng = m.ng;
+  c.kappa = m.kappa;
+  c.row_bytes = (size_t)m.row_bytes;
+  c.codes = m.codes;
+  c.scales = m.scales;
+  c.mins = m.mins;
+  c.chan = m.chan;
+  return c;
+}
+
+__global__ __launch_bounds__(kBlock) void k_decode_wave_mix(MArgs a) {
+  extern __shared__ float smem[];
+  const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
+  const int h = blockIdx.y / HG;
+  const long long rq = blockIdx.z;                   // (b*L + l)*n_q + i
+  const int l = (int)((rq / a.n_q) % a.L);
+  const int b = (int)(rq / ((long long)a.n_q * a.L));
+  int ti = 0;                                        // the tiles cover every (layer, head) once
+  while (ti + 1 < a.ntiles) {
+    const MixTile& t = a.tile[ti];
+    if (l >= t.l0 && l < t.l0 + t.ls && h >= t.h0 && h < t.h0 + t.hs) break;
+    ++ti;
+  }
+  const MixTile& t = a.tile[ti];
+  const int ll = l - t.l0, hl = h - t.h0;            // the unit inside its tile's arrays
+  const long long urow0 = (((long long)b * t.ls + ll) * t.hs + hl) * a.T;
+  const DevCodec kc = mix_codec(t.k), vc = mix_codec(t.v);
+  const float* kch = kc.chan ? kc.chan + ((size_t)ll * t.hs + hl) * a.D : nullptr;
+  switch (t.pair) {
+#define KVQ_MIX_CASE(id, KCB, KB, VCB, VB) \
+  case id: wave_unit<KCB, KB, VCB, VB>(a, kc, vc, smem, urow0, kch); break;
+    KVQ_MIX_PAIRS(KVQ_MIX_CASE)
+#undef KVQ_MIX_CASE
+    default: break;
+  }
+}
+
 // ------------------------------------------------------------------ combine
 
 // One block per (query row, query head).  Merges the S split partials:
 // M = max m_s, L = sum l_s e^{m_s - M}, o = sum o_s e^{m_s - M} / L; then
 // rotates o back if V was rotated and divides V's per-channel scale.
+struct MixV {            // a tile of a codec map: its value rotation and channel scales, its key mean
+  int l0, ls, h0, hs, vW;
+  float vkappa;
+  const float* vchan;    // [ls][hs][D] or null
+  const float* kmean;    // [ls][hs][D] or null
+};
+
 struct CArgs {
   const float* ws;
   int S, D, Hq, G, H, L, n_q;
@@ -849,6 +958,10 @@ struct CArgs {
   float vkappa;
   const float* vchan;
   int* ctr;             // decode chunk counters to set back to zero, or null
+  int ntiles;           // > 0: a codec map; the tile of (layer, KV head) gives vW, vkappa, vchan
+  const uint16_t* q;    // codec map: the queries, for the lse shift of a tile's key mean
+  float sm;             // codec map: the logit scale
+  MixV tile[kMaxSegments];
 };
 
 struct ErrOut {          // error outputs beyond KL / relative error (each nullable)
@@ -959,14 +1072,44 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(CArgs a, float* out, fl
     orow[pidx(tid)] = o;
   }
   __syncthreads();
-  if (a.vW > 1) fwht_lds_rows(orow, 1, 0, D, a.vW, a.vkappa);
+  int vW = a.vW;
+  float vkappa = a.vkappa;
+  const float* vchan = a.vchan ? a.vchan + ((size_t)l * a.H + h) * D : nullptr;
+  const float* kmean = nullptr;
+  if (a.ntiles > 0) {                            // the tile of (l, h); the tiles cover each once
+    int ti = 0;
+    while (ti + 1 < a.ntiles) {
+      const MixV& t = a.tile[ti];
+      if (l >= t.l0 && l < t.l0 + t.ls && h >= t.h0 && h < t.h0 + t.hs) break;
+      ++ti;
+    }
+    const MixV& t = a.tile[ti];
+    const size_t u = ((size_t)(l - t.l0) * t.hs + (h - t.h0)) * D;
+    vW = t.vW;
+    vkappa = t.vkappa;
+    vchan = t.vchan ? t.vchan + u : nullptr;
+    kmean = t.kmean ? t.kmean + u : nullptr;
+  }
+  if (vW > 1) fwht_lds_rows(orow, 1, 0, D, vW, vkappa);
   if (tid < D) {
     o = orow[pidx(tid)];
-    if (a.vchan) o = o / a.vchan[((size_t)l * a.H + h) * D + tid];
+    if (vchan) o = o / vchan[tid];
   }
   if (!ERR) {
+    // a tile whose keys carry a mean: every logit of the row is larger by q.mean, so the
+    // weights stay and the lse moves by sm * q.mean
+    float shift = 0.0f;
+    if (kmean && lse) {
+      red[0][tid] = (tid < D) ? (double)h2f(a.q[(size_t)rh * D + tid]) * (double)kmean[tid] : 0.0;
+      __syncthreads();
+      for (int st = kBlock / 2; st > 0; st >>= 1) {
+        if (tid < st) red[0][tid] += red[0][tid + st];
+        __syncthreads();
+      }
+      shift = a.sm * (float)red[0][0];
+    }
     if (tid < D) out[(size_t)rh * D + tid] = o;
-    if (tid == 0 && lse) lse[rh] = (Lq > 0.0) ? (float)(M + log(Lq)) : -INFINITY;
+    if (tid == 0 && lse) lse[rh] = (Lq > 0.0) ? (float)(M + log(Lq)) + shift : -INFINITY;
     if (tid == 0 && a.ctr && j % a.G == 0) a.ctr[rq * a.H + h] = 0;   // ready for the next call
     return;
   }
@@ -1433,6 +1576,114 @@ hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st) {
 }  // namespace kvq
 
 namespace kvq {
+
+static int code_bits(int cb, int bits) {
+  switch (cb) {
+    case KVQ_FP16: return 16;
+    case KVQ_TERNARY: return 2;
+    case KVQ_SIGN: return 1;
+    case KVQ_NF4: return 4;
+    case KVQ_INT8_SYM: return 8;
+    default: return bits;
+  }
+}
+
+static int mix_pair(const kvq_packed& k, const kvq_packed& v) {
+  const int kcb = k.codec.codebook, kb = code_bits(kcb, k.codec.bits);
+  const int vcb = v.codec.codebook, vb = code_bits(vcb, v.codec.bits);
+#define KVQ_MIX_ID(id, KCB, KB, VCB, VB) \
+  if (kcb == KCB && kb == KB && vcb == VCB && vb == VB) return id;
+  KVQ_MIX_PAIRS(KVQ_MIX_ID)
+#undef KVQ_MIX_ID
+  return -1;
+}
+
+bool mixed_decode_supported(const kvq_segment* segs, int n, int tokens) {
+  if (n < 1 || n > kMaxSegments) return false;
+  for (int i = 0; i < n; ++i) {
+    if (segs[i].token0 != 0 || segs[i].k->shape.tokens != tokens) return false;
+    if (mix_pair(*segs[i].k, *segs[i].v) < 0) return false;
+  }
+  return true;
+}
+
+static kvq_shape mixed_shape(const kvq_segment* segs, int layers, int heads, int tokens) {
+  kvq_shape s = segs[0].k->shape;
+  s.layers = layers;
+  s.heads = heads;
+  s.tokens = tokens;
+  return s;
+}
+
+size_t mixed_ws_bytes(const kvq_segment* segs, int layers, int heads, int tokens, int Hq, int n_q) {
+  const kvq_shape s = mixed_shape(segs, layers, heads, tokens);
+  const int S = decode_wave_splits(s, Hq, n_q);
+  return (size_t)s.batch * s.layers * n_q * Hq * S * (s.head_dim + 2) * sizeof(float);
+}
+
+static MixCodec mix_codec_of(const kvq_packed& p) {
+  const DevCodec d = dev_codec(p);
+  MixCodec m{};
+  m.codes = d.codes;
+  m.scales = d.scales;
+  m.mins = d.mins;
+  m.chan = d.chan;
+  m.row_bytes = (int)d.row_bytes;
+  m.ng = d.ng;
+  m.g = d.g;
+  m.W = d.W;
+  m.kappa = d.kappa;
+  m.cb = d.cb;
+  m.bits = d.bits;
+  return m;
+}
+
+hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q,
+                               const uint16_t* q, const int32_t* kv_len, float sm, float* out, float* lse,
+                               void* part, hipStream_t st) {
+  const kvq_shape s = mixed_shape(segs, layers, heads, tokens);
+  MArgs a{};
+  a.q = q;
+  a.kv_len = kv_len;
+  a.ws = static_cast<float*>(part);
+  a.sm_scale = sm;
+  a.B = s.batch; a.L = layers; a.H = heads; a.T = tokens; a.D = s.head_dim;
+  a.Hq = Hq; a.G = Hq / heads; a.n_q = n_q;
+  a.S = decode_wave_splits(s, Hq, n_q);
+  const int rpw = wave_rows_per_step(a.D);
+  a.chunk = ((tokens + a.S - 1) / a.S + rpw - 1) / rpw * rpw;
+  a.lpt_log2 = lpt_log2_of(a.D);
+  a.ntiles = n;
+  a.tab = host_tables();
+  CArgs c{};
+  c.ws = a.ws;
+  c.S = a.S; c.D = a.D; c.Hq = Hq; c.G = a.G; c.H = heads; c.L = layers; c.n_q = n_q;
+  c.ntiles = n;
+  c.q = q;
+  c.sm = sm;
+  for (int i = 0; i < n; ++i) {
+    const kvq_segment& g = segs[i];
+    MixTile& t = a.tile[i];
+    t.k = mix_codec_of(*g.k);
+    t.v = mix_codec_of(*g.v);
+    t.l0 = g.layer0; t.ls = g.k->shape.layers; t.h0 = g.head0; t.hs = g.k->shape.heads;
+    t.pair = mix_pair(*g.k, *g.v);
+    MixV& m = c.tile[i];
+    m.l0 = t.l0; m.ls = t.ls; m.h0 = t.h0; m.hs = t.hs;
+    m.vW = g.v->codec.rot_width > 1 ? g.v->codec.rot_width : 0;
+    m.vkappa = kappa_of(m.vW);
+    m.vchan = g.v->chan_scale;
+    m.kmean = g.k->mean;
+  }
+  const long long R = (long long)a.B * a.L * a.n_q;
+  const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
+  const size_t smem = ((size_t)2 * kWaveHeads * (17 * (a.D / 16) + 17) + 512 + kWaveHeads * 16 * 20 + 64) * sizeof(float);
+  k_decode_wave_mix<<<dim3(a.S / 4, a.H * HG, (unsigned)R), kBlock, smem, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_attn_combine<false><<<(unsigned)(R * Hq), kBlock, 0, st>>>(c, out, lse, nullptr, nullptr, ErrOut{});
+  return hipGetLastError();
+}
 
 hipError_t launch_lse_mean(const AttnProblem& pr, hipStream_t st) {
   const kvq_shape& sh = pr.k->shape;

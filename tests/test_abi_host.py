@@ -395,3 +395,31 @@ def test_segments_reject_a_missing_head(K):
     arr2, keep2 = _segs(K, parts)
     arr2[1].head0, arr2[2].head0 = 1, 3
     assert L.kvq_effective_bits(arr2, 3, 2, 4, 64) == pytest.approx(4.25)
+
+
+def test_segments_path_is_validated_before_launching(K):
+    """kvq_decode_attn_segments_ex: a path outside 0..2 is an argument error, and the
+    one-launch path refuses segments that are not whole-token tiles, or whose codec
+    pair the mixed kernel does not compile, before any launch."""
+    L = K._lib
+    whole = [(I4, I4, (1, 1, 4, 100, 128), 0, 0), ((1, 3, 64, 0, 0), I4, (1, 1, 4, 100, 128), 1, 0)]
+    arr, keep = _segs(K, whole)
+    need = L.kvq_decode_attn_segments_workspace(arr, 2, 2, 4, 16, 1)
+    assert need > 65536
+
+    def call(a, n, tokens, path, wsb=need):
+        return L.kvq_decode_attn_segments_ex(a, n, 2, 4, tokens, 16, 1, FAKE, None, 0.0, FAKE, None, FAKE, wsb, path,
+                                             None)
+    for bad in (-1, 3, 7):
+        assert call(arr, 2, 100, bad) == ERR_ARG
+    assert call(arr, 2, 100, 2, wsb=need - 1) == ERR_WORKSPACE
+    ranges = [(I4, I4, (1, 2, 4, 64, 128), 0, 0), (I4, I4, (1, 2, 4, 36, 128), 0, 64)]   # token ranges
+    arr2, keep2 = _segs(K, ranges)
+    need2 = L.kvq_decode_attn_segments_workspace(arr2, 2, 2, 4, 16, 1)
+    assert L.kvq_decode_attn_segments_ex(arr2, 2, 2, 4, 100, 16, 1, FAKE, None, 0.0, FAKE, None, FAKE, need2, 2,
+                                         None) == ERR_UNSUPPORTED
+    sym = [(I4, I4, (1, 1, 4, 100, 128), 0, 0), (I4, (9, 2, 64, 0, 0), (1, 1, 4, 100, 128), 1, 0)]
+    arr3, keep3 = _segs(K, sym)                             # 4-bit keys, 2-bit symmetric values: not compiled
+    need3 = L.kvq_decode_attn_segments_workspace(arr3, 2, 2, 4, 16, 1)
+    assert L.kvq_decode_attn_segments_ex(arr3, 2, 2, 4, 100, 16, 1, FAKE, None, 0.0, FAKE, None, FAKE, need3, 2,
+                                         None) == ERR_UNSUPPORTED

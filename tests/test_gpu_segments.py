@@ -6,6 +6,8 @@ recipe, Selective-Layer Decode Anchoring):
 * decode over segments (anchors at other precisions on chosen layers and tokens,
   per-layer codecs, a key mean on one segment) against the oracle's decode of the
   assembled cache, within the attention bars;
+* codec maps (per-layer and per-head codec pairs over whole-token tiles) decoded by
+  one launch, by per-segment launches and by the default route;
 * an append-then-decode loop gives, step by step, the decode of the fully quantised
   cache at the same lengths."""
 import numpy as np
@@ -69,22 +71,25 @@ def test_append_windows_equal_the_whole_tensor(cspec, D, with_mean):
         assert np.array_equal(b[rows], a[rows]) and np.array_equal(b[~rows], f[~rows])
 
 
-def _oracle_seg(K, x, codec, mean=None):
+def _oracle_seg(K, x, codec, mean=None, chan=None):
     oc = oracle_codec(K, O, codec)
-    w, s, z = O.quantize_pack(x, oc, None, mean)
-    return O.dequant(w, s, z, oc, x.shape, None, mean)
+    w, s, z = O.quantize_pack(x, oc, chan, mean)
+    return O.dequant(w, s, z, oc, x.shape, chan, mean)
 
 
-def _gpu_seg(K, x, codec, mean=None):
-    p = K.alloc_packed(codec, K.Shape(*x.shape), mean=to_dev(mean) if mean is not None else None)
+def _gpu_seg(K, x, codec, mean=None, chan=None):
+    p = K.alloc_packed(codec, K.Shape(*x.shape), mean=to_dev(mean) if mean is not None else None,
+                       chan_scale=to_dev(chan) if chan is not None else None)
     if codec.codebook == K.FP16:
         return K.packed_from_fp16(to_dev(x), K.Shape(*x.shape))
     K.kvq_quantize_pack(to_dev(x), p)
     return p
 
 
-def _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg=None):
-    """layout: list of (kcodec, vcodec, layer0, n_layers, token0, n_tokens[, head0, n_heads])."""
+def _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg=None, path=None, chan_seg=None):
+    """layout: list of (kcodec, vcodec, layer0, n_layers, token0, n_tokens[, head0, n_heads]);
+    segment mean_seg carries a key mean, segment chan_seg per-channel key scales
+    (calibrated on its sequence 0); path as for kvq_decode_attn_segments_ex."""
     import torch
     B, L, H, T, D = Kx.shape
     nq, Hq = q.shape[2], q.shape[3]
@@ -95,15 +100,16 @@ def _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg=None):
         ks = np.ascontiguousarray(Kx[:, l0:l0 + nl, h0:h0 + nh, t0:t0 + nt])
         vs = np.ascontiguousarray(Vx[:, l0:l0 + nl, h0:h0 + nh, t0:t0 + nt])
         mean = O.key_mean(ks) if i == mean_seg else None
-        segs.append(K.Segment(_gpu_seg(K, ks, kc, mean), _gpu_seg(K, vs, vc), l0, t0, h0))
-        ref.append((_oracle_seg(K, ks, kc, mean), _oracle_seg(K, vs, vc), l0, t0, h0))
+        chan = O.calibrate_chan_scale(ks[0]) if i == chan_seg else None
+        segs.append(K.Segment(_gpu_seg(K, ks, kc, mean, chan), _gpu_seg(K, vs, vc), l0, t0, h0))
+        ref.append((_oracle_seg(K, ks, kc, mean, chan), _oracle_seg(K, vs, vc), l0, t0, h0))
     Kd, Vd = O.assemble_segments(ref, B, L, H, T, D)
     out = torch.empty((B, L, nq, Hq, D), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, L, nq, Hq), dtype=torch.float32, device="cuda:0")
     wsb = K.kvq_decode_attn_segments_workspace(segs, L, H, Hq, nq)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda:0")
     K.kvq_decode_attn_segments(segs, L, H, T, Hq, nq, to_dev(q), to_dev(kv_len) if kv_len is not None else None, 0.0,
-                               out, lse, ws, wsb)
+                               out, lse, ws, wsb, path=path)
     torch.cuda.synchronize()
     ref_out, ref_lse = O.decode_attn(q, Kd, Vd, kv_len)
     _check_decode(to_np(out), to_np(lse), ref_out, ref_lse, kv_len)
@@ -145,6 +151,70 @@ def test_decode_over_segments(variant):
                   (k4, v2, 0, 4, 0, 704, 1, 2), (k3, v2, 0, 4, 0, 704, 3, 1)]
     announce(f"segments {variant}")
     _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg)
+
+
+MAPS = ["alloc_319", "heads_entropy", "anchor_layer", "g8_heads", "mfma_tile"]
+
+
+@pytest.mark.parametrize("path", [None, 1, 2])
+@pytest.mark.parametrize("variant", MAPS)
+def test_codec_map_in_one_launch(variant, path):
+    """Codec maps (every segment a whole-token tile of layers x KV heads) decoded by one
+    launch (path 2), by per-segment launches (path 1) and by the default choice, each
+    against the oracle's decode of the assembled cache."""
+    import kv_cache_bit_fwht_amd as K
+    A = K.INT_ABSMAX
+    mean_seg = chan_seg = None
+    if variant == "alloc_319":
+        # per-layer bits of [E21W] Result's 3.19-bit allocation (rotated, groups of 128):
+        # 2-bit keys on layers 2 and 7, 4-bit values on layers 1, 3 and 4, 3 bits elsewhere
+        w = synth.get("c3", L=8, T=600, n_q=2)
+        Kx, Vx = synth.gen_kv(w)
+        q, _ = synth.gen_queries(w)
+        kv_len = np.random.default_rng(31).integers(0, 601, (1, 8, 2)).astype(np.int32)
+        k2, k3 = K.Codec(A, 2, 128, 256), K.Codec(A, 3, 128, 256)
+        v3, v4 = K.Codec(A, 3, 128, 256), K.Codec(A, 4, 128, 256)
+        layout = [(k3, v3, 0, 1, 0, 600), (k3, v4, 1, 1, 0, 600), (k2, v3, 2, 1, 0, 600), (k3, v4, 3, 2, 0, 600),
+                  (k3, v3, 5, 2, 0, 600), (k2, v3, 7, 1, 0, 600)]
+        chan_seg = 3
+    elif variant == "heads_entropy":
+        # per-head key bits [5, 4, 4, 3] over 4-bit values, a key mean on head 0
+        w = synth.get("c3", B=2, L=3, T=520, n_q=2, k_head_scales=(3.0, 1.0, 1.0, 0.5), k_mean_share=0.3)
+        Kx, Vx = synth.gen_kv(w)
+        q, _ = synth.gen_queries(w)
+        kv_len = np.random.default_rng(32).integers(0, 521, (2, 3, 2)).astype(np.int32)
+        kv_len[1, 2, 1] = 0
+        v4 = K.Codec(A, 4, 128, 0)
+        layout = [(K.Codec(A, 5, 128, 256), v4, 0, 3, 0, 520, 0, 1), (K.Codec(A, 4, 128, 256), v4, 0, 3, 0, 520, 1, 2),
+                  (K.Codec(A, 3, 128, 256), v4, 0, 3, 0, 520, 3, 1)]
+        mean_seg = 0
+    elif variant == "anchor_layer":
+        # head_dim 128: an fp16 layer, then ternary / NF4+int4 / int8 / sign tiles
+        w = synth.get("c4", B=1, L=4, H=4, Hq=16, T=300, n_q=2)
+        Kx, Vx = synth.gen_kv(w)
+        q, kv_len = synth.gen_queries(w)
+        f16, tern = K.Codec(K.FP16), K.Codec(K.TERNARY, 2, 8, 0)
+        nf4, a4, i8 = K.Codec(K.NF4, 4, 64, 0), K.Codec(A, 4, 64, 0), K.Codec(K.INT8_SYM, 8, 128, 0)
+        sgn = K.Codec(K.SIGN, 1, 8, 0)
+        layout = [(f16, f16, 0, 1, 0, 300), (tern, tern, 1, 2, 0, 300, 0, 2), (nf4, a4, 1, 1, 0, 300, 2, 2),
+                  (i8, i8, 2, 1, 0, 300, 2, 2), (sgn, sgn, 3, 1, 0, 300)]
+    elif variant == "g8_heads":
+        # 8 query heads per KV head (two head groups per block row), rotated 2-bit values on head 0
+        w = synth.get("c3", L=2, H=2, Hq=16, T=400, n_q=2)
+        Kx, Vx = synth.gen_kv(w)
+        q, _ = synth.gen_queries(w)
+        kv_len = np.array([[[400, 0], [1, 333]]], dtype=np.int32)
+        layout = [(K.Codec(A, 2, 128, 0), K.Codec(A, 2, 128, 256), 0, 2, 0, 400, 0, 1),
+                  (K.Codec(A, 6, 64, 128), K.Codec(A, 3, 32, 0), 0, 2, 0, 400, 1, 1)]
+    else:
+        # a tile the MFMA kernel would take (4-bit rotated keys, 2-bit values) beside an fp16 layer
+        w = synth.get("c3", L=3, T=448, n_q=2)
+        Kx, Vx = synth.gen_kv(w)
+        q, kv_len = synth.gen_queries(w)
+        layout = [(K.Codec(K.FP16), K.Codec(K.FP16), 0, 1, 0, 448),
+                  (K.Codec(A, 4, 128, 256), K.Codec(A, 2, 128, 0), 1, 2, 0, 448)]
+    announce(f"codec map {variant} path={path}")
+    _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg, path, chan_seg)
 
 
 def test_append_then_decode_loop_matches_the_whole_cache():
