@@ -487,6 +487,100 @@ def entropy_workload(reps):
             "decode_step_us": round(t * 1e6, 1)}), flush=True)
 
 
+# [E21W] Result: the 3.19-bit allocation (rotated, groups of 128): 2-bit keys on layers
+# 2 and 7, 4-bit values on layers 1, 3 and 4, 3 bits everywhere else
+ALLOC_K_BITS = (3, 3, 2, 3, 3, 3, 3, 2)
+ALLOC_V_BITS = (3, 4, 3, 4, 4, 3, 3, 3)
+
+
+def allocation_workload(reps):
+    """c2a: the per-layer K/V bit allocation of [E21W] Result against rotated 4-bit and
+    3-bit caches at group 32 ([E21W] What I tested, variant B at 3 and 4 bits), on the
+    proxy-query probe shape (3 sequences x 8 layers x 4 KV heads x 6,000 tokens x 256;
+    queries are the keys at 128 positions in [3,000, 6,000), each attending the keys
+    before it).  Per sequence: mean attention output error and attention KL
+    (kvq_attn_error_ex).  Decode: one call over all 3 x 128 queries, the allocation as one
+    codec-map launch and as a launch per layer segment."""
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.get("c2")
+    log(f"generating {w.description}")
+    Kx, Vx = synth.gen_kv(w)
+    q, kv_len = synth.gen_queries(w, Kx)
+    B, L, H, T, D, Hq, nq = w.B, w.L, w.H, w.T, w.D, w.Hq, w.n_q
+    kd = torch.from_numpy(Kx.view(np.int16)).to(dev)
+    vd = torch.from_numpy(Vx.view(np.int16)).to(dev)
+    qd = torch.from_numpy(q.view(np.int16)).to(dev)
+    kvl = torch.from_numpy(kv_len).to(dev)
+    A = K.INT_ABSMAX
+
+    def errors(kp, vp, k16, v16, qq, kl_len, nl):
+        kl = torch.empty((B, nl, nq, Hq), dtype=torch.float32, device=dev)
+        re = torch.empty_like(kl)
+        wb = K.kvq_attn_error_workspace(kp.shape, Hq, nq)
+        wsp = torch.empty(wb, dtype=torch.uint8, device=dev)
+        K.kvq_attn_error_ex(k16, v16, kp, vp, Hq, nq, qq, kl_len, 0.0, wsp, wb, kl=kl, relerr=re)
+        torch.cuda.synchronize()
+        return kl.double().cpu().numpy(), re.double().cpu().numpy()
+
+    out = torch.empty((B, L, nq, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, L, nq, Hq), dtype=torch.float32, device=dev)
+    recs = []
+    shape = K.Shape(B, L, H, T, D)
+    for name, bits in (("rotated 4-bit g32 (variant B, q4_0-like)", 4), ("rotated 3-bit g32 (variant B)", 3)):
+        c = K.Codec(A, bits, 32, 256)
+        kp, vp = K.alloc_packed(c, shape, dev), K.alloc_packed(c, shape, dev)
+        K.kvq_quantize_pack(kd, kp)
+        K.kvq_quantize_pack(vd, vp)
+        kl, re = errors(kp, vp, kd, vd, qd, kvl, L)
+        wsb = K.kvq_decode_attn_workspace(shape, Hq, nq)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+        fn = lambda: K.kvq_decode_attn(kp, vp, Hq, nq, qd, kvl, 0.0, out, lse, ws, wsb)
+        fn()
+        t = _median_time(torch, fn, reps)
+        recs.append((name, [bits] * L, [bits] * L, K.kvq_bits_per_value(c, D), kl, re, {"decode_us": t}))
+        del kp, vp, ws
+    # the allocation: one segment per run of layers with the same (key bits, value bits)
+    runs, l0 = [], 0
+    for l in range(1, L + 1):
+        if l == L or (ALLOC_K_BITS[l], ALLOC_V_BITS[l]) != (ALLOC_K_BITS[l0], ALLOC_V_BITS[l0]):
+            runs.append((l0, l - l0))
+            l0 = l
+    segs, kl, re = [], np.zeros((B, L, nq, Hq)), np.zeros((B, L, nq, Hq))
+    bpv = 0.0
+    for l0, nl in runs:
+        sub = K.Shape(B, nl, H, T, D)
+        kc, vc = K.Codec(A, ALLOC_K_BITS[l0], 128, 256), K.Codec(A, ALLOC_V_BITS[l0], 128, 256)
+        k16 = kd[:, l0:l0 + nl].contiguous()
+        v16 = vd[:, l0:l0 + nl].contiguous()
+        kp, vp = K.alloc_packed(kc, sub, dev), K.alloc_packed(vc, sub, dev)
+        K.kvq_quantize_pack(k16, kp)
+        K.kvq_quantize_pack(v16, vp)
+        kls, res = errors(kp, vp, k16, v16, qd[:, l0:l0 + nl].contiguous(), kvl[:, l0:l0 + nl].contiguous(), nl)
+        kl[:, l0:l0 + nl], re[:, l0:l0 + nl] = kls, res
+        bpv += nl * (K.kvq_bits_per_value(kc, D) + K.kvq_bits_per_value(vc, D)) / 2
+        segs.append(K.Segment(kp, vp, l0, 0, 0))
+    wsb = K.kvq_decode_attn_segments_workspace(segs, L, H, Hq, nq)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    times = {}
+    for path, key in ((2, "decode_us"), (1, "decode_us_per_segment_launches")):
+        fn = lambda: K.kvq_decode_attn_segments(segs, L, H, T, Hq, nq, qd, kvl, 0.0, out, lse, ws, wsb, path=path)
+        fn()
+        times[key] = _median_time(torch, fn, reps)
+    recs.append((f"3.19-bit allocation, {len(runs)} layer segments", list(ALLOC_K_BITS), list(ALLOC_V_BITS), bpv / L,
+                 kl, re, times))
+    for name, kb, vb, bpv, kl, re, t in recs:
+        print(json.dumps({
+            "workload": f"c2a: B={B} L={L} H={H} T={T} D={D} Hq={Hq}, {nq} proxy queries per sequence and layer "
+                        f"(keys at positions in [3000, 6000), causal)",
+            "arm": name, "key_bits_per_layer": kb, "value_bits_per_layer": vb, "bits_per_value": round(bpv, 4),
+            "attention_error_per_sequence": [round(float(re[b].mean()), 4) for b in range(B)],
+            "KL_per_sequence": [round(float(kl[b].mean()), 5) for b in range(B)],
+            **{k: round(v * 1e6, 1) for k, v in t.items()}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -499,12 +593,13 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for hardware-counter passes: a known-size copy (the counters' "
                          "calibration), one quantize+pack pair and --decode-queries decode calls")
-    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v", "c3m", "c3a", "c3h"],
+    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v", "c3m", "c3a", "c3h", "c2a"],
                     help="c3: the headline line (default); c4/c5: one line per codec arm of those configs; "
                          "c3v: the 64K cache with each value codebook, with attention KL; "
                          "c3m: the 64K cache with a shared key mean, keys coded with and without it; "
                          "c3a: the 64K cache as decode segments with fp16 anchors, and the append path; "
-                         "c3h: per-head key bits from attention entropy, as head segments")
+                         "c3h: per-head key bits from attention entropy, as head segments; "
+                         "c2a: the per-layer 3.19-bit allocation on the proxy-query probe")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions per arm (c4/c5)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -517,6 +612,9 @@ def main():
         return
     if args.workload == "c3h":
         entropy_workload(args.reps)
+        return
+    if args.workload == "c2a":
+        allocation_workload(args.reps)
         return
     if args.workload != "c3":
         secondary(args.workload, args.reps)

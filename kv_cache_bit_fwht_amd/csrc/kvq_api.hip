@@ -566,7 +566,7 @@ kvq_status kvq_decode_attn_segments_ex(const kvq_segment* segs, int32_t n_seg, i
   const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)D));
   if (use_mix)
     return hip_status(launch_decode_mixed(segs, n_seg, layers, heads, tokens, q_heads, n_q, q, kv_len, sm, out, lse,
-                                          w + kWsCounterBytes, s));
+                                          w + kWsCounterBytes, true, s));
   const size_t rpl = (size_t)n_q * q_heads;                     // output rows per (sequence, layer)
   float* lacc = lse ? lse : reinterpret_cast<float*>(w + pl.lacc);
   hipError_t e = hipSuccess;

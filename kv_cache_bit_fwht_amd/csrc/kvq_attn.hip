@@ -1410,8 +1410,11 @@ static hipError_t launch_wave(const AArgs& a, long long R, hipStream_t st) {
 }
 
 // The codec pairs of the five workloads get their own instantiation (codes decoded
-// with compile-time widths); any other pair takes the runtime-codec one.
-static hipError_t dispatch_wave(const AArgs& a, long long R, hipStream_t st) {
+// with compile-time widths).  For any other pair nothing is launched and *compiled is
+// set false: the caller takes the codec-map kernel if it compiles the pair, else the
+// runtime-codec instance.
+static hipError_t dispatch_wave(const AArgs& a, long long R, hipStream_t st, bool* compiled) {
+  *compiled = true;
   const int kc = a.k.cb, kb = a.k.bits, vc = a.v.cb, vb = a.v.bits;
   auto is = [](int cb, int bits, int c2, int b2) { return cb == c2 && (bits == b2 || b2 < 0); };
   if (is(kc, kb, KVQ_INT_ABSMAX, 4) && is(vc, vb, KVQ_INT_ABSMAX, 2))
@@ -1453,8 +1456,11 @@ static hipError_t dispatch_wave(const AArgs& a, long long R, hipStream_t st) {
     return launch_wave<KVQ_INT_ABSMAX, 4, KVQ_LLOYD, 3>(a, R, st);
   if (kc == KVQ_RFFT_POLAR && vc == KVQ_FP16) return launch_wave<KVQ_RFFT_POLAR, 0, KVQ_FP16, 16>(a, R, st);
   if (kc == KVQ_RFFT_CART && vc == KVQ_FP16) return launch_wave<KVQ_RFFT_CART, 0, KVQ_FP16, 16>(a, R, st);
-  return launch_wave<-1, 0, -1, 0>(a, R, st);
+  *compiled = false;
+  return hipSuccess;
 }
+
+static int mix_pair(const kvq_packed& k, const kvq_packed& v);
 
 hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
   AArgs a = make_aargs(pr);
@@ -1467,8 +1473,19 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
     const int rpw = wave_rows_per_step(a.D);
     a.chunk = ((s.tokens + a.S - 1) / a.S + rpw - 1) / rpw * rpw;
     const long long R = (long long)a.B * a.L * a.n_q;
-    hipError_t e = dispatch_wave(a, R, st);
+    bool compiled = false;
+    hipError_t e = dispatch_wave(a, R, st, &compiled);
     if (e != hipSuccess) return e;
+    if (!compiled) {
+      if (!rk && mix_pair(*pr.k, *pr.v) >= 0) {      // a pair the codec-map kernel compiles: one tile
+        const kvq_segment sg{pr.k, pr.v, 0, 0, 0};
+        const kvq_shape& s = pr.k->shape;
+        return launch_decode_mixed(&sg, 1, s.layers, s.heads, s.tokens, pr.Hq, pr.n_q, pr.q, pr.kv_len,
+                                   pr.sm_scale, pr.out, pr.lse, pr.ws, false, st);
+      }
+      e = launch_wave<-1, 0, -1, 0>(a, R, st);
+      if (e != hipSuccess) return e;
+    }
     return launch_combine_partials(pr, a.S, nullptr, st);
   }
   const long long R = (long long)a.B * a.L * a.n_q;
@@ -1640,7 +1657,7 @@ static MixCodec mix_codec_of(const kvq_packed& p) {
 
 hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q,
                                const uint16_t* q, const int32_t* kv_len, float sm, float* out, float* lse,
-                               void* part, hipStream_t st) {
+                               void* part, bool mean_shift, hipStream_t st) {
   const kvq_shape s = mixed_shape(segs, layers, heads, tokens);
   MArgs a{};
   a.q = q;
@@ -1673,7 +1690,7 @@ hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int h
     m.vW = g.v->codec.rot_width > 1 ? g.v->codec.rot_width : 0;
     m.vkappa = kappa_of(m.vW);
     m.vchan = g.v->chan_scale;
-    m.kmean = g.k->mean;
+    m.kmean = mean_shift ? g.k->mean : nullptr;
   }
   const long long R = (long long)a.B * a.L * a.n_q;
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;

@@ -203,12 +203,14 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st);
 hipError_t launch_attn_error(const AttnProblem& pr, hipStream_t st);
 hipError_t launch_lse_mean(const AttnProblem& pr, hipStream_t st);
 // A codec map in one launch: segments that each cover every token of their (layer range
-// x head range) tile, with codec pairs the mixed decode kernel compiles.
+// x head range) tile, with codec pairs the mixed decode kernel compiles.  With
+// mean_shift the combine adds each tile's key-mean shift to the lse (otherwise the
+// caller does).
 bool mixed_decode_supported(const kvq_segment* segs, int n, int tokens);
 size_t mixed_ws_bytes(const kvq_segment* segs, int layers, int heads, int tokens, int Hq, int n_q);
 hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q,
                                const uint16_t* q, const int32_t* kv_len, float sm, float* out, float* lse,
-                               void* part, hipStream_t st);
+                               void* part, bool mean_shift, hipStream_t st);
 hipError_t launch_seg_init(float* out, float* lse, long long rows, int D, hipStream_t st);
 hipError_t launch_seg_prepare(const uint16_t* q, const int32_t* kvl, uint16_t* qs, int32_t* kvls, int B, int L,
                               int Ls, int l0, int n_q, int Hq, int j0, int hq, int D, int t0, int Ts, hipStream_t st);

@@ -180,6 +180,25 @@ def test_c3_value_codebooks_decode_and_error(arm):
     _run_case(K, Kx, Vx, q, None, kc, vc)
 
 
+@pytest.mark.parametrize("arm", ["map_pair", "map_pair_rot_v", "runtime"])
+def test_single_codec_routes_of_the_general_kernel(arm):
+    """Codec pairs without an instance of their own: one the codec-map kernel compiles
+    (decoded as a one-tile map) and one it does not (the runtime-codec instance)."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", B=2, L=2, T=610, n_q=2)
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    kv_len = np.random.default_rng(41).integers(0, 611, (2, 2, 2)).astype(np.int32)
+    if arm == "map_pair":
+        kc, vc = K.Codec(K.INT_ABSMAX, 2, 64, 256), K.Codec(K.INT_ABSMAX, 3, 32, 0)
+    elif arm == "map_pair_rot_v":
+        kc, vc = K.Codec(K.INT_ABSMAX, 6, 128, 0), K.Codec(K.INT_ABSMAX, 2, 128, 256)
+    else:
+        kc, vc = K.Codec(K.INT_MINMAX, 4, 32, 0), K.Codec(K.INT_SYM, 3, 64, 0)
+    announce(f"single codec route {arm}")
+    _run_case(K, Kx, Vx, q, kv_len, kc, vc, path=1)
+
+
 @pytest.mark.parametrize("arm", ["polar", "cart", "fwht6"])
 def test_c5_transform_arms(arm):
     import kv_cache_bit_fwht_amd as K
