@@ -739,7 +739,11 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
     for (int g = 0; g < kWaveHeads; ++g) {
       float x = 0.0f;
       if constexpr (KR) {
-        const float4* qv = reinterpret_cast<const float4*>(qsp + (g * LPT + j) * 20);
+        // the LDS offset is opaque per step, so the query spectrum is re-read here rather
+        // than hoisted out of the loop into 80 loop-carried registers
+        int qo = (g * LPT + j) * 20;
+        asm volatile("" : "+v"(qo));
+        const float4* qv = reinterpret_cast<const float4*>(qsp + qo);
         const float4 r0 = qv[0], r1 = qv[1], i0 = qv[2], i1 = qv[3], ny = qv[4];
         const float qr8[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
         const float qi8[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
@@ -809,8 +813,9 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
       load(it + 5, k2, v2);
     }
   }
-  // ---- sum the row slots; lanes of slot 0 write the partial (o in original value
-  // coordinates of the codec, m in natural-log units, l)
+  // ---- sum the row slots, then merge the block's 4 wavefronts (4 consecutive splits)
+  // through LDS into one partial per query head: o in the codec's value coordinates,
+  // m in natural-log units, l.  Partial index: blockIdx.x of gridDim.x per row.
 #pragma unroll
   for (int g = 0; g < kWaveHeads; ++g) {
     for (int m = LPT; m < 64; m <<= 1) lsum[g] += __shfl_xor(lsum[g], m);
@@ -818,20 +823,43 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
     for (int k = 0; k < 16; ++k)
       for (int m = LPT; m < 64; m <<= 1) acc[g][k] += __shfl_xor(acc[g][k], m);
   }
-  if (split < a.S && r == 0) {
-    constexpr float kLn2 = 0.6931471805599453f;
-    const int P = D + 2;
+  constexpr int NW = kBlock / 64;
+  __syncthreads();                                   // every wavefront is past its last LDS read
+  float* mo = smem;                                  // [NW][kWaveHeads][D] wavefront outputs
+  float* mm = mo + NW * kWaveHeads * D;              // [NW][kWaveHeads] reference maxima (log2 units)
+  float* ml = mm + NW * kWaveHeads;                  // [NW][kWaveHeads] sums
+  if (r == 0) {
 #pragma unroll
     for (int g = 0; g < kWaveHeads; ++g) {
-      if (g < GH) {
-        float* dst = a.ws + (((size_t)rq * a.Hq + (size_t)h * a.G + (size_t)kWaveHeads * hg + g) * a.S + split) * P;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) dst[16 * j + k] = acc[g][k];
-        if (j == 0) {
-          dst[D] = (mref[g] == -INFINITY) ? -INFINITY : mref[g] * kLn2;
-          dst[D + 1] = lsum[g];
-        }
+      for (int k = 0; k < 16; ++k) mo[(wave * kWaveHeads + g) * D + 16 * j + k] = acc[g][k];
+      if (j == 0) {
+        mm[wave * kWaveHeads + g] = mref[g];
+        ml[wave * kWaveHeads + g] = lsum[g];
       }
+    }
+  }
+  __syncthreads();
+  constexpr float kLn2 = 0.6931471805599453f;
+  const int P = D + 2;
+  for (int p = tid; p < GH * D; p += kBlock) {
+    const int g = p / D, d = p - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w * kWaveHeads + g]);
+    float o = 0.0f, lw = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float m = mm[w * kWaveHeads + g];
+      const float wt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+      o = __builtin_fmaf(wt, mo[(w * kWaveHeads + g) * D + d], o);
+      lw = __builtin_fmaf(wt, ml[w * kWaveHeads + g], lw);
+    }
+    float* dst = a.ws + (((size_t)rq * a.Hq + (size_t)h * a.G + (size_t)kWaveHeads * hg + g) * gridDim.x + blockIdx.x) * P;
+    dst[d] = o;
+    if (d == 0) {
+      dst[D] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+      dst[D + 1] = lw;
     }
   }
 }
@@ -1401,10 +1429,18 @@ static size_t split_smem(const AArgs& a, bool err) {
   return f * sizeof(float) + (2 * kMaxG * TB + 16 * kMaxG) * acc_bytes;
 }
 
+// Dynamic LDS of the wavefront kernels: query rows, rFFT tables and levels during the
+// loop, then the 4 wavefronts' outputs for the block merge.
+static size_t wave_smem_bytes(int D) {
+  const size_t loop = (size_t)2 * kWaveHeads * (17 * (D / 16) + 17) + 512 + kWaveHeads * 16 * 20 + 64;
+  const size_t merge = (size_t)(kBlock / 64) * kWaveHeads * (D + 2);
+  return std::max(loop, merge) * sizeof(float);
+}
+
 template <int KCB, int KB, int VCB, int VB>
 static hipError_t launch_wave(const AArgs& a, long long R, hipStream_t st) {
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
-  const size_t smem = ((size_t)2 * kWaveHeads * (17 * (a.D / 16) + 17) + 512 + kWaveHeads * 16 * 20 + 64) * sizeof(float);
+  const size_t smem = wave_smem_bytes(a.D);
   k_decode_wave<KCB, KB, VCB, VB><<<dim3(a.S / 4, a.H * HG, (unsigned)R), kBlock, smem, st>>>(a);
   return hipGetLastError();
 }
@@ -1486,7 +1522,7 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
       e = launch_wave<-1, 0, -1, 0>(a, R, st);
       if (e != hipSuccess) return e;
     }
-    return launch_combine_partials(pr, a.S, nullptr, st);
+    return launch_combine_partials(pr, a.S / 4, nullptr, st);   // one partial per block of 4 splits
   }
   const long long R = (long long)a.B * a.L * a.n_q;
   const size_t smem = split_smem(a, false);
@@ -1674,7 +1710,8 @@ hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int h
   a.tab = host_tables();
   CArgs c{};
   c.ws = a.ws;
-  c.S = a.S; c.D = a.D; c.Hq = Hq; c.G = a.G; c.H = heads; c.L = layers; c.n_q = n_q;
+  c.S = a.S / 4;                                     // one partial per block of 4 splits
+  c.D = a.D; c.Hq = Hq; c.G = a.G; c.H = heads; c.L = layers; c.n_q = n_q;
   c.ntiles = n;
   c.q = q;
   c.sm = sm;
@@ -1694,7 +1731,7 @@ hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int h
   }
   const long long R = (long long)a.B * a.L * a.n_q;
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
-  const size_t smem = ((size_t)2 * kWaveHeads * (17 * (a.D / 16) + 17) + 512 + kWaveHeads * 16 * 20 + 64) * sizeof(float);
+  const size_t smem = wave_smem_bytes(a.D);
   k_decode_wave_mix<<<dim3(a.S / 4, a.H * HG, (unsigned)R), kBlock, smem, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
