@@ -1,9 +1,10 @@
 // MFMA decode attention over a packed cache with 4-bit signed-absmax keys
-// (group 128 or 256, any Walsh-Hadamard rotation) and 2-bit signed-absmax
-// values (group >= 16), head_dim 256, up to 4 query heads per KV head: the
-// 64K-token decode workload of [E22L] ("Can 4-bit keys and 2-bit values hit a
-// 1M-token memory budget?", What I tested: arm A, rotated 4-bit keys and 2-bit
-// values at group 128).
+// (group 128 or 256, any Walsh-Hadamard rotation) and 2- or 4-bit values on an
+// affine grid (signed absmax or the symmetric grid, group >= 64), head_dim 256,
+// up to 4 query heads per KV head: the 64K-token decode workload of [E22L] ("Can
+// 4-bit keys and 2-bit values hit a 1M-token memory budget?", What I tested: arm
+// A, rotated 4-bit keys and 2-bit values at group 128), and the same cache with
+// 4-bit values (the q4_0-style pair of [LCPP] Finding 1).
 //
 // Why MFMA: at 0.39 bytes per cached value, HBM speed leaves about two VALU
 // lane-ops per value, while unpacking plus four grouped-head multiply-adds per
@@ -20,13 +21,16 @@
 //  * online softmax per head against a reference maximum that moves only when a
 //    logit exceeds it by more than 1 (log2 units), so rescaling is rare.
 //  * P.V: v_mfma_f32_4x4x4_16b_f16, 16 blocks of (4 heads x 4 tokens) x
-//    (4 tokens x 4 dims): lane l owns value word l%16 (16 dims, one scale
-//    group) for tokens 8(l/16)..+7; A = fp16(p) * s_v, B = one byte of each of
-//    4 tokens' words masked to its low 2, 4, 6 or 8 bits as fp16 subnormals, so
-//    four accumulators per byte hold prefix sums of its fields weighted 1, 4,
-//    16, 64 and the fields come out as differences after the loop.
-//    Output: 2^24 * field - o * sum of the weights per group, o = 2 for signed
-//    absmax codes (levels c - 2) and 1.5 for the symmetric grid (levels c - 1.5).
+//    (4 tokens x 4 dims): lane l owns value dims 16(l%16)..+15 (one scale
+//    group; one code word at 2 bits, two at 4 bits) for tokens 8(l/16)..+7;
+//    A = fp16(p) * s_v, B = one byte of each of 4 tokens' codes masked to its
+//    low 2, 4, 6 and 8 bits (2-bit codes) or its low 4 and 8 bits (4-bit codes)
+//    as fp16 subnormals, so the accumulators of a byte hold prefix sums of its
+//    fields weighted 1, 4, 16, 64 (or 1, 16) and the fields come out as
+//    differences after the loop: 16 accumulators either way.
+//    Output: 2^24 * field - o * sum of the weights per group, o = 2^(b-1) for
+//    signed absmax codes (levels c - 2^(b-1)) and (2^b - 1)/2 for the symmetric
+//    grid.
 // Several blocks of 8 wavefronts (two per SIMD) share the tokens of one (query,
 // KV head): each block claims chunks of steps from a device-wide counter of the
 // unit and hands their steps to its wavefronts from an LDS counter, then merges
@@ -56,7 +60,7 @@ constexpr int kMaxSlots = kMaxChunks + 4;
 struct FArgs {
   const uint8_t* kc;               // key codes, 128 B per row
   const uint16_t* ks;              // key scales, nks per row
-  const uint8_t* vc;               // value codes, 64 B per row
+  const uint8_t* vc;               // value codes, 64 B (2-bit) or 128 B (4-bit) per row
   const uint16_t* vs;              // value scales, nvs per row
   const uint16_t* q;
   const int32_t* kv_len;
@@ -80,15 +84,15 @@ struct FArgs {
 
 __device__ __forceinline__ uint32_t h2bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
 
-// Lane (kg, n16) of a wavefront step: key code words of its two QK tiles, value
-// word n16 of tokens 8kg..8kg+7, and the scale words of one token, 8kg + n16%8;
-// the other lanes of its 16-lane row fetch those of the other seven tokens and a
-// DPP row broadcast hands them round when they are used.
-template <int NVS>
+// Lane (kg, n16) of a wavefront step: key code words of its two QK tiles, the value
+// codes of dims 16 n16..16 n16+15 of tokens 8kg..8kg+7, and the scale words of one
+// token, 8kg + n16%8; the other lanes of its 16-lane row fetch those of the other
+// seven tokens and a DPP row broadcast hands them round when they are used.
+template <int NVS, int VB>
 struct StepData {
   u32x4_t kw[2][2];    // key codes: QK tile u, row half (words 4kg.. and 16+4kg..)
   uint32_t ks;         // key scale(s) of token 8kg + n16%8 (fp16; both groups when there are two)
-  uint32_t vw[8];      // value word n16 of tokens 8kg + j
+  uint32_t vw[4 * VB];  // 2-bit: word n16 of token 8kg + j at [j]; 4-bit: words 2 n16, 2 n16 + 1 at [2j], [2j + 1]
   uint32_t vs[NVS == 4 ? 2 : 1];   // value scales of token 8kg + n16%8
 };
 
@@ -96,18 +100,18 @@ struct StepData {
 struct LaneOffsets {
   uint32_t k[2];       // key code bytes of QK tile u (row half 0; half 1 is +64)
   uint32_t ks;         // key scale row of token 8kg + n16%8
-  uint32_t v;          // value code bytes of token 8kg, word n16
+  uint32_t v;          // value code bytes of token 8kg, dims 16 n16..
   uint32_t vs;         // value scale row of token 8kg + n16%8
 };
 
-template <int NKS, int NVS>
+template <int NKS, int NVS, int VB>
 __device__ __forceinline__ LaneOffsets lane_offsets(int kg, int n16) {
   LaneOffsets o;
 #pragma unroll
   for (int u = 0; u < 2; ++u) o.k[u] = (uint32_t)(8 * (n16 >> 2) + 4 * u + (n16 & 3)) * 128u + 16u * kg;
   const uint32_t sc = (uint32_t)(8 * kg + (n16 & 7));
   o.ks = sc * 2u * NKS;
-  o.v = (uint32_t)(8 * kg) * 64u + 4u * n16;
+  o.v = (uint32_t)(8 * kg) * (32u * VB) + (uint32_t)(2 * VB) * n16;
   o.vs = sc * 2u * NVS;
   return o;
 }
@@ -116,8 +120,8 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int kg, int n16) {
 // address is a scalar base plus the lane's 32-bit byte offset; the offsets pass
 // through an empty asm so that the compiler cannot fold them into loop-invariant
 // 64-bit per-lane pointers (two registers per stream).
-template <int NKS, int NVS>
-__device__ __forceinline__ void load_step(const FArgs& a, size_t rb, LaneOffsets o, StepData<NVS>& d) {
+template <int NKS, int NVS, int VB>
+__device__ __forceinline__ void load_step(const FArgs& a, size_t rb, LaneOffsets o, StepData<NVS, VB>& d) {
   asm volatile("" : "+v"(o.k[0]), "+v"(o.k[1]), "+v"(o.ks), "+v"(o.v), "+v"(o.vs));
   const char* kb = reinterpret_cast<const char*>(a.kc) + rb * 128;
 #pragma unroll
@@ -128,9 +132,18 @@ __device__ __forceinline__ void load_step(const FArgs& a, size_t rb, LaneOffsets
   const char* ksb = reinterpret_cast<const char*>(a.ks) + rb * (2 * NKS);
   if constexpr (NKS == 2) d.ks = *reinterpret_cast<const uint32_t*>(ksb + o.ks);
   else d.ks = *reinterpret_cast<const uint16_t*>(ksb + o.ks);
-  const char* vb = reinterpret_cast<const char*>(a.vc) + rb * 64;
+  const char* vb = reinterpret_cast<const char*>(a.vc) + rb * (32 * VB);
+  if constexpr (VB == 2) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) d.vw[j] = *reinterpret_cast<const uint32_t*>(vb + o.v + 64 * j);
+    for (int j = 0; j < 8; ++j) d.vw[j] = *reinterpret_cast<const uint32_t*>(vb + o.v + 64 * j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x2_t t = *reinterpret_cast<const u32x2_t*>(vb + o.v + 128 * j);
+      d.vw[2 * j] = t[0];
+      d.vw[2 * j + 1] = t[1];
+    }
+  }
   const char* vsb = reinterpret_cast<const char*>(a.vs) + rb * (2 * NVS);
   if constexpr (NVS == 4) {
     const u32x2_t v2 = *reinterpret_cast<const u32x2_t*>(vsb + o.vs);
@@ -212,7 +225,7 @@ __device__ __forceinline__ int claim_global(int* ctr) {
 // wavefronts that share a SIMD do not run at the same speed (the older one is
 // issued first), so the block's 32-token steps are handed out dynamically from an
 // LDS counter instead of being split evenly in advance.
-template <int NKS, int NVS>
+template <int NKS, int NVS, int VB>
 __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   constexpr int NW = kFastBlock / 64;                // wavefronts per block
   __shared__ __align__(16) float qs[4][kFastD + 16];
@@ -277,14 +290,14 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     qraw = *reinterpret_cast<const u32x2_t*>(qsrc + (size_t)wave * kFastD + 4 * lane);
     if (a.kchan) kch = *reinterpret_cast<const float4_t*>(a.kchan + ((size_t)l * a.H + h) * kFastD + 4 * lane);
   }
-  const LaneOffsets lofs = lane_offsets<NKS, NVS>(kg, n16);
+  const LaneOffsets lofs = lane_offsets<NKS, NVS, VB>(kg, n16);
   // local indices wave and wave + NW of slot 0 (chunk x, C >= 16) are handed out statically
   auto first_step = [&](int k) { return (x < total_chunks && (x << cl2) + k < total_steps) ? (x << cl2) + k : -1; };
   int i0 = first_step(wave), i1 = first_step(wave + NW);   // steps held by the two buffers (-1: none)
   int last = i1 >= 0 ? i1 : i0;                       // the wavefront's latest valid step
-  StepData<NVS> b0, b1;
-  load_step<NKS, NVS>(a, step_row(i0, last), lofs, b0);
-  load_step<NKS, NVS>(a, step_row(i1, last), lofs, b1);
+  StepData<NVS, VB> b0, b1;
+  load_step<NKS, NVS, VB>(a, step_row(i0, last), lofs, b0);
+  load_step<NKS, NVS, VB>(a, step_row(i1, last), lofs, b1);
 
   // ---- query prologue, one wavefront per query head (no block barrier until the end):
   // q in the key coordinates (divide by the channel scale, rotate: strides 1 and 2 in the
@@ -375,7 +388,7 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
 
   // One 32-token step on the loaded data `cur` (consumed in place: no register copies,
   // so the other buffer's loads stay in flight while this one computes).
-  auto process = [&](const StepData<NVS>& cur, const int t0) {
+  auto process = [&](const StepData<NVS, VB>& cur, const int t0) {
     // ---- Q.K^T
     float4_t cq[2][2];
 #pragma unroll
@@ -463,23 +476,29 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
       aw[s2 >> 1][2 * (s2 & 1)] = w2[0];
       aw[s2 >> 1][2 * (s2 & 1) + 1] = w2[1];
     }
-    // ---- P.V: byte k of the value words of tokens (4s..4s+3) holds dims 4k..4k+3 of this
-    // lane's word.  B = the byte masked to its low 2, 4, 6 and 8 bits (fp16 subnormals),
-    // so the four accumulators of byte k hold prefix sums of the fields weighted 1, 4,
-    // 16, 64; the fields are separated after the loop.
+    // ---- P.V: byte k of the lane's value codes of tokens (4s..4s+3) holds dims 4k..4k+3
+    // (2-bit) or 2k, 2k+1 (4-bit) of its 16.  B = the byte masked to its low 2, 4, 6 and 8
+    // bits, or its low 4 and 8 bits (fp16 subnormals), so the accumulators of byte k hold
+    // prefix sums of the fields weighted 1, 4, 16, 64 (or 1, 16); the fields are
+    // separated after the loop.
+    constexpr int NB = (VB == 2) ? 4 : 8;            // code bytes per lane and token
+    constexpr int NM = (VB == 2) ? 4 : 2;            // masks per byte
 #pragma unroll
     for (int s4 = 0; s4 < 2; ++s4) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t sel = (uint32_t)k | (0x0Cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0Cu << 24);
-        const uint32_t r01 = __builtin_amdgcn_perm(cur.vw[4 * s4 + 1], cur.vw[4 * s4 + 0], sel);
-        const uint32_t r23 = __builtin_amdgcn_perm(cur.vw[4 * s4 + 3], cur.vw[4 * s4 + 2], sel);
+      for (int k = 0; k < NB; ++k) {
+        const int kb = k & 3, wi = k >> 2;           // byte of the word, word of the lane (4-bit)
+        const uint32_t sel = (uint32_t)kb | (0x0Cu << 8) | ((uint32_t)(4 + kb) << 16) | (0x0Cu << 24);
+        const int W = VB / 2;                        // code words per lane and token
+        const uint32_t r01 = __builtin_amdgcn_perm(cur.vw[W * (4 * s4 + 1) + wi], cur.vw[W * (4 * s4 + 0) + wi], sel);
+        const uint32_t r23 = __builtin_amdgcn_perm(cur.vw[W * (4 * s4 + 3) + wi], cur.vw[W * (4 * s4 + 2) + wi], sel);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const uint32_t mask = (0x00040004u << (2 * ii)) - 0x00010001u;   // low 2(ii+1) bits of each half
-          const u32x2_t bp = (ii == 3) ? u32x2_t{r01, r23} : u32x2_t{r01 & mask, r23 & mask};
+        for (int ii = 0; ii < NM; ++ii) {
+          // low VB(ii+1) bits of each half
+          const uint32_t mask = ((0x00010001u << (VB * (ii + 1))) - 0x00010001u);
+          const u32x2_t bp = (ii == NM - 1) ? u32x2_t{r01, r23} : u32x2_t{r01 & mask, r23 & mask};
           const half4_t bv = __builtin_bit_cast(half4_t, bp);
-          acc[4 * k + ii] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw[s4], bv, acc[4 * k + ii], 0, 0, 0);
+          acc[NM * k + ii] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw[s4], bv, acc[NM * k + ii], 0, 0, 0);
         }
       }
     }
@@ -515,12 +534,12 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     process(b0, i0 * kStep);
     i0 = claim();
     if (i0 >= 0) last = i0;
-    load_step<NKS, NVS>(a, step_row(i0, last), lofs, b0);
+    load_step<NKS, NVS, VB>(a, step_row(i0, last), lofs, b0);
     if (i1 < 0) break;
     process(b1, i1 * kStep);
     i1 = claim();
     if (i1 >= 0) last = i1;
-    load_step<NKS, NVS>(a, step_row(i1, last), lofs, b1);
+    load_step<NKS, NVS, VB>(a, step_row(i1, last), lofs, b1);
   }
 
   // ---- reduce the token subsets of the four lane groups (same word, kg = 0..3)
@@ -546,13 +565,23 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     const float wsum[4] = {ws0, ws1, ws2, ws3};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      if constexpr (VB == 2) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // prefix sums M1..M4 of byte k -> fields f0 = M1, f1 = (M2-M1)/4, f2 = (M3-M2)/16, f3 = (M4-M3)/64
-        const float m1 = acc[4 * k][c], m2 = acc[4 * k + 1][c], m3 = acc[4 * k + 2][c], m4 = acc[4 * k + 3][c];
-        const float f[4] = {m1, (m2 - m1) * 0.25f, (m3 - m2) * 0.0625f, (m4 - m3) * 0.015625f};
+        for (int k = 0; k < 4; ++k) {
+          // prefix sums M1..M4 of byte k -> fields f0 = M1, f1 = (M2-M1)/4, f2 = (M3-M2)/16, f3 = (M4-M3)/64
+          const float m1 = acc[4 * k][c], m2 = acc[4 * k + 1][c], m3 = acc[4 * k + 2][c], m4 = acc[4 * k + 3][c];
+          const float f[4] = {m1, (m2 - m1) * 0.25f, (m3 - m2) * 0.0625f, (m4 - m3) * 0.015625f};
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) so[wave][c][16 * n16 + 4 * k + ii] = f[ii] * 16777216.0f - a.voff * wsum[c];
+          for (int ii = 0; ii < 4; ++ii) so[wave][c][16 * n16 + 4 * k + ii] = f[ii] * 16777216.0f - a.voff * wsum[c];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          // prefix sums M1, M2 of byte k -> fields f0 = M1, f1 = (M2-M1)/16
+          const float m1 = acc[2 * k][c], m2 = acc[2 * k + 1][c];
+          so[wave][c][16 * n16 + 2 * k] = m1 * 16777216.0f - a.voff * wsum[c];
+          so[wave][c][16 * n16 + 2 * k + 1] = ((m2 - m1) * 0.0625f) * 16777216.0f - a.voff * wsum[c];
+        }
       }
     }
   }
@@ -717,8 +746,9 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   if (Hq / s.heads > 4) return false;
   if (k.codec.codebook != KVQ_INT_ABSMAX || k.codec.bits != 4) return false;
   if (k.codec.group != 128 && k.codec.group != 256) return false;
-  // 2-bit values: signed absmax (levels c - 2) or the symmetric grid (levels c - 1.5)
-  if ((v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) || v.codec.bits != 2) return false;
+  // 2- or 4-bit values: signed absmax (levels c - 2^(b-1)) or the symmetric grid (levels c - (2^b - 1)/2)
+  if (v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) return false;
+  if (v.codec.bits != 2 && v.codec.bits != 4) return false;
   if (v.codec.group < 64) return false;   // a P.V block's 4 value words share one scale group
   if (v.chan_scale) return false;
   return true;
@@ -748,6 +778,19 @@ size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q) {
   const int bpu = fast_blocks_per_unit(s, n_q);
   const size_t b = (size_t)s.batch * s.layers * n_q * Hq * bpu * (kFastD + 2) * sizeof(float);
   return (b + 255) / 256 * 256;
+}
+
+template <int VB>
+static void launch_mfma(const FArgs& a, dim3 grid, hipStream_t st) {
+  if (a.nks == 2) {
+    if (a.nvs == 1) k_decode_mfma<2, 1, VB><<<grid, kFastBlock, 0, st>>>(a);
+    else if (a.nvs == 2) k_decode_mfma<2, 2, VB><<<grid, kFastBlock, 0, st>>>(a);
+    else k_decode_mfma<2, 4, VB><<<grid, kFastBlock, 0, st>>>(a);
+  } else {
+    if (a.nvs == 1) k_decode_mfma<1, 1, VB><<<grid, kFastBlock, 0, st>>>(a);
+    else if (a.nvs == 2) k_decode_mfma<1, 2, VB><<<grid, kFastBlock, 0, st>>>(a);
+    else k_decode_mfma<1, 4, VB><<<grid, kFastBlock, 0, st>>>(a);
+  }
 }
 
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
@@ -781,7 +824,8 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
     a.vkappa = (a.vW > 1) ? ((e % 2 == 0) ? ldexpf(1.0f, -e / 2) : (float)(1.0 / std::sqrt((double)a.vW))) : 1.0f;
   }
   a.sm_scale = pr.sm_scale;
-  a.voff = (v.codec.codebook == KVQ_INT_SYM) ? 1.5f : 2.0f;
+  const int vb = v.codec.bits;
+  a.voff = (v.codec.codebook == KVQ_INT_SYM) ? 0.5f * (float)((1 << vb) - 1) : (float)(1 << (vb - 1));
   a.blocks_per_unit = fast_blocks_per_unit(s, pr.n_q);
   a.chunk_log2 = fast_chunk_log2(s);
   // shared chunk counters when the rows fit the workspace's counter region
@@ -794,15 +838,8 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
   a.lse = pr.lse;
   const long long units = (long long)s.batch * s.layers * s.heads;
   const dim3 grid(a.blocks_per_unit, (unsigned)units, (unsigned)pr.n_q);
-  if (a.nks == 2) {
-    if (a.nvs == 1) k_decode_mfma<2, 1><<<grid, kFastBlock, 0, st>>>(a);
-    else if (a.nvs == 2) k_decode_mfma<2, 2><<<grid, kFastBlock, 0, st>>>(a);
-    else k_decode_mfma<2, 4><<<grid, kFastBlock, 0, st>>>(a);
-  } else {
-    if (a.nvs == 1) k_decode_mfma<1, 1><<<grid, kFastBlock, 0, st>>>(a);
-    else if (a.nvs == 2) k_decode_mfma<1, 2><<<grid, kFastBlock, 0, st>>>(a);
-    else k_decode_mfma<1, 4><<<grid, kFastBlock, 0, st>>>(a);
-  }
+  if (vb == 2) launch_mfma<2>(a, grid, st);
+  else launch_mfma<4>(a, grid, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
   if (v.codec.rot_width > 1 || v.chan_scale) return launch_combine_partials(pr, a.blocks_per_unit, a.ctr, st);

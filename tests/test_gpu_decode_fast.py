@@ -1,4 +1,4 @@
-"""GPU parity of the MFMA decode-attention kernel (4-bit keys, 2-bit values,
+"""GPU parity of the MFMA decode-attention kernel (4-bit keys, 2- or 4-bit values,
 head_dim 256) against the CPU oracle, and against the general kernel.
 
 Bar: outputs within 2e-3 relative L2 per row, lse within 1e-4 absolute.  The
@@ -41,7 +41,8 @@ def test_fast_c3_shape_shrunk():
 
 
 @pytest.mark.parametrize("variant", ["kgroup256", "vgroup64", "vgroup256", "rot128", "norot", "G2", "G1",
-                                     "vrot", "vsym", "vsym_rot"])
+                                     "vrot", "vsym", "vsym_rot", "v4", "v4_g64", "v4_g256_k256", "v4_rot",
+                                     "v4_sym", "v4_sym_rot", "v4_G1"])
 def test_fast_variants(variant):
     import kv_cache_bit_fwht_amd as K
     kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
@@ -66,6 +67,21 @@ def test_fast_variants(variant):
         vc = K.Codec(K.INT_SYM, 2, 128, 0)
     elif variant == "vsym_rot":
         vc = K.Codec(K.INT_SYM, 2, 128, 256)
+    elif variant == "v4":
+        vc = K.Codec(K.INT_ABSMAX, 4, 128, 0)
+    elif variant == "v4_g64":
+        vc = K.Codec(K.INT_ABSMAX, 4, 64, 0)
+    elif variant == "v4_g256_k256":
+        kc, vc = K.Codec(K.INT_ABSMAX, 4, 256, 256), K.Codec(K.INT_ABSMAX, 4, 256, 0)
+    elif variant == "v4_rot":
+        vc = K.Codec(K.INT_ABSMAX, 4, 128, 256)
+    elif variant == "v4_sym":
+        vc = K.Codec(K.INT_SYM, 4, 128, 0)
+    elif variant == "v4_sym_rot":
+        vc = K.Codec(K.INT_SYM, 4, 64, 128)
+    elif variant == "v4_G1":
+        w = w.with_sizes(Hq=4)
+        vc = K.Codec(K.INT_ABSMAX, 4, 128, 0)
     announce(f"mfma variant {variant}")
     _case(K, w, kc, vc)
 
@@ -86,6 +102,15 @@ def test_fast_many_blocks_per_unit():
     kv_len = np.array([[[16384, 9000]]], dtype=np.int32)
     announce("mfma many blocks per unit")
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), kv_len)
+
+
+def test_fast_4bit_values_many_blocks_and_lengths():
+    """4-bit values: 32 blocks per unit on a counter, causal lengths ending mid-step."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=1, T=16384, n_q=3)
+    kv_len = np.array([[[16384, 9001, 31]]], dtype=np.int32)
+    announce("mfma 4-bit values, many blocks per unit")
+    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0), kv_len)
 
 
 def test_fast_static_chunks_many_rows():
