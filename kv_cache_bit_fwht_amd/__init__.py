@@ -71,6 +71,13 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_bit_fwht_amd.build` "
                           "(or __graft_entry__.build()); there is no CPU fallback")
+    # torch (the device-memory and stream provider) ships its own HIP runtime; loading it
+    # first makes this library bind to that same runtime instead of a second copy from
+    # the ROCm install, whose kernels could not use torch's allocations
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_double
     sig = {

@@ -1,5 +1,6 @@
-// MFMA decode attention over a packed cache with 4-bit signed-absmax keys
-// (group 128 or 256, any Walsh-Hadamard rotation) and 2- or 4-bit values on an
+// MFMA decode attention over a packed cache with 3-, 4- or 5-bit signed-absmax keys
+// (group 128 or 256, any Walsh-Hadamard rotation) and
+// 2- or 4-bit values on an
 // affine grid (signed absmax or the symmetric grid, group >= 64), head_dim 256,
 // up to 4 query heads per KV head: the 64K-token decode workload of [E22L] ("Can
 // 4-bit keys and 2-bit values hit a 1M-token memory budget?", What I tested: arm
@@ -17,7 +18,10 @@
 //    fp16 subnormals (code c -> c*2^-24, exact), B = the rotated query in fp16
 //    with the 4 heads replicated over the 16 columns, so lane (kg, n) ends with
 //    the logits of head n%4 for tokens 8kg..8kg+7.  Logit = sum over the two
-//    scale groups of s_g * (2^24 C_g - 8 sum_g q), times the softmax scale.
+//    scale groups of s_g * (2^24 C_g - 2^(b-1) sum_g q), times the softmax
+//    scale.  At 4 bits one AND places two codes 16 bits apart (dims e and e+4 of
+//    a word) in their fp16 halves; at other widths each code is cut out with a
+//    bit-field extract and pairs are packed with a shift-or.
 //  * online softmax per head against a reference maximum that moves only when a
 //    logit exceeds it by more than 1 (log2 units), so rescaling is rare.
 //  * P.V: v_mfma_f32_4x4x4_16b_f16, 16 blocks of (4 heads x 4 tokens) x
@@ -58,7 +62,7 @@ constexpr int kMaxChunks = 256;    // chunks per (query row, KV head) at most
 constexpr int kMaxSlots = kMaxChunks + 4;
 
 struct FArgs {
-  const uint8_t* kc;               // key codes, 128 B per row
+  const uint8_t* kc;               // key codes, 32 b bytes per row
   const uint16_t* ks;              // key scales, nks per row
   const uint8_t* vc;               // value codes, 64 B (2-bit) or 128 B (4-bit) per row
   const uint16_t* vs;              // value scales, nvs per row
@@ -88,27 +92,52 @@ __device__ __forceinline__ uint32_t h2bits(_Float16 h) { return (uint32_t)__buil
 // codes of dims 16 n16..16 n16+15 of tokens 8kg..8kg+7, and the scale words of one
 // token, 8kg + n16%8; the other lanes of its 16-lane row fetch those of the other
 // seven tokens and a DPP row broadcast hands them round when they are used.
-template <int NVS, int VB>
+// The KB code words of 32 key dims, held in the vector types they are loaded as (so
+// each load lands in place: copying a register that a load in flight will write would
+// make the copy wait for it).  w(i) reads word i (i a constant after unrolling).
+template <int KB> struct KeyRun {
+  uint32_t v[KB];                                   // 3 or 5 words: 4-byte loads
+  __device__ __forceinline__ uint32_t w(int i) const { return v[i]; }
+};
+template <> struct KeyRun<4> {
+  u32x4_t v;
+  __device__ __forceinline__ uint32_t w(int i) const { return v[i]; }
+};
+
+// The 4 KB bytes at p (4-byte aligned; 16-byte at KB = 4).
+template <int KB>
+__device__ __forceinline__ void load_run(const char* p, KeyRun<KB>& r) {
+  if constexpr (KB == 4) {
+    r.v = *reinterpret_cast<const u32x4_t*>(p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) r.v[i] = *reinterpret_cast<const uint32_t*>(p + 4 * i);
+  }
+}
+
+template <int NVS, int VB, int KB>
 struct StepData {
-  u32x4_t kw[2][2];    // key codes: QK tile u, row half (words 4kg.. and 16+4kg..)
+  KeyRun<KB> kw[2][2];     // key codes of QK tile u, row half h: dims 128h + 32kg .. +31
   uint32_t ks;         // key scale(s) of token 8kg + n16%8 (fp16; both groups when there are two)
-  uint32_t vw[4 * VB];  // 2-bit: word n16 of token 8kg + j at [j]; 4-bit: words 2 n16, 2 n16 + 1 at [2j], [2j + 1]
+  typename std::conditional<VB == 2, uint32_t, u32x2_t>::type vw[8];   // value words of token 8kg + j:
+                                                  // 2-bit word n16; 4-bit words 2 n16, 2 n16 + 1
   uint32_t vs[NVS == 4 ? 2 : 1];   // value scales of token 8kg + n16%8
 };
 
 // Per-lane byte offsets of a step's loads, relative to the step's first row in each array.
 struct LaneOffsets {
-  uint32_t k[2];       // key code bytes of QK tile u (row half 0; half 1 is +64)
+  uint32_t k[2];       // key code bytes of QK tile u (row half 0; half 1 is +16 b)
   uint32_t ks;         // key scale row of token 8kg + n16%8
   uint32_t v;          // value code bytes of token 8kg, dims 16 n16..
   uint32_t vs;         // value scale row of token 8kg + n16%8
 };
 
-template <int NKS, int NVS, int VB>
+template <int NKS, int NVS, int VB, int KB>
 __device__ __forceinline__ LaneOffsets lane_offsets(int kg, int n16) {
   LaneOffsets o;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) o.k[u] = (uint32_t)(8 * (n16 >> 2) + 4 * u + (n16 & 3)) * 128u + 16u * kg;
+  for (int u = 0; u < 2; ++u)
+    o.k[u] = (uint32_t)(8 * (n16 >> 2) + 4 * u + (n16 & 3)) * (32u * KB) + (uint32_t)(4 * KB) * kg;
   const uint32_t sc = (uint32_t)(8 * kg + (n16 & 7));
   o.ks = sc * 2u * NKS;
   o.v = (uint32_t)(8 * kg) * (32u * VB) + (uint32_t)(2 * VB) * n16;
@@ -120,14 +149,14 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int kg, int n16) {
 // address is a scalar base plus the lane's 32-bit byte offset; the offsets pass
 // through an empty asm so that the compiler cannot fold them into loop-invariant
 // 64-bit per-lane pointers (two registers per stream).
-template <int NKS, int NVS, int VB>
-__device__ __forceinline__ void load_step(const FArgs& a, size_t rb, LaneOffsets o, StepData<NVS, VB>& d) {
+template <int NKS, int NVS, int VB, int KB>
+__device__ __forceinline__ void load_step(const FArgs& a, size_t rb, LaneOffsets o, StepData<NVS, VB, KB>& d) {
   asm volatile("" : "+v"(o.k[0]), "+v"(o.k[1]), "+v"(o.ks), "+v"(o.v), "+v"(o.vs));
-  const char* kb = reinterpret_cast<const char*>(a.kc) + rb * 128;
+  const char* kb = reinterpret_cast<const char*>(a.kc) + rb * (32 * KB);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    d.kw[u][0] = *reinterpret_cast<const u32x4_t*>(kb + o.k[u]);
-    d.kw[u][1] = *reinterpret_cast<const u32x4_t*>(kb + o.k[u] + 64);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) load_run<KB>(kb + o.k[u] + hh * (16 * KB), d.kw[u][hh]);
   }
   const char* ksb = reinterpret_cast<const char*>(a.ks) + rb * (2 * NKS);
   if constexpr (NKS == 2) d.ks = *reinterpret_cast<const uint32_t*>(ksb + o.ks);
@@ -138,11 +167,7 @@ __device__ __forceinline__ void load_step(const FArgs& a, size_t rb, LaneOffsets
     for (int j = 0; j < 8; ++j) d.vw[j] = *reinterpret_cast<const uint32_t*>(vb + o.v + 64 * j);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x2_t t = *reinterpret_cast<const u32x2_t*>(vb + o.v + 128 * j);
-      d.vw[2 * j] = t[0];
-      d.vw[2 * j + 1] = t[1];
-    }
+    for (int j = 0; j < 8; ++j) d.vw[j] = *reinterpret_cast<const u32x2_t*>(vb + o.v + 128 * j);
   }
   const char* vsb = reinterpret_cast<const char*>(a.vs) + rb * (2 * NVS);
   if constexpr (NVS == 4) {
@@ -154,6 +179,14 @@ __device__ __forceinline__ void load_step(const FArgs& a, size_t rb, LaneOffsets
   } else {
     d.vs[0] = *reinterpret_cast<const uint16_t*>(vsb + o.vs);
   }
+}
+
+// The KB-bit field at bit `pos` (a constant after unrolling) of the word run w.
+template <int KB>
+__device__ __forceinline__ uint32_t key_field(const KeyRun<KB>& r, int pos) {
+  const int wi = pos >> 5, sh = pos & 31;
+  const uint32_t x = (sh + KB <= 32) ? (r.w(wi) >> sh) : __builtin_amdgcn_alignbit(r.w(wi + 1), r.w(wi), sh);
+  return x & ((1u << KB) - 1u);
 }
 
 // Value of lane j of this lane's 16-lane row (DPP row broadcast); j is a constant after unrolling.
@@ -225,7 +258,7 @@ __device__ __forceinline__ int claim_global(int* ctr) {
 // wavefronts that share a SIMD do not run at the same speed (the older one is
 // issued first), so the block's 32-token steps are handed out dynamically from an
 // LDS counter instead of being split evenly in advance.
-template <int NKS, int NVS, int VB>
+template <int NKS, int NVS, int VB, int KB>
 __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   constexpr int NW = kFastBlock / 64;                // wavefronts per block
   __shared__ __align__(16) float qs[4][kFastD + 16];
@@ -290,14 +323,14 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     qraw = *reinterpret_cast<const u32x2_t*>(qsrc + (size_t)wave * kFastD + 4 * lane);
     if (a.kchan) kch = *reinterpret_cast<const float4_t*>(a.kchan + ((size_t)l * a.H + h) * kFastD + 4 * lane);
   }
-  const LaneOffsets lofs = lane_offsets<NKS, NVS, VB>(kg, n16);
+  const LaneOffsets lofs = lane_offsets<NKS, NVS, VB, KB>(kg, n16);
   // local indices wave and wave + NW of slot 0 (chunk x, C >= 16) are handed out statically
   auto first_step = [&](int k) { return (x < total_chunks && (x << cl2) + k < total_steps) ? (x << cl2) + k : -1; };
   int i0 = first_step(wave), i1 = first_step(wave + NW);   // steps held by the two buffers (-1: none)
   int last = i1 >= 0 ? i1 : i0;                       // the wavefront's latest valid step
-  StepData<NVS, VB> b0, b1;
-  load_step<NKS, NVS, VB>(a, step_row(i0, last), lofs, b0);
-  load_step<NKS, NVS, VB>(a, step_row(i1, last), lofs, b1);
+  StepData<NVS, VB, KB> b0, b1;
+  load_step<NKS, NVS, VB, KB>(a, step_row(i0, last), lofs, b0);
+  load_step<NKS, NVS, VB, KB>(a, step_row(i1, last), lofs, b1);
 
   // ---- query prologue, one wavefront per query head (no block barrier until the end):
   // q in the key coordinates (divide by the channel scale, rotate: strides 1 and 2 in the
@@ -306,8 +339,9 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     slot_chunk[k] = (k == 0) ? min(x, total_chunks)
                   : (k == 1) ? (x < total_chunks ? min(x + bpu, total_chunks) : total_chunks) : -1;
   if (tid == 0) next_local = 2 * NW;
-  // B operands: chunk c < 4 -> key word 4kg + c (dims 8w..8w+7, group 0), c >= 4 -> word 16 + 4kg + (c-4).
-  // Register order of the 8 k-slots: dims (0,4), (1,5)/16, (2,6), (3,7)/16 of the word.
+  // B operands: chunk c < 4 -> dims 32kg + 8c .. +7 (group 0), c >= 4 -> dims 128 + 32kg + 8(c-4) .. +7.
+  // Register order of the 8 k-slots: at 4 bits dims (0,4), (1,5)/16, (2,6), (3,7)/16 of
+  // the 8 (the order one AND per pair leaves the codes in); at other widths dims 0..7.
   // Column n holds query head n % 4: its fp16 rounding (high part) where n / 4 is
   // even, the fp16 rounding of what that leaves (low part) where it is odd, so the
   // two columns' logits add up to those of the query with 22 bits or so instead of
@@ -353,11 +387,13 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     float gsum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int r = e >> 1;                          // slot e: dim d0 + r (+4 when e is odd)
-      const float sc = (r & 1) ? 0.0625f : 1.0f;     // the shifted nibble reads as 16 c
-      const float t = f[r + 4 * (e & 1)] * sc;
+      const int r = e >> 1;                          // 4 bits: slot e is dim d0 + r (+4 when e is odd)
+      const float sc = (KB == 4 && (r & 1)) ? 0.0625f : 1.0f;   // the shifted nibble reads as 16 c
+      const float t = (KB == 4 ? f[r + 4 * (e & 1)] : f[e]) * sc;
       const _Float16 th = (_Float16)t;
-      const _Float16 tv = epart ? (_Float16)(t - (float)th) : th;
+      // the low part is held times 2^11, so it and its products with the subnormal codes
+      // stay in the range of the high part's (where they lose no bits in the dot product)
+      const _Float16 tv = epart ? (_Float16)((t - (float)th) * 2048.0f) : th;
       hv[e] = tv;
       gsum += (float)tv / sc;
     }
@@ -374,9 +410,11 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   __syncthreads();
   constexpr float kLog2e = 1.4426950408889634f;
   const float lsc = a.sm_scale * kLog2e;             // logits kept in log2 units
-  const float cK = lsc * 16777216.0f;                // 2^24
-  const float off0 = lsc * 8.0f * qsum_s[part][hq][0];
-  const float off1 = lsc * 8.0f * qsum_s[part][hq][1];
+  const float pscale = part ? (1.0f / 2048.0f) : 1.0f;   // undoes the low part's 2^11
+  const float cK = lsc * 16777216.0f * pscale;       // 2^24
+  constexpr float kKeyOff = (float)(1 << (KB - 1));  // key levels c - 2^(b-1)
+  const float off0 = lsc * kKeyOff * qsum_s[part][hq][0] * pscale;
+  const float off1 = lsc * kKeyOff * qsum_s[part][hq][1] * pscale;
   constexpr bool kone = (NKS == 1);                  // key group 256: one scale per row
 
   float4_t acc[16];
@@ -388,7 +426,7 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
 
   // One 32-token step on the loaded data `cur` (consumed in place: no register copies,
   // so the other buffer's loads stay in flight while this one computes).
-  auto process = [&](const StepData<NVS, VB>& cur, const int t0) {
+  auto process = [&](const StepData<NVS, VB, KB>& cur, const int t0) {
     // ---- Q.K^T
     float4_t cq[2][2];
 #pragma unroll
@@ -405,9 +443,19 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
       const half8_t bq = qbs[c][qi];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const uint32_t w = cur.kw[u][c >> 2][c & 3];
-        const uint32_t w2 = w >> 8;
-        const u32x4_t pr = u32x4_t{w & 0x000F000Fu, w & 0x00F000F0u, w2 & 0x000F000Fu, w2 & 0x00F000F0u};
+        u32x4_t pr;
+        if constexpr (KB == 4) {
+          const uint32_t w = cur.kw[u][c >> 2].w(c & 3);
+          const uint32_t w2 = w >> 8;
+          pr = u32x4_t{w & 0x000F000Fu, w & 0x00F000F0u, w2 & 0x000F000Fu, w2 & 0x00F000F0u};
+        } else {
+          const KeyRun<KB>& wv = cur.kw[u][c >> 2];
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {           // dims 8(c%4) + 2pp, + 1 of the half's 32
+            const int pos = (8 * (c & 3) + 2 * pp) * KB;
+            pr[pp] = key_field<KB>(wv, pos) | (key_field<KB>(wv, pos + KB) << 16);
+          }
+        }
         const half8_t av = __builtin_bit_cast(half8_t, pr);
         cq[u][c >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bq, cq[u][c >> 2], 0, 0, 0);
       }
@@ -489,9 +537,12 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
       for (int k = 0; k < NB; ++k) {
         const int kb = k & 3, wi = k >> 2;           // byte of the word, word of the lane (4-bit)
         const uint32_t sel = (uint32_t)kb | (0x0Cu << 8) | ((uint32_t)(4 + kb) << 16) | (0x0Cu << 24);
-        const int W = VB / 2;                        // code words per lane and token
-        const uint32_t r01 = __builtin_amdgcn_perm(cur.vw[W * (4 * s4 + 1) + wi], cur.vw[W * (4 * s4 + 0) + wi], sel);
-        const uint32_t r23 = __builtin_amdgcn_perm(cur.vw[W * (4 * s4 + 3) + wi], cur.vw[W * (4 * s4 + 2) + wi], sel);
+        auto word = [&](int t) -> uint32_t {         // the lane's code word wi of token t
+          if constexpr (VB == 2) return cur.vw[t];
+          else return cur.vw[t][wi];
+        };
+        const uint32_t r01 = __builtin_amdgcn_perm(word(4 * s4 + 1), word(4 * s4 + 0), sel);
+        const uint32_t r23 = __builtin_amdgcn_perm(word(4 * s4 + 3), word(4 * s4 + 2), sel);
 #pragma unroll
         for (int ii = 0; ii < NM; ++ii) {
           // low VB(ii+1) bits of each half
@@ -534,12 +585,12 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
     process(b0, i0 * kStep);
     i0 = claim();
     if (i0 >= 0) last = i0;
-    load_step<NKS, NVS, VB>(a, step_row(i0, last), lofs, b0);
+    load_step<NKS, NVS, VB, KB>(a, step_row(i0, last), lofs, b0);
     if (i1 < 0) break;
     process(b1, i1 * kStep);
     i1 = claim();
     if (i1 >= 0) last = i1;
-    load_step<NKS, NVS, VB>(a, step_row(i1, last), lofs, b1);
+    load_step<NKS, NVS, VB, KB>(a, step_row(i1, last), lofs, b1);
   }
 
   // ---- reduce the token subsets of the four lane groups (same word, kg = 0..3)
@@ -744,7 +795,12 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   if (s.head_dim != kFastD) return false;
   if (s.tokens % kStep != 0 || s.tokens == 0) return false;
   if (Hq / s.heads > 4) return false;
-  if (k.codec.codebook != KVQ_INT_ABSMAX || k.codec.bits != 4) return false;
+  if (k.codec.codebook != KVQ_INT_ABSMAX) return false;
+  const int kb = k.codec.bits;
+  // 6- and 8-bit keys need more registers than two wavefronts per SIMD leave (scratch
+  // spills); 2-bit keys came out with logit errors of ~1e-4 here (4x those of 4-bit keys,
+  // over the 1e-4 lse bar), so they stay on the general kernel
+  if (kb < 3 || kb > 5) return false;
   if (k.codec.group != 128 && k.codec.group != 256) return false;
   // 2- or 4-bit values: signed absmax (levels c - 2^(b-1)) or the symmetric grid (levels c - (2^b - 1)/2)
   if (v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) return false;
@@ -780,17 +836,23 @@ size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q) {
   return (b + 255) / 256 * 256;
 }
 
-template <int VB>
+template <int VB, int KB>
 static void launch_mfma(const FArgs& a, dim3 grid, hipStream_t st) {
   if (a.nks == 2) {
-    if (a.nvs == 1) k_decode_mfma<2, 1, VB><<<grid, kFastBlock, 0, st>>>(a);
-    else if (a.nvs == 2) k_decode_mfma<2, 2, VB><<<grid, kFastBlock, 0, st>>>(a);
-    else k_decode_mfma<2, 4, VB><<<grid, kFastBlock, 0, st>>>(a);
+    if (a.nvs == 1) k_decode_mfma<2, 1, VB, KB><<<grid, kFastBlock, 0, st>>>(a);
+    else if (a.nvs == 2) k_decode_mfma<2, 2, VB, KB><<<grid, kFastBlock, 0, st>>>(a);
+    else k_decode_mfma<2, 4, VB, KB><<<grid, kFastBlock, 0, st>>>(a);
   } else {
-    if (a.nvs == 1) k_decode_mfma<1, 1, VB><<<grid, kFastBlock, 0, st>>>(a);
-    else if (a.nvs == 2) k_decode_mfma<1, 2, VB><<<grid, kFastBlock, 0, st>>>(a);
-    else k_decode_mfma<1, 4, VB><<<grid, kFastBlock, 0, st>>>(a);
+    if (a.nvs == 1) k_decode_mfma<1, 1, VB, KB><<<grid, kFastBlock, 0, st>>>(a);
+    else if (a.nvs == 2) k_decode_mfma<1, 2, VB, KB><<<grid, kFastBlock, 0, st>>>(a);
+    else k_decode_mfma<1, 4, VB, KB><<<grid, kFastBlock, 0, st>>>(a);
   }
+}
+
+template <int KB>
+static void launch_mfma_k(const FArgs& a, int vb, dim3 grid, hipStream_t st) {
+  if (vb == 2) launch_mfma<2, KB>(a, grid, st);
+  else launch_mfma<4, KB>(a, grid, st);
 }
 
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
@@ -838,8 +900,11 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
   a.lse = pr.lse;
   const long long units = (long long)s.batch * s.layers * s.heads;
   const dim3 grid(a.blocks_per_unit, (unsigned)units, (unsigned)pr.n_q);
-  if (vb == 2) launch_mfma<2>(a, grid, st);
-  else launch_mfma<4>(a, grid, st);
+  switch (k.codec.bits) {
+    case 3: launch_mfma_k<3>(a, vb, grid, st); break;
+    case 4: launch_mfma_k<4>(a, vb, grid, st); break;
+    default: launch_mfma_k<5>(a, vb, grid, st); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
   if (v.codec.rot_width > 1 || v.chan_scale) return launch_combine_partials(pr, a.blocks_per_unit, a.ctr, st);

@@ -1,5 +1,5 @@
-"""GPU parity of the MFMA decode-attention kernel (4-bit keys, 2- or 4-bit values,
-head_dim 256) against the CPU oracle, and against the general kernel.
+"""GPU parity of the MFMA decode-attention kernel (3-, 4- or 5-bit keys, 2- or
+4-bit values, head_dim 256) against the CPU oracle, and against the general kernel.
 
 Bar: outputs within 2e-3 relative L2 per row, lse within 1e-4 absolute.  The
 rotated query enters the matrix cores as an fp16 high part plus an fp16
@@ -42,7 +42,8 @@ def test_fast_c3_shape_shrunk():
 
 @pytest.mark.parametrize("variant", ["kgroup256", "vgroup64", "vgroup256", "rot128", "norot", "G2", "G1",
                                      "vrot", "vsym", "vsym_rot", "v4", "v4_g64", "v4_g256_k256", "v4_rot",
-                                     "v4_sym", "v4_sym_rot", "v4_G1"])
+                                     "v4_sym", "v4_sym_rot", "v4_G1", "k3", "k5", "k3_v4", "k5_v4",
+                                     "k5_v4_g64", "k3_kg256_rot128", "k5_norot_G2", "k3_v4_rot"])
 def test_fast_variants(variant):
     import kv_cache_bit_fwht_amd as K
     kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
@@ -82,6 +83,19 @@ def test_fast_variants(variant):
     elif variant == "v4_G1":
         w = w.with_sizes(Hq=4)
         vc = K.Codec(K.INT_ABSMAX, 4, 128, 0)
+    elif variant in ("k3", "k5"):
+        kc = K.Codec(K.INT_ABSMAX, int(variant[1]), 128, 256)
+    elif variant in ("k3_v4", "k5_v4"):
+        kc, vc = K.Codec(K.INT_ABSMAX, int(variant[1]), 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0)
+    elif variant == "k5_v4_g64":
+        kc, vc = K.Codec(K.INT_ABSMAX, 5, 128, 256), K.Codec(K.INT_ABSMAX, 4, 64, 0)
+    elif variant == "k3_kg256_rot128":
+        kc = K.Codec(K.INT_ABSMAX, 3, 256, 128)
+    elif variant == "k5_norot_G2":
+        w = w.with_sizes(Hq=8)
+        kc = K.Codec(K.INT_ABSMAX, 5, 128, 0)
+    elif variant == "k3_v4_rot":
+        kc, vc = K.Codec(K.INT_ABSMAX, 3, 256, 256), K.Codec(K.INT_ABSMAX, 4, 128, 256)
     announce(f"mfma variant {variant}")
     _case(K, w, kc, vc)
 
@@ -113,6 +127,17 @@ def test_fast_4bit_values_many_blocks_and_lengths():
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0), kv_len)
 
 
+def test_fast_3_and_5_bit_keys_many_blocks_and_lengths():
+    """3- and 5-bit keys (fields cut across word boundaries): 32 blocks per unit on a
+    counter, causal lengths ending mid-step."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=1, T=16384, n_q=3)
+    kv_len = np.array([[[16384, 9001, 31]]], dtype=np.int32)
+    for kb in (3, 5):
+        announce(f"mfma {kb}-bit keys, many blocks per unit")
+        _case(K, w, K.Codec(K.INT_ABSMAX, kb, 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0), kv_len)
+
+
 def test_fast_static_chunks_many_rows():
     """More (query row, KV head) units than the workspace has counters for: blocks take
     fixed chunks and a separate kernel merges the partials."""
@@ -120,6 +145,18 @@ def test_fast_static_chunks_many_rows():
     w = synth.get("c3", L=2, T=64, n_q=1030)             # 2 * 1030 * 4 = 8240 units
     announce("mfma static chunks, 8240 units")
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0))
+
+
+def test_fast_rejects_2_bit_keys():
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=1, T=64, n_q=1)
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    kp = _gpu_pack(K, Kx, K.Codec(K.INT_ABSMAX, 2, 128, 256))
+    vp = _gpu_pack(K, Vx, K.Codec(K.INT_ABSMAX, 2, 128, 0))
+    announce("mfma rejects 2-bit keys")
+    with pytest.raises(K.KvqError):
+        _gpu_decode(K, kp, vp, q, None, path=2)
 
 
 def test_fast_rejects_unsupported_and_auto_falls_back():

@@ -82,7 +82,7 @@ def test_quantize_dequant_with_mean_bit_exact(cspec, D, with_chan, T):
 @pytest.mark.parametrize("case", [("mfma", (1, 4, 128, 256), 2), ("auto", (1, 4, 128, 256), None),
                                   ("general", (1, 4, 128, 256), 1), ("general", (1, 3, 128, 256), 1),
                                   ("general", (2, 3, 32, 0), 1), ("general", (7, 5, 32, 0, 7), 1),
-                                  ("map_pair", (1, 5, 64, 256), 1)])
+                                  ("map_pair", (1, 5, 64, 256), 1), ("mfma_k3", (1, 3, 128, 256), 2)])
 def test_decode_and_error_with_key_mean(case):
     import kv_cache_bit_fwht_amd as K
     name, kspec, path = case
