@@ -222,8 +222,8 @@ def test_decode_validates_before_launching(K):
     assert _decode(K, k, v_rfft) == ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("case", ["tokens_not_mult_32", "head_dim_128", "k_3bit", "v_group_32",
-                                  "k_minmax", "v_chan_scale", "g8"])
+@pytest.mark.parametrize("case", ["tokens_not_mult_32", "head_dim_128", "k_2bit", "k_6bit", "v_3bit", "v_group_32",
+                                  "k_minmax", "v_chan_scale", "g8", "v_lloyd"])
 def test_mfma_path_rejects_what_it_does_not_cover(K, case):
     kc, vc, shape, q_heads = (1, 4, 128, 256, 0), (1, 2, 128, 0, 0), (1, 2, 4, 64, 256), 16
     v_chan = None
@@ -232,8 +232,14 @@ def test_mfma_path_rejects_what_it_does_not_cover(K, case):
     elif case == "head_dim_128":
         shape = (1, 2, 4, 64, 128)
         kc = (1, 4, 128, 128, 0)
-    elif case == "k_3bit":
-        kc = (1, 3, 128, 256, 0)
+    elif case == "k_2bit":
+        kc = (1, 2, 128, 256, 0)
+    elif case == "k_6bit":
+        kc = (1, 6, 128, 256, 0)
+    elif case == "v_3bit":
+        vc = (1, 3, 128, 0, 0)
+    elif case == "v_lloyd":
+        vc = (10, 2, 128, 0, 0)
     elif case == "v_group_32":
         vc = (1, 2, 32, 0, 0)
     elif case == "k_minmax":
