@@ -471,6 +471,7 @@ static SegPlan seg_plan(const kvq_segment* segs, int32_t n_seg, int32_t layers, 
   for (int i = 0; i < n_seg; ++i) tokens = std::max(tokens, segs[i].token0 + segs[i].k->shape.tokens);
   p.mixed_bytes = mixed_ws_bytes(segs, layers, heads, tokens, q_heads, n_q);
   p.total = std::max(p.total, kWsCounterBytes + p.mixed_bytes);
+  p.total = std::max(p.total, kWsCounterBytes + mixed_fast_ws_bytes(segs, layers, heads, tokens, q_heads, n_q));
   return p;
 }
 
@@ -553,17 +554,22 @@ kvq_status kvq_decode_attn_segments_ex(const kvq_segment* segs, int32_t n_seg, i
   hipStream_t s = (hipStream_t)stream;
   char* w = static_cast<char*>(ws);
   const int B = segs[0].k->shape.batch, D = segs[0].k->shape.head_dim, G = q_heads / heads;
-  // a codec map (every segment a whole-token tile) in one launch: asked for, or, by
-  // default, when there are several tiles and none would take the MFMA kernel
+  // a codec map (every segment a whole-token tile) in one launch, asked for or by default
+  // with several tiles: on the MFMA kernel when every tile is one of its pairs at group
+  // 128, else on the general kernel when no tile would take the MFMA kernel
+  const bool mixf_ok = mixed_fast_supported(segs, n_seg, layers, heads, tokens, q_heads, n_q);
   const bool mix_ok = mixed_decode_supported(segs, n_seg, tokens);
-  if (path == 2 && !mix_ok) return KVQ_ERR_UNSUPPORTED;
+  if (path == 2 && !mixf_ok && !mix_ok) return KVQ_ERR_UNSUPPORTED;
+  const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)D));
+  if (mixf_ok && (path == 2 || (path == 0 && n_seg > 1)))
+    return hip_status(launch_decode_fast_mixed(segs, n_seg, layers, heads, tokens, q_heads, n_q, q, kv_len, sm, out,
+                                               lse, reinterpret_cast<int*>(w), w + kWsCounterBytes, s));
   bool use_mix = path == 2;
   if (path == 0 && mix_ok && n_seg > 1) {
     use_mix = true;
     for (int i = 0; i < n_seg; ++i)
       if (fast_decode_supported(*segs[i].k, *segs[i].v, segs[i].k->shape.heads * G)) use_mix = false;
   }
-  const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)D));
   if (use_mix)
     return hip_status(launch_decode_mixed(segs, n_seg, layers, heads, tokens, q_heads, n_q, q, kv_len, sm, out, lse,
                                           w + kWsCounterBytes, true, s));

@@ -268,491 +268,107 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   __shared__ half8_t qbs[8][32];                     // MFMA B operands [chunk][16 part + 4 kg + head]
   __shared__ int next_local;                         // next step index of the block not yet handed out
   __shared__ int slot_chunk[kMaxSlots];              // chunk of each slot of C local indices (-1 = not yet known)
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront-uniform
-  const int kg = lane >> 4, n16 = lane & 15;
   const long long unit = blockIdx.y;                 // (b*L + l)*H + h
   const int h = (int)(unit % a.H);
   const long long bl = unit / a.H;                   // b*L + l
   const int l = (int)(bl % a.L);
-  const int i = blockIdx.z;                          // query index
-  const long long rq = bl * a.n_q + i;
-  const int G = a.G;
-  int n = a.T;
-  if (a.kv_len) n = min(max(a.kv_len[rq], 0), a.T);
+  const long long rq = bl * a.n_q + blockIdx.z;      // blockIdx.z: query index
+  const size_t urow0 = (size_t)unit * a.T;
+  const float* const kchu = a.kchan ? a.kchan + ((size_t)l * a.H + h) * kFastD : nullptr;
+#include "kvq_mfma_body.inc"
+}
 
-  // ---- steps.  The unit's 32-token steps are grouped in chunks of C = 2^chunk_log2.
-  // Slot s < S0 of block x holds chunk x + s * bpu (about three quarters of the unit's
-  // chunks, taken without any atomic); every later chunk comes from a counter shared by
-  // the unit's blocks, which sit on different XCDs whose speeds differ from run to run,
-  // so the fast ones take more of the tail.  Without counters every slot is static.
-  // Inside the block, wavefronts take local step indices from an LDS counter: index k
-  // is step (k mod C) of the chunk of slot k / C.  Chunks are claimed one slot ahead by
-  // the wavefront that takes a slot's first index, and only after that slot's own chunk
-  // is known, so a block's chunks increase with the slot (static ones lie below
-  // S0 * bpu, counted ones above): once a slot holds the end marker every later one
-  // does too.
-  const int bpu = a.blocks_per_unit;
-  const int x = blockIdx.x;
-  const int cl2 = a.chunk_log2;
-  const int t_end = n;                               // tokens >= t_end are masked
-  const int total_steps = (n + kStep - 1) / kStep;
-  const int total_chunks = (total_steps + (1 << cl2) - 1) >> cl2;
-  int* const ctr = a.ctr ? a.ctr + (rq * a.H + h) : nullptr;
-  // static slots per block: at least 2 (slots 0 and 1 are known at the start)
-  const int S0 = ctr ? max(2, (3 * total_chunks) / (4 * bpu)) : 0x7fffffff;
-  const size_t row0 = (size_t)unit * a.T;
-  const int vgrp = (16 * n16) / a.gv;                // scale group of this lane's value word
-  const uint32_t vsel = (NVS > 1 && (vgrp & 1)) ? 0x07060302u : 0x05040100u;
-  const uint32_t vhi = (NVS == 4 && (vgrp & 2)) ? 0xFFFFFFFFu : 0u;
-  // first row of step s; a refill past the end re-reads the wavefront's last valid step
-  // (an L2 hit), and a wavefront that never had a step reads the unit's first rows
-  auto step_row = [&](int s, int last) -> size_t {
-    return row0 + (size_t)(s >= 0 ? s : (last >= 0 ? last : 0)) * kStep;
-  };
+// ------------------------------------------------------------------ codec maps in one launch
+//
+// A cache tiled into (layer range x KV-head range) tiles over every token, each with its
+// own key and value bit widths at group 128 (per-head key bits, [LCPP] Finding 2; a
+// per-layer allocation, [E21W] Result): one launch decodes all of it.  Each block finds
+// the tile of its (layer, KV head), takes that tile's arrays, rotations and value grid,
+// and runs the decode compiled for the tile's (key bits, value bits).  Counters, partials,
+// queries, lengths and outputs are indexed over the whole map, so the in-kernel merge
+// writes the final rows.  The pairs compiled in (id, key bits, value bits):
+#define KVQ_MFMA_MIX_PAIRS(X) X(0, 3, 2) X(1, 4, 2) X(2, 5, 2) X(3, 3, 4) X(4, 4, 4) X(5, 5, 4)
 
-  // The query is read first so that the prologue waits for it alone; each wavefront's
-  // first two steps (w and w + NW, handed out statically) are loaded right after it and
-  // land while the prologue runs.  Loads are never issued under a branch, so that every
-  // wait names exactly the data it needs.
-  const uint16_t* qsrc = a.q + (size_t)rq * a.Hq * kFastD + (size_t)h * G * kFastD;
-  // wavefront w < 4 holds query head w, dims 4 lane .. 4 lane + 3 (zero for heads >= G)
-  u32x2_t qraw = u32x2_t{0u, 0u};
-  float4_t kch = float4_t{1.0f, 1.0f, 1.0f, 1.0f};   // key channel scales of those dims
-  if (wave < G) {
-    qraw = *reinterpret_cast<const u32x2_t*>(qsrc + (size_t)wave * kFastD + 4 * lane);
-    if (a.kchan) kch = *reinterpret_cast<const float4_t*>(a.kchan + ((size_t)l * a.H + h) * kFastD + 4 * lane);
-  }
-  const LaneOffsets lofs = lane_offsets<NKS, NVS, VB, KB>(kg, n16);
-  // local indices wave and wave + NW of slot 0 (chunk x, C >= 16) are handed out statically
-  auto first_step = [&](int k) { return (x < total_chunks && (x << cl2) + k < total_steps) ? (x << cl2) + k : -1; };
-  int i0 = first_step(wave), i1 = first_step(wave + NW);   // steps held by the two buffers (-1: none)
-  int last = i1 >= 0 ? i1 : i0;                       // the wavefront's latest valid step
-  StepData<NVS, VB, KB> b0, b1;
-  load_step<NKS, NVS, VB, KB>(a, step_row(i0, last), lofs, b0);
-  load_step<NKS, NVS, VB, KB>(a, step_row(i1, last), lofs, b1);
+struct MfmaTile {
+  const uint8_t* kc;
+  const uint16_t* ks;
+  const uint8_t* vc;
+  const uint16_t* vs;
+  const float* kchan;              // [ls][hs][256] or null
+  int l0, ls, h0, hs;              // layers [l0, l0 + ls) x KV heads [h0, h0 + hs)
+  int kW, vW;
+  float kkappa, vkappa, voff;
+  int pair;                        // index into KVQ_MFMA_MIX_PAIRS
+};
 
-  // ---- query prologue, one wavefront per query head (no block barrier until the end):
-  // q in the key coordinates (divide by the channel scale, rotate: strides 1 and 2 in the
-  // lane, 4 to 128 across lanes), then the MFMA B operands and per-group offset sums.
-  for (int k = tid; k < kMaxSlots; k += kFastBlock)
-    slot_chunk[k] = (k == 0) ? min(x, total_chunks)
-                  : (k == 1) ? (x < total_chunks ? min(x + bpu, total_chunks) : total_chunks) : -1;
-  if (tid == 0) next_local = 2 * NW;
-  // B operands: chunk c < 4 -> dims 32kg + 8c .. +7 (group 0), c >= 4 -> dims 128 + 32kg + 8(c-4) .. +7.
-  // Register order of the 8 k-slots: at 4 bits dims (0,4), (1,5)/16, (2,6), (3,7)/16 of
-  // the 8 (the order one AND per pair leaves the codes in); at other widths dims 0..7.
-  // Column n holds query head n % 4: its fp16 rounding (high part) where n / 4 is
-  // even, the fp16 rounding of what that leaves (low part) where it is odd, so the
-  // two columns' logits add up to those of the query with 22 bits or so instead of
-  // 11.  Each part folds the (c - 8) code offset with its own per-group sum.
-  // Columns of heads >= G see an all-zero query row; their logits and output rows
-  // are computed but never written.  They stay in LDS (read once per step) to keep
-  // registers for the second buffer of loads in flight.
-  if (wave < 4) {
-    float v[4] = {h2f((uint16_t)(qraw[0] & 0xffffu)), h2f((uint16_t)(qraw[0] >> 16)),
-                  h2f((uint16_t)(qraw[1] & 0xffffu)), h2f((uint16_t)(qraw[1] >> 16))};
-    if (a.kchan) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = v[e] / kch[e];
-    }
-    if (a.kW > 1) {
-      if (a.kW >= 2) {                               // stride 1
-        const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
-        v[0] = x0 + x1; v[1] = x0 - x1; v[2] = x2 + x3; v[3] = x2 - x3;
-      }
-      if (a.kW >= 4) {                               // stride 2
-        const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
-        v[0] = x0 + x2; v[2] = x0 - x2; v[1] = x1 + x3; v[3] = x1 - x3;
-      }
-      for (int m = 1; 4 * m < a.kW; m <<= 1) {       // stride 4m: lane ^ m
-        const bool hi = (lane & m) != 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float y = __shfl_xor(v[e], m);
-          v[e] = hi ? (y - v[e]) : (v[e] + y);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] *= a.kkappa;
-    }
-    *reinterpret_cast<float4_t*>(&qs[wave][4 * lane]) = float4_t{v[0], v[1], v[2], v[3]};
-    // lane -> B entry (chunk c, lane group kg, part); its 8 dims are d0 .. d0 + 7
-    const int c = lane & 7, ekg = (lane >> 3) & 3, epart = lane >> 5;
-    const int d0 = 8 * ((c < 4) ? (4 * ekg + c) : (16 + 4 * ekg + (c - 4)));
-    const float4_t f0 = *reinterpret_cast<const float4_t*>(&qs[wave][d0]);
-    const float4_t f1 = *reinterpret_cast<const float4_t*>(&qs[wave][d0 + 4]);
-    const float f[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
-    half8_t hv;
-    float gsum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = e >> 1;                          // 4 bits: slot e is dim d0 + r (+4 when e is odd)
-      const float sc = (KB == 4 && (r & 1)) ? 0.0625f : 1.0f;   // the shifted nibble reads as 16 c
-      const float t = (KB == 4 ? f[r + 4 * (e & 1)] : f[e]) * sc;
-      const _Float16 th = (_Float16)t;
-      // the low part is held times 2^11, so it and its products with the subnormal codes
-      // stay in the range of the high part's (where they lose no bits in the dot product)
-      const _Float16 tv = epart ? (_Float16)((t - (float)th) * 2048.0f) : th;
-      hv[e] = tv;
-      gsum += (float)tv / sc;
-    }
-    qbs[c][16 * epart + 4 * ekg + wave] = hv;
-    // sum over the lanes of the same (part, key group): lane bits 0, 1 (c % 4) and 3, 4 (kg)
-    gsum += __shfl_xor(gsum, 1);
-    gsum += __shfl_xor(gsum, 2);
-    gsum += __shfl_xor(gsum, 8);
-    gsum += __shfl_xor(gsum, 16);
-    if ((lane & 0x1B) == 0) qsum_s[epart][wave][c >> 2] = gsum;
-  }
-  const int hq = n16 & 3;                            // query head of this lane's column
-  const int part = (n16 >> 2) & 1;                   // 0: high part, 1: low part
-  __syncthreads();
-  constexpr float kLog2e = 1.4426950408889634f;
-  const float lsc = a.sm_scale * kLog2e;             // logits kept in log2 units
-  const float pscale = part ? (1.0f / 2048.0f) : 1.0f;   // undoes the low part's 2^11
-  const float cK = lsc * 16777216.0f * pscale;       // 2^24
-  constexpr float kKeyOff = (float)(1 << (KB - 1));  // key levels c - 2^(b-1)
-  const float off0 = lsc * kKeyOff * qsum_s[part][hq][0] * pscale;
-  const float off1 = lsc * kKeyOff * qsum_s[part][hq][1] * pscale;
-  constexpr bool kone = (NKS == 1);                  // key group 256: one scale per row
+struct FMixArgs {
+  FArgs base;                      // the whole map's geometry, counters, partials and outputs
+  int ntiles;
+  MfmaTile tile[kMaxSegments];
+};
 
-  float4_t acc[16];
-#pragma unroll
-  for (int f = 0; f < 16; ++f) acc[f] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_ref = -INFINITY;       // reference max (log2 units) of head hq
-  float l_part = 0.0f;           // sum of p over this lane's tokens (head hq)
-  float w_part = 0.0f;           // sum of the fp16 weights fp16(p) * s_v over this lane's tokens (head hq, group vgrp)
+struct MfmaLds {                   // the LDS of one block (as k_decode_mfma declares it)
+  alignas(16) float qs[4][kFastD + 16];
+  float qsum_s[2][4][2];
+  float so[kFastBlock / 64][4][kFastD];
+  float sm[kFastBlock / 64][4], sl[kFastBlock / 64][4];
+  half8_t qbs[8][32];
+  int next_local;
+  int slot_chunk[kMaxSlots];
+};
 
-  // One 32-token step on the loaded data `cur` (consumed in place: no register copies,
-  // so the other buffer's loads stay in flight while this one computes).
-  auto process = [&](const StepData<NVS, VB, KB>& cur, const int t0) {
-    // ---- Q.K^T
-    float4_t cq[2][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      cq[u][0] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      cq[u][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    // The LDS index is made opaque per step so the operands are re-read here rather
-    // than hoisted out of the loop into 32 loop-carried registers.
-    int qi = 16 * part + 4 * kg + hq;
-    asm volatile("" : "+v"(qi));
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const half8_t bq = qbs[c][qi];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4_t pr;
-        if constexpr (KB == 4) {
-          const uint32_t w = cur.kw[u][c >> 2].w(c & 3);
-          const uint32_t w2 = w >> 8;
-          pr = u32x4_t{w & 0x000F000Fu, w & 0x00F000F0u, w2 & 0x000F000Fu, w2 & 0x00F000F0u};
-        } else {
-          const KeyRun<KB>& wv = cur.kw[u][c >> 2];
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {           // dims 8(c%4) + 2pp, + 1 of the half's 32
-            const int pos = (8 * (c & 3) + 2 * pp) * KB;
-            pr[pp] = key_field<KB>(wv, pos) | (key_field<KB>(wv, pos + KB) << 16);
-          }
-        }
-        const half8_t av = __builtin_bit_cast(half8_t, pr);
-        cq[u][c >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bq, cq[u][c >> 2], 0, 0, 0);
-      }
-    }
-    // logits (log2 units) of tokens 8kg + 4u + r, head hq
-    float lg[8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 4 * u + r;                      // token 8kg + j
-        const uint32_t kw2 = row_bcast(cur.ks, j);
-        float s0, s1;
-        if constexpr (kone) {
-          s0 = s1 = h2f((uint16_t)kw2);
-        } else {
-          s0 = h2f((uint16_t)kw2);
-          s1 = h2f((uint16_t)(kw2 >> 16));
-        }
-        lg[j] = s0 * (cq[u][0][r] * cK - off0) + s1 * (cq[u][1][r] * cK - off1);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lg[j] = add_row_ror4(lg[j]);   // high + low part
-    if (t0 + kStep > t_end) {                        // partial step: mask tokens >= t_end
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (t0 + 8 * kg + j >= t_end) lg[j] = -INFINITY;
-    }
-    // ---- online softmax (per head; lanes with equal n16%4 hold identical values).
-    // The reference maximum moves only when a logit exceeds it by more than 1 (log2
-    // units), so weights stay below 2 and p * s_v stays inside fp16 range; the
-    // result does not depend on where the reference sits.
-    float mt = lg[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) mt = fmaxf(mt, lg[k]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool grow = mt > m_ref + 1.0f;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mt : m_ref;
-      const float alpha = grow ? ((m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new)) : 1.0f;
-      m_ref = m_new;
-      l_part *= alpha;
-      w_part *= alpha;
-      // accumulator component c belongs to head c: take head c's factor from lane c
-      const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2), a3 = __shfl(alpha, 3);
-#pragma unroll
-      for (int f = 0; f < 16; ++f) {
-        acc[f][0] *= a0;
-        acc[f][1] *= a1;
-        acc[f][2] *= a2;
-        acc[f][3] *= a3;
-      }
-    }
-    // ---- P.V weights: fp16(p) * s_v(token, group of this lane's value word), in fp16 pairs
-    half4_t aw[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {                   // tokens 2 s2, 2 s2 + 1
-      const float p0 = __builtin_amdgcn_exp2f(lg[2 * s2] - m_ref);   // masked tokens: exp2(-inf) = 0
-      const float p1 = __builtin_amdgcn_exp2f(lg[2 * s2 + 1] - m_ref);
-      l_part += p0 + p1;
-      const uint32_t sv = vscale_pair<NVS>(cur.vs, 2 * s2, vsel, vhi);
-      const half2_t w2 = half2_t{(_Float16)p0, (_Float16)p1} * __builtin_bit_cast(half2_t, sv);
-      w_part = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, w_part, false);
-      aw[s2 >> 1][2 * (s2 & 1)] = w2[0];
-      aw[s2 >> 1][2 * (s2 & 1) + 1] = w2[1];
-    }
-    // ---- P.V: byte k of the lane's value codes of tokens (4s..4s+3) holds dims 4k..4k+3
-    // (2-bit) or 2k, 2k+1 (4-bit) of its 16.  B = the byte masked to its low 2, 4, 6 and 8
-    // bits, or its low 4 and 8 bits (fp16 subnormals), so the accumulators of byte k hold
-    // prefix sums of the fields weighted 1, 4, 16, 64 (or 1, 16); the fields are
-    // separated after the loop.
-    constexpr int NB = (VB == 2) ? 4 : 8;            // code bytes per lane and token
-    constexpr int NM = (VB == 2) ? 4 : 2;            // masks per byte
-#pragma unroll
-    for (int s4 = 0; s4 < 2; ++s4) {
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const int kb = k & 3, wi = k >> 2;           // byte of the word, word of the lane (4-bit)
-        const uint32_t sel = (uint32_t)kb | (0x0Cu << 8) | ((uint32_t)(4 + kb) << 16) | (0x0Cu << 24);
-        auto word = [&](int t) -> uint32_t {         // the lane's code word wi of token t
-          if constexpr (VB == 2) return cur.vw[t];
-          else return cur.vw[t][wi];
-        };
-        const uint32_t r01 = __builtin_amdgcn_perm(word(4 * s4 + 1), word(4 * s4 + 0), sel);
-        const uint32_t r23 = __builtin_amdgcn_perm(word(4 * s4 + 3), word(4 * s4 + 2), sel);
-#pragma unroll
-        for (int ii = 0; ii < NM; ++ii) {
-          // low VB(ii+1) bits of each half
-          const uint32_t mask = ((0x00010001u << (VB * (ii + 1))) - 0x00010001u);
-          const u32x2_t bp = (ii == NM - 1) ? u32x2_t{r01, r23} : u32x2_t{r01 & mask, r23 & mask};
-          const half4_t bv = __builtin_bit_cast(half4_t, bp);
-          acc[NM * k + ii] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw[s4], bv, acc[NM * k + ii], 0, 0, 0);
-        }
-      }
-    }
-  };
+template <int VB, int KB>
+__device__ __forceinline__ void mfma_tile_unit(const FArgs& a, MfmaLds& S, int h, long long rq, size_t urow0,
+                                               const float* kchu) {
+  constexpr int NKS = 2, NVS = 2;                    // key and value group 128
+  constexpr int NW = kFastBlock / 64;
+  auto& qs = S.qs;
+  auto& qsum_s = S.qsum_s;
+  auto& so = S.so;
+  auto& sm = S.sm;
+  auto& sl = S.sl;
+  auto& qbs = S.qbs;
+  int& next_local = S.next_local;
+  auto& slot_chunk = S.slot_chunk;
+#include "kvq_mfma_body.inc"
+}
 
-  // Next step for this wavefront (wavefront-uniform), or -1 when the block is done.
-  // Every lane takes part in the LDS atomic (lane 0 adds 1, the others 0), so lane 0
-  // receives the old count whatever order the lanes are served in, with no single-lane
-  // branch (which would cost registers in this loop); the counter atomic likewise.
-  auto claim = [&]() -> int {
-    const int k = __builtin_amdgcn_readfirstlane(atomicAdd(&next_local, lane == 0 ? 1 : 0));
-    const int sl = min(k >> cl2, kMaxSlots - 2), pos = k & ((1 << cl2) - 1);
-    int c;
-    do {                                             // the slot's chunk, once its claimer has written it
-      c = __builtin_amdgcn_readfirstlane(
-          __hip_atomic_load(&slot_chunk[sl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-    } while (c < 0);
-    if (pos == 0) {                                  // first index of the slot: claim the next slot's chunk
-      int nc = total_chunks;
-      if (c < total_chunks) {
-        nc = (sl + 1 < S0) ? c + bpu : S0 * bpu + claim_global(ctr);
-        nc = min(nc, total_chunks);
-      }
-      __hip_atomic_store(&slot_chunk[sl + 1], nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    const int step = (c << cl2) + pos;
-    return (c < total_chunks && step < total_steps) ? step : -1;
-  };
-  // Each buffer is refilled right after it is consumed.  A wavefront's claims follow
-  // its local indices, so once one returns -1 so do all later ones: the first -1 ends
-  // the loop with no claimed step left unprocessed.
-  while (i0 >= 0) {
-    process(b0, i0 * kStep);
-    i0 = claim();
-    if (i0 >= 0) last = i0;
-    load_step<NKS, NVS, VB, KB>(a, step_row(i0, last), lofs, b0);
-    if (i1 < 0) break;
-    process(b1, i1 * kStep);
-    i1 = claim();
-    if (i1 >= 0) last = i1;
-    load_step<NKS, NVS, VB, KB>(a, step_row(i1, last), lofs, b1);
+__global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma_mix(FMixArgs m) {
+  __shared__ MfmaLds S;
+  const FArgs& g = m.base;
+  const long long unit = blockIdx.y;                 // (b*L + l)*H + h over the whole map
+  const int h = (int)(unit % g.H);
+  const long long bl = unit / g.H;
+  const int l = (int)(bl % g.L);
+  const long long b = bl / g.L;
+  const long long rq = bl * g.n_q + blockIdx.z;
+  int ti = 0;                                        // the tiles cover every (layer, head) once
+  while (ti + 1 < m.ntiles) {
+    const MfmaTile& t = m.tile[ti];
+    if (l >= t.l0 && l < t.l0 + t.ls && h >= t.h0 && h < t.h0 + t.hs) break;
+    ++ti;
   }
-
-  // ---- reduce the token subsets of the four lane groups (same word, kg = 0..3)
-#pragma unroll
-  for (int f = 0; f < 16; ++f) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float x = acc[f][c];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[f][c] = x;
-    }
-  }
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
-  w_part += __shfl_xor(w_part, 16);
-  w_part += __shfl_xor(w_part, 32);
-  // sum of the fp16 weights of head c in this lane's value group: the lane of the same 4-lane block with lane%4 == c
-  const int base_l = lane & ~3;
-  const float ws0 = __shfl(w_part, base_l | 0), ws1 = __shfl(w_part, base_l | 1);
-  const float ws2 = __shfl(w_part, base_l | 2), ws3 = __shfl(w_part, base_l | 3);
-  if (lane < 16) {
-    const float wsum[4] = {ws0, ws1, ws2, ws3};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if constexpr (VB == 2) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // prefix sums M1..M4 of byte k -> fields f0 = M1, f1 = (M2-M1)/4, f2 = (M3-M2)/16, f3 = (M4-M3)/64
-          const float m1 = acc[4 * k][c], m2 = acc[4 * k + 1][c], m3 = acc[4 * k + 2][c], m4 = acc[4 * k + 3][c];
-          const float f[4] = {m1, (m2 - m1) * 0.25f, (m3 - m2) * 0.0625f, (m4 - m3) * 0.015625f};
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) so[wave][c][16 * n16 + 4 * k + ii] = f[ii] * 16777216.0f - a.voff * wsum[c];
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          // prefix sums M1, M2 of byte k -> fields f0 = M1, f1 = (M2-M1)/16
-          const float m1 = acc[2 * k][c], m2 = acc[2 * k + 1][c];
-          so[wave][c][16 * n16 + 2 * k] = m1 * 16777216.0f - a.voff * wsum[c];
-          so[wave][c][16 * n16 + 2 * k + 1] = ((m2 - m1) * 0.0625f) * 16777216.0f - a.voff * wsum[c];
-        }
-      }
-    }
-  }
-  if (lane < 4) {
-    sm[wave][lane] = m_ref;
-    sl[wave][lane] = l_part;
-  }
-  __syncthreads();
-  // ---- merge the wavefronts of the block; one partial per (query row, head, block)
-  constexpr float kLn2 = 0.6931471805599453f;
-  const int P = kFastD + 2;
-  const int d = tid & (kFastD - 1);
-#pragma unroll
-  for (int c0 = 0; c0 < 4; c0 += kFastBlock / kFastD) {
-    const int c = c0 + tid / kFastD;                 // head of this thread
-    if (c < G) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][c]);
-      float L = 0.0f, O = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float wt = (sm[w][c] == -INFINITY) ? 0.0f : exp2f(sm[w][c] - M);
-        L += wt * sl[w][c];
-        O += wt * so[w][c][d];
-      }
-      float* dst = a.ws + ((rq * a.Hq + (size_t)h * G + c) * a.blocks_per_unit + blockIdx.x) * P;
-      // merged in this kernel: device-coherent stores (written through to memory), so
-      // that another XCD's block can read them without any cache being flushed
-      auto put = [&](float* ptr, float val) {
-        if (a.done) __hip_atomic_store(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else *ptr = val;
-      };
-      put(dst + d, O);
-      if (d == 0) {
-        put(dst + kFastD, (M == -INFINITY) ? -INFINITY : M * kLn2);
-        put(dst + kFastD + 1, L);
-      }
-    }
-  }
-  if (!a.done) return;
-  // ---- the unit's last block to finish merges the bpu partials:
-  // out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, lse = M + ln(that sum).
-  // Every thread waits until its coherent partial stores have completed before the
-  // block is counted, and the last block reads the partials with coherent loads.
-  __shared__ int is_last;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(a.done + (rq * a.H + h), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == bpu - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  auto get = [](const float* ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  // (m, l) of every partial into LDS (the per-wave output buffer is free by now), all
-  // loads in flight at once; then each thread's output loads go out 8 at a time.
-  static_assert(8 * kMaxChunks + 4 * kFastD <= NW * 4 * kFastD, "merge tables exceed the per-wave output buffer");
-  float* const pm = &so[0][0][0];                    // [head][block], stride kMaxChunks (blocks <= chunks)
-  float* const pl = pm + 4 * kMaxChunks;
-  float* const rot = pl + 4 * kMaxChunks;             // [head][dim] merged output before rotating back
-  const float* const ubase = a.ws + (rq * a.Hq + (size_t)h * G) * bpu * P;
-  for (int t = tid; t < G * bpu; t += kFastBlock) {
-    const int c = t / bpu, sb = t - c * bpu;
-    const float* p = ubase + (size_t)t * P;
-    const float mv = get(p + kFastD), lv = get(p + kFastD + 1);
-    pm[c * kMaxChunks + sb] = mv;
-    pl[c * kMaxChunks + sb] = lv;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int c0 = 0; c0 < 4; c0 += kFastBlock / kFastD) {
-    const int c = c0 + tid / kFastD;
-    if (c < G) {
-      const size_t rh = rq * a.Hq + (size_t)h * G + c;
-      const float* src = a.ws + rh * bpu * P;
-      const float* cm = pm + c * kMaxChunks;
-      const float* cl = pl + c * kMaxChunks;
-      float M = -INFINITY;
-      for (int sb = 0; sb < bpu; ++sb) M = fmaxf(M, cm[sb]);
-      float L = 0.0f, O = 0.0f;
-      for (int s0 = 0; s0 < bpu; s0 += 8) {
-        float ov[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ov[j] = get(src + (size_t)min(s0 + j, bpu - 1) * P + d);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (s0 + j < bpu) {
-            const float ms = cm[s0 + j];
-            const float wt = (ms == -INFINITY) ? 0.0f : expf(ms - M);
-            L += wt * cl[s0 + j];
-            O += wt * ov[j];
-          }
-        }
-      }
-      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      if (a.vW > 1) rot[c * kFastD + d] = O * inv;
-      else a.out[rh * kFastD + d] = O * inv;
-      if (d == 0 && a.lse) a.lse[rh] = L > 0.0f ? M + logf(L) : -INFINITY;
-    }
-  }
-  if (a.vW > 1) {   // rotated values: the normalised transform is its own inverse
-    __syncthreads();
-    const int c = tid >> 7, pp = tid & 127;          // one butterfly per thread and stage (4 heads x 128)
-    for (int ls = 0; (1 << ls) < a.vW; ++ls) {
-      const int st = 1 << ls;
-      const int ii = ((pp >> ls) << (ls + 1)) | (pp & (st - 1));
-      if (c < G) {
-        const float x = rot[c * kFastD + ii], y = rot[c * kFastD + ii + st];
-        rot[c * kFastD + ii] = x + y;
-        rot[c * kFastD + ii + st] = x - y;
-      }
-      __syncthreads();
-    }
-    for (int p = tid; p < G * kFastD; p += kFastBlock)
-      a.out[(rq * a.Hq + (size_t)h * G) * kFastD + p] = rot[p] * a.vkappa;
-  }
-  if (tid == 0) {   // ready for the next call: every block of the unit has made its last claim
-    ctr[0] = 0;
-    a.done[rq * a.H + h] = 0;
+  const MfmaTile& t = m.tile[ti];
+  const int ll = l - t.l0, hl = h - t.h0;
+  FArgs a = g;
+  a.kc = t.kc;
+  a.ks = t.ks;
+  a.vc = t.vc;
+  a.vs = t.vs;
+  a.kchan = t.kchan;
+  a.kW = t.kW;
+  a.kkappa = t.kkappa;
+  a.vW = t.vW;
+  a.vkappa = t.vkappa;
+  a.voff = t.voff;
+  const size_t urow0 = (((size_t)b * t.ls + ll) * t.hs + hl) * g.T;
+  const float* const kchu = t.kchan ? t.kchan + ((size_t)ll * t.hs + hl) * kFastD : nullptr;
+  switch (t.pair) {
+#define KVQ_MFMA_MIX_CASE(id, KB, VB) \
+  case id: mfma_tile_unit<VB, KB>(a, S, h, rq, urow0, kchu); break;
+    KVQ_MFMA_MIX_PAIRS(KVQ_MFMA_MIX_CASE)
+#undef KVQ_MFMA_MIX_CASE
+    default: break;
   }
 }
 
@@ -853,6 +469,93 @@ template <int KB>
 static void launch_mfma_k(const FArgs& a, int vb, dim3 grid, hipStream_t st) {
   if (vb == 2) launch_mfma<2, KB>(a, grid, st);
   else launch_mfma<4, KB>(a, grid, st);
+}
+
+static float kappa_w(int W) {
+  if (W <= 1) return 1.0f;
+  int e = 0;
+  while ((1 << e) < W) ++e;
+  return (e % 2 == 0) ? ldexpf(1.0f, -e / 2) : (float)(1.0 / std::sqrt((double)W));
+}
+
+static int mfma_mix_pair(int kb, int vb) {
+#define KVQ_MFMA_MIX_ID(id, KB, VB) \
+  if (kb == KB && vb == VB) return id;
+  KVQ_MFMA_MIX_PAIRS(KVQ_MFMA_MIX_ID)
+#undef KVQ_MFMA_MIX_ID
+  return -1;
+}
+
+bool mixed_fast_supported(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q) {
+  if (n < 1 || n > kMaxSegments || Hq % heads != 0) return false;
+  const int G = Hq / heads;
+  const kvq_shape& s0 = segs[0].k->shape;
+  if ((long long)s0.batch * layers * n_q * heads > kWsCounterRows) return false;   // the merge needs counters
+  for (int i = 0; i < n; ++i) {
+    const kvq_packed& k = *segs[i].k;
+    const kvq_packed& v = *segs[i].v;
+    if (segs[i].token0 != 0 || k.shape.tokens != tokens) return false;
+    if (!fast_decode_supported(k, v, k.shape.heads * G)) return false;
+    if (k.codec.group != 128 || v.codec.group != 128 || k.mean) return false;
+    if (mfma_mix_pair(k.codec.bits, v.codec.bits) < 0) return false;
+  }
+  return true;
+}
+
+size_t mixed_fast_ws_bytes(const kvq_segment* segs, int layers, int heads, int tokens, int Hq, int n_q) {
+  kvq_shape s = segs[0].k->shape;
+  s.layers = layers;
+  s.heads = heads;
+  s.tokens = tokens;
+  return fast_part_bytes(s, Hq, n_q);
+}
+
+hipError_t launch_decode_fast_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq,
+                                    int n_q, const uint16_t* q, const int32_t* kv_len, float sm, float* out,
+                                    float* lse, int* ctr, void* part, hipStream_t st) {
+  kvq_shape s = segs[0].k->shape;
+  s.layers = layers;
+  s.heads = heads;
+  s.tokens = tokens;
+  FMixArgs m{};
+  FArgs& a = m.base;
+  a.q = q;
+  a.kv_len = kv_len;
+  a.ws = static_cast<float*>(part);
+  a.B = s.batch; a.L = layers; a.H = heads; a.T = tokens; a.Hq = Hq; a.G = Hq / heads;
+  a.n_q = n_q;
+  a.nks = 2;
+  a.nvs = 2;
+  a.gv = 128;
+  a.sm_scale = sm;
+  a.blocks_per_unit = fast_blocks_per_unit(s, n_q);
+  a.chunk_log2 = fast_chunk_log2(s);
+  a.ctr = ctr;
+  a.done = ctr + kWsCounterRows;
+  a.out = out;
+  a.lse = lse;
+  m.ntiles = n;
+  for (int i = 0; i < n; ++i) {
+    const kvq_packed& k = *segs[i].k;
+    const kvq_packed& v = *segs[i].v;
+    MfmaTile& t = m.tile[i];
+    t.kc = reinterpret_cast<const uint8_t*>(k.codes);
+    t.ks = k.scales;
+    t.vc = reinterpret_cast<const uint8_t*>(v.codes);
+    t.vs = v.scales;
+    t.kchan = k.chan_scale;
+    t.l0 = segs[i].layer0; t.ls = k.shape.layers; t.h0 = segs[i].head0; t.hs = k.shape.heads;
+    t.kW = k.codec.rot_width > 1 ? k.codec.rot_width : 0;
+    t.kkappa = kappa_w(t.kW);
+    t.vW = v.codec.rot_width > 1 ? v.codec.rot_width : 0;
+    t.vkappa = kappa_w(t.vW);
+    const int vb = v.codec.bits;
+    t.voff = (v.codec.codebook == KVQ_INT_SYM) ? 0.5f * (float)((1 << vb) - 1) : (float)(1 << (vb - 1));
+    t.pair = mfma_mix_pair(k.codec.bits, vb);
+  }
+  const long long units = (long long)s.batch * layers * heads;
+  k_decode_mfma_mix<<<dim3(a.blocks_per_unit, (unsigned)units, (unsigned)n_q), kFastBlock, 0, st>>>(m);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {

@@ -211,6 +211,13 @@ size_t mixed_ws_bytes(const kvq_segment* segs, int layers, int heads, int tokens
 hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q,
                                const uint16_t* q, const int32_t* kv_len, float sm, float* out, float* lse,
                                void* part, bool mean_shift, hipStream_t st);
+// A codec map of MFMA tiles (3-5-bit keys, 2- or 4-bit values, groups of 128, no key
+// mean) in one launch of the MFMA kernel; ctr: the workspace's counter region.
+bool mixed_fast_supported(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q);
+size_t mixed_fast_ws_bytes(const kvq_segment* segs, int layers, int heads, int tokens, int Hq, int n_q);
+hipError_t launch_decode_fast_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq,
+                                    int n_q, const uint16_t* q, const int32_t* kv_len, float sm, float* out,
+                                    float* lse, int* ctr, void* part, hipStream_t st);
 hipError_t launch_seg_init(float* out, float* lse, long long rows, int D, hipStream_t st);
 hipError_t launch_seg_prepare(const uint16_t* q, const int32_t* kvl, uint16_t* qs, int32_t* kvls, int B, int L,
                               int Ls, int l0, int n_q, int Hq, int j0, int hq, int D, int t0, int Ts, hipStream_t st);

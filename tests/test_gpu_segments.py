@@ -153,7 +153,7 @@ def test_decode_over_segments(variant):
     _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg)
 
 
-MAPS = ["alloc_319", "heads_entropy", "anchor_layer", "g8_heads", "mfma_tile"]
+MAPS = ["alloc_319", "heads_entropy", "anchor_layer", "g8_heads", "mfma_tile", "mfma_map_heads", "mfma_map_layers"]
 
 
 @pytest.mark.parametrize("path", [None, 1, 2])
@@ -206,6 +206,28 @@ def test_codec_map_in_one_launch(variant, path):
         kv_len = np.array([[[400, 0], [1, 333]]], dtype=np.int32)
         layout = [(K.Codec(A, 2, 128, 0), K.Codec(A, 2, 128, 256), 0, 2, 0, 400, 0, 1),
                   (K.Codec(A, 6, 64, 128), K.Codec(A, 3, 32, 0), 0, 2, 0, 400, 1, 1)]
+    elif variant == "mfma_map_heads":
+        # per-head key bits [5, 4, 4, 3] over 4-bit values at group 128: every tile an MFMA
+        # pair, so the default and path 2 run the map in one MFMA launch
+        w = synth.get("c3", B=2, L=3, T=512, n_q=2, k_head_scales=(3.0, 1.0, 1.0, 0.5))
+        Kx, Vx = synth.gen_kv(w)
+        q, _ = synth.gen_queries(w)
+        kv_len = np.random.default_rng(33).integers(0, 513, (2, 3, 2)).astype(np.int32)
+        kv_len[0, 1, 0] = 0
+        v4 = K.Codec(A, 4, 128, 0)
+        layout = [(K.Codec(A, 5, 128, 256), v4, 0, 3, 0, 512, 0, 1), (K.Codec(A, 4, 128, 256), v4, 0, 3, 0, 512, 1, 2),
+                  (K.Codec(A, 3, 128, 256), v4, 0, 3, 0, 512, 3, 1)]
+    elif variant == "mfma_map_layers":
+        # per-layer pairs with 2- and 4-bit values, a rotated-value tile and a tile with key
+        # channel scales, 4 query heads per KV head
+        w = synth.get("c3", L=4, T=448, n_q=3)
+        Kx, Vx = synth.gen_kv(w)
+        q, _ = synth.gen_queries(w)
+        kv_len = np.array([[[448, 31, 200], [1, 447, 448], [0, 64, 65], [300, 301, 96]]], dtype=np.int32)
+        layout = [(K.Codec(A, 3, 128, 256), K.Codec(A, 2, 128, 0), 0, 1, 0, 448),
+                  (K.Codec(A, 4, 128, 256), K.Codec(A, 4, 128, 256), 1, 2, 0, 448),
+                  (K.Codec(A, 5, 128, 128), K.Codec(K.INT_SYM, 2, 128, 0), 3, 1, 0, 448)]
+        chan_seg = 2
     else:
         # a tile the MFMA kernel would take (4-bit rotated keys, 2-bit values) beside an fp16 layer
         w = synth.get("c3", L=3, T=448, n_q=2)
