@@ -489,9 +489,11 @@ static hipError_t decode_packed(const kvq_packed* k, const kvq_packed* v, int32_
   pr.ws = part;
   pr.ws_bytes = part_bytes;
   const bool use_fast = (path == 2) || (path == 0 && fast_ok);
-  hipError_t e = use_fast ? launch_decode_fast(pr, st) : launch_decode_generic(pr, st);
-  // a key mean adds q.mean to every logit of a query: weights unchanged, lse shifted
-  if (e == hipSuccess && k->mean && lse) e = launch_lse_mean(pr, st);
+  bool mean_done = false;
+  hipError_t e = use_fast ? launch_decode_fast(pr, st, &mean_done) : launch_decode_generic(pr, st);
+  // a key mean adds q.mean to every logit of a query: weights unchanged, lse shifted (by
+  // the MFMA kernel's own merge when it merges, else here)
+  if (e == hipSuccess && k->mean && lse && !mean_done) e = launch_lse_mean(pr, st);
   return e;
 }
 

@@ -69,6 +69,7 @@ struct FArgs {
   const uint16_t* q;
   const int32_t* kv_len;
   const float* kchan;
+  const float* kmean;              // key mean [L][H][256] shifted into the lse by the in-kernel merge, or null
   float* ws;
   int B, L, H, T, Hq, G, n_q;
   int nks, nvs, gv;                // scales per row, value group
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   const long long rq = bl * a.n_q + blockIdx.z;      // blockIdx.z: query index
   const size_t urow0 = (size_t)unit * a.T;
   const float* const kchu = a.kchan ? a.kchan + ((size_t)l * a.H + h) * kFastD : nullptr;
+  const float* const kmeanu = a.kmean ? a.kmean + ((size_t)l * a.H + h) * kFastD : nullptr;
 #include "kvq_mfma_body.inc"
 }
 
@@ -295,6 +297,7 @@ struct MfmaTile {
   const uint8_t* vc;
   const uint16_t* vs;
   const float* kchan;              // [ls][hs][256] or null
+  const float* kmean;              // [ls][hs][256] or null
   int l0, ls, h0, hs;              // layers [l0, l0 + ls) x KV heads [h0, h0 + hs)
   int kW, vW;
   float kkappa, vkappa, voff;
@@ -319,7 +322,7 @@ struct MfmaLds {                   // the LDS of one block (as k_decode_mfma dec
 
 template <int VB, int KB>
 __device__ __forceinline__ void mfma_tile_unit(const FArgs& a, MfmaLds& S, int h, long long rq, size_t urow0,
-                                               const float* kchu) {
+                                               const float* kchu, const float* kmeanu) {
   constexpr int NKS = 2, NVS = 2;                    // key and value group 128
   constexpr int NW = kFastBlock / 64;
   auto& qs = S.qs;
@@ -363,9 +366,10 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma_mix(FMixArgs m) {
   a.voff = t.voff;
   const size_t urow0 = (((size_t)b * t.ls + ll) * t.hs + hl) * g.T;
   const float* const kchu = t.kchan ? t.kchan + ((size_t)ll * t.hs + hl) * kFastD : nullptr;
+  const float* const kmeanu = t.kmean ? t.kmean + ((size_t)ll * t.hs + hl) * kFastD : nullptr;
   switch (t.pair) {
 #define KVQ_MFMA_MIX_CASE(id, KB, VB) \
-  case id: mfma_tile_unit<VB, KB>(a, S, h, rq, urow0, kchu); break;
+  case id: mfma_tile_unit<VB, KB>(a, S, h, rq, urow0, kchu, kmeanu); break;
     KVQ_MFMA_MIX_PAIRS(KVQ_MFMA_MIX_CASE)
 #undef KVQ_MFMA_MIX_CASE
     default: break;
@@ -496,7 +500,7 @@ bool mixed_fast_supported(const kvq_segment* segs, int n, int layers, int heads,
     const kvq_packed& v = *segs[i].v;
     if (segs[i].token0 != 0 || k.shape.tokens != tokens) return false;
     if (!fast_decode_supported(k, v, k.shape.heads * G)) return false;
-    if (k.codec.group != 128 || v.codec.group != 128 || k.mean) return false;
+    if (k.codec.group != 128 || v.codec.group != 128) return false;
     if (mfma_mix_pair(k.codec.bits, v.codec.bits) < 0) return false;
   }
   return true;
@@ -544,6 +548,7 @@ hipError_t launch_decode_fast_mixed(const kvq_segment* segs, int n, int layers, 
     t.vc = reinterpret_cast<const uint8_t*>(v.codes);
     t.vs = v.scales;
     t.kchan = k.chan_scale;
+    t.kmean = k.mean;
     t.l0 = segs[i].layer0; t.ls = k.shape.layers; t.h0 = segs[i].head0; t.hs = k.shape.heads;
     t.kW = k.codec.rot_width > 1 ? k.codec.rot_width : 0;
     t.kkappa = kappa_w(t.kW);
@@ -558,7 +563,7 @@ hipError_t launch_decode_fast_mixed(const kvq_segment* segs, int n, int layers, 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
+hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_done) {
   const kvq_packed& k = *pr.k;
   const kvq_packed& v = *pr.v;
   const kvq_shape& s = k.shape;
@@ -599,6 +604,8 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st) {
   // unrotated values without channel scales: the last block of a unit merges its partials
   const bool fused = a.ctr && !v.chan_scale;
   a.done = fused ? pr.ctr + kWsCounterRows : nullptr;
+  a.kmean = fused ? k.mean : nullptr;              // the in-kernel merge applies a key mean's lse shift
+  if (mean_done) *mean_done = fused && k.mean;
   a.out = pr.out;
   a.lse = pr.lse;
   const long long units = (long long)s.batch * s.layers * s.heads;

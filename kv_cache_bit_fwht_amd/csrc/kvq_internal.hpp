@@ -211,8 +211,9 @@ size_t mixed_ws_bytes(const kvq_segment* segs, int layers, int heads, int tokens
 hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q,
                                const uint16_t* q, const int32_t* kv_len, float sm, float* out, float* lse,
                                void* part, bool mean_shift, hipStream_t st);
-// A codec map of MFMA tiles (3-5-bit keys, 2- or 4-bit values, groups of 128, no key
-// mean) in one launch of the MFMA kernel; ctr: the workspace's counter region.
+// A codec map of MFMA tiles (3-5-bit keys, 2- or 4-bit values, groups of 128; a tile's
+// key mean shifts its lse in the kernel's merge) in one launch of the MFMA kernel; ctr:
+// the workspace's counter region.
 bool mixed_fast_supported(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q);
 size_t mixed_fast_ws_bytes(const kvq_segment* segs, int layers, int heads, int tokens, int Hq, int n_q);
 hipError_t launch_decode_fast_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq,
@@ -225,7 +226,8 @@ hipError_t launch_seg_merge(int n, const int* l0, const int* ls, const int* j0, 
                             float* const* lsp, float* out, float* lse, int B, int L, int n_q, int Hq, int D,
                             hipStream_t st);
 bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
-hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st);
+// mean_done (optional): set when the kernel's own merge applied the key mean's lse shift.
+hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_done = nullptr);
 size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q);
 hipError_t launch_combine_partials(const AttnProblem& pr, int S, int* ctr, hipStream_t st);
 
