@@ -49,6 +49,7 @@ struct AArgs {
   const uint16_t* v16;
   float sm_scale;
   int B, L, H, T, D, Hq, G, n_q, S, chunk;
+  int qp, nqg;         // wavefront decode: query rows per wavefront, row groups per (b, l)
   int lpt_log2;
   int Dc;              // coded key length (D, or 2*(D/2+1) for rFFT keys)
   float* ws;           // split partials
@@ -56,6 +57,18 @@ struct AArgs {
   Tables tab;
   FftTables tw;        // twiddles of head_dim (rFFT keys: the query's DFT)
   DirTables dirs;      // phase-sector directions (rFFT polar keys)
+};
+
+// The problem-wide fields the wavefront body reads, as scalars (and the level tables by
+// reference), so that the codec-map kernel hands its body values rather than the address
+// of its large argument block (which the compiler would then copy to scratch).
+struct WaveView {
+  const uint16_t* q;
+  const int32_t* kv_len;
+  float* ws;
+  float sm_scale;
+  int B, L, H, T, D, Hq, G, n_q, S, chunk, lpt_log2, qp, nqg;
+  const Tables& tab;
 };
 
 // Error-kernel split partials: [2*D floats (o_quant, o_fp16)][kErrDoubles doubles]:
@@ -642,19 +655,48 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
   const int h = blockIdx.y / HG, hg = blockIdx.y - h * HG;
   const int GH = min(kWaveHeads, a.G - kWaveHeads * hg);      // query heads of this head group
-  const long long rq = blockIdx.z;                   // (b*L + l)*n_q + i
-  int n = a.T;
-  if (a.kv_len) n = min(max(a.kv_len[rq], 0), a.T);
+  // The 4 slots of a wavefront: with qp == 1, query heads 4hg.. of one query row; with
+  // qp > 1 (fewer than 4 query heads per KV head), the G heads of qp consecutive rows.
+  const long long bl = (long long)blockIdx.z / a.nqg;         // b*L + l
+  const int qg = (int)(blockIdx.z - bl * a.nqg);
+  // slot g -> its query row ((b*L + l)*n_q + i) and query head, or row -1 (absent)
+  const int qp = a.qp, Gq = a.G, nq = a.n_q;
+  auto slot = [qp, Gq, nq, qg, bl, h, hg, GH](int g, long long& row, int& head) __attribute__((always_inline)) {
+    int i;
+    if (qp > 1) {
+      i = qg * qp + g / Gq;
+      head = h * Gq + g % Gq;
+    } else {
+      i = qg;
+      head = h * Gq + kWaveHeads * hg + g;
+    }
+    const bool ok = (qp > 1) ? (i < nq) : (g < GH);
+    row = ok ? bl * nq + i : -1;
+  };
   const int split = blockIdx.x * (kBlock / 64) + wave;
-  const int t_begin = split * a.chunk, t_end = min(t_begin + a.chunk, n);
+  const int t_begin = split * a.chunk;
+  int t_end_s[kWaveHeads];                           // per slot: end of its keys in this split
+  int t_end = t_begin;                               // the furthest of them
+#pragma unroll
+  for (int g = 0; g < kWaveHeads; ++g) {
+    long long row;
+    int head;
+    slot(g, row, head);
+    int n = a.T;
+    if (row >= 0 && a.kv_len) n = min(max(a.kv_len[row], 0), a.T);
+    t_end_s[g] = row >= 0 ? min(t_begin + a.chunk, n) : t_begin;
+    t_end = max(t_end, t_end_s[g]);
+  }
   const int glog2k = 31 - __builtin_clz(kc.g > 0 ? kc.g : 1), glog2v = 31 - __builtin_clz(vc.g > 0 ? vc.g : 1);
 
-  // ---- query prologue: heads 4 hg .. 4 hg + GH - 1 in the key codec's coordinates,
-  // times the logit scale in log2 units; rows of absent heads are zero
-  const uint16_t* qsrc = a.q + ((size_t)rq * a.Hq + (size_t)h * a.G + (size_t)kWaveHeads * hg) * D;
+  // ---- query prologue: the slots' query rows in the key codec's coordinates, times the
+  // logit scale in log2 units; rows of absent slots are zero
   for (int p = tid; p < kWaveHeads * D; p += kBlock) {
     const int g = p / D, d = p - g * D;
-    float x = (g < GH) ? h2f(qsrc[(size_t)g * D + d]) : 0.0f;
+    long long row;
+    int head;
+    slot(g, row, head);
+    float x = (row >= 0) ? h2f(a.q[((size_t)row * a.Hq + head) * D + d]) : 0.0f;
     if (kch) x = x / kch[d];
     qc[g * RS + pidx(d)] = x;
   }
@@ -722,14 +764,14 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
     for (int k = 0; k < 16; ++k) acc[g][k] = 0.0f;
   }
   // rows past the range re-read a valid row of the unit (weight 0, nothing stored)
-  auto load = [&](int it, KRaw& kr, RawChunk<VCB, VB>& vr) {
+  auto load = [&](int it, KRaw& kr, RawChunk<VCB, VB>& vr) __attribute__((always_inline)) {
     const long long row = urow0 + min(t_begin + it * RPW + r, a.T - 1);
     if constexpr (KR) rfft_raw_load(kc, row, j, LPT, kr);
     else raw_load<KCB, KB>(kc, row, j, glog2k, kr);
     raw_load<VCB, VB>(vc, row, j, glog2v, vr);
   };
-  auto step = [&](int it, const KRaw& kr, const RawChunk<VCB, VB>& vr) {
-    const bool valid = t_begin + it * RPW + r < t_end;
+  auto step = [&](int it, const KRaw& kr, const RawChunk<VCB, VB>& vr) __attribute__((always_inline)) {
+    const int trow = t_begin + it * RPW + r;
     float kv[16], zr[9], zi[9];
     if constexpr (KR) rfft_raw_decode(kc, kr, j, dirc, dirs, zr, zi);
     else raw_decode<KCB, KB>(kc, kr, j, a.tab, nf4l, kv);
@@ -755,7 +797,7 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
         for (int k = 0; k < 16; ++k) x = __builtin_fmaf(q[g][k], kv[k], x);
       }
       x = row_lanes_sum(x, LPT);
-      sc[g] = valid ? x : -INFINITY;
+      sc[g] = (trow < t_end_s[g]) ? x : -INFINITY;
       grow |= sc[g] > mref[g] + 8.0f;
     }
     // the wavefront's maximum is only needed when some logit passes the reference by 8
@@ -842,8 +884,12 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
   __syncthreads();
   constexpr float kLn2 = 0.6931471805599453f;
   const int P = D + 2;
-  for (int p = tid; p < GH * D; p += kBlock) {
+  for (int p = tid; p < kWaveHeads * D; p += kBlock) {
     const int g = p / D, d = p - g * D;
+    long long row;
+    int head;
+    slot(g, row, head);
+    if (row < 0) continue;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w * kWaveHeads + g]);
@@ -855,7 +901,7 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
       o = __builtin_fmaf(wt, mo[(w * kWaveHeads + g) * D + d], o);
       lw = __builtin_fmaf(wt, ml[w * kWaveHeads + g], lw);
     }
-    float* dst = a.ws + (((size_t)rq * a.Hq + (size_t)h * a.G + (size_t)kWaveHeads * hg + g) * gridDim.x + blockIdx.x) * P;
+    float* dst = a.ws + (((size_t)row * a.Hq + head) * gridDim.x + blockIdx.x) * P;
     dst[d] = o;
     if (d == 0) {
       dst[D] = (M == -INFINITY) ? -INFINITY : M * kLn2;
@@ -869,9 +915,9 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave(AArgs a) {
   extern __shared__ float smem[];
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
   const int h = blockIdx.y / HG;
-  const long long rq = blockIdx.z;                   // (b*L + l)*n_q + i
-  const int l = (int)((rq / a.n_q) % a.L);
-  const int b = (int)(rq / ((long long)a.n_q * a.L));
+  const long long bl = (long long)blockIdx.z / a.nqg;          // b*L + l
+  const int l = (int)(bl % a.L);
+  const int b = (int)(bl / a.L);
   const long long urow0 = (((long long)b * a.L + l) * a.H + h) * a.T;
   const float* kch = a.k.chan ? a.k.chan + ((size_t)l * a.H + h) * a.D : nullptr;
   wave_unit<KCB, KB, VCB, VB>(a, a.k, a.v, smem, urow0, kch);
@@ -919,6 +965,7 @@ struct MArgs {
   float* ws;             // split partials, as the single-codec kernel writes them
   float sm_scale;
   int B, L, H, T, D, Hq, G, n_q, S, chunk, lpt_log2;
+  int qp, nqg;           // query rows per wavefront, row groups per (b, l)
   int ntiles;
   Tables tab;
   MixTile tile[kMaxSegments];
@@ -944,9 +991,9 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave_mix(MArgs a) {
   extern __shared__ float smem[];
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
   const int h = blockIdx.y / HG;
-  const long long rq = blockIdx.z;                   // (b*L + l)*n_q + i
-  const int l = (int)((rq / a.n_q) % a.L);
-  const int b = (int)(rq / ((long long)a.n_q * a.L));
+  const long long bl = (long long)blockIdx.z / a.nqg;          // b*L + l
+  const int l = (int)(bl % a.L);
+  const int b = (int)(bl / a.L);
   int ti = 0;                                        // the tiles cover every (layer, head) once
   while (ti + 1 < a.ntiles) {
     const MixTile& t = a.tile[ti];
@@ -958,9 +1005,11 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave_mix(MArgs a) {
   const long long urow0 = (((long long)b * t.ls + ll) * t.hs + hl) * a.T;
   const DevCodec kc = mix_codec(t.k), vc = mix_codec(t.v);
   const float* kch = kc.chan ? kc.chan + ((size_t)ll * t.hs + hl) * a.D : nullptr;
+  const WaveView v{a.q, a.kv_len, a.ws, a.sm_scale, a.B, a.L, a.H, a.T, a.D, a.Hq, a.G, a.n_q, a.S, a.chunk,
+                   a.lpt_log2, a.qp, a.nqg, a.tab};
   switch (t.pair) {
 #define KVQ_MIX_CASE(id, KCB, KB, VCB, VB) \
-  case id: wave_unit<KCB, KB, VCB, VB>(a, kc, vc, smem, urow0, kch); break;
+  case id: wave_unit<KCB, KB, VCB, VB>(v, kc, vc, smem, urow0, kch); break;
     KVQ_MIX_PAIRS(KVQ_MIX_CASE)
 #undef KVQ_MIX_CASE
     default: break;
@@ -1356,9 +1405,13 @@ static int split_chunk(const kvq_shape& s, int S) {
 // Splits (one wavefront each) of the wavefront decode kernel: about 8192 wavefronts
 // in all, a multiple of the 4 wavefronts of a block, at least 4 steps each.
 static int wave_rows_per_step(int D) { return 64 / (D / 16); }
+// Query rows per wavefront: with 1 or 2 query heads per KV head, the wavefront's 4 query
+// slots take the heads of 4 or 2 consecutive query rows (rows attend the same keys).
+static int wave_qp(int G, int n_q) { return (n_q > 1 && (G == 1 || G == 2)) ? kWaveHeads / G : 1; }
+static int wave_nqg(int G, int n_q) { const int qp = wave_qp(G, n_q); return (n_q + qp - 1) / qp; }
 static int decode_wave_splits(const kvq_shape& s, int Hq, int n_q) {
   const int G = Hq / s.heads, HG = (G + kWaveHeads - 1) / kWaveHeads;
-  const long long units = (long long)s.batch * s.layers * n_q * s.heads * HG;
+  const long long units = (long long)s.batch * s.layers * wave_nqg(G, n_q) * s.heads * HG;
   long long S = (8192 + units - 1) / units;
   const long long max_s = std::max(1, s.tokens / (4 * wave_rows_per_step(s.head_dim)));
   S = std::min(S, max_s);
@@ -1407,6 +1460,8 @@ static AArgs make_aargs(const AttnProblem& pr) {
   a.Hq = pr.Hq; a.G = pr.Hq / s.heads; a.n_q = pr.n_q;
   a.S = decode_splits(s, pr.Hq, pr.n_q);
   a.chunk = split_chunk(s, a.S);
+  a.qp = 1;
+  a.nqg = a.n_q;
   a.lpt_log2 = lpt_log2_of(a.D);
   a.Dc = (a.k.cb == KVQ_RFFT_POLAR || a.k.cb == KVQ_RFFT_CART) ? 2 * (a.D / 2 + 1) : a.D;
   a.ws = static_cast<float*>(pr.ws);
@@ -1508,7 +1563,9 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
     a.S = decode_wave_splits(s, pr.Hq, pr.n_q);
     const int rpw = wave_rows_per_step(a.D);
     a.chunk = ((s.tokens + a.S - 1) / a.S + rpw - 1) / rpw * rpw;
-    const long long R = (long long)a.B * a.L * a.n_q;
+    a.qp = wave_qp(a.G, a.n_q);
+    a.nqg = wave_nqg(a.G, a.n_q);
+    const long long R = (long long)a.B * a.L * a.nqg;
     bool compiled = false;
     hipError_t e = dispatch_wave(a, R, st, &compiled);
     if (e != hipSuccess) return e;
@@ -1706,6 +1763,8 @@ hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int h
   const int rpw = wave_rows_per_step(a.D);
   a.chunk = ((tokens + a.S - 1) / a.S + rpw - 1) / rpw * rpw;
   a.lpt_log2 = lpt_log2_of(a.D);
+  a.qp = wave_qp(a.G, n_q);
+  a.nqg = wave_nqg(a.G, n_q);
   a.ntiles = n;
   a.tab = host_tables();
   CArgs c{};
@@ -1729,10 +1788,10 @@ hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int h
     m.vchan = g.v->chan_scale;
     m.kmean = mean_shift ? g.k->mean : nullptr;
   }
-  const long long R = (long long)a.B * a.L * a.n_q;
+  const long long R = (long long)a.B * a.L * a.n_q;  // query rows per head
   const int HG = (a.G + kWaveHeads - 1) / kWaveHeads;
   const size_t smem = wave_smem_bytes(a.D);
-  k_decode_wave_mix<<<dim3(a.S / 4, a.H * HG, (unsigned)R), kBlock, smem, st>>>(a);
+  k_decode_wave_mix<<<dim3(a.S / 4, a.H * HG, (unsigned)((long long)a.B * a.L * a.nqg)), kBlock, smem, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_attn_combine<false><<<(unsigned)(R * Hq), kBlock, 0, st>>>(c, out, lse, nullptr, nullptr, ErrOut{});
