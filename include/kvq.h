@@ -235,10 +235,11 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
  * where it applies, else the general one), 1 = the general kernel (every codec
  * above), 2 = the MFMA kernel, KVQ_ERR_UNSUPPORTED unless: head_dim 256, tokens
  * a positive multiple of 32, at most 4 query heads per KV head, K INT_ABSMAX
- * 4-bit at group 128 or 256 (any rotation, optional chan_scale), V INT_ABSMAX
- * 2-bit or INT_SYM 2-bit at group 64..256 without chan_scale (any rotation) --
- * the 4-bit-key / 2-bit-value arms of [E22L] What I tested, and the symmetric
- * value grid of [E22L] Result. */
+ * 3-, 4- or 5-bit at group 128 or 256 (any rotation, optional chan_scale), V
+ * INT_ABSMAX or INT_SYM, 2- or 4-bit, at group 64..256 without chan_scale (any
+ * rotation) -- the 4-bit-key / 2-bit-value arms of [E22L] What I tested, the
+ * symmetric value grid of [E22L] Result, 4-bit values ([LCPP] Finding 1) and the
+ * per-head key widths of [LCPP] Finding 2. */
 kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
                               int32_t n_q, const uint16_t* q, const int32_t* kv_len,
                               float sm_scale, float* out, float* lse, void* ws,
@@ -279,9 +280,8 @@ size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg
  * segment's key mean shifts only its own lse, as the whole cache's would.
  * A codec map (every segment holding all tokens of its layer range x head range,
  * as for a per-layer bit allocation, [E21W] Result, or per-head bit widths,
- * [LCPP] Finding 2) whose codec pairs the mixed kernel compiles is decoded by
- * one launch when there are two or more segments and none would take the MFMA
- * kernel: see kvq_decode_attn_segments_ex. */
+ * [LCPP] Finding 2) with two or more segments is decoded by one launch when its
+ * tiles qualify: see kvq_decode_attn_segments_ex. */
 kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int32_t layers,
                                     int32_t heads, int32_t tokens, int32_t q_heads, int32_t n_q,
                                     const uint16_t* q,
@@ -292,12 +292,17 @@ kvq_status kvq_decode_attn_segments(const kvq_segment* segs, int32_t n_seg, int3
  * kvq_decode_attn_segments; 1 = each segment by its own launches and a
  * log-sum-exp merge; 2 = one decode launch for the whole codec map (every block
  * looks up the segment of its (layer, KV head) and decodes with that segment's
- * codecs) and one split combine.  Path 2 needs every segment to hold tokens
- * [0, tokens) of its tile and a key/value codec pair among: signed absmax keys of
- * 2-6 bits with signed absmax values of 2, 3 or 4 bits (any group, rotation and
- * channel scale), fp16/fp16, int8/int8, ternary/ternary, sign/sign, NF4 keys with
- * 4-bit signed absmax values; else KVQ_ERR_UNSUPPORTED (nothing launched).
- * Segment key means are applied by both paths.  Same workspace query; any other
+ * codecs).  Path 2 needs every segment to hold tokens [0, tokens) of its tile.  It
+ * runs on the MFMA kernel (which merges in the kernel) when every tile is one the
+ * MFMA decode takes at groups of 128 (head_dim 256, 3-5-bit signed absmax keys, 2- or
+ * 4-bit signed absmax or symmetric-grid values, no value channel scales) and the
+ * rows fit the workspace counters; otherwise on the general kernel plus one split
+ * combine, when every key/value codec pair is among: signed absmax keys of 2-6 bits
+ * with signed absmax values of 2, 3 or 4 bits (any group, rotation and channel
+ * scale), fp16/fp16, int8/int8, ternary/ternary, sign/sign, NF4 keys with 4-bit
+ * signed absmax values; else KVQ_ERR_UNSUPPORTED (nothing launched).  Path 0 takes
+ * the MFMA one-launch route whenever it applies and there are several segments.
+ * Segment key means are applied by every route.  Same workspace query; any other
  * path value is KVQ_ERR_ARG. */
 kvq_status kvq_decode_attn_segments_ex(const kvq_segment* segs, int32_t n_seg, int32_t layers,
                                        int32_t heads, int32_t tokens, int32_t q_heads, int32_t n_q,
