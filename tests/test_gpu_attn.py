@@ -199,6 +199,25 @@ def test_single_codec_routes_of_the_general_kernel(arm):
     _run_case(K, Kx, Vx, q, kv_len, kc, vc, path=1)
 
 
+@pytest.mark.parametrize("G,n_q", [(1, 5), (1, 4), (2, 3), (2, 1), (1, 1)])
+def test_general_kernel_packs_query_rows(G, n_q):
+    """With one or two query heads per KV head, the general kernel's four query slots
+    take the heads of several query rows (a group of rows may be partly filled); each
+    row keeps its own key count, including none."""
+    import kv_cache_bit_fwht_amd as K
+    H = 3
+    w = synth.get("c3", B=2, L=2, H=H, Hq=G * H, T=333, n_q=n_q)
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    kv_len = np.random.default_rng(51 + G * 10 + n_q).integers(0, 334, (2, 2, n_q)).astype(np.int32)
+    kv_len[0, 0, 0] = 0
+    kv_len[1, 1, -1] = 333
+    announce(f"general kernel, {G} query heads per KV head, {n_q} query rows")
+    for kc, vc in ((K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)),
+                   (K.Codec(K.TERNARY, 2, 8, 0), K.Codec(K.TERNARY, 2, 8, 0))):
+        _run_case(K, Kx, Vx, q, kv_len, kc, vc, check_error=False, path=1)
+
+
 @pytest.mark.parametrize("arm", ["polar", "cart", "fwht6"])
 def test_c5_transform_arms(arm):
     import kv_cache_bit_fwht_amd as K
