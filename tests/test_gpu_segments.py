@@ -153,7 +153,8 @@ def test_decode_over_segments(variant):
     _run_segments(K, Kx, Vx, q, kv_len, layout, mean_seg)
 
 
-MAPS = ["alloc_319", "heads_entropy", "anchor_layer", "g8_heads", "mfma_tile", "mfma_map_heads", "mfma_map_layers"]
+MAPS = ["alloc_319", "heads_entropy", "anchor_layer", "g8_heads", "mfma_tile", "mfma_map_heads", "mfma_map_layers",
+        "mfma_map_g2", "wave_map_g1"]
 
 
 @pytest.mark.parametrize("path", [None, 1, 2])
@@ -228,6 +229,25 @@ def test_codec_map_in_one_launch(variant, path):
                   (K.Codec(A, 4, 128, 256), K.Codec(A, 4, 128, 256), 1, 2, 0, 448),
                   (K.Codec(A, 5, 128, 128), K.Codec(K.INT_SYM, 2, 128, 0), 3, 1, 0, 448)]
         chan_seg = 2
+    elif variant == "mfma_map_g2":
+        # two query heads per KV head on the MFMA codec map, a key mean on one tile
+        w = synth.get("c3", L=2, Hq=8, T=384, n_q=2, k_mean_share=0.3)
+        Kx, Vx = synth.gen_kv(w)
+        q, _ = synth.gen_queries(w)
+        kv_len = np.array([[[384, 100], [33, 0]]], dtype=np.int32)
+        layout = [(K.Codec(A, 5, 128, 256), K.Codec(A, 2, 128, 0), 0, 2, 0, 384, 0, 3),
+                  (K.Codec(A, 3, 128, 256), K.Codec(A, 4, 128, 256), 0, 2, 0, 384, 3, 1)]
+        mean_seg = 1
+    elif variant == "wave_map_g1":
+        # one query head per KV head on the general codec map: four query rows share a
+        # wavefront, each with its own key count
+        w = synth.get("c3", L=2, Hq=4, T=300, n_q=5)
+        Kx, Vx = synth.gen_kv(w)
+        q, _ = synth.gen_queries(w)
+        kv_len = np.random.default_rng(34).integers(0, 301, (1, 2, 5)).astype(np.int32)
+        kv_len[0, 1, 4] = 0
+        layout = [(K.Codec(A, 2, 128, 256), K.Codec(A, 3, 128, 0), 0, 1, 0, 300),
+                  (K.Codec(K.SIGN, 1, 8, 0), K.Codec(K.SIGN, 1, 8, 0), 1, 1, 0, 300)]
     else:
         # a tile the MFMA kernel would take (4-bit rotated keys, 2-bit values) beside an fp16 layer
         w = synth.get("c3", L=3, T=448, n_q=2)
