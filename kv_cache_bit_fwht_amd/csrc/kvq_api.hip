@@ -560,7 +560,7 @@ kvq_status kvq_decode_attn_segments_ex(const kvq_segment* segs, int32_t n_seg, i
   // with several tiles: on the MFMA kernel when every tile is one of its pairs at group
   // 128, else on the general kernel when no tile would take the MFMA kernel
   const bool mixf_ok = mixed_fast_supported(segs, n_seg, layers, heads, tokens, q_heads, n_q);
-  const bool mix_ok = mixed_decode_supported(segs, n_seg, tokens);
+  const bool mix_ok = mixed_decode_supported(segs, n_seg, layers, heads, tokens, q_heads, n_q);
   if (path == 2 && !mixf_ok && !mix_ok) return KVQ_ERR_UNSUPPORTED;
   const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)D));
   if (mixf_ok && (path == 2 || (path == 0 && n_seg > 1)))

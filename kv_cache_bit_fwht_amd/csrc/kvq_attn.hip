@@ -1708,8 +1708,13 @@ static int mix_pair(const kvq_packed& k, const kvq_packed& v) {
   return -1;
 }
 
-bool mixed_decode_supported(const kvq_segment* segs, int n, int tokens) {
-  if (n < 1 || n > kMaxSegments) return false;
+bool mixed_decode_supported(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q) {
+  if (n < 1 || n > kMaxSegments || heads < 1 || Hq % heads != 0) return false;
+  // the launch grids over the whole map: (splits, heads x head groups, rows x row groups)
+  const int G = Hq / heads;
+  const long long gy = (long long)heads * ((G + kWaveHeads - 1) / kWaveHeads);
+  const long long gz = (long long)segs[0].k->shape.batch * layers * wave_nqg(G, n_q);
+  if (gy > 65535 || gz > 65535 || (long long)segs[0].k->shape.batch * layers * n_q * Hq > 0x7fffffffLL) return false;
   for (int i = 0; i < n; ++i) {
     if (segs[i].token0 != 0 || segs[i].k->shape.tokens != tokens) return false;
     if (mix_pair(*segs[i].k, *segs[i].v) < 0) return false;

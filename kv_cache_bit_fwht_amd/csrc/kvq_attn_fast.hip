@@ -495,6 +495,7 @@ bool mixed_fast_supported(const kvq_segment* segs, int n, int layers, int heads,
   const int G = Hq / heads;
   const kvq_shape& s0 = segs[0].k->shape;
   if ((long long)s0.batch * layers * n_q * heads > kWsCounterRows) return false;   // the merge needs counters
+  if ((long long)s0.batch * layers * heads > 65535 || n_q > 65535) return false;    // launch grid (y, z)
   for (int i = 0; i < n; ++i) {
     const kvq_packed& k = *segs[i].k;
     const kvq_packed& v = *segs[i].v;

@@ -206,7 +206,7 @@ hipError_t launch_lse_mean(const AttnProblem& pr, hipStream_t st);
 // x head range) tile, with codec pairs the mixed decode kernel compiles.  With
 // mean_shift the combine adds each tile's key-mean shift to the lse (otherwise the
 // caller does).
-bool mixed_decode_supported(const kvq_segment* segs, int n, int tokens);
+bool mixed_decode_supported(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q);
 size_t mixed_ws_bytes(const kvq_segment* segs, int layers, int heads, int tokens, int Hq, int n_q);
 hipError_t launch_decode_mixed(const kvq_segment* segs, int n, int layers, int heads, int tokens, int Hq, int n_q,
                                const uint16_t* q, const int32_t* kv_len, float sm, float* out, float* lse,

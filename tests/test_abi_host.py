@@ -429,3 +429,16 @@ def test_segments_path_is_validated_before_launching(K):
     need3 = L.kvq_decode_attn_segments_workspace(arr3, 2, 2, 4, 16, 1)
     assert L.kvq_decode_attn_segments_ex(arr3, 2, 2, 4, 100, 16, 1, FAKE, None, 0.0, FAKE, None, FAKE, need3, 2,
                                          None) == ERR_UNSUPPORTED
+
+
+def test_one_launch_codec_map_respects_the_launch_grid(K):
+    """Three one-layer tiles of 30,000 sequences each: every tile alone fits a launch
+    grid, the whole map in one launch would not (90,000 rows), so path 2 is refused
+    before anything is launched."""
+    L = K._lib
+    parts = [(I4, I4, (30000, 1, 4, 64, 128), l, 0) for l in range(3)]
+    arr, keep = _segs(K, parts)
+    need = L.kvq_decode_attn_segments_workspace(arr, 3, 3, 4, 16, 1)
+    assert need > 0
+    assert L.kvq_decode_attn_segments_ex(arr, 3, 3, 4, 64, 16, 1, FAKE, None, 0.0, FAKE, None, FAKE, need, 2,
+                                         None) == ERR_UNSUPPORTED
