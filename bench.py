@@ -602,6 +602,9 @@ def main():
                          "c3h: per-head key bits from attention entropy, as head segments; "
                          "c2a: the per-layer 3.19-bit allocation on the proxy-query probe")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions per arm (c4/c5)")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="c3 only: tokens per (layer, KV head) instead of 65,536 (a multiple of 32), to see how "
+                         "the per-call fixed costs amortise; the headline line is the default")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -626,7 +629,7 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
-    w = synth.get("c3")
+    w = synth.get("c3") if args.tokens is None else synth.get("c3", T=args.tokens)
     nq = min(args.decode_queries, w.n_q)
     log(f"generating {w.description}")
     Kx, Vx = synth.gen_kv(w)
@@ -733,7 +736,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded fp16 K/V with outlier channels, N(0,1) queries)",
-        "config": {"workload": "64K decode: B=1 L=8 H=4 T=65536 D=256, Hq=16 (GQA 4:1), "
+        "config": {"workload": f"{'64K' if w.T == 65536 else str(w.T)} decode: B=1 L=8 H=4 T={w.T} D=256, Hq=16 (GQA 4:1), "
                                "K FWHT-256 int4 absmax g128, V int2 absmax g128 (3.125 bpv), "
                                f"{nq} decode queries per step",
                    "decode_calls_per_step": nq, "packed_cache_copies": len(copies),
@@ -748,7 +751,8 @@ def main():
         "ceilings": ceil,
         "roofline": {"bound": "hbm", "kernel": "kvq_decode_attn", "achieved": round(dec_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for("decode", 1)},
+                     # the counters were read on the 64K workload
+                     "traffic": traffic_for("decode", 1) if w.T == 65536 else None},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
