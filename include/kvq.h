@@ -233,8 +233,8 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
 
 /* As kvq_decode_attn, choosing the kernel: path 0 = automatic (the MFMA kernel
  * where it applies, else the general one), 1 = the general kernel (every codec
- * above), 2 = the MFMA kernel, KVQ_ERR_UNSUPPORTED unless: head_dim 256, tokens
- * a positive multiple of 32, at most 4 query heads per KV head, K INT_ABSMAX
+ * above), 2 = the MFMA kernel, KVQ_ERR_UNSUPPORTED unless: head_dim 256, at least
+ * 32 tokens, at most 4 query heads per KV head, K INT_ABSMAX
  * 3-, 4- or 5-bit at group 128 or 256 (any rotation, optional chan_scale), V
  * INT_ABSMAX or INT_SYM, 2- or 4-bit, at group 64..256 without chan_scale (any
  * rotation) -- the 4-bit-key / 2-bit-value arms of [E22L] What I tested, the

@@ -763,9 +763,12 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc[g][k] = 0.0f;
   }
-  // rows past the range re-read a valid row of the unit (weight 0, nothing stored)
+  // rows past the split's last attended key re-read that key's row (weight 0, nothing
+  // stored): rows at or past the keys attended may never have been written (a cache
+  // filled by appends), and a weight of 0 times a code decoded from garbage can be NaN
+  const int last_row = min(max(t_end, t_begin + 1) - 1, a.T - 1);
   auto load = [&](int it, KRaw& kr, RawChunk<VCB, VB>& vr) __attribute__((always_inline)) {
-    const long long row = urow0 + min(t_begin + it * RPW + r, a.T - 1);
+    const long long row = urow0 + min(t_begin + it * RPW + r, last_row);
     if constexpr (KR) rfft_raw_load(kc, row, j, LPT, kr);
     else raw_load<KCB, KB>(kc, row, j, glog2k, kr);
     raw_load<VCB, VB>(vc, row, j, glog2v, vr);

@@ -413,7 +413,7 @@ __global__ __launch_bounds__(256) void k_fast_combine(const float* __restrict__ 
 bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   const kvq_shape& s = k.shape;
   if (s.head_dim != kFastD) return false;
-  if (s.tokens % kStep != 0 || s.tokens == 0) return false;
+  if (s.tokens < kStep) return false;              // a last step short of 32 rows reads the unit's last 32
   if (Hq / s.heads > 4) return false;
   if (k.codec.codebook != KVQ_INT_ABSMAX) return false;
   const int kb = k.codec.bits;
@@ -433,7 +433,7 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
 // Chunk size: at least 16 steps (one step per wavefront of a block to start with), and
 // at most kMaxChunks chunks per (query row, KV head).
 static int fast_chunk_log2(const kvq_shape& s) {
-  const long long steps = s.tokens / kStep;
+  const long long steps = (s.tokens + kStep - 1) / kStep;
   int cl2 = 4;
   while (((steps + (1LL << cl2) - 1) >> cl2) > kMaxChunks) ++cl2;
   return cl2;
@@ -443,14 +443,15 @@ static int fast_blocks_per_unit(const kvq_shape& s, int n_q) {
   const long long pairs = (long long)s.batch * s.layers * n_q * s.heads;
   // about one block (eight wavefronts, two per SIMD) per CU, and no more blocks than chunks
   long long bpu = (256 + pairs - 1) / pairs;
-  const long long chunks = ((long long)(s.tokens / kStep) + (1LL << fast_chunk_log2(s)) - 1) >> fast_chunk_log2(s);
+  const long long chunks = ((long long)((s.tokens + kStep - 1) / kStep) + (1LL << fast_chunk_log2(s)) - 1) >>
+                           fast_chunk_log2(s);
   if (bpu > chunks) bpu = chunks;
   if (bpu < 1) bpu = 1;
   return (int)bpu;
 }
 
 size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q) {
-  if (s.head_dim != kFastD || s.tokens % kStep != 0 || s.tokens == 0) return 0;
+  if (s.head_dim != kFastD || s.tokens < kStep) return 0;
   const int bpu = fast_blocks_per_unit(s, n_q);
   const size_t b = (size_t)s.batch * s.layers * n_q * Hq * bpu * (kFastD + 2) * sizeof(float);
   return (b + 255) / 256 * 256;

@@ -222,13 +222,13 @@ def test_decode_validates_before_launching(K):
     assert _decode(K, k, v_rfft) == ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("case", ["tokens_not_mult_32", "head_dim_128", "k_2bit", "k_6bit", "v_3bit", "v_group_32",
+@pytest.mark.parametrize("case", ["tokens_below_32", "head_dim_128", "k_2bit", "k_6bit", "v_3bit", "v_group_32",
                                   "k_minmax", "v_chan_scale", "g8", "v_lloyd"])
 def test_mfma_path_rejects_what_it_does_not_cover(K, case):
     kc, vc, shape, q_heads = (1, 4, 128, 256, 0), (1, 2, 128, 0, 0), (1, 2, 4, 64, 256), 16
     v_chan = None
-    if case == "tokens_not_mult_32":
-        shape = (1, 2, 4, 100, 256)
+    if case == "tokens_below_32":
+        shape = (1, 2, 4, 20, 256)
     elif case == "head_dim_128":
         shape = (1, 2, 4, 64, 128)
         kc = (1, 4, 128, 128, 0)

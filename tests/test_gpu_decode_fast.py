@@ -138,6 +138,18 @@ def test_fast_3_and_5_bit_keys_many_blocks_and_lengths():
         _case(K, w, K.Codec(K.INT_ABSMAX, kb, 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0), kv_len)
 
 
+@pytest.mark.parametrize("T", [32, 33, 48, 100, 333, 1000])
+def test_fast_token_counts_not_a_multiple_of_32(T):
+    """The last step of a cache whose length is not a multiple of 32 reads the unit's last
+    32 rows and masks the tokens before the step; with causal lengths too."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", B=2, L=1, T=T, n_q=3)
+    kv_len = np.array([[[T, T - 1, 1]], [[max(T - 17, 0), 0, T // 2]]], dtype=np.int32)
+    announce(f"mfma {T} tokens")
+    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), kv_len)
+    _case(K, w, K.Codec(K.INT_ABSMAX, 3, 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0), None)
+
+
 def test_fast_static_chunks_many_rows():
     """More (query row, KV head) units than the workspace has counters for: blocks take
     fixed chunks and a separate kernel merges the partials."""
@@ -161,7 +173,7 @@ def test_fast_rejects_2_bit_keys():
 
 def test_fast_rejects_unsupported_and_auto_falls_back():
     import kv_cache_bit_fwht_amd as K
-    w = synth.get("c3", L=1, T=100, n_q=1)                 # tokens not a multiple of 32
+    w = synth.get("c3", L=1, T=20, n_q=1)                  # fewer than 32 tokens
     Kx, Vx = synth.gen_kv(w)
     q, _ = synth.gen_queries(w)
     kp = _gpu_pack(K, Kx, K.Codec(K.INT_ABSMAX, 4, 128, 256))
@@ -228,3 +240,30 @@ def test_fast_full_size_64k_sampled():
             rel = np.linalg.norm(go - ro, axis=-1) / np.linalg.norm(ro, axis=-1)
             assert rel.max() < 2e-3, f"query {i} unit {(l, h)} rel {rel.max():.3g}"
             assert np.abs(lse[0, l, 0, h * G:(h + 1) * G] - rl).max() < 1e-4
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_unwritten_rows_past_the_lengths_do_not_matter(path):
+    """A cache filled by appends has rows past every query's key count that nothing has
+    written: NaN scales and all-ones codes there leave the decode of keys [0, kv_len)
+    exactly as on a clean cache (MFMA kernel and general kernel)."""
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", B=1, L=2, T=352, n_q=2)
+    Kx, Vx = synth.gen_kv(w)
+    q, _ = synth.gen_queries(w)
+    kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    kv_len = np.array([[[300, 289], [1, 299]]], dtype=np.int32)
+    announce(f"unwritten rows past the lengths, path {path}")
+    clean = (_gpu_pack(K, Kx, kc), _gpu_pack(K, Vx, vc))
+    dirty = (_gpu_pack(K, Kx, kc), _gpu_pack(K, Vx, vc))
+    B, L, H, T, D = Kx.shape
+    t = torch.arange(B * L * H * T, device="cuda:0") % T
+    for p in dirty:
+        p.scales[t >= 300] = 0x7E00                     # fp16 NaN
+        p.codes[t >= 300] = -1                          # every code bit set
+    torch.cuda.synchronize()
+    o1, l1 = _gpu_decode(K, clean[0], clean[1], q, kv_len, path=path)
+    o2, l2 = _gpu_decode(K, dirty[0], dirty[1], q, kv_len, path=path)
+    assert np.isfinite(o2).all() and np.isfinite(l2).all()
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
