@@ -212,21 +212,32 @@ def _dec_sign(codes, s16):
 
 
 def nf4_levels() -> np.ndarray:
-    """NormalFloat-4 levels (QLoRA, Dettmers et al. 2023, section 3): 8 positive
-    normal quantiles at probabilities linspace(1-d, 1/2, 9)[:-1] and 7 negative
-    ones at linspace(1-d, 1/2, 8)[:-1] with d = (1/30 + 1/32)/2, plus an exact
-    zero, scaled so the largest is 1.  Computed in fp64, rounded to binary32.
+    """NormalFloat-4 levels as published with QLoRA (Dettmers et al. 2023: the
+    construction of section 3, the table of Appendix E).
 
-    The pages name NF4 ([FMAG-6, Milestone]; fixed non-uniform codebooks win,
-    [FMAG-6, Mechanism findings]) but print no levels: parity unpinned by the
-    pages; pinned to this construction.
+    Steps, in this order:
+    - o = RN32(0.9677083), the offset to seven decimals, halfway between 1 - 1/30
+      and 1 - 1/32 (so the outermost quantiles are finite);
+    - positive side: the 9 probabilities p_i = RN32(o + i * (1/2 - o) / 8),
+      i = 0..8, each formed in fp64 then rounded to binary32, last one dropped;
+    - negative side: the same with 8 probabilities (divisor 7), last dropped,
+      and the sign flipped;
+    - each level = RN32 of the fp64 standard-normal quantile of its binary32
+      probability; an exact zero is added and the 16 values are sorted;
+    - every level is divided by the largest, in binary32.
+
+    This reproduces the 16 values printed in the paper's Appendix E bit for bit
+    (pinned by ``tests/golden/nf4_qlora.json``).  The pages name NF4 keys
+    ([FMAG-6, Milestone]; fixed non-uniform codebooks win, [FMAG-6, Mechanism
+    findings]) without printing levels, so the published table is the reading.
     """
     from scipy.stats import norm
-    off = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0)
-    pos = norm.ppf(np.linspace(off, 0.5, 9)[:-1])
-    neg = -norm.ppf(np.linspace(off, 0.5, 8)[:-1])
-    v = np.sort(np.concatenate([pos, [0.0], neg]))
-    return (v / v.max()).astype(F32)
+    o = float(F32(0.9677083))
+    pos = [F32(o + i * (0.5 - o) / 8.0) for i in range(8)]
+    neg = [F32(o + i * (0.5 - o) / 7.0) for i in range(7)]
+    v = [F32(norm.ppf(float(p))) for p in pos] + [F32(0.0)] + [F32(-norm.ppf(float(p))) for p in neg]
+    v = np.sort(np.array(v, dtype=F32))
+    return (v / v[-1]).astype(F32)
 
 
 def nf4_midpoints(levels=None) -> np.ndarray:
