@@ -6,8 +6,8 @@ group 128, values 2-bit signed absmax at group 128 (3.125 bits per value with
 the fp16 scales); 256 decode queries ~ N(0,1).  Seeded synthetic fp16 K/V stand
 in for the real 64K-span caches the pages measure on.
 
-One step = quantise+pack K and V of the whole cache (kvq_quantize_pack, two
-launches) + 256 decode-attention calls (kvq_decode_attn, one per decode query,
+One step = quantise+pack K and V of the whole cache (kvq_quantize_pack_kv, one
+launch) + 256 decode-attention calls (kvq_decode_attn, one per decode query,
 each reading the whole packed cache).  Inputs are resident in HBM before the
 timed region; three copies of the packed cache are rotated so the 256 MB
 Infinity Cache cannot serve repeats.
@@ -92,9 +92,17 @@ def measure_ceilings(torch, dev):
 
 
 def cpu_baseline(Kx, Vx, q, units_sample=2, queries_sample=4):
-    """The oracle as it stands on a bounded sample of the same workload, scaled
-    to the whole step: quantise+pack+dequantise `units_sample` (layer, head)
-    units and run fp64 attention for `queries_sample` queries on them."""
+    """The oracle as it stands, timed on this host's cores on a bounded sample of
+    the same workload and extrapolated to the whole step (the full step would take
+    about an hour of CPU time).
+
+    - quantise+pack: `units_sample` whole (layer, head) units of K and V (65,536
+      rows each) through the oracle's binary32 codec (NumPy elementwise: 1 core);
+    - decode attention: `queries_sample` decode queries against those units in
+      fp64 on the oracle's dequantised cache, once with BLAS held to 1 thread and
+      once with every core in this process's affinity mask.
+    value = decode tokens per second of the whole step (all units quantised, every
+    query attended over all units) with the all-cores attention leg."""
     from threadpoolctl import threadpool_limits
     import oracle as O
     B, L, H, T, D = Kx.shape
@@ -102,45 +110,70 @@ def cpu_baseline(Kx, Vx, q, units_sample=2, queries_sample=4):
     G = q.shape[3] // H
     kc = O.Codec(O.INT_ABSMAX, 4, 128, rot=256)
     vc = O.Codec(O.INT_ABSMAX, 2, 128)
+    ncores = len(os.sched_getaffinity(0))
+    deq = []
+    t_q = 0.0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        deq = []
         for u in range(units_sample):
             l, h = u // H, u % H
             ku = Kx[0, l, h][None, None, None]
             vu = Vx[0, l, h][None, None, None]
+            t0 = time.perf_counter()
             wk, sk, zk = O.quantize_pack(ku, kc)
             wv, sv, zv = O.quantize_pack(vu, vc)
+            t_q += time.perf_counter() - t0
             deq.append((O.dequant(wk, sk, zk, kc, ku.shape)[0, 0, 0], O.dequant(wv, sv, zv, vc, vu.shape)[0, 0, 0]))
-        t_qd = (time.perf_counter() - t0) / units_sample
+    t_q /= units_sample
+
+    def attend_all():
         t0 = time.perf_counter()
         for u in range(units_sample):
             l, h = u // H, u % H
             Kd, Vd = deq[u]
             for i in range(queries_sample):
                 O.attention.attend(q[0, l, i, h * G:(h + 1) * G].astype(np.float64), Kd, Vd, T, 1.0 / np.sqrt(D))
-        t_att = (time.perf_counter() - t0) / (units_sample * queries_sample)
+        return (time.perf_counter() - t0) / (units_sample * queries_sample)
+
+    with threadpool_limits(limits=1):
+        t_att1 = attend_all()
+    with threadpool_limits(limits=ncores):
+        t_attn = attend_all()
     units = B * L * H
-    step_s = units * t_qd + nq * units * t_att
+    unit_bytes = T * (2 * D * 2 + D * 4 // 8 + 4 + D * 2 // 8 + 4)
+    step1 = units * t_q + nq * units * t_att1
+    stepn = units * t_q + nq * units * t_attn
     return {
-        "value": round(nq * B / step_s, 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{units_sample} of {units} (layer, head) units quantised+packed+dequantised and "
-                   f"{queries_sample} of {nq} decode queries attended in fp64, scaled to the full step "
-                   f"({units} units, {nq} queries); NumPy, BLAS limited to 1 thread"),
-        "seconds_per_unit_codec": round(t_qd, 3), "seconds_per_query_unit_attention": round(t_att, 4),
+        "value": round(nq * B / stepn, 6), "unit": "tok/s", "cores": ncores, "kind": "oracle",
+        "sample": (f"extrapolated: {units_sample} of {units} (layer, head) units quantised+packed (K and V, "
+                   f"{T} rows each) and {queries_sample} of {nq} decode queries attended over them in fp64, "
+                   f"scaled to the whole step ({units} units, {nq} queries); quantise on 1 core (NumPy "
+                   f"elementwise), attention with BLAS on all {ncores} affinity cores"),
+        "value_1core": round(nq * B / step1, 6),
+        "quantize_pack_GBps_1core": round(unit_bytes / t_q / 1e9, 5),
+        "seconds_per_unit_quantize_pack": round(t_q, 3),
+        "seconds_per_query_unit_attention": {"1 core": round(t_att1, 5), f"{ncores} cores": round(t_attn, 5)},
         "cpu": _cpu_name(),
     }
 
 
 def _cpu_name():
+    """CPU model string and family/model numbers from /proc/cpuinfo."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = (x.strip() for x in line.split(":", 1))
+                    if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                        fields[k] = v
+                if not line.strip() and fields:
+                    break
     except OSError:
         pass
-    return "unknown"
+    if not fields:
+        return "unknown"
+    return (f"{fields.get('model name', 'unknown')} (family {fields.get('cpu family', '?')}, "
+            f"model {fields.get('model', '?')}, stepping {fields.get('stepping', '?')})")
 
 
 def _median_time(torch, fn, reps):
@@ -242,9 +275,10 @@ def secondary(workload, reps):
         vp = K.packed_from_fp16(vq, shape) if vc.codebook == K.FP16 else K.alloc_packed(vc, shape, dev)
 
         def quant():
-            K.kvq_quantize_pack(kq, kp)
             if vc.codebook != K.FP16:
-                K.kvq_quantize_pack(vq, vp)
+                K.kvq_quantize_pack_kv(kq, vq, kp, vp)
+            else:
+                K.kvq_quantize_pack(kq, kp)
 
         quant()
         torch.cuda.synchronize()
@@ -352,8 +386,7 @@ def anchors_workload(reps):
         K.kvq_decode_attn(kfull, vfull, Hq, 1, qd, None, 0.0, out, lse, ws1, wsb1)
 
     def append():
-        K.kvq_quantize_pack_tokens(newk, T - 1, 1, kfull)
-        K.kvq_quantize_pack_tokens(newv, T - 1, 1, vfull)
+        K.kvq_quantize_pack_tokens_kv(newk, newv, T - 1, 1, kfull, vfull)
 
     for f in (seg_step, one_step, append):
         f()
@@ -648,8 +681,7 @@ def main():
     ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     for kp, vp in copies:
-        K.kvq_quantize_pack(kd, kp)
-        K.kvq_quantize_pack(vd, vp)
+        K.kvq_quantize_pack_kv(kd, vd, kp, vp)
     torch.cuda.synchronize()
 
     if args.profile:
@@ -662,8 +694,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         kp, vp = copies[0]
-        K.kvq_quantize_pack(kd, kp)
-        K.kvq_quantize_pack(vd, vp)
+        K.kvq_quantize_pack_kv(kd, vd, kp, vp)
         for i in range(nq):
             kp2, vp2 = copies[i % len(copies)]
             K.kvq_decode_attn(kp2, vp2, w.Hq, 1, qd[i], None, 0.0, out, lse, ws, wsb, None,
@@ -690,8 +721,7 @@ def main():
         kp, vp = copies[c]
         if ev:
             ev[0].record(stream)
-        K.kvq_quantize_pack(kd, kp, sh)
-        K.kvq_quantize_pack(vd, vp, sh)
+        K.kvq_quantize_pack_kv(kd, vd, kp, vp, sh)
         if ev:
             ev[1].record(stream)
         for i in range(nq):
@@ -734,7 +764,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp16 MFMA operands, fp32 accumulation (codec: fp32)",
         "data": "synthetic (seeded fp16 K/V with outlier channels, N(0,1) queries)",
         "config": {"workload": f"{'64K' if w.T == 65536 else str(w.T)} decode: B=1 L=8 H=4 T={w.T} D=256, Hq=16 (GQA 4:1), "
                                "K FWHT-256 int4 absmax g128, V int2 absmax g128 (3.125 bpv), "

@@ -197,9 +197,33 @@ kvq_status kvq_quantize_pack(const uint16_t* x_fp16, const kvq_packed* out, void
 kvq_status kvq_quantize_pack_tokens(const uint16_t* x_fp16, int32_t token0, int32_t n_tokens,
                                     const kvq_packed* out, void* stream);
 
+/* The keys and values of one cache in one call: the same results as
+ * kvq_quantize_pack(k_fp16, k) followed by kvq_quantize_pack(v_fp16, v) ([E22L]
+ * What I tested: 4-bit rotated keys with 2-bit values; [LCPP] independent K and V
+ * cache types).  When both are signed-absmax codecs at head_dim 256 (2, 4 or 8
+ * bits, rotation 0 or 256, group >= 16) without a mean or channel scales, one
+ * kernel codes both tensors (each wavefront a quad of key rows and the same quad
+ * of value rows); otherwise the two tensors are coded by their own launches.
+ * k and v must have the same shape and distinct outputs; k_fp16 and v_fp16 are
+ * [B][L][H][T][D] fp16.  Errors as for kvq_quantize_pack; nothing is launched on
+ * an error.  A cache with no tokens is a no-op. */
+kvq_status kvq_quantize_pack_kv(const uint16_t* k_fp16, const uint16_t* v_fp16, const kvq_packed* k,
+                                const kvq_packed* v, void* stream);
+
+/* Append path for keys and values together: kvq_quantize_pack_tokens on k and on
+ * v with the same window, in one launch where kvq_quantize_pack_kv would use one
+ * ([FMAG-6] The winning recipe: each decode step writes its token's K and V into
+ * the cache).  k_fp16 and v_fp16 are [B][L][H][n_tokens][D]. */
+kvq_status kvq_quantize_pack_tokens_kv(const uint16_t* k_fp16, const uint16_t* v_fp16, int32_t token0,
+                                       int32_t n_tokens, const kvq_packed* k, const kvq_packed* v,
+                                       void* stream);
+
 /* Dequantise `in` to fp32 x_hat [B][L][H][T][D] in the original coordinates
  * (inverse codebook, inverse rotation, division by chan_scale, addition of the
- * mean). */
+ * mean): the reconstructed K and V whose error against fp16 is the squared error
+ * over signal energy of [E21W] Benchmark, and the values read back by the
+ * simulations of [E22L] What I tested (quantise, then dequantise post-RoPE K/V).
+ * Every element is written; results are bit-identical to the CPU oracle. */
 kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream);
 
 /* Bytes of workspace kvq_decode_attn needs for these sizes.  Its first 65536

@@ -30,7 +30,7 @@ EXPORTS = [
     "kvq_attn_error_workspace", "kvq_attn_error", "kvq_quantize_pack_tokens",
     "kvq_decode_attn_segments_workspace", "kvq_decode_attn_segments", "kvq_decode_attn_segments_ex",
     "kvq_effective_bits",
-    "kvq_attn_error_ex",
+    "kvq_attn_error_ex", "kvq_quantize_pack_kv", "kvq_quantize_pack_tokens_kv",
 ]
 
 
@@ -102,6 +102,8 @@ def _load():
         "kvq_decode_attn_segments_ex": ([P, I32, I32, I32, I32, I32, I32, P, P, F, P, P, P, SZ, I32, P], I32),
         "kvq_effective_bits": ([P, I32, I32, I32, I32], D),
         "kvq_attn_error_ex": ([P, P, P, P, I32, I32, P, P, F, P, P, SZ, P], I32),
+        "kvq_quantize_pack_kv": ([P, P, P, P, P], I32),
+        "kvq_quantize_pack_tokens_kv": ([P, P, I32, I32, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -241,6 +243,21 @@ def kvq_quantize_pack_tokens(x_fp16, token0: int, n_tokens: int, out: Packed, st
     pc = out.c()
     _check("kvq_quantize_pack_tokens",
            _lib.kvq_quantize_pack_tokens(_ptr(x_fp16), token0, n_tokens, ctypes.byref(pc), _stream(stream)))
+
+
+def kvq_quantize_pack_kv(k_fp16, v_fp16, k: Packed, v: Packed, stream=None):
+    """Keys and values of one cache in one call (one launch where both codecs allow)."""
+    kc, vc = k.c(), v.c()
+    _check("kvq_quantize_pack_kv", _lib.kvq_quantize_pack_kv(_ptr(k_fp16), _ptr(v_fp16), ctypes.byref(kc),
+                                                             ctypes.byref(vc), _stream(stream)))
+
+
+def kvq_quantize_pack_tokens_kv(k_fp16, v_fp16, token0: int, n_tokens: int, k: Packed, v: Packed, stream=None):
+    """Append path for K and V together: tokens [token0, token0 + n_tokens) of both."""
+    kc, vc = k.c(), v.c()
+    _check("kvq_quantize_pack_tokens_kv",
+           _lib.kvq_quantize_pack_tokens_kv(_ptr(k_fp16), _ptr(v_fp16), token0, n_tokens, ctypes.byref(kc),
+                                            ctypes.byref(vc), _stream(stream)))
 
 
 @dataclasses.dataclass

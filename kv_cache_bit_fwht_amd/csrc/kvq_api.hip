@@ -52,30 +52,26 @@ static void lloyd_max_levels(int n, float* out) {
   for (int k = n; k < 16; ++k) out[k] = INFINITY;
 }
 
-// NormalFloat-4 (QLoRA, Dettmers et al. 2023, section 3): 8 positive normal
-// quantiles at probabilities linspace(1-d, 1/2, 9) without its last point, 7
-// negative ones at linspace(1-d, 1/2, 8) without its last point, d = (1/30 +
-// 1/32)/2, an exact zero, all divided by the largest; fp64 then binary32.
-// The pages name NF4 ([FMAG-6] Milestone) without printing levels.
+// NormalFloat-4 levels as published with QLoRA (Dettmers et al. 2023: the
+// construction of section 3, the table of Appendix E): offset o = RN32(0.9677083);
+// 8 positive levels at probabilities RN32(o + i (1/2 - o) / 8), i < 8, and 7
+// negative ones at RN32(o + i (1/2 - o) / 7), i < 7 (each probability formed in
+// fp64, rounded to binary32); each level the fp64 normal quantile of its binary32
+// probability, rounded to binary32; an exact zero; all divided by the largest in
+// binary32.  This gives the paper's printed table bit for bit.  The pages name NF4
+// ([FMAG-6] Milestone) without printing levels.
 static Tables build_tables() {
   Tables t{};
-  const double off = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
-  double v[16];
+  const double o = (double)(float)0.9677083;
+  float v[16];
   int n = 0;
-  {
-    const double step = (0.5 - off) / 8.0;
-    for (int i = 0; i < 8; ++i) v[n++] = norm_ppf(i * step + off);
-  }
-  v[n++] = 0.0;
-  {
-    const double step = (0.5 - off) / 7.0;
-    for (int i = 0; i < 7; ++i) v[n++] = -norm_ppf(i * step + off);
-  }
+  for (int i = 0; i < 8; ++i) v[n++] = (float)norm_ppf((double)(float)(o + i * (0.5 - o) / 8.0));
+  v[n++] = 0.0f;
+  for (int i = 0; i < 7; ++i) v[n++] = (float)(-norm_ppf((double)(float)(o + i * (0.5 - o) / 7.0)));
   // sort ascending (insertion sort: 16 values)
   for (int i = 1; i < 16; ++i)
-    for (int k = i; k > 0 && v[k - 1] > v[k]; --k) { double tmp = v[k]; v[k] = v[k - 1]; v[k - 1] = tmp; }
-  const double mx = v[15];
-  for (int i = 0; i < 16; ++i) t.nf4_lv[i] = (float)(v[i] / mx);
+    for (int k = i; k > 0 && v[k - 1] > v[k]; --k) { float tmp = v[k]; v[k] = v[k - 1]; v[k - 1] = tmp; }
+  for (int i = 0; i < 16; ++i) t.nf4_lv[i] = v[i] / v[15];
   for (int i = 0; i < 15; ++i) {
     const float s = t.nf4_lv[i] + t.nf4_lv[i + 1];
     t.nf4_mid[i] = s * 0.5f;
@@ -333,6 +329,50 @@ kvq_status kvq_quantize_pack_tokens(const uint16_t* x_fp16, int32_t token0, int3
   if (is_rfft(out->codec.codebook))
     return hip_status(launch_rfft_quantize_tokens(x_fp16, *out, token0, n_tokens, (hipStream_t)stream));
   return hip_status(launch_quantize_tokens(x_fp16, *out, token0, n_tokens, (hipStream_t)stream));
+}
+
+// K and V of one cache: the two kvq_quantize_pack_tokens calls in one, sharing a
+// launch when both codecs allow it.
+static kvq_status quantize_kv(const uint16_t* k_fp16, const uint16_t* v_fp16, bool whole, int32_t token0,
+                              int32_t n_tokens, const kvq_packed* k, const kvq_packed* v, void* stream) {
+  kvq_status st = check_packed(k, true);
+  if (st != KVQ_OK) return st;
+  st = check_packed(v, true);
+  if (st != KVQ_OK) return st;
+  if (!same_shape(k->shape, v->shape)) return KVQ_ERR_ARG;
+  if (!k_fp16 || !v_fp16) return KVQ_ERR_ARG;
+  if (!aligned16(k_fp16) || !aligned16(v_fp16)) return KVQ_ERR_ALIGN;
+  if (k->codes == v->codes || (k->scales && k->scales == v->scales)) return KVQ_ERR_ARG;
+  if (whole) {
+    token0 = 0;
+    n_tokens = k->shape.tokens;
+    if (n_tokens == 0) return KVQ_OK;
+  } else if (token0 < 0 || n_tokens < 1 || (long long)token0 + n_tokens > k->shape.tokens) {
+    return KVQ_ERR_ARG;
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  const bool window = !whole && n_tokens != k->shape.tokens;
+  if (is_rfft(k->codec.codebook) || is_rfft(v->codec.codebook)) {
+    auto one = [&](const uint16_t* x, const kvq_packed& p) {
+      if (is_rfft(p.codec.codebook))
+        return window ? launch_rfft_quantize_tokens(x, p, token0, n_tokens, s) : launch_rfft_quantize(x, p, s);
+      return window ? launch_quantize_tokens(x, p, token0, n_tokens, s) : launch_quantize(x, p, s);
+    };
+    const hipError_t e = one(k_fp16, *k);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(one(v_fp16, *v));
+  }
+  return hip_status(launch_quantize_kv(k_fp16, v_fp16, *k, *v, token0, n_tokens, s));
+}
+
+kvq_status kvq_quantize_pack_kv(const uint16_t* k_fp16, const uint16_t* v_fp16, const kvq_packed* k,
+                                const kvq_packed* v, void* stream) {
+  return quantize_kv(k_fp16, v_fp16, true, 0, 0, k, v, stream);
+}
+
+kvq_status kvq_quantize_pack_tokens_kv(const uint16_t* k_fp16, const uint16_t* v_fp16, int32_t token0,
+                                       int32_t n_tokens, const kvq_packed* k, const kvq_packed* v, void* stream) {
+  return quantize_kv(k_fp16, v_fp16, false, token0, n_tokens, k, v, stream);
 }
 
 kvq_status kvq_dequant(const kvq_packed* in, float* x_hat, void* stream) {

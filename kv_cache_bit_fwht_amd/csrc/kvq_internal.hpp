@@ -156,6 +156,8 @@ struct RowGeom {        // a [B][L][H][T][D] tensor seen as rows
 
 hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t st);
 hipError_t launch_quantize_tokens(const uint16_t* x, const kvq_packed& p, int t0, int n, hipStream_t st);
+hipError_t launch_quantize_kv(const uint16_t* kx, const uint16_t* vx, const kvq_packed& kp, const kvq_packed& vp,
+                              int t0, int n, hipStream_t st);
 hipError_t launch_rfft_quantize_tokens(const uint16_t* x, const kvq_packed& p, int t0, int n, hipStream_t st);
 hipError_t launch_dequant(const kvq_packed& p, float* xhat, hipStream_t st);
 hipError_t launch_calibrate(const uint16_t* k, const kvq_shape& s, float* c, hipStream_t st);
