@@ -269,6 +269,27 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
                               float sm_scale, float* out, float* lse, void* ws,
                               size_t ws_bytes, int32_t path, void* stream);
 
+/* Bytes of the library's own device scratch used by kvq_decode_attn_static (one
+ * copy on every GPU the library runs on, held until the process ends). */
+#define KVQ_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* kvq_decode_attn without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The split-K partials and work counters live in a static device
+ * array of KVQ_STATIC_SCRATCH_BYTES per GPU instead of `ws`; nothing is allocated
+ * or freed, by the library or by anything it calls.  Runs on the current device
+ * (`stream` must belong to it); the first call on a device takes the array's
+ * device address and clears its counter region with a kernel on `stream`.  Every
+ * call on a GPU shares that GPU's array and leaves its counters zero (the partials
+ * keep the last call's contents): calls on one GPU that overlap in time (other
+ * streams, other threads) race and must be serialised by the caller.  Returns
+ * KVQ_ERR_WORKSPACE, launching nothing, when kvq_decode_attn_workspace() for these
+ * sizes exceeds KVQ_STATIC_SCRATCH_BYTES (the 64K workload with one decode query
+ * needs about 1.1 MB).  Arguments, results and other errors as kvq_decode_attn. */
+kvq_status kvq_decode_attn_static(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
+                                  int32_t n_q, const uint16_t* q, const int32_t* kv_len,
+                                  float sm_scale, float* out, float* lse, void* stream);
+
 /* One piece of a logical cache of `layers` x `heads` x `tokens`: packed K and V
  * (same shape; batch and head_dim equal to the other segments') holding layers
  * [layer0, layer0 + k->shape.layers), KV heads [head0, head0 + k->shape.heads)

@@ -30,7 +30,7 @@ EXPORTS = [
     "kvq_attn_error_workspace", "kvq_attn_error", "kvq_quantize_pack_tokens",
     "kvq_decode_attn_segments_workspace", "kvq_decode_attn_segments", "kvq_decode_attn_segments_ex",
     "kvq_effective_bits",
-    "kvq_attn_error_ex", "kvq_quantize_pack_kv", "kvq_quantize_pack_tokens_kv",
+    "kvq_attn_error_ex", "kvq_quantize_pack_kv", "kvq_quantize_pack_tokens_kv", "kvq_decode_attn_static",
 ]
 
 
@@ -104,6 +104,7 @@ def _load():
         "kvq_attn_error_ex": ([P, P, P, P, I32, I32, P, P, F, P, P, SZ, P], I32),
         "kvq_quantize_pack_kv": ([P, P, P, P, P], I32),
         "kvq_quantize_pack_tokens_kv": ([P, P, I32, I32, P, P, P], I32),
+        "kvq_decode_attn_static": ([P, P, I32, I32, P, P, F, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -339,6 +340,18 @@ def kvq_decode_attn(k: Packed, v: Packed, q_heads: int, n_q: int, q, kv_len, sm_
 def kvq_decode_attn_ex(k: Packed, v: Packed, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes,
                        path: int, stream=None):
     kvq_decode_attn(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes, stream, path)
+
+
+STATIC_SCRATCH_BYTES = 16 << 20      # KVQ_STATIC_SCRATCH_BYTES of kvq.h
+
+
+def kvq_decode_attn_static(k: Packed, v: Packed, q_heads: int, n_q: int, q, kv_len, sm_scale: float, out, lse,
+                           stream=None):
+    """kvq_decode_attn on the library's own device scratch: no workspace, nothing allocated."""
+    kc, vc = k.c(), v.c()
+    _check("kvq_decode_attn_static",
+           _lib.kvq_decode_attn_static(ctypes.byref(kc), ctypes.byref(vc), q_heads, n_q, _ptr(q), _ptr(kv_len),
+                                       sm_scale, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def kvq_attn_error_workspace(shape: Shape, q_heads: int, n_q: int) -> int:

@@ -201,6 +201,40 @@ static kvq_status hip_status(hipError_t e) {
   return KVQ_ERR_HIP;
 }
 
+// Allocation-free decode: the workspace is the library's own device array `scratch`
+// (KVQ_STATIC_SCRATCH_BYTES, one copy per GPU, alive until the process ends).  Host
+// code never passes the array's name to a kernel: on the first call on a device (that
+// device current) its device address is taken with hipGetSymbolAddress and kept per
+// device, and the counter region is cleared once by a fill kernel on the caller's
+// stream (a kernel rather than a memset, so a first call inside graph capture records
+// a kernel node).  Every decode leaves the counters zero again.
+static __device__ __align__(256) unsigned char scratch[KVQ_STATIC_SCRATCH_BYTES];
+
+__global__ void k_zero_words(uint32_t* p, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static kvq_status static_scratch(void** out, hipStream_t st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return KVQ_ERR_HIP;
+    const long long words = (long long)(kWsCounterBytes / sizeof(uint32_t));
+    k_zero_words<<<(unsigned)((words + kBlock - 1) / kBlock), kBlock, 0, st>>>(static_cast<uint32_t*>(ptr), words);
+    if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
 }  // namespace kvq
 
 using namespace kvq;
@@ -565,6 +599,23 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
                            const uint16_t* q, const int32_t* kv_len, float sm_scale, float* out, float* lse,
                            void* ws, size_t ws_bytes, void* stream) {
   return kvq_decode_attn_ex(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes, 0, stream);
+}
+
+kvq_status kvq_decode_attn_static(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
+                                  const uint16_t* q, const int32_t* kv_len, float sm_scale, float* out, float* lse,
+                                  void* stream) {
+  kvq_status st = check_attn(k, v, q_heads, n_q, q);
+  if (st != KVQ_OK) return st;
+  if (!out) return KVQ_ERR_ARG;
+  if (!aligned16(out) || (lse && !aligned16(lse)) || (kv_len && !aligned16(kv_len))) return KVQ_ERR_ALIGN;
+  if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
+  const size_t need = kWsCounterBytes + decode_ws_bytes(k->shape, q_heads, n_q);
+  if (need > (size_t)KVQ_STATIC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = static_scratch(&ws, (hipStream_t)stream);
+  if (st != KVQ_OK) return st;
+  return kvq_decode_attn_ex(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, (size_t)KVQ_STATIC_SCRATCH_BYTES,
+                            0, stream);
 }
 
 size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,
