@@ -263,7 +263,7 @@ template <int NKS, int NVS, int VB, int KB>
 __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   constexpr int NW = kFastBlock / 64;                // wavefronts per block
   __shared__ __align__(16) float qs[4][kFastD + 16];
-  __shared__ float qsum_s[2][4][2];                 // [part][head][key group] sums of the MFMA query operand
+  __shared__ float qsum_s[2][4][3];                 // [part][head][key group] sums of the MFMA query operand; [0][head][2] 1 / query scale
   __shared__ float so[NW][4][kFastD];               // per-wave outputs [wave][head][dim]
   __shared__ float sm[NW][4], sl[NW][4];            // per-wave reference max (log2 units) and sum
   __shared__ half8_t qbs[8][32];                     // MFMA B operands [chunk][16 part + 4 kg + head]
@@ -312,7 +312,7 @@ struct FMixArgs {
 
 struct MfmaLds {                   // the LDS of one block (as k_decode_mfma declares it)
   alignas(16) float qs[4][kFastD + 16];
-  float qsum_s[2][4][2];
+  float qsum_s[2][4][3];
   float so[kFastBlock / 64][4][kFastD];
   float sm[kFastBlock / 64][4], sl[kFastBlock / 64][4];
   half8_t qbs[8][32];

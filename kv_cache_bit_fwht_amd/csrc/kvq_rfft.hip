@@ -1,8 +1,13 @@
 // rFFT physical codecs ([FMAG-R] HF forum thread "Fourier Magnitude KV Cache
 // Quantization", Colab-probe reply: rFFT + packed magnitude index + packed
 // phase-angle index, and the real/imaginary control): quantise+pack and
-// dequantise kernels.  One wavefront per row, in an LDS region of its own, so the
-// per-row steps need no block barrier; the transform runs in LDS.
+// dequantise kernels.  A row is held by N/16 lanes, so a wavefront codes 16, 8 or
+// 4 rows at once: each lane gathers 16 bit-reversed inputs and runs the radix-2
+// stages of span <= 16 in registers; one wavefront-local LDS transpose hands every
+// lane the inputs of the longer spans, which also run in registers with twiddles
+// from LDS.  Scales come from DPP reductions over half rows, phase sectors from two
+// side tests around an arctangent estimate, and codes are packed through LDS into
+// coalesced stores.  No block barrier follows the table load.
 #include "kvq_rfft.hpp"
 
 namespace kvq {
