@@ -287,6 +287,11 @@ def secondary(workload, reps):
         torch.cuda.synchronize()
         t_d = _median_time(torch, lambda: K.kvq_decode_attn(kp, vp, Hq, 1, qq, None, 0.0, out, lse, ws, wsb), reps)
         quality = None
+        if workload in ("c4", "c5"):                 # attention-visible error of 16 decode queries
+            nqe = 16
+            qe = torch.from_numpy(np.ascontiguousarray(q[:, lo:, :nqe]).view(np.int16)).to(dev)
+            quality, _ = _quality(K, torch, dev, kq, vq, kp, vp, qe, None, Hq, nqe, shape)
+            quality["queries"] = nqe
         if workload in ("c3v", "c3m"):               # attention-visible error of 16 queries
             nqe = 16
             qe = torch.from_numpy(np.ascontiguousarray(q[:, :, :nqe]).view(np.int16)).to(dev)
@@ -326,6 +331,98 @@ def secondary(workload, reps):
         if workload == "c3m":
             rec["key_mean"] = {"subtracted": bool(use_mean), "kvq_key_mean_us": round(mean_us, 1),
                                "share_of_key_energy": w.k_mean_share}
+        print(json.dumps(rec), flush=True)
+        del kp, vp
+        torch.cuda.empty_cache()
+
+
+def _quality(K, torch, dev, k16, v16, kp, vp, qq, kv_len, Hq, nq, shape):
+    """Attention-visible error of a packed cache against fp16 ([E21W] Benchmark): per-row
+    KL and output error, per-unit K/V squared error over energy, and the ladder's other
+    rungs, from kvq_attn_error_ex on the GPU; summaries as in the pages (means over rows
+    and units, pooled energies)."""
+    B, L = shape.batch, shape.layers
+    rows = (B, L, nq, Hq)
+    o = {k: torch.empty(rows, dtype=torch.float32, device=dev) for k in ("kl", "relerr", "renyi2", "js",
+                                                                       "logit_relerr", "top1")}
+    kv = torch.empty((B, L, shape.heads, 4), dtype=torch.float64, device=dev)
+    wb = K.kvq_attn_error_workspace(shape, Hq, nq)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=dev)
+    K.kvq_attn_error_ex(k16, v16, kp, vp, Hq, nq, qq, kv_len, 0.0, ws, wb, kv_err=kv, **o)
+    torch.cuda.synchronize()
+    a = {k: v.double().cpu().numpy() for k, v in o.items()}
+    kvn = kv.double().cpu().numpy()
+    unit = lambda i: np.where(kvn[..., i + 1] > 0, kvn[..., i] / np.maximum(kvn[..., i + 1], 1e-300), 0.0)
+    return {"mean_KL": float(a["kl"].mean()), "p99_KL": float(np.quantile(a["kl"], 0.99)),
+            "mean_out_relerr": float(a["relerr"].mean()), "mean_JS": float(a["js"].mean()),
+            "mean_logit_relerr": float(a["logit_relerr"].mean()), "top1_flip_rate": float(a["top1"].mean()),
+            "mean_renyi2_fp16": float(a["renyi2"].mean()),
+            "K_rel_sq_err": float(kvn[..., 0].sum() / kvn[..., 1].sum()),
+            "V_rel_sq_err": float(kvn[..., 2].sum() / kvn[..., 3].sum()) if kvn[..., 3].sum() > 0 else 0.0,
+            "K_rel_sq_err_unit_mean": float(unit(0).mean()), "V_rel_sq_err_unit_mean": float(unit(2).mean()),
+            "rows": int(np.prod(rows))}, a
+
+
+def config_quality(workload):
+    """c1 and c2: the quality reports these configurations ask for, at full size, from
+    the GPU error kernel.
+
+    c1 (tiny reference): K and V int4 min-max at group 32 with an fp16 scale and an fp16
+    minimum per group, no rotation; 16 causal queries at positions in [256, 512), keys
+    [0, p]; K/V squared error over signal energy, attention output error, KL.
+    c2 (proxy-query probe, [E21W] What I tested and Result): arms A (min-max), B
+    (Hadamard-256 then signed absmax), C (per-channel key scales calibrated on sequence
+    0, then min-max) and D (the scales, then Hadamard then absmax; values Hadamard then
+    absmax), each at 3 and 4 bits, group 32, on K and V; 128 proxy queries per sequence
+    and layer (the keys at positions in [3000, 6000)) attending the keys before them;
+    attention error and KL per sequence."""
+    import torch
+    import kv_cache_bit_fwht_amd as K
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.get(workload)
+    log(f"generating {w.description}")
+    Kx, Vx = synth.gen_kv(w)
+    q, kv_len = synth.gen_queries(w, Kx)
+    B, L, H, T, D, Hq, nq = w.B, w.L, w.H, w.T, w.D, w.Hq, w.n_q
+    shape = K.Shape(B, L, H, T, D)
+    kd = torch.from_numpy(Kx.view(np.int16)).to(dev)
+    vd = torch.from_numpy(Vx.view(np.int16)).to(dev)
+    qd = torch.from_numpy(q.view(np.int16)).to(dev)
+    kvl = torch.from_numpy(kv_len).to(dev)
+    A, MM = K.INT_ABSMAX, K.INT_MINMAX
+    if workload == "c1":
+        arms = {"K, V int4 min-max g32 (fp16 scale and min), no rotation": (K.Codec(MM, 4, 32, 0),
+                                                                            K.Codec(MM, 4, 32, 0), False)}
+    else:
+        arms = {}
+        for b in (3, 4):
+            arms[f"A: min-max, {b}-bit g32"] = (K.Codec(MM, b, 32, 0), K.Codec(MM, b, 32, 0), False)
+            arms[f"B: Hadamard-256 + signed absmax, {b}-bit g32"] = (K.Codec(A, b, 32, 256), K.Codec(A, b, 32, 256),
+                                                                    False)
+            arms[f"C: K channel scales + min-max, {b}-bit g32"] = (K.Codec(MM, b, 32, 0), K.Codec(MM, b, 32, 0), True)
+            arms[f"D: K channel scales + Hadamard-256 + absmax, {b}-bit g32"] = (K.Codec(A, b, 32, 256),
+                                                                             K.Codec(A, b, 32, 256), True)
+    chan = None
+    if any(a[2] for a in arms.values()):
+        chan = torch.empty((L, H, D), dtype=torch.float32, device=dev)
+        K.kvq_calibrate_chan_scale(kd[:1].contiguous(), K.Shape(1, L, H, T, D), chan)
+    for name, (kc, vc, pre) in arms.items():
+        kp = K.alloc_packed(kc, shape, dev, chan_scale=chan if pre else None)
+        vp = K.alloc_packed(vc, shape, dev)
+        K.kvq_quantize_pack_kv(kd, vd, kp, vp)
+        summ, a = _quality(K, torch, dev, kd, vd, kp, vp, qd, kvl, Hq, nq, shape)
+        rec = {"workload": f"{workload}: B={B} L={L} H={H} T={T} D={D} Hq={Hq}, {nq} queries per sequence and layer"
+                           + (" (proxy queries: the keys at positions in [3000, 6000), keys before them)"
+                              if workload == "c2" else " at positions in [256, 512), keys [0, p]"),
+               "arm": name,
+               "bits_per_value": round((K.kvq_bits_per_value(kc, D) + K.kvq_bits_per_value(vc, D)) / 2, 4),
+               "quality": summ}
+        if B > 1:
+            rec["per_sequence"] = {"mean_out_relerr": [round(float(a["relerr"][b].mean()), 5) for b in range(B)],
+                                   "mean_KL": [round(float(a["kl"][b].mean()), 6) for b in range(B)]}
+            if workload == "c2":
+                rec["per_sequence"]["note"] = "sequence 0 is the channel-scale calibration sequence"
         print(json.dumps(rec), flush=True)
         del kp, vp
         torch.cuda.empty_cache()
@@ -627,8 +724,10 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for hardware-counter passes: a known-size copy (the counters' "
                          "calibration), one quantize+pack pair and --decode-queries decode calls")
-    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "c3v", "c3m", "c3a", "c3h", "c2a"],
-                    help="c3: the headline line (default); c4/c5: one line per codec arm of those configs; "
+    ap.add_argument("--workload", default="c3", choices=["c3", "c1", "c2", "c4", "c5", "c3v", "c3m", "c3a", "c3h", "c2a"],
+                    help="c3: the headline line (default); c1/c2: the quality reports of the tiny reference and "
+                         "of the proxy-query probe's arms A-D at 3 and 4 bits; c4/c5: one line per codec arm of "
+                         "those configs, with throughput and the attention error and KL of 16 decode queries; "
                          "c3v: the 64K cache with each value codebook, with attention KL; "
                          "c3m: the 64K cache with a shared key mean, keys coded with and without it; "
                          "c3a: the 64K cache as decode segments with fp16 anchors, and the append path; "
@@ -644,6 +743,9 @@ def main():
               "(see DESIGN.md for how the path would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload in ("c1", "c2"):
+        config_quality(args.workload)
+        return
     if args.workload == "c3a":
         anchors_workload(args.reps)
         return

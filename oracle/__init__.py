@@ -32,9 +32,10 @@ in; stored scales are IEEE binary16 as the pages fix (fp16 group scales,
 oracle's own dequantised values.
 
 Functions whose results the pages do not pin are marked "parity unpinned" in
-their docstrings: the NF4 level values (the pages name NF4 but print no table)
-and the Gaussian Lloyd-Max levels (named, not printed; pinned by the Lloyd-Max
-optimality conditions instead).
+their docstrings: the Gaussian Lloyd-Max levels (named, not printed; pinned by
+the Lloyd-Max optimality conditions instead).  The NF4 levels (the pages name NF4
+but print no table) follow the QLoRA construction and are pinned to the table
+printed in that paper's Appendix E.
 """
 from .codec import (  # noqa: F401
     Codec,
