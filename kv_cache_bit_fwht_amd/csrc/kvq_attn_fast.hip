@@ -80,7 +80,7 @@ struct FArgs {
   float sm_scale;
   float voff;                      // value code offset: 2 (signed absmax, c - 2) or 1.5 (symmetric grid, c - 1.5)
   int blocks_per_unit;             // blocks (and partials) per (query row, KV head)
-  int chunk_log2;                  // log2 of the 32-token steps per chunk (>= 4)
+  int chunk_log2;                  // log2 of the 32-token steps per chunk (>= 3)
   int* ctr;                        // per (query row, KV head) chunk counters, or null (static chunks)
   int* done;                       // per (query row, KV head) finished-block counters, or null (separate merge)
   float* out;                      // merged output and log-sum-exp, written when done is set
@@ -430,11 +430,12 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   return true;
 }
 
-// Chunk size: at least 16 steps (one step per wavefront of a block to start with), and
-// at most kMaxChunks chunks per (query row, KV head).
+// Chunk size: at least 8 steps, and at most kMaxChunks chunks per (query row, KV head).
+// The unit's blocks finish within about one chunk of each other (a 16-step chunk is ~4 us
+// of one block's share of the bandwidth at the 64K workload; 8 steps halve that).
 static int fast_chunk_log2(const kvq_shape& s) {
   const long long steps = (s.tokens + kStep - 1) / kStep;
-  int cl2 = 4;
+  int cl2 = 3;
   while (((steps + (1LL << cl2) - 1) >> cl2) > kMaxChunks) ++cl2;
   return cl2;
 }
