@@ -435,7 +435,9 @@ def anchors_workload(reps):
     same 4/2 codec on layers 4-7; the last 16 in 4/2 everywhere.  Times the append of
     one decoded token (K and V of every layer and head into the packed cache) and one
     decode step over the four segments, against the decode of the same cache held as
-    one packed tensor; reports the effective bits."""
+    one packed tensor; the append followed by the decode, as two launches and as one
+    (kvq_append_decode_attn); reports the effective bits.  Times are per call over 100
+    back-to-back calls."""
     import torch
     import kv_cache_bit_fwht_amd as K
     import synth
@@ -485,12 +487,23 @@ def anchors_workload(reps):
     def append():
         K.kvq_quantize_pack_tokens_kv(newk, newv, T - 1, 1, kfull, vfull)
 
-    for f in (seg_step, one_step, append):
+    def append_then_decode():
+        append()
+        one_step()
+
+    def append_decode():
+        K.kvq_append_decode_attn(newk, newv, T - 1, 1, kfull, vfull, Hq, 1, qd, None, 0.0, out, lse, ws1, wsb1)
+
+    for f in (seg_step, one_step, append, append_decode):
         f()
     torch.cuda.synchronize()
-    t_seg = _median_time(torch, seg_step, reps)
-    t_one = _median_time(torch, one_step, reps)
-    t_app = _median_time(torch, append, reps)
+    # per call, over 100 back-to-back calls (a decoding loop issues its steps that way);
+    # the median of the passes
+    t_seg = _median_time(torch, lambda: [seg_step() for _ in range(100)], reps) / 100
+    t_one = _median_time(torch, lambda: [one_step() for _ in range(100)], reps) / 100
+    t_app = _median_time(torch, lambda: [append() for _ in range(100)], reps) / 100
+    t_atd = _median_time(torch, lambda: [append_then_decode() for _ in range(100)], reps) / 100
+    t_ad = _median_time(torch, lambda: [append_decode() for _ in range(100)], reps) / 100
     eff = K.kvq_effective_bits(segs, L, H, T)
     d_bytes = sum(s.k.codes.numel() * 4 + (s.k.scales.numel() * 2 if s.k.scales is not None else 0) +
                   s.v.codes.numel() * 4 + (s.v.scales.numel() * 2 if s.v.scales is not None else 0) for s in segs)
@@ -501,7 +514,10 @@ def anchors_workload(reps):
                                     "GB/s": round(d_bytes / t_seg / 1e9, 1),
                                     "frac_hbm": round(d_bytes / t_seg / 1e9 / HBM_PEAK_GBS, 4), "bytes": d_bytes},
            "decode_step_one_tensor": {"us": round(t_one * 1e6, 1)},
-           "append_one_token_kv": {"us": round(t_app * 1e6, 1), "rows": 2 * B * L * H}}
+           "append_one_token_kv": {"us": round(t_app * 1e6, 1), "rows": 2 * B * L * H},
+           "append_then_decode_two_launches": {"us": round(t_atd * 1e6, 1)},
+           "append_decode_one_launch": {"us": round(t_ad * 1e6, 1),
+                                        "over_decode_alone": round(t_ad / t_one - 1.0, 4)}}
     print(json.dumps(rec), flush=True)
 
 

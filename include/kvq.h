@@ -269,6 +269,23 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
                               float sm_scale, float* out, float* lse, void* ws,
                               size_t ws_bytes, int32_t path, void* stream);
 
+/* One decode step of a growing cache ([FMAG-6] The winning recipe: each decode step
+ * writes its token's K and V into the quantised cache, then attends over it):
+ * kvq_quantize_pack_tokens_kv(k_new, v_new, token0, n_new, k, v) followed by
+ * kvq_decode_attn(k, v, ...), with the same results.  k_new, v_new: fp16
+ * [B][L][H][n_new][D].  When the MFMA decode applies (see kvq_decode_attn_ex) with
+ * 4-bit signed-absmax keys, signed-absmax values, rotation 0 or 256, no channel
+ * scales or mean, and n_new <= 8, one launch does both: the first block of each
+ * (query row, KV head) codes the new rows before it reads them, and the steps holding
+ * them are decoded by that block.  Otherwise an append launch precedes the decode.
+ * The workspace is kvq_decode_attn's (same size query).  Arguments are validated
+ * before anything is launched; errors as for the two calls. */
+kvq_status kvq_append_decode_attn(const uint16_t* k_new, const uint16_t* v_new, int32_t token0,
+                                  int32_t n_new, const kvq_packed* k, const kvq_packed* v,
+                                  int32_t q_heads, int32_t n_q, const uint16_t* q,
+                                  const int32_t* kv_len, float sm_scale, float* out, float* lse,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of the library's own device scratch used by kvq_decode_attn_static (one
  * copy on every GPU the library runs on, held until the process ends). */
 #define KVQ_STATIC_SCRATCH_BYTES (16u << 20)

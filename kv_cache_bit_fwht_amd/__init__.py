@@ -31,6 +31,7 @@ EXPORTS = [
     "kvq_decode_attn_segments_workspace", "kvq_decode_attn_segments", "kvq_decode_attn_segments_ex",
     "kvq_effective_bits",
     "kvq_attn_error_ex", "kvq_quantize_pack_kv", "kvq_quantize_pack_tokens_kv", "kvq_decode_attn_static",
+    "kvq_append_decode_attn",
 ]
 
 
@@ -105,6 +106,7 @@ def _load():
         "kvq_quantize_pack_kv": ([P, P, P, P, P], I32),
         "kvq_quantize_pack_tokens_kv": ([P, P, I32, I32, P, P, P], I32),
         "kvq_decode_attn_static": ([P, P, I32, I32, P, P, F, P, P, P], I32),
+        "kvq_append_decode_attn": ([P, P, I32, I32, P, P, I32, I32, P, P, F, P, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -340,6 +342,16 @@ def kvq_decode_attn(k: Packed, v: Packed, q_heads: int, n_q: int, q, kv_len, sm_
 def kvq_decode_attn_ex(k: Packed, v: Packed, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes,
                        path: int, stream=None):
     kvq_decode_attn(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, ws_bytes, stream, path)
+
+
+def kvq_append_decode_attn(k_new, v_new, token0: int, n_new: int, k: Packed, v: Packed, q_heads: int, n_q: int,
+                           q, kv_len, sm_scale: float, out, lse, ws, ws_bytes: int, stream=None):
+    """Append n_new tokens' K and V at token0, then decode (one launch where the codecs allow)."""
+    kc, vc = k.c(), v.c()
+    _check("kvq_append_decode_attn",
+           _lib.kvq_append_decode_attn(_ptr(k_new), _ptr(v_new), token0, n_new, ctypes.byref(kc), ctypes.byref(vc),
+                                       q_heads, n_q, _ptr(q), _ptr(kv_len), sm_scale, _ptr(out), _ptr(lse),
+                                       _ptr(ws), ws_bytes, _stream(stream)))
 
 
 STATIC_SCRATCH_BYTES = 16 << 20      # KVQ_STATIC_SCRATCH_BYTES of kvq.h

@@ -551,12 +551,18 @@ static SegPlan seg_plan(const kvq_segment* segs, int32_t n_seg, int32_t layers, 
 
 // One decode of a packed K/V pair: counters at ctr (kWsCounterBytes, zero and left zero),
 // split-K partials at part.
+// app_n > 0: the MFMA kernel also codes app_k / app_v into tokens [app_t0, app_t0 + app_n)
+// (the caller has checked fused_append_supported).
 static hipError_t decode_packed(const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
                                 const uint16_t* q, const int32_t* kv_len, float sm_scale, float* out, float* lse,
-                                void* ctr, void* part, size_t part_bytes, int32_t path, hipStream_t st) {
+                                void* ctr, void* part, size_t part_bytes, int32_t path, hipStream_t st,
+                                const uint16_t* app_k = nullptr, const uint16_t* app_v = nullptr, int app_t0 = 0,
+                                int app_n = 0) {
   const bool fast_ok = fast_decode_supported(*k, *v, q_heads);
   AttnProblem pr{};
   pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
+  pr.app_k = app_k; pr.app_v = app_v; pr.app_t0 = app_t0; pr.app_n = app_n;
+  if (app_n > 0) path = 2;
   pr.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / std::sqrt((double)k->shape.head_dim));
   pr.out = out; pr.lse = lse;
   pr.ctr = static_cast<int*>(ctr);
@@ -616,6 +622,41 @@ kvq_status kvq_decode_attn_static(const kvq_packed* k, const kvq_packed* v, int3
   if (st != KVQ_OK) return st;
   return kvq_decode_attn_ex(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, (size_t)KVQ_STATIC_SCRATCH_BYTES,
                             0, stream);
+}
+
+kvq_status kvq_append_decode_attn(const uint16_t* k_new, const uint16_t* v_new, int32_t token0, int32_t n_new,
+                                  const kvq_packed* k, const kvq_packed* v, int32_t q_heads, int32_t n_q,
+                                  const uint16_t* q, const int32_t* kv_len, float sm_scale, float* out, float* lse,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  // every check before anything is launched
+  kvq_status st = check_attn(k, v, q_heads, n_q, q);
+  if (st != KVQ_OK) return st;
+  if (!out || !k_new || !v_new) return KVQ_ERR_ARG;
+  if (!aligned16(out) || (lse && !aligned16(lse)) || (kv_len && !aligned16(kv_len)) || !aligned16(k_new) ||
+      !aligned16(v_new))
+    return KVQ_ERR_ALIGN;
+  if (!(sm_scale >= 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_ARG;
+  if (token0 < 0 || n_new < 1 || (long long)token0 + n_new > k->shape.tokens) return KVQ_ERR_ARG;
+  if (k->codes == v->codes || (k->scales && k->scales == v->scales)) return KVQ_ERR_ARG;
+  if (is_rfft(v->codec.codebook)) return KVQ_ERR_UNSUPPORTED;
+  const size_t need = kWsCounterBytes + decode_ws_bytes(k->shape, q_heads, n_q);
+  if (ws_bytes < need || (need && !ws)) return KVQ_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return KVQ_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  char* part = static_cast<char*>(ws) + kWsCounterBytes;
+  if (fused_append_supported(*k, *v, q_heads, n_new))
+    return hip_status(decode_packed(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, part,
+                                    ws_bytes - kWsCounterBytes, 2, s, k_new, v_new, token0, n_new));
+  hipError_t e;
+  if (is_rfft(k->codec.codebook)) {
+    e = launch_rfft_quantize_tokens(k_new, *k, token0, n_new, s);
+    if (e == hipSuccess) e = launch_quantize_tokens(v_new, *v, token0, n_new, s);
+  } else {
+    e = launch_quantize_kv(k_new, v_new, *k, *v, token0, n_new, s);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(decode_packed(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws, part,
+                                  ws_bytes - kWsCounterBytes, 0, s));
 }
 
 size_t kvq_decode_attn_segments_workspace(const kvq_segment* segs, int32_t n_seg, int32_t layers, int32_t heads,

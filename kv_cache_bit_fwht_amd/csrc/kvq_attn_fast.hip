@@ -44,6 +44,7 @@
 #include <cmath>
 
 #include "kvq_internal.hpp"
+#include "kvq_quant256.hpp"
 
 namespace kvq {
 
@@ -85,6 +86,16 @@ struct FArgs {
   int* done;                       // per (query row, KV head) finished-block counters, or null (separate merge)
   float* out;                      // merged output and log-sum-exp, written when done is set
   float* lse;
+  // fused append: fp16 rows [B][L][H][app_n][256] coded into tokens [app_t0, app_t0 + app_n)
+  // through the writable views below (app_n = 0: none)
+  const uint16_t* app_k;
+  const uint16_t* app_v;
+  int app_t0, app_n;
+  uint32_t* kcw;
+  uint16_t* ksw;
+  uint32_t* vcw;
+  uint16_t* vsw;
+  int app_kg, app_vg;              // key and value groups
 };
 
 __device__ __forceinline__ uint32_t h2bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
@@ -259,7 +270,7 @@ __device__ __forceinline__ int claim_global(int* ctr) {
 // wavefronts that share a SIMD do not run at the same speed (the older one is
 // issued first), so the block's 32-token steps are handed out dynamically from an
 // LDS counter instead of being split evenly in advance.
-template <int NKS, int NVS, int VB, int KB>
+template <int NKS, int NVS, int VB, int KB, bool APP = false>
 __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   constexpr int NW = kFastBlock / 64;                // wavefronts per block
   __shared__ __align__(16) float qs[4][kFastD + 16];
@@ -333,6 +344,7 @@ __device__ __forceinline__ void mfma_tile_unit(const FArgs& a, MfmaLds& S, int h
   auto& qbs = S.qbs;
   int& next_local = S.next_local;
   auto& slot_chunk = S.slot_chunk;
+  constexpr bool APP = false;
 #include "kvq_mfma_body.inc"
 }
 
@@ -460,6 +472,20 @@ size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q) {
 
 template <int VB, int KB>
 static void launch_mfma(const FArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (KB == 4) {
+    if (a.app_n > 0) {                               // the fused-append instances
+      if (a.nks == 2) {
+        if (a.nvs == 1) k_decode_mfma<2, 1, VB, 4, true><<<grid, kFastBlock, 0, st>>>(a);
+        else if (a.nvs == 2) k_decode_mfma<2, 2, VB, 4, true><<<grid, kFastBlock, 0, st>>>(a);
+        else k_decode_mfma<2, 4, VB, 4, true><<<grid, kFastBlock, 0, st>>>(a);
+      } else {
+        if (a.nvs == 1) k_decode_mfma<1, 1, VB, 4, true><<<grid, kFastBlock, 0, st>>>(a);
+        else if (a.nvs == 2) k_decode_mfma<1, 2, VB, 4, true><<<grid, kFastBlock, 0, st>>>(a);
+        else k_decode_mfma<1, 4, VB, 4, true><<<grid, kFastBlock, 0, st>>>(a);
+      }
+      return;
+    }
+  }
   if (a.nks == 2) {
     if (a.nvs == 1) k_decode_mfma<2, 1, VB, KB><<<grid, kFastBlock, 0, st>>>(a);
     else if (a.nvs == 2) k_decode_mfma<2, 2, VB, KB><<<grid, kFastBlock, 0, st>>>(a);
@@ -475,6 +501,15 @@ template <int KB>
 static void launch_mfma_k(const FArgs& a, int vb, dim3 grid, hipStream_t st) {
   if (vb == 2) launch_mfma<2, KB>(a, grid, st);
   else launch_mfma<4, KB>(a, grid, st);
+}
+
+bool fused_append_supported(const kvq_packed& k, const kvq_packed& v, int Hq, int n_new) {
+  if (!fast_decode_supported(k, v, Hq)) return false;
+  if (n_new < 1 || n_new > kFusedAppendRows) return false;
+  if (k.codec.codebook != KVQ_INT_ABSMAX || k.codec.bits != 4 || k.chan_scale || k.mean) return false;
+  if (v.codec.codebook != KVQ_INT_ABSMAX || v.chan_scale || v.mean) return false;
+  auto rot_ok = [](int w) { return w <= 1 || w == 256; };
+  return rot_ok(k.codec.rot_width) && rot_ok(v.codec.rot_width);
 }
 
 static float kappa_w(int W) {
@@ -611,6 +646,18 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_
   if (mean_done) *mean_done = fused && k.mean;
   a.out = pr.out;
   a.lse = pr.lse;
+  if (pr.app_n > 0) {
+    a.app_k = pr.app_k;
+    a.app_v = pr.app_v;
+    a.app_t0 = pr.app_t0;
+    a.app_n = pr.app_n;
+    a.kcw = k.codes;
+    a.ksw = k.scales;
+    a.vcw = v.codes;
+    a.vsw = v.scales;
+    a.app_kg = k.codec.group;
+    a.app_vg = v.codec.group;
+  }
   const long long units = (long long)s.batch * s.layers * s.heads;
   const dim3 grid(a.blocks_per_unit, (unsigned)units, (unsigned)pr.n_q);
   switch (k.codec.bits) {

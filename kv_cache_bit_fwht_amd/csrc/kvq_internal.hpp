@@ -189,6 +189,11 @@ struct AttnProblem {
   void* ws;          // partials (the workspace past its counter region)
   size_t ws_bytes;
   int* ctr;          // the workspace's counter region (kWsCounterBytes, zero between calls)
+  // fused append (MFMA decode only): fp16 K and V rows [B][L][H][app_n][D] coded into tokens
+  // [app_t0, app_t0 + app_n) of k and v by the decode launch itself; app_n = 0: none
+  const uint16_t* app_k;
+  const uint16_t* app_v;
+  int app_t0, app_n;
 };
 
 // The first bytes of every decode workspace hold two arrays of per-(query row,
@@ -228,6 +233,11 @@ hipError_t launch_seg_merge(int n, const int* l0, const int* ls, const int* j0, 
                             float* const* lsp, float* out, float* lse, int B, int L, int n_q, int Hq, int D,
                             hipStream_t st);
 bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
+// The MFMA decode can code appended rows itself: 4-bit signed-absmax keys at group 128
+// or 256 and 2- or 4-bit signed-absmax values (rotation 0 or 256, no channel scales or
+// mean), at most kFusedAppendRows rows per (sequence, layer, head).
+constexpr int kFusedAppendRows = 8;
+bool fused_append_supported(const kvq_packed& k, const kvq_packed& v, int Hq, int n_new);
 // mean_done (optional): set when the kernel's own merge applied the key mean's lse shift.
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_done = nullptr);
 size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q);

@@ -13,6 +13,7 @@
 // lane writes the fp16 scale.  The transform's strides >= 16 go through one
 // padded LDS tile per block (17 floats per 16 values).
 #include "kvq_codec.hpp"
+#include "kvq_quant256.hpp"
 
 namespace kvq {
 
@@ -367,7 +368,6 @@ static int grid_for(long long rows, int lpt_log2) {
 //  * the code is RN32(RN32(u * inv) + (1.5 * 2^23 + 2^(b-1))): in [2^23, 2^24) the ulp
 //    is 1, so that addition performs the round-to-nearest-even, and the integer sits
 //    in the low bits of the result (bits b..21 zero after clamping), ready to pack.
-constexpr int kRowLds = 256 + 16;                    // LDS floats per row (padding spreads banks)
 
 // Quads of rows q_first, q_first + q_stride, ... of one tensor; each wavefront of the
 // caller owns one quad per step (16 lanes per row).
@@ -567,177 +567,6 @@ __global__ __launch_bounds__(kBlock) void k_quantize_absmax256(QArgs a) {
                                  lds[tid >> 4], tid & 63);
 }
 
-// ---- one row quad per wavefront (no mean, no channel scales)
-// The same codes as absmax256_rows with fewer instructions and a launch shape that
-// streams better: every wavefront codes one quad of rows and exits, so the rows in
-// flight at any moment are a contiguous window of the tensor (measured 10-15% faster
-// than a grid-stride loop over a resident grid), and the fp16 input is read with
-// non-temporal loads (it is read once).  Arithmetic changes, all exact rewrites:
-//  * the first butterfly stage (strides 1: the two halves of one input word) is one
-//    v_fma_mix per output, a*1 + b and a*1 - b on the fp16 halves with a single
-//    rounding, which is RN32(a + b) of the converted values;
-//  * without a rotation the group extremes are taken on the fp16 values (packed
-//    fp16 max/min; conversion to fp32 is exact and monotone), and each code's
-//    product RN32(x * inv) is one v_fma_mix on the fp16 operand (x*inv + 0 rounds
-//    once; only the sign of a zero product can differ, and the bias added next
-//    removes it).
-typedef _Float16 kvq_h2 __attribute__((ext_vector_type(2)));
-typedef unsigned int kvq_u4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void load_row256_nt(const uint16_t* x, long long rows, long long row, int j, uint4& p0,
-                                               uint4& p1) {
-  if (row >= rows) row = rows - 1;                   // the tail quad re-reads the last row
-  const kvq_u4* src = reinterpret_cast<const kvq_u4*>(x + (size_t)row * 256 + 16 * j);
-  const kvq_u4 a0 = __builtin_nontemporal_load(src), a1 = __builtin_nontemporal_load(src + 1);
-  p0 = make_uint4(a0.x, a0.y, a0.z, a0.w);
-  p1 = make_uint4(a1.x, a1.y, a1.z, a1.w);
-}
-
-__device__ __forceinline__ float max16(const float v[16]) {
-  const float a = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
-  const float b = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
-  const float c = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
-  const float d = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
-  const float e = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
-  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a, b), c), __builtin_fmaxf(__builtin_fmaxf(d, e), v[15]));
-}
-
-__device__ __forceinline__ float min16(const float v[16]) {
-  const float a = __builtin_fminf(__builtin_fminf(v[0], v[1]), v[2]);
-  const float b = __builtin_fminf(__builtin_fminf(v[3], v[4]), v[5]);
-  const float c = __builtin_fminf(__builtin_fminf(v[6], v[7]), v[8]);
-  const float d = __builtin_fminf(__builtin_fminf(v[9], v[10]), v[11]);
-  const float e = __builtin_fminf(__builtin_fminf(v[12], v[13]), v[14]);
-  return __builtin_fminf(__builtin_fminf(__builtin_fminf(a, b), c), __builtin_fminf(__builtin_fminf(d, e), v[15]));
-}
-
-// Codes and scales of one row (16 lanes, lane j holding values 16j..16j+15 as the
-// raw fp16 words p0, p1) of a 256-wide signed-absmax tensor.  `row` is the input
-// row; rows at or past a.rows compute but store nothing.
-template <int BITS, bool ROT>
-__device__ __forceinline__ void code_row256(const QArgs& a, long long row, const uint4 p0, const uint4 p1, float* rl,
-                                            int j) {
-  constexpr int D = 256;
-  constexpr float kFold = ROT ? 0.0625f : 1.0f;      // the 256-point transform's 1/sqrt(256)
-  constexpr float neg_step = -kFold / (float)(1 << (BITS - 1));
-  constexpr uint32_t kMagic = 0x4B400000u;           // bit pattern of 1.5 * 2^23
-  constexpr float kBias = 12582912.0f + (float)(1 << (BITS - 1));
-  const int lpg = a.g >> 4;                          // lanes per group
-  const uint32_t raw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-  float v[16];
-  float mx, mn;
-  if constexpr (!ROT) {
-    kvq_h2 hx = __builtin_bit_cast(kvq_h2, raw[0]), hn = hx;
-#pragma unroll
-    for (int k = 1; k < 8; ++k) {
-      hx = __builtin_elementwise_max(hx, __builtin_bit_cast(kvq_h2, raw[k]));
-      hn = __builtin_elementwise_min(hn, __builtin_bit_cast(kvq_h2, raw[k]));
-    }
-    mx = __builtin_fmaxf((float)hx.x, (float)hx.y);
-    mn = __builtin_fminf((float)hn.x, (float)hn.y);
-  } else {
-    // stride 1 from the fp16 halves of each word, strides 2, 4, 8 in the lane
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(v[2 * k]) : "v"(raw[k]));
-      asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(v[2 * k + 1]) : "v"(raw[k]));
-    }
-#pragma unroll
-    for (int s = 2; s < 16; s <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (!(i & s)) {
-          const float x = v[i], y = v[i + s];
-          v[i] = x + y;
-          v[i + s] = x - y;
-        }
-    }
-    // transpose (lane j takes values j + 16 r), strides 16..128, transpose back; quads of
-    // a lane's values sit at quad index (q ^ (owner & 3)) of the owner's 16-float slot
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<float4*>(rl + 16 * j + 4 * (q ^ (j & 3))) =
-          make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = rl[16 * r + 4 * ((j >> 2) ^ (r & 3)) + (j & 3)];
-#pragma unroll
-    for (int rs = 1; rs < 16; rs <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (!(i & rs)) {
-          const float x = v[i], y = v[i + rs];
-          v[i] = x + y;
-          v[i + rs] = x - y;
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rl[16 * r + 4 * ((j >> 2) ^ (r & 3)) + (j & 3)] = v[r];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 t = *reinterpret_cast<const float4*>(rl + 16 * j + 4 * (q ^ (j & 3)));
-      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-    }
-    mx = max16(v);
-    mn = min16(v);
-  }
-  for (int m = 1; m < lpg; m <<= 1) {
-    mx = xor_max(mx, m);
-    mn = xor_min(mn, m);
-  }
-  const float ext = (-mn >= mx) ? mn : mx;
-  const uint16_t s16 = rn16(ext * neg_step);         // exact product: neg_step is a power of two
-  const float inv = inv_scale(s16) * kFold;          // exact: kFold is a power of two
-  uint32_t c[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float t;
-    if constexpr (!ROT) {
-      if (i & 1) asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(t) : "v"(raw[i >> 1]), "v"(inv));
-      else asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(t) : "v"(raw[i >> 1]), "v"(inv));
-    } else {
-      t = __fmul_rn(v[i], inv);
-    }
-    const float f = __fadd_rn(t, kBias);
-    const int b = (int)__builtin_bit_cast(uint32_t, f);
-    c[i] = (uint32_t)min(max(b, (int)kMagic), (int)(kMagic + (1u << BITS) - 1u));
-  }
-  if (row >= a.rows) return;
-  const long long orow = out_row(a, row);
-  uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + (size_t)orow * (D * BITS / 8) + (size_t)j * 2 * BITS;
-  if constexpr (BITS == 4) {
-    uint32_t w[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t t0 = (c[8 * k + 1] << 4) | c[8 * k + 0], t1 = (c[8 * k + 3] << 4) | c[8 * k + 2];
-      const uint32_t t2 = (c[8 * k + 5] << 4) | c[8 * k + 4], t3 = (c[8 * k + 7] << 4) | c[8 * k + 6];
-      const uint32_t h0 = __builtin_amdgcn_perm(t1, t0, 0x0C0C0400u);
-      const uint32_t h1 = __builtin_amdgcn_perm(t3, t2, 0x0C0C0400u);
-      w[k] = (h1 << 16) | h0;
-    }
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-  } else if constexpr (BITS == 2) {
-    uint32_t by[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = (c[4 * k + 1] << 2) | c[4 * k + 0], hi = (c[4 * k + 3] << 2) | c[4 * k + 2];
-      by[k] = (hi << 4) | lo;
-    }
-    const uint32_t h0 = __builtin_amdgcn_perm(by[1], by[0], 0x0C0C0400u);
-    const uint32_t h1 = __builtin_amdgcn_perm(by[3], by[2], 0x0C0C0400u);
-    *reinterpret_cast<uint32_t*>(dst) = (h1 << 16) | h0;
-  } else {
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t h0 = __builtin_amdgcn_perm(c[4 * k + 1], c[4 * k + 0], 0x0C0C0400u);
-      const uint32_t h1 = __builtin_amdgcn_perm(c[4 * k + 3], c[4 * k + 2], 0x0C0C0400u);
-      w[k] = (h1 << 16) | h0;
-    }
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  if ((j & (lpg - 1)) == 0) a.scales[(size_t)orow * (D / a.g) + j / lpg] = s16;
-}
-
 constexpr int kQuadWaves = 4;                        // wavefronts (row quads) per block
 
 template <int BITS, bool ROT>
@@ -748,7 +577,7 @@ __global__ __launch_bounds__(kQuadWaves * 64) void k_quantize_q256(QArgs a) {
   if (((long long)blockIdx.x * kQuadWaves + (tid >> 6)) * 4 >= a.rows) return;   // whole wavefront past the end
   uint4 p0, p1;
   load_row256_nt(a.x, a.rows, row, j, p0, p1);
-  code_row256<BITS, ROT>(a, row, p0, p1, lds[tid >> 4], j);
+  code_row256<BITS, ROT, false>(a.codes, a.scales, a.g, out_row(a, row), row < a.rows, p0, p1, lds[tid >> 4], j);
 }
 
 // K and V of one cache in one launch: each wavefront loads one quad of key rows and
@@ -765,8 +594,8 @@ __global__ __launch_bounds__(kQuadWaves * 64) void k_quantize_kv256(QArgs ak, QA
   uint4 k0, k1, v0, v1;
   load_row256_nt(ak.x, ak.rows, row, j, k0, k1);
   load_row256_nt(av.x, av.rows, row, j, v0, v1);
-  code_row256<KB, KROT>(ak, row, k0, k1, lds[tid >> 4], j);
-  code_row256<VB, VROT>(av, row, v0, v1, lds[tid >> 4], j);
+  code_row256<KB, KROT, false>(ak.codes, ak.scales, ak.g, out_row(ak, row), row < ak.rows, k0, k1, lds[tid >> 4], j);
+  code_row256<VB, VROT, false>(av.codes, av.scales, av.g, out_row(av, row), row < av.rows, v0, v1, lds[tid >> 4], j);
 }
 
 static unsigned quad_blocks(long long rows) {
