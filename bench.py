@@ -33,8 +33,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
 KERNEL_SRC = {"decode": ["kv_cache_bit_fwht_amd/csrc/kvq_attn_fast.hip", "kv_cache_bit_fwht_amd/csrc/kvq_mfma_body.inc",
-                         "kv_cache_bit_fwht_amd/csrc/kvq_attn.hip"],
-              "quantize": ["kv_cache_bit_fwht_amd/csrc/kvq_quant.hip", "kv_cache_bit_fwht_amd/csrc/kvq_codec.hpp"]}
+                         "kv_cache_bit_fwht_amd/csrc/kvq_attn.hip", "kv_cache_bit_fwht_amd/csrc/kvq_quant256.hpp"],
+              "quantize": ["kv_cache_bit_fwht_amd/csrc/kvq_quant.hip", "kv_cache_bit_fwht_amd/csrc/kvq_codec.hpp",
+                           "kv_cache_bit_fwht_amd/csrc/kvq_quant256.hpp"]}
 
 
 def log(msg):
