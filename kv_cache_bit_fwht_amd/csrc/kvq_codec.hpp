@@ -59,7 +59,7 @@ __device__ __forceinline__ void fwht_rows(float v[16], float* rowlds, int j, int
 
 // ------------------------------------------------------------------ group statistics
 // Two groups per lane when g == 8 (halves of the 16 values), else one group
-// spread over g/16 lanes (xor-shuffle reductions inside the row's lanes).
+// spread over g/16 lanes (DPP reductions inside the row's lanes).
 
 __device__ __forceinline__ void stat_maxmin(const float v[16], int g, float mx[2], float mn[2]) {
   float a0 = v[0], b0 = v[0], a1 = v[8], b1 = v[8];
@@ -73,7 +73,7 @@ __device__ __forceinline__ void stat_maxmin(const float v[16], int g, float mx[2
     return;
   }
   float a = __builtin_fmaxf(a0, a1), b = __builtin_fminf(b0, b1);
-  for (int m = 1; m < g / 16; m <<= 1) { a = xor_max(a, m); b = xor_min(b, m); }
+  run_maxmin(a, b, g / 16);
   mx[0] = mx[1] = a;
   mn[0] = mn[1] = b;
 }
@@ -87,7 +87,7 @@ __device__ __forceinline__ void stat_absmax(const float v[16], int g, float am[2
   }
   if (g == 8) { am[0] = a0; am[1] = a1; return; }
   float a = __builtin_fmaxf(a0, a1);
-  for (int m = 1; m < g / 16; m <<= 1) a = xor_max(a, m);
+  a = run_max(a, g / 16);
   am[0] = am[1] = a;
 }
 

@@ -60,11 +60,48 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 // accurate to about one ulp; the builtin adds the exact residual checks.)
 __device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }
 
-// Correctly rounded reciprocal of a stored scale; zero scale -> zero.
+// Correctly rounded reciprocal of a stored scale; zero scale -> zero.  The hardware
+// reciprocal is within one ulp; one Newton step with fused multiply-adds,
+// y + y(1 - s y), then gives the correctly rounded binary32 1/s for every s with at
+// most 11 significant bits (every fp16 value), from any start within two ulps: checked
+// with exact rational arithmetic over all 1024 such significands (1/s stays a normal
+// binary32 for every fp16 s, so the exponent plays no part).
 __device__ __forceinline__ float inv_scale(uint16_t sb) {
-  float s = h2f(sb);
-  return s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+  const float s = h2f(sb);
+  const float y = __builtin_amdgcn_rcpf(s);
+  const float r = __builtin_fmaf(y, __builtin_fmaf(-s, y, 1.0f), y);
+  return s == 0.0f ? 0.0f : r;
 }
+
+// Maximum and minimum over aligned runs of `lpg` lanes (lpg a power of two, at most 16):
+// pairs, pairs of pairs, then the two quads of each 8 lanes and the two halves of each
+// 16 lanes exchange values through DPP lane permutations, one v_max/v_min per step
+// (the compiler's own fmaxf would quiet the permuted operand first, two instructions
+// more).  Each step reads only lanes of the same run, so a run whose lanes are all
+// inactive disturbs no other.  The s_nop covers the wait states a DPP read needs after
+// a VALU write of its operand or of EXEC.
+#define KVQ_DPP_MAXMIN(CTRL)                                                     \
+  asm("s_nop 4\n\tv_max_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+      "v_min_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf"             \
+      : "+v"(mx), "+v"(mn))
+#define KVQ_DPP_MAX(CTRL) \
+  asm("s_nop 4\n\tv_max_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf" : "+v"(a))
+
+__device__ __forceinline__ void run_maxmin(float& mx, float& mn, int lpg) {
+  if (lpg >= 2) KVQ_DPP_MAXMIN("quad_perm:[1,0,3,2]");
+  if (lpg >= 4) KVQ_DPP_MAXMIN("quad_perm:[2,3,0,1]");
+  if (lpg >= 8) KVQ_DPP_MAXMIN("row_half_mirror");
+  if (lpg >= 16) KVQ_DPP_MAXMIN("row_mirror");
+}
+__device__ __forceinline__ float run_max(float a, int lpg) {
+  if (lpg >= 2) KVQ_DPP_MAX("quad_perm:[1,0,3,2]");
+  if (lpg >= 4) KVQ_DPP_MAX("quad_perm:[2,3,0,1]");
+  if (lpg >= 8) KVQ_DPP_MAX("row_half_mirror");
+  if (lpg >= 16) KVQ_DPP_MAX("row_mirror");
+  return a;
+}
+#undef KVQ_DPP_MAXMIN
+#undef KVQ_DPP_MAX
 
 __device__ __forceinline__ float xor_max(float v, int m) { return __builtin_fmaxf(v, __shfl_xor(v, m)); }
 __device__ __forceinline__ float xor_min(float v, int m) { return __builtin_fminf(v, __shfl_xor(v, m)); }

@@ -139,10 +139,10 @@ __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
       if constexpr (CB == KVQ_INT_MINMAX)
         *reinterpret_cast<uint32_t*>(a.mins + sbase + 2 * j) = (uint32_t)z16[0] | ((uint32_t)z16[1] << 16);
     } else {
-      const int lpg = a.g >> 4;        // lanes per group
-      if ((j & (lpg - 1)) == 0) {
-        a.scales[sbase + j / lpg] = s16[0];
-        if constexpr (CB == KVQ_INT_MINMAX) a.mins[sbase + j / lpg] = z16[0];
+      const int lg = __builtin_ctz(a.g);   // groups are powers of two
+      if ((j & ((a.g >> 4) - 1)) == 0) {
+        a.scales[sbase + (j >> (lg - 4))] = s16[0];
+        if constexpr (CB == KVQ_INT_MINMAX) a.mins[sbase + (j >> (lg - 4))] = z16[0];
       }
     }
   }
@@ -506,10 +506,7 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
       mx = __builtin_fmaxf(mx, v[i]);
       mn = __builtin_fminf(mn, v[i]);
     }
-    for (int m = 1; m < lpg; m <<= 1) {
-      mx = xor_max(mx, m);
-      mn = xor_min(mn, m);
-    }
+    run_maxmin(mx, mn, lpg);
     const float ext = (-mn >= mx) ? mn : mx;
     const uint16_t s16 = rn16(ext * neg_step);       // exact product: neg_step is a power of two
     const float inv = inv_scale(s16) * kFold;        // exact: kFold is a power of two
@@ -554,7 +551,8 @@ __device__ __forceinline__ void absmax256_rows(const QArgs& a, long long q_first
       }
       *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    if ((j & (lpg - 1)) == 0) a.scales[(size_t)orow * (D / a.g) + j / lpg] = s16;
+    const int lg = __builtin_ctz(a.g);               // groups are powers of two
+    if ((j & (lpg - 1)) == 0) a.scales[(size_t)orow * (D >> lg) + (j >> (lg - 4))] = s16;
   }
 }
 
@@ -580,22 +578,28 @@ __global__ __launch_bounds__(kQuadWaves * 64) void k_quantize_q256(QArgs a) {
   code_row256<BITS, ROT, false>(a.codes, a.scales, a.g, out_row(a, row), row < a.rows, p0, p1, lds[tid >> 4], j);
 }
 
-// K and V of one cache in one launch: each wavefront loads one quad of key rows and
-// the same quad of value rows, then codes both.  The two tensors' kernels would
-// each stream at the same rate; one launch keeps both streams in flight together
-// and pays one launch and one tail.
+// K and V of one cache in one launch: wavefront 2q codes quad q of the key rows and
+// wavefront 2q + 1 the same quad of the value rows.  One launch keeps both streams in
+// flight together and pays one launch and one tail.  Alternating the tensors by
+// wavefront measured 6% faster than one wavefront coding both quads (and 2% faster
+// than one launch per tensor): a wavefront has half the bytes to wait for, and the
+// rotated keys' arithmetic overlaps the values' loads on the same SIMD.
 template <int KB, bool KROT, int VB, bool VROT>
 __global__ __launch_bounds__(kQuadWaves * 64) void k_quantize_kv256(QArgs ak, QArgs av) {
   __shared__ float lds[kQuadWaves * 4][kRowLds];
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15;
-  const long long q0 = ((long long)blockIdx.x * kQuadWaves + (tid >> 6)) * 4;
+  const long long w = (long long)blockIdx.x * kQuadWaves + (tid >> 6);
+  const long long q0 = (w >> 1) * 4;
   if (q0 >= ak.rows) return;
   const long long row = q0 + (lane >> 4);
-  uint4 k0, k1, v0, v1;
-  load_row256_nt(ak.x, ak.rows, row, j, k0, k1);
-  load_row256_nt(av.x, av.rows, row, j, v0, v1);
-  code_row256<KB, KROT, false>(ak.codes, ak.scales, ak.g, out_row(ak, row), row < ak.rows, k0, k1, lds[tid >> 4], j);
-  code_row256<VB, VROT, false>(av.codes, av.scales, av.g, out_row(av, row), row < av.rows, v0, v1, lds[tid >> 4], j);
+  uint4 p0, p1;
+  if (w & 1) {
+    load_row256_nt(av.x, av.rows, row, j, p0, p1);
+    code_row256<VB, VROT, false>(av.codes, av.scales, av.g, out_row(av, row), row < av.rows, p0, p1, lds[tid >> 4], j);
+  } else {
+    load_row256_nt(ak.x, ak.rows, row, j, p0, p1);
+    code_row256<KB, KROT, false>(ak.codes, ak.scales, ak.g, out_row(ak, row), row < ak.rows, p0, p1, lds[tid >> 4], j);
+  }
 }
 
 static unsigned quad_blocks(long long rows) {
@@ -713,7 +717,8 @@ hipError_t launch_quantize_kv(const uint16_t* kx, const uint16_t* vx, const kvq_
   ak.t0 = av.t0 = t0;
   ak.rows = av.rows = (long long)kp.shape.batch * kp.shape.layers * kp.shape.heads * n;
   if (ak.rows == 0) return hipSuccess;
-  const dim3 grid(quad_blocks(ak.rows));
+  const long long waves = 2 * ((ak.rows + 3) / 4);  // two wavefronts (K, V) per row quad
+  const dim3 grid((unsigned)((waves + kQuadWaves - 1) / kQuadWaves));
   const bool krot = kp.codec.rot_width == 256, vrot = vp.codec.rot_width == 256;
   const int vb = vp.codec.bits;
   switch (kp.codec.bits) {

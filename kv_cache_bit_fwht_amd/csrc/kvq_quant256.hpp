@@ -126,10 +126,7 @@ __device__ __forceinline__ void code_row256(uint32_t* codes, uint16_t* scales, i
     mx = max16(v);
     mn = min16(v);
   }
-  for (int m = 1; m < lpg; m <<= 1) {
-    mx = xor_max(mx, m);
-    mn = xor_min(mn, m);
-  }
+  run_maxmin(mx, mn, lpg);
   const float ext = (-mn >= mx) ? mn : mx;
   const uint16_t s16 = rn16(ext * neg_step);         // exact product: neg_step is a power of two
   const float inv = inv_scale(s16) * kFold;          // exact: kFold is a power of two
@@ -178,7 +175,8 @@ __device__ __forceinline__ void code_row256(uint32_t* codes, uint16_t* scales, i
   }
   constexpr int nw = BITS / 2;                       // code words of the lane's 16 values
   uint32_t* dst = codes + (size_t)orow * (D * BITS / 32) + (size_t)j * nw;
-  uint16_t* sdst = scales + (size_t)orow * (D / g) + j / lpg;
+  const int lg = __builtin_ctz(g);                   // g is a power of two (it divides 256)
+  uint16_t* sdst = scales + (size_t)orow * (D >> lg) + (j >> (lg - 4));
   const bool first = (j & (lpg - 1)) == 0;
   if constexpr (COH) {
 #pragma unroll
