@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 
-SOURCES = ["kvq_api.hip", "kvq_quant.hip", "kvq_attn.hip", "kvq_attn_fast.hip", "kvq_rfft.hip"]
+SOURCES = ["kvq_api.hip", "kvq_quant.hip", "kvq_attn.hip", "kvq_attn_fast.hip", "kvq_attn_m128.hip", "kvq_rfft.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -559,6 +559,7 @@ static hipError_t decode_packed(const kvq_packed* k, const kvq_packed* v, int32_
                                 const uint16_t* app_k = nullptr, const uint16_t* app_v = nullptr, int app_t0 = 0,
                                 int app_n = 0) {
   const bool fast_ok = fast_decode_supported(*k, *v, q_heads);
+  const bool m128_ok = app_n == 0 && m128_decode_supported(*k, *v, q_heads);
   AttnProblem pr{};
   pr.k = k; pr.v = v; pr.Hq = q_heads; pr.n_q = n_q; pr.q = q; pr.kv_len = kv_len;
   pr.app_k = app_k; pr.app_v = app_v; pr.app_t0 = app_t0; pr.app_n = app_n;
@@ -568,9 +569,11 @@ static hipError_t decode_packed(const kvq_packed* k, const kvq_packed* v, int32_
   pr.ctr = static_cast<int*>(ctr);
   pr.ws = part;
   pr.ws_bytes = part_bytes;
-  const bool use_fast = (path == 2) || (path == 0 && fast_ok);
+  const bool use_fast = (path == 2) || (path == 0 && (fast_ok || m128_ok));
   bool mean_done = false;
-  hipError_t e = use_fast ? launch_decode_fast(pr, st, &mean_done) : launch_decode_generic(pr, st);
+  hipError_t e = !use_fast ? launch_decode_generic(pr, st)
+                 : (m128_ok && !fast_ok) ? launch_decode_m128(pr, st)
+                                         : launch_decode_fast(pr, st, &mean_done);
   // a key mean adds q.mean to every logit of a query: weights unchanged, lse shifted (by
   // the MFMA kernel's own merge when it merges, else here)
   if (e == hipSuccess && k->mean && lse && !mean_done) e = launch_lse_mean(pr, st);
@@ -594,7 +597,8 @@ kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t 
   const size_t need = kWsCounterBytes + decode_ws_bytes(k->shape, q_heads, n_q);
   if (ws_bytes < need || (need && !ws)) return KVQ_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return KVQ_ERR_ALIGN;
-  if (path == 2 && !fast_decode_supported(*k, *v, q_heads)) return KVQ_ERR_UNSUPPORTED;
+  if (path == 2 && !fast_decode_supported(*k, *v, q_heads) && !m128_decode_supported(*k, *v, q_heads))
+    return KVQ_ERR_UNSUPPORTED;
   // no keys (tokens = 0): zero output, lse = -inf (the generic kernel's combine)
   return hip_status(decode_packed(k, v, q_heads, n_q, q, kv_len, sm_scale, out, lse, ws,
                                   static_cast<char*>(ws) + kWsCounterBytes, ws_bytes - kWsCounterBytes, path,

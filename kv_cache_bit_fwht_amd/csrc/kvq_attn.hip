@@ -1424,6 +1424,8 @@ static int decode_wave_splits(const kvq_shape& s, int Hq, int n_q) {
   return (int)std::max(4LL, std::min(S, 512LL));
 }
 
+int decode_wave_split_count(const kvq_shape& s, int Hq, int n_q) { return decode_wave_splits(s, Hq, n_q); }
+
 // Workspace of kvq_decode_attn: split partials of whichever kernel runs.
 size_t decode_ws_bytes(const kvq_shape& s, int Hq, int n_q) {
   const int S = std::max(decode_splits(s, Hq, n_q), decode_wave_splits(s, Hq, n_q));

@@ -1,0 +1,545 @@
+// MFMA decode attention at head_dim 128 over the extreme low-bit caches of [FMAG-6]
+// ("Milestone" and "Best results": ternary {-s, 0, +s} and sign {-s, +s} codes at
+// group 8, the int8 per-token row as reference, and the fp16 anchor layer), up to 4
+// query heads per KV head.  The general kernel decodes these codecs on the VALU at
+// about nine lane-operations per cached value; here both contractions run on the
+// matrix cores and the VALU only turns codes into MFMA operands.
+//
+// One wavefront per (query row, KV head, token split), 32 tokens per step:
+//  * Q.K^T on v_mfma_f32_16x16x32_f16, two 16-token tiles per step.  A = the keys
+//    of 16 tokens x 32 dims as fp16: ternary and sign levels times their fp16 scale
+//    are exact fp16 values (+-s or 0), so the keys are formed exactly; int8 codes
+//    are fp16 subnormals (code c -> c * 2^-24, exact) and the row's single scale and
+//    its offset 127 are applied to the logit (offset folded as 127 * sum q); fp16
+//    keys are used as they are.  B = the fp16 query, 4 heads in columns n % 4 (the
+//    query is fp16 already, so one part is exact).
+//  * online softmax per head in log2 units, against a reference maximum that moves
+//    only when a logit exceeds it by more than 1, so weights stay at most 2.
+//  * P.V on v_mfma_f32_16x16x16_f16: A = fp16(p) for 4 heads (rows 0-3) x 16
+//    tokens, B = 16 tokens x 16 value dims as fp16 (ternary and sign exact, fp16 as
+//    stored); int8 values enter as subnormal codes with A = fp16(p) * s_v and the
+//    offset folded as 127 * sum of A, as for keys.
+// Each wavefront writes one (o, m, l) partial per query head (m in natural-log
+// units); the general combine kernel merges a row's splits in order.
+//
+// Lane layouts (l = lane, i = l % 16, kq = l / 16):
+//  * Q.K^T tile u: A row i is token 8(i / 4) + 4u + i % 4 of the step, so the
+//    output rows 4kq + r of lane l are tokens 8kq + 4u + r: a lane's 8 logits are
+//    the 8 consecutive tokens 8kq .. 8kq + 7.  A's 8 k-values of lane l are dims of
+//    its k-block kq (dims 32kq .. 32kq + 31 over the four 32-wide chunks, ordered
+//    per codec so that unpacking is cheap; the query B operand uses the same order).
+//  * P.V: MFMA u takes tokens 8kq + 4u + r in k-slots 4kq + r, so lane l supplies
+//    A = its own weights of tokens 8kq + 4u + r and B = the values of those tokens
+//    for value dim 8i + c (chunk c = 0..7): each lane reads 8 consecutive dims of
+//    its 8 tokens, one scale group of the group-8 codecs.
+#include <algorithm>
+#include <cmath>
+
+#include "kvq_internal.hpp"
+
+namespace kvq {
+
+namespace {
+
+typedef _Float16 mh8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mh4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mh2 __attribute__((ext_vector_type(2)));
+typedef float mf4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mu4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mu2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMD = 128;              // head_dim
+constexpr int kMStep = 32;            // tokens per wavefront step
+constexpr int kMWaves = 4;            // independent wavefronts per block
+constexpr int kMPart = kMD + 2;       // floats per partial: o[128], m, l
+
+enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3 };
+
+struct M128Args {
+  const uint8_t* kc;
+  const uint16_t* ks;
+  const uint8_t* vc;
+  const uint16_t* vs;
+  const uint16_t* q;                  // [rows][Hq][128] fp16
+  const int32_t* kv_len;              // [rows] or null
+  float* part;                        // [rows * Hq][S][130]
+  int H, T, Hq, G, n_q, S, cs;        // cs: steps per split
+  long long items;                    // rows * H * S
+  float lsc;                          // softmax scale * log2(e)
+};
+
+template <int C> struct Row {          // bytes of one row's codes, scales per row
+  static constexpr int code = C == MC_TER ? 32 : C == MC_SIGN ? 16 : C == MC_INT8 ? 128 : 256;
+  static constexpr int scales = C == MC_TER || C == MC_SIGN ? 16 : C == MC_INT8 ? 1 : 0;
+};
+
+// ---- key data of one 16-token tile for lane (i, kq): token tok(i, u), dims 32kq .. 32kq + 31
+template <int C> struct KTile;
+template <> struct KTile<MC_TER> { mu2 c; mu2 s; };              // 64 code bits, groups 4kq .. 4kq + 3
+template <> struct KTile<MC_SIGN> { uint32_t c; mu2 s; };        // 32 code bits, the same groups
+template <> struct KTile<MC_INT8> { mu4 c0, c1; uint32_t s[4]; };  // 32 code bytes; s: output tokens' scales
+template <> struct KTile<MC_F16> { mu4 c[4]; };                  // 32 fp16 values
+
+// ---- value data for lane (i, kq): dims 8i .. 8i + 7 of tokens 8kq .. 8kq + 7.  Ternary
+// and sign: one register per token pair for the codes (token 2j in the low half, 2j + 1
+// in the high half) and one for the two scales, each filled by two 16-bit loads.
+template <int C> struct VData;
+template <> struct VData<MC_TER> { mh2 c[4], s[4]; };
+template <> struct VData<MC_SIGN> { mh2 c[4], s[4]; };
+template <> struct VData<MC_INT8> { mu2 c[8]; mh2 s[4]; };      // 8 code bytes per token; the rows' scales
+template <> struct VData<MC_F16> { mu4 c[8]; };                  // 8 fp16 values per token
+
+template <int KC, int VC> struct MStep {
+  KTile<KC> k[2];
+  VData<VC> v;
+};
+
+__device__ __forceinline__ int tile_row(int i, int u) { return 8 * (i >> 2) + 4 * u + (i & 3); }
+
+// Per-lane byte offsets of a step's loads relative to the step's first row in each array
+// (a step's base address is wavefront-uniform: scalar base + 32-bit lane offset).
+struct MOffsets {
+  uint32_t k[2];      // key codes of tile u
+  uint32_t ks[2];     // key scales of tile u (ternary, sign); int8: first output token's scale
+  uint32_t v;         // value codes of token 8kq, dims 8i ..
+  uint32_t vs;        // value scale of token 8kq (group i, or the row's)
+};
+
+template <int KC, int VC>
+__device__ __forceinline__ MOffsets m_offsets(int i, int kq) {
+  MOffsets o;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t r = (uint32_t)tile_row(i, u);
+    if constexpr (KC == MC_TER) { o.k[u] = r * 32 + 8 * kq; o.ks[u] = (r * 16 + 4 * kq) * 2; }
+    else if constexpr (KC == MC_SIGN) { o.k[u] = r * 16 + 4 * kq; o.ks[u] = (r * 16 + 4 * kq) * 2; }
+    else if constexpr (KC == MC_INT8) { o.k[u] = r * 128 + 32 * kq; o.ks[u] = (8 * kq + 4 * u) * 2; }
+    else { o.k[u] = r * 256 + 64 * kq; o.ks[u] = 0; }
+  }
+  const uint32_t t = 8 * kq;
+  if constexpr (VC == MC_TER) { o.v = t * 32 + 2 * i; o.vs = (t * 16 + i) * 2; }
+  else if constexpr (VC == MC_SIGN) { o.v = t * 16 + i; o.vs = (t * 16 + i) * 2; }
+  else if constexpr (VC == MC_INT8) { o.v = t * 128 + 8 * i; o.vs = t * 2; }
+  else { o.v = t * 256 + 16 * i; o.vs = 0; }
+  return o;
+}
+
+template <typename T>
+__device__ __forceinline__ T ld(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
+// Loads of the step whose first row (unit row base + first token) is rb.  The offsets
+// pass through an empty asm so the compiler keeps scalar bases plus 32-bit offsets
+// instead of folding them into 64-bit per-lane pointers.
+template <int KC, int VC>
+__device__ __forceinline__ void m_load(const M128Args& a, size_t rb, MOffsets o, MStep<KC, VC>& d) {
+  asm volatile("" : "+v"(o.k[0]), "+v"(o.k[1]), "+v"(o.ks[0]), "+v"(o.ks[1]), "+v"(o.v), "+v"(o.vs));
+  const uint8_t* kb = a.kc + rb * Row<KC>::code;
+  const uint8_t* ksb = reinterpret_cast<const uint8_t*>(a.ks) + rb * 2 * Row<KC>::scales;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if constexpr (KC == MC_TER) {
+      d.k[u].c = ld<mu2>(kb, o.k[u]);
+      d.k[u].s = ld<mu2>(ksb, o.ks[u]);
+    } else if constexpr (KC == MC_SIGN) {
+      d.k[u].c = ld<uint32_t>(kb, o.k[u]);
+      d.k[u].s = ld<mu2>(ksb, o.ks[u]);
+    } else if constexpr (KC == MC_INT8) {
+      d.k[u].c0 = ld<mu4>(kb, o.k[u]);
+      d.k[u].c1 = ld<mu4>(kb, o.k[u] + 16);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) d.k[u].s[rr] = ld<uint16_t>(ksb, o.ks[u] + 2 * rr);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) d.k[u].c[c] = ld<mu4>(kb, o.k[u] + 16 * c);
+    }
+  }
+  const uint8_t* vb = a.vc + rb * Row<VC>::code;
+  const uint8_t* vsb = reinterpret_cast<const uint8_t*>(a.vs) + rb * 2 * Row<VC>::scales;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (VC == MC_TER || VC == MC_SIGN) {
+      constexpr uint32_t R = Row<VC>::code;
+      if constexpr (VC == MC_TER) {
+        d.v.c[j][0] = ld<_Float16>(vb, o.v + R * (2 * j));
+        d.v.c[j][1] = ld<_Float16>(vb, o.v + R * (2 * j + 1));
+      } else {                                       // a code byte, zero-extended into each half
+        d.v.c[j] = __builtin_bit_cast(mh2, (uint32_t)ld<uint8_t>(vb, o.v + R * (2 * j)) |
+                                               ((uint32_t)ld<uint8_t>(vb, o.v + R * (2 * j + 1)) << 16));
+      }
+      d.v.s[j][0] = ld<_Float16>(vsb, o.vs + 32 * (2 * j));
+      d.v.s[j][1] = ld<_Float16>(vsb, o.vs + 32 * (2 * j + 1));
+    } else if constexpr (VC == MC_INT8) {
+      d.v.c[2 * j] = ld<mu2>(vb, o.v + 128 * (2 * j));
+      d.v.c[2 * j + 1] = ld<mu2>(vb, o.v + 128 * (2 * j + 1));
+      d.v.s[j][0] = ld<_Float16>(vsb, o.vs + 2 * (2 * j));
+      d.v.s[j][1] = ld<_Float16>(vsb, o.vs + 2 * (2 * j + 1));
+    } else {
+      d.v.c[2 * j] = ld<mu4>(vb, o.v + 256 * (2 * j));
+      d.v.c[2 * j + 1] = ld<mu4>(vb, o.v + 256 * (2 * j + 1));
+    }
+  }
+}
+
+// (x & mask) | 0x64006400 as one v_and_or: the or-value is hidden from the compiler so
+// that it stays in a register (a literal would split the pair into two instructions)
+__device__ __forceinline__ uint32_t or6400(uint32_t x, uint32_t mask) {
+  uint32_t m = 0x64006400u;
+  asm("" : "+v"(m));
+  return (x & mask) | m;
+}
+
+__device__ __forceinline__ uint32_t pk_unit_scale(uint32_t x, uint32_t s2) {
+  // x: two ternary codes in the low bits of each half, or-ed with 0x6400 (the fp16
+  // 1024 + c); (1024 + c) - 1025 = c - 1 exactly, times the scale pair: +-s or 0, exact
+  const mh2 u = __builtin_bit_cast(mh2, x) - mh2{(_Float16)1025.0f, (_Float16)1025.0f};
+  return __builtin_bit_cast(uint32_t, u * __builtin_bit_cast(mh2, s2));
+}
+
+// A operand of key chunk c (0..3) of a tile.  Ternary and sign: dword m of chunk c
+// holds dims (p, p + 16) of the lane's 32, p = 4c + m; int8 and fp16: dims 8c .. 8c + 7
+// in order.
+template <int KC>
+__device__ __forceinline__ mh8 key_operand(const KTile<KC>& t, int c) {
+  mu4 r;
+  if constexpr (KC == MC_TER) {
+    // codes of dims p and p + 16 at bits 2p' and 16 + 2p' of z (p' = p mod 8)
+    const uint32_t z = (c < 2) ? __builtin_amdgcn_perm(t.c.y, t.c.x, 0x05040100u)
+                               : __builtin_amdgcn_perm(t.c.y, t.c.x, 0x07060302u);
+    // scales of dims (p, p + 16): groups (p / 8, 2 + p / 8) of the lane's four
+    const uint32_t s2 = (c < 2) ? __builtin_amdgcn_perm(t.s.y, t.s.x, 0x05040100u)
+                                : __builtin_amdgcn_perm(t.s.y, t.s.x, 0x07060302u);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int sh = 2 * (4 * (c & 1) + m);
+      r[m] = pk_unit_scale(or6400(z >> sh, 0x00030003u), s2);
+    }
+  } else if constexpr (KC == MC_SIGN) {
+    const uint32_t s2 = (c < 2) ? __builtin_amdgcn_perm(t.s.y, t.s.x, 0x05040100u)
+                                : __builtin_amdgcn_perm(t.s.y, t.s.x, 0x07060302u);
+    const uint32_t neg = s2 ^ 0x80008000u;            // (-s_a, -s_b); code 1 flips the sign
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int p = 4 * c + m;                       // bits p and p + 16 -> 15 and 31
+      r[m] = ((t.c << (15 - p)) & 0x80008000u) ^ neg;
+    }
+  } else if constexpr (KC == MC_INT8) {
+    const uint32_t w0 = (c == 0) ? t.c0.x : (c == 1) ? t.c0.z : (c == 2) ? t.c1.x : t.c1.z;
+    const uint32_t w1 = (c == 0) ? t.c0.y : (c == 1) ? t.c0.w : (c == 2) ? t.c1.y : t.c1.w;
+    r[0] = __builtin_amdgcn_perm(0u, w0, 0x0C010C00u);   // bytes -> fp16 subnormals c * 2^-24
+    r[1] = __builtin_amdgcn_perm(0u, w0, 0x0C030C02u);
+    r[2] = __builtin_amdgcn_perm(0u, w1, 0x0C010C00u);
+    r[3] = __builtin_amdgcn_perm(0u, w1, 0x0C030C02u);
+  } else {
+    r = t.c[c];
+  }
+  return __builtin_bit_cast(mh8, r);
+}
+
+// B operand of value chunk c (dim 8i + c) for tokens 4u .. 4u + 3 of the lane's 8.
+// keep01 / keep23: all-ones halves for the tokens that count (partial steps).
+template <int VC>
+__device__ __forceinline__ mh4 value_operand(const VData<VC>& v, int u, int c, uint32_t keep01, uint32_t keep23) {
+  mu2 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int pj = 2 * u + h;                        // token pair (4u + 2h, 4u + 2h + 1)
+    uint32_t x;
+    if constexpr (VC == MC_TER) {
+      const uint32_t y = __builtin_bit_cast(uint32_t, v.c[pj]);
+      x = pk_unit_scale(or6400(y >> (2 * c), 0x00030003u), __builtin_bit_cast(uint32_t, v.s[pj]));
+    } else if constexpr (VC == MC_SIGN) {
+      const uint32_t y = __builtin_bit_cast(uint32_t, v.c[pj]);
+      x = ((y << (15 - c)) & 0x80008000u) ^ (__builtin_bit_cast(uint32_t, v.s[pj]) ^ 0x80008000u);
+    } else if constexpr (VC == MC_INT8) {
+      const uint32_t sel = (uint32_t)(c & 3) | (0x0Cu << 8) | ((uint32_t)(4 + (c & 3)) << 16) | (0x0Cu << 24);
+      x = __builtin_amdgcn_perm(v.c[2 * pj + 1][c >> 2], v.c[2 * pj][c >> 2], sel);
+    } else {
+      x = __builtin_amdgcn_perm(v.c[2 * pj + 1][c >> 1], v.c[2 * pj][c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
+    }
+    if constexpr (VC != MC_INT8) x &= (h == 0) ? keep01 : keep23;
+    r[h] = x;
+  }
+  return __builtin_bit_cast(mh4, r);
+}
+
+template <int KC, int VC>
+__global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 : 2) void k_decode_m128(M128Args a) {
+  const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
+  // the wavefront index through readfirstlane: everything derived from it is known
+  // to be wavefront-uniform (scalar registers, scalar address arithmetic)
+  const long long item = (long long)blockIdx.x * kMWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= a.items) return;                       // whole wavefront
+  const int s = (int)(item % a.S);
+  const long long x = item / a.S;
+  const int h = (int)(x % a.H);
+  const long long rq = x / a.H;                      // query row ((b * L + l) * n_q + query)
+  const size_t urow = ((size_t)(rq / a.n_q) * a.H + h) * a.T;   // first row of the (b, l, h) unit
+  const int hq = i & 3;                              // query head of this lane's column
+  // ---- query operand (the fp16 query, exact) and, for int8 keys, the head's sum
+  const bool head_ok = hq < a.G;
+  const uint16_t* qrow = a.q + ((size_t)rq * a.Hq + (size_t)h * a.G + (head_ok ? hq : 0)) * kMD + 32 * kq;
+  mu4 qw[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qw[c] = head_ok ? *reinterpret_cast<const mu4*>(qrow + 8 * c) : mu4{0u, 0u, 0u, 0u};
+  mh8 bq[4];
+  if constexpr (KC == MC_TER || KC == MC_SIGN) {
+    // dword m of chunk c: dims (p, p + 16) of the lane's 32, p = 4c + m
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mu4 r;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int p = 4 * c + m;
+        const uint32_t lo = qw[p >> 3][(p & 7) >> 1], hi = qw[2 + (p >> 3)][(p & 7) >> 1];
+        r[m] = __builtin_amdgcn_perm(hi, lo, (p & 1) ? 0x07060302u : 0x05040100u);
+      }
+      bq[c] = __builtin_bit_cast(mh8, r);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bq[c] = __builtin_bit_cast(mh8, qw[c]);
+  }
+  float koff = 0.0f;                                 // int8 keys: 127 * sum of the head's query
+  if constexpr (KC == MC_INT8) {
+    float qs = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const mh8 v = bq[c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qs += (float)v[e];
+    }
+    qs += __shfl_xor(qs, 16);
+    qs += __shfl_xor(qs, 32);
+    koff = 127.0f * qs;
+  }
+  // ---- token range of this split: steps [k0, k1), tokens below t_hi
+  int n = a.T;
+  if (a.kv_len) n = min(max(a.kv_len[rq], 0), a.T);
+  const int steps = (n + kMStep - 1) / kMStep;
+  const int k0 = s * a.cs, k1 = min(k0 + a.cs, steps);
+  const int t_hi = min(k1 * kMStep, n);
+  // ---- state
+  mf4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = mf4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_ref = -INFINITY;       // reference max (log2 units) of head hq
+  float l_part = 0.0f;           // sum of p over this lane's tokens (head hq)
+  float w_part = 0.0f;           // int8 values: sum of the fp16 weights fp16(p) * s_v (head hq)
+  const float kscale = (KC == MC_INT8) ? a.lsc * 16777216.0f : a.lsc;
+
+  auto process = [&](const MStep<KC, VC>& d, int step) {
+    const int t0 = step * kMStep;
+    const int tb = min(t0, a.T - kMStep);            // first token of the rows loaded
+    // ---- Q.K^T: tile u, output rows = tokens 8kq + 4u + r
+    mf4 cq[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      cq[u] = mf4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cq[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<KC>(d.k[u], c), bq[c], cq[u], 0, 0, 0);
+    }
+    float lg[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (KC == MC_INT8) {
+          const float sk = h2f((uint16_t)d.k[u].s[r]);
+          lg[4 * u + r] = sk * (cq[u][r] * kscale - koff * a.lsc);
+        } else {
+          lg[4 * u + r] = cq[u][r] * kscale;
+        }
+      }
+    }
+    const bool partial = (tb < t0) || (tb + kMStep > t_hi);   // wavefront-uniform
+    uint32_t keep[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    if (partial) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = tb + 8 * kq + j;
+        if (t < t0 || t >= t_hi) {
+          lg[j] = -INFINITY;
+          keep[j >> 1] &= (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        }
+      }
+    }
+    // ---- online softmax (lanes with equal i % 4 hold the same head)
+    float mt = lg[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mt = fmaxf(mt, lg[k]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool grow = mt > m_ref + 1.0f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : m_ref;
+      const float alpha = grow ? ((m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new)) : 1.0f;
+      m_ref = m_new;
+      l_part *= alpha;
+      w_part *= alpha;
+      // accumulator component r belongs to head r (rows 0-3): take head r's factor from lane r
+      const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2), a3 = __shfl(alpha, 3);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        acc[c][0] *= a0;
+        acc[c][1] *= a1;
+        acc[c][2] *= a2;
+        acc[c][3] *= a3;
+      }
+    }
+    // ---- P.V
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      mh4 ap;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(lg[4 * u + r] - m_ref);   // masked: exp2(-inf) = 0
+        l_part += p;
+        if constexpr (VC == MC_INT8) {
+          // a masked token may sit on a row nobody wrote yet: its weight is 0, not 0 * scale
+          _Float16 w = (_Float16)p * d.v.s[2 * u + (r >> 1)][r & 1];
+          w = (p == 0.0f) ? (_Float16)0.0f : w;
+          w_part += (float)w;
+          ap[r] = w;
+        } else {
+          ap[r] = (_Float16)p;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap, value_operand<VC>(d.v, u, c, keep[2 * u], keep[2 * u + 1]),
+                                                      acc[c], 0, 0, 0);
+    }
+  };
+
+  // ---- steps k0 .. k1 - 1, two steps of loads in flight (buffers refilled in place)
+  MStep<KC, VC> b0, b1;
+  const MOffsets mo = m_offsets<KC, VC>(i, kq);
+  auto row_of = [&](int step) -> size_t {
+    const int st = min(step, max(k1 - 1, 0));
+    return urow + (size_t)min(st * kMStep, a.T - kMStep);
+  };
+  if (k0 < k1) {
+    m_load<KC, VC>(a, row_of(k0), mo, b0);
+    m_load<KC, VC>(a, row_of(k0 + 1), mo, b1);
+    for (int k = k0; k < k1; k += 2) {
+      process(b0, k);
+      m_load<KC, VC>(a, row_of(k + 2), mo, b0);
+      if (k + 1 >= k1) break;
+      process(b1, k + 1);
+      m_load<KC, VC>(a, row_of(k + 3), mo, b1);
+    }
+  }
+  // ---- the wavefront's partial per query head
+  l_part += __shfl_xor(l_part, 16);
+  l_part += __shfl_xor(l_part, 32);
+  if constexpr (VC == MC_INT8) {
+    w_part += __shfl_xor(w_part, 16);
+    w_part += __shfl_xor(w_part, 32);
+  }
+  // lane r (< 4) holds head r's m and l; lanes 0-15 hold rows 0-3 (heads) of the outputs
+  const float wp0 = __shfl(w_part, 0), wp1 = __shfl(w_part, 1), wp2 = __shfl(w_part, 2), wp3 = __shfl(w_part, 3);
+  if (kq == 0) {
+    const float wp[4] = {wp0, wp1, wp2, wp3};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r >= a.G) break;
+      float* dst = a.part + (((size_t)rq * a.Hq + (size_t)h * a.G + r) * a.S + s) * kMPart;
+      float o[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if constexpr (VC == MC_INT8) o[c] = acc[c][r] * 16777216.0f - 127.0f * wp[r];
+        else o[c] = acc[c][r];
+      }
+      // a partial is 130 floats, so rows are 8-byte aligned: float2 stores
+#pragma unroll
+      for (int c = 0; c < 8; c += 2) *reinterpret_cast<float2*>(dst + 8 * i + c) = make_float2(o[c], o[c + 1]);
+      if (i == r) {
+        dst[kMD] = (m_ref == -INFINITY) ? -INFINITY : m_ref * 0.69314718055994531f;
+        dst[kMD + 1] = l_part;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+}  // namespace kvq
+
+namespace kvq {
+
+namespace {
+
+int m128_codec(const kvq_codec& c) {
+  if (c.rot_width > 1) return -1;
+  switch (c.codebook) {
+    case KVQ_TERNARY: return c.group == 8 ? MC_TER : -1;
+    case KVQ_SIGN: return c.group == 8 ? MC_SIGN : -1;
+    case KVQ_INT8_SYM: return c.group == 128 ? MC_INT8 : -1;
+    case KVQ_FP16: return MC_F16;
+    default: return -1;
+  }
+}
+
+template <int KC>
+hipError_t launch_m128_v(int vc, const M128Args& a, unsigned grid, hipStream_t st) {
+  switch (vc) {
+    case MC_TER: k_decode_m128<KC, MC_TER><<<grid, kMWaves * 64, 0, st>>>(a); break;
+    case MC_SIGN: k_decode_m128<KC, MC_SIGN><<<grid, kMWaves * 64, 0, st>>>(a); break;
+    case MC_INT8: k_decode_m128<KC, MC_INT8><<<grid, kMWaves * 64, 0, st>>>(a); break;
+    default: k_decode_m128<KC, MC_F16><<<grid, kMWaves * 64, 0, st>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool m128_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
+  const kvq_shape& s = k.shape;
+  if (s.head_dim != kMD || s.tokens < kMStep || s.heads < 1 || Hq % s.heads != 0) return false;
+  const int G = Hq / s.heads;
+  if (G < 1 || G > 4) return false;
+  if (k.chan_scale || k.mean || v.chan_scale || v.mean) return false;
+  return m128_codec(k.codec) >= 0 && m128_codec(v.codec) >= 0;
+}
+
+hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
+  const kvq_shape& s = pr.k->shape;
+  M128Args a{};
+  a.kc = reinterpret_cast<const uint8_t*>(pr.k->codes);
+  a.ks = pr.k->scales;
+  a.vc = reinterpret_cast<const uint8_t*>(pr.v->codes);
+  a.vs = pr.v->scales;
+  a.q = pr.q;
+  a.kv_len = pr.kv_len;
+  a.part = static_cast<float*>(pr.ws);
+  a.H = s.heads;
+  a.T = s.tokens;
+  a.Hq = pr.Hq;
+  a.G = pr.Hq / s.heads;
+  a.n_q = pr.n_q;
+  // splits as the workspace holds them, but at least 8 steps each (a wavefront's query
+  // set-up and first loads are a fixed cost)
+  const int nsteps = (s.tokens + kMStep - 1) / kMStep;
+  a.S = std::max(1, std::min(decode_wave_split_count(s, pr.Hq, pr.n_q), nsteps / 8));
+  a.cs = (nsteps + a.S - 1) / a.S;
+  const long long rows = (long long)s.batch * s.layers * pr.n_q;
+  a.items = rows * s.heads * a.S;
+  a.lsc = pr.sm_scale * 1.4426950408889634f;
+  if (a.items == 0) return hipSuccess;
+  if ((size_t)rows * pr.Hq * a.S * kMPart * sizeof(float) > pr.ws_bytes) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((a.items + kMWaves - 1) / kMWaves);
+  hipError_t e;
+  const int vc = m128_codec(pr.v->codec);
+  switch (m128_codec(pr.k->codec)) {
+    case MC_TER: e = launch_m128_v<MC_TER>(vc, a, grid, st); break;
+    case MC_SIGN: e = launch_m128_v<MC_SIGN>(vc, a, grid, st); break;
+    case MC_INT8: e = launch_m128_v<MC_INT8>(vc, a, grid, st); break;
+    default: e = launch_m128_v<MC_F16>(vc, a, grid, st); break;
+  }
+  if (e != hipSuccess) return e;
+  return launch_combine_partials(pr, a.S, nullptr, st);
+}
+
+}  // namespace kvq

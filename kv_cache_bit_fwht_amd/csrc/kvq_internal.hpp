@@ -279,5 +279,13 @@ bool fused_append_supported(const kvq_packed& k, const kvq_packed& v, int Hq, in
 hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_done = nullptr);
 size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q);
 hipError_t launch_combine_partials(const AttnProblem& pr, int S, int* ctr, hipStream_t st);
+// Splits per (query row, query head) that the decode workspace holds partials for with the
+// wavefront-per-split kernels.
+int decode_wave_split_count(const kvq_shape& s, int Hq, int n_q);
+// MFMA decode at head_dim 128: ternary and sign codes at group 8, int8 rows, fp16 (keys
+// and values in any combination of these, no rotation, channel scales or mean), up to 4
+// query heads per KV head, at least 32 tokens.  Partials go to pr.ws, then the combine.
+bool m128_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
+hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st);
 
 }  // namespace kvq
