@@ -77,16 +77,19 @@ template <int C> struct Row {          // bytes of one row's codes, scales per r
 template <int C> struct KTile;
 template <> struct KTile<MC_TER> { mu2 c; mu2 s; };              // 64 code bits, groups 4kq .. 4kq + 3
 template <> struct KTile<MC_SIGN> { uint32_t c; mu2 s; };        // 32 code bits, the same groups
-template <> struct KTile<MC_INT8> { mu4 c0, c1; uint32_t s[4]; };  // 32 code bytes; s: output tokens' scales
+template <> struct KTile<MC_INT8> { mu4 c0, c1; uint32_t s; };  // 32 code bytes; s: the scale of token 8kq + i % 8
 template <> struct KTile<MC_F16> { mu4 c[4]; };                  // 32 fp16 values
 
-// ---- value data for lane (i, kq): dims 8i .. 8i + 7 of tokens 8kq .. 8kq + 7.  Ternary
+// ---- value data for lane (i, kq): dims 8i .. 8i + 7 of tokens 8kq .. 8kq + 7.  (Row
+// scales of int8 tokens are loaded one per lane and shared by DPP broadcasts: eight
+// adjacent 16-bit loads would be merged into one 16-byte load, which returned wrong data
+// at the 2-byte alignment rows can have.)  Ternary
 // and sign: one register per token pair for the codes (token 2j in the low half, 2j + 1
 // in the high half) and one for the two scales, each filled by two 16-bit loads.
 template <int C> struct VData;
 template <> struct VData<MC_TER> { mh2 c[4], s[4]; };
 template <> struct VData<MC_SIGN> { mh2 c[4], s[4]; };
-template <> struct VData<MC_INT8> { mu2 c[8]; mh2 s[4]; };      // 8 code bytes per token; the rows' scales
+template <> struct VData<MC_INT8> { mu2 c[8]; uint32_t s; };   // 8 code bytes per token; the scale of token 8kq + i % 8
 template <> struct VData<MC_F16> { mu4 c[8]; };                  // 8 fp16 values per token
 
 template <int KC, int VC> struct MStep {
@@ -113,28 +116,53 @@ __device__ __forceinline__ MOffsets m_offsets(int i, int kq) {
     const uint32_t r = (uint32_t)tile_row(i, u);
     if constexpr (KC == MC_TER) { o.k[u] = r * 32 + 8 * kq; o.ks[u] = (r * 16 + 4 * kq) * 2; }
     else if constexpr (KC == MC_SIGN) { o.k[u] = r * 16 + 4 * kq; o.ks[u] = (r * 16 + 4 * kq) * 2; }
-    else if constexpr (KC == MC_INT8) { o.k[u] = r * 128 + 32 * kq; o.ks[u] = (8 * kq + 4 * u) * 2; }
+    else if constexpr (KC == MC_INT8) { o.k[u] = r * 128 + 32 * kq; o.ks[u] = (8 * kq + (i & 7)) * 2; }
     else { o.k[u] = r * 256 + 64 * kq; o.ks[u] = 0; }
   }
   const uint32_t t = 8 * kq;
   if constexpr (VC == MC_TER) { o.v = t * 32 + 2 * i; o.vs = (t * 16 + i) * 2; }
   else if constexpr (VC == MC_SIGN) { o.v = t * 16 + i; o.vs = (t * 16 + i) * 2; }
-  else if constexpr (VC == MC_INT8) { o.v = t * 128 + 8 * i; o.vs = t * 2; }
+  else if constexpr (VC == MC_INT8) { o.v = t * 128 + 8 * i; o.vs = (t + (i & 7)) * 2; }
   else { o.v = t * 256 + 16 * i; o.vs = 0; }
+  asm volatile("" : "+v"(o.k[0]), "+v"(o.k[1]), "+v"(o.ks[0]), "+v"(o.ks[1]), "+v"(o.v), "+v"(o.vs));
   return o;
 }
 
-template <typename T>
+// base: wavefront-uniform; off: the lane's offset; IMM: a constant the load instruction
+// carries in its offset field (added in 64-bit, so it can be)
+template <typename T, int IMM = 0>
 __device__ __forceinline__ T ld(const uint8_t* base, uint32_t off) {
-  return *reinterpret_cast<const T*>(base + off);
+  return *reinterpret_cast<const T*>(base + (size_t)off + IMM);
 }
 
-// Loads of the step whose first row (unit row base + first token) is rb.  The offsets
-// pass through an empty asm so the compiler keeps scalar bases plus 32-bit offsets
-// instead of folding them into 64-bit per-lane pointers.
+// Loads of the step whose first row (unit row base + first token) is rb: scalar bases
+// plus the lane's 32-bit offsets (the offsets pass through an empty asm once, where they
+// are made, so the compiler does not fold them into 64-bit per-lane pointers).
+template <int J, int KC, int VC>
+__device__ __forceinline__ void m_load_vpair(const uint8_t* vb, const uint8_t* vsb, const MOffsets& o, VData<VC>& v) {
+  constexpr int R = Row<VC>::code;
+  if constexpr (VC == MC_TER) {
+    v.c[J][0] = ld<_Float16, R * (2 * J)>(vb, o.v);
+    v.c[J][1] = ld<_Float16, R * (2 * J + 1)>(vb, o.v);
+  } else if constexpr (VC == MC_SIGN) {                // a code byte, zero-extended into each half
+    v.c[J] = __builtin_bit_cast(mh2, (uint32_t)ld<uint8_t, R * (2 * J)>(vb, o.v) |
+                                         ((uint32_t)ld<uint8_t, R * (2 * J + 1)>(vb, o.v) << 16));
+  } else if constexpr (VC == MC_INT8) {
+    v.c[2 * J] = ld<mu2, R * (2 * J)>(vb, o.v);
+    v.c[2 * J + 1] = ld<mu2, R * (2 * J + 1)>(vb, o.v);
+    if constexpr (J == 0) v.s = ld<uint16_t>(vsb, o.vs);
+  } else {
+    v.c[2 * J] = ld<mu4, R * (2 * J)>(vb, o.v);
+    v.c[2 * J + 1] = ld<mu4, R * (2 * J + 1)>(vb, o.v);
+  }
+  if constexpr (VC == MC_TER || VC == MC_SIGN) {
+    v.s[J][0] = ld<_Float16, 32 * (2 * J)>(vsb, o.vs);
+    v.s[J][1] = ld<_Float16, 32 * (2 * J + 1)>(vsb, o.vs);
+  }
+}
+
 template <int KC, int VC>
-__device__ __forceinline__ void m_load(const M128Args& a, size_t rb, MOffsets o, MStep<KC, VC>& d) {
-  asm volatile("" : "+v"(o.k[0]), "+v"(o.k[1]), "+v"(o.ks[0]), "+v"(o.ks[1]), "+v"(o.v), "+v"(o.vs));
+__device__ __forceinline__ void m_load(const M128Args& a, size_t rb, const MOffsets& o, MStep<KC, VC>& d) {
   const uint8_t* kb = a.kc + rb * Row<KC>::code;
   const uint8_t* ksb = reinterpret_cast<const uint8_t*>(a.ks) + rb * 2 * Row<KC>::scales;
 #pragma unroll
@@ -147,38 +175,38 @@ __device__ __forceinline__ void m_load(const M128Args& a, size_t rb, MOffsets o,
       d.k[u].s = ld<mu2>(ksb, o.ks[u]);
     } else if constexpr (KC == MC_INT8) {
       d.k[u].c0 = ld<mu4>(kb, o.k[u]);
-      d.k[u].c1 = ld<mu4>(kb, o.k[u] + 16);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) d.k[u].s[rr] = ld<uint16_t>(ksb, o.ks[u] + 2 * rr);
+      d.k[u].c1 = ld<mu4, 16>(kb, o.k[u]);
+      if (u == 0) d.k[0].s = ld<uint16_t>(ksb, o.ks[0]);
     } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) d.k[u].c[c] = ld<mu4>(kb, o.k[u] + 16 * c);
+      d.k[u].c[0] = ld<mu4, 0>(kb, o.k[u]);
+      d.k[u].c[1] = ld<mu4, 16>(kb, o.k[u]);
+      d.k[u].c[2] = ld<mu4, 32>(kb, o.k[u]);
+      d.k[u].c[3] = ld<mu4, 48>(kb, o.k[u]);
     }
   }
   const uint8_t* vb = a.vc + rb * Row<VC>::code;
   const uint8_t* vsb = reinterpret_cast<const uint8_t*>(a.vs) + rb * 2 * Row<VC>::scales;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (VC == MC_TER || VC == MC_SIGN) {
-      constexpr uint32_t R = Row<VC>::code;
-      if constexpr (VC == MC_TER) {
-        d.v.c[j][0] = ld<_Float16>(vb, o.v + R * (2 * j));
-        d.v.c[j][1] = ld<_Float16>(vb, o.v + R * (2 * j + 1));
-      } else {                                       // a code byte, zero-extended into each half
-        d.v.c[j] = __builtin_bit_cast(mh2, (uint32_t)ld<uint8_t>(vb, o.v + R * (2 * j)) |
-                                               ((uint32_t)ld<uint8_t>(vb, o.v + R * (2 * j + 1)) << 16));
-      }
-      d.v.s[j][0] = ld<_Float16>(vsb, o.vs + 32 * (2 * j));
-      d.v.s[j][1] = ld<_Float16>(vsb, o.vs + 32 * (2 * j + 1));
-    } else if constexpr (VC == MC_INT8) {
-      d.v.c[2 * j] = ld<mu2>(vb, o.v + 128 * (2 * j));
-      d.v.c[2 * j + 1] = ld<mu2>(vb, o.v + 128 * (2 * j + 1));
-      d.v.s[j][0] = ld<_Float16>(vsb, o.vs + 2 * (2 * j));
-      d.v.s[j][1] = ld<_Float16>(vsb, o.vs + 2 * (2 * j + 1));
-    } else {
-      d.v.c[2 * j] = ld<mu4>(vb, o.v + 256 * (2 * j));
-      d.v.c[2 * j + 1] = ld<mu4>(vb, o.v + 256 * (2 * j + 1));
-    }
+  m_load_vpair<0, KC, VC>(vb, vsb, o, d.v);
+  m_load_vpair<1, KC, VC>(vb, vsb, o, d.v);
+  m_load_vpair<2, KC, VC>(vb, vsb, o, d.v);
+  m_load_vpair<3, KC, VC>(vb, vsb, o, d.v);
+}
+
+// x of lane j of this lane's 16-lane row (DPP row broadcast; every lane of the row active)
+template <int J>
+__device__ __forceinline__ uint32_t m_bcast_c(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x150 + J, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t m_bcast(uint32_t x, int j) {   // j a constant after unrolling
+  switch (j) {
+    case 0: return m_bcast_c<0>(x);
+    case 1: return m_bcast_c<1>(x);
+    case 2: return m_bcast_c<2>(x);
+    case 3: return m_bcast_c<3>(x);
+    case 4: return m_bcast_c<4>(x);
+    case 5: return m_bcast_c<5>(x);
+    case 6: return m_bcast_c<6>(x);
+    default: return m_bcast_c<7>(x);
   }
 }
 
@@ -239,7 +267,7 @@ __device__ __forceinline__ mh8 key_operand(const KTile<KC>& t, int c) {
 
 // B operand of value chunk c (dim 8i + c) for tokens 4u .. 4u + 3 of the lane's 8.
 // keep01 / keep23: all-ones halves for the tokens that count (partial steps).
-template <int VC>
+template <int VC, bool MASK>
 __device__ __forceinline__ mh4 value_operand(const VData<VC>& v, int u, int c, uint32_t keep01, uint32_t keep23) {
   mu2 r;
 #pragma unroll
@@ -258,7 +286,7 @@ __device__ __forceinline__ mh4 value_operand(const VData<VC>& v, int u, int c, u
     } else {
       x = __builtin_amdgcn_perm(v.c[2 * pj + 1][c >> 1], v.c[2 * pj][c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
     }
-    if constexpr (VC != MC_INT8) x &= (h == 0) ? keep01 : keep23;
+    if constexpr (MASK && VC != MC_INT8) x &= (h == 0) ? keep01 : keep23;
     r[h] = x;
   }
   return __builtin_bit_cast(mh4, r);
@@ -346,7 +374,7 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (KC == MC_INT8) {
-          const float sk = h2f((uint16_t)d.k[u].s[r]);
+          const float sk = h2f((uint16_t)m_bcast(d.k[0].s, 4 * u + r));   // token 8kq + 4u + r
           lg[4 * u + r] = sk * (cq[u][r] * kscale - koff * a.lsc);
         } else {
           lg[4 * u + r] = cq[u][r] * kscale;
@@ -398,7 +426,7 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
         l_part += p;
         if constexpr (VC == MC_INT8) {
           // a masked token may sit on a row nobody wrote yet: its weight is 0, not 0 * scale
-          _Float16 w = (_Float16)p * d.v.s[2 * u + (r >> 1)][r & 1];
+          _Float16 w = (_Float16)p * __builtin_bit_cast(_Float16, (uint16_t)m_bcast(d.v.s, 4 * u + r));
           w = (p == 0.0f) ? (_Float16)0.0f : w;
           w_part += (float)w;
           ap[r] = w;
@@ -406,14 +434,33 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
           ap[r] = (_Float16)p;
         }
       }
+      // The B values of masked tokens must be 0, not NaN (their rows may hold anything):
+      // ternary and sign take masked scales (a zero scale gives +-0 for any code), fp16
+      // values are masked only in partial steps; int8 codes are always finite.
+      if constexpr (VC == MC_TER || VC == MC_SIGN) {
+        VData<VC> vm = d.v;
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap, value_operand<VC>(d.v, u, c, keep[2 * u], keep[2 * u + 1]),
-                                                      acc[c], 0, 0, 0);
+        for (int h2 = 0; h2 < 2; ++h2)
+          vm.s[2 * u + h2] = __builtin_bit_cast(mh2, __builtin_bit_cast(uint32_t, d.v.s[2 * u + h2]) & keep[2 * u + h2]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap, value_operand<VC, false>(vm, u, c, 0u, 0u), acc[c], 0, 0, 0);
+      } else if (VC == MC_F16 && partial) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              ap, value_operand<VC, true>(d.v, u, c, keep[2 * u], keep[2 * u + 1]), acc[c], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap, value_operand<VC, false>(d.v, u, c, 0u, 0u), acc[c], 0, 0, 0);
+      }
     }
   };
 
-  // ---- steps k0 .. k1 - 1, two steps of loads in flight (buffers refilled in place)
+  // ---- steps k0 .. k1 - 1 with two steps of loads in flight (buffers refilled in place;
+  // a third buffer measured no faster: the low-bit steps are bound by their VALU work)
+  constexpr int NB = 2;
   MStep<KC, VC> b0, b1;
   const MOffsets mo = m_offsets<KC, VC>(i, kq);
   auto row_of = [&](int step) -> size_t {
@@ -423,12 +470,12 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   if (k0 < k1) {
     m_load<KC, VC>(a, row_of(k0), mo, b0);
     m_load<KC, VC>(a, row_of(k0 + 1), mo, b1);
-    for (int k = k0; k < k1; k += 2) {
+    for (int k = k0; k < k1; k += NB) {
       process(b0, k);
-      m_load<KC, VC>(a, row_of(k + 2), mo, b0);
+      m_load<KC, VC>(a, row_of(k + NB), mo, b0);
       if (k + 1 >= k1) break;
       process(b1, k + 1);
-      m_load<KC, VC>(a, row_of(k + 3), mo, b1);
+      m_load<KC, VC>(a, row_of(k + NB + 1), mo, b1);
     }
   }
   // ---- the wavefront's partial per query head
