@@ -178,6 +178,8 @@ def _cpu_name():
 
 
 def _median_time(torch, fn, reps):
+    fn()                                             # warm: code loaded, clocks up
+    torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
