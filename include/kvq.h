@@ -264,10 +264,11 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
  * rotation) -- the 4-bit-key / 2-bit-value arms of [E22L] What I tested, the
  * symmetric value grid of [E22L] Result, 4-bit values ([LCPP] Finding 1) and the
  * per-head key widths of [LCPP] Finding 2; or head_dim 128, at least 32 tokens, at
- * most 4 query heads per KV head, K and V each TERNARY or SIGN at group 8,
- * INT8_SYM at group 128 or FP16, without rotation, chan_scale or mean -- the
- * extreme low-bit arms, the int8 reference row and the fp16 anchor layer of
- * [FMAG-6] Milestone and Best results. */
+ * most 4 query heads per KV head, K TERNARY or SIGN at group 8, INT8_SYM at group
+ * 128, FP16 or NF4 at group 64, V TERNARY or SIGN at group 8, INT8_SYM at group 128,
+ * FP16 or 4-bit INT_ABSMAX at group 64, without rotation, chan_scale or mean -- the
+ * extreme low-bit arms, NF4 keys with 4-bit values, the int8 reference row and the
+ * fp16 anchor layer of [FMAG-6] Milestone and Best results. */
 kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
                               int32_t n_q, const uint16_t* q, const int32_t* kv_len,
                               float sm_scale, float* out, float* lse, void* ws,

@@ -53,7 +53,8 @@ constexpr int kMStep = 32;            // tokens per wavefront step
 constexpr int kMWaves = 4;            // independent wavefronts per block
 constexpr int kMPart = kMD + 2;       // floats per partial: o[128], m, l
 
-enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3 };
+// MC_NF4: keys only (NF4 at group 64); MC_I4: values only (4-bit signed absmax at group 64)
+enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3, MC_NF4 = 4, MC_I4 = 5 };
 
 struct M128Args {
   const uint8_t* kc;
@@ -66,11 +67,12 @@ struct M128Args {
   int H, T, Hq, G, n_q, S, cs;        // cs: steps per split
   long long items;                    // rows * H * S
   float lsc;                          // softmax scale * log2(e)
+  float nf4[16];                      // NF4 levels (binary32)
 };
 
 template <int C> struct Row {          // bytes of one row's codes, scales per row
-  static constexpr int code = C == MC_TER ? 32 : C == MC_SIGN ? 16 : C == MC_INT8 ? 128 : 256;
-  static constexpr int scales = C == MC_TER || C == MC_SIGN ? 16 : C == MC_INT8 ? 1 : 0;
+  static constexpr int code = C == MC_TER ? 32 : C == MC_SIGN ? 16 : C == MC_INT8 ? 128 : C == MC_F16 ? 256 : 64;
+  static constexpr int scales = C == MC_TER || C == MC_SIGN ? 16 : C == MC_INT8 ? 1 : C == MC_F16 ? 0 : 2;
 };
 
 // ---- key data of one 16-token tile for lane (i, kq): token tok(i, u), dims 32kq .. 32kq + 31
@@ -79,6 +81,8 @@ template <> struct KTile<MC_TER> { mu2 c; mu2 s; };              // 64 code bits
 template <> struct KTile<MC_SIGN> { uint32_t c; mu2 s; };        // 32 code bits, the same groups
 template <> struct KTile<MC_INT8> { mu4 c0, c1; uint32_t s; };  // 32 code bytes; s: the scale of token 8kq + i % 8
 template <> struct KTile<MC_F16> { mu4 c[4]; };                  // 32 fp16 values
+template <> struct KTile<MC_NF4> { uint32_t c[4]; uint32_t s; };  // 8 codes of each 32-dim chunk; s: the two
+                                                                  // scales of token 8kq + i % 8 (tile 0 only)
 
 // ---- value data for lane (i, kq): dims 8i .. 8i + 7 of tokens 8kq .. 8kq + 7.  (Row
 // scales of int8 tokens are loaded one per lane and shared by DPP broadcasts: eight
@@ -91,6 +95,7 @@ template <> struct VData<MC_TER> { mh2 c[4], s[4]; };
 template <> struct VData<MC_SIGN> { mh2 c[4], s[4]; };
 template <> struct VData<MC_INT8> { mu2 c[8]; uint32_t s; };   // 8 code bytes per token; the scale of token 8kq + i % 8
 template <> struct VData<MC_F16> { mu4 c[8]; };                  // 8 fp16 values per token
+template <> struct VData<MC_I4> { uint32_t c[8]; uint32_t s; };  // 8 codes per token; the two scales of token 8kq + i % 8
 
 template <int KC, int VC> struct MStep {
   KTile<KC> k[2];
@@ -117,13 +122,15 @@ __device__ __forceinline__ MOffsets m_offsets(int i, int kq) {
     if constexpr (KC == MC_TER) { o.k[u] = r * 32 + 8 * kq; o.ks[u] = (r * 16 + 4 * kq) * 2; }
     else if constexpr (KC == MC_SIGN) { o.k[u] = r * 16 + 4 * kq; o.ks[u] = (r * 16 + 4 * kq) * 2; }
     else if constexpr (KC == MC_INT8) { o.k[u] = r * 128 + 32 * kq; o.ks[u] = (8 * kq + (i & 7)) * 2; }
-    else { o.k[u] = r * 256 + 64 * kq; o.ks[u] = 0; }
+    else if constexpr (KC == MC_F16) { o.k[u] = r * 256 + 64 * kq; o.ks[u] = 0; }
+    else { o.k[u] = r * 64 + 4 * kq; o.ks[u] = (8 * kq + (i & 7)) * 4; }
   }
   const uint32_t t = 8 * kq;
   if constexpr (VC == MC_TER) { o.v = t * 32 + 2 * i; o.vs = (t * 16 + i) * 2; }
   else if constexpr (VC == MC_SIGN) { o.v = t * 16 + i; o.vs = (t * 16 + i) * 2; }
   else if constexpr (VC == MC_INT8) { o.v = t * 128 + 8 * i; o.vs = (t + (i & 7)) * 2; }
-  else { o.v = t * 256 + 16 * i; o.vs = 0; }
+  else if constexpr (VC == MC_F16) { o.v = t * 256 + 16 * i; o.vs = 0; }
+  else { o.v = t * 64 + 4 * i; o.vs = (t + (i & 7)) * 4; }
   asm volatile("" : "+v"(o.k[0]), "+v"(o.k[1]), "+v"(o.ks[0]), "+v"(o.ks[1]), "+v"(o.v), "+v"(o.vs));
   return o;
 }
@@ -151,9 +158,13 @@ __device__ __forceinline__ void m_load_vpair(const uint8_t* vb, const uint8_t* v
     v.c[2 * J] = ld<mu2, R * (2 * J)>(vb, o.v);
     v.c[2 * J + 1] = ld<mu2, R * (2 * J + 1)>(vb, o.v);
     if constexpr (J == 0) v.s = ld<uint16_t>(vsb, o.vs);
-  } else {
+  } else if constexpr (VC == MC_F16) {
     v.c[2 * J] = ld<mu4, R * (2 * J)>(vb, o.v);
     v.c[2 * J + 1] = ld<mu4, R * (2 * J + 1)>(vb, o.v);
+  } else {
+    v.c[2 * J] = ld<uint32_t, R * (2 * J)>(vb, o.v);
+    v.c[2 * J + 1] = ld<uint32_t, R * (2 * J + 1)>(vb, o.v);
+    if constexpr (J == 0) v.s = ld<uint32_t>(vsb, o.vs);
   }
   if constexpr (VC == MC_TER || VC == MC_SIGN) {
     v.s[J][0] = ld<_Float16, 32 * (2 * J)>(vsb, o.vs);
@@ -177,11 +188,17 @@ __device__ __forceinline__ void m_load(const M128Args& a, size_t rb, const MOffs
       d.k[u].c0 = ld<mu4>(kb, o.k[u]);
       d.k[u].c1 = ld<mu4, 16>(kb, o.k[u]);
       if (u == 0) d.k[0].s = ld<uint16_t>(ksb, o.ks[0]);
-    } else {
+    } else if constexpr (KC == MC_F16) {
       d.k[u].c[0] = ld<mu4, 0>(kb, o.k[u]);
       d.k[u].c[1] = ld<mu4, 16>(kb, o.k[u]);
       d.k[u].c[2] = ld<mu4, 32>(kb, o.k[u]);
       d.k[u].c[3] = ld<mu4, 48>(kb, o.k[u]);
+    } else {
+      d.k[u].c[0] = ld<uint32_t, 0>(kb, o.k[u]);
+      d.k[u].c[1] = ld<uint32_t, 16>(kb, o.k[u]);
+      d.k[u].c[2] = ld<uint32_t, 32>(kb, o.k[u]);
+      d.k[u].c[3] = ld<uint32_t, 48>(kb, o.k[u]);
+      if (u == 0) d.k[0].s = ld<uint32_t>(ksb, o.ks[0]);
     }
   }
   const uint8_t* vb = a.vc + rb * Row<VC>::code;
@@ -265,6 +282,22 @@ __device__ __forceinline__ mh8 key_operand(const KTile<KC>& t, int c) {
   return __builtin_bit_cast(mh8, r);
 }
 
+// NF4 keys, chunk c (dims 32c + 8kq .. + 7, one group of 64 per two chunks): the levels
+// as fp16 high parts and fp16 remainders (22 significant bits together) from a table of
+// code bytes (two dims) in LDS.
+__device__ __forceinline__ void nf4_operands(const KTile<MC_NF4>& t, int c, const mu2* lut, mh8& hi, mh8& lo) {
+  const uint32_t w = t.c[c];
+  mu4 h, l;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const mu2 e = lut[(w >> (8 * k)) & 0xFFu];
+    h[k] = e.x;
+    l[k] = e.y;
+  }
+  hi = __builtin_bit_cast(mh8, h);
+  lo = __builtin_bit_cast(mh8, l);
+}
+
 // B operand of value chunk c (dim 8i + c) for tokens 4u .. 4u + 3 of the lane's 8.
 // keep01 / keep23: all-ones halves for the tokens that count (partial steps).
 template <int VC, bool MASK>
@@ -283,10 +316,13 @@ __device__ __forceinline__ mh4 value_operand(const VData<VC>& v, int u, int c, u
     } else if constexpr (VC == MC_INT8) {
       const uint32_t sel = (uint32_t)(c & 3) | (0x0Cu << 8) | ((uint32_t)(4 + (c & 3)) << 16) | (0x0Cu << 24);
       x = __builtin_amdgcn_perm(v.c[2 * pj + 1][c >> 2], v.c[2 * pj][c >> 2], sel);
-    } else {
+    } else if constexpr (VC == MC_F16) {
       x = __builtin_amdgcn_perm(v.c[2 * pj + 1][c >> 1], v.c[2 * pj][c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
+    } else {                                         // 4-bit codes as fp16 subnormals c * 2^-24
+      const uint32_t y = __builtin_amdgcn_perm(v.c[2 * pj + 1], v.c[2 * pj], (c < 4) ? 0x05040100u : 0x07060302u);
+      x = (y >> (4 * (c & 3))) & 0x000F000Fu;
     }
-    if constexpr (MASK && VC != MC_INT8) x &= (h == 0) ? keep01 : keep23;
+    if constexpr (MASK && VC != MC_INT8 && VC != MC_I4) x &= (h == 0) ? keep01 : keep23;
     r[h] = x;
   }
   return __builtin_bit_cast(mh4, r);
@@ -295,6 +331,17 @@ __device__ __forceinline__ mh4 value_operand(const VData<VC>& v, int u, int c, u
 template <int KC, int VC>
 __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 : 2) void k_decode_m128(M128Args a) {
   const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
+  // NF4 keys: the block's table of code bytes -> (high parts, remainders) of two levels
+  __shared__ mu2 nf4_lut[KC == MC_NF4 ? 256 : 1];
+  if constexpr (KC == MC_NF4) {
+    const int b = threadIdx.x;                       // 256 threads, one entry each
+    const float l0 = a.nf4[b & 15], l1 = a.nf4[b >> 4];
+    const _Float16 h0 = (_Float16)l0, h1 = (_Float16)l1;
+    const _Float16 r0 = (_Float16)(l0 - (float)h0), r1 = (_Float16)(l1 - (float)h1);
+    nf4_lut[b] = mu2{(uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
+                     (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16)};
+    __syncthreads();
+  }
   // the wavefront index through readfirstlane: everything derived from it is known
   // to be wavefront-uniform (scalar registers, scalar address arithmetic)
   const long long item = (long long)blockIdx.x * kMWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -310,7 +357,12 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   const uint16_t* qrow = a.q + ((size_t)rq * a.Hq + (size_t)h * a.G + (head_ok ? hq : 0)) * kMD + 32 * kq;
   mu4 qw[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) qw[c] = head_ok ? *reinterpret_cast<const mu4*>(qrow + 8 * c) : mu4{0u, 0u, 0u, 0u};
+  for (int c = 0; c < 4; ++c) {
+    // NF4 keys: chunk c is dims 32c .. 32c + 31 (k-block kq: 32c + 8kq ..); otherwise the
+    // lane's chunks are dims 32kq .. 32kq + 31
+    const uint16_t* qp = (KC == MC_NF4) ? qrow - 32 * kq + 32 * c + 8 * kq : qrow + 8 * c;
+    qw[c] = head_ok ? *reinterpret_cast<const mu4*>(qp) : mu4{0u, 0u, 0u, 0u};
+  }
   mh8 bq[4];
   if constexpr (KC == MC_TER || KC == MC_SIGN) {
     // dword m of chunk c: dims (p, p + 16) of the lane's 32, p = 4c + m
@@ -361,12 +413,21 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
     const int t0 = step * kMStep;
     const int tb = min(t0, a.T - kMStep);            // first token of the rows loaded
     // ---- Q.K^T: tile u, output rows = tokens 8kq + 4u + r
-    mf4 cq[2];
+    mf4 cq[2][2];                                    // [tile][key group] (group 1 for NF4 only)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      cq[u] = mf4{0.0f, 0.0f, 0.0f, 0.0f};
+      cq[u][0] = cq[u][1] = mf4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cq[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<KC>(d.k[u], c), bq[c], cq[u], 0, 0, 0);
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (KC == MC_NF4) {
+          mh8 ahi, alo;
+          nf4_operands(d.k[u], c, nf4_lut, ahi, alo);
+          cq[u][c >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bq[c], cq[u][c >> 1], 0, 0, 0);
+          cq[u][c >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bq[c], cq[u][c >> 1], 0, 0, 0);
+        } else {
+          cq[u][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<KC>(d.k[u], c), bq[c], cq[u][0], 0, 0, 0);
+        }
+      }
     }
     float lg[8];
 #pragma unroll
@@ -375,9 +436,12 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
       for (int r = 0; r < 4; ++r) {
         if constexpr (KC == MC_INT8) {
           const float sk = h2f((uint16_t)m_bcast(d.k[0].s, 4 * u + r));   // token 8kq + 4u + r
-          lg[4 * u + r] = sk * (cq[u][r] * kscale - koff * a.lsc);
+          lg[4 * u + r] = sk * (cq[u][0][r] * kscale - koff * a.lsc);
+        } else if constexpr (KC == MC_NF4) {
+          const uint32_t sw = m_bcast(d.k[0].s, 4 * u + r);                 // its two group scales
+          lg[4 * u + r] = (h2f((uint16_t)sw) * cq[u][0][r] + h2f((uint16_t)(sw >> 16)) * cq[u][1][r]) * kscale;
         } else {
-          lg[4 * u + r] = cq[u][r] * kscale;
+          lg[4 * u + r] = cq[u][0][r] * kscale;
         }
       }
     }
@@ -424,9 +488,13 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
       for (int r = 0; r < 4; ++r) {
         const float p = __builtin_amdgcn_exp2f(lg[4 * u + r] - m_ref);   // masked: exp2(-inf) = 0
         l_part += p;
-        if constexpr (VC == MC_INT8) {
-          // a masked token may sit on a row nobody wrote yet: its weight is 0, not 0 * scale
-          _Float16 w = (_Float16)p * __builtin_bit_cast(_Float16, (uint16_t)m_bcast(d.v.s, 4 * u + r));
+        if constexpr (VC == MC_INT8 || VC == MC_I4) {
+          // A = fp16(p) * the value scale; 4-bit values: rows 0-3 take group 0's scale (dims
+          // 0-63), rows 4-7 group 1's.  A masked token may sit on a row nobody wrote yet: its
+          // weight is 0, not 0 * scale.
+          uint32_t sw = m_bcast(d.v.s, 4 * u + r);   // token 8kq + 4u + r
+          if constexpr (VC == MC_I4) sw = (i & 4) ? (sw >> 16) : sw;
+          _Float16 w = (_Float16)p * __builtin_bit_cast(_Float16, (uint16_t)sw);
           w = (p == 0.0f) ? (_Float16)0.0f : w;
           w_part += (float)w;
           ap[r] = w;
@@ -481,13 +549,18 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   // ---- the wavefront's partial per query head
   l_part += __shfl_xor(l_part, 16);
   l_part += __shfl_xor(l_part, 32);
-  if constexpr (VC == MC_INT8) {
+  if constexpr (VC == MC_INT8 || VC == MC_I4) {
     w_part += __shfl_xor(w_part, 16);
     w_part += __shfl_xor(w_part, 32);
   }
   // lane r (< 4) holds head r's m and l; lanes 0-15 hold rows 0-3 (heads) of the outputs
-  const float wp0 = __shfl(w_part, 0), wp1 = __shfl(w_part, 1), wp2 = __shfl(w_part, 2), wp3 = __shfl(w_part, 3);
-  if (kq == 0) {
+  // the weight sum of output row 4kq + r (int8: rows 0-3; 4-bit values: rows 0-7)
+  const float wp0 = __shfl(w_part, 4 * kq), wp1 = __shfl(w_part, 4 * kq + 1);
+  const float wp2 = __shfl(w_part, 4 * kq + 2), wp3 = __shfl(w_part, 4 * kq + 3);
+  // lanes holding outputs: rows 0-3 (heads) for every column; 4-bit values: rows 0-3 for
+  // value dims 0-63 (columns 0-7), rows 4-7 for dims 64-127 (columns 8-15)
+  const bool writer = (VC == MC_I4) ? (kq == (i >> 3)) : (kq == 0);
+  if (writer) {
     const float wp[4] = {wp0, wp1, wp2, wp3};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -497,12 +570,13 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         if constexpr (VC == MC_INT8) o[c] = acc[c][r] * 16777216.0f - 127.0f * wp[r];
+        else if constexpr (VC == MC_I4) o[c] = acc[c][r] * 16777216.0f - 8.0f * wp[r];
         else o[c] = acc[c][r];
       }
       // a partial is 130 floats, so rows are 8-byte aligned: float2 stores
 #pragma unroll
       for (int c = 0; c < 8; c += 2) *reinterpret_cast<float2*>(dst + 8 * i + c) = make_float2(o[c], o[c + 1]);
-      if (i == r) {
+      if (kq == 0 && i == r) {
         dst[kMD] = (m_ref == -INFINITY) ? -INFINITY : m_ref * 0.69314718055994531f;
         dst[kMD + 1] = l_part;
       }
@@ -518,13 +592,16 @@ namespace kvq {
 
 namespace {
 
-int m128_codec(const kvq_codec& c) {
+// The kernel's codec of a key (K) or value (V) codec, or -1.
+int m128_codec(const kvq_codec& c, bool key) {
   if (c.rot_width > 1) return -1;
   switch (c.codebook) {
     case KVQ_TERNARY: return c.group == 8 ? MC_TER : -1;
     case KVQ_SIGN: return c.group == 8 ? MC_SIGN : -1;
     case KVQ_INT8_SYM: return c.group == 128 ? MC_INT8 : -1;
     case KVQ_FP16: return MC_F16;
+    case KVQ_NF4: return (key && c.group == 64) ? MC_NF4 : -1;
+    case KVQ_INT_ABSMAX: return (!key && c.bits == 4 && c.group == 64) ? MC_I4 : -1;
     default: return -1;
   }
 }
@@ -535,6 +612,7 @@ hipError_t launch_m128_v(int vc, const M128Args& a, unsigned grid, hipStream_t s
     case MC_TER: k_decode_m128<KC, MC_TER><<<grid, kMWaves * 64, 0, st>>>(a); break;
     case MC_SIGN: k_decode_m128<KC, MC_SIGN><<<grid, kMWaves * 64, 0, st>>>(a); break;
     case MC_INT8: k_decode_m128<KC, MC_INT8><<<grid, kMWaves * 64, 0, st>>>(a); break;
+    case MC_I4: k_decode_m128<KC, MC_I4><<<grid, kMWaves * 64, 0, st>>>(a); break;
     default: k_decode_m128<KC, MC_F16><<<grid, kMWaves * 64, 0, st>>>(a); break;
   }
   return hipGetLastError();
@@ -548,7 +626,7 @@ bool m128_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   const int G = Hq / s.heads;
   if (G < 1 || G > 4) return false;
   if (k.chan_scale || k.mean || v.chan_scale || v.mean) return false;
-  return m128_codec(k.codec) >= 0 && m128_codec(v.codec) >= 0;
+  return m128_codec(k.codec, true) >= 0 && m128_codec(v.codec, false) >= 0;
 }
 
 hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
@@ -578,11 +656,13 @@ hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
   if ((size_t)rows * pr.Hq * a.S * kMPart * sizeof(float) > pr.ws_bytes) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((a.items + kMWaves - 1) / kMWaves);
   hipError_t e;
-  const int vc = m128_codec(pr.v->codec);
-  switch (m128_codec(pr.k->codec)) {
+  const int vc = m128_codec(pr.v->codec, false);
+  std::copy(host_tables().nf4_lv, host_tables().nf4_lv + 16, a.nf4);
+  switch (m128_codec(pr.k->codec, true)) {
     case MC_TER: e = launch_m128_v<MC_TER>(vc, a, grid, st); break;
     case MC_SIGN: e = launch_m128_v<MC_SIGN>(vc, a, grid, st); break;
     case MC_INT8: e = launch_m128_v<MC_INT8>(vc, a, grid, st); break;
+    case MC_NF4: e = launch_m128_v<MC_NF4>(vc, a, grid, st); break;
     default: e = launch_m128_v<MC_F16>(vc, a, grid, st); break;
   }
   if (e != hipSuccess) return e;

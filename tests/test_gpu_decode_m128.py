@@ -1,7 +1,9 @@
 """GPU parity of the head_dim-128 MFMA decode (kvq_decode_attn_ex path 2 at head_dim
-128) against the CPU oracle: keys and values each ternary at group 8, sign at group
-8, int8 rows or fp16, in every combination ([FMAG-6] Milestone and Best results: the
-extreme low-bit arms, the int8 reference row and the fp16 anchor layer).
+128) against the CPU oracle: keys ternary or sign at group 8, int8 rows, fp16 or NF4
+at group 64, values ternary or sign at group 8, int8 rows, fp16 or 4-bit signed absmax
+at group 64, in every combination ([FMAG-6] Milestone and Best results: the extreme
+low-bit arms, NF4 keys with 4-bit values, the int8 reference row and the fp16 anchor
+layer).
 
 Bars: attention outputs within 2e-3 relative L2 per row and lse within 1e-4 of the
 oracle's fp64 attention over the oracle's dequantised cache; path 0 takes the same
@@ -17,12 +19,14 @@ from tests.test_gpu_attn import _check_decode, _gpu_decode
 
 pytestmark = pytest.mark.gpu
 
-CODECS = ["ter", "sign", "int8", "f16"]
+K_CODECS = ["ter", "sign", "int8", "f16", "nf4"]
+V_CODECS = ["ter", "sign", "int8", "f16", "i4"]
 
 
 def _codec(K, name):
     return {"ter": K.Codec(K.TERNARY, 2, 8, 0), "sign": K.Codec(K.SIGN, 1, 8, 0),
-            "int8": K.Codec(K.INT8_SYM, 8, 128, 0), "f16": K.Codec(K.FP16)}[name]
+            "int8": K.Codec(K.INT8_SYM, 8, 128, 0), "f16": K.Codec(K.FP16),
+            "nf4": K.Codec(K.NF4, 4, 64, 0), "i4": K.Codec(K.INT_ABSMAX, 4, 64, 0)}[name]
 
 
 def _pack(K, x, codec, shape):
@@ -43,8 +47,8 @@ def _inputs(B=2, L=2, T=333, n_q=2, Hq=32):
     return w, Kx, Vx, q
 
 
-@pytest.mark.parametrize("kname", CODECS)
-@pytest.mark.parametrize("vname", CODECS)
+@pytest.mark.parametrize("kname", K_CODECS)
+@pytest.mark.parametrize("vname", V_CODECS)
 def test_codec_pairs(kname, vname):
     """T = 333 (ragged last step), two queries per row with lengths T and 200."""
     import kv_cache_bit_fwht_amd as K
@@ -93,7 +97,8 @@ def test_cache_lengths(T):
     _check_decode(out, lse, ref_out, ref_lse, None)
 
 
-@pytest.mark.parametrize("kname,vname", [("ter", "ter"), ("sign", "sign"), ("int8", "int8"), ("f16", "f16")])
+@pytest.mark.parametrize("kname,vname", [("ter", "ter"), ("sign", "sign"), ("int8", "int8"), ("f16", "f16"),
+                                         ("nf4", "i4")])
 def test_garbage_rows_past_the_keys(kname, vname):
     """Rows at and past each query's length hold NaN scales and all-ones codes (fp16: NaN
     values); the outputs equal those of a clean cache within the bars."""
@@ -120,29 +125,30 @@ def test_garbage_rows_past_the_keys(kname, vname):
     _check_decode(out, lse, ref_out, ref_lse, kv_len)
 
 
-def test_full_size_c4_sampled_units():
+@pytest.mark.parametrize("kname,vname", [("ter", "ter"), ("nf4", "i4")])
+def test_full_size_c4_sampled_units(kname, vname):
     """The extreme low-bit configuration at its full unit size (4 sequences x 8 KV heads x
-    16,384 tokens x 128, 32 query heads; 3 of its layers), ternary keys and values, one
-    decode query per sequence; sampled units against the oracle."""
+    16,384 tokens x 128, 32 query heads; 3 of its layers), one decode query per sequence;
+    sampled units against the oracle."""
     import torch
     import kv_cache_bit_fwht_amd as K
     w = synth.get("c4", L=3, n_q=1)
     Kx, Vx = synth.gen_kv(w)
     q, _ = synth.gen_queries(w)
     shape = K.Shape(w.B, w.L, w.H, w.T, w.D)
-    kc = vc = _codec(K, "ter")
+    kc, vc = _codec(K, kname), _codec(K, vname)
     kp, vp = K.alloc_packed(kc, shape), K.alloc_packed(vc, shape)
     K.kvq_quantize_pack_kv(to_dev(Kx), to_dev(Vx), kp, vp)
-    announce("m128 decode full-size c4 ternary")
+    announce(f"m128 decode full-size c4 K={kname} V={vname}")
     out, lse = _gpu_decode(K, kp, vp, q, None, path=2)
     G = w.Hq // w.H
-    oc = oracle_codec(K, O, kc)
+    okc, ovc = oracle_codec(K, O, kc), oracle_codec(K, O, vc)
     for (b, l, h) in [(0, 0, 0), (3, 2, 7), (1, 1, 4)]:
         ku, vu = Kx[b, l, h][None, None, None], Vx[b, l, h][None, None, None]
-        wk, sk, zk = O.quantize_pack(ku, oc)
-        wv, sv, zv = O.quantize_pack(vu, oc)
-        Kd = O.dequant(wk, sk, zk, oc, ku.shape)[0, 0, 0]
-        Vd = O.dequant(wv, sv, zv, oc, vu.shape)[0, 0, 0]
+        wk, sk, zk = O.quantize_pack(ku, okc)
+        wv, sv, zv = O.quantize_pack(vu, ovc)
+        Kd = O.dequant(wk, sk, zk, okc, ku.shape)[0, 0, 0]
+        Vd = O.dequant(wv, sv, zv, ovc, vu.shape)[0, 0, 0]
         ro, rl, _ = O.attention.attend(q[b, l, 0, h * G:(h + 1) * G].astype(np.float64), Kd, Vd, w.T,
                                        1.0 / np.sqrt(w.D))
         go = out[b, l, 0, h * G:(h + 1) * G].astype(np.float64)
