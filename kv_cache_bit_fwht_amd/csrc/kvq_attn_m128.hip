@@ -81,8 +81,8 @@ template <> struct KTile<MC_TER> { mu2 c; mu2 s; };              // 64 code bits
 template <> struct KTile<MC_SIGN> { uint32_t c; mu2 s; };        // 32 code bits, the same groups
 template <> struct KTile<MC_INT8> { mu4 c0, c1; uint32_t s; };  // 32 code bytes; s: the scale of token 8kq + i % 8
 template <> struct KTile<MC_F16> { mu4 c[4]; };                  // 32 fp16 values
-template <> struct KTile<MC_NF4> { uint32_t c[4]; uint32_t s; };  // 8 codes of each 32-dim chunk; s: the two
-                                                                  // scales of token 8kq + i % 8 (tile 0 only)
+template <> struct KTile<MC_NF4> { mu2 c[2]; uint32_t s; };  // 16 codes of each group (dims 64g + 16kq ..); s:
+                                                             // the two scales of token 8kq + i % 8 (tile 0 only)
 
 // ---- value data for lane (i, kq): dims 8i .. 8i + 7 of tokens 8kq .. 8kq + 7.  (Row
 // scales of int8 tokens are loaded one per lane and shared by DPP broadcasts: eight
@@ -123,7 +123,7 @@ __device__ __forceinline__ MOffsets m_offsets(int i, int kq) {
     else if constexpr (KC == MC_SIGN) { o.k[u] = r * 16 + 4 * kq; o.ks[u] = (r * 16 + 4 * kq) * 2; }
     else if constexpr (KC == MC_INT8) { o.k[u] = r * 128 + 32 * kq; o.ks[u] = (8 * kq + (i & 7)) * 2; }
     else if constexpr (KC == MC_F16) { o.k[u] = r * 256 + 64 * kq; o.ks[u] = 0; }
-    else { o.k[u] = r * 64 + 4 * kq; o.ks[u] = (8 * kq + (i & 7)) * 4; }
+    else { o.k[u] = r * 64 + 8 * kq; o.ks[u] = (8 * kq + (i & 7)) * 4; }
   }
   const uint32_t t = 8 * kq;
   if constexpr (VC == MC_TER) { o.v = t * 32 + 2 * i; o.vs = (t * 16 + i) * 2; }
@@ -194,10 +194,8 @@ __device__ __forceinline__ void m_load(const M128Args& a, size_t rb, const MOffs
       d.k[u].c[2] = ld<mu4, 32>(kb, o.k[u]);
       d.k[u].c[3] = ld<mu4, 48>(kb, o.k[u]);
     } else {
-      d.k[u].c[0] = ld<uint32_t, 0>(kb, o.k[u]);
-      d.k[u].c[1] = ld<uint32_t, 16>(kb, o.k[u]);
-      d.k[u].c[2] = ld<uint32_t, 32>(kb, o.k[u]);
-      d.k[u].c[3] = ld<uint32_t, 48>(kb, o.k[u]);
+      d.k[u].c[0] = ld<mu2, 0>(kb, o.k[u]);
+      d.k[u].c[1] = ld<mu2, 32>(kb, o.k[u]);
       if (u == 0) d.k[0].s = ld<uint32_t>(ksb, o.ks[0]);
     }
   }
@@ -282,20 +280,15 @@ __device__ __forceinline__ mh8 key_operand(const KTile<KC>& t, int c) {
   return __builtin_bit_cast(mh8, r);
 }
 
-// NF4 keys, chunk c (dims 32c + 8kq .. + 7, one group of 64 per two chunks): the levels
-// as fp16 high parts and fp16 remainders (22 significant bits together) from a table of
-// code bytes (two dims) in LDS.
-__device__ __forceinline__ void nf4_operands(const KTile<MC_NF4>& t, int c, const mu2* lut, mh8& hi, mh8& lo) {
-  const uint32_t w = t.c[c];
-  mu4 h, l;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const mu2 e = lut[(w >> (8 * k)) & 0xFFu];
-    h[k] = e.x;
-    l[k] = e.y;
-  }
-  hi = __builtin_bit_cast(mh8, h);
-  lo = __builtin_bit_cast(mh8, l);
+// NF4 keys, MFMA c (0..7) of a tile: group c / 4, lane k-block kq, dims
+// 64(c / 4) + 16kq + 4(c % 4) .. + 3; each dim fills two k-slots, its level's fp16 high
+// part and fp16 remainder (22 significant bits together; the query operand repeats the
+// dim's value in both), read per code byte (two dims) from a table in LDS.
+__device__ __forceinline__ mh8 nf4_operand(const KTile<MC_NF4>& t, int c, const mu2* lut) {
+  const uint32_t w = t.c[c >> 2][(c >> 1) & 1];      // the 8 codes of dims 64g + 16kq + 8((c / 2) % 2) ..
+  const int sh = 16 * (c & 1);                       // its bytes for this MFMA's 4 dims
+  const mu2 e0 = lut[(w >> sh) & 0xFFu], e1 = lut[(w >> (sh + 8)) & 0xFFu];
+  return __builtin_bit_cast(mh8, mu4{e0.x, e0.y, e1.x, e1.y});
 }
 
 // B operand of value chunk c (dim 8i + c) for tokens 4u .. 4u + 3 of the lane's 8.
@@ -331,15 +324,15 @@ __device__ __forceinline__ mh4 value_operand(const VData<VC>& v, int u, int c, u
 template <int KC, int VC>
 __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 : 2) void k_decode_m128(M128Args a) {
   const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
-  // NF4 keys: the block's table of code bytes -> (high parts, remainders) of two levels
+  // NF4 keys: the block's table of code bytes -> (high part, remainder) of two levels
   __shared__ mu2 nf4_lut[KC == MC_NF4 ? 256 : 1];
   if constexpr (KC == MC_NF4) {
     const int b = threadIdx.x;                       // 256 threads, one entry each
     const float l0 = a.nf4[b & 15], l1 = a.nf4[b >> 4];
     const _Float16 h0 = (_Float16)l0, h1 = (_Float16)l1;
     const _Float16 r0 = (_Float16)(l0 - (float)h0), r1 = (_Float16)(l1 - (float)h1);
-    nf4_lut[b] = mu2{(uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
-                     (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16)};
+    nf4_lut[b] = mu2{(uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, r0) << 16),
+                     (uint32_t)__builtin_bit_cast(uint16_t, h1) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16)};
     __syncthreads();
   }
   // the wavefront index through readfirstlane: everything derived from it is known
@@ -358,12 +351,12 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   mu4 qw[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    // NF4 keys: chunk c is dims 32c .. 32c + 31 (k-block kq: 32c + 8kq ..); otherwise the
+    // NF4 keys: dims 64g + 16kq .. + 15 of group g = c / 2 (eight per load); otherwise the
     // lane's chunks are dims 32kq .. 32kq + 31
-    const uint16_t* qp = (KC == MC_NF4) ? qrow - 32 * kq + 32 * c + 8 * kq : qrow + 8 * c;
+    const uint16_t* qp = (KC == MC_NF4) ? qrow - 32 * kq + 64 * (c >> 1) + 16 * kq + 8 * (c & 1) : qrow + 8 * c;
     qw[c] = head_ok ? *reinterpret_cast<const mu4*>(qp) : mu4{0u, 0u, 0u, 0u};
   }
-  mh8 bq[4];
+  mh8 bq[KC == MC_NF4 ? 8 : 4];
   if constexpr (KC == MC_TER || KC == MC_SIGN) {
     // dword m of chunk c: dims (p, p + 16) of the lane's 32, p = 4c + m
 #pragma unroll
@@ -376,6 +369,15 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
         r[m] = __builtin_amdgcn_perm(hi, lo, (p & 1) ? 0x07060302u : 0x05040100u);
       }
       bq[c] = __builtin_bit_cast(mh8, r);
+    }
+  } else if constexpr (KC == MC_NF4) {
+    // MFMA c: dims 64(c / 4) + 16kq + 4(c % 4) .. + 3, each twice (high part, remainder)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const mu4 src = qw[2 * (c >> 2) + ((c >> 1) & 1)];
+      const uint32_t lo = src[2 * (c & 1)], hi = src[2 * (c & 1) + 1];
+      bq[c] = __builtin_bit_cast(mh8, mu4{__builtin_amdgcn_perm(lo, lo, 0x01000100u), __builtin_amdgcn_perm(lo, lo, 0x03020302u),
+                                          __builtin_amdgcn_perm(hi, hi, 0x01000100u), __builtin_amdgcn_perm(hi, hi, 0x03020302u)});
     }
   } else {
 #pragma unroll
@@ -420,10 +422,9 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if constexpr (KC == MC_NF4) {
-          mh8 ahi, alo;
-          nf4_operands(d.k[u], c, nf4_lut, ahi, alo);
-          cq[u][c >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bq[c], cq[u][c >> 1], 0, 0, 0);
-          cq[u][c >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bq[c], cq[u][c >> 1], 0, 0, 0);
+#pragma unroll
+          for (int cc = 2 * c; cc < 2 * c + 2; ++cc)
+            cq[u][cc >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(nf4_operand(d.k[u], cc, nf4_lut), bq[cc], cq[u][cc >> 2], 0, 0, 0);
         } else {
           cq[u][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<KC>(d.k[u], c), bq[c], cq[u][0], 0, 0, 0);
         }
