@@ -1,4 +1,4 @@
-// MFMA decode attention over a packed cache with 3-, 4- or 5-bit signed-absmax keys
+// MFMA decode attention over a packed cache with 2-, 3-, 4- or 5-bit signed-absmax keys
 // (group 128 or 256, any Walsh-Hadamard rotation) and
 // 2- or 4-bit values on an
 // affine grid (signed absmax or the symmetric grid, group >= 64), head_dim 256,
@@ -10,18 +10,16 @@
 // Why MFMA: at 0.39 bytes per cached value, HBM speed leaves about two VALU
 // lane-ops per value, while unpacking plus four grouped-head multiply-adds per
 // key and per value costs four to five.  Both contractions go to the matrix
-// cores; the VALU only unpacks codes (one AND per pair of codes) and runs the
-// softmax.
+// cores; the VALU only unpacks codes and runs the softmax.
 //
 // Per wavefront, 32 tokens per step:
-//  * Q.K^T: v_mfma_f32_16x16x32_f16, A = 16 tokens x 32 dims of key codes as
-//    fp16 subnormals (code c -> c*2^-24, exact), B = the rotated query in fp16
-//    with the 4 heads replicated over the 16 columns, so lane (kg, n) ends with
-//    the logits of head n%4 for tokens 8kg..8kg+7.  Logit = sum over the two
-//    scale groups of s_g * (2^24 C_g - 2^(b-1) sum_g q), times the softmax
-//    scale.  At 4 bits one AND places two codes 16 bits apart (dims e and e+4 of
-//    a word) in their fp16 halves; at other widths each code is cut out with a
-//    bit-field extract and pairs are packed with a shift-or.
+//  * Q.K^T: v_mfma_i32_16x16x64_i8, A = 16 tokens x 64 dims of key codes as
+//    bytes, B = the rotated query as an integer in four 7-bit digits, 4 digits x
+//    4 heads over the 16 columns, so lane (kg, n) ends with digit n/4's exact
+//    integer logits of head n%4 for tokens 8kg..8kg+7.  Logit = sum over the two
+//    scale groups of s_g * (sum of digit * (c - 2^(b-1))), weighted 2^(7 digit)
+//    over the query scale and added over the digit columns, times the softmax
+//    scale.
 //  * online softmax per head against a reference maximum that moves only when a
 //    logit exceeds it by more than 1 (log2 units), so rescaling is rare.
 //  * P.V: v_mfma_f32_4x4x4_16b_f16, 16 blocks of (4 heads x 4 tokens) x
@@ -55,6 +53,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFastD = 256;
 constexpr int kStep = 32;          // tokens per wavefront step
@@ -201,6 +200,51 @@ __device__ __forceinline__ uint32_t key_field(const KeyRun<KB>& r, int pos) {
   return x & ((1u << KB) - 1u);
 }
 
+// The QK product runs on the int8 matrix cores: key codes as bytes (0 .. 2^KB - 1),
+// the query as 7-bit digits of an integer, so every dot product is an
+// exact integer sum.  Four digits (the B operand's 16 columns are 4 digits x 4 heads)
+// carry the rotated fp32 query exactly.  (The fp16 matrix cores align their products by exponent field,
+// so fp16 subnormal codes, the other cheap operand form, lose low bits of the smaller
+// products: up to 1e-4 of the largest, biased, in measurement.)
+// A operand of QK chunk c (0..3) of one tile: 16 bytes per lane, the codes of 16 of
+// the lane's 64 key dims; key_dim gives which, for byte J of the lane's k group kg
+// (the query operand is laid out by the same map).  Chunk c lies in the dims
+// 128 (c >> 1) .. +127 (one key group of 128); run = the lane's 32 dims there.
+template <int KB>
+__device__ __forceinline__ int key_dim(int c, int kg, int J) {
+  const int base = 128 * (c >> 1) + 32 * kg, p = c & 1;
+  if constexpr (KB == 4) return base + 2 * J + p;                  // nibble p of byte J
+  else if constexpr (KB == 2) return base + 16 * ((J >> 2) >> 1) + 4 * (J & 3) + 2 * p + ((J >> 2) & 1);
+  else return base + 16 * p + J;                                   // half p of the run
+}
+template <int KB>
+__device__ __forceinline__ i32x4_t key_bytes(const KeyRun<KB>& r, int p) {
+  u32x4_t b;
+  if constexpr (KB == 4) {                           // byte J = 4j + b of word j: nibble p of its byte b
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = (r.w(j) >> (4 * p)) & 0x0F0F0F0Fu;
+  } else if constexpr (KB == 2) {                    // word 2m + t: fields 2p + t of the bytes of word m
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (r.w(i >> 1) >> (2 * (2 * p + (i & 1)))) & 0x03030303u;
+  } else {                                           // one field per byte, dims 16p .. 16p + 15
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 16 * p + 4 * i;
+      const uint32_t lo = key_field<KB>(r, KB * d0) | (key_field<KB>(r, KB * (d0 + 1)) << 8);
+      const uint32_t hi = key_field<KB>(r, KB * (d0 + 2)) | (key_field<KB>(r, KB * (d0 + 3)) << 8);
+      b[i] = lo | (hi << 16);
+    }
+  }
+  return __builtin_bit_cast(i32x4_t, b);
+}
+
+// x + (x of the lanes 4, 8 and 12 places along in the same row of 16): sums the
+// four digit columns of one query head.
+__device__ __forceinline__ float add_digit_cols(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
+}
+
 // Value of lane j of this lane's 16-lane row (DPP row broadcast); j is a constant after unrolling.
 template <int J>
 __device__ __forceinline__ uint32_t row_bcast_c(uint32_t x) {
@@ -217,12 +261,6 @@ __device__ __forceinline__ uint32_t row_bcast(uint32_t x, int j) {
     case 6: return row_bcast_c<6>(x);
     default: return row_bcast_c<7>(x);
   }
-}
-
-// x + (x of the lane 4 places along in the same row of 16, cyclically): joins the
-// high- and low-part logits of a query head, which sit in columns n and n ^ 4.
-__device__ __forceinline__ float add_row_ror4(float x) {
-  return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
 }
 
 // fp16 value scales of tokens 8kg + k and 8kg + k + 1 (k constant) in this lane's
@@ -274,10 +312,11 @@ template <int NKS, int NVS, int VB, int KB, bool APP = false>
 __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   constexpr int NW = kFastBlock / 64;                // wavefronts per block
   __shared__ __align__(16) float qs[4][kFastD + 16];
-  __shared__ float qsum_s[2][4][3];                 // [part][head][key group] sums of the MFMA query operand; [0][head][2] 1 / query scale
+  __shared__ int qoff_s[4][4][2];                   // [head][digit][key group] sums of the query digits
+  __shared__ float qinv_s[4];                        // [head] 1 / (the head's query scale)
   __shared__ float so[NW][4][kFastD];               // per-wave outputs [wave][head][dim]
   __shared__ float sm[NW][4], sl[NW][4];            // per-wave reference max (log2 units) and sum
-  __shared__ half8_t qbs[8][32];                     // MFMA B operands [chunk][16 part + 4 kg + head]
+  __shared__ i32x4_t qbs[4][4][16];                  // MFMA B operands [chunk][lane group][4 digit + head]
   __shared__ int next_local;                         // next step index of the block not yet handed out
   __shared__ int slot_chunk[kMaxSlots];              // chunk of each slot of C local indices (-1 = not yet known)
   const long long unit = blockIdx.y;                 // (b*L + l)*H + h
@@ -300,7 +339,8 @@ __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
 // and runs the decode compiled for the tile's (key bits, value bits).  Counters, partials,
 // queries, lengths and outputs are indexed over the whole map, so the in-kernel merge
 // writes the final rows.  The pairs compiled in (id, key bits, value bits):
-#define KVQ_MFMA_MIX_PAIRS(X) X(0, 3, 2) X(1, 4, 2) X(2, 5, 2) X(3, 3, 4) X(4, 4, 4) X(5, 5, 4)
+#define KVQ_MFMA_MIX_PAIRS(X) \
+  X(0, 3, 2) X(1, 4, 2) X(2, 5, 2) X(3, 3, 4) X(4, 4, 4) X(5, 5, 4) X(6, 2, 2) X(7, 2, 4)
 
 struct MfmaTile {
   const uint8_t* kc;
@@ -323,10 +363,11 @@ struct FMixArgs {
 
 struct MfmaLds {                   // the LDS of one block (as k_decode_mfma declares it)
   alignas(16) float qs[4][kFastD + 16];
-  float qsum_s[2][4][3];
+  int qoff_s[4][4][2];
+  float qinv_s[4];
   float so[kFastBlock / 64][4][kFastD];
   float sm[kFastBlock / 64][4], sl[kFastBlock / 64][4];
-  half8_t qbs[8][32];
+  i32x4_t qbs[4][4][16];
   int next_local;
   int slot_chunk[kMaxSlots];
 };
@@ -337,7 +378,8 @@ __device__ __forceinline__ void mfma_tile_unit(const FArgs& a, MfmaLds& S, int h
   constexpr int NKS = 2, NVS = 2;                    // key and value group 128
   constexpr int NW = kFastBlock / 64;
   auto& qs = S.qs;
-  auto& qsum_s = S.qsum_s;
+  auto& qoff_s = S.qoff_s;
+  auto& qinv_s = S.qinv_s;
   auto& so = S.so;
   auto& sm = S.sm;
   auto& sl = S.sl;
@@ -429,10 +471,8 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   if (Hq / s.heads > 4) return false;
   if (k.codec.codebook != KVQ_INT_ABSMAX) return false;
   const int kb = k.codec.bits;
-  // 6- and 8-bit keys need more registers than two wavefronts per SIMD leave (scratch
-  // spills); 2-bit keys came out with logit errors of ~1e-4 here (4x those of 4-bit keys,
-  // over the 1e-4 lse bar), so they stay on the general kernel
-  if (kb < 3 || kb > 5) return false;
+  // 6- and 8-bit keys need more registers than two wavefronts per SIMD leave (scratch spills)
+  if (kb < 2 || kb > 5) return false;
   if (k.codec.group != 128 && k.codec.group != 256) return false;
   // 2- or 4-bit values: signed absmax (levels c - 2^(b-1)) or the symmetric grid (levels c - (2^b - 1)/2)
   if (v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) return false;
@@ -661,6 +701,7 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_
   const long long units = (long long)s.batch * s.layers * s.heads;
   const dim3 grid(a.blocks_per_unit, (unsigned)units, (unsigned)pr.n_q);
   switch (k.codec.bits) {
+    case 2: launch_mfma_k<2>(a, vb, grid, st); break;
     case 3: launch_mfma_k<3>(a, vb, grid, st); break;
     case 4: launch_mfma_k<4>(a, vb, grid, st); break;
     default: launch_mfma_k<5>(a, vb, grid, st); break;

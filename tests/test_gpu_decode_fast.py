@@ -1,9 +1,10 @@
-"""GPU parity of the MFMA decode-attention kernel (3-, 4- or 5-bit keys, 2- or
+"""GPU parity of the MFMA decode-attention kernel (2-, 3-, 4- or 5-bit keys, 2- or
 4-bit values, head_dim 256) against the CPU oracle, and against the general kernel.
 
 Bar: outputs within 2e-3 relative L2 per row, lse within 1e-4 absolute.  The
-rotated query enters the matrix cores as an fp16 high part plus an fp16
-remainder (about 22 bits), and the P.V weights as fp16 (2^-11 relative per
+rotated query enters the int8 matrix cores as an integer (four 7-bit digits, the
+fp32 query exactly) against the key codes as bytes, so QK is exact up to the
+query's fp32 rotation; the P.V weights enter as fp16 (2^-11 relative per
 weight), which sets the output error (a few 1e-4 at most).
 """
 import numpy as np
@@ -43,7 +44,8 @@ def test_fast_c3_shape_shrunk():
 @pytest.mark.parametrize("variant", ["kgroup256", "vgroup64", "vgroup256", "rot128", "norot", "G2", "G1",
                                      "vrot", "vsym", "vsym_rot", "v4", "v4_g64", "v4_g256_k256", "v4_rot",
                                      "v4_sym", "v4_sym_rot", "v4_G1", "k3", "k5", "k3_v4", "k5_v4",
-                                     "k5_v4_g64", "k3_kg256_rot128", "k5_norot_G2", "k3_v4_rot"])
+                                     "k5_v4_g64", "k3_kg256_rot128", "k5_norot_G2", "k3_v4_rot", "k2", "k2_v4",
+                                     "k2_norot_G2", "k2_kg256_rot128", "k2_v4_rot"])
 def test_fast_variants(variant):
     import kv_cache_bit_fwht_amd as K
     kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
@@ -96,6 +98,17 @@ def test_fast_variants(variant):
         kc = K.Codec(K.INT_ABSMAX, 5, 128, 0)
     elif variant == "k3_v4_rot":
         kc, vc = K.Codec(K.INT_ABSMAX, 3, 256, 256), K.Codec(K.INT_ABSMAX, 4, 128, 256)
+    elif variant == "k2":
+        kc = K.Codec(K.INT_ABSMAX, 2, 128, 256)
+    elif variant == "k2_v4":
+        kc, vc = K.Codec(K.INT_ABSMAX, 2, 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0)
+    elif variant == "k2_norot_G2":
+        w = w.with_sizes(Hq=8)
+        kc = K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    elif variant == "k2_kg256_rot128":
+        kc = K.Codec(K.INT_ABSMAX, 2, 256, 128)
+    elif variant == "k2_v4_rot":
+        kc, vc = K.Codec(K.INT_ABSMAX, 2, 128, 256), K.Codec(K.INT_ABSMAX, 4, 64, 256)
     announce(f"mfma variant {variant}")
     _case(K, w, kc, vc)
 
@@ -127,13 +140,13 @@ def test_fast_4bit_values_many_blocks_and_lengths():
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0), kv_len)
 
 
-def test_fast_3_and_5_bit_keys_many_blocks_and_lengths():
-    """3- and 5-bit keys (fields cut across word boundaries): 32 blocks per unit on a
-    counter, causal lengths ending mid-step."""
+def test_fast_2_3_and_5_bit_keys_many_blocks_and_lengths():
+    """2-, 3- and 5-bit keys (3 and 5: fields cut across word boundaries): 32 blocks per
+    unit on a counter, causal lengths ending mid-step."""
     import kv_cache_bit_fwht_amd as K
     w = synth.get("c3", L=1, T=16384, n_q=3)
     kv_len = np.array([[[16384, 9001, 31]]], dtype=np.int32)
-    for kb in (3, 5):
+    for kb in (2, 3, 5):
         announce(f"mfma {kb}-bit keys, many blocks per unit")
         _case(K, w, K.Codec(K.INT_ABSMAX, kb, 128, 256), K.Codec(K.INT_ABSMAX, 4, 128, 0), kv_len)
 
@@ -159,16 +172,27 @@ def test_fast_static_chunks_many_rows():
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0))
 
 
-def test_fast_rejects_2_bit_keys():
+@pytest.mark.parametrize("kb", [2, 3, 4, 5])
+@pytest.mark.parametrize("rot", [0, 256])
+def test_fast_single_token_logits(kb, rot):
+    """With one attended key the lse is that key's logit: the QK product on the int8
+    matrix cores (query as an exact integer, codes as bytes) leaves only the query's
+    rotation in fp32 and the final scaling, so single logits sit well inside the lse
+    bar (3e-6 here; the fp16 matrix cores with fp16 subnormal codes left up to 2e-4)."""
     import kv_cache_bit_fwht_amd as K
-    w = synth.get("c3", L=1, T=64, n_q=1)
+    w = synth.get("c3", L=1, T=640, n_q=8)
+    kv_len = np.tile(np.array([1, 1, 2, 3, 5, 8, 1, 1], np.int32), (w.B, w.L, 1))
+    kc, vc = K.Codec(K.INT_ABSMAX, kb, 128, rot), K.Codec(K.INT_ABSMAX, 2, 128, 0)
     Kx, Vx = synth.gen_kv(w)
     q, _ = synth.gen_queries(w)
-    kp = _gpu_pack(K, Kx, K.Codec(K.INT_ABSMAX, 2, 128, 256))
-    vp = _gpu_pack(K, Vx, K.Codec(K.INT_ABSMAX, 2, 128, 0))
-    announce("mfma rejects 2-bit keys")
-    with pytest.raises(K.KvqError):
-        _gpu_decode(K, kp, vp, q, None, path=2)
+    kp, vp = _gpu_pack(K, Kx, kc), _gpu_pack(K, Vx, vc)
+    _, Kd, Vd = _oracle(Kx, Vx, oracle_codec(K, O, kc), oracle_codec(K, O, vc), q, kv_len)
+    announce(f"mfma single-token logits kb={kb} rot={rot}")
+    _, lse = _gpu_decode(K, kp, vp, q, kv_len, path=2)
+    _, ref_lse = O.decode_attn(q, Kd, Vd, kv_len)
+    err = np.abs(lse - ref_lse).max()
+    print(f"max lse error {err:.2e}")
+    assert err < 3e-6
 
 
 def test_fast_rejects_unsupported_and_auto_falls_back():

@@ -154,7 +154,7 @@ def test_decode_over_segments(variant):
 
 
 MAPS = ["alloc_319", "heads_entropy", "anchor_layer", "g8_heads", "mfma_tile", "mfma_map_heads", "mfma_map_layers",
-        "mfma_map_g2", "wave_map_g1"]
+        "mfma_map_g2", "mfma_map_k2", "wave_map_g1"]
 
 
 @pytest.mark.parametrize("path", [None, 1, 2])
@@ -238,6 +238,15 @@ def test_codec_map_in_one_launch(variant, path):
         layout = [(K.Codec(A, 5, 128, 256), K.Codec(A, 2, 128, 0), 0, 2, 0, 384, 0, 3),
                   (K.Codec(A, 3, 128, 256), K.Codec(A, 4, 128, 256), 0, 2, 0, 384, 3, 1)]
         mean_seg = 1
+    elif variant == "mfma_map_k2":
+        # 2-bit keys (over 2- and 4-bit values) beside 4-bit keys, all MFMA pairs: one launch
+        w = synth.get("c3", L=3, T=352, n_q=2)
+        Kx, Vx = synth.gen_kv(w)
+        q, _ = synth.gen_queries(w)
+        kv_len = np.array([[[352, 33], [0, 351], [200, 1]]], dtype=np.int32)
+        layout = [(K.Codec(A, 2, 128, 256), K.Codec(A, 2, 128, 0), 0, 1, 0, 352),
+                  (K.Codec(A, 2, 128, 0), K.Codec(A, 4, 128, 256), 1, 1, 0, 352),
+                  (K.Codec(A, 4, 128, 256), K.Codec(A, 2, 128, 0), 2, 1, 0, 352)]
     elif variant == "wave_map_g1":
         # one query head per KV head on the general codec map: four query rows share a
         # wavefront, each with its own key count
