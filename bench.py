@@ -885,7 +885,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 MFMA operands, fp32 accumulation (codec: fp32)",
+        "dtype": "decode: int8 MFMA for QK (exact integer sums), fp16 MFMA for PV with fp32 accumulation; codec: fp32",
         "data": "synthetic (seeded fp16 K/V with outlier channels, N(0,1) queries)",
         "config": {"workload": f"{'64K' if w.T == 65536 else str(w.T)} decode: B=1 L=8 H=4 T={w.T} D=256, Hq=16 (GQA 4:1), "
                                "K FWHT-256 int4 absmax g128, V int2 absmax g128 (3.125 bpv), "
