@@ -731,6 +731,53 @@ def allocation_workload(reps):
             **{k: round(v * 1e6, 1) for k, v in t.items()}}), flush=True)
 
 
+TIMELINE_SLOTS = ["entry", "query prologue done", "after prologue barrier", "loop end", "wavefront reduced",
+                  "after block barrier", "partial stores issued", "partial stores complete", "block counted",
+                  "last block: merge tables in", "merge end"]
+
+
+def decode_timeline(K, torch, call, w):
+    """One decode call on the profiling build: the clock stamps of every wavefront
+    ([block][wave][slot], 100 MHz), as percentiles per slot from the first entry, and the
+    spreads that make the fixed cost of a call."""
+    n = 4096 * 8 * 16
+    K.kvq_timeline_read(n)                             # clears what the warm-up left
+    call()
+    torch.cuda.synchronize()
+    ts = K.kvq_timeline_read(n).reshape(4096, 8, 16).astype(np.int64)
+    used = ts[:, :, 0] > 0
+    nblk = int(used.any(axis=1).sum())
+    if nblk == 0:
+        raise RuntimeError("no stamps: the call did not take the MFMA decode")
+    ts = ts[:nblk]
+    t0 = ts[:, :, 0][ts[:, :, 0] > 0].min()
+    us = lambda x: (x - t0) * 0.01                     # 100 MHz clock
+    units = int((ts[:, 0, 10] > 0).sum())             # one merging block per unit
+    bpu = nblk // max(units, 1)
+    pct = lambda v: {"min": round(float(np.min(v)), 2), "p10": round(float(np.percentile(v, 10)), 2),
+                     "p50": round(float(np.percentile(v, 50)), 2), "p90": round(float(np.percentile(v, 90)), 2),
+                     "max": round(float(np.max(v)), 2)}
+    slots = {}
+    for i, name in enumerate(TIMELINE_SLOTS):
+        v = ts[:, :, i][ts[:, :, i] > 0]
+        if v.size:
+            slots[name] = dict(pct(us(v)), n=int(v.size))
+    loop_end = us(ts[:, :, 3])                         # [block][wave]
+    wave_spread = loop_end.max(axis=1) - loop_end.min(axis=1)
+    blk_end = loop_end.max(axis=1).reshape(units, bpu)
+    merge_end = us(ts[:, :, 10].max(axis=1)).reshape(units, bpu).max(axis=1)
+    rec = {"timeline": "64K decode, one call, per-wavefront s_memrealtime stamps (us from the first entry)",
+           "blocks": nblk, "units": units, "blocks_per_unit": bpu, "slots": slots,
+           "wave_loop_end_spread_in_block_us": pct(wave_spread),
+           "block_loop_end_spread_in_unit_us": pct(blk_end.max(axis=1) - blk_end.min(axis=1)),
+           "merge_end_after_unit_last_loop_end_us": pct(merge_end - blk_end.max(axis=1)),
+           "kernel_span_us": round(float(us(ts[ts > 0].max())), 2)}
+    for name, v in slots.items():
+        log(f"{name:30s} n={v['n']:5d} min {v['min']:7.2f} p10 {v['p10']:7.2f} p50 {v['p50']:7.2f} "
+            f"p90 {v['p90']:7.2f} max {v['max']:7.2f} us")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -753,6 +800,10 @@ def main():
                          "c3h: per-head key bits from attention entropy, as head segments; "
                          "c2a: the per-layer 3.19-bit allocation on the proxy-query probe")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions per arm (c4/c5)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="c3 only: load the profiling build (libkvq_timeline.so, from build.py --timeline), "
+                         "run one 64K decode call and print its per-wavefront clock timeline instead of the "
+                         "bench line")
     ap.add_argument("--tokens", type=int, default=None,
                     help="c3 only: tokens per (layer, KV head) instead of 65,536 (a multiple of 32), to see how "
                          "the per-call fixed costs amortise; the headline line is the default")
@@ -778,6 +829,8 @@ def main():
         secondary(args.workload, args.reps)
         return
 
+    if args.timeline:
+        os.environ["KVQ_TIMELINE"] = "1"
     import torch
     import kv_cache_bit_fwht_amd as K
     import synth
@@ -855,6 +908,10 @@ def main():
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
+    if args.timeline:
+        decode_timeline(K, torch, lambda: K.kvq_decode_attn(copies[0][0], copies[0][1], w.Hq, 1, q_ptrs[0], None,
+                                                           0.0, out_p, lse_p, ws_p, wsb, sh, path), w)
+        return
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} step(s) of quantize+pack + {nq} decode calls")
     torch.cuda.synchronize()

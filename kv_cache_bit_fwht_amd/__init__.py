@@ -14,7 +14,9 @@ import dataclasses
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_TIMELINE=1 selects the profiling build (per-wavefront clock stamps in the MFMA
+# decode, kvq_timeline_read); the results are the same
+LIB_PATH = os.path.join(_HERE, "libkvq_timeline.so" if os.environ.get("KVQ_TIMELINE") == "1" else "libkvq.so")
 
 # codebooks (kvq_codebook)
 FP16, INT_ABSMAX, INT_MINMAX, TERNARY, SIGN, NF4, INT8_SYM, RFFT_POLAR, RFFT_CART, INT_SYM, LLOYD = range(11)
@@ -112,6 +114,9 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
+    if hasattr(lib, "kvq_timeline_read"):              # the profiling build only
+        lib.kvq_timeline_read.argtypes = [P, SZ]
+        lib.kvq_timeline_read.restype = I32
     return lib
 
 
@@ -355,6 +360,18 @@ def kvq_append_decode_attn(k_new, v_new, token0: int, n_new: int, k: Packed, v: 
 
 
 STATIC_SCRATCH_BYTES = 16 << 20      # KVQ_STATIC_SCRATCH_BYTES of kvq.h
+
+
+def kvq_timeline_read(count: int):
+    """The MFMA decode's clock stamps ([block][wave][slot], uint64), then cleared; only in
+    the profiling build (KVQ_TIMELINE=1 with libkvq_timeline.so)."""
+    import numpy as np
+    if not hasattr(_lib, "kvq_timeline_read"):
+        raise RuntimeError(f"{LIB_PATH} is not the timeline build (build it with `build.py --timeline`, "
+                           "load it with KVQ_TIMELINE=1)")
+    dst = np.zeros(count, dtype=np.uint64)
+    _check("kvq_timeline_read", _lib.kvq_timeline_read(dst.ctypes.data, count))
+    return dst
 
 
 def kvq_decode_attn_static(k: Packed, v: Packed, q_heads: int, n_q: int, q, kv_len, sm_scale: float, out, lse,

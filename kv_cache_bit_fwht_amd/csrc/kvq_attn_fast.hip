@@ -56,6 +56,26 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFastD = 256;
+
+// Timeline build (-DKVQ_TIMELINE, libkvq_timeline.so): lane 0 of every wavefront of the
+// first kTimelineBlocks blocks records s_memrealtime (a 100 MHz clock) at fixed points of
+// the MFMA decode, read back with kvq_timeline_read.  The default build compiles the
+// stamps out.
+constexpr int kTimelineBlocks = 4096;
+constexpr int kTimelineSlots = 16;
+#ifdef KVQ_TIMELINE
+__device__ unsigned long long g_kvq_timeline[kTimelineBlocks * 8 * kTimelineSlots];
+#define KVQ_STAMP(slot)                                                                                    \
+  do {                                                                                                     \
+    const unsigned long long t_ = __builtin_amdgcn_s_memrealtime();                                        \
+    const long long b_ = blockIdx.x + (long long)gridDim.x * (blockIdx.y + (long long)gridDim.y * blockIdx.z); \
+    if (lane == 0 && b_ < kTimelineBlocks) g_kvq_timeline[(b_ * 8 + wave) * kTimelineSlots + (slot)] = t_; \
+  } while (0)
+#else
+#define KVQ_STAMP(slot) \
+  do {                  \
+  } while (0)
+#endif
 constexpr int kStep = 32;          // tokens per wavefront step
 constexpr int kFastBlock = 512;    // threads per block: two wavefronts per SIMD
 constexpr int kMaxChunks = 256;    // chunks per (query row, KV head) at most
@@ -734,3 +754,16 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_
 }
 
 }  // namespace kvq
+
+#ifdef KVQ_TIMELINE
+#include "kvq_timeline.h"
+extern "C" kvq_status kvq_timeline_read(unsigned long long* dst, size_t count) {
+  const size_t n = (size_t)kvq::kTimelineBlocks * 8 * kvq::kTimelineSlots;
+  if (!dst || count > n) return KVQ_ERR_ARG;
+  if (hipMemcpyFromSymbol(dst, HIP_SYMBOL(kvq::g_kvq_timeline), count * sizeof(unsigned long long)) != hipSuccess)
+    return KVQ_ERR_HIP;
+  static unsigned long long zeros[kvq::kTimelineBlocks * 8 * kvq::kTimelineSlots];
+  if (hipMemcpyToSymbol(HIP_SYMBOL(kvq::g_kvq_timeline), zeros, sizeof(zeros)) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+#endif

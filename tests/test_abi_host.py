@@ -56,6 +56,17 @@ def test_library_exports_every_declared_entry_point(K):
     assert sorted(K.EXPORTS) == declared, "the Python binding must mirror the header one to one"
 
 
+def test_timeline_entry_point_only_in_the_profiling_build(K):
+    """kvq_timeline_read is declared in its own header and exported only by the
+    profiling build (libkvq_timeline.so); the default library keeps the stamps out."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kvq_timeline.h")).read(), flags=re.S)
+    assert re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", text) == ["kvq_timeline_read"]
+    assert not hasattr(ctypes.CDLL(os.path.join(os.path.dirname(K.LIB_PATH), "libkvq.so")), "kvq_timeline_read")
+    tl = os.path.join(os.path.dirname(K.LIB_PATH), "libkvq_timeline.so")
+    if os.path.exists(tl):
+        assert hasattr(ctypes.CDLL(tl), "kvq_timeline_read")
+
+
 def test_status_strings_and_version(K):
     assert K.kvq_version().startswith("kvq")
     for st in (OK, ERR_ARG, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, -5):
