@@ -33,9 +33,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
 KERNEL_SRC = {"decode": ["kv_cache_bit_fwht_amd/csrc/kvq_attn_fast.hip", "kv_cache_bit_fwht_amd/csrc/kvq_mfma_body.inc",
-                         "kv_cache_bit_fwht_amd/csrc/kvq_attn.hip", "kv_cache_bit_fwht_amd/csrc/kvq_quant256.hpp"],
+                         "kv_cache_bit_fwht_amd/csrc/kvq_attn.hip", "kv_cache_bit_fwht_amd/csrc/kvq_quant256.hpp",
+                         "kv_cache_bit_fwht_amd/csrc/kvq_internal.hpp"],
               "quantize": ["kv_cache_bit_fwht_amd/csrc/kvq_quant.hip", "kv_cache_bit_fwht_amd/csrc/kvq_codec.hpp",
-                           "kv_cache_bit_fwht_amd/csrc/kvq_quant256.hpp"]}
+                           "kv_cache_bit_fwht_amd/csrc/kvq_quant256.hpp", "kv_cache_bit_fwht_amd/csrc/kvq_internal.hpp"]}
 
 
 def log(msg):

@@ -265,24 +265,6 @@ __device__ __forceinline__ float add_digit_cols(float x) {
   return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
 }
 
-// Sum / maximum of x over the four 16-lane rows (lanes l, l^16, l^32, l^48), in every
-// lane: the row swaps of v_permlane32_swap and v_permlane16_swap move whole rows between
-// two registers in the VALU, where a lane shuffle would go through the LDS crossbar.
-__device__ __forceinline__ float f_bits(uint32_t x) { return __builtin_bit_cast(float, x); }
-__device__ __forceinline__ uint32_t u_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ float sum_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(u_bits(x), u_bits(x), false, false);
-  const float y = f_bits(a[0]) + f_bits(a[1]);       // x + x of lane l^32
-  const auto b = __builtin_amdgcn_permlane16_swap(u_bits(y), u_bits(y), false, false);
-  return f_bits(b[0]) + f_bits(b[1]);                // y + y of lane l^16
-}
-__device__ __forceinline__ float max_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(u_bits(x), u_bits(x), false, false);
-  const float y = __builtin_fmaxf(f_bits(a[0]), f_bits(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(u_bits(y), u_bits(y), false, false);
-  return __builtin_fmaxf(f_bits(b[0]), f_bits(b[1]));
-}
-
 // Value of lane j of this lane's 16-lane row (DPP row broadcast); j is a constant after unrolling.
 template <int J>
 __device__ __forceinline__ uint32_t row_bcast_c(uint32_t x) {

@@ -392,9 +392,7 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
 #pragma unroll
       for (int e = 0; e < 8; ++e) qs += (float)v[e];
     }
-    qs += __shfl_xor(qs, 16);
-    qs += __shfl_xor(qs, 32);
-    koff = 127.0f * qs;
+    koff = 127.0f * sum_rows(qs);
   }
   // ---- token range of this split: steps [k0, k1), tokens below t_hi
   int n = a.T;
@@ -462,6 +460,7 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
     float mt = lg[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) mt = fmaxf(mt, lg[k]);
+    // (lane shuffles through the LDS crossbar here: this loop's VALU is the busy unit)
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const bool grow = mt > m_ref + 1.0f;
@@ -548,12 +547,8 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
     }
   }
   // ---- the wavefront's partial per query head
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
-  if constexpr (VC == MC_INT8 || VC == MC_I4) {
-    w_part += __shfl_xor(w_part, 16);
-    w_part += __shfl_xor(w_part, 32);
-  }
+  l_part = sum_rows(l_part);
+  if constexpr (VC == MC_INT8 || VC == MC_I4) w_part = sum_rows(w_part);
   // lane r (< 4) holds head r's m and l; lanes 0-15 hold rows 0-3 (heads) of the outputs
   // the weight sum of output row 4kq + r (int8: rows 0-3; 4-bit values: rows 0-7)
   const float wp0 = __shfl(w_part, 4 * kq), wp1 = __shfl(w_part, 4 * kq + 1);

@@ -288,4 +288,23 @@ int decode_wave_split_count(const kvq_shape& s, int Hq, int n_q);
 bool m128_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
 hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st);
 
+// Sum / maximum of x over the four 16-lane rows (lanes l, l^16, l^32, l^48), in every
+// lane: the row swaps of v_permlane32_swap and v_permlane16_swap move whole rows between
+// two registers in the VALU, where a lane shuffle would go through the LDS crossbar.
+__device__ __forceinline__ float f_bits(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t u_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float sum_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(u_bits(x), u_bits(x), false, false);
+  const float y = f_bits(a[0]) + f_bits(a[1]);       // x + x of lane l^32
+  const auto b = __builtin_amdgcn_permlane16_swap(u_bits(y), u_bits(y), false, false);
+  return f_bits(b[0]) + f_bits(b[1]);                // y + y of lane l^16
+}
+__device__ __forceinline__ float max_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(u_bits(x), u_bits(x), false, false);
+  const float y = __builtin_fmaxf(f_bits(a[0]), f_bits(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(u_bits(y), u_bits(y), false, false);
+  return __builtin_fmaxf(f_bits(b[0]), f_bits(b[1]));
+}
+
+
 }  // namespace kvq
