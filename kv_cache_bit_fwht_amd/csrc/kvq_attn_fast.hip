@@ -1,7 +1,8 @@
 // MFMA decode attention over a packed cache with 2-, 3-, 4- or 5-bit signed-absmax keys
 // (group 128 or 256, any Walsh-Hadamard rotation) and
 // 2- or 4-bit values on an
-// affine grid (signed absmax or the symmetric grid, group >= 64), head_dim 256,
+// affine grid (signed absmax or the symmetric grid, group >= 64) or 2-bit Gaussian
+// Lloyd-Max values ([E22L] Result: the next test, on rotated values), head_dim 256,
 // up to 4 query heads per KV head: the 64K-token decode workload of [E22L] ("Can
 // 4-bit keys and 2-bit values hit a 1M-token memory budget?", What I tested: arm
 // A, rotated 4-bit keys and 2-bit values at group 128), and the same cache with
@@ -99,6 +100,8 @@ struct FArgs {
   float vkappa;
   float sm_scale;
   float voff;                      // value code offset: 2 (signed absmax, c - 2) or 1.5 (symmetric grid, c - 1.5)
+  uint32_t vlut_lo, vlut_hi;       // 2-bit Lloyd-Max values: low and high bytes of the four levels in fp16
+  int vll;                         // 1: 2-bit Lloyd-Max values (levels from vlut, no offset)
   int blocks_per_unit;             // blocks (and partials) per (query row, KV head)
   int chunk_log2;                  // log2 of the 32-token steps per chunk (>= 3)
   int* ctr;                        // per (query row, KV head) chunk counters, or null (static chunks)
@@ -328,7 +331,7 @@ __device__ __forceinline__ int claim_global(int* ctr) {
 // wavefronts that share a SIMD do not run at the same speed (the older one is
 // issued first), so the block's 32-token steps are handed out dynamically from an
 // LDS counter instead of being split evenly in advance.
-template <int NKS, int NVS, int VB, int KB, bool APP = false>
+template <int NKS, int NVS, int VB, int KB, bool APP = false, bool LL = false>
 __global__ __launch_bounds__(kFastBlock, 1) void k_decode_mfma(FArgs a) {
   constexpr int NW = kFastBlock / 64;                // wavefronts per block
   __shared__ __align__(16) float qs[4][kFastD + 16];
@@ -407,6 +410,7 @@ __device__ __forceinline__ void mfma_tile_unit(const FArgs& a, MfmaLds& S, int h
   int& next_local = S.next_local;
   auto& slot_chunk = S.slot_chunk;
   constexpr bool APP = false;
+  constexpr bool LL = false;
 #include "kvq_mfma_body.inc"
 }
 
@@ -495,7 +499,12 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   if (kb < 2 || kb > 5) return false;
   if (k.codec.group != 128 && k.codec.group != 256) return false;
   // 2- or 4-bit values: signed absmax (levels c - 2^(b-1)) or the symmetric grid (levels c - (2^b - 1)/2)
-  if (v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) return false;
+  // affine 2- and 4-bit value grids, and 2-bit Lloyd-Max levels (a four-entry table)
+  if (v.codec.codebook == KVQ_LLOYD) {
+    if (v.codec.bits != 2) return false;
+  } else if (v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) {
+    return false;
+  }
   if (v.codec.bits != 2 && v.codec.bits != 4) return false;
   if (v.codec.group < 64) return false;   // a P.V block's 4 value words share one scale group
   if (v.chan_scale) return false;
@@ -532,6 +541,20 @@ size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q) {
 
 template <int VB, int KB>
 static void launch_mfma(const FArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (VB == 2) {
+    if (a.vll) {                                     // 2-bit Lloyd-Max values
+      if (a.nks == 2) {
+        if (a.nvs == 1) k_decode_mfma<2, 1, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        else if (a.nvs == 2) k_decode_mfma<2, 2, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        else k_decode_mfma<2, 4, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+      } else {
+        if (a.nvs == 1) k_decode_mfma<1, 1, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        else if (a.nvs == 2) k_decode_mfma<1, 2, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        else k_decode_mfma<1, 4, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+      }
+      return;
+    }
+  }
   if constexpr (KB == 4) {
     if (a.app_n > 0) {                               // the fused-append instances
       if (a.nks == 2) {
@@ -599,6 +622,7 @@ bool mixed_fast_supported(const kvq_segment* segs, int n, int layers, int heads,
     if (segs[i].token0 != 0 || k.shape.tokens != tokens) return false;
     if (!fast_decode_supported(k, v, k.shape.heads * G)) return false;
     if (k.codec.group != 128 || v.codec.group != 128) return false;
+    if (v.codec.codebook == KVQ_LLOYD) return false;    // affine value grids only
     if (mfma_mix_pair(k.codec.bits, v.codec.bits) < 0) return false;
   }
   return true;
@@ -694,6 +718,16 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_
   a.sm_scale = pr.sm_scale;
   const int vb = v.codec.bits;
   a.voff = (v.codec.codebook == KVQ_INT_SYM) ? 0.5f * (float)((1 << vb) - 1) : (float)(1 << (vb - 1));
+  if (v.codec.codebook == KVQ_LLOYD) {               // levels rounded to fp16, as the matrix cores take them
+    a.vll = 1;
+    a.voff = 0.0f;
+    a.vlut_lo = a.vlut_hi = 0;
+    for (int c = 0; c < 4; ++c) {
+      const uint16_t hb = __builtin_bit_cast(uint16_t, (_Float16)host_tables().lloyd_lv[0][c]);
+      a.vlut_lo |= (uint32_t)(hb & 0xFFu) << (8 * c);
+      a.vlut_hi |= (uint32_t)(hb >> 8) << (8 * c);
+    }
+  }
   a.blocks_per_unit = fast_blocks_per_unit(s, pr.n_q);
   a.chunk_log2 = fast_chunk_log2(s);
   // shared chunk counters when the rows fit the workspace's counter region

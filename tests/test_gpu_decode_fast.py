@@ -1,5 +1,6 @@
 """GPU parity of the MFMA decode-attention kernel (2-, 3-, 4- or 5-bit keys, 2- or
-4-bit values, head_dim 256) against the CPU oracle, and against the general kernel.
+4-bit affine values or 2-bit Lloyd-Max values, head_dim 256) against the CPU oracle,
+and against the general kernel.
 
 Bar: outputs within 2e-3 relative L2 per row, lse within 1e-4 absolute.  The
 rotated query enters the int8 matrix cores as an integer (four 7-bit digits, the
@@ -45,7 +46,9 @@ def test_fast_c3_shape_shrunk():
                                      "vrot", "vsym", "vsym_rot", "v4", "v4_g64", "v4_g256_k256", "v4_rot",
                                      "v4_sym", "v4_sym_rot", "v4_G1", "k3", "k5", "k3_v4", "k5_v4",
                                      "k5_v4_g64", "k3_kg256_rot128", "k5_norot_G2", "k3_v4_rot", "k2", "k2_v4",
-                                     "k2_norot_G2", "k2_kg256_rot128", "k2_v4_rot"])
+                                     "k2_norot_G2", "k2_kg256_rot128", "k2_v4_rot", "vlloyd", "vlloyd_rot",
+                                     "vlloyd_g64", "vlloyd_g256_k256", "vlloyd_k3_G1", "vlloyd_k2_rot128",
+                                     "vlloyd_k5_G2"])
 def test_fast_variants(variant):
     import kv_cache_bit_fwht_amd as K
     kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
@@ -109,6 +112,22 @@ def test_fast_variants(variant):
         kc = K.Codec(K.INT_ABSMAX, 2, 256, 128)
     elif variant == "k2_v4_rot":
         kc, vc = K.Codec(K.INT_ABSMAX, 2, 128, 256), K.Codec(K.INT_ABSMAX, 4, 64, 256)
+    elif variant == "vlloyd":
+        vc = K.Codec(K.LLOYD, 2, 128, 0)
+    elif variant == "vlloyd_rot":
+        vc = K.Codec(K.LLOYD, 2, 128, 256)
+    elif variant == "vlloyd_g64":
+        vc = K.Codec(K.LLOYD, 2, 64, 256)
+    elif variant == "vlloyd_g256_k256":
+        kc, vc = K.Codec(K.INT_ABSMAX, 4, 256, 256), K.Codec(K.LLOYD, 2, 256, 256)
+    elif variant == "vlloyd_k3_G1":
+        w = w.with_sizes(Hq=4)
+        kc, vc = K.Codec(K.INT_ABSMAX, 3, 128, 256), K.Codec(K.LLOYD, 2, 128, 256)
+    elif variant == "vlloyd_k2_rot128":
+        kc, vc = K.Codec(K.INT_ABSMAX, 2, 128, 128), K.Codec(K.LLOYD, 2, 128, 128)
+    elif variant == "vlloyd_k5_G2":
+        w = w.with_sizes(Hq=8)
+        kc, vc = K.Codec(K.INT_ABSMAX, 5, 128, 0), K.Codec(K.LLOYD, 2, 128, 0)
     announce(f"mfma variant {variant}")
     _case(K, w, kc, vc)
 
@@ -129,6 +148,16 @@ def test_fast_many_blocks_per_unit():
     kv_len = np.array([[[16384, 9000]]], dtype=np.int32)
     announce("mfma many blocks per unit")
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), kv_len)
+
+
+def test_fast_lloyd_values_many_blocks_and_lengths():
+    """2-bit Lloyd-Max values (rotated, [E22L] Result's next test): 32 blocks per unit on a
+    counter, causal lengths ending mid-step."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=1, T=16384, n_q=3)
+    kv_len = np.array([[[16384, 9001, 31]]], dtype=np.int32)
+    announce("mfma Lloyd-Max values, many blocks per unit")
+    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.LLOYD, 2, 128, 256), kv_len)
 
 
 def test_fast_4bit_values_many_blocks_and_lengths():
@@ -274,9 +303,10 @@ DIRTY = [(352, [[300, 289], [1, 299]], 300), (333, [[332, 289], [1, 299]], 332),
          (1000, [[700, 33], [32, 699]], 700)]
 
 
+@pytest.mark.parametrize("vname", ["absmax2", "lloyd2"])
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("T,lens,dirty_from", DIRTY)
-def test_unwritten_rows_past_the_lengths_do_not_matter(path, T, lens, dirty_from):
+def test_unwritten_rows_past_the_lengths_do_not_matter(path, T, lens, dirty_from, vname):
     """A cache filled by appends has rows past every query's key count that nothing has
     written: NaN scales and all-ones codes there leave the decode of keys [0, kv_len)
     as on a clean cache (MFMA kernel and general kernel)."""
@@ -285,10 +315,11 @@ def test_unwritten_rows_past_the_lengths_do_not_matter(path, T, lens, dirty_from
     w = synth.get("c3", B=1, L=2, T=T, n_q=2)
     Kx, Vx = synth.gen_kv(w)
     q, _ = synth.gen_queries(w)
-    kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
+    kc = K.Codec(K.INT_ABSMAX, 4, 128, 256)
+    vc = K.Codec(K.INT_ABSMAX, 2, 128, 0) if vname == "absmax2" else K.Codec(K.LLOYD, 2, 128, 256)
     kv_len = np.array([lens], dtype=np.int32)
     assert kv_len.max() <= dirty_from
-    announce(f"unwritten rows past the lengths, path {path}, T={T}, from {dirty_from}")
+    announce(f"unwritten rows past the lengths, path {path}, T={T}, from {dirty_from}, V {vname}")
     clean = (_gpu_pack(K, Kx, kc), _gpu_pack(K, Vx, vc))
     dirty = (_gpu_pack(K, Kx, kc), _gpu_pack(K, Vx, vc))
     B, L, H, T, D = Kx.shape
