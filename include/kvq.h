@@ -260,7 +260,7 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
  * above), 2 = the MFMA kernel, KVQ_ERR_UNSUPPORTED unless: head_dim 256, at least
  * 32 tokens, at most 4 query heads per KV head, K INT_ABSMAX
  * 2-, 3-, 4- or 5-bit at group 128 or 256 (any rotation, optional chan_scale), V
- * INT_ABSMAX or INT_SYM, 2- or 4-bit, or LLOYD 2-bit, at group 64..256 without
+ * INT_ABSMAX or INT_SYM, 2-, 3- or 4-bit, or LLOYD 2-bit, at group 64..256 without
  * chan_scale (any rotation) -- the 4-bit-key / 2-bit-value arms of [E22L] What I
  * tested, the Gaussian Lloyd-Max values on rotated values of [E22L] Result, the
  * 2-bit keys of the per-layer allocation of [E21W] Result, the

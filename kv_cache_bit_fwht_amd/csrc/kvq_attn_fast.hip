@@ -1,6 +1,6 @@
 // MFMA decode attention over a packed cache with 2-, 3-, 4- or 5-bit signed-absmax keys
 // (group 128 or 256, any Walsh-Hadamard rotation) and
-// 2- or 4-bit values on an
+// 2-, 3- or 4-bit values on an
 // affine grid (signed absmax or the symmetric grid, group >= 64) or 2-bit Gaussian
 // Lloyd-Max values ([E22L] Result: the next test, on rotated values), head_dim 256,
 // up to 4 query heads per KV head: the 64K-token decode workload of [E22L] ("Can
@@ -174,7 +174,9 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int kg, int n16) {
     o.k[u] = (uint32_t)(8 * (n16 >> 2) + 4 * u + (n16 & 3)) * (32u * KB) + (uint32_t)(4 * KB) * kg;
   const uint32_t sc = (uint32_t)(8 * kg + (n16 & 7));
   o.ks = sc * 2u * NKS;
-  o.v = (uint32_t)(8 * kg) * (32u * VB) + (uint32_t)(2 * VB) * n16;
+  // 3-bit values: the lane's 6 bytes start at byte 6 n16, 2-byte aligned only; the lane
+  // loads the 4-byte aligned 8 bytes around them (and drops 16 bits when n16 is odd)
+  o.v = (uint32_t)(8 * kg) * (32u * VB) + (VB == 3 ? (uint32_t)((6 * n16) & ~3) : (uint32_t)(2 * VB) * n16);
   o.vs = sc * 2u * NVS;
   return o;
 }
@@ -201,7 +203,7 @@ __device__ __forceinline__ void load_step(const FArgs& a, size_t rb, LaneOffsets
     for (int j = 0; j < 8; ++j) d.vw[j] = *reinterpret_cast<const uint32_t*>(vb + o.v + 64 * j);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) d.vw[j] = *reinterpret_cast<const u32x2_t*>(vb + o.v + 128 * j);
+    for (int j = 0; j < 8; ++j) d.vw[j] = *reinterpret_cast<const u32x2_t*>(vb + o.v + 32 * VB * j);
   }
   const char* vsb = reinterpret_cast<const char*>(a.vs) + rb * (2 * NVS);
   if constexpr (NVS == 4) {
@@ -505,7 +507,7 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   } else if (v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) {
     return false;
   }
-  if (v.codec.bits != 2 && v.codec.bits != 4) return false;
+  if (v.codec.bits < 2 || v.codec.bits > 4) return false;
   if (v.codec.group < 64) return false;   // a P.V block's 4 value words share one scale group
   if (v.chan_scale) return false;
   return true;
@@ -555,7 +557,7 @@ static void launch_mfma(const FArgs& a, dim3 grid, hipStream_t st) {
       return;
     }
   }
-  if constexpr (KB == 4) {
+  if constexpr (KB == 4 && VB != 3) {
     if (a.app_n > 0) {                               // the fused-append instances
       if (a.nks == 2) {
         if (a.nvs == 1) k_decode_mfma<2, 1, VB, 4, true><<<grid, kFastBlock, 0, st>>>(a);
@@ -583,6 +585,7 @@ static void launch_mfma(const FArgs& a, dim3 grid, hipStream_t st) {
 template <int KB>
 static void launch_mfma_k(const FArgs& a, int vb, dim3 grid, hipStream_t st) {
   if (vb == 2) launch_mfma<2, KB>(a, grid, st);
+  else if (vb == 3) launch_mfma<3, KB>(a, grid, st);
   else launch_mfma<4, KB>(a, grid, st);
 }
 
@@ -591,6 +594,7 @@ bool fused_append_supported(const kvq_packed& k, const kvq_packed& v, int Hq, in
   if (n_new < 1 || n_new > kFusedAppendRows) return false;
   if (k.codec.codebook != KVQ_INT_ABSMAX || k.codec.bits != 4 || k.chan_scale || k.mean) return false;
   if (v.codec.codebook != KVQ_INT_ABSMAX || v.chan_scale || v.mean) return false;
+  if (v.codec.bits != 2 && v.codec.bits != 4) return false;   // the row coder packs 2- and 4-bit codes
   auto rot_ok = [](int w) { return w <= 1 || w == 256; };
   return rot_ok(k.codec.rot_width) && rot_ok(v.codec.rot_width);
 }

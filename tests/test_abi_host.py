@@ -246,7 +246,7 @@ def test_decode_validates_before_launching(K):
     assert _decode(K, k, v_rfft) == ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("case", ["tokens_below_32", "head_dim_128", "k_6bit", "v_3bit", "v_group_32",
+@pytest.mark.parametrize("case", ["tokens_below_32", "head_dim_128", "k_6bit", "v_5bit", "v_group_32",
                                   "k_minmax", "v_chan_scale", "g8", "v_lloyd_3bit"])
 def test_mfma_path_rejects_what_it_does_not_cover(K, case):
     kc, vc, shape, q_heads = (1, 4, 128, 256, 0), (1, 2, 128, 0, 0), (1, 2, 4, 64, 256), 16
@@ -258,8 +258,8 @@ def test_mfma_path_rejects_what_it_does_not_cover(K, case):
         kc = (1, 4, 128, 128, 0)
     elif case == "k_6bit":
         kc = (1, 6, 128, 256, 0)
-    elif case == "v_3bit":
-        vc = (1, 3, 128, 0, 0)
+    elif case == "v_5bit":
+        vc = (1, 5, 128, 0, 0)
     elif case == "v_lloyd_3bit":
         vc = (10, 3, 128, 0, 0)
     elif case == "v_group_32":

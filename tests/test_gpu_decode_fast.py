@@ -1,4 +1,4 @@
-"""GPU parity of the MFMA decode-attention kernel (2-, 3-, 4- or 5-bit keys, 2- or
+"""GPU parity of the MFMA decode-attention kernel (2-, 3-, 4- or 5-bit keys, 2-, 3- or
 4-bit affine values or 2-bit Lloyd-Max values, head_dim 256) against the CPU oracle,
 and against the general kernel.
 
@@ -48,7 +48,8 @@ def test_fast_c3_shape_shrunk():
                                      "k5_v4_g64", "k3_kg256_rot128", "k5_norot_G2", "k3_v4_rot", "k2", "k2_v4",
                                      "k2_norot_G2", "k2_kg256_rot128", "k2_v4_rot", "vlloyd", "vlloyd_rot",
                                      "vlloyd_g64", "vlloyd_g256_k256", "vlloyd_k3_G1", "vlloyd_k2_rot128",
-                                     "vlloyd_k5_G2"])
+                                     "vlloyd_k5_G2", "v3", "v3_sym_rot", "v3_g64", "v3_g256_k2", "v3_k3_G1",
+                                     "v3_sym_k5_G2"])
 def test_fast_variants(variant):
     import kv_cache_bit_fwht_amd as K
     kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
@@ -128,6 +129,20 @@ def test_fast_variants(variant):
     elif variant == "vlloyd_k5_G2":
         w = w.with_sizes(Hq=8)
         kc, vc = K.Codec(K.INT_ABSMAX, 5, 128, 0), K.Codec(K.LLOYD, 2, 128, 0)
+    elif variant == "v3":
+        vc = K.Codec(K.INT_ABSMAX, 3, 128, 0)
+    elif variant == "v3_sym_rot":
+        vc = K.Codec(K.INT_SYM, 3, 128, 256)
+    elif variant == "v3_g64":
+        vc = K.Codec(K.INT_ABSMAX, 3, 64, 256)
+    elif variant == "v3_g256_k2":
+        kc, vc = K.Codec(K.INT_ABSMAX, 2, 256, 256), K.Codec(K.INT_SYM, 3, 256, 0)
+    elif variant == "v3_k3_G1":
+        w = w.with_sizes(Hq=4)
+        kc, vc = K.Codec(K.INT_ABSMAX, 3, 128, 256), K.Codec(K.INT_ABSMAX, 3, 128, 0)
+    elif variant == "v3_sym_k5_G2":
+        w = w.with_sizes(Hq=8)
+        kc, vc = K.Codec(K.INT_ABSMAX, 5, 128, 0), K.Codec(K.INT_SYM, 3, 64, 128)
     announce(f"mfma variant {variant}")
     _case(K, w, kc, vc)
 
@@ -158,6 +173,16 @@ def test_fast_lloyd_values_many_blocks_and_lengths():
     kv_len = np.array([[[16384, 9001, 31]]], dtype=np.int32)
     announce("mfma Lloyd-Max values, many blocks per unit")
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.LLOYD, 2, 128, 256), kv_len)
+
+
+def test_fast_3bit_values_many_blocks_and_lengths():
+    """3-bit values (the symmetric grid, rotated: [E22L] Result's next test at 3 bits): 32
+    blocks per unit on a counter, causal lengths ending mid-step."""
+    import kv_cache_bit_fwht_amd as K
+    w = synth.get("c3", L=1, T=16384, n_q=3)
+    kv_len = np.array([[[16384, 9001, 31]]], dtype=np.int32)
+    announce("mfma 3-bit values, many blocks per unit")
+    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_SYM, 3, 128, 256), kv_len)
 
 
 def test_fast_4bit_values_many_blocks_and_lengths():
@@ -303,7 +328,7 @@ DIRTY = [(352, [[300, 289], [1, 299]], 300), (333, [[332, 289], [1, 299]], 332),
          (1000, [[700, 33], [32, 699]], 700)]
 
 
-@pytest.mark.parametrize("vname", ["absmax2", "lloyd2"])
+@pytest.mark.parametrize("vname", ["absmax2", "lloyd2", "sym3"])
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("T,lens,dirty_from", DIRTY)
 def test_unwritten_rows_past_the_lengths_do_not_matter(path, T, lens, dirty_from, vname):
@@ -316,7 +341,8 @@ def test_unwritten_rows_past_the_lengths_do_not_matter(path, T, lens, dirty_from
     Kx, Vx = synth.gen_kv(w)
     q, _ = synth.gen_queries(w)
     kc = K.Codec(K.INT_ABSMAX, 4, 128, 256)
-    vc = K.Codec(K.INT_ABSMAX, 2, 128, 0) if vname == "absmax2" else K.Codec(K.LLOYD, 2, 128, 256)
+    vc = {"absmax2": K.Codec(K.INT_ABSMAX, 2, 128, 0), "lloyd2": K.Codec(K.LLOYD, 2, 128, 256),
+          "sym3": K.Codec(K.INT_SYM, 3, 128, 0)}[vname]
     kv_len = np.array([lens], dtype=np.int32)
     assert kv_len.max() <= dirty_from
     announce(f"unwritten rows past the lengths, path {path}, T={T}, from {dirty_from}, V {vname}")
