@@ -125,9 +125,30 @@ __device__ __forceinline__ void stat_sqsum(const float v[16], int g, float sm[2]
 
 // ------------------------------------------------------------------ codebooks
 
+// NF4 code lookup: cell i of [-1, 1) (width 1/128, index trunc((t + 1) * 128) clamped to
+// 0..255) holds the number of midpoints below -1 + (i - 1)/128 and the one midpoint in
+// [-1 + (i - 1)/128, -1 + (i + 2)/128), or +inf.  The index is off by at most one cell
+// from t's (fp32 rounding near a cell edge), so t lies in that three-cell window, which
+// holds at most one midpoint (they are 0.08 apart or more); outside [-1, 1) the clamped
+// end cells are right as well (every midpoint lies in (-0.85, 0.87)).  The code is the
+// count plus (midpoint < t): the number of midpoints strictly below t, as compared one
+// by one.  One cell per thread of a 256-thread block.
+__device__ __forceinline__ void nf4_cells_init(const Tables& tab, float2* cells, int i) {
+  const float lo = -1.0f + (float)(i - 1) * (1.0f / 128.0f);   // exact: multiples of 2^-7
+  const float hi = -1.0f + (float)(i + 2) * (1.0f / 128.0f);
+  float cnt = 0.0f, cand = __builtin_inff();
+#pragma unroll
+  for (int m = 0; m < 15; ++m) {
+    const float mid = tab.nf4_mid[m];
+    if (mid < lo) cnt += 1.0f;
+    else if (mid < hi) cand = mid;
+  }
+  cells[i] = make_float2(cnt, cand);
+}
+
 template <int CB, int BITS>
 __device__ __forceinline__ void encode16(const float v[16], int g, const Tables& tab, uint32_t c[16],
-                                         uint16_t s16[2], uint16_t z16[2]) {
+                                         uint16_t s16[2], uint16_t z16[2], const float2* nf4_cells = nullptr) {
   if constexpr (CB == KVQ_INT_ABSMAX) {
     float mx[2], mn[2];
     stat_maxmin(v, g, mx, mn);
@@ -180,12 +201,10 @@ __device__ __forceinline__ void encode16(const float v[16], int g, const Tables&
       } else if constexpr (CB == KVQ_INT8_SYM) {
         c[i] = (uint32_t)((int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(t), -127.0f), 127.0f) + 127);
       } else {
-        // number of midpoints strictly below t (the 15 compares use uniform table
-        // indices: a per-lane index into the argument table would be a memory read)
-        uint32_t k = 0;
-#pragma unroll
-        for (int m = 0; m < 15; ++m) k += (tab.nf4_mid[m] < t) ? 1u : 0u;
-        c[i] = k;
+        // number of midpoints strictly below t, from the cell table in LDS
+        const int ci = min(max((int)((t + 1.0f) * 128.0f), 0), 255);
+        const float2 e = nf4_cells[ci];
+        c[i] = (uint32_t)e.x + ((e.y < t) ? 1u : 0u);
       }
     }
   } else if constexpr (CB == KVQ_INT_SYM) {

@@ -87,7 +87,13 @@ __device__ __forceinline__ void pre_row(float (&v)[16], const float* mean, const
 template <int CB, int BITS>
 __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
   __shared__ float lds[kBlock * 17];
+  __shared__ float2 nf4_cells[CB == KVQ_NF4 ? 256 : 1];
   const int tid = threadIdx.x;
+  if constexpr (CB == KVQ_NF4) {
+    static_assert(kBlock == 256, "one NF4 cell per thread");
+    nf4_cells_init(a.tab, nf4_cells, tid);
+    __syncthreads();
+  }
   const int LPT = 1 << a.lpt_log2;
   const int j = tid & (LPT - 1);
   const int rloc = tid >> a.lpt_log2;
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
     if (a.W > 1) fwht_rows(v, rowlds, j, LPT, a.W, a.kappa);
     uint32_t c[16];
     uint16_t s16[2], z16[2];
-    encode16<CB, BITS>(v, a.g, a.tab, c, s16, z16);
+    encode16<CB, BITS>(v, a.g, a.tab, c, s16, z16, nf4_cells);
     if (!active) continue;
     uint32_t w[8];
     pack16<BITS>(c, w);
