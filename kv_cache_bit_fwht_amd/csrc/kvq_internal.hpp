@@ -288,22 +288,36 @@ int decode_wave_split_count(const kvq_shape& s, int Hq, int n_q);
 bool m128_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq);
 hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st);
 
-// Sum / maximum of x over the four 16-lane rows (lanes l, l^16, l^32, l^48), in every
-// lane: the row swaps of v_permlane32_swap and v_permlane16_swap move whole rows between
-// two registers in the VALU, where a lane shuffle would go through the LDS crossbar.
+// Row swaps: v_permlane32_swap exchanges the upper 32 lanes of a with the lower 32 of b,
+// v_permlane16_swap the odd 16-lane rows of a with the even rows of b, in the VALU (a
+// lane shuffle would go through the LDS crossbar).  Written as inline asm with both
+// registers read-write: this compiler's builtins for them have returned the first
+// result in place of the second (a standalone kernel added a result to itself).  The
+// s_nop covers the wait states a VALU write needs before a permute reads it.
 __device__ __forceinline__ float f_bits(uint32_t x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ uint32_t u_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ void swap_rows32(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+// Sum / maximum of x over the four 16-lane rows (lanes l, l^16, l^32, l^48), in every lane.
 __device__ __forceinline__ float sum_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(u_bits(x), u_bits(x), false, false);
-  const float y = f_bits(a[0]) + f_bits(a[1]);       // x + x of lane l^32
-  const auto b = __builtin_amdgcn_permlane16_swap(u_bits(y), u_bits(y), false, false);
-  return f_bits(b[0]) + f_bits(b[1]);                // y + y of lane l^16
+  uint32_t a = u_bits(x), b = a;
+  swap_rows32(a, b);
+  const float y = f_bits(a) + f_bits(b);             // x + x of lane l^32
+  uint32_t c = u_bits(y), d = c;
+  swap_rows16(c, d);
+  return f_bits(c) + f_bits(d);                      // y + y of lane l^16
 }
 __device__ __forceinline__ float max_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(u_bits(x), u_bits(x), false, false);
-  const float y = __builtin_fmaxf(f_bits(a[0]), f_bits(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(u_bits(y), u_bits(y), false, false);
-  return __builtin_fmaxf(f_bits(b[0]), f_bits(b[1]));
+  uint32_t a = u_bits(x), b = a;
+  swap_rows32(a, b);
+  const float y = __builtin_fmaxf(f_bits(a), f_bits(b));
+  uint32_t c = u_bits(y), d = c;
+  swap_rows16(c, d);
+  return __builtin_fmaxf(f_bits(c), f_bits(d));
 }
 
 
