@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_absmax256(QArgs a) {
 
 constexpr int kQuadWaves = 4;                        // wavefronts (row quads) per block
 
-template <int BITS, bool ROT>
+template <int BITS, bool ROT, int CB = KVQ_INT_ABSMAX>
 __global__ __launch_bounds__(kQuadWaves * 64) void k_quantize_q256(QArgs a) {
   __shared__ float lds[kQuadWaves * 4][kRowLds];
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15;
@@ -595,7 +595,8 @@ __global__ __launch_bounds__(kQuadWaves * 64) void k_quantize_q256(QArgs a) {
   if (((long long)blockIdx.x * kQuadWaves + (tid >> 6)) * 4 >= a.rows) return;   // whole wavefront past the end
   uint4 p0, p1;
   load_row256_nt(a.x, a.rows, row, j, p0, p1);
-  code_row256<BITS, ROT, false>(a.codes, a.scales, a.g, out_row(a, row), row < a.rows, p0, p1, lds[tid >> 4], j);
+  code_row256<BITS, ROT, false, CB>(a.codes, a.scales, a.g, out_row(a, row), row < a.rows, p0, p1, lds[tid >> 4], j,
+                                    &a.tab);
 }
 
 // K and V of one cache in one launch: wavefront 2q codes quad q of the key rows and
@@ -629,7 +630,14 @@ static unsigned quad_blocks(long long rows) {
 
 static bool absmax256_supported(const kvq_packed& p, int tokens_in) {
   const kvq_codec& c = p.codec;
-  if (c.codebook != KVQ_INT_ABSMAX || p.shape.head_dim != 256) return false;
+  if (p.shape.head_dim != 256) return false;
+  if (c.codebook == KVQ_INT_SYM || c.codebook == KVQ_LLOYD) {
+    // the one-quad-per-wavefront coder has these grids too (without a mean or channel scales)
+    if (p.chan_scale || p.mean) return false;
+    if (c.codebook == KVQ_LLOYD && c.bits == 8) return false;
+  } else if (c.codebook != KVQ_INT_ABSMAX) {
+    return false;
+  }
   if ((p.chan_scale || p.mean) && tokens_in % 4 != 0) return false;   // a quad would span two units
   if (c.bits != 2 && c.bits != 4 && c.bits != 8) return false;
   if (c.group < 16 || c.group > 256) return false;
@@ -663,12 +671,27 @@ static void launch_absmax256(const QArgs& a, const kvq_codec& c, hipStream_t st)
   if (pre == 0) {
     const dim3 grid(quad_blocks(a.rows));
     const bool rot = c.rot_width == 256;
-    if (c.bits == 2) rot ? k_quantize_q256<2, true><<<grid, kQuadWaves * 64, 0, st>>>(a)
-                         : k_quantize_q256<2, false><<<grid, kQuadWaves * 64, 0, st>>>(a);
-    else if (c.bits == 4) rot ? k_quantize_q256<4, true><<<grid, kQuadWaves * 64, 0, st>>>(a)
-                              : k_quantize_q256<4, false><<<grid, kQuadWaves * 64, 0, st>>>(a);
-    else rot ? k_quantize_q256<8, true><<<grid, kQuadWaves * 64, 0, st>>>(a)
-             : k_quantize_q256<8, false><<<grid, kQuadWaves * 64, 0, st>>>(a);
+    const dim3 blk(kQuadWaves * 64);
+    if (c.codebook == KVQ_INT_SYM) {
+      if (c.bits == 2) rot ? k_quantize_q256<2, true, KVQ_INT_SYM><<<grid, blk, 0, st>>>(a)
+                           : k_quantize_q256<2, false, KVQ_INT_SYM><<<grid, blk, 0, st>>>(a);
+      else if (c.bits == 4) rot ? k_quantize_q256<4, true, KVQ_INT_SYM><<<grid, blk, 0, st>>>(a)
+                                : k_quantize_q256<4, false, KVQ_INT_SYM><<<grid, blk, 0, st>>>(a);
+      else rot ? k_quantize_q256<8, true, KVQ_INT_SYM><<<grid, blk, 0, st>>>(a)
+               : k_quantize_q256<8, false, KVQ_INT_SYM><<<grid, blk, 0, st>>>(a);
+    } else if (c.codebook == KVQ_LLOYD) {
+      if (c.bits == 2) rot ? k_quantize_q256<2, true, KVQ_LLOYD><<<grid, blk, 0, st>>>(a)
+                           : k_quantize_q256<2, false, KVQ_LLOYD><<<grid, blk, 0, st>>>(a);
+      else rot ? k_quantize_q256<4, true, KVQ_LLOYD><<<grid, blk, 0, st>>>(a)
+               : k_quantize_q256<4, false, KVQ_LLOYD><<<grid, blk, 0, st>>>(a);
+    } else {
+      if (c.bits == 2) rot ? k_quantize_q256<2, true><<<grid, blk, 0, st>>>(a)
+                           : k_quantize_q256<2, false><<<grid, blk, 0, st>>>(a);
+      else if (c.bits == 4) rot ? k_quantize_q256<4, true><<<grid, blk, 0, st>>>(a)
+                                : k_quantize_q256<4, false><<<grid, blk, 0, st>>>(a);
+      else rot ? k_quantize_q256<8, true><<<grid, blk, 0, st>>>(a)
+               : k_quantize_q256<8, false><<<grid, blk, 0, st>>>(a);
+    }
   }
   else if (pre == 1) launch_absmax256_pre<1>(a, c, st);
   else if (pre == 2) launch_absmax256_pre<2>(a, c, st);
@@ -723,8 +746,11 @@ hipError_t launch_quantize_kv(const uint16_t* kx, const uint16_t* vx, const kvq_
                               int t0, int n, hipStream_t st) {
   const bool window = !(t0 == 0 && n == kp.shape.tokens);
   auto lean = [&](const kvq_packed& p) {
-    return absmax256_supported(p, n) && p.mean == nullptr && p.chan_scale == nullptr;
+    return absmax256_supported(p, n) && p.codec.codebook == KVQ_INT_ABSMAX && p.mean == nullptr &&
+           p.chan_scale == nullptr;
   };
+  // (symmetric-grid or Lloyd-Max values take two launches of the quad coder: one launch
+  // for both measured no faster with rotated values)
   if (!lean(kp) || !lean(vp)) {
     hipError_t e = window ? launch_quantize_tokens(kx, kp, t0, n, st) : launch_quantize(kx, kp, st);
     if (e != hipSuccess) return e;

@@ -54,14 +54,19 @@ __device__ __forceinline__ float min16(const float v[16]) {
 }
 
 // Codes and scales of one row (16 lanes, lane j holding values 16j..16j+15 as the
-// raw fp16 words p0, p1) of a 256-wide signed-absmax tensor with `g` values per
-// scale, stored at row `orow` of codes / scales when `store` (else computed only).
-// rl: this row's LDS region (kRowLds floats; used with ROT).  COH: the stores are
-// device-coherent (written through to memory), for rows another block may read in
-// the same launch.
-template <int BITS, bool ROT, bool COH>
+// raw fp16 words p0, p1) of a 256-wide tensor with `g` values per scale, stored at row
+// `orow` of codes / scales when `store` (else computed only).  CB: the signed absmax
+// grid, the symmetric grid (s = RN16(absmax / h), k = rne(RN32(t + h)), h = (2^b - 1)/2)
+// or Gaussian Lloyd-Max levels (s = RN16(sqrt(RN32(S / g))) with S the adjacent-pairs
+// tree sum of the squares; k = midpoints below t), with the same binary32 steps as the
+// codec's general kernel and the CPU oracle.  rl: this row's LDS region (kRowLds
+// floats; used with ROT).  COH: the stores are device-coherent (written through to
+// memory), for rows another block may read in the same launch.  tab: the Lloyd-Max
+// levels (LLOYD only).
+template <int BITS, bool ROT, bool COH, int CB = KVQ_INT_ABSMAX>
 __device__ __forceinline__ void code_row256(uint32_t* codes, uint16_t* scales, int g, long long orow, bool store,
-                                            const uint4 p0, const uint4 p1, float* rl, int j) {
+                                            const uint4 p0, const uint4 p1, float* rl, int j,
+                                            const Tables* tab = nullptr) {
 #pragma clang fp contract(off)
   constexpr int D = 256;
   constexpr float kFold = ROT ? 0.0625f : 1.0f;      // the 256-point transform's 1/sqrt(256)
@@ -126,9 +131,41 @@ __device__ __forceinline__ void code_row256(uint32_t* codes, uint16_t* scales, i
     mx = max16(v);
     mn = min16(v);
   }
-  run_maxmin(mx, mn, lpg);
-  const float ext = (-mn >= mx) ? mn : mx;
-  const uint16_t s16 = rn16(ext * neg_step);         // exact product: neg_step is a power of two
+  uint16_t s16;
+  if constexpr (CB == KVQ_LLOYD) {
+    // sum of squares: adjacent pairs of the lane's 16 values, then adjacent lanes
+    float sq[16];
+    if constexpr (!ROT) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float a = h2f((uint16_t)(raw[k] & 0xffffu)), b = h2f((uint16_t)(raw[k] >> 16));
+        sq[2 * k] = __fmul_rn(a, a);
+        sq[2 * k + 1] = __fmul_rn(b, b);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sq[i] = __fmul_rn(v[i], v[i]);   // 256 times the rotated square, exactly
+    }
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2 * w) sq[i] = __fadd_rn(sq[i], sq[i + w]);
+    }
+    float S = sq[0];
+    for (int m = 1; m < lpg; m <<= 1) S = __fadd_rn(S, __shfl_xor(S, m));
+    if constexpr (ROT) S = S * (1.0f / 256.0f);      // exact: a power of two
+    s16 = rn16(sqrt_rn(__fmul_rn(S, 1.0f / (float)g)));   // 1/g exact: g is a power of two
+  } else {
+    run_maxmin(mx, mn, lpg);
+    if constexpr (CB == KVQ_INT_SYM) {
+      constexpr float h = (float)((1 << BITS) - 1) * 0.5f;
+      const float am = __builtin_fmaxf(mx, -mn) * kFold;   // exact: kFold is a power of two
+      s16 = rn16(__fdiv_rn(am, h));
+    } else {
+      const float ext = (-mn >= mx) ? mn : mx;
+      s16 = rn16(ext * neg_step);                    // exact product: neg_step is a power of two
+    }
+  }
   const float inv = inv_scale(s16) * kFold;          // exact: kFold is a power of two
   uint32_t c[16];
 #pragma unroll
@@ -140,9 +177,21 @@ __device__ __forceinline__ void code_row256(uint32_t* codes, uint16_t* scales, i
     } else {
       t = __fmul_rn(v[i], inv);
     }
-    const float f = __fadd_rn(t, kBias);
-    const int b = (int)__builtin_bit_cast(uint32_t, f);
-    c[i] = (uint32_t)min(max(b, (int)kMagic), (int)(kMagic + (1u << BITS) - 1u));
+    if constexpr (CB == KVQ_INT_SYM) {
+      constexpr float h = (float)((1 << BITS) - 1) * 0.5f;
+      c[i] = (uint32_t)(int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fadd_rn(t, h)), 0.0f),
+                                           (float)((1 << BITS) - 1));
+    } else if constexpr (CB == KVQ_LLOYD) {
+      const float* L = tab->lloyd_lv[BITS - 2];
+      uint32_t k = 0;
+#pragma unroll
+      for (int m = 0; m < (1 << BITS) - 1; ++m) k += (__fmul_rn(__fadd_rn(L[m], L[m + 1]), 0.5f) < t) ? 1u : 0u;
+      c[i] = k;
+    } else {
+      const float f = __fadd_rn(t, kBias);
+      const int b = (int)__builtin_bit_cast(uint32_t, f);
+      c[i] = (uint32_t)min(max(b, (int)kMagic), (int)(kMagic + (1u << BITS) - 1u));
+    }
   }
   if (!store) return;
   uint32_t w[4];

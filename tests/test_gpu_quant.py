@@ -71,6 +71,10 @@ CASES.append((256, (1, 4, 256, 256)))
 for D in (64, 128, 256):
     CASES += [(D, (9, 2, 8, 0)), (D, (9, 3, 32, D)), (D, (9, 4, 64, 0)), (D, (9, 8, 32, 0)),
               (D, (10, 2, 8, 0)), (D, (10, 2, 64, D)), (D, (10, 3, 32, 0)), (D, (10, 4, 16, D))]
+# at head_dim 256 (2-, 4- and 8-bit, groups of 16 or more) these run on the one-quad-per-
+# wavefront row coder: more groups, rotations and the 64K experiment's value arms
+CASES += [(256, (9, 2, 128, 256)), (256, (9, 2, 16, 0)), (256, (9, 4, 256, 256)), (256, (9, 8, 128, 256)),
+          (256, (10, 2, 128, 256)), (256, (10, 2, 256, 0)), (256, (10, 4, 32, 0)), (256, (10, 2, 16, 256))]
 
 
 @pytest.mark.parametrize("D,cspec", CASES)

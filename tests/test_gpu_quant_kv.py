@@ -28,6 +28,9 @@ def _check(K, x, p, codec, chan=None, mean=None):
 # (K codec, V codec) as (codebook, bits, group, rot); the first six take the one-launch route
 PAIRS = [((1, 4, 128, 256), (1, 2, 128, 0)), ((1, 2, 32, 256), (1, 4, 64, 256)), ((1, 8, 256, 0), (1, 8, 16, 256)),
          ((1, 4, 16, 0), (1, 2, 256, 0)), ((1, 2, 128, 0), (1, 2, 128, 0)), ((1, 8, 64, 256), (1, 4, 32, 0)),
+         # symmetric-grid or Lloyd-Max values: two launches of the quad coder
+         ((1, 4, 128, 256), (9, 2, 128, 256)), ((1, 4, 128, 256), (10, 2, 128, 256)), ((1, 4, 64, 0), (9, 4, 32, 0)),
+         ((1, 4, 256, 256), (10, 4, 16, 0)),
          # fallbacks: another codebook or bit width on one side
          ((1, 3, 128, 256), (1, 2, 128, 0)), ((5, 4, 64, 0), (1, 4, 64, 0)), ((2, 4, 32, 0), (2, 4, 32, 0)),
          ((7, 5, 32, 0), (0, 16, 0, 0))]
