@@ -13,6 +13,13 @@
 //    its offset 127 are applied to the logit (offset folded as 127 * sum q); fp16
 //    keys are used as they are.  B = the fp16 query, 4 heads in columns n % 4 (the
 //    query is fp16 already, so one part is exact).
+//  * 6-bit signed absmax keys at group 32 (the Hadamard arm of the matched-rate
+//    transform control, [FMAG-R] Colab-probe reply): MFMA g takes group g's 32 dims,
+//    A = the codes as exact fp16 integers c - 32, and the group's scale multiplies
+//    that MFMA's logits.  The query is rotated in the prologue when the keys are
+//    (kappa * H q, an orthonormal identity), scaled per head by a power of two, and
+//    split into an fp16 high part and remainder, which fill alternate groups of four
+//    B columns; a row rotation by four lanes adds the two.
 //  * online softmax per head in log2 units, against a reference maximum that moves
 //    only when a logit exceeds it by more than 1, so weights stay at most 2.
 //  * P.V on v_mfma_f32_16x16x16_f16: A = fp16(p) for 4 heads (rows 0-3) x 16
@@ -53,8 +60,9 @@ constexpr int kMStep = 32;            // tokens per wavefront step
 constexpr int kMWaves = 4;            // independent wavefronts per block
 constexpr int kMPart = kMD + 2;       // floats per partial: o[128], m, l
 
-// MC_NF4: keys only (NF4 at group 64); MC_I4: values only (4-bit signed absmax at group 64)
-enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3, MC_NF4 = 4, MC_I4 = 5 };
+// MC_NF4: keys only (NF4 at group 64); MC_I4: values only (4-bit signed absmax at group 64);
+// MC_I6: keys only (6-bit signed absmax at group 32, unrotated or Hadamard-128 rotated)
+enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3, MC_NF4 = 4, MC_I4 = 5, MC_I6 = 6 };
 
 struct M128Args {
   const uint8_t* kc;
@@ -67,12 +75,15 @@ struct M128Args {
   int H, T, Hq, G, n_q, S, cs;        // cs: steps per split
   long long items;                    // rows * H * S
   float lsc;                          // softmax scale * log2(e)
+  int krot;                           // 6-bit keys: 1 if rotated by the normalised Hadamard-128
   float nf4[16];                      // NF4 levels (binary32)
 };
 
 template <int C> struct Row {          // bytes of one row's codes, scales per row
-  static constexpr int code = C == MC_TER ? 32 : C == MC_SIGN ? 16 : C == MC_INT8 ? 128 : C == MC_F16 ? 256 : 64;
-  static constexpr int scales = C == MC_TER || C == MC_SIGN ? 16 : C == MC_INT8 ? 1 : C == MC_F16 ? 0 : 2;
+  static constexpr int code = C == MC_TER ? 32 : C == MC_SIGN ? 16 : C == MC_INT8 ? 128 : C == MC_F16 ? 256
+                              : C == MC_I6 ? 96 : 64;
+  static constexpr int scales = C == MC_TER || C == MC_SIGN ? 16 : C == MC_INT8 ? 1 : C == MC_F16 ? 0
+                                : C == MC_I6 ? 4 : 2;
 };
 
 // ---- key data of one 16-token tile for lane (i, kq): token tok(i, u), dims 32kq .. 32kq + 31
@@ -83,6 +94,9 @@ template <> struct KTile<MC_INT8> { mu4 c0, c1; uint32_t s; };  // 32 code bytes
 template <> struct KTile<MC_F16> { mu4 c[4]; };                  // 32 fp16 values
 template <> struct KTile<MC_NF4> { mu2 c[2]; uint32_t s; };  // 16 codes of each group (dims 64g + 16kq ..); s:
                                                              // the two scales of token 8kq + i % 8 (tile 0 only)
+// 6-bit keys: c[g] = the dword-aligned 8 bytes holding the 48 code bits of dims
+// 32g + 8kq .. + 7 (group g); s: the four group scales of token 8kq + i % 8 (tile 0 only)
+template <> struct KTile<MC_I6> { mu2 c[4]; mu2 s; };
 
 // ---- value data for lane (i, kq): dims 8i .. 8i + 7 of tokens 8kq .. 8kq + 7.  (Row
 // scales of int8 tokens are loaded one per lane and shared by DPP broadcasts: eight
@@ -123,6 +137,7 @@ __device__ __forceinline__ MOffsets m_offsets(int i, int kq) {
     else if constexpr (KC == MC_SIGN) { o.k[u] = r * 16 + 4 * kq; o.ks[u] = (r * 16 + 4 * kq) * 2; }
     else if constexpr (KC == MC_INT8) { o.k[u] = r * 128 + 32 * kq; o.ks[u] = (8 * kq + (i & 7)) * 2; }
     else if constexpr (KC == MC_F16) { o.k[u] = r * 256 + 64 * kq; o.ks[u] = 0; }
+    else if constexpr (KC == MC_I6) { o.k[u] = r * 96 + ((6 * kq) & ~3u); o.ks[u] = (8 * kq + (i & 7)) * 8; }
     else { o.k[u] = r * 64 + 8 * kq; o.ks[u] = (8 * kq + (i & 7)) * 4; }
   }
   const uint32_t t = 8 * kq;
@@ -188,6 +203,12 @@ __device__ __forceinline__ void m_load(const M128Args& a, size_t rb, const MOffs
       d.k[u].c0 = ld<mu4>(kb, o.k[u]);
       d.k[u].c1 = ld<mu4, 16>(kb, o.k[u]);
       if (u == 0) d.k[0].s = ld<uint16_t>(ksb, o.ks[0]);
+    } else if constexpr (KC == MC_I6) {
+      d.k[u].c[0] = ld<mu2, 0>(kb, o.k[u]);
+      d.k[u].c[1] = ld<mu2, 24>(kb, o.k[u]);
+      d.k[u].c[2] = ld<mu2, 48>(kb, o.k[u]);
+      d.k[u].c[3] = ld<mu2, 72>(kb, o.k[u]);
+      if (u == 0) d.k[0].s = ld<mu2>(ksb, o.ks[0]);
     } else if constexpr (KC == MC_F16) {
       d.k[u].c[0] = ld<mu4, 0>(kb, o.k[u]);
       d.k[u].c[1] = ld<mu4, 16>(kb, o.k[u]);
@@ -291,6 +312,29 @@ __device__ __forceinline__ mh8 nf4_operand(const KTile<MC_NF4>& t, int c, const 
   return __builtin_bit_cast(mh8, mu4{e0.x, e0.y, e1.x, e1.y});
 }
 
+// 6-bit keys, MFMA g (group g): dims 32g + 8kq + e, e = 0..7 in order, as fp16 c - 32
+// (exact).  The lane's 48 code bits start at bit sh (0 or 16) of its 8-byte window;
+// dword m holds dims (2m, 2m + 1) in its halves: each half gets its code at bits 0-5
+// (bit-field insert of two shifted copies), or-ed with 0x6400 (the fp16 1024 + c), and
+// 1056 comes off both halves in one packed subtract.
+__device__ __forceinline__ mh8 i6_operand(const KTile<MC_I6>& t, int g, int sh) {
+  const uint32_t lo = __builtin_amdgcn_alignbit(t.c[g].y, t.c[g].x, sh);   // code bits 0..31
+  const uint32_t hi = t.c[g].y >> sh;                                      // code bits 32..47
+  const uint32_t hm = 0xFFFF0000u;
+  uint32_t x[4];
+  x[0] = ((lo << 10) & hm) | (lo & ~hm);                                                    // e0 (bit 0), e1 (6)
+  x[1] = ((lo >> 2) & hm) | ((lo >> 12) & ~hm);                                             // e2 (12), e3 (18)
+  x[2] = (__builtin_amdgcn_alignbit(hi, lo, 14) & hm) | (__builtin_amdgcn_alignbit(hi, lo, 24) & ~hm);   // e4 (24), e5 (30)
+  x[3] = ((hi << 6) & hm) | ((hi >> 4) & ~hm);                                              // e6 (36), e7 (42)
+  mu4 r;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const mh2 u = __builtin_bit_cast(mh2, or6400(x[m], 0x003F003Fu)) - mh2{(_Float16)1056.0f, (_Float16)1056.0f};
+    r[m] = __builtin_bit_cast(uint32_t, u);
+  }
+  return __builtin_bit_cast(mh8, r);
+}
+
 // B operand of value chunk c (dim 8i + c) for tokens 4u .. 4u + 3 of the lane's 8.
 // keep01 / keep23: all-ones halves for the tokens that count (partial steps).
 template <int VC, bool MASK>
@@ -353,11 +397,87 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   for (int c = 0; c < 4; ++c) {
     // NF4 keys: dims 64g + 16kq .. + 15 of group g = c / 2 (eight per load); otherwise the
     // lane's chunks are dims 32kq .. 32kq + 31
-    const uint16_t* qp = (KC == MC_NF4) ? qrow - 32 * kq + 64 * (c >> 1) + 16 * kq + 8 * (c & 1) : qrow + 8 * c;
+    // 6-bit keys: chunk c is dims 32c + 8kq .. + 7 (group c)
+    const uint16_t* qp = (KC == MC_NF4) ? qrow - 32 * kq + 64 * (c >> 1) + 16 * kq + 8 * (c & 1)
+                         : (KC == MC_I6) ? qrow - 32 * kq + 32 * c + 8 * kq : qrow + 8 * c;
     qw[c] = head_ok ? *reinterpret_cast<const mu4*>(qp) : mu4{0u, 0u, 0u, 0u};
   }
   mh8 bq[KC == MC_NF4 ? 8 : 4];
-  if constexpr (KC == MC_TER || KC == MC_SIGN) {
+  float qscale = 1.0f;                               // 6-bit keys: the logit's factor of the head's query scaling
+  if constexpr (KC == MC_I6) {
+    // q in the key coordinates: y = kappa * H q (Sylvester order, kappa = RN32(1/sqrt(128)))
+    // when the keys are rotated.  Dim bits 0-2 and 5-6 are the lane's own (e and the
+    // chunk), bits 3 and 4 are lane bits 4 and 5 (kq): those two stages pair lanes
+    // through row swaps, the lane with the bit set taking (partner - own).
+    float y[4][8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[c][e] = h2f((uint16_t)(qw[c][e >> 1] >> (16 * (e & 1))));
+    if (a.krot) {
+#pragma unroll
+      for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (!(e & st)) {
+              const float u = y[c][e], v = y[c][e + st];
+              y[c][e] = u + v;
+              y[c][e + st] = u - v;
+            }
+#pragma unroll
+      for (int st = 1; st < 4; st <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (!(c & st))
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float u = y[c][e], v = y[c + st][e];
+              y[c][e] = u + v;
+              y[c + st][e] = u - v;
+            }
+      const bool b16 = (lane & 16) != 0, b32 = (lane & 32) != 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t p0 = u_bits(y[c][e]), p1 = p0;
+          swap_rows16(p0, p1);                       // p0: lane without bit 4, p1: lane with it
+          float z = b16 ? f_bits(p0) - f_bits(p1) : f_bits(p0) + f_bits(p1);
+          uint32_t r0 = u_bits(z), r1 = r0;
+          swap_rows32(r0, r1);
+          z = b32 ? f_bits(r0) - f_bits(r1) : f_bits(r0) + f_bits(r1);
+          y[c][e] = z * 0x1.6a09e6p-4f;              // RN32(1/sqrt(128))
+        }
+    }
+    // scale the head's query by a power of two so that its largest entry lies in
+    // [2^13, 2^14): the fp16 operands cannot overflow, and the logit takes the factor back
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[c][e]));
+    amax = max_rows(amax);
+    int ex = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &ex);
+    const int sc = min(max(14 - ex, -100), 100);
+    qscale = ldexpf(1.0f, -sc);
+    // columns i with (i / 4) even take the fp16 high part, odd the fp16 remainder: each
+    // lane's partner four columns away (either way, mod 16) holds the other part
+    const int part = (i >> 2) & 1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mh8 r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ldexpf(y[c][e], sc);
+        const _Float16 hv = (_Float16)v;
+        r[e] = part == 0 ? hv : (_Float16)(v - (float)hv);
+      }
+      bq[c] = r;
+    }
+  } else if constexpr (KC == MC_TER || KC == MC_SIGN) {
     // dword m of chunk c: dims (p, p + 16) of the lane's 32, p = 4c + m
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -407,19 +527,23 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   float m_ref = -INFINITY;       // reference max (log2 units) of head hq
   float l_part = 0.0f;           // sum of p over this lane's tokens (head hq)
   float w_part = 0.0f;           // int8 values: sum of the fp16 weights fp16(p) * s_v (head hq)
-  const float kscale = (KC == MC_INT8) ? a.lsc * 16777216.0f : a.lsc;
+  const float kscale = (KC == MC_INT8) ? a.lsc * 16777216.0f : (KC == MC_I6) ? a.lsc * qscale : a.lsc;
 
   auto process = [&](const MStep<KC, VC>& d, int step) {
     const int t0 = step * kMStep;
     const int tb = min(t0, a.T - kMStep);            // first token of the rows loaded
     // ---- Q.K^T: tile u, output rows = tokens 8kq + 4u + r
-    mf4 cq[2][2];                                    // [tile][key group] (group 1 for NF4 only)
+    constexpr int NG = KC == MC_I6 ? 4 : 2;
+    mf4 cq[2][NG];                                   // [tile][key group] (group 1 for NF4, 1-3 for 6-bit keys)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      cq[u][0] = cq[u][1] = mf4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) cq[u][g] = mf4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if constexpr (KC == MC_NF4) {
+        if constexpr (KC == MC_I6) {
+          cq[u][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i6_operand(d.k[u], c, (kq & 1) ? 16 : 0), bq[c], cq[u][c], 0, 0, 0);
+        } else if constexpr (KC == MC_NF4) {
 #pragma unroll
           for (int cc = 2 * c; cc < 2 * c + 2; ++cc)
             cq[u][cc >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(nf4_operand(d.k[u], cc, nf4_lut), bq[cc], cq[u][cc >> 2], 0, 0, 0);
@@ -436,6 +560,16 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
         if constexpr (KC == MC_INT8) {
           const float sk = h2f((uint16_t)m_bcast(d.k[0].s, 4 * u + r));   // token 8kq + 4u + r
           lg[4 * u + r] = sk * (cq[u][0][r] * kscale - koff * a.lsc);
+        } else if constexpr (KC == MC_I6) {
+          // its four group scales; then each column adds its partner's part (row
+          // rotation by 4), so every lane holds the full logit of head i % 4
+          const uint32_t s01 = m_bcast(d.k[0].s.x, 4 * u + r), s23 = m_bcast(d.k[0].s.y, 4 * u + r);
+          float t = h2f((uint16_t)s01) * cq[u][0][r];
+          t = __builtin_fmaf(h2f((uint16_t)(s01 >> 16)), cq[u][1][r], t);
+          t = __builtin_fmaf(h2f((uint16_t)s23), cq[u][2][r], t);
+          t = __builtin_fmaf(h2f((uint16_t)(s23 >> 16)), cq[u][3][r], t);
+          const float tr = f_bits((uint32_t)__builtin_amdgcn_mov_dpp((int)u_bits(t), 0x124, 0xF, 0xF, true));   // row_ror:4
+          lg[4 * u + r] = (t + tr) * kscale;
         } else if constexpr (KC == MC_NF4) {
           const uint32_t sw = m_bcast(d.k[0].s, 4 * u + r);                 // its two group scales
           lg[4 * u + r] = (h2f((uint16_t)sw) * cq[u][0][r] + h2f((uint16_t)(sw >> 16)) * cq[u][1][r]) * kscale;
@@ -590,6 +724,9 @@ namespace {
 
 // The kernel's codec of a key (K) or value (V) codec, or -1.
 int m128_codec(const kvq_codec& c, bool key) {
+  // 6-bit signed absmax keys at group 32, unrotated or rotated over the whole row
+  if (key && c.codebook == KVQ_INT_ABSMAX && c.bits == 6 && c.group == 32 && (c.rot_width <= 1 || c.rot_width == kMD))
+    return MC_I6;
   if (c.rot_width > 1) return -1;
   switch (c.codebook) {
     case KVQ_TERNARY: return c.group == 8 ? MC_TER : -1;
@@ -648,6 +785,7 @@ hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
   const long long rows = (long long)s.batch * s.layers * pr.n_q;
   a.items = rows * s.heads * a.S;
   a.lsc = pr.sm_scale * 1.4426950408889634f;
+  a.krot = pr.k->codec.rot_width == kMD ? 1 : 0;
   if (a.items == 0) return hipSuccess;
   if ((size_t)rows * pr.Hq * a.S * kMPart * sizeof(float) > pr.ws_bytes) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((a.items + kMWaves - 1) / kMWaves);
@@ -659,6 +797,7 @@ hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
     case MC_SIGN: e = launch_m128_v<MC_SIGN>(vc, a, grid, st); break;
     case MC_INT8: e = launch_m128_v<MC_INT8>(vc, a, grid, st); break;
     case MC_NF4: e = launch_m128_v<MC_NF4>(vc, a, grid, st); break;
+    case MC_I6: e = launch_m128_v<MC_I6>(vc, a, grid, st); break;
     default: e = launch_m128_v<MC_F16>(vc, a, grid, st); break;
   }
   if (e != hipSuccess) return e;

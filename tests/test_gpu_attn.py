@@ -27,7 +27,7 @@ def _gpu_pack(K, x, codec, chan=None):
     return p
 
 
-def _gpu_decode(K, kp, vp, q, kv_len, path=None, ws=None):
+def _gpu_decode(K, kp, vp, q, kv_len, path=None, ws=None, sm_scale=0.0):
     """One decode call; `ws` (a zero-filled device byte tensor) is reused when given."""
     import torch
     B, L, nq, Hq, D = q.shape
@@ -38,7 +38,7 @@ def _gpu_decode(K, kp, vp, q, kv_len, path=None, ws=None):
         ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda:0")
     assert ws.numel() >= wsb
     kl = to_dev(kv_len) if kv_len is not None else None
-    K.kvq_decode_attn(kp, vp, Hq, nq, to_dev(q), kl, 0.0, out, lse, ws, wsb, path=path)
+    K.kvq_decode_attn(kp, vp, Hq, nq, to_dev(q), kl, sm_scale, out, lse, ws, wsb, path=path)
     torch.cuda.synchronize()
     return to_np(out), to_np(lse)
 
