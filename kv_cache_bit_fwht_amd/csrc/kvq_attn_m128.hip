@@ -20,6 +20,11 @@
 //    (kappa * H q, an orthonormal identity), scaled per head by a power of two, and
 //    split into an fp16 high part and remainder, which fill alternate groups of four
 //    B columns; a row rotation by four lanes adds the two.
+//  * rFFT keys with 6-bit real and imaginary parts at group 32 (the real/imaginary
+//    arm): the logit is the weighted sum over bins of Re Q Re Z + Im Q Im Z (Parseval),
+//    so the keys enter as for 6-bit keys, MFMA g taking real groups 0, 1 then
+//    imaginary groups 0, 1; bin 64 (its own scale group) is added on the VALU.  The
+//    weighted query spectrum comes from k_m128_qspec, run just before on the stream.
 //  * online softmax per head in log2 units, against a reference maximum that moves
 //    only when a logit exceeds it by more than 1, so weights stay at most 2.
 //  * P.V on v_mfma_f32_16x16x16_f16: A = fp16(p) for 4 heads (rows 0-3) x 16
@@ -61,8 +66,10 @@ constexpr int kMWaves = 4;            // independent wavefronts per block
 constexpr int kMPart = kMD + 2;       // floats per partial: o[128], m, l
 
 // MC_NF4: keys only (NF4 at group 64); MC_I4: values only (4-bit signed absmax at group 64);
-// MC_I6: keys only (6-bit signed absmax at group 32, unrotated or Hadamard-128 rotated)
-enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3, MC_NF4 = 4, MC_I4 = 5, MC_I6 = 6 };
+// MC_I6: keys only (6-bit signed absmax at group 32, unrotated or Hadamard-128 rotated);
+// MC_RC: keys only (rFFT along head_dim, real and imaginary parts 6-bit at group 32)
+enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3, MC_NF4 = 4, MC_I4 = 5, MC_I6 = 6, MC_RC = 7 };
+constexpr int kQSpec = 132;           // floats per (query row, head) of a prepared query spectrum
 
 struct M128Args {
   const uint8_t* kc;
@@ -76,14 +83,15 @@ struct M128Args {
   long long items;                    // rows * H * S
   float lsc;                          // softmax scale * log2(e)
   int krot;                           // 6-bit keys: 1 if rotated by the normalised Hadamard-128
+  const float* qspec;                 // rFFT keys: [rows][Hq][kQSpec] weighted query spectra
   float nf4[16];                      // NF4 levels (binary32)
 };
 
 template <int C> struct Row {          // bytes of one row's codes, scales per row
   static constexpr int code = C == MC_TER ? 32 : C == MC_SIGN ? 16 : C == MC_INT8 ? 128 : C == MC_F16 ? 256
-                              : C == MC_I6 ? 96 : 64;
+                              : C == MC_I6 ? 96 : C == MC_RC ? 100 : 64;
   static constexpr int scales = C == MC_TER || C == MC_SIGN ? 16 : C == MC_INT8 ? 1 : C == MC_F16 ? 0
-                                : C == MC_I6 ? 4 : 2;
+                                : C == MC_I6 ? 4 : C == MC_RC ? 6 : 2;
 };
 
 // ---- key data of one 16-token tile for lane (i, kq): token tok(i, u), dims 32kq .. 32kq + 31
@@ -97,6 +105,12 @@ template <> struct KTile<MC_NF4> { mu2 c[2]; uint32_t s; };  // 16 codes of each
 // 6-bit keys: c[g] = the dword-aligned 8 bytes holding the 48 code bits of dims
 // 32g + 8kq .. + 7 (group g); s: the four group scales of token 8kq + i % 8 (tile 0 only)
 template <> struct KTile<MC_I6> { mu2 c[4]; mu2 s; };
+// rFFT Cartesian keys: c[0..1] = the windows of real bins 32g + 8kq .. + 7 (as for 6-bit
+// keys), c[2..3] + x[0..1] = the dword-aligned 12 bytes holding imaginary bins
+// 32g + 8kq .. + 7; for token 8kq + i % 8 (tile 0 only): s, s2 = its six scales (real
+// groups 0-2, imaginary groups 0-2), n0, n1 = the words holding bin 64's real and
+// imaginary codes
+template <> struct KTile<MC_RC> { mu2 c[4]; uint32_t x[2]; mu2 s; uint32_t s2, n0, n1; };
 
 // ---- value data for lane (i, kq): dims 8i .. 8i + 7 of tokens 8kq .. 8kq + 7.  (Row
 // scales of int8 tokens are loaded one per lane and shared by DPP broadcasts: eight
@@ -138,6 +152,10 @@ __device__ __forceinline__ MOffsets m_offsets(int i, int kq) {
     else if constexpr (KC == MC_INT8) { o.k[u] = r * 128 + 32 * kq; o.ks[u] = (8 * kq + (i & 7)) * 2; }
     else if constexpr (KC == MC_F16) { o.k[u] = r * 256 + 64 * kq; o.ks[u] = 0; }
     else if constexpr (KC == MC_I6) { o.k[u] = r * 96 + ((6 * kq) & ~3u); o.ks[u] = (8 * kq + (i & 7)) * 8; }
+    else if constexpr (KC == MC_RC) {              // ks[1]: code row of token 8kq + i % 8
+      o.k[u] = r * 100 + ((6 * kq) & ~3u);
+      o.ks[u] = u == 0 ? (8 * kq + (i & 7)) * 12 : (8 * kq + (i & 7)) * 100;
+    }
     else { o.k[u] = r * 64 + 8 * kq; o.ks[u] = (8 * kq + (i & 7)) * 4; }
   }
   const uint32_t t = 8 * kq;
@@ -203,6 +221,20 @@ __device__ __forceinline__ void m_load(const M128Args& a, size_t rb, const MOffs
       d.k[u].c0 = ld<mu4>(kb, o.k[u]);
       d.k[u].c1 = ld<mu4, 16>(kb, o.k[u]);
       if (u == 0) d.k[0].s = ld<uint16_t>(ksb, o.ks[0]);
+    } else if constexpr (KC == MC_RC) {
+      // imaginary bin b starts at bit 390 + 6b: its window is the real one's plus 48 bytes
+      d.k[u].c[0] = ld<mu2, 0>(kb, o.k[u]);
+      d.k[u].c[1] = ld<mu2, 24>(kb, o.k[u]);
+      d.k[u].c[2] = ld<mu2, 48>(kb, o.k[u]);
+      d.k[u].x[0] = ld<uint32_t, 56>(kb, o.k[u]);
+      d.k[u].c[3] = ld<mu2, 72>(kb, o.k[u]);
+      d.k[u].x[1] = ld<uint32_t, 80>(kb, o.k[u]);
+      if (u == 0) {
+        d.k[0].s = ld<mu2>(ksb, o.ks[0]);
+        d.k[0].s2 = ld<uint32_t, 8>(ksb, o.ks[0]);
+        d.k[0].n0 = ld<uint32_t, 48>(kb, o.ks[1]);    // bits 384..415: bin 64 real at 384
+        d.k[0].n1 = ld<uint32_t, 96>(kb, o.ks[1]);    // bits 768..799: bin 64 imaginary at 774
+      }
     } else if constexpr (KC == MC_I6) {
       d.k[u].c[0] = ld<mu2, 0>(kb, o.k[u]);
       d.k[u].c[1] = ld<mu2, 24>(kb, o.k[u]);
@@ -317,9 +349,7 @@ __device__ __forceinline__ mh8 nf4_operand(const KTile<MC_NF4>& t, int c, const 
 // dword m holds dims (2m, 2m + 1) in its halves: each half gets its code at bits 0-5
 // (bit-field insert of two shifted copies), or-ed with 0x6400 (the fp16 1024 + c), and
 // 1056 comes off both halves in one packed subtract.
-__device__ __forceinline__ mh8 i6_operand(const KTile<MC_I6>& t, int g, int sh) {
-  const uint32_t lo = __builtin_amdgcn_alignbit(t.c[g].y, t.c[g].x, sh);   // code bits 0..31
-  const uint32_t hi = t.c[g].y >> sh;                                      // code bits 32..47
+__device__ __forceinline__ mh8 i6_codes(uint32_t lo, uint32_t hi) {
   const uint32_t hm = 0xFFFF0000u;
   uint32_t x[4];
   x[0] = ((lo << 10) & hm) | (lo & ~hm);                                                    // e0 (bit 0), e1 (6)
@@ -333,6 +363,20 @@ __device__ __forceinline__ mh8 i6_operand(const KTile<MC_I6>& t, int g, int sh) 
     r[m] = __builtin_bit_cast(uint32_t, u);
   }
   return __builtin_bit_cast(mh8, r);
+}
+__device__ __forceinline__ mh8 i6_operand(const KTile<MC_I6>& t, int g, int sh) {
+  // code bits 0..31 and 32..47 of the lane's run
+  return i6_codes(__builtin_amdgcn_alignbit(t.c[g].y, t.c[g].x, sh), t.c[g].y >> sh);
+}
+// rFFT Cartesian keys, MFMA g: real bins 32g + 8kq .. + 7 (g < 2), imaginary bins
+// 32(g - 2) + 8kq .. + 7 (g >= 2), whose runs start at bit 6 or 22 of a 3-word window
+__device__ __forceinline__ mh8 rc_operand(const KTile<MC_RC>& t, int g, int kq) {
+  if (g < 2) {
+    const int sh = (kq & 1) ? 16 : 0;
+    return i6_codes(__builtin_amdgcn_alignbit(t.c[g].y, t.c[g].x, sh), t.c[g].y >> sh);
+  }
+  const int sh = (kq & 1) ? 22 : 6;
+  return i6_codes(__builtin_amdgcn_alignbit(t.c[g].y, t.c[g].x, sh), __builtin_amdgcn_alignbit(t.x[g - 2], t.c[g].y, sh));
 }
 
 // B operand of value chunk c (dim 8i + c) for tokens 4u .. 4u + 3 of the lane's 8.
@@ -403,8 +447,49 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
     qw[c] = head_ok ? *reinterpret_cast<const mu4*>(qp) : mu4{0u, 0u, 0u, 0u};
   }
   mh8 bq[KC == MC_NF4 ? 8 : 4];
-  float qscale = 1.0f;                               // 6-bit keys: the logit's factor of the head's query scaling
-  if constexpr (KC == MC_I6) {
+  float qscale = 1.0f;                               // 6-bit / rFFT keys: the logit's factor of the head's query scaling
+  float nyr = 0.0f, nyi = 0.0f;                      // rFFT keys: the scaled query weights of bin 64
+  if constexpr (KC == MC_RC) {
+    // the head's weighted query spectrum, prepared by k_m128_qspec: chunk c holds its
+    // real (c < 2) or imaginary (c >= 2) weights of bins 32(c % 2) + 8kq .. + 7
+    float y[4][8];
+    const float* qsp = a.qspec + ((size_t)rq * a.Hq + (size_t)h * a.G + (head_ok ? hq : 0)) * kQSpec;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 v0 = *reinterpret_cast<const float4*>(qsp + 32 * c + 8 * kq);
+      const float4 v1 = *reinterpret_cast<const float4*>(qsp + 32 * c + 8 * kq + 4);
+      const float z[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[c][e] = head_ok ? z[e] : 0.0f;
+    }
+    const float2 ny = *reinterpret_cast<const float2*>(qsp + 128);
+    nyr = head_ok ? ny.x : 0.0f;
+    nyi = head_ok ? ny.y : 0.0f;
+    float amax = fmaxf(fabsf(nyr), fabsf(nyi));
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[c][e]));
+    amax = max_rows(amax);
+    int ex = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &ex);
+    const int sc = min(max(14 - ex, -100), 100);
+    qscale = ldexpf(1.0f, -sc);
+    nyr = ldexpf(nyr, sc);
+    nyi = ldexpf(nyi, sc);
+    const int part = (i >> 2) & 1;                   // as for 6-bit keys: high part / remainder columns
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mh8 r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ldexpf(y[c][e], sc);
+        const _Float16 hv = (_Float16)v;
+        r[e] = part == 0 ? hv : (_Float16)(v - (float)hv);
+      }
+      bq[c] = r;
+    }
+  } else if constexpr (KC == MC_I6) {
     // q in the key coordinates: y = kappa * H q (Sylvester order, kappa = RN32(1/sqrt(128)))
     // when the keys are rotated.  Dim bits 0-2 and 5-6 are the lane's own (e and the
     // chunk), bits 3 and 4 are lane bits 4 and 5 (kq): those two stages pair lanes
@@ -527,13 +612,13 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   float m_ref = -INFINITY;       // reference max (log2 units) of head hq
   float l_part = 0.0f;           // sum of p over this lane's tokens (head hq)
   float w_part = 0.0f;           // int8 values: sum of the fp16 weights fp16(p) * s_v (head hq)
-  const float kscale = (KC == MC_INT8) ? a.lsc * 16777216.0f : (KC == MC_I6) ? a.lsc * qscale : a.lsc;
+  const float kscale = (KC == MC_INT8) ? a.lsc * 16777216.0f : (KC == MC_I6 || KC == MC_RC) ? a.lsc * qscale : a.lsc;
 
   auto process = [&](const MStep<KC, VC>& d, int step) {
     const int t0 = step * kMStep;
     const int tb = min(t0, a.T - kMStep);            // first token of the rows loaded
     // ---- Q.K^T: tile u, output rows = tokens 8kq + 4u + r
-    constexpr int NG = KC == MC_I6 ? 4 : 2;
+    constexpr int NG = (KC == MC_I6 || KC == MC_RC) ? 4 : 2;
     mf4 cq[2][NG];                                   // [tile][key group] (group 1 for NF4, 1-3 for 6-bit keys)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -543,6 +628,8 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
       for (int c = 0; c < 4; ++c) {
         if constexpr (KC == MC_I6) {
           cq[u][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i6_operand(d.k[u], c, (kq & 1) ? 16 : 0), bq[c], cq[u][c], 0, 0, 0);
+        } else if constexpr (KC == MC_RC) {
+          cq[u][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rc_operand(d.k[u], c, kq), bq[c], cq[u][c], 0, 0, 0);
         } else if constexpr (KC == MC_NF4) {
 #pragma unroll
           for (int cc = 2 * c; cc < 2 * c + 2; ++cc)
@@ -553,6 +640,12 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
       }
     }
     float lg[8];
+    float nre = 0.0f, nim = 0.0f;                    // rFFT keys: bin 64 of token 8kq + i % 8
+    if constexpr (KC == MC_RC) {
+      const uint32_t s23 = d.k[0].s.y, s45 = d.k[0].s2;
+      nre = (float)((int)(d.k[0].n0 & 63u) - 32) * h2f((uint16_t)s23);
+      nim = (float)((int)((d.k[0].n1 >> 6) & 63u) - 32) * h2f((uint16_t)(s45 >> 16));
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -560,6 +653,17 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
         if constexpr (KC == MC_INT8) {
           const float sk = h2f((uint16_t)m_bcast(d.k[0].s, 4 * u + r));   // token 8kq + 4u + r
           lg[4 * u + r] = sk * (cq[u][0][r] * kscale - koff * a.lsc);
+        } else if constexpr (KC == MC_RC) {
+          // groups: real 0, 1 (s.x), imaginary 0 (s.y high), 1 (s2 low); bin 64 apart
+          const int j = 4 * u + r;
+          const uint32_t s01 = m_bcast(d.k[0].s.x, j), s23 = m_bcast(d.k[0].s.y, j), s45 = m_bcast(d.k[0].s2, j);
+          float t = h2f((uint16_t)s01) * cq[u][0][r];
+          t = __builtin_fmaf(h2f((uint16_t)(s01 >> 16)), cq[u][1][r], t);
+          t = __builtin_fmaf(h2f((uint16_t)(s23 >> 16)), cq[u][2][r], t);
+          t = __builtin_fmaf(h2f((uint16_t)s45), cq[u][3][r], t);
+          const float tr = f_bits((uint32_t)__builtin_amdgcn_mov_dpp((int)u_bits(t), 0x124, 0xF, 0xF, true));   // row_ror:4
+          const float ny = __builtin_fmaf(nyr, f_bits(m_bcast(u_bits(nre), j)), nyi * f_bits(m_bcast(u_bits(nim), j)));
+          lg[j] = (t + tr + ny) * kscale;
         } else if constexpr (KC == MC_I6) {
           // its four group scales; then each column adds its partner's part (row
           // rotation by 4), so every lane holds the full logit of head i % 4
@@ -722,11 +826,48 @@ namespace kvq {
 
 namespace {
 
+// Weighted query spectra for rFFT keys, one wavefront per (query row, query head):
+// Q = DFT(q) (forward sign, Q_f = sum_n q_n e^{-2 pi i f n / 128}), and the logit of a
+// key with spectrum Z is sum_f w_f (Re Q_f Re Z_f + Im Q_f Im Z_f) (Parseval for real
+// rows), w = 1/128 at bins 0 and 64, 2/128 elsewhere.  Written as w Re Q of bins 0-63,
+// w Im Q of bins 0-63, then bin 64's two, two zeros.
+__global__ __launch_bounds__(64) void k_m128_qspec(const uint16_t* q, float* qs, FftTables tw) {
+  __shared__ float x[kMD];
+  const size_t p = blockIdx.x;
+  const int t = threadIdx.x;
+  x[t] = h2f(q[p * kMD + t]);
+  x[t + 64] = h2f(q[p * kMD + 64 + t]);
+  __syncthreads();
+  float* o = qs + p * kQSpec;
+  for (int f = t; f <= 64; f += 64) {
+    float sr = 0.0f, si = 0.0f;
+    for (int n = 0; n < kMD; ++n) {
+      const int m = (f * n) & (kMD - 1);
+      const float cs = m < 64 ? tw.tw_c[m] : -tw.tw_c[m - 64];    // cos(2 pi m / 128)
+      const float sn = m < 64 ? -tw.tw_s[m] : tw.tw_s[m - 64];    // sin(2 pi m / 128)
+      sr = __builtin_fmaf(x[n], cs, sr);
+      si = __builtin_fmaf(-x[n], sn, si);
+    }
+    const float w = (f == 0 || f == 64) ? 1.0f / 128.0f : 2.0f / 128.0f;
+    if (f < 64) {
+      o[f] = sr * w;
+      o[64 + f] = si * w;
+    } else {
+      o[128] = sr * w;
+      o[129] = si * w;
+      o[130] = 0.0f;
+      o[131] = 0.0f;
+    }
+  }
+}
+
 // The kernel's codec of a key (K) or value (V) codec, or -1.
 int m128_codec(const kvq_codec& c, bool key) {
   // 6-bit signed absmax keys at group 32, unrotated or rotated over the whole row
   if (key && c.codebook == KVQ_INT_ABSMAX && c.bits == 6 && c.group == 32 && (c.rot_width <= 1 || c.rot_width == kMD))
     return MC_I6;
+  // rFFT Cartesian keys with 6-bit parts at group 32
+  if (key && c.codebook == KVQ_RFFT_CART && c.bits == 6 && c.group == 32) return MC_RC;
   if (c.rot_width > 1) return -1;
   switch (c.codebook) {
     case KVQ_TERNARY: return c.group == 8 ? MC_TER : -1;
@@ -781,23 +922,44 @@ hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
   // set-up and first loads are a fixed cost)
   const int nsteps = (s.tokens + kMStep - 1) / kMStep;
   a.S = std::max(1, std::min(decode_wave_split_count(s, pr.Hq, pr.n_q), nsteps / 8));
-  a.cs = (nsteps + a.S - 1) / a.S;
   const long long rows = (long long)s.batch * s.layers * pr.n_q;
+  const int kcod = m128_codec(pr.k->codec, true);
+  if (kcod == MC_RC && rows > 0) {
+    // the query spectra follow the partials (16-byte aligned): at most as many splits
+    // as leave room for them in the workspace
+    const size_t per = pr.ws_bytes / ((size_t)rows * pr.Hq * sizeof(float));   // floats per (row, head)
+    const long long fit = per >= (size_t)kQSpec + 4 ? (long long)(per - kQSpec - 4) / kMPart : 0;
+    if (fit < 1) return hipErrorInvalidValue;
+    a.S = (int)std::min<long long>(a.S, fit);
+  }
+  a.cs = (nsteps + a.S - 1) / a.S;
   a.items = rows * s.heads * a.S;
   a.lsc = pr.sm_scale * 1.4426950408889634f;
   a.krot = pr.k->codec.rot_width == kMD ? 1 : 0;
   if (a.items == 0) return hipSuccess;
-  if ((size_t)rows * pr.Hq * a.S * kMPart * sizeof(float) > pr.ws_bytes) return hipErrorInvalidValue;
+  const size_t part_bytes = (size_t)rows * pr.Hq * a.S * kMPart * sizeof(float);
+  if (part_bytes > pr.ws_bytes) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((a.items + kMWaves - 1) / kMWaves);
   hipError_t e;
+  if (kcod == MC_RC) {
+    const size_t off = (part_bytes + 15) / 16 * 16;
+    if (off + (size_t)rows * pr.Hq * kQSpec * sizeof(float) > pr.ws_bytes) return hipErrorInvalidValue;
+    float* qs = reinterpret_cast<float*>(static_cast<char*>(pr.ws) + off);
+    a.qspec = qs;
+    FftTables tw;
+    host_fft_tables(kMD, &tw);
+    k_m128_qspec<<<(unsigned)(rows * pr.Hq), 64, 0, st>>>(pr.q, qs, tw);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int vc = m128_codec(pr.v->codec, false);
   std::copy(host_tables().nf4_lv, host_tables().nf4_lv + 16, a.nf4);
-  switch (m128_codec(pr.k->codec, true)) {
+  switch (kcod) {
     case MC_TER: e = launch_m128_v<MC_TER>(vc, a, grid, st); break;
     case MC_SIGN: e = launch_m128_v<MC_SIGN>(vc, a, grid, st); break;
     case MC_INT8: e = launch_m128_v<MC_INT8>(vc, a, grid, st); break;
     case MC_NF4: e = launch_m128_v<MC_NF4>(vc, a, grid, st); break;
     case MC_I6: e = launch_m128_v<MC_I6>(vc, a, grid, st); break;
+    case MC_RC: e = launch_m128_v<MC_RC>(vc, a, grid, st); break;
     default: e = launch_m128_v<MC_F16>(vc, a, grid, st); break;
   }
   if (e != hipSuccess) return e;

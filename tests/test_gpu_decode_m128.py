@@ -4,7 +4,8 @@ at group 64, values ternary or sign at group 8, int8 rows, fp16 or 4-bit signed 
 at group 64, in every combination ([FMAG-6] Milestone and Best results: the extreme
 low-bit arms, NF4 keys with 4-bit values, the int8 reference row and the fp16 anchor
 layer); and 6-bit signed absmax keys at group 32, unrotated or rotated by the
-normalised Hadamard-128 (the Hadamard arm of the matched-rate transform control in the
+normalised Hadamard-128, and rFFT keys with 6-bit real and imaginary parts at group
+32 (the Hadamard and real/imaginary arms of the matched-rate transform control in the
 Fourier Magnitude thread's Colab-probe reply).
 
 Bars: attention outputs within 2e-3 relative L2 per row and lse within 1e-4 of the
@@ -21,7 +22,7 @@ from tests.test_gpu_attn import _check_decode, _gpu_decode
 
 pytestmark = pytest.mark.gpu
 
-K_CODECS = ["ter", "sign", "int8", "f16", "nf4", "i6", "i6h"]
+K_CODECS = ["ter", "sign", "int8", "f16", "nf4", "i6", "i6h", "rc"]
 V_CODECS = ["ter", "sign", "int8", "f16", "i4"]
 
 
@@ -29,7 +30,8 @@ def _codec(K, name):
     return {"ter": K.Codec(K.TERNARY, 2, 8, 0), "sign": K.Codec(K.SIGN, 1, 8, 0),
             "int8": K.Codec(K.INT8_SYM, 8, 128, 0), "f16": K.Codec(K.FP16),
             "nf4": K.Codec(K.NF4, 4, 64, 0), "i4": K.Codec(K.INT_ABSMAX, 4, 64, 0),
-            "i6": K.Codec(K.INT_ABSMAX, 6, 32, 0), "i6h": K.Codec(K.INT_ABSMAX, 6, 32, 128)}[name]
+            "i6": K.Codec(K.INT_ABSMAX, 6, 32, 0), "i6h": K.Codec(K.INT_ABSMAX, 6, 32, 128),
+            "rc": K.Codec(K.RFFT_CART, 6, 32, 0)}[name]
 
 
 def _pack(K, x, codec, shape):
@@ -101,7 +103,8 @@ def test_cache_lengths(T):
 
 
 @pytest.mark.parametrize("kname,vname", [("ter", "ter"), ("sign", "sign"), ("int8", "int8"), ("f16", "f16"),
-                                         ("nf4", "i4"), ("i6h", "f16"), ("i6", "int8")])
+                                         ("nf4", "i4"), ("i6h", "f16"), ("i6", "int8"),
+                                         ("rc", "f16"), ("rc", "i4")])
 def test_garbage_rows_past_the_keys(kname, vname):
     """Rows at and past each query's length hold NaN scales and all-ones codes (fp16: NaN
     values); the outputs equal those of a clean cache within the bars."""
@@ -159,18 +162,20 @@ def test_full_size_c4_sampled_units(kname, vname):
         assert np.abs(lse[b, l, 0, h * G:(h + 1) * G] - rl).max() < 1e-4
 
 
+@pytest.mark.parametrize("kname", ["i6h", "rc"])
 @pytest.mark.parametrize("qmag", [1e-3, 3e3])
-def test_i6_query_range(qmag):
-    """Rotated 6-bit keys with queries scaled by 1e-3 and 3e3 (fp16 inputs up to ~1.4e4,
-    whose rotation reaches past what an unscaled fp16 operand holds), G = 4 and 2."""
+def test_i6_query_range(qmag, kname):
+    """Rotated 6-bit or rFFT keys with queries scaled by 1e-3 and 3e3 (fp16 inputs up to
+    ~1.4e4, whose rotation or spectrum reaches past what an unscaled fp16 operand holds),
+    G = 4 and 2."""
     import kv_cache_bit_fwht_amd as K
     for Hq in (32, 16):
         w, Kx, Vx, q = _inputs(B=1, L=2, T=700, n_q=2, Hq=Hq)
         q = (q.astype(np.float32) * qmag).astype(np.float16)
         shape = K.Shape(w.B, w.L, w.H, w.T, w.D)
-        kp, Kd = _pack(K, Kx, _codec(K, "i6h"), shape)
+        kp, Kd = _pack(K, Kx, _codec(K, kname), shape)
         vp, Vd = _pack(K, Vx, _codec(K, "f16"), shape)
-        announce(f"m128 decode i6h query x{qmag} Hq={Hq}")
+        announce(f"m128 decode {kname} query x{qmag} Hq={Hq}")
         # the logit scale is shrunk with large queries so the softmax stays comparable
         sm = 1.0 / np.sqrt(w.D) / max(qmag, 1.0)
         out, lse = _gpu_decode(K, kp, vp, q, None, path=2, sm_scale=sm)
@@ -178,21 +183,23 @@ def test_i6_query_range(qmag):
         _check_decode(out, lse, ref_out, ref_lse, None)
 
 
-def test_full_size_c5_hadamard_sampled_units():
-    """The transform-ablation configuration's Hadamard arm at its full unit size (4
-    sequences x 8 KV heads x 32,768 tokens x 128, 32 query heads; 2 of its 16 layers;
-    keys RoPE-rotated, then FWHT-128 + 6-bit absmax at group 32; fp16 values), one decode
-    query per sequence; sampled units against the oracle."""
+@pytest.mark.parametrize("kname", ["i6h", "rc"])
+def test_full_size_c5_sampled_units(kname):
+    """The transform-ablation configuration's Hadamard and real/imaginary arms at their
+    full unit size (4 sequences x 8 KV heads x 32,768 tokens x 128, 32 query heads; 2 of
+    its 16 layers; keys RoPE-rotated, then FWHT-128 + 6-bit absmax at group 32, or rFFT
+    with 6-bit real and imaginary parts at group 32; fp16 values), one decode query per
+    sequence; sampled units against the oracle."""
     import kv_cache_bit_fwht_amd as K
     w = synth.get("c5", L=2, n_q=1)
     Kx, Vx = synth.gen_kv(w)
     q, _ = synth.gen_queries(w)
     shape = K.Shape(w.B, w.L, w.H, w.T, w.D)
-    kc = _codec(K, "i6h")
+    kc = _codec(K, kname)
     kp = K.alloc_packed(kc, shape)
     K.kvq_quantize_pack(to_dev(Kx), kp)
     vp = K.packed_from_fp16(to_dev(Vx), shape)
-    announce("m128 decode full-size c5 Hadamard arm")
+    announce(f"m128 decode full-size c5 {kname}")
     out, lse = _gpu_decode(K, kp, vp, q, None, path=2)
     out0, lse0 = _gpu_decode(K, kp, vp, q, None, path=0)
     assert np.array_equal(out0, out) and np.array_equal(lse0, lse), "path 0 should take the MFMA kernel"
