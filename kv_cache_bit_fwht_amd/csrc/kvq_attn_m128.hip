@@ -25,6 +25,10 @@
 //    so the keys enter as for 6-bit keys, MFMA g taking real groups 0, 1 then
 //    imaginary groups 0, 1; bin 64 (its own scale group) is added on the VALU.  The
 //    weighted query spectrum comes from k_m128_qspec, run just before on the stream.
+//  * rFFT polar keys (5-bit magnitude at group 32, 7-bit phase): each bin's code pair
+//    indexes a 4096-entry LDS table of the fp16 high part and remainder of A cos and
+//    A sin of its sector; per bin four k-slots (query real weight twice, imaginary
+//    twice), so two MFMAs per 16 dims' worth of bins, and the group scale after.
 //  * online softmax per head in log2 units, against a reference maximum that moves
 //    only when a logit exceeds it by more than 1, so weights stay at most 2.
 //  * P.V on v_mfma_f32_16x16x16_f16: A = fp16(p) for 4 heads (rows 0-3) x 16
@@ -67,8 +71,10 @@ constexpr int kMPart = kMD + 2;       // floats per partial: o[128], m, l
 
 // MC_NF4: keys only (NF4 at group 64); MC_I4: values only (4-bit signed absmax at group 64);
 // MC_I6: keys only (6-bit signed absmax at group 32, unrotated or Hadamard-128 rotated);
-// MC_RC: keys only (rFFT along head_dim, real and imaginary parts 6-bit at group 32)
-enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3, MC_NF4 = 4, MC_I4 = 5, MC_I6 = 6, MC_RC = 7 };
+// MC_RC: keys only (rFFT along head_dim, real and imaginary parts 6-bit at group 32);
+// MC_RP: keys only (rFFT along head_dim, 5-bit magnitude at group 32 + 7-bit phase)
+enum M128Codec { MC_TER = 0, MC_SIGN = 1, MC_INT8 = 2, MC_F16 = 3, MC_NF4 = 4, MC_I4 = 5, MC_I6 = 6, MC_RC = 7,
+                 MC_RP = 8 };
 constexpr int kQSpec = 132;           // floats per (query row, head) of a prepared query spectrum
 
 struct M128Args {
@@ -84,14 +90,15 @@ struct M128Args {
   float lsc;                          // softmax scale * log2(e)
   int krot;                           // 6-bit keys: 1 if rotated by the normalised Hadamard-128
   const float* qspec;                 // rFFT keys: [rows][Hq][kQSpec] weighted query spectra
+  float dirc[128], dirs[128];         // polar rFFT keys: cos, sin of the 128 phase sectors (binary32)
   float nf4[16];                      // NF4 levels (binary32)
 };
 
 template <int C> struct Row {          // bytes of one row's codes, scales per row
   static constexpr int code = C == MC_TER ? 32 : C == MC_SIGN ? 16 : C == MC_INT8 ? 128 : C == MC_F16 ? 256
-                              : C == MC_I6 ? 96 : C == MC_RC ? 100 : 64;
+                              : C == MC_I6 ? 96 : (C == MC_RC || C == MC_RP) ? 100 : 64;
   static constexpr int scales = C == MC_TER || C == MC_SIGN ? 16 : C == MC_INT8 ? 1 : C == MC_F16 ? 0
-                                : C == MC_I6 ? 4 : C == MC_RC ? 6 : 2;
+                                : C == MC_I6 ? 4 : C == MC_RC ? 6 : C == MC_RP ? 3 : 2;
 };
 
 // ---- key data of one 16-token tile for lane (i, kq): token tok(i, u), dims 32kq .. 32kq + 31
@@ -111,6 +118,11 @@ template <> struct KTile<MC_I6> { mu2 c[4]; mu2 s; };
 // groups 0-2, imaginary groups 0-2), n0, n1 = the words holding bin 64's real and
 // imaginary codes
 template <> struct KTile<MC_RC> { mu2 c[4]; uint32_t x[2]; mu2 s; uint32_t s2, n0, n1; };
+// rFFT polar keys: m[g] = the dword-aligned 8 bytes holding the 40 magnitude bits of bins
+// 32g + 8kq .. + 7, p[g] + px[g] = the 12 bytes holding their 56 phase bits; for token
+// 8kq + i % 8 (tile 0 only): s01 = its scales of groups 0 and 1, s2 = group 2's (bin 64),
+// n0, n1 = the words holding bin 64's magnitude and phase codes
+template <> struct KTile<MC_RP> { mu2 m[2]; mu2 p[2]; uint32_t px[2]; uint32_t s01, s2, n0, n1; };
 
 // ---- value data for lane (i, kq): dims 8i .. 8i + 7 of tokens 8kq .. 8kq + 7.  (Row
 // scales of int8 tokens are loaded one per lane and shared by DPP broadcasts: eight
@@ -135,6 +147,7 @@ __device__ __forceinline__ int tile_row(int i, int u) { return 8 * (i >> 2) + 4 
 // Per-lane byte offsets of a step's loads relative to the step's first row in each array
 // (a step's base address is wavefront-uniform: scalar base + 32-bit lane offset).
 struct MOffsets {
+  uint32_t kp[2];     // polar rFFT keys: phase codes of tile u
   uint32_t k[2];      // key codes of tile u
   uint32_t ks[2];     // key scales of tile u (ternary, sign); int8: first output token's scale
   uint32_t v;         // value codes of token 8kq, dims 8i ..
@@ -155,6 +168,12 @@ __device__ __forceinline__ MOffsets m_offsets(int i, int kq) {
     else if constexpr (KC == MC_RC) {              // ks[1]: code row of token 8kq + i % 8
       o.k[u] = r * 100 + ((6 * kq) & ~3u);
       o.ks[u] = u == 0 ? (8 * kq + (i & 7)) * 12 : (8 * kq + (i & 7)) * 100;
+    } else if constexpr (KC == MC_RP) {
+      // magnitudes of bins 8kq ..: bit 40kq, window at byte 4kq; phases: bit 325 + 56kq,
+      // window at its dword
+      o.k[u] = r * 100 + 4 * kq;
+      o.kp[u] = r * 100 + ((325 + 56 * kq) >> 5) * 4;
+      o.ks[u] = u == 0 ? (8 * kq + (i & 7)) * 6 : (8 * kq + (i & 7)) * 100;
     }
     else { o.k[u] = r * 64 + 8 * kq; o.ks[u] = (8 * kq + (i & 7)) * 4; }
   }
@@ -165,6 +184,7 @@ __device__ __forceinline__ MOffsets m_offsets(int i, int kq) {
   else if constexpr (VC == MC_F16) { o.v = t * 256 + 16 * i; o.vs = 0; }
   else { o.v = t * 64 + 4 * i; o.vs = (t + (i & 7)) * 4; }
   asm volatile("" : "+v"(o.k[0]), "+v"(o.k[1]), "+v"(o.ks[0]), "+v"(o.ks[1]), "+v"(o.v), "+v"(o.vs));
+  if constexpr (KC == MC_RP) asm volatile("" : "+v"(o.kp[0]), "+v"(o.kp[1]));
   return o;
 }
 
@@ -221,6 +241,20 @@ __device__ __forceinline__ void m_load(const M128Args& a, size_t rb, const MOffs
       d.k[u].c0 = ld<mu4>(kb, o.k[u]);
       d.k[u].c1 = ld<mu4, 16>(kb, o.k[u]);
       if (u == 0) d.k[0].s = ld<uint16_t>(ksb, o.ks[0]);
+    } else if constexpr (KC == MC_RP) {
+      // group 1 lies 32 bins on: 160 magnitude bits (20 bytes), 224 phase bits (28 bytes)
+      d.k[u].m[0] = ld<mu2, 0>(kb, o.k[u]);
+      d.k[u].m[1] = ld<mu2, 20>(kb, o.k[u]);
+      d.k[u].p[0] = ld<mu2, 0>(kb, o.kp[u]);
+      d.k[u].px[0] = ld<uint32_t, 8>(kb, o.kp[u]);
+      d.k[u].p[1] = ld<mu2, 28>(kb, o.kp[u]);
+      d.k[u].px[1] = ld<uint32_t, 36>(kb, o.kp[u]);
+      if (u == 0) {                                   // scale rows are 6 bytes: 16-bit loads
+        d.k[0].s01 = (uint32_t)ld<uint16_t>(ksb, o.ks[0]) | ((uint32_t)ld<uint16_t, 2>(ksb, o.ks[0]) << 16);
+        d.k[0].s2 = ld<uint16_t, 4>(ksb, o.ks[0]);
+        d.k[0].n0 = ld<uint32_t, 40>(kb, o.ks[1]);    // bits 320..351: bin 64 magnitude at 320
+        d.k[0].n1 = ld<uint32_t, 96>(kb, o.ks[1]);    // bits 768..799: bin 64 phase at 773
+      }
     } else if constexpr (KC == MC_RC) {
       // imaginary bin b starts at bit 390 + 6b: its window is the real one's plus 48 bytes
       d.k[u].c[0] = ld<mu2, 0>(kb, o.k[u]);
@@ -379,6 +413,29 @@ __device__ __forceinline__ mh8 rc_operand(const KTile<MC_RC>& t, int g, int kq) 
   return i6_codes(__builtin_amdgcn_alignbit(t.c[g].y, t.c[g].x, sh), __builtin_amdgcn_alignbit(t.x[g - 2], t.c[g].y, sh));
 }
 
+// nb bits at compile-time bit pos of the 64-bit (hi, lo)
+template <int POS, int NB>
+__device__ __forceinline__ uint32_t field64(uint32_t lo, uint32_t hi) {
+  if constexpr (POS + NB <= 32) return __builtin_amdgcn_ubfe(lo, POS, NB);
+  else if constexpr (POS >= 32) return __builtin_amdgcn_ubfe(hi, POS - 32, NB);
+  else return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(hi, lo, POS), 0, NB);
+}
+// rFFT polar keys, MFMA m: bins e0 = 2(m % 4), e0 + 1 of the lane's 8 in group m / 4; per
+// bin four k-slots: fp16 high part and remainder of A cos(theta), then of A sin(theta),
+// read from the block's table by (magnitude code | phase code << 5)
+template <int M>
+__device__ __forceinline__ mh8 rp_operand(const KTile<MC_RP>& t, int kq, const mu2* lut) {
+  constexpr int g = M >> 2, e0 = 2 * (M & 3);
+  const int shm = 8 * kq, shp = (325 + 56 * kq) & 31;
+  const uint32_t ml = __builtin_amdgcn_alignbit(t.m[g].y, t.m[g].x, shm), mhw = t.m[g].y >> shm;
+  const uint32_t pl = __builtin_amdgcn_alignbit(t.p[g].y, t.p[g].x, shp);
+  const uint32_t ph = __builtin_amdgcn_alignbit(t.px[g], t.p[g].y, shp);
+  const uint32_t i0 = field64<5 * e0, 5>(ml, mhw) | (field64<7 * e0, 7>(pl, ph) << 5);
+  const uint32_t i1 = field64<5 * e0 + 5, 5>(ml, mhw) | (field64<7 * e0 + 7, 7>(pl, ph) << 5);
+  const mu2 a0 = lut[i0], a1 = lut[i1];
+  return __builtin_bit_cast(mh8, mu4{a0.x, a0.y, a1.x, a1.y});
+}
+
 // B operand of value chunk c (dim 8i + c) for tokens 4u .. 4u + 3 of the lane's 8.
 // keep01 / keep23: all-ones halves for the tokens that count (partial steps).
 template <int VC, bool MASK>
@@ -414,6 +471,20 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
   // NF4 keys: the block's table of code bytes -> (high part, remainder) of two levels
   __shared__ mu2 nf4_lut[KC == MC_NF4 ? 256 : 1];
+  // polar rFFT keys: the block's table of (magnitude A, phase sector k) -> fp16 high part
+  // and remainder of RN32(A cos), then of RN32(A sin), at A | k << 5
+  __shared__ mu2 rp_lut[KC == MC_RP ? 4096 : 1];
+  if constexpr (KC == MC_RP) {
+    for (int e = threadIdx.x; e < 4096; e += kMWaves * 64) {
+      const float A = (float)(e & 31);
+      const float vc = A * a.dirc[e >> 5], vs = A * a.dirs[e >> 5];
+      const _Float16 hc = (_Float16)vc, hs = (_Float16)vs;
+      const _Float16 lc = (_Float16)(vc - (float)hc), ls = (_Float16)(vs - (float)hs);
+      rp_lut[e] = mu2{(uint32_t)__builtin_bit_cast(uint16_t, hc) | ((uint32_t)__builtin_bit_cast(uint16_t, lc) << 16),
+                      (uint32_t)__builtin_bit_cast(uint16_t, hs) | ((uint32_t)__builtin_bit_cast(uint16_t, ls) << 16)};
+    }
+    __syncthreads();
+  }
   if constexpr (KC == MC_NF4) {
     const int b = threadIdx.x;                       // 256 threads, one entry each
     const float l0 = a.nf4[b & 15], l1 = a.nf4[b >> 4];
@@ -446,10 +517,61 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
                          : (KC == MC_I6) ? qrow - 32 * kq + 32 * c + 8 * kq : qrow + 8 * c;
     qw[c] = head_ok ? *reinterpret_cast<const mu4*>(qp) : mu4{0u, 0u, 0u, 0u};
   }
-  mh8 bq[KC == MC_NF4 ? 8 : 4];
+  mh8 bq[(KC == MC_NF4 || KC == MC_RP) ? 8 : 4];
   float qscale = 1.0f;                               // 6-bit / rFFT keys: the logit's factor of the head's query scaling
   float nyr = 0.0f, nyi = 0.0f;                      // rFFT keys: the scaled query weights of bin 64
-  if constexpr (KC == MC_RC) {
+  if constexpr (KC == MC_RP) {
+    // the head's weighted query spectrum (k_m128_qspec): yr / yi = real / imaginary
+    // weights of bins 32g + 8kq .. + 7; MFMA m's B column holds, for its bins e0 and
+    // e0 + 1, (re, re, im, im) of each, matching the key operand's k-slots
+    float yr[2][8], yi[2][8];
+    const float* qsp = a.qspec + ((size_t)rq * a.Hq + (size_t)h * a.G + (head_ok ? hq : 0)) * kQSpec;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const float4 v0 = *reinterpret_cast<const float4*>(qsp + 64 * part + 32 * g + 8 * kq);
+        const float4 v1 = *reinterpret_cast<const float4*>(qsp + 64 * part + 32 * g + 8 * kq + 4);
+        const float z[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) (part == 0 ? yr : yi)[g][e] = head_ok ? z[e] : 0.0f;
+      }
+    const float2 ny = *reinterpret_cast<const float2*>(qsp + 128);
+    nyr = head_ok ? ny.x : 0.0f;
+    nyi = head_ok ? ny.y : 0.0f;
+    float amax = fmaxf(fabsf(nyr), fabsf(nyi));
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(yr[g][e]), fabsf(yi[g][e])));
+    amax = max_rows(amax);
+    int ex = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &ex);
+    const int sc = min(max(14 - ex, -100), 100);
+    qscale = ldexpf(1.0f, -sc);
+    nyr = ldexpf(nyr, sc);
+    nyi = ldexpf(nyi, sc);
+    const int part = (i >> 2) & 1;                   // high part / remainder columns
+    auto half = [&](float x) -> _Float16 {
+      const float v = ldexpf(x, sc);
+      const _Float16 hv = (_Float16)v;
+      return part == 0 ? hv : (_Float16)(v - (float)hv);
+    };
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int g = m >> 2, e0 = 2 * (m & 3);
+      mh8 r;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const _Float16 re = half(yr[g][e0 + b]), im = half(yi[g][e0 + b]);
+        r[4 * b] = re;
+        r[4 * b + 1] = re;
+        r[4 * b + 2] = im;
+        r[4 * b + 3] = im;
+      }
+      bq[m] = r;
+    }
+  } else if constexpr (KC == MC_RC) {
     // the head's weighted query spectrum, prepared by k_m128_qspec: chunk c holds its
     // real (c < 2) or imaginary (c >= 2) weights of bins 32(c % 2) + 8kq .. + 7
     float y[4][8];
@@ -612,7 +734,8 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   float m_ref = -INFINITY;       // reference max (log2 units) of head hq
   float l_part = 0.0f;           // sum of p over this lane's tokens (head hq)
   float w_part = 0.0f;           // int8 values: sum of the fp16 weights fp16(p) * s_v (head hq)
-  const float kscale = (KC == MC_INT8) ? a.lsc * 16777216.0f : (KC == MC_I6 || KC == MC_RC) ? a.lsc * qscale : a.lsc;
+  const float kscale = (KC == MC_INT8) ? a.lsc * 16777216.0f
+                       : (KC == MC_I6 || KC == MC_RC || KC == MC_RP) ? a.lsc * qscale : a.lsc;
 
   auto process = [&](const MStep<KC, VC>& d, int step) {
     const int t0 = step * kMStep;
@@ -626,7 +749,15 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
       for (int g = 0; g < NG; ++g) cq[u][g] = mf4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if constexpr (KC == MC_I6) {
+        if constexpr (KC == MC_RP) {
+          // MFMAs 2c, 2c + 1: group c / 2
+          const mh8 k0 = (c == 0) ? rp_operand<0>(d.k[u], kq, rp_lut) : (c == 1) ? rp_operand<2>(d.k[u], kq, rp_lut)
+                         : (c == 2) ? rp_operand<4>(d.k[u], kq, rp_lut) : rp_operand<6>(d.k[u], kq, rp_lut);
+          const mh8 k1 = (c == 0) ? rp_operand<1>(d.k[u], kq, rp_lut) : (c == 1) ? rp_operand<3>(d.k[u], kq, rp_lut)
+                         : (c == 2) ? rp_operand<5>(d.k[u], kq, rp_lut) : rp_operand<7>(d.k[u], kq, rp_lut);
+          cq[u][c >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, bq[2 * c], cq[u][c >> 1], 0, 0, 0);
+          cq[u][c >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, bq[2 * c + 1], cq[u][c >> 1], 0, 0, 0);
+        } else if constexpr (KC == MC_I6) {
           cq[u][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i6_operand(d.k[u], c, (kq & 1) ? 16 : 0), bq[c], cq[u][c], 0, 0, 0);
         } else if constexpr (KC == MC_RC) {
           cq[u][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rc_operand(d.k[u], c, kq), bq[c], cq[u][c], 0, 0, 0);
@@ -641,6 +772,12 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
     }
     float lg[8];
     float nre = 0.0f, nim = 0.0f;                    // rFFT keys: bin 64 of token 8kq + i % 8
+    if constexpr (KC == MC_RP) {
+      const mu2 e = rp_lut[(d.k[0].n0 & 31u) | (((d.k[0].n1 >> 5) & 127u) << 5)];
+      const float s2 = h2f((uint16_t)d.k[0].s2);
+      nre = s2 * ((float)__builtin_bit_cast(_Float16, (uint16_t)e.x) + (float)__builtin_bit_cast(_Float16, (uint16_t)(e.x >> 16)));
+      nim = s2 * ((float)__builtin_bit_cast(_Float16, (uint16_t)e.y) + (float)__builtin_bit_cast(_Float16, (uint16_t)(e.y >> 16)));
+    }
     if constexpr (KC == MC_RC) {
       const uint32_t s23 = d.k[0].s.y, s45 = d.k[0].s2;
       nre = (float)((int)(d.k[0].n0 & 63u) - 32) * h2f((uint16_t)s23);
@@ -653,6 +790,14 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
         if constexpr (KC == MC_INT8) {
           const float sk = h2f((uint16_t)m_bcast(d.k[0].s, 4 * u + r));   // token 8kq + 4u + r
           lg[4 * u + r] = sk * (cq[u][0][r] * kscale - koff * a.lsc);
+        } else if constexpr (KC == MC_RP) {
+          const int j = 4 * u + r;
+          const uint32_t s01 = m_bcast(d.k[0].s01, j);
+          float t = h2f((uint16_t)s01) * cq[u][0][r];
+          t = __builtin_fmaf(h2f((uint16_t)(s01 >> 16)), cq[u][1][r], t);
+          const float tr = f_bits((uint32_t)__builtin_amdgcn_mov_dpp((int)u_bits(t), 0x124, 0xF, 0xF, true));   // row_ror:4
+          const float ny = __builtin_fmaf(nyr, f_bits(m_bcast(u_bits(nre), j)), nyi * f_bits(m_bcast(u_bits(nim), j)));
+          lg[j] = (t + tr + ny) * kscale;
         } else if constexpr (KC == MC_RC) {
           // groups: real 0, 1 (s.x), imaginary 0 (s.y high), 1 (s2 low); bin 64 apart
           const int j = 4 * u + r;
@@ -868,6 +1013,8 @@ int m128_codec(const kvq_codec& c, bool key) {
     return MC_I6;
   // rFFT Cartesian keys with 6-bit parts at group 32
   if (key && c.codebook == KVQ_RFFT_CART && c.bits == 6 && c.group == 32) return MC_RC;
+  // rFFT polar keys: 5-bit magnitudes at group 32, 7-bit phases (128 sectors)
+  if (key && c.codebook == KVQ_RFFT_POLAR && c.bits == 5 && c.aux_bits == 7 && c.group == 32) return MC_RP;
   if (c.rot_width > 1) return -1;
   switch (c.codebook) {
     case KVQ_TERNARY: return c.group == 8 ? MC_TER : -1;
@@ -924,7 +1071,7 @@ hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
   a.S = std::max(1, std::min(decode_wave_split_count(s, pr.Hq, pr.n_q), nsteps / 8));
   const long long rows = (long long)s.batch * s.layers * pr.n_q;
   const int kcod = m128_codec(pr.k->codec, true);
-  if (kcod == MC_RC && rows > 0) {
+  if ((kcod == MC_RC || kcod == MC_RP) && rows > 0) {
     // the query spectra follow the partials (16-byte aligned): at most as many splits
     // as leave room for them in the workspace
     const size_t per = pr.ws_bytes / ((size_t)rows * pr.Hq * sizeof(float));   // floats per (row, head)
@@ -941,7 +1088,13 @@ hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
   if (part_bytes > pr.ws_bytes) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((a.items + kMWaves - 1) / kMWaves);
   hipError_t e;
-  if (kcod == MC_RC) {
+  if (kcod == MC_RP) {
+    PhaseTables pt;
+    host_phase_tables(128, &pt);
+    std::copy(pt.dir_c, pt.dir_c + 128, a.dirc);
+    std::copy(pt.dir_s, pt.dir_s + 128, a.dirs);
+  }
+  if (kcod == MC_RC || kcod == MC_RP) {
     const size_t off = (part_bytes + 15) / 16 * 16;
     if (off + (size_t)rows * pr.Hq * kQSpec * sizeof(float) > pr.ws_bytes) return hipErrorInvalidValue;
     float* qs = reinterpret_cast<float*>(static_cast<char*>(pr.ws) + off);
@@ -960,6 +1113,7 @@ hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
     case MC_NF4: e = launch_m128_v<MC_NF4>(vc, a, grid, st); break;
     case MC_I6: e = launch_m128_v<MC_I6>(vc, a, grid, st); break;
     case MC_RC: e = launch_m128_v<MC_RC>(vc, a, grid, st); break;
+    case MC_RP: e = launch_m128_v<MC_RP>(vc, a, grid, st); break;
     default: e = launch_m128_v<MC_F16>(vc, a, grid, st); break;
   }
   if (e != hipSuccess) return e;

@@ -4,9 +4,10 @@ at group 64, values ternary or sign at group 8, int8 rows, fp16 or 4-bit signed 
 at group 64, in every combination ([FMAG-6] Milestone and Best results: the extreme
 low-bit arms, NF4 keys with 4-bit values, the int8 reference row and the fp16 anchor
 layer); and 6-bit signed absmax keys at group 32, unrotated or rotated by the
-normalised Hadamard-128, and rFFT keys with 6-bit real and imaginary parts at group
-32 (the Hadamard and real/imaginary arms of the matched-rate transform control in the
-Fourier Magnitude thread's Colab-probe reply).
+normalised Hadamard-128, rFFT keys with 6-bit real and imaginary parts at group 32,
+and rFFT keys with 5-bit magnitudes at group 32 and 7-bit phases (the Hadamard,
+real/imaginary and polar arms of the matched-rate transform control in the Fourier
+Magnitude thread's Colab-probe reply).
 
 Bars: attention outputs within 2e-3 relative L2 per row and lse within 1e-4 of the
 oracle's fp64 attention over the oracle's dequantised cache; path 0 takes the same
@@ -22,7 +23,7 @@ from tests.test_gpu_attn import _check_decode, _gpu_decode
 
 pytestmark = pytest.mark.gpu
 
-K_CODECS = ["ter", "sign", "int8", "f16", "nf4", "i6", "i6h", "rc"]
+K_CODECS = ["ter", "sign", "int8", "f16", "nf4", "i6", "i6h", "rc", "rp"]
 V_CODECS = ["ter", "sign", "int8", "f16", "i4"]
 
 
@@ -31,7 +32,7 @@ def _codec(K, name):
             "int8": K.Codec(K.INT8_SYM, 8, 128, 0), "f16": K.Codec(K.FP16),
             "nf4": K.Codec(K.NF4, 4, 64, 0), "i4": K.Codec(K.INT_ABSMAX, 4, 64, 0),
             "i6": K.Codec(K.INT_ABSMAX, 6, 32, 0), "i6h": K.Codec(K.INT_ABSMAX, 6, 32, 128),
-            "rc": K.Codec(K.RFFT_CART, 6, 32, 0)}[name]
+            "rc": K.Codec(K.RFFT_CART, 6, 32, 0), "rp": K.Codec(K.RFFT_POLAR, 5, 32, 0, 7)}[name]
 
 
 def _pack(K, x, codec, shape):
@@ -104,7 +105,7 @@ def test_cache_lengths(T):
 
 @pytest.mark.parametrize("kname,vname", [("ter", "ter"), ("sign", "sign"), ("int8", "int8"), ("f16", "f16"),
                                          ("nf4", "i4"), ("i6h", "f16"), ("i6", "int8"),
-                                         ("rc", "f16"), ("rc", "i4")])
+                                         ("rc", "f16"), ("rc", "i4"), ("rp", "f16"), ("rp", "sign")])
 def test_garbage_rows_past_the_keys(kname, vname):
     """Rows at and past each query's length hold NaN scales and all-ones codes (fp16: NaN
     values); the outputs equal those of a clean cache within the bars."""
@@ -162,7 +163,7 @@ def test_full_size_c4_sampled_units(kname, vname):
         assert np.abs(lse[b, l, 0, h * G:(h + 1) * G] - rl).max() < 1e-4
 
 
-@pytest.mark.parametrize("kname", ["i6h", "rc"])
+@pytest.mark.parametrize("kname", ["i6h", "rc", "rp"])
 @pytest.mark.parametrize("qmag", [1e-3, 3e3])
 def test_i6_query_range(qmag, kname):
     """Rotated 6-bit or rFFT keys with queries scaled by 1e-3 and 3e3 (fp16 inputs up to
@@ -183,13 +184,13 @@ def test_i6_query_range(qmag, kname):
         _check_decode(out, lse, ref_out, ref_lse, None)
 
 
-@pytest.mark.parametrize("kname", ["i6h", "rc"])
+@pytest.mark.parametrize("kname", ["i6h", "rc", "rp"])
 def test_full_size_c5_sampled_units(kname):
-    """The transform-ablation configuration's Hadamard and real/imaginary arms at their
-    full unit size (4 sequences x 8 KV heads x 32,768 tokens x 128, 32 query heads; 2 of
-    its 16 layers; keys RoPE-rotated, then FWHT-128 + 6-bit absmax at group 32, or rFFT
-    with 6-bit real and imaginary parts at group 32; fp16 values), one decode query per
-    sequence; sampled units against the oracle."""
+    """The transform-ablation configuration's three arms at their full unit size (4 sequences x 8 KV heads x 32,768 tokens x 128, 32 query heads; 2 of
+    its 16 layers; keys RoPE-rotated, then FWHT-128 + 6-bit absmax at group 32, rFFT with
+    6-bit real and imaginary parts at group 32, or rFFT with 5-bit magnitudes at group 32
+    and 7-bit phases; fp16 values), one decode query per sequence; sampled units against
+    the oracle."""
     import kv_cache_bit_fwht_amd as K
     w = synth.get("c5", L=2, n_q=1)
     Kx, Vx = synth.gen_kv(w)
