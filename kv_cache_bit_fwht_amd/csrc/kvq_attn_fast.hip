@@ -100,8 +100,9 @@ struct FArgs {
   float vkappa;
   float sm_scale;
   float voff;                      // value code offset: 2 (signed absmax, c - 2) or 1.5 (symmetric grid, c - 1.5)
-  uint32_t vlut_lo, vlut_hi;       // 2-bit Lloyd-Max values: low and high bytes of the four levels in fp16
-  int vll;                         // 1: 2-bit Lloyd-Max values (levels from vlut, no offset)
+  uint32_t vlut_lo, vlut_hi;       // Lloyd-Max values: low and high bytes of levels 0-3 in fp16
+  uint32_t vlut_lo2, vlut_hi2;     // 3-bit Lloyd-Max values: the same of levels 4-7
+  int vll;                         // 1: Lloyd-Max values (levels from vlut, no offset)
   int blocks_per_unit;             // blocks (and partials) per (query row, KV head)
   int chunk_log2;                  // log2 of the 32-token steps per chunk (>= 3)
   int* ctr;                        // per (query row, KV head) chunk counters, or null (static chunks)
@@ -501,9 +502,9 @@ bool fast_decode_supported(const kvq_packed& k, const kvq_packed& v, int Hq) {
   if (kb < 2 || kb > 5) return false;
   if (k.codec.group != 128 && k.codec.group != 256) return false;
   // 2- or 4-bit values: signed absmax (levels c - 2^(b-1)) or the symmetric grid (levels c - (2^b - 1)/2)
-  // affine 2- and 4-bit value grids, and 2-bit Lloyd-Max levels (a four-entry table)
+  // affine 2- to 4-bit value grids, and 2- or 3-bit Lloyd-Max levels (four- or eight-entry tables)
   if (v.codec.codebook == KVQ_LLOYD) {
-    if (v.codec.bits != 2) return false;
+    if (v.codec.bits != 2 && v.codec.bits != 3) return false;
   } else if (v.codec.codebook != KVQ_INT_ABSMAX && v.codec.codebook != KVQ_INT_SYM) {
     return false;
   }
@@ -543,16 +544,16 @@ size_t fast_part_bytes(const kvq_shape& s, int Hq, int n_q) {
 
 template <int VB, int KB>
 static void launch_mfma(const FArgs& a, dim3 grid, hipStream_t st) {
-  if constexpr (VB == 2) {
-    if (a.vll) {                                     // 2-bit Lloyd-Max values
+  if constexpr (VB == 2 || VB == 3) {
+    if (a.vll) {                                     // 2- and 3-bit Lloyd-Max values
       if (a.nks == 2) {
-        if (a.nvs == 1) k_decode_mfma<2, 1, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
-        else if (a.nvs == 2) k_decode_mfma<2, 2, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
-        else k_decode_mfma<2, 4, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        if (a.nvs == 1) k_decode_mfma<2, 1, VB, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        else if (a.nvs == 2) k_decode_mfma<2, 2, VB, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        else k_decode_mfma<2, 4, VB, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
       } else {
-        if (a.nvs == 1) k_decode_mfma<1, 1, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
-        else if (a.nvs == 2) k_decode_mfma<1, 2, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
-        else k_decode_mfma<1, 4, 2, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        if (a.nvs == 1) k_decode_mfma<1, 1, VB, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        else if (a.nvs == 2) k_decode_mfma<1, 2, VB, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
+        else k_decode_mfma<1, 4, VB, KB, false, true><<<grid, kFastBlock, 0, st>>>(a);
       }
       return;
     }
@@ -725,11 +726,13 @@ hipError_t launch_decode_fast(const AttnProblem& pr, hipStream_t st, bool* mean_
   if (v.codec.codebook == KVQ_LLOYD) {               // levels rounded to fp16, as the matrix cores take them
     a.vll = 1;
     a.voff = 0.0f;
-    a.vlut_lo = a.vlut_hi = 0;
-    for (int c = 0; c < 4; ++c) {
-      const uint16_t hb = __builtin_bit_cast(uint16_t, (_Float16)host_tables().lloyd_lv[0][c]);
-      a.vlut_lo |= (uint32_t)(hb & 0xFFu) << (8 * c);
-      a.vlut_hi |= (uint32_t)(hb >> 8) << (8 * c);
+    a.vlut_lo = a.vlut_hi = a.vlut_lo2 = a.vlut_hi2 = 0;
+    for (int c = 0; c < (1 << vb); ++c) {
+      const uint16_t hb = __builtin_bit_cast(uint16_t, (_Float16)host_tables().lloyd_lv[vb - 2][c]);
+      uint32_t& lo = c < 4 ? a.vlut_lo : a.vlut_lo2;
+      uint32_t& hi = c < 4 ? a.vlut_hi : a.vlut_hi2;
+      lo |= (uint32_t)(hb & 0xFFu) << (8 * (c & 3));
+      hi |= (uint32_t)(hb >> 8) << (8 * (c & 3));
     }
   }
   a.blocks_per_unit = fast_blocks_per_unit(s, pr.n_q);

@@ -49,7 +49,8 @@ def test_fast_c3_shape_shrunk():
                                      "k2_norot_G2", "k2_kg256_rot128", "k2_v4_rot", "vlloyd", "vlloyd_rot",
                                      "vlloyd_g64", "vlloyd_g256_k256", "vlloyd_k3_G1", "vlloyd_k2_rot128",
                                      "vlloyd_k5_G2", "v3", "v3_sym_rot", "v3_g64", "v3_g256_k2", "v3_k3_G1",
-                                     "v3_sym_k5_G2"])
+                                     "v3_sym_k5_G2", "vlloyd3", "vlloyd3_rot", "vlloyd3_g64", "vlloyd3_g256_k2",
+                                     "vlloyd3_k3_G1", "vlloyd3_k5_G2"])
 def test_fast_variants(variant):
     import kv_cache_bit_fwht_amd as K
     kc, vc = K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0)
@@ -143,6 +144,20 @@ def test_fast_variants(variant):
     elif variant == "v3_sym_k5_G2":
         w = w.with_sizes(Hq=8)
         kc, vc = K.Codec(K.INT_ABSMAX, 5, 128, 0), K.Codec(K.INT_SYM, 3, 64, 128)
+    elif variant == "vlloyd3":
+        vc = K.Codec(K.LLOYD, 3, 128, 0)
+    elif variant == "vlloyd3_rot":
+        vc = K.Codec(K.LLOYD, 3, 128, 256)
+    elif variant == "vlloyd3_g64":
+        vc = K.Codec(K.LLOYD, 3, 64, 256)
+    elif variant == "vlloyd3_g256_k2":
+        kc, vc = K.Codec(K.INT_ABSMAX, 2, 256, 256), K.Codec(K.LLOYD, 3, 256, 0)
+    elif variant == "vlloyd3_k3_G1":
+        w = w.with_sizes(Hq=4)
+        kc, vc = K.Codec(K.INT_ABSMAX, 3, 128, 256), K.Codec(K.LLOYD, 3, 128, 256)
+    elif variant == "vlloyd3_k5_G2":
+        w = w.with_sizes(Hq=8)
+        kc, vc = K.Codec(K.INT_ABSMAX, 5, 128, 0), K.Codec(K.LLOYD, 3, 64, 128)
     announce(f"mfma variant {variant}")
     _case(K, w, kc, vc)
 
@@ -165,14 +180,15 @@ def test_fast_many_blocks_per_unit():
     _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), kv_len)
 
 
-def test_fast_lloyd_values_many_blocks_and_lengths():
-    """2-bit Lloyd-Max values (rotated, [E22L] Result's next test): 32 blocks per unit on a
-    counter, causal lengths ending mid-step."""
+@pytest.mark.parametrize("vb", [2, 3])
+def test_fast_lloyd_values_many_blocks_and_lengths(vb):
+    """2- and 3-bit Lloyd-Max values (rotated, [E22L] Result's next test): 32 blocks per
+    unit on a counter, causal lengths ending mid-step."""
     import kv_cache_bit_fwht_amd as K
     w = synth.get("c3", L=1, T=16384, n_q=3)
     kv_len = np.array([[[16384, 9001, 31]]], dtype=np.int32)
-    announce("mfma Lloyd-Max values, many blocks per unit")
-    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.LLOYD, 2, 128, 256), kv_len)
+    announce(f"mfma {vb}-bit Lloyd-Max values, many blocks per unit")
+    _case(K, w, K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.LLOYD, vb, 128, 256), kv_len)
 
 
 def test_fast_3bit_values_many_blocks_and_lengths():
@@ -328,7 +344,7 @@ DIRTY = [(352, [[300, 289], [1, 299]], 300), (333, [[332, 289], [1, 299]], 332),
          (1000, [[700, 33], [32, 699]], 700)]
 
 
-@pytest.mark.parametrize("vname", ["absmax2", "lloyd2", "sym3"])
+@pytest.mark.parametrize("vname", ["absmax2", "lloyd2", "sym3", "lloyd3"])
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("T,lens,dirty_from", DIRTY)
 def test_unwritten_rows_past_the_lengths_do_not_matter(path, T, lens, dirty_from, vname):
@@ -342,7 +358,7 @@ def test_unwritten_rows_past_the_lengths_do_not_matter(path, T, lens, dirty_from
     q, _ = synth.gen_queries(w)
     kc = K.Codec(K.INT_ABSMAX, 4, 128, 256)
     vc = {"absmax2": K.Codec(K.INT_ABSMAX, 2, 128, 0), "lloyd2": K.Codec(K.LLOYD, 2, 128, 256),
-          "sym3": K.Codec(K.INT_SYM, 3, 128, 0)}[vname]
+          "sym3": K.Codec(K.INT_SYM, 3, 128, 0), "lloyd3": K.Codec(K.LLOYD, 3, 128, 256)}[vname]
     kv_len = np.array([lens], dtype=np.int32)
     assert kv_len.max() <= dirty_from
     announce(f"unwritten rows past the lengths, path {path}, T={T}, from {dirty_from}, V {vname}")
