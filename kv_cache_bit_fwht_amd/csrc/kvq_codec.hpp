@@ -8,11 +8,46 @@
 
 namespace kvq {
 
+// Value of lane (l ^ X) of this lane's 16-lane row, X = 1, 2, 4 or 8 (DPP moves; every
+// lane of the row active).  X = 4: lanes of banks 0 and 2 take lane + 4, lanes of banks
+// 1 and 3 lane - 4.
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (X == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
+  else if constexpr (X == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  else if constexpr (X == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror 8
+  else {
+    r = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);                      // row_shl 4
+    r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, false);                      // row_shr 4
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// One butterfly stage of stride 16 X across the LPT lanes of a row: the lane without bit
+// X takes (own + partner), the one with it (partner - own), the same two binary32
+// operations as a butterfly held in one lane.
+template <int X>
+__device__ __forceinline__ void fwht_lane_stage(float v[16], int j) {
+  const bool hi = (j & X) != 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p = lane_xor<X>(v[i]);
+    v[i] = hi ? p - v[i] : v[i] + p;
+  }
+}
+
 // Normalised Walsh-Hadamard transform of the rows held by this block (layout
 // 1 in, layout 1 out).  Butterfly stages in ascending stride, each pair (i, i+s)
-// -> (RN32(u_i + u_{i+s}), RN32(u_i - u_{i+s})), then RN32(u * kappa).
+// -> (RN32(u_i + u_{i+s}), RN32(u_i - u_{i+s})), then RN32(u * kappa).  Strides
+// below 16 are within a lane; strides 16 .. 128 pair lanes 1, 2, 4 and 8 apart within
+// the row's LPT lanes (rows of D <= 256 fill at most one 16-lane row).  Every lane of
+// the wavefront must call it (no barrier, no LDS: `rowlds` is unused).
 __device__ __forceinline__ void fwht_rows(float v[16], float* rowlds, int j, int LPT, int W,
                                           float kappa) {
+  (void)rowlds;
+  (void)LPT;
 #pragma unroll
   for (int s = 1; s < 16; s <<= 1) {
     if (s < W) {
@@ -25,32 +60,10 @@ __device__ __forceinline__ void fwht_rows(float v[16], float* rowlds, int j, int
         }
     }
   }
-  if (W > 16) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) rowlds[17 * j + k] = v[k];
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = rowlds[pidx(j + LPT * r)];
-#pragma unroll
-    for (int rs = 1; rs < 16; rs <<= 1) {
-      const int S = rs * LPT;             // stride in value index
-      if (S >= 16 && S < W) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (!(i & rs)) {
-            const float a = v[i], b = v[i + rs];
-            v[i] = a + b;
-            v[i + rs] = a - b;
-          }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rowlds[pidx(j + LPT * r)] = v[r];
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = rowlds[17 * j + k];
-    __syncthreads();
-  }
+  if (W > 16) fwht_lane_stage<1>(v, j);
+  if (W > 32) fwht_lane_stage<2>(v, j);
+  if (W > 64) fwht_lane_stage<4>(v, j);
+  if (W > 128) fwht_lane_stage<8>(v, j);
   if (W > 1) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) v[k] = v[k] * kappa;
