@@ -15,9 +15,9 @@ template <int X>
 __device__ __forceinline__ float lane_xor(float v) {
   const int x = __builtin_bit_cast(int, v);
   int r;
-  if constexpr (X == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
-  else if constexpr (X == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
-  else if constexpr (X == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror 8
+  if constexpr (X == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);         // quad_perm 1,0,3,2
+  else if constexpr (X == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);    // quad_perm 2,3,0,1
+  else if constexpr (X == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);   // row_ror 8
   else {
     r = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);                      // row_shl 4
     r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, false);                      // row_shr 4
@@ -27,15 +27,14 @@ __device__ __forceinline__ float lane_xor(float v) {
 
 // One butterfly stage of stride 16 X across the LPT lanes of a row: the lane without bit
 // X takes (own + partner), the one with it (partner - own), the same two binary32
-// operations as a butterfly held in one lane.
+// operations as a butterfly held in one lane.  partner - own is computed as
+// partner + (-own), which is the same IEEE operation, so one add serves both lanes.
 template <int X>
 __device__ __forceinline__ void fwht_lane_stage(float v[16], int j) {
-  const bool hi = (j & X) != 0;
+  const uint32_t sg = (j & X) ? 0x80000000u : 0u;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float p = lane_xor<X>(v[i]);
-    v[i] = hi ? p - v[i] : v[i] + p;
-  }
+  for (int i = 0; i < 16; ++i)
+    v[i] = lane_xor<X>(v[i]) + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[i]) ^ sg);
 }
 
 // Normalised Walsh-Hadamard transform of the rows held by this block (layout
