@@ -1250,11 +1250,9 @@ struct EArgs {
 };
 
 __global__ __launch_bounds__(kBlock) void k_kverr(EArgs a) {
-  __shared__ float lds[kBlock * 17];
   __shared__ double red[2][kBlock];
   const int tid = threadIdx.x;
   const int LPT = 1 << a.lpt_log2, j = tid & (LPT - 1), rloc = tid >> a.lpt_log2, RPB = kBlock >> a.lpt_log2;
-  float* rowlds = lds + rloc * 17 * LPT;
   const long long unit = blockIdx.y;
   const int per = (a.T + a.chunks - 1) / a.chunks;
   const int t0 = blockIdx.x * per, t1 = min(a.T, t0 + per);
@@ -1277,7 +1275,7 @@ __global__ __launch_bounds__(kBlock) void k_kverr(EArgs a) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] = 0.0f;
     }
-    if (a.c.W > 1) fwht_rows(v, rowlds, j, LPT, a.c.W, a.c.kappa);
+    if (a.c.W > 1) fwht_rows(v, j, a.c.W, a.c.kappa);
     if (active) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {

@@ -41,12 +41,9 @@ __device__ __forceinline__ void fwht_lane_stage(float v[16], int j) {
 // 1 in, layout 1 out).  Butterfly stages in ascending stride, each pair (i, i+s)
 // -> (RN32(u_i + u_{i+s}), RN32(u_i - u_{i+s})), then RN32(u * kappa).  Strides
 // below 16 are within a lane; strides 16 .. 128 pair lanes 1, 2, 4 and 8 apart within
-// the row's LPT lanes (rows of D <= 256 fill at most one 16-lane row).  Every lane of
-// the wavefront must call it (no barrier, no LDS: `rowlds` is unused).
-__device__ __forceinline__ void fwht_rows(float v[16], float* rowlds, int j, int LPT, int W,
-                                          float kappa) {
-  (void)rowlds;
-  (void)LPT;
+// the row's lanes (j = the lane's index in its row; rows of D <= 256 fill at most one
+// 16-lane row).  Every lane of the wavefront must call it.
+__device__ __forceinline__ void fwht_rows(float v[16], int j, int W, float kappa) {
 #pragma unroll
   for (int s = 1; s < 16; s <<= 1) {
     if (s < W) {

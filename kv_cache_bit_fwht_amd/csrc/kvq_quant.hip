@@ -86,7 +86,6 @@ __device__ __forceinline__ void pre_row(float (&v)[16], const float* mean, const
 
 template <int CB, int BITS>
 __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
-  __shared__ float lds[kBlock * 17];
   __shared__ float2 nf4_cells[CB == KVQ_NF4 ? 256 : 1];
   const int tid = threadIdx.x;
   if constexpr (CB == KVQ_NF4) {
@@ -98,7 +97,6 @@ __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
   const int j = tid & (LPT - 1);
   const int rloc = tid >> a.lpt_log2;
   const int RPB = kBlock >> a.lpt_log2;
-  float* rowlds = lds + rloc * 17 * LPT;
   const size_t row_bytes = (size_t)a.D * BITS / 8;
   uint8_t* cbytes = reinterpret_cast<uint8_t*>(a.codes);
   for (long long base = (long long)blockIdx.x * RPB; base < a.rows; base += (long long)gridDim.x * RPB) {
@@ -130,7 +128,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
       row_unit(row, a.T, a.H, a.L, l, h);
       pre_row(v, a.mean, a.chan, ((size_t)l * a.H + h) * a.D + 16 * j);
     }
-    if (a.W > 1) fwht_rows(v, rowlds, j, LPT, a.W, a.kappa);
+    if (a.W > 1) fwht_rows(v, j, a.W, a.kappa);
     uint32_t c[16];
     uint16_t s16[2], z16[2];
     encode16<CB, BITS>(v, a.g, a.tab, c, s16, z16, nf4_cells);
@@ -157,13 +155,11 @@ __global__ __launch_bounds__(kBlock) void k_quantize(QArgs a) {
 
 template <int CB, int BITS>
 __global__ __launch_bounds__(kBlock) void k_dequant(QArgs a) {
-  __shared__ float lds[kBlock * 17];
   const int tid = threadIdx.x;
   const int LPT = 1 << a.lpt_log2;
   const int j = tid & (LPT - 1);
   const int rloc = tid >> a.lpt_log2;
   const int RPB = kBlock >> a.lpt_log2;
-  float* rowlds = lds + rloc * 17 * LPT;
   const size_t row_bytes = (size_t)a.D * BITS / 8;
   const uint8_t* cbytes = reinterpret_cast<const uint8_t*>(a.codes);
   for (long long base = (long long)blockIdx.x * RPB; base < a.rows; base += (long long)gridDim.x * RPB) {
@@ -191,7 +187,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant(QArgs a) {
     unpack16<BITS>(w, c);
     float v[16];
     decode16<CB, BITS>(c, s16, z16, a.tab, v);
-    if (a.W > 1) fwht_rows(v, rowlds, j, LPT, a.W, a.kappa);
+    if (a.W > 1) fwht_rows(v, j, a.W, a.kappa);
     if (!active) continue;
     if (a.chan != nullptr || a.mean != nullptr) {
       int l, h;
