@@ -260,8 +260,8 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
  * above), 2 = the MFMA kernel, KVQ_ERR_UNSUPPORTED unless: head_dim 256, at least
  * 32 tokens, at most 4 query heads per KV head, K INT_ABSMAX
  * 2-, 3-, 4- or 5-bit at group 128 or 256 (any rotation, optional chan_scale), V
- * INT_ABSMAX or INT_SYM, 2-, 3- or 4-bit, or LLOYD 2-bit, at group 64..256 without
- * chan_scale (any rotation) -- the 4-bit-key / 2-bit-value arms of [E22L] What I
+ * INT_ABSMAX or INT_SYM, 2-, 3- or 4-bit, or LLOYD 2- or 3-bit, at group 64..256
+ * without chan_scale (any rotation) -- the 4-bit-key / 2-bit-value arms of [E22L] What I
  * tested, the Gaussian Lloyd-Max values on rotated values of [E22L] Result, the
  * 2-bit keys of the per-layer allocation of [E21W] Result, the
  * symmetric value grid of [E22L] Result, 4-bit values ([LCPP] Finding 1) and the
@@ -270,7 +270,12 @@ kvq_status kvq_decode_attn(const kvq_packed* k, const kvq_packed* v, int32_t q_h
  * 128, FP16 or NF4 at group 64, V TERNARY or SIGN at group 8, INT8_SYM at group 128,
  * FP16 or 4-bit INT_ABSMAX at group 64, without rotation, chan_scale or mean -- the
  * extreme low-bit arms, NF4 keys with 4-bit values, the int8 reference row and the
- * fp16 anchor layer of [FMAG-6] Milestone and Best results. */
+ * fp16 anchor layer of [FMAG-6] Milestone and Best results -- and also K 6-bit
+ * INT_ABSMAX at group 32 (unrotated or rot_width 128), RFFT_CART 6-bit at group 32 or
+ * RFFT_POLAR 5-bit magnitude + 7-bit phase at group 32 (the Hadamard, real/imaginary
+ * and polar arms of the matched-rate transform control, [FMAG-R] Colab-probe reply)
+ * with any of those values.  With rFFT keys the weighted query spectra are kept in
+ * the workspace after the partials (the call then uses fewer splits). */
 kvq_status kvq_decode_attn_ex(const kvq_packed* k, const kvq_packed* v, int32_t q_heads,
                               int32_t n_q, const uint16_t* q, const int32_t* kv_len,
                               float sm_scale, float* out, float* lse, void* ws,
