@@ -978,28 +978,30 @@ namespace {
 // w Im Q of bins 0-63, then bin 64's two, two zeros.
 __global__ __launch_bounds__(64) void k_m128_qspec(const uint16_t* q, float* qs, FftTables tw) {
   __shared__ float x[kMD];
+  __shared__ float2 w[kMD];                          // (cos, sin) of 2 pi m / 128
   const size_t p = blockIdx.x;
   const int t = threadIdx.x;
   x[t] = h2f(q[p * kMD + t]);
   x[t + 64] = h2f(q[p * kMD + 64 + t]);
+  w[t] = make_float2(tw.tw_c[t], -tw.tw_s[t]);
+  w[t + 64] = make_float2(-tw.tw_c[t], tw.tw_s[t]);
   __syncthreads();
   float* o = qs + p * kQSpec;
   for (int f = t; f <= 64; f += 64) {
     float sr = 0.0f, si = 0.0f;
+#pragma unroll 8
     for (int n = 0; n < kMD; ++n) {
-      const int m = (f * n) & (kMD - 1);
-      const float cs = m < 64 ? tw.tw_c[m] : -tw.tw_c[m - 64];    // cos(2 pi m / 128)
-      const float sn = m < 64 ? -tw.tw_s[m] : tw.tw_s[m - 64];    // sin(2 pi m / 128)
-      sr = __builtin_fmaf(x[n], cs, sr);
-      si = __builtin_fmaf(-x[n], sn, si);
+      const float2 cs = w[(f * n) & (kMD - 1)];
+      sr = __builtin_fmaf(x[n], cs.x, sr);
+      si = __builtin_fmaf(-x[n], cs.y, si);
     }
-    const float w = (f == 0 || f == 64) ? 1.0f / 128.0f : 2.0f / 128.0f;
+    const float wf = (f == 0 || f == 64) ? 1.0f / 128.0f : 2.0f / 128.0f;
     if (f < 64) {
-      o[f] = sr * w;
-      o[64 + f] = si * w;
+      o[f] = sr * wf;
+      o[64 + f] = si * wf;
     } else {
-      o[128] = sr * w;
-      o[129] = si * w;
+      o[128] = sr * wf;
+      o[129] = si * wf;
       o[130] = 0.0f;
       o[131] = 0.0f;
     }
