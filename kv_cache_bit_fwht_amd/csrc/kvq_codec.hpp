@@ -8,9 +8,10 @@
 
 namespace kvq {
 
-// Value of lane (l ^ X) of this lane's 16-lane row, X = 1, 2, 4 or 8 (DPP moves; every
-// lane of the row active).  X = 4: lanes of banks 0 and 2 take lane + 4, lanes of banks
-// 1 and 3 lane - 4.
+// Value of lane (l ^ X) of this lane's 16-lane row, X = 1, 2, 4 or 8 (every lane of the
+// row active): DPP moves for 1, 2 and 8 (folded into the add that uses them), a
+// swizzle in xor mode for 4 (it runs on the LDS crossbar, not the VALU, where DPP would
+// take two masked moves).
 template <int X>
 __device__ __forceinline__ float lane_xor(float v) {
   const int x = __builtin_bit_cast(int, v);
@@ -18,10 +19,7 @@ __device__ __forceinline__ float lane_xor(float v) {
   if constexpr (X == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);         // quad_perm 1,0,3,2
   else if constexpr (X == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);    // quad_perm 2,3,0,1
   else if constexpr (X == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);   // row_ror 8
-  else {
-    r = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);                      // row_shl 4
-    r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, false);                      // row_shr 4
-  }
+  else r = __builtin_amdgcn_ds_swizzle(x, (4 << 10) | 0x1F);                           // and 31, xor 4
   return __builtin_bit_cast(float, r);
 }
 
@@ -32,9 +30,17 @@ __device__ __forceinline__ float lane_xor(float v) {
 template <int X>
 __device__ __forceinline__ void fwht_lane_stage(float v[16], int j) {
   const uint32_t sg = (j & X) ? 0x80000000u : 0u;
+  if constexpr (X == 4) {                            // swizzles: all issued first, then the adds
+    float p[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    v[i] = lane_xor<X>(v[i]) + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[i]) ^ sg);
+    for (int i = 0; i < 16; ++i) p[i] = lane_xor<X>(v[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = p[i] + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[i]) ^ sg);
+  } else {                                           // DPP moves fold into the adds
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      v[i] = lane_xor<X>(v[i]) + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[i]) ^ sg);
+  }
 }
 
 // Normalised Walsh-Hadamard transform of the rows held by this block (layout
