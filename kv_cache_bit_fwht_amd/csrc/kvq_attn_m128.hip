@@ -467,7 +467,7 @@ __device__ __forceinline__ mh4 value_operand(const VData<VC>& v, int u, int c, u
 }
 
 template <int KC, int VC>
-__global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 : 2) void k_decode_m128(M128Args a) {
+__global__ __launch_bounds__(kMWaves * 64, ((KC <= MC_SIGN && VC <= MC_SIGN) || (KC == MC_NF4 && VC == MC_I4)) ? 3 : 2) void k_decode_m128(M128Args a) {
   const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
   // NF4 keys: the block's table of code bytes -> (high part, remainder) of two levels
   __shared__ mu2 nf4_lut[KC == MC_NF4 ? 256 : 1];
@@ -737,6 +737,9 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
   const float kscale = (KC == MC_INT8) ? a.lsc * 16777216.0f
                        : (KC == MC_I6 || KC == MC_RC || KC == MC_RP) ? a.lsc * qscale : a.lsc;
 
+  // byte address for ds_bpermute of copy 0 of this lane's head in its row
+  constexpr bool kDedup = KC != MC_RP;
+  const int gsrc = 4 * ((lane & 0x30) | (i & 3));
   auto process = [&](const MStep<KC, VC>& d, int step) {
     const int t0 = step * kMStep;
     const int tb = min(t0, a.T - kMStep);            // first token of the rows loaded
@@ -839,10 +842,28 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
         }
       }
     }
-    // ---- online softmax (lanes with equal i % 4 hold the same head)
-    float mt = lg[0];
+    // ---- online softmax.  Lanes with equal i % 4 hold the same head, and the four column
+    // copies of a row (lanes i, i + 4, i + 8, i + 12) hold the same logits: each copy takes
+    // one output row of each tile (row i / 4: token 8kq + 4u + i / 4), so the weights are
+    // computed once.
+    // (Polar rFFT keys keep the per-lane form: their registers have no room for the gather.)
+    float lu[2];
+    float mt;
+    if constexpr (kDedup) {
 #pragma unroll
-    for (int k = 1; k < 8; ++k) mt = fmaxf(mt, lg[k]);
+      for (int u = 0; u < 2; ++u) {
+        const float x01 = (i & 4) ? lg[4 * u + 1] : lg[4 * u];
+        const float x23 = (i & 4) ? lg[4 * u + 3] : lg[4 * u + 2];
+        lu[u] = (i & 8) ? x23 : x01;
+      }
+      mt = fmaxf(lu[0], lu[1]);
+      mt = fmaxf(mt, f_bits((uint32_t)__builtin_amdgcn_mov_dpp((int)u_bits(mt), 0x124, 0xF, 0xF, false)));   // row_ror:4
+      mt = fmaxf(mt, f_bits((uint32_t)__builtin_amdgcn_mov_dpp((int)u_bits(mt), 0x128, 0xF, 0xF, false)));   // row_ror:8
+    } else {
+      mt = lg[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) mt = fmaxf(mt, lg[k]);
+    }
     // (lane shuffles through the LDS crossbar here: this loop's VALU is the busy unit)
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -863,26 +884,42 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
         acc[c][3] *= a3;
       }
     }
-    // ---- P.V
+    // ---- P.V.  The lane's two weights (fp32 into l_part, its share of the head's sum),
+    // then as fp16 to every lane of its head in this row: lane i gathers token r of each
+    // tile from copy r (lane 4r + i % 4).
+    mh2 pg[4];
+    if constexpr (kDedup) {
+      const float pu0 = __builtin_amdgcn_exp2f(lu[0] - m_ref), pu1 = __builtin_amdgcn_exp2f(lu[1] - m_ref);   // masked: 0
+      l_part += pu0 + pu1;
+      const int pp = (int)__builtin_bit_cast(uint32_t, mh2{(_Float16)pu0, (_Float16)pu1});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pg[r] = __builtin_bit_cast(mh2, __builtin_amdgcn_ds_bpermute(gsrc + 16 * r, pp));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float q0 = __builtin_amdgcn_exp2f(lg[r] - m_ref), q1 = __builtin_amdgcn_exp2f(lg[4 + r] - m_ref);
+        l_part += q0 + q1;
+        pg[r] = mh2{(_Float16)q0, (_Float16)q1};
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       mh4 ap;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(lg[4 * u + r] - m_ref);   // masked: exp2(-inf) = 0
-        l_part += p;
+        const _Float16 p = pg[r][u];                 // fp16 weight of token 8kq + 4u + r
         if constexpr (VC == MC_INT8 || VC == MC_I4) {
           // A = fp16(p) * the value scale; 4-bit values: rows 0-3 take group 0's scale (dims
           // 0-63), rows 4-7 group 1's.  A masked token may sit on a row nobody wrote yet: its
           // weight is 0, not 0 * scale.
           uint32_t sw = m_bcast(d.v.s, 4 * u + r);   // token 8kq + 4u + r
           if constexpr (VC == MC_I4) sw = (i & 4) ? (sw >> 16) : sw;
-          _Float16 w = (_Float16)p * __builtin_bit_cast(_Float16, (uint16_t)sw);
-          w = (p == 0.0f) ? (_Float16)0.0f : w;
+          _Float16 w = p * __builtin_bit_cast(_Float16, (uint16_t)sw);
+          w = (p == (_Float16)0.0f) ? (_Float16)0.0f : w;
           w_part += (float)w;
           ap[r] = w;
         } else {
-          ap[r] = (_Float16)p;
+          ap[r] = p;
         }
       }
       // The B values of masked tokens must be 0, not NaN (their rows may hold anything):
@@ -929,8 +966,12 @@ __global__ __launch_bounds__(kMWaves * 64, (KC <= MC_SIGN && VC <= MC_SIGN) ? 3 
       m_load<KC, VC>(a, row_of(k + NB + 1), mo, b1);
     }
   }
-  // ---- the wavefront's partial per query head
+  // ---- the wavefront's partial per query head (l_part: over the rows, then the copies)
   l_part = sum_rows(l_part);
+  if constexpr (kDedup) {
+    l_part += f_bits((uint32_t)__builtin_amdgcn_mov_dpp((int)u_bits(l_part), 0x124, 0xF, 0xF, false));   // row_ror:4
+    l_part += f_bits((uint32_t)__builtin_amdgcn_mov_dpp((int)u_bits(l_part), 0x128, 0xF, 0xF, false));   // row_ror:8
+  }
   if constexpr (VC == MC_INT8 || VC == MC_I4) w_part = sum_rows(w_part);
   // lane r (< 4) holds head r's m and l; lanes 0-15 hold rows 0-3 (heads) of the outputs
   // the weight sum of output row 4kq + r (int8: rows 0-3; 4-bit values: rows 0-7)
