@@ -1,7 +1,8 @@
 """The allocation-free decode entry point, kvq_decode_attn_static, against
 kvq_decode_attn with a caller workspace (both through the C ABI), on calls in a
-row: a 64K-style MFMA-path cache, then a smaller general-path cache, then the first
-size again (the shared device scratch must have been left ready).  Also checks the
+row: a 64K-style MFMA-path cache, then two smaller head_dim-128 caches (NF4 keys; rFFT
+keys, whose query spectra share the scratch), then the first size again (the shared
+device scratch must have been left ready).  Also checks the
 size limit, which is enforced before anything is launched."""
 import numpy as np
 import pytest
@@ -62,7 +63,9 @@ def test_static_decode_matches_workspace_decode_on_consecutive_calls():
     import kv_cache_bit_fwht_amd as K
     big = ((1, 2, 4, 1000, 256), K.Codec(K.INT_ABSMAX, 4, 128, 256), K.Codec(K.INT_ABSMAX, 2, 128, 0), 16, 2)
     small = ((1, 1, 2, 300, 128), K.Codec(K.NF4, 4, 64, 0), K.Codec(K.INT_ABSMAX, 4, 64, 0), 4, 1)
-    for step, (dims, kc, vc, Hq, n_q) in enumerate((big, small, big)):
+    # rFFT keys keep their query spectra in the scratch after the partials
+    spec = ((2, 1, 2, 700, 128), K.Codec(K.RFFT_CART, 6, 32, 0), K.Codec(K.INT_ABSMAX, 4, 64, 0), 8, 2)
+    for step, (dims, kc, vc, Hq, n_q) in enumerate((big, small, spec, big)):
         announce(f"kvq_decode_attn_static call {step}: dims={dims} K={kc} V={vc} Hq={Hq} n_q={n_q}")
         k, v, q, kv_len, shape, kp, vp = _cache(K, dims, kc, vc, n_q, Hq, seed=100 + step)
         out_s, lse_s, out_w, lse_w = _both(K, kp, vp, shape, q, kv_len, Hq, n_q)
