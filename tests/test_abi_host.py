@@ -247,7 +247,8 @@ def test_decode_validates_before_launching(K):
 
 
 @pytest.mark.parametrize("case", ["tokens_below_32", "head_dim_128", "k_6bit", "v_5bit", "v_group_32",
-                                  "k_minmax", "v_chan_scale", "g8", "v_lloyd_3bit"])
+                                  "k_minmax", "v_chan_scale", "g8", "v_lloyd_4bit", "d128_k_6bit_g64",
+                                  "d128_k_cart_5bit", "d128_k_polar_6bit", "d128_k_6bit_rot64"])
 def test_mfma_path_rejects_what_it_does_not_cover(K, case):
     kc, vc, shape, q_heads = (1, 4, 128, 256, 0), (1, 2, 128, 0, 0), (1, 2, 4, 64, 256), 16
     v_chan = None
@@ -260,8 +261,15 @@ def test_mfma_path_rejects_what_it_does_not_cover(K, case):
         kc = (1, 6, 128, 256, 0)
     elif case == "v_5bit":
         vc = (1, 5, 128, 0, 0)
-    elif case == "v_lloyd_3bit":
-        vc = (10, 3, 128, 0, 0)
+    elif case == "v_lloyd_4bit":
+        vc = (10, 4, 128, 0, 0)
+    elif case.startswith("d128_"):
+        # head_dim 128: 6-bit keys only at group 32 and rotation 0 or 128, rFFT keys only
+        # 6+6-bit Cartesian or 5+7-bit polar at group 32
+        shape = (1, 2, 4, 64, 128)
+        vc = (1, 4, 64, 0, 0)
+        kc = {"d128_k_6bit_g64": (1, 6, 64, 128, 0), "d128_k_cart_5bit": (8, 5, 32, 0, 0),
+              "d128_k_polar_6bit": (7, 6, 32, 0, 7), "d128_k_6bit_rot64": (1, 6, 32, 64, 0)}[case]
     elif case == "v_group_32":
         vc = (1, 2, 32, 0, 0)
     elif case == "k_minmax":
