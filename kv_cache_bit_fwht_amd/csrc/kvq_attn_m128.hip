@@ -1049,6 +1049,52 @@ __global__ __launch_bounds__(64) void k_m128_qspec(const uint16_t* q, float* qs,
   }
 }
 
+// Merge of the splits' partials, one wavefront per (query row, query head): M = the
+// largest split maximum, split weights e^(m_s - M), L = sum of l_s times them, out = the
+// weighted sum of the splits' o over L (fp64, in split order), lse = M + ln L.  The
+// values this kernel decodes are never rotated or channel-scaled and the keys carry no
+// mean, so nothing else is applied.
+constexpr int kMMaxSplits = 512;
+__global__ __launch_bounds__(256) void k_m128_combine(const float* __restrict__ part, int S, long long rows_hq,
+                                                      float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ double wsh[4][kMMaxSplits];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long rh = (long long)blockIdx.x * 4 + wave;
+  if (rh >= rows_hq) return;                         // whole wavefront
+  const float* src = part + (size_t)rh * S * kMPart;
+  double* w = wsh[wave];
+  double mx = -INFINITY;
+  for (int s = lane; s < S; s += 64) mx = fmax(mx, (double)src[(size_t)s * kMPart + kMD]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+  double ls = 0.0;
+  for (int s = lane; s < S; s += 64) {
+    const double ms = (double)src[(size_t)s * kMPart + kMD];
+    const double ww = (mx == -INFINITY || ms == -INFINITY) ? 0.0 : exp(ms - mx);
+    w[s] = ww;
+    ls += (double)src[(size_t)s * kMPart + kMD + 1] * ww;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+  wave_lds_sync();                                   // the weights in LDS, read by every lane
+#pragma unroll
+  for (int d0 = 0; d0 < kMD; d0 += 64) {
+    const int d = d0 + lane;
+    double acc = 0.0;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {                     // eight splits' loads in flight
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(s + u) * kMPart + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += (double)v[u] * w[s + u];
+    }
+    for (; s < S; ++s) acc += (double)src[(size_t)s * kMPart + d] * w[s];
+    out[(size_t)rh * kMD + d] = ls > 0.0 ? (float)(acc / ls) : 0.0f;
+  }
+  if (lane == 0 && lse) lse[rh] = ls > 0.0 ? (float)(mx + log(ls)) : -INFINITY;
+}
+
 // The kernel's codec of a key (K) or value (V) codec, or -1.
 int m128_codec(const kvq_codec& c, bool key) {
   // 6-bit signed absmax keys at group 32, unrotated or rotated over the whole row
@@ -1160,7 +1206,10 @@ hipError_t launch_decode_m128(const AttnProblem& pr, hipStream_t st) {
     default: e = launch_m128_v<MC_F16>(vc, a, grid, st); break;
   }
   if (e != hipSuccess) return e;
-  return launch_combine_partials(pr, a.S, nullptr, st);
+  if (a.S > kMMaxSplits) return launch_combine_partials(pr, a.S, nullptr, st);
+  const long long rows_hq = rows * pr.Hq;
+  k_m128_combine<<<(unsigned)((rows_hq + 3) / 4), 256, 0, st>>>(a.part, a.S, rows_hq, pr.out, pr.lse);
+  return hipGetLastError();
 }
 
 }  // namespace kvq
