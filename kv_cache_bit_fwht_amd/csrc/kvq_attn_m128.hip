@@ -36,7 +36,7 @@
 //    stored); int8 values enter as subnormal codes with A = fp16(p) * s_v and the
 //    offset folded as 127 * sum of A, as for keys.
 // Each wavefront writes one (o, m, l) partial per query head (m in natural-log
-// units); the general combine kernel merges a row's splits in order.
+// units); k_m128_combine merges a row's splits in order.
 //
 // Lane layouts (l = lane, i = l % 16, kq = l / 16):
 //  * Q.K^T tile u: A row i is token 8(i / 4) + 4u + i % 4 of the step, so the
