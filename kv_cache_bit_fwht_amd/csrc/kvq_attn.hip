@@ -53,6 +53,8 @@ struct AArgs {
   int lpt_log2;
   int Dc;              // coded key length (D, or 2*(D/2+1) for rFFT keys)
   float* ws;           // split partials
+  float* dout;         // wavefront decode with one block per row: the output, written by the
+  float* dlse;         // block merge itself (no combine launch); else null.  lse nullable
   const double* js_rowz;  // error kernel, JS pass: per row (ln Z of fp16, ln Z of quant), else null
   Tables tab;
   FftTables tw;        // twiddles of head_dim (rFFT keys: the query's DFT)
@@ -66,6 +68,8 @@ struct WaveView {
   const uint16_t* q;
   const int32_t* kv_len;
   float* ws;
+  float* dout;
+  float* dlse;
   float sm_scale;
   int B, L, H, T, D, Hq, G, n_q, S, chunk, lpt_log2, qp, nqg;
   const Tables& tab;
@@ -904,6 +908,14 @@ __device__ __forceinline__ void wave_unit(const A& a, const DevCodec& kc, const 
       o = __builtin_fmaf(wt, mo[(w * kWaveHeads + g) * D + d], o);
       lw = __builtin_fmaf(wt, ml[w * kWaveHeads + g], lw);
     }
+    if (a.dout) {
+      // the only partial of its row: what the combine would make of it (its fp64 steps)
+      const double lq = (double)lw;
+      a.dout[((size_t)row * a.Hq + head) * D + d] = lq > 0.0 ? (float)((double)o / lq) : 0.0f;
+      if (d == 0 && a.dlse)
+        a.dlse[(size_t)row * a.Hq + head] = lq > 0.0 ? (float)((double)(M * kLn2) + log(lq)) : -INFINITY;
+      continue;
+    }
     float* dst = a.ws + (((size_t)row * a.Hq + head) * gridDim.x + blockIdx.x) * P;
     dst[d] = o;
     if (d == 0) {
@@ -1008,7 +1020,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_wave_mix(MArgs a) {
   const long long urow0 = (((long long)b * t.ls + ll) * t.hs + hl) * a.T;
   const DevCodec kc = mix_codec(t.k), vc = mix_codec(t.v);
   const float* kch = kc.chan ? kc.chan + ((size_t)ll * t.hs + hl) * a.D : nullptr;
-  const WaveView v{a.q, a.kv_len, a.ws, a.sm_scale, a.B, a.L, a.H, a.T, a.D, a.Hq, a.G, a.n_q, a.S, a.chunk,
+  const WaveView v{a.q, a.kv_len, a.ws, nullptr, nullptr, a.sm_scale, a.B, a.L, a.H, a.T, a.D, a.Hq, a.G, a.n_q, a.S, a.chunk,
                    a.lpt_log2, a.qp, a.nqg, a.tab};
   switch (t.pair) {
 #define KVQ_MIX_CASE(id, KCB, KB, VCB, VB) \
@@ -1569,6 +1581,13 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
     a.qp = wave_qp(a.G, a.n_q);
     a.nqg = wave_nqg(a.G, a.n_q);
     const long long R = (long long)a.B * a.L * a.nqg;
+    // one block (4 splits) per row, no value rotation, channel scale or key mean: the
+    // block merge writes the output (the combine would only divide by l)
+    const bool direct = a.S == 4 && pr.v->codec.rot_width <= 1 && !pr.v->chan_scale && !pr.k->mean;
+    if (direct) {
+      a.dout = pr.out;
+      a.dlse = pr.lse;
+    }
     bool compiled = false;
     hipError_t e = dispatch_wave(a, R, st, &compiled);
     if (e != hipSuccess) return e;
@@ -1582,6 +1601,7 @@ hipError_t launch_decode_generic(const AttnProblem& pr, hipStream_t st) {
       e = launch_wave<-1, 0, -1, 0>(a, R, st);
       if (e != hipSuccess) return e;
     }
+    if (direct) return hipSuccess;
     return launch_combine_partials(pr, a.S / 4, nullptr, st);   // one partial per block of 4 splits
   }
   const long long R = (long long)a.B * a.L * a.n_q;
