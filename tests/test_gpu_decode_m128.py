@@ -90,6 +90,25 @@ def test_query_heads_per_kv_head(G):
     _check_decode(out, lse, ref_out, ref_lse, kv_len)
 
 
+@pytest.mark.parametrize("kname", ["i6h", "rc", "rp"])
+@pytest.mark.parametrize("G", [1, 2, 3])
+def test_query_heads_per_kv_head_transform_keys(G, kname):
+    """The 6-bit and rFFT keys (query rotated or transformed in the prologue, high part
+    and remainder in alternate columns) with 1-3 query heads per KV head: the columns of
+    absent heads carry a zero query; lengths 0, 1, 31, 32, 33, T-1, T across rows."""
+    import kv_cache_bit_fwht_amd as K
+    H = 8
+    w, Kx, Vx, q = _inputs(B=1, L=2, T=1000, n_q=4, Hq=G * H)
+    shape = K.Shape(w.B, w.L, w.H, w.T, w.D)
+    kp, Kd = _pack(K, Kx, _codec(K, kname), shape)
+    vp, Vd = _pack(K, Vx, _codec(K, "i4"), shape)
+    kv_len = np.array([[[0, 1, 31, 32], [33, 999, 1000, 517]]], np.int32)
+    announce(f"m128 decode {kname} G={G}")
+    out, lse = _gpu_decode(K, kp, vp, q, kv_len, path=2)
+    ref_out, ref_lse = O.decode_attn(q, Kd, Vd, kv_len)
+    _check_decode(out, lse, ref_out, ref_lse, kv_len)
+
+
 @pytest.mark.parametrize("T", [32, 100, 4096])
 def test_cache_lengths(T):
     import kv_cache_bit_fwht_amd as K
