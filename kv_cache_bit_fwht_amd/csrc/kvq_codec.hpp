@@ -161,6 +161,16 @@ __device__ __forceinline__ void nf4_cells_init(const Tables& tab, float2* cells,
   cells[i] = make_float2(cnt, cand);
 }
 
+// rne(clamp(t, lo, hi)) + off as an unsigned code (lo, hi integers, |lo|, |hi| < 2^22,
+// lo + off >= 0).  Clamping to integer bounds and then rounding is rounding and then
+// clamping; the clamped value plus 1.5 * 2^23 is rounded to the nearest integer (ties to
+// even: 1.5 * 2^23 is even), which then sits in the low mantissa bits of the sum, so
+// one add and one integer subtract replace the round and the float-to-int conversion.
+__device__ __forceinline__ uint32_t rne_code(float t, float lo, float hi, uint32_t off) {
+  const float x = __builtin_fminf(__builtin_fmaxf(t, lo), hi) + 12582912.0f;
+  return __builtin_bit_cast(uint32_t, x) - (0x4B400000u - off);
+}
+
 template <int CB, int BITS>
 __device__ __forceinline__ void encode16(const float v[16], int g, const Tables& tab, uint32_t c[16],
                                          uint16_t s16[2], uint16_t z16[2], const float2* nf4_cells = nullptr) {
@@ -178,8 +188,7 @@ __device__ __forceinline__ void encode16(const float v[16], int g, const Tables&
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i] * inv[i >> 3]), lo), hi);
-      c[i] = (uint32_t)((int)q + (1 << (BITS - 1)));
+      c[i] = rne_code(v[i] * inv[i >> 3], lo, hi, 1u << (BITS - 1));
     }
   } else if constexpr (CB == KVQ_INT_MINMAX) {
     float mx[2], mn[2];
@@ -196,8 +205,7 @@ __device__ __forceinline__ void encode16(const float v[16], int g, const Tables&
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float t = (v[i] - zf[i >> 3]) * inv[i >> 3];
-      const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(t), 0.0f), steps);
-      c[i] = (uint32_t)(int)q;
+      c[i] = rne_code(t, 0.0f, steps, 0u);
     }
   } else if constexpr (CB == KVQ_TERNARY || CB == KVQ_NF4 || CB == KVQ_INT8_SYM) {
     float am[2];
@@ -212,9 +220,9 @@ __device__ __forceinline__ void encode16(const float v[16], int g, const Tables&
     for (int i = 0; i < 16; ++i) {
       const float t = v[i] * inv[i >> 3];
       if constexpr (CB == KVQ_TERNARY) {
-        c[i] = (uint32_t)((int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(t), -1.0f), 1.0f) + 1);
+        c[i] = rne_code(t, -1.0f, 1.0f, 1u);
       } else if constexpr (CB == KVQ_INT8_SYM) {
-        c[i] = (uint32_t)((int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(t), -127.0f), 127.0f) + 127);
+        c[i] = rne_code(t, -127.0f, 127.0f, 127u);
       } else {
         // number of midpoints strictly below t, from the cell table in LDS
         const int ci = min(max((int)((t + 1.0f) * 128.0f), 0), 255);
@@ -237,7 +245,7 @@ __device__ __forceinline__ void encode16(const float v[16], int g, const Tables&
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float t = v[i] * inv[i >> 3];
-      c[i] = (uint32_t)(int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(t + h), 0.0f), top);
+      c[i] = rne_code(t + h, 0.0f, top, 0u);
     }
   } else if constexpr (CB == KVQ_LLOYD) {
     // Gaussian Lloyd-Max levels L; s = RMS = sqrt(RN32(sum y^2 * 1/g)); code = number of
