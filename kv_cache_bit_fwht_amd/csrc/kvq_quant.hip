@@ -309,16 +309,18 @@ static int grid_for(long long rows, int lpt_log2) {
   return (int)(blocks < 1 ? 1 : blocks);
 }
 
-// The general quantise kernel's grid.  Sign and int8 codes run faster with one block per
-// RPB rows that codes its rows once and exits (the rows in flight are then a contiguous
-// window of the tensor); the other codecs faster on the capped grid-stride grid (NF4
-// builds its cell table once per block; measured on head_dim-128 tensors of 16.8M rows:
-// sign 1,103 -> 1,000 us and int8 1,424 -> 1,250 us one-pass, while ternary, NF4, 4-bit
-// and rotated 6-bit codes are 0-48% slower that way).
-static unsigned quantize_grid(long long rows, int lpt_log2, int codebook) {
-  if (codebook != KVQ_SIGN && codebook != KVQ_INT8_SYM) return (unsigned)grid_for(rows, lpt_log2);
+// The general quantise kernel's grid, as measured on head_dim-128 tensors of 16.8M rows
+// (HIP events, one box; the kernel holds no LDS tile, so occupancy is set by registers):
+// one block per RPB rows that codes its rows once and exits is fastest for unrotated
+// codes (ternary 1,103 -> 1,021 us, 4-bit 1,166 -> 994 us against the grid capped at
+// 2,048 blocks; sign 924 us, int8 1,106 us); NF4, which builds a cell table per block,
+// and rotated codes are fastest on a grid-stride grid of 65,536 blocks (NF4 1,158 ->
+// 1,026 us against 2,048 blocks and 1,389 us one-pass; rotated 6-bit 1,454 -> 1,294 us
+// against 2,048 blocks and 1,416 us one-pass).
+static unsigned quantize_grid(long long rows, int lpt_log2, int codebook, int rot_width) {
   const long long rpb = kBlock >> lpt_log2;
-  const long long blocks = (rows + rpb - 1) / rpb;
+  long long blocks = (rows + rpb - 1) / rpb;
+  if ((codebook == KVQ_NF4 || rot_width > 1) && blocks > 65536) blocks = 65536;
   return (unsigned)(blocks < 1 ? 1 : blocks);
 }
 
@@ -702,7 +704,7 @@ hipError_t launch_quantize(const uint16_t* x, const kvq_packed& p, hipStream_t s
     launch_absmax256(a, p.codec, st);
     return hipGetLastError();
   }
-  const dim3 grid(quantize_grid(a.rows, a.lpt_log2, p.codec.codebook)), block(kBlock);
+  const dim3 grid(quantize_grid(a.rows, a.lpt_log2, p.codec.codebook, a.W)), block(kBlock);
   KVQ_DISPATCH_CODEC(p.codec.codebook, p.codec.bits, k_quantize, <<<grid, block, 0, st>>>(a))
   return hipGetLastError();
 }
@@ -718,7 +720,7 @@ hipError_t launch_quantize_tokens(const uint16_t* x, const kvq_packed& p, int t0
     launch_absmax256(a, p.codec, st);
     return hipGetLastError();
   }
-  const dim3 grid(quantize_grid(a.rows, a.lpt_log2, p.codec.codebook)), block(kBlock);
+  const dim3 grid(quantize_grid(a.rows, a.lpt_log2, p.codec.codebook, a.W)), block(kBlock);
   KVQ_DISPATCH_CODEC(p.codec.codebook, p.codec.bits, k_quantize, <<<grid, block, 0, st>>>(a))
   return hipGetLastError();
 }
